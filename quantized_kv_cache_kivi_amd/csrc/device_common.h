@@ -1,0 +1,83 @@
+// Device helpers shared by the libkvq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr float EPS_SCALE = 1e-5f;  // eps of the affine scale (StreamingLLM + KIVI page, "Affine quantisation formula")
+
+__device__ __forceinline__ uint16_t f16_bits(float x) {
+  const _Float16 h = (_Float16)x;  // v_cvt_f16_f32: round to nearest even, subnormals kept
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// One input element (fp16 or fp32 as the caller hands it), as fp32.
+__device__ __forceinline__ float ld_in(const void* p, int64_t i, int in_f32) {
+  return in_f32 ? static_cast<const float*>(p)[i] : (float)static_cast<const _Float16*>(p)[i];
+}
+// The fp16 bit pattern of an input element (fp16 input is copied, fp32 input rounded to nearest even).
+__device__ __forceinline__ uint16_t ld_in_f16(const void* p, int64_t i, int in_f32) {
+  return in_f32 ? f16_bits(static_cast<const float*>(p)[i]) : static_cast<const uint16_t*>(p)[i];
+}
+
+// Word-interleaved packing: code k of a 32-bit word of b-bit codes sits at bit 16*(k%2) + b*(k/2).
+__device__ __forceinline__ int code_shift(int k, int b) { return 16 * (k & 1) + b * (k >> 1); }
+
+// Byte offset of the word holding K code (t, c) inside the K section, and its in-word index.
+__device__ __forceinline__ void k_code_pos(int t, int c, int D, int b, int* word, int* k) {
+  const int per = 32 / b;
+  *word = t * (D * b / 32) + c / per;
+  *k = c % per;
+}
+// V tile order: token t, channel c -> chunk 16*kg + i, sequence index 8*mu + e.
+__device__ __forceinline__ void v_code_pos(int t, int c, int D, int b, int* word, int* k) {
+  const int kg = (t & 15) >> 2, e = ((t >> 4) << 2) | (t & 3);
+  const int i = c & 15, mu = c >> 4;
+  const int q = 16 * kg + i, s = 8 * mu + e, per = 32 / b;
+  *word = q * (D * b / 64) + s / per;
+  *k = s % per;
+}
+// Token of element e of V token group kg.
+__device__ __forceinline__ int v_tok(int kg, int e) { return 16 * (e >> 2) + 4 * kg + (e & 3); }
+
+__device__ __forceinline__ float wave_sum_xor(float a, int first_off) {
+  for (int off = first_off; off >= 1; off >>= 1) a = a + __shfl_xor(a, off);
+  return a;
+}
+
+// In-wave fast Walsh-Hadamard transform of a D-vector held two per lane
+// (lane l holds elements 2l, 2l+1; lanes >= D/2 carry don't-care values).
+// Stages len = 1, 2, ..., D/2: (u, v) -> (u + v, u - v) with u the lower element
+// ("TurboQuant KV Cache Compression — Spec", "Hadamard Transform Detail").
+__device__ __forceinline__ void wave_fwht(float& y0, float& y1, int D, int lane) {
+  const float a = y0 + y1, b = y0 - y1;
+  y0 = a;
+  y1 = b;
+  for (int len = 2; len < D; len <<= 1) {
+    const int m = len >> 1;
+    const float p0 = __shfl_xor(y0, m), p1 = __shfl_xor(y1, m);
+    if (lane & m) {
+      y0 = p0 - y0;
+      y1 = p1 - y1;
+    } else {
+      y0 = y0 + p0;
+      y1 = y1 + p1;
+    }
+  }
+}
+
+// Canonical fp32 sum of squares of a D-vector held two per lane: pair products,
+// then a butterfly over lane offsets D/4, D/8, ..., 1 (every lane ends with the sum).
+__device__ __forceinline__ float wave_sumsq(float y0, float y1, int D) {
+  const float p = y0 * y0;
+  const float q = y1 * y1;
+  return wave_sum_xor(p + q, D >> 2);
+}
+
+}  // namespace kvq

@@ -1,0 +1,496 @@
+// Host side of the C ABI: validation, storage layout, call-order state and
+// launch glue.  Every compute step runs in the HIP kernels; this file only
+// checks arguments, tracks (P, lo) per layer and issues launches.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+thread_local std::string g_err;
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+struct RecordSections {
+  uint64_t kc, vc, km, vm, rec;
+};
+
+RecordSections record_sections(const kvq_config& c) {
+  RecordSections r;
+  const uint64_t D = c.head_dim;
+  r.kc = G * D * c.k_bits / 8;
+  r.vc = G * D * c.v_bits / 8;
+  if (c.format == KVQ_FMT_KIVI) {
+    r.km = 2 * 2 * D;
+    r.vm = 2 * 2 * G * (D / 32);
+  } else if (c.format == KVQ_FMT_Q2K) {
+    r.km = 2 * D;
+    r.vm = 2 * G * (D / 32);
+  } else {
+    r.km = 4 * G;
+    r.vm = 4 * G;
+  }
+  r.rec = r.kc + r.vc + r.km + r.vm;
+  return r;
+}
+
+int32_t effective_capacity(const kvq_config& c) {
+  if (c.capacity > 0) return c.capacity;
+  if (c.window > 0) return G * ((c.window + 1 + G - 1) / G + 1);
+  return 0;
+}
+
+kvq_status check(const kvq_config* c) {
+  if (!c) return fail(KVQ_EINVAL, "config is NULL");
+  if (c->n_layers < 1 || c->batch < 1 || c->n_kv_heads < 1 || c->n_q_heads < 1)
+    return fail(KVQ_EINVAL, "n_layers, batch, n_kv_heads and n_q_heads must be >= 1");
+  if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > MAX_GQA)
+    return fail(KVQ_EINVAL, "n_q_heads must be a multiple of n_kv_heads with ratio <= %d", MAX_GQA);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVQ_EINVAL, "head_dim must be 32, 64 or 128 (got %d)", c->head_dim);
+  auto okb = [](int b) { return b == 2 || b == 4 || b == 8; };
+  switch (c->format) {
+    case KVQ_FMT_KIVI:
+      if (!okb(c->k_bits) || !okb(c->v_bits)) return fail(KVQ_EINVAL, "KIVI bits must be 2, 4 or 8");
+      break;
+    case KVQ_FMT_Q2K:
+      if (c->k_bits != 2 || c->v_bits != 4) return fail(KVQ_EINVAL, "Q2K needs k_bits = 2 and v_bits = 4");
+      break;
+    case KVQ_FMT_TQ:
+      if ((c->k_bits != 2 && c->k_bits != 4) || (c->v_bits != 2 && c->v_bits != 4))
+        return fail(KVQ_EINVAL, "TQ bits must be 2 or 4");
+      break;
+    default:
+      return fail(KVQ_EINVAL, "unknown format %d", c->format);
+  }
+  if (c->sink_mode < KVQ_SINK_NONE || c->sink_mode > KVQ_SINK_TOPK) return fail(KVQ_EINVAL, "unknown sink_mode");
+  if (c->n_sink < 0 || c->n_sink > MAX_SINK) return fail(KVQ_EINVAL, "n_sink must be in [0, %d]", MAX_SINK);
+  if (c->sink_mode == KVQ_SINK_NONE && c->n_sink != 0) return fail(KVQ_EINVAL, "n_sink > 0 needs a sink mode");
+  if (c->window < 0 || c->residual < 0) return fail(KVQ_EINVAL, "window and residual must be >= 0");
+  if (c->in_dtype != KVQ_IN_F16 && c->in_dtype != KVQ_IN_F32) return fail(KVQ_EINVAL, "in_dtype must be 0 or 1");
+  if (c->capacity < 0 || c->capacity % G != 0) return fail(KVQ_EINVAL, "capacity must be a multiple of 32");
+  const int32_t cap = effective_capacity(*c);
+  if (cap < G) return fail(KVQ_EINVAL, "capacity must be given (>= 32) when window = 0");
+  if (c->window > 0 && cap < G * ((c->window + G - 1) / G + 1))
+    return fail(KVQ_EINVAL, "capacity %d too small for window %d (needs one spare block)", cap, c->window);
+  if (c->residual > cap) return fail(KVQ_EINVAL, "residual larger than capacity");
+  g_err.clear();
+  return KVQ_OK;
+}
+
+kvq_layout make_layout(const kvq_config& c) {
+  kvq_layout L;
+  std::memset(&L, 0, sizeof(L));
+  const RecordSections rs = record_sections(c);
+  const uint64_t S = (uint64_t)c.batch * c.n_kv_heads, D = c.head_dim;
+  const uint64_t esz = c.in_dtype == KVQ_IN_F32 ? 4 : 2;
+  L.capacity = effective_capacity(c);
+  L.cap_blocks = L.capacity / G;
+  L.record_bytes = rs.rec;
+  L.rec_k_codes = 0;
+  L.rec_v_codes = rs.kc;
+  L.rec_k_meta = rs.kc + rs.vc;
+  L.rec_v_meta = rs.kc + rs.vc + rs.km;
+  uint64_t off = 0;
+  L.bulk = off;
+  off = align256(off + S * L.cap_blocks * rs.rec);
+  L.staging = off;
+  if (c.format != KVQ_FMT_TQ) off = align256(off + S * G * D * esz);
+  L.win_k = off;
+  off = align256(off + S * c.residual * D * 2);
+  L.win_v = off;
+  off = align256(off + S * c.residual * D * 2);
+  L.sink_k = off;
+  off = align256(off + S * c.n_sink * D * 2);
+  L.sink_v = off;
+  off = align256(off + S * c.n_sink * D * 2);
+  L.sink_pos = off;
+  off = align256(off + (uint64_t)c.batch * c.n_sink * 4);
+  L.sink_score = off;
+  off = align256(off + (uint64_t)c.batch * c.n_sink * 4);
+  L.sink_count = off;
+  off = align256(off + (uint64_t)c.batch * 4);
+  L.counters = off;
+  off = align256(off + S * 4);
+  L.layer_stride = off;
+  L.tables = (uint64_t)c.n_layers * L.layer_stride;
+  L.total = L.tables + align256(sizeof(Tables));
+  return L;
+}
+
+constexpr int TARGET_WGS = 2048;       // split-K target: many more workgroups than the 256 CUs
+constexpr int MIN_BLOCKS_PER_SPLIT = 2;
+
+int max_splits(const kvq_config& c) {
+  const int streams = c.batch * c.n_kv_heads;
+  int s = (TARGET_WGS + streams - 1) / streams;
+  return std::max(1, std::min(s, 64));
+}
+
+}  // namespace
+
+struct kvq_cache {
+  kvq_config cfg;
+  kvq_layout lay;
+  uint8_t* base;
+  std::vector<int64_t> P, lo, pend_P;
+  std::vector<int32_t> pend_n;
+  Tables tables;
+};
+
+namespace {
+
+Shape shape_of(const kvq_config& c) {
+  Shape s;
+  s.B = c.batch;
+  s.Hkv = c.n_kv_heads;
+  s.Hq = c.n_q_heads;
+  s.D = c.head_dim;
+  s.fmt = c.format;
+  s.kb = c.k_bits;
+  s.vb = c.v_bits;
+  s.sink_mode = c.n_sink > 0 ? c.sink_mode : KVQ_SINK_NONE;
+  s.n_sink = c.n_sink;
+  s.W = c.window;
+  s.R = c.residual;
+  s.in_f32 = c.in_dtype == KVQ_IN_F32;
+  return s;
+}
+
+LayerView view_of(const kvq_cache* c, int layer) {
+  const kvq_layout& L = c->lay;
+  uint8_t* b = c->base + (uint64_t)layer * L.layer_stride;
+  LayerView v;
+  v.bulk = b + L.bulk;
+  v.staging = b + L.staging;
+  v.win_k = (uint16_t*)(b + L.win_k);
+  v.win_v = (uint16_t*)(b + L.win_v);
+  v.sink_k = (uint16_t*)(b + L.sink_k);
+  v.sink_v = (uint16_t*)(b + L.sink_v);
+  v.sink_pos = (int32_t*)(b + L.sink_pos);
+  v.sink_score = (float*)(b + L.sink_score);
+  v.sink_count = (int32_t*)(b + L.sink_count);
+  v.counters = (int32_t*)(b + L.counters);
+  v.tables = (const Tables*)(c->base + L.tables);
+  v.rec = (int64_t)L.record_bytes;
+  v.k_codes = (int64_t)L.rec_k_codes;
+  v.v_codes = (int64_t)L.rec_v_codes;
+  v.k_meta = (int64_t)L.rec_k_meta;
+  v.v_meta = (int64_t)L.rec_v_meta;
+  v.cap_b = L.cap_blocks;
+  return v;
+}
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+kvq_status check_layer(const kvq_cache* c, int32_t layer) {
+  if (!c) return fail(KVQ_EINVAL, "cache is NULL");
+  if (layer < 0 || layer >= c->cfg.n_layers) return fail(KVQ_EINVAL, "layer %d out of range", layer);
+  return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_config_check(const kvq_config* cfg) { return check(cfg); }
+
+size_t kvq_required_bytes(const kvq_config* cfg) {
+  if (check(cfg) != KVQ_OK) return 0;
+  return (size_t)make_layout(*cfg).total;
+}
+
+kvq_status kvq_get_layout(const kvq_config* cfg, kvq_layout* out) {
+  kvq_status st = check(cfg);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_EINVAL, "out is NULL");
+  *out = make_layout(*cfg);
+  return KVQ_OK;
+}
+
+size_t kvq_workspace_bytes(const kvq_config* cfg) {
+  if (check(cfg) != KVQ_OK) return 0;
+  const size_t streams = (size_t)cfg->batch * cfg->n_kv_heads;
+  const size_t r = cfg->n_q_heads / cfg->n_kv_heads;
+  return streams * (size_t)(max_splits(*cfg) + 1) * r * (size_t)(cfg->head_dim + 2) * sizeof(float);
+}
+
+kvq_status kvq_create(const kvq_config* cfg, void* dev_buf, size_t dev_bytes, void* stream, kvq_cache** out) {
+  kvq_status st = check(cfg);
+  if (st != KVQ_OK) return st;
+  if (!dev_buf || !out) return fail(KVQ_EINVAL, "dev_buf and out must not be NULL");
+  if (((uintptr_t)dev_buf & 255) != 0) return fail(KVQ_EINVAL, "dev_buf must be 256-byte aligned");
+  const kvq_layout lay = make_layout(*cfg);
+  if (dev_bytes < lay.total) return fail(KVQ_EINVAL, "dev_bytes %zu < required %llu", dev_bytes,
+                                         (unsigned long long)lay.total);
+  kvq_cache* c = new (std::nothrow) kvq_cache;
+  if (!c) return fail(KVQ_EINVAL, "out of host memory");
+  c->cfg = *cfg;
+  c->cfg.capacity = lay.capacity;
+  c->lay = lay;
+  c->base = (uint8_t*)dev_buf;
+  c->P.assign(cfg->n_layers, 0);
+  c->lo.assign(cfg->n_layers, 0);
+  c->pend_P.assign(cfg->n_layers, -1);
+  c->pend_n.assign(cfg->n_layers, -1);
+  make_tables(c->cfg, &c->tables);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemsetAsync(dev_buf, 0, lay.total, s);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "hipMemsetAsync");
+  }
+  if (cfg->n_sink > 0) {
+    for (int l = 0; l < cfg->n_layers && e == hipSuccess; ++l)
+      e = hipMemsetAsync(c->base + (uint64_t)l * lay.layer_stride + lay.sink_pos, 0xFF,
+                         (size_t)cfg->batch * cfg->n_sink * 4, s);
+    if (e != hipSuccess) {
+      delete c;
+      return hip_fail(e, "hipMemsetAsync");
+    }
+  }
+  e = hipMemcpyAsync(c->base + lay.tables, &c->tables, sizeof(Tables), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host table copy must land before the handle is used
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, "table upload");
+  }
+  *out = c;
+  g_err.clear();
+  return KVQ_OK;
+}
+
+kvq_status kvq_destroy(kvq_cache* c) {
+  if (!c) return fail(KVQ_EINVAL, "cache is NULL");
+  delete c;
+  return KVQ_OK;
+}
+
+kvq_status kvq_select_sinks(kvq_cache* c, int32_t layer, const void* k, int32_t n, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!k || n < 1) return fail(KVQ_EINVAL, "k must not be NULL and n >= 1");
+  c->pend_P[layer] = c->P[layer];
+  c->pend_n[layer] = n;
+  if (c->cfg.sink_mode != KVQ_SINK_TOPK || c->cfg.n_sink == 0) return KVQ_OK;
+  SelectArgs a;
+  a.sh = shape_of(c->cfg);
+  a.lv = view_of(c, layer);
+  a.k = k;
+  a.P = c->P[layer];
+  a.n = n;
+  hipError_t e = launch_select(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "select launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_append(kvq_cache* c, int32_t layer, const void* k, const void* v, int32_t n, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!k || !v || n < 1) return fail(KVQ_EINVAL, "k and v must not be NULL and n >= 1");
+  const kvq_config& cf = c->cfg;
+  const int64_t P = c->P[layer];
+  if (cf.sink_mode == KVQ_SINK_TOPK && cf.n_sink > 0 && (c->pend_P[layer] != P || c->pend_n[layer] != n))
+    return fail(KVQ_EORDER, "TOPK mode: call kvq_select_sinks on this chunk (P=%lld, n=%d) first", (long long)P, n);
+  if (cf.window == 0) {
+    if (P + n > cf.capacity)
+      return fail(KVQ_ECAPACITY, "append of %d rows at P=%lld exceeds capacity %d", n, (long long)P, cf.capacity);
+  } else {
+    const int64_t last = (P + n - 1) / G;
+    if ((last - c->lay.cap_blocks + 1) * G > c->lo[layer])
+      return fail(KVQ_ECAPACITY, "append of %d rows at P=%lld would overwrite a live block (lo=%lld); evict first",
+                  n, (long long)P, (long long)c->lo[layer]);
+  }
+  AppendArgs a;
+  a.sh = shape_of(cf);
+  a.lv = view_of(c, layer);
+  a.k = k;
+  a.v = v;
+  a.P = P;
+  a.n = n;
+  a.blk0 = P / G;
+  a.nblk = (int)((P + n - 1) / G - a.blk0 + 1);
+  hipError_t e = launch_append(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  c->P[layer] = P + n;
+  c->pend_P[layer] = -1;
+  c->pend_n[layer] = -1;
+  return KVQ_OK;
+}
+
+kvq_status kvq_evict(kvq_cache* c, int32_t layer) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (c->cfg.window > 0) c->lo[layer] = std::max(c->lo[layer], c->P[layer] - (int64_t)c->cfg.window);
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
+                           size_t ws_bytes, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || !ws) return fail(KVQ_EINVAL, "q, out and ws must not be NULL");
+  if (ws_bytes < kvq_workspace_bytes(&c->cfg)) return fail(KVQ_EINVAL, "ws_bytes too small");
+  const kvq_config& cf = c->cfg;
+  const int64_t P = c->P[layer], lo = c->lo[layer];
+  if (P == 0) return fail(KVQ_ERANGE, "layer %d is empty", layer);
+  DecodeArgs a;
+  a.sh = shape_of(cf);
+  a.lv = view_of(c, layer);
+  a.q = q;
+  a.out = out;
+  a.ws = (float*)ws;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)cf.head_dim);
+  a.P = P;
+  a.lo = lo;
+  a.bulk_lo = lo;
+  a.bulk_hi = std::max(lo, P - (int64_t)cf.residual);
+  if (a.bulk_hi > a.bulk_lo) {
+    a.blk_first = a.bulk_lo / G;
+    a.nblk = (int)((a.bulk_hi - 1) / G - a.blk_first + 1);
+    int s = std::min(max_splits(cf), (a.nblk + MIN_BLOCKS_PER_SPLIT - 1) / MIN_BLOCKS_PER_SPLIT);
+    s = std::max(1, s);
+    a.blocks_per_split = (a.nblk + s - 1) / s;
+    a.splits = (a.nblk + a.blocks_per_split - 1) / a.blocks_per_split;
+  } else {
+    a.blk_first = 0;
+    a.nblk = 0;
+    a.splits = 0;
+    a.blocks_per_split = 0;
+  }
+  hipError_t e = launch_decode(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_dequant(kvq_cache* c, int32_t layer, int32_t which, int64_t pos0, int32_t count, uint16_t* out,
+                       void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!out || (which != 0 && which != 1)) return fail(KVQ_EINVAL, "out must not be NULL and which in {0, 1}");
+  if (count < 1 || pos0 < c->lo[layer] || pos0 + count > c->P[layer])
+    return fail(KVQ_ERANGE, "positions [%lld, %lld) not inside the valid range [%lld, %lld)", (long long)pos0,
+                (long long)(pos0 + count), (long long)c->lo[layer], (long long)c->P[layer]);
+  DequantArgs a;
+  a.sh = shape_of(c->cfg);
+  a.lv = view_of(c, layer);
+  a.which = which;
+  a.P = c->P[layer];
+  a.lo = c->lo[layer];
+  a.pos0 = pos0;
+  a.count = count;
+  a.out = out;
+  hipError_t e = launch_dequant(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_account(kvq_cache* c, int32_t layer, kvq_bytes* out, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!out) return fail(KVQ_EINVAL, "out is NULL");
+  const kvq_config& cf = c->cfg;
+  const int B = cf.batch, ns = cf.n_sink;
+  std::vector<int32_t> pos((size_t)B * std::max(ns, 1), -1), cnt(B, 0);
+  hipStream_t s = (hipStream_t)stream;
+  LayerView v = view_of(c, layer);
+  hipError_t e = hipSuccess;
+  if (ns > 0) {
+    e = hipMemcpyAsync(pos.data(), v.sink_pos, (size_t)B * ns * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(cnt.data(), v.sink_count, (size_t)B * 4, hipMemcpyDeviceToHost, s);
+  }
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "account copy");
+  const int64_t P = c->P[layer], lo = c->lo[layer], R = cf.residual;
+  const int64_t H = cf.n_kv_heads, D = cf.head_dim;
+  const RecordSections rs = record_sections(cf);
+  std::memset(out, 0, sizeof(*out));
+  const int64_t wlo = std::max(lo, P - R);
+  for (int b = 0; b < B; ++b) {
+    std::vector<int64_t> sinks;
+    for (int i = 0; i < cnt[b] && i < ns; ++i)
+      if (pos[(size_t)b * ns + i] >= 0 && pos[(size_t)b * ns + i] < P) sinks.push_back(pos[(size_t)b * ns + i]);
+    std::sort(sinks.begin(), sinks.end());
+    int64_t n_win = std::max<int64_t>(0, P - wlo), n_bulk = std::max<int64_t>(0, wlo - lo);
+    std::vector<int64_t> bulk_blocks_with_sink_only;
+    for (int64_t p : sinks) {
+      if (p >= wlo) --n_win;
+      else if (p >= lo) --n_bulk;
+    }
+    // blocks holding >= 1 compressed row
+    int64_t nblocks = 0;
+    if (wlo > lo) {
+      for (int64_t blk = lo / G; blk <= (wlo - 1) / G; ++blk) {
+        const int64_t a = std::max(lo, blk * G), z = std::min(wlo, (blk + 1) * G);
+        int64_t rows = z - a;
+        for (int64_t p : sinks)
+          if (p >= a && p < z) --rows;
+        if (rows > 0) ++nblocks;
+      }
+    }
+    const int64_t n_s = (int64_t)sinks.size();
+    out->n_sink += n_s;
+    out->n_residual += n_win;
+    out->n_compressed += n_bulk;
+    out->n_valid += n_s + n_win + n_bulk;
+    int64_t meta = cf.format == KVQ_FMT_TQ ? n_bulk * 8 * H
+                                           : nblocks * (int64_t)rs.km * H + n_bulk * (int64_t)(rs.vm / G) * H;
+    out->compressed_bytes += n_bulk * H * D * (cf.k_bits + cf.v_bits) / 8 + meta;
+    out->sink_fp16_bytes += n_s * H * D * 2 * 2;
+    out->residual_fp16_bytes += n_win * H * D * 2 * 2;
+  }
+  out->current_length = P;
+  return KVQ_OK;
+}
+
+kvq_status kvq_get_state(const kvq_cache* c, int32_t layer, int64_t* P, int64_t* lo) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (P) *P = c->P[layer];
+  if (lo) *lo = c->lo[layer];
+  return KVQ_OK;
+}
+
+kvq_status kvq_format_tables(const kvq_config* cfg, float* signs, float* k_bnd, float* k_cen, float* v_bnd,
+                             float* v_cen, float* q2k_thr, float* q2k_lvl) {
+  kvq_status st = check(cfg);
+  if (st != KVQ_OK) return st;
+  Tables t;
+  make_tables(*cfg, &t);
+  const int kl = 1 << cfg->k_bits, vl = 1 << cfg->v_bits;
+  if (signs) std::memcpy(signs, t.signs, sizeof(float) * cfg->head_dim);
+  if (cfg->format == KVQ_FMT_TQ) {
+    if (k_bnd) std::memcpy(k_bnd, t.k_bnd, sizeof(float) * (kl - 1));
+    if (k_cen) std::memcpy(k_cen, t.k_cen, sizeof(float) * kl);
+    if (v_bnd) std::memcpy(v_bnd, t.v_bnd, sizeof(float) * (vl - 1));
+    if (v_cen) std::memcpy(v_cen, t.v_cen, sizeof(float) * vl);
+  }
+  if (q2k_thr) std::memcpy(q2k_thr, t.q2k_thr, sizeof(float) * 3);
+  if (q2k_lvl) std::memcpy(q2k_lvl, t.q2k_lvl, sizeof(float) * 4);
+  return KVQ_OK;
+}
+
+const char* kvq_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

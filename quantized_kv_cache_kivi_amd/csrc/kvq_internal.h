@@ -1,0 +1,100 @@
+// Internal declarations shared by the host code and the HIP kernels of libkvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int G = 32;          // token block length and V channel-group length
+constexpr int MAX_SINK = 16;   // largest n_sink
+constexpr int MAX_GQA = 16;    // largest n_q_heads / n_kv_heads
+constexpr int MAX_D = 128;     // largest head_dim
+
+// fp32 tables written once into the device buffer (tables region).
+struct Tables {
+  float signs[MAX_D];   // TQ sign diagonal (+-1)
+  float k_bnd[16];      // TQ K boundaries in t-space (2^k_bits - 1 used)
+  float k_cen[16];      // TQ K centroids
+  float v_bnd[16];      // TQ V boundaries
+  float v_cen[16];      // TQ V centroids
+  float q2k_thr[4];     // Gaussian 4-level Lloyd-Max thresholds (3 used)
+  float q2k_lvl[4];     // Gaussian 4-level Lloyd-Max levels
+};
+
+// Everything a kernel needs to address one layer of the cache.
+struct LayerView {
+  uint8_t* bulk;        // [S][cap_b][rec]
+  uint8_t* staging;     // [S][32][D] in_dtype
+  uint16_t* win_k;      // [S][R][D]
+  uint16_t* win_v;
+  uint16_t* sink_k;     // [S][n_sink][D]
+  uint16_t* sink_v;
+  int32_t* sink_pos;    // [B][n_sink]
+  float* sink_score;    // [B][n_sink]
+  int32_t* sink_count;  // [B]
+  int32_t* counters;    // [B*Hkv]
+  const Tables* tables;
+  int64_t rec, k_codes, v_codes, k_meta, v_meta;  // record size and section offsets
+  int cap_b;
+};
+
+struct Shape {
+  int B, Hkv, Hq, D, fmt, kb, vb, sink_mode, n_sink, W, R, in_f32;
+};
+
+struct AppendArgs {
+  Shape sh;
+  LayerView lv;
+  const void* k;        // [B][Hkv][n][D]
+  const void* v;
+  int64_t P;            // rows already appended
+  int n;                // rows in this call
+  int64_t blk0;         // first block touched
+  int nblk;             // blocks touched
+};
+
+struct SelectArgs {
+  Shape sh;
+  LayerView lv;
+  const void* k;
+  int64_t P;
+  int n;
+};
+
+struct DecodeArgs {
+  Shape sh;
+  LayerView lv;
+  const void* q;        // [B][Hq][D]
+  float* out;           // [B][Hq][D]
+  float* ws;            // partials
+  float scale;
+  int64_t P, lo;
+  int64_t bulk_lo, bulk_hi;  // bulk token range [bulk_lo, bulk_hi)
+  int64_t blk_first;         // first bulk block
+  int nblk;                  // bulk blocks
+  int splits;                // bulk splits S (the fp16 split is index S)
+  int blocks_per_split;
+};
+
+struct DequantArgs {
+  Shape sh;
+  LayerView lv;
+  int which;
+  int64_t P, lo, pos0;
+  int count;
+  uint16_t* out;
+};
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+
+// Host-side table generation (tables.cpp).
+void make_tables(const kvq_config& cfg, Tables* t);
+
+}  // namespace kvq

@@ -1,0 +1,182 @@
+"""ctypes binding of libkvq (include/kvq.h): argument marshalling only.
+
+Every entry point of the C ABI is exposed under the same name.  Torch is used
+for device memory and streams only: ``Cache`` owns the cache buffer and the
+decode workspace as torch uint8 tensors and passes raw pointers and the
+current HIP stream to the library.  Nothing here computes any step of the
+method; if the shared library is missing the import fails loudly.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+FMT = {"kivi": 0, "q2k": 1, "tq": 2}
+SINK = {"none": 0, "first_n": 1, "topk": 2}
+IN_DTYPE = {"f16": 0, "f32": 1}
+STATUS = {0: "KVQ_OK", -1: "KVQ_EINVAL", -2: "KVQ_ERANGE", -3: "KVQ_ECAPACITY", -4: "KVQ_EORDER", -5: "KVQ_EDEVICE"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class kvq_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "batch", "n_kv_heads", "n_q_heads", "head_dim", "format", "k_bits", "v_bits",
+        "sink_mode", "n_sink", "window", "residual", "capacity", "in_dtype")] + [("seed", ctypes.c_uint64)]
+
+
+class kvq_bytes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "n_valid", "n_compressed", "n_sink", "n_residual", "current_length",
+        "compressed_bytes", "sink_fp16_bytes", "residual_fp16_bytes")]
+
+
+class kvq_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "layer_stride", "bulk", "record_bytes", "rec_k_codes", "rec_v_codes", "rec_k_meta", "rec_v_meta",
+        "staging", "win_k", "win_v", "sink_k", "sink_v", "sink_pos", "sink_score", "sink_count", "counters",
+        "tables", "total")] + [("cap_blocks", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_kv_cache_kivi_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    cfgp = ctypes.POINTER(kvq_config)
+    sig = {
+        "kvq_config_check": (I32, [cfgp]),
+        "kvq_required_bytes": (SZ, [cfgp]),
+        "kvq_get_layout": (I32, [cfgp, ctypes.POINTER(kvq_layout)]),
+        "kvq_workspace_bytes": (SZ, [cfgp]),
+        "kvq_create": (I32, [cfgp, P, SZ, P, ctypes.POINTER(P)]),
+        "kvq_destroy": (I32, [P]),
+        "kvq_select_sinks": (I32, [P, I32, P, I32, P]),
+        "kvq_append": (I32, [P, I32, P, P, I32, P]),
+        "kvq_evict": (I32, [P, I32]),
+        "kvq_decode_attn": (I32, [P, I32, P, P, F32, P, SZ, P]),
+        "kvq_dequant": (I32, [P, I32, I32, I64, I32, P, P]),
+        "kvq_account": (I32, [P, I32, ctypes.POINTER(kvq_bytes), P]),
+        "kvq_get_state": (I32, [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
+        "kvq_format_tables": (I32, [cfgp, P, P, P, P, P, P, P]),
+        "kvq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    return lib
+
+
+lib = _load()
+
+
+def last_error():
+    return lib.kvq_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise KvqError(status, last_error())
+
+
+def make_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, fmt="kivi", k_bits=2, v_bits=2,
+                sink_mode="none", n_sink=0, window=0, residual=0, capacity=0, in_dtype="f16", seed=0):
+    return kvq_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, FMT[fmt], k_bits, v_bits, SINK[sink_mode],
+                      n_sink, window, residual, capacity, IN_DTYPE[in_dtype], seed)
+
+
+def config_check(cfg):
+    return lib.kvq_config_check(ctypes.byref(cfg))
+
+
+def required_bytes(cfg):
+    return lib.kvq_required_bytes(ctypes.byref(cfg))
+
+
+def workspace_bytes(cfg):
+    return lib.kvq_workspace_bytes(ctypes.byref(cfg))
+
+
+def get_layout(cfg):
+    lay = kvq_layout()
+    _check(lib.kvq_get_layout(ctypes.byref(cfg), ctypes.byref(lay)))
+    return lay
+
+
+def format_tables(cfg):
+    """Host tables the library computes: dict of fp32 lists."""
+    d = cfg.head_dim
+    kl, vl = 1 << cfg.k_bits, 1 << cfg.v_bits
+    bufs = {"signs": (ctypes.c_float * d)(), "k_bnd": (ctypes.c_float * (kl - 1))(), "k_cen": (ctypes.c_float * kl)(),
+            "v_bnd": (ctypes.c_float * (vl - 1))(), "v_cen": (ctypes.c_float * vl)(),
+            "q2k_thr": (ctypes.c_float * 3)(), "q2k_lvl": (ctypes.c_float * 4)()}
+    _check(lib.kvq_format_tables(ctypes.byref(cfg), *[ctypes.cast(b, ctypes.c_void_p) for b in bufs.values()]))
+    return {k: list(v) for k, v in bufs.items()}
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class Cache:
+    """A cache bound to a torch-allocated device buffer on the current device."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.layout = get_layout(cfg)
+        nbytes = required_bytes(cfg)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(workspace_bytes(cfg), 16), dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        _check(lib.kvq_create(ctypes.byref(cfg), _ptr(self.buf), nbytes, _stream(), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            lib.kvq_destroy(h)
+            self.handle = None
+
+    # entry points, same names as the C ABI
+    def kvq_select_sinks(self, layer, k):
+        _check(lib.kvq_select_sinks(self.handle, layer, _ptr(k), k.shape[2], _stream()))
+
+    def kvq_append(self, layer, k, v):
+        _check(lib.kvq_append(self.handle, layer, _ptr(k), _ptr(v), k.shape[2], _stream()))
+
+    def kvq_evict(self, layer):
+        _check(lib.kvq_evict(self.handle, layer))
+
+    def kvq_decode_attn(self, layer, q, out, scale=0.0):
+        _check(lib.kvq_decode_attn(self.handle, layer, _ptr(q), _ptr(out), scale, _ptr(self.ws),
+                                   self.ws.numel(), _stream()))
+
+    def kvq_dequant(self, layer, which, pos0, count, out):
+        _check(lib.kvq_dequant(self.handle, layer, which, pos0, count, _ptr(out), _stream()))
+
+    def kvq_account(self, layer):
+        b = kvq_bytes()
+        _check(lib.kvq_account(self.handle, layer, ctypes.byref(b), _stream()))
+        return {n: getattr(b, n) for n, _ in kvq_bytes._fields_}
+
+    def kvq_get_state(self, layer):
+        P, lo = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.kvq_get_state(self.handle, layer, ctypes.byref(P), ctypes.byref(lo)))
+        return P.value, lo.value
+
+    # raw views of the documented storage regions (for tests)
+    def region(self, layer, name, nbytes):
+        off = layer * self.layout.layer_stride + getattr(self.layout, name)
+        return self.buf[off: off + nbytes]

@@ -1,0 +1,161 @@
+"""Test driver: runs the same call sequence through the HIP library and the oracle and compares.
+
+Inputs come from quantized_kv_cache_kivi_amd.synth and are handed to both sides
+as the same buffers (the oracle gets a host copy of exactly what the library
+read).  Nothing here computes any step of the method.
+"""
+
+import numpy as np
+import torch
+
+from oracle import attention as oattn
+from oracle import cache as ocache
+from quantized_kv_cache_kivi_amd import synth
+
+TOL_ATTN = 1e-3  # max over (b, j) of ||o_gpu - o_ref||_inf / ||o_ref||_inf
+
+
+def rel_attn_err(out_gpu, out_ref):
+    o = np.asarray(out_gpu, np.float64)
+    r = np.asarray(out_ref, np.float64)
+    num = np.abs(o - r).max(axis=-1)
+    den = np.abs(r).max(axis=-1)
+    return float((num / den).max())
+
+
+class Pair:
+    def __init__(self, data_seed=1, **kw):
+        from quantized_kv_cache_kivi_amd import kvq
+        self.kvq = kvq
+        self.kw = kw
+        self.ocfg = ocache.Config(**{("fmt" if k == "fmt" else k): v for k, v in kw.items()})
+        self.cfg = kvq.make_config(**kw)
+        self.gpu = kvq.Cache(self.cfg)
+        self.model = ocache.CacheModel(self.ocfg.with_(capacity=self.gpu.layout.capacity))
+        self.seed = data_seed
+        self.step = 0
+        self.tdtype = torch.float32 if kw.get("in_dtype", "f16") == "f32" else torch.float16
+
+    # -- inputs ------------------------------------------------------------------------------
+    def rows(self, n, k_mult=None, planted=None, tag_base=0):
+        c = self.ocfg
+        shape = (c.batch, c.n_kv_heads, n, c.head_dim)
+        t = 100 + 10 * self.step + tag_base
+        k = synth.normal(shape, self.seed, t, "cuda")
+        v = synth.normal(shape, self.seed, t + 1, "cuda")
+        if k_mult is not None:
+            k = k * k_mult[None, :, None, :].to(k)
+        if planted is not None:
+            for b, pos in planted:
+                k[b, :, pos, :] *= 25.0
+        self.step += 1
+        return k.to(self.tdtype).contiguous(), v.to(self.tdtype).contiguous()
+
+    def query(self, tag=7):
+        c = self.ocfg
+        q = synth.normal((c.batch, c.n_q_heads, c.head_dim), self.seed, 90000 + tag, "cuda")
+        return q.to(self.tdtype).contiguous()
+
+    # -- calls on both sides -----------------------------------------------------------------------
+    def select(self, layer, k):
+        self.gpu.kvq_select_sinks(layer, k)
+        self.model.select(layer, k.cpu().numpy())
+
+    def append(self, layer, k, v):
+        self.gpu.kvq_append(layer, k, v)
+        self.model.append(layer, k.cpu().numpy(), v.cpu().numpy())
+
+    def evict(self, layer):
+        self.gpu.kvq_evict(layer)
+        self.model.evict(layer)
+
+    def push(self, layer, n, evict=True, **kw):
+        k, v = self.rows(n, **kw)
+        self.select(layer, k)
+        self.append(layer, k, v)
+        if evict:
+            self.evict(layer)
+        return k, v
+
+    # -- comparisons ----------------------------------------------------------------------------
+    def gpu_regions(self, layer):
+        c, L = self.ocfg, self.gpu.layout
+        S, D = c.batch * c.n_kv_heads, c.head_dim
+        torch.cuda.synchronize()
+        reg = lambda name, n: self.gpu.region(layer, name, n).cpu().numpy()  # noqa: E731
+        out = {"bulk": reg("bulk", S * L.cap_blocks * L.record_bytes).reshape(S, L.cap_blocks, L.record_bytes)}
+        if c.residual:
+            out["win_k"] = reg("win_k", S * c.residual * D * 2).view(np.uint16).reshape(S, c.residual, D)
+            out["win_v"] = reg("win_v", S * c.residual * D * 2).view(np.uint16).reshape(S, c.residual, D)
+        if c.n_sink:
+            out["sink_k"] = reg("sink_k", S * c.n_sink * D * 2).view(np.uint16).reshape(S, c.n_sink, D)
+            out["sink_v"] = reg("sink_v", S * c.n_sink * D * 2).view(np.uint16).reshape(S, c.n_sink, D)
+            out["sink_pos"] = reg("sink_pos", c.batch * c.n_sink * 4).view(np.int32).reshape(c.batch, c.n_sink)
+            out["sink_score"] = reg("sink_score", c.batch * c.n_sink * 4).view(np.float32).reshape(c.batch, c.n_sink)
+            out["sink_count"] = reg("sink_count", c.batch * 4).view(np.int32)
+        if c.fmt != "tq":
+            esz = 4 if c.in_dtype == "f32" else 2
+            st = reg("staging", S * 32 * D * esz)
+            out["staging"] = (st.view(np.float32) if esz == 4 else st.view(np.float16).astype(np.float32)
+                              ).reshape(S, 32, D)
+        return out
+
+    def compare_bytes(self, layer, streams=None):
+        """Bit-exact comparison of every stored region; returns the number of streams checked."""
+        c = self.ocfg
+        g = self.gpu_regions(layer)
+        if c.n_sink:
+            pos, sc, cnt = self.model.sink_state(layer)
+            assert np.array_equal(g["sink_count"], cnt), (g["sink_count"], cnt)
+            assert np.array_equal(g["sink_pos"], pos), (g["sink_pos"], pos)
+            assert np.array_equal(g["sink_score"].view(np.uint32), sc.view(np.uint32))
+        streams = range(c.batch * c.n_kv_heads) if streams is None else streams
+        for s in streams:
+            b, h = divmod(s, c.n_kv_heads)
+            img = self.model.image(layer, b, h)
+            bad = np.flatnonzero((g["bulk"][s] != img["bulk"]).any(axis=1))
+            assert bad.size == 0, f"stream {s}: bulk slots differ: {bad[:8]}"
+            for key in ("win_k", "win_v", "sink_k", "sink_v"):
+                if key in g:
+                    assert np.array_equal(g[key][s], img[key]), f"stream {s}: {key} differs"
+            if "staging" in g:
+                n = img["staging"].shape[0]
+                assert np.array_equal(g["staging"][s, :n], img["staging"]), f"stream {s}: staging differs"
+        return len(streams)
+
+    def compare_dequant(self, layer, which, pos0=None, count=None, batches=None):
+        P, lo = self.model.P[layer], self.model.lo[layer]
+        pos0 = lo if pos0 is None else pos0
+        count = P - pos0 if count is None else count
+        c = self.ocfg
+        out = torch.empty((c.batch, c.n_kv_heads, count, c.head_dim), dtype=torch.int16, device="cuda")
+        self.gpu.kvq_dequant(layer, which, pos0, count, out)
+        got = out.cpu().numpy().view(np.uint16)
+        worst = 0
+        for b in (range(c.batch) if batches is None else batches):
+            for h in range(c.n_kv_heads):
+                ref = oattn.dequant16(self.model, layer, b, h, "k" if which == 0 else "v",
+                                      list(range(pos0, pos0 + count)))
+                d = np.abs(got[b, h].astype(np.int32) - ref.astype(np.int32))
+                # adjacent fp16 bit patterns of the same sign differ by 1 ulp
+                same_sign = (got[b, h] >> 15) == (ref >> 15)
+                d = np.where(same_sign, d, np.where((got[b, h] & 0x7FFF) + (ref & 0x7FFF) == 0, 0, 99))
+                worst = max(worst, int(d.max()))
+        return worst
+
+    def attention(self, layer, q=None, scale=0.0):
+        c = self.ocfg
+        q = self.query() if q is None else q
+        out = torch.empty((c.batch, c.n_q_heads, c.head_dim), dtype=torch.float32, device="cuda")
+        self.gpu.kvq_decode_attn(layer, q, out, scale)
+        torch.cuda.synchronize()
+        return q, out
+
+    def compare_attention(self, layer, q=None, scale=0.0, batches=None, heads=None):
+        q, out = self.attention(layer, q, scale)
+        ref = oattn.decode_attention(self.model, layer, q.cpu().numpy(), scale or None, batches=batches, heads=heads)
+        got = out.cpu().numpy()
+        bsel = list(range(self.ocfg.batch)) if batches is None else list(batches)
+        hsel = list(range(self.ocfg.n_q_heads)) if heads is None else list(heads)
+        got = got[np.ix_(bsel, hsel)]
+        return rel_attn_err(got, ref), out

@@ -1,0 +1,128 @@
+"""GPU parity: the HIP library against the oracle on seeded inputs, element by element.
+
+Bar: stored bytes (codes, packed words, metadata, fp16 overlay, sink
+positions and scores) bit-exact; dequantized fp16 within 1 ulp; decode
+attention max over (b, j) of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3.
+Sizes span several 32-token blocks, ragged tails, ring wrap-around and the
+open-block re-quantization.
+"""
+import numpy as np
+import pytest
+import torch
+
+from harness import TOL_ATTN, Pair
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "kivi2_topk_res16": dict(n_layers=2, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="kivi", k_bits=2,
+                             v_bits=2, sink_mode="topk", n_sink=3, residual=16, capacity=512),
+    "kivi8_f32_firstn_ring": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="kivi",
+                                  k_bits=8, v_bits=8, sink_mode="first_n", n_sink=4, window=64, in_dtype="f32"),
+    "kivi4_firstn_win_res": dict(n_layers=1, batch=3, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="kivi", k_bits=4,
+                                 v_bits=4, sink_mode="first_n", n_sink=4, window=96, residual=8),
+    "kivi24_nosink": dict(n_layers=1, batch=2, n_kv_heads=1, n_q_heads=16, head_dim=128, fmt="kivi", k_bits=2,
+                          v_bits=4, residual=0, capacity=384),
+    "q2k_firstn_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="q2k", k_bits=2,
+                           v_bits=4, sink_mode="first_n", n_sink=4, residual=24, capacity=512),
+    "tq42": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=4, v_bits=2,
+                 capacity=512, seed=0x5EED0004),
+    "tq24_topk_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=2,
+                          v_bits=4, sink_mode="topk", n_sink=2, window=128, residual=8, seed=77),
+}
+
+SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_sequence(name):
+    kw = CASES[name]
+    pair = Pair(data_seed=hash(name) % 1000, **kw)
+    rng = np.random.default_rng(5)
+    layers = range(kw["n_layers"])
+    D = kw["head_dim"]
+    worst_attn = 0.0
+    sched = SCHEDULE if not kw.get("window") else SCHEDULE + [32, 5, 27, 1, 30, 2, 31, 1, 32, 32, 7]
+    for step, n in enumerate(sched):
+        if kw.get("window"):
+            # a windowed ring admits an append only up to the slot of the oldest live block
+            cap_b, P, lo = pair.gpu.layout.cap_blocks, pair.model.P[0], pair.model.lo[0]
+            n = max(1, min(n, 32 * (cap_b + lo // 32) - P))
+        for layer in layers:
+            mult = None
+            if kw["fmt"] != "tq":
+                mult = torch.from_numpy(6.0 ** rng.random((kw["n_kv_heads"], D))).cuda()
+            planted = None
+            if kw.get("sink_mode") == "topk" and step == 0:
+                planted = [(b, [int(x) for x in rng.choice(n, 2, replace=False)]) for b in range(kw["batch"])]
+            _log(f"[{name}] step {step} layer {layer} append n={n}")
+            pair.push(layer, n, k_mult=mult, planted=planted)
+            pair.compare_bytes(layer)
+            err, _ = pair.compare_attention(layer)
+            worst_attn = max(worst_attn, err)
+            assert err <= TOL_ATTN, f"attention rel err {err:.3e} at step {step}"
+    for layer in layers:
+        for which in (0, 1):
+            ulp = pair.compare_dequant(layer, which)
+            assert ulp <= 1, f"dequant differs by {ulp} ulp"
+    _log(f"[{name}] worst attention rel err {worst_attn:.3e}")
+
+
+def test_attention_deterministic_and_scale():
+    kw = CASES["kivi2_topk_res16"]
+    pair = Pair(data_seed=3, **kw)
+    pair.push(0, 300)
+    q = pair.query()
+    _, o1 = pair.attention(0, q)
+    _, o2 = pair.attention(0, q)
+    assert torch.equal(o1, o2)
+    err, _ = pair.compare_attention(0, q, scale=0.05)
+    assert err <= TOL_ATTN
+
+
+def test_error_paths_are_host_checked():
+    from quantized_kv_cache_kivi_amd import kvq
+    kw = CASES["kivi2_topk_res16"]
+    pair = Pair(data_seed=4, **kw)
+    k, v = pair.rows(10)
+    with pytest.raises(kvq.KvqError) as e:
+        pair.gpu.kvq_append(0, k, v)  # TOPK append without select
+    assert e.value.status == -4
+    pair.select(0, k)
+    with pytest.raises(kvq.KvqError) as e:
+        pair.gpu.kvq_append(0, k[:, :, :5].contiguous(), v[:, :, :5].contiguous())  # different chunk
+    assert e.value.status == -4
+    pair.append(0, k, v)
+    out = torch.empty((2, 2, 4, 128), dtype=torch.int16, device="cuda")
+    with pytest.raises(kvq.KvqError) as e:
+        pair.gpu.kvq_dequant(0, 0, 8, 4, out)  # past P
+    assert e.value.status == -2
+    ring = Pair(data_seed=4, **CASES["kivi8_f32_firstn_ring"])
+    with pytest.raises(kvq.KvqError) as e:
+        for _ in range(12):
+            ring.push(0, 16, evict=False)  # never evicting fills the ring
+    assert e.value.status == -3
+    empty = Pair(data_seed=4, **CASES["tq42"])
+    with pytest.raises(kvq.KvqError) as e:
+        empty.attention(0)
+    assert e.value.status == -2
+
+
+def test_account_matches_oracle():
+    from oracle import accounting
+    kw = CASES["kivi4_firstn_win_res"]
+    pair = Pair(data_seed=6, **kw)
+    for n in (50, 1, 77, 3):
+        pair.push(0, n)
+    got = pair.gpu.kvq_account(0)
+    ref = {k: 0 for k in got}
+    for b in range(kw["batch"]):
+        a = accounting.account(pair.model, 0, b)
+        for k in ref:
+            ref[k] += a[k] if k != "current_length" else 0
+    ref["current_length"] = pair.model.P[0]
+    assert got == ref
