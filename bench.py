@@ -1,0 +1,342 @@
+"""Benchmark of the quantized KV cache decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+
+A step is one pass of the hot path for one decode token of one layer:
+kvq_select_sinks -> kvq_append (1 row) -> kvq_evict -> kvq_decode_attn, on
+seeded synthetic inputs already resident in HBM.  The default workload is the
+KIVI 2-bit cache with dynamic sinks: 1 layer, batch 8, 8 KV heads, 32 query
+heads, head_dim 128, fp16 K/V with channel outliers (RMS spread up to 6x) and
+5 planted 25x sink rows per batch element, a 4096-token prefill, 5 top-k key-
+norm sinks, an fp16 window of 32, int2 K and V in 32-token groups.
+
+Cold cache: the cache is replicated enough times to exceed the 256 MB
+Infinity Cache, and consecutive steps use different replicas, so each
+decode-attention call streams its cache from HBM.  A warm-cache figure (one
+replica) is reported separately.
+
+value = algorithmic decode-attention bytes per step / wall time per step
+(whole step: select + append + evict + attention).  The roofline object is the
+decode-attention kernel alone: the same algorithmic bytes / its average
+duration from HIP events on its stream.  Algorithmic bytes = packed codes and
+metadata of the valid quantized tokens + fp16 sink and window rows + q + out.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode-attn HBM GB/s (% of peak) + context tokens/s over quantized KV cache"
+HBM_PEAK_GBPS = 8000.0
+
+CONFIGS = {
+    1: dict(name="tiny-streaming-int8", kw=dict(n_layers=12, batch=1, n_kv_heads=8, n_q_heads=8, head_dim=32,
+                                                fmt="kivi", k_bits=8, v_bits=8, sink_mode="first_n", n_sink=4,
+                                                window=256, residual=0, in_dtype="f32"),
+            prefill=0, desc="12 layers, batch 1, 8 heads, d=32, fp32 K/V, int8 K/V, sink 4, window 256, "
+                            "decode from empty"),
+    2: dict(name="kivi2-dynamic-sinks", kw=dict(n_layers=1, batch=8, n_kv_heads=8, n_q_heads=32, head_dim=128,
+                                                fmt="kivi", k_bits=2, v_bits=2, sink_mode="topk", n_sink=5,
+                                                residual=32),
+            prefill=4096, desc="1 layer, batch 8, 8 KV / 32 q heads, d=128, fp16 K/V, int2 K/V group 32, "
+                               "5 top-k key-norm sinks (planted 25x), fp16 window 32, T=4096 prefill"),
+    3: dict(name="q2k", kw=dict(n_layers=1, batch=16, n_kv_heads=8, n_q_heads=32, head_dim=128, fmt="q2k",
+                                k_bits=2, v_bits=4, sink_mode="first_n", n_sink=4, residual=128),
+            prefill=32768, desc="1 layer, batch 16, 8 KV / 32 q heads, d=128, fp16 K/V, K 2-bit Lloyd-Max over "
+                                "block RMS (channel spread log-U[5.8, 74.9]), V 4-bit, 4 sinks, fp16 window 128, "
+                                "T=32768"),
+    4: dict(name="turboquant-k4v2", kw=dict(n_layers=1, batch=8, n_kv_heads=8, n_q_heads=32, head_dim=128,
+                                            fmt="tq", k_bits=4, v_bits=2, seed=0x5EED0004),
+            prefill=16384, desc="1 layer, batch 8, 8 KV / 32 q heads, d=128, fp16 AR(1) rho=0.8 K/V, "
+                                "TurboQuant K4/V2, T=16384"),
+    5: dict(name="long-streaming-int4", kw=dict(n_layers=1, batch=64, n_kv_heads=8, n_q_heads=32, head_dim=128,
+                                                fmt="kivi", k_bits=4, v_bits=4, sink_mode="first_n", n_sink=4,
+                                                window=65536, residual=128),
+            prefill=65540, desc="1 layer, batch 64, 8 KV / 32 q heads, d=128, fp16 K/V, int4 K/V, sink 4, "
+                                "window 65536, fp16 window 128, full 65540-token cache"),
+}
+SEEDS = {1: 0x5EED0001, 2: 0x5EED0002, 3: 0x5EED0003, 4: 0x5EED0004, 5: 0x5EED0005}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_rows(cfgno, kw, n, seed, tag, device, kmult=None, planted=None):
+    import torch
+    from quantized_kv_cache_kivi_amd import synth
+    B, H, D = kw["batch"], kw["n_kv_heads"], kw["head_dim"]
+    shape = (B, H, n, D)
+    if cfgno == 4:
+        k = synth.ar1(shape, 0.8, seed, tag, device)
+        v = synth.ar1(shape, 0.8, seed, tag + 1, device)
+    else:
+        k = synth.normal(shape, seed, tag, device)
+        v = synth.normal(shape, seed, tag + 1, device)
+    if kmult is not None:
+        k = k * kmult[None, :, None, :]
+    if planted is not None:
+        for b, pos in enumerate(planted):
+            k[b, :, pos, :] *= 25.0
+    dt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
+    return k.to(dt).contiguous(), v.to(dt).contiguous()
+
+
+def key_multipliers(cfgno, kw, seed, device):
+    from quantized_kv_cache_kivi_amd import synth
+    H, D = kw["n_kv_heads"], kw["head_dim"]
+    if cfgno in (2, 5):
+        return synth.channel_multipliers(H, D, 6.0, seed, 7, device)
+    if cfgno == 3:
+        return synth.q2k_multipliers(H, D, seed, 7, device)
+    return None
+
+
+def algorithmic_bytes(kw, P, lo, sinks_per_b):
+    """Bytes one decode-attention call must move (valid tokens only)."""
+    D, H, Hq, B = kw["head_dim"], kw["n_kv_heads"], kw["n_q_heads"], kw["batch"]
+    R = kw.get("residual", 0)
+    fmt, kb, vb = kw.get("fmt", "kivi"), kw.get("k_bits", 2), kw.get("v_bits", 2)
+    if fmt == "kivi":
+        kmeta_blk, vmeta_tok = 4 * D, 4 * (D // 32)
+    elif fmt == "q2k":
+        kmeta_blk, vmeta_tok = 2 * D, 2 * (D // 32)
+    else:
+        kmeta_blk, vmeta_tok = 0, 8
+    wlo = max(lo, P - R)
+    total = 0
+    n_ctx = 0
+    for b in range(B):
+        C = {p for p in sinks_per_b[b] if 0 <= p < P}
+        c_bulk = sorted(p for p in C if lo <= p < wlo)
+        n_fp = len(C) + (P - wlo) - sum(1 for p in C if p >= wlo)
+        n_bulk = (wlo - lo) - len(c_bulk)
+        nblk = (wlo - 1) // 32 - lo // 32 + 1 if wlo > lo else 0
+        for blk in {p // 32 for p in c_bulk}:  # a block whose bulk rows are all sinks holds no compressed row
+            a, z = max(lo, 32 * blk), min(wlo, 32 * blk + 32)
+            if (z - a) == sum(1 for p in c_bulk if a <= p < z):
+                nblk -= 1
+        total += H * (n_bulk * (D * (kb + vb) // 8 + vmeta_tok) + nblk * kmeta_blk + n_fp * 2 * D * 2)
+        n_ctx += (P - lo) + sum(1 for p in C if p < lo)
+    esz = 4 if kw.get("in_dtype") == "f32" else 2
+    total += B * Hq * D * esz + B * Hq * D * 4
+    return total, n_ctx
+
+
+def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, budget_s=20.0):
+    """The oracle as it stands, timed on the host on a bounded sample of the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as oattn
+    from oracle import cache as ocache
+    sub = dict(kw)
+    nb = 1  # one batch element (all its KV and query heads) of the workload
+    sub["batch"] = nb
+    ocfg = ocache.Config(**{**sub, "capacity": sub.get("capacity", 0)})
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        m = ocache.CacheModel(ocfg.with_(capacity=ocache.default_capacity(kw.get("window", 0),
+                                                                           prefill_k.shape[2] + 64)),
+                              reserve=prefill_k.shape[2] + 64)
+        k0 = prefill_k[:nb].cpu().numpy()
+        v0 = prefill_v[:nb].cpu().numpy()
+        m.select(0, k0)
+        m.append(0, k0, v0)
+        m.evict(0)
+        t_prefill = time.perf_counter() - t0
+        calls, t_attn, nbytes = 0, 0.0, 0
+        for (k, v), qq in zip(steps_kv, q):
+            kk, vv = k[:nb].cpu().numpy(), v[:nb].cpu().numpy()
+            m.select(0, kk)
+            m.append(0, kk, vv)
+            m.evict(0)
+            t1 = time.perf_counter()
+            oattn.decode_attention(m, 0, qq[:nb].cpu().numpy())
+            t_attn += time.perf_counter() - t1
+            calls += 1
+            sinks = [[p for p, _ in m.sink_list(0, 0)]]
+            nbytes += algorithmic_bytes(sub, m.P[0], m.lo[0], sinks)[0]
+            if time.perf_counter() - t0 > budget_s:
+                break
+    return {"value": nbytes / t_attn / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch element 0 of the workload ({kw['n_kv_heads']} KV heads, {kw['n_q_heads']} query "
+                      f"heads): prefill of {prefill_k.shape[2]} rows ({t_prefill:.1f} s), then {calls} decode "
+                      f"steps; value = algorithmic decode-attention bytes of that batch element / oracle "
+                      f"decode-attention time (fp64, numpy, 1 BLAS thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough to exceed 1 GB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (every stream of the cache is "
+              "independent; sharding batch or KV heads across GPUs needs no exchange). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from quantized_kv_cache_kivi_amd import kvq, synth
+
+    dev = "cuda"
+    C = CONFIGS[args.config]
+    kw = dict(C["kw"])
+    seed = SEEDS[args.config]
+    T0 = C["prefill"]
+    total_steps = args.steps + args.warmup
+    # capacity: prefill + every step's row on one replica, rounded to blocks (windowed configs use the default ring)
+    if kw.get("window", 0) == 0:
+        kw["capacity"] = 32 * math.ceil((T0 + total_steps + 32) / 32)
+    cfg = kvq.make_config(**kw)
+    per_rep = kvq.required_bytes(cfg)
+    L = kw["n_layers"]
+    if args.replicas:
+        nrep = args.replicas
+    else:
+        call_bytes_guess = max(per_rep // L, 1)
+        nrep = max(1, min(64, math.ceil(1.0e9 / call_bytes_guess)))
+        nrep = min(nrep, max(1, int(200e9 // per_rep)))
+    log(f"[bench] config {args.config} ({C['name']}): {nrep} replicas x {per_rep / 1e6:.1f} MB")
+
+    kmult = key_multipliers(args.config, kw, seed, dev)
+    planted = None
+    if kw.get("sink_mode") == "topk":
+        planted = synth.planted_positions(kw["batch"], kw["n_sink"], T0, seed, 11)
+    reps = []
+    pre_k = pre_v = None
+    if T0 > 0:
+        pre_k, pre_v = make_rows(args.config, kw, T0, seed, 100, dev, kmult, planted)
+    for r in range(nrep):
+        c = kvq.Cache(cfg)
+        for layer in range(L):
+            if T0 > 0:
+                chunk = 4096
+                for s0 in range(0, T0, chunk):
+                    k = pre_k[:, :, s0:s0 + chunk].contiguous()
+                    v = pre_v[:, :, s0:s0 + chunk].contiguous()
+                    c.kvq_select_sinks(layer, k)
+                    c.kvq_append(layer, k, v)
+                    c.kvq_evict(layer)
+        reps.append(c)
+    torch.cuda.synchronize()
+    sinks_per_b = [[] for _ in range(kw["batch"])]
+    if kw.get("n_sink", 0) > 0:
+        n = kw["batch"] * kw["n_sink"]
+        pos = reps[0].region(0, "sink_pos", n * 4).cpu().view(torch.int32).reshape(kw["batch"], kw["n_sink"])
+        sinks_per_b = [[int(p) for p in row if p >= 0] for row in pos.tolist()]
+    log(f"[bench] prefill done; sinks of b=0: {sinks_per_b[0]}")
+
+    # per-step inputs, resident on the GPU before timing
+    step_kv = [make_rows(args.config, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(total_steps)]
+    dt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
+    qs = [synth.normal((kw["batch"], kw["n_q_heads"], kw["head_dim"]), seed, 50_000 + i, dev).to(dt).contiguous()
+          for i in range(total_steps)]
+    out = torch.empty((kw["batch"], kw["n_q_heads"], kw["head_dim"]), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        c = reps[i % nrep]
+        k, v = step_kv[i]
+        for layer in range(L):
+            c.kvq_select_sinks(layer, k)
+            c.kvq_append(layer, k, v)
+            c.kvq_evict(layer)
+            if ev is not None:
+                ev[0].record(stream)
+            c.kvq_decode_attn(layer, qs[i], out)
+            if ev is not None:
+                ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    nbytes, nctx = 0, 0
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(args.warmup + j, evs[j])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    # exact (P, lo) each timed call saw: prefill, plus one row per earlier step on the same replica
+    rows_on = [0] * nrep
+    for i in range(args.warmup):
+        rows_on[i % nrep] += 1
+    W = kw.get("window", 0)
+    for j in range(args.steps):
+        r = (args.warmup + j) % nrep
+        rows_on[r] += 1
+        P = T0 + rows_on[r]
+        lo = max(0, P - W) if W > 0 else 0
+        b_, n_ = algorithmic_bytes(kw, P, lo, sinks_per_b)
+        nbytes += b_ * L
+        nctx += n_ * L
+    kern_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps  # per step (all layers)
+    ms_step = elapsed * 1e3 / args.steps
+    bytes_per_step = nbytes / args.steps
+    calls_per_step = L
+    achieved = bytes_per_step / calls_per_step / (kern_ms / calls_per_step * 1e-3) / 1e9
+
+    # warm cache: one replica, decode-attention only
+    warm = None
+    if nrep > 1:
+        wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(50)]
+        for i in range(50):
+            wev[i][0].record(stream)
+            reps[0].kvq_decode_attn(0, qs[0], out)
+            wev[i][1].record(stream)
+        torch.cuda.synchronize()
+        wms = sum(a.elapsed_time(b) for a, b in wev[10:]) / 40
+        P, lo = reps[0].kvq_get_state(0)
+        wb, _ = algorithmic_bytes(kw, P, lo, sinks_per_b)
+        warm = {"decode_attn_us": wms * 1e3, "GBps": wb / (wms * 1e-3) / 1e9,
+                "note": "same cache re-read back to back (served partly from the Infinity Cache)"}
+
+    res = {
+        "metric": METRIC,
+        "value": bytes_per_step / (ms_step * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{C['name']}: {C['desc']}", "steps_are": "select_sinks + append(1 row) + evict + "
+                   "decode_attn per layer", "cache_replicas": nrep, "parallelism": "1 GPU"},
+        "context_tokens_per_s": nctx / args.steps / (ms_step * 1e-3),
+        "decode_attn": {"us_per_call": kern_ms * 1e3 / calls_per_step, "GBps": achieved,
+                        "context_tokens_per_s": nctx / args.steps / (kern_ms * 1e-3),
+                        "bytes_per_call": bytes_per_step / calls_per_step},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+        "warm_cache": warm,
+    }
+    if not args.no_cpu_baseline:
+        try:
+            n_cpu = min(args.steps, 16)
+            res["cpu_baseline"] = cpu_baseline(args.config, kw, pre_k if pre_k is not None else
+                                               step_kv[0][0][:, :, :0], pre_v if pre_v is not None else
+                                               step_kv[0][1][:, :, :0], step_kv[:n_cpu], qs[:n_cpu],
+                                               kw.get("sink_mode") == "topk")
+        except Exception as e:  # the baseline is a report, never a reason to lose the GPU line
+            res["cpu_baseline"] = {"value": None, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                   "sample": f"failed: {e!r}"}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
