@@ -117,7 +117,6 @@ typedef struct { /* byte offsets inside the caller's device buffer */
   uint64_t win_k, win_v;          /* [batch][n_kv_heads][residual][head_dim] fp16 */
   uint64_t sink_k, sink_v;        /* [batch][n_kv_heads][n_sink][head_dim] fp16 */
   uint64_t sink_pos, sink_score, sink_count; /* [batch][n_sink] int32, fp32; [batch] int32 */
-  uint64_t counters;              /* [batch][n_kv_heads] int32, self-resetting split counters */
   uint64_t tables;                /* once, not per layer: fp32 tables (TQ signs and codebooks, Q2K grid) */
   uint64_t total;                 /* = kvq_required_bytes */
   int32_t cap_blocks;
@@ -174,8 +173,9 @@ kvq_status kvq_evict(kvq_cache* c, int32_t layer);
  * from the packed bulk ([SK] "Affine quantisation formula"; [TQ]
  * "Optimization: Fused dequant-dot": TQ scores and values are accumulated in
  * the rotated domain and the output is rotated back once).  scale <= 0 means
- * 1/sqrt(head_dim).  ws: >= kvq_workspace_bytes device bytes.  One kernel
- * launch; results are deterministic (fixed-order split merge). */
+ * 1/sqrt(head_dim).  ws: >= kvq_workspace_bytes device bytes (split partials).
+ * Two kernel launches (split-K partials, then a fixed-order merge per stream);
+ * results are deterministic. */
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
                            size_t ws_bytes, void* stream);
 

@@ -1,4 +1,4 @@
-// Single-query decode attention over the packed cache (one launch per call).
+// Single-query decode attention over the packed cache.
 //
 // out[b][j] = sum_p softmax_p(scale * q[b][j] . k_p) v_p over the valid set of
 // the layer: committed sinks (fp16 sink pool), the fp16 window and the
@@ -10,334 +10,192 @@
 // back once ("TurboQuant KV Cache Compression — Spec", "Optimization: Fused
 // dequant-dot").
 //
-// Grid: (splits + 1, batch * n_kv_heads).  Workgroup sigma < splits scans a
-// contiguous range of bulk blocks; workgroup `splits` scans the fp16 rows.
-// Each writes an online-softmax partial (m, l, acc) for the r query heads of
-// its KV head; the last one to finish (a per-stream arrival counter that it
-// resets) merges all partials in fixed order, so results do not depend on
-// scheduling.
-#include "device_common.h"
+// Two launches.  The split kernel (grid (splits, batch * n_kv_heads); the
+// MFMA kernel of decode_fast.hip or the generic one here) writes one
+// online-softmax partial (m, l, acc) per (bulk split, stream) for the r query
+// heads of the stream.  The merge kernel (grid (batch * n_kv_heads, r)) scores
+// the fp16 rows (window minus sinks, then sinks) of its head itself and merges
+// them with the bulk partials in fixed order, so results do not depend on
+// scheduling.  TurboQuant keeps a per-stream merge: its bulk partials live in
+// the rotated domain, and its fp16 rows are one more generic partial (index
+// splits).
+#include "decode_shared.h"
 
 namespace kvq {
 namespace {
 
-constexpr int NT = 256;
-constexpr int MAX_REC = 2 * G * MAX_D + 4 * MAX_D + 4 * G * 4;  // 8-bit K and V, KIVI metadata
-
-struct Smem {
-  float q[MAX_GQA][MAX_D];      // query (rotated for TurboQuant bulk)
-  float sc[MAX_GQA][G];         // scores, then weights, of the current 32 rows
-  float fac[MAX_GQA];           // rescale factors of the current step
-  float m[MAX_GQA], l[MAX_GQA]; // running max and denominator
-  float red[NT][MAX_GQA];  // cross-slice reduction scratch (acc)
-  int sinks[MAX_SINK];
-  int nsinks;
-  int last;
-  alignas(16) uint8_t rec[MAX_REC];
-  uint16_t rows_k[G][MAX_D];    // fp16 rows of the current chunk (fp16 split)
-  uint16_t rows_v[G][MAX_D];
-};
-
-__device__ __forceinline__ uint32_t code_at(const uint8_t* sec, int word, int k, int b) {
-  return (reinterpret_cast<const uint32_t*>(sec)[word] >> code_shift(k, b)) & ((1u << b) - 1u);
+__global__ __launch_bounds__(DNT) void k_decode(DecodeArgs a) {
+  __shared__ Smem S;
+  generic_partial(a, S);
 }
 
-// Dequantized K value of (t, c) of the staged record; TurboQuant values are rotated-domain centroids
-// (the per-token norm is applied to the score).
-__device__ __forceinline__ float k_val(const Shape& sh, const uint8_t* rec, const LayerView& lv, int t, int c) {
-  int w, k;
-  k_code_pos(t, c, sh.D, sh.kb, &w, &k);
-  const uint32_t u = code_at(rec + lv.k_codes, w, k, sh.kb);
-  const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + lv.k_meta);
-  if (sh.fmt == KVQ_FMT_KIVI) return (float)u * f16_val(km[c]) + f16_val(km[sh.D + c]);
-  if (sh.fmt == KVQ_FMT_Q2K) return lv.tables->q2k_lvl[u] * f16_val(km[c]);
-  return lv.tables->k_cen[u];
-}
-__device__ __forceinline__ float v_val(const Shape& sh, const uint8_t* rec, const LayerView& lv, int t, int c) {
-  int w, k;
-  v_code_pos(t, c, sh.D, sh.vb, &w, &k);
-  const uint32_t u = code_at(rec + lv.v_codes, w, k, sh.vb);
-  const uint16_t* vm = reinterpret_cast<const uint16_t*>(rec + lv.v_meta);
-  const int ng = sh.D / 32, g = c >> 5;
-  if (sh.fmt == KVQ_FMT_KIVI) return (float)u * f16_val(vm[t * ng + g]) + f16_val(vm[G * ng + t * ng + g]);
-  if (sh.fmt == KVQ_FMT_Q2K) return ((float)u - 8.f) * f16_val(vm[t * ng + g]);
-  return lv.tables->v_cen[u];
+__global__ __launch_bounds__(DNT) void k_decode_merge(DecodeArgs a) {
+  __shared__ Smem S;
+  merge_partials(a, S);
 }
 
-__global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
+constexpr int MNT = 256;  // threads of a merge workgroup
+constexpr int MCH = 256;  // fp16 rows per chunk of the merge kernel
+
+// Address (in fp16 elements) of fp16 row i of stream s: window rows [bulk_hi, P) first, then
+// the committed sinks in slot order.
+__device__ __forceinline__ int64_t fp16_row(const DecodeArgs& a, int s, int64_t i, int64_t nwin, const int* slot,
+                                            bool* is_sink) {
+  const int D = a.sh.D;
+  if (i < nwin) {
+    *is_sink = false;
+    const int64_t p = a.bulk_hi + i;
+    return ((int64_t)s * a.sh.R + p % a.sh.R) * D;
+  }
+  *is_sink = true;
+  return ((int64_t)s * a.sh.n_sink + slot[i - nwin]) * D;
+}
+
+// Merge for formats without a rotation: one workgroup per (stream, query head).  The fp16 rows
+// are scored (one row per D/8 lanes, 8 channels a lane), turned into weights chunk by chunk with
+// an online max, and accumulated (two channels a lane, rows strided over the row slices); the
+// bulk partials of the head are then folded in, in split order.
+__global__ __launch_bounds__(MNT) void k_merge_heads(DecodeArgs a) {
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
-  const int D = sh.D, r = sh.Hq / sh.Hkv, tid = threadIdx.x, lane = tid & 63;
-  const int sigma = blockIdx.x, s = blockIdx.y, b = s / sh.Hkv, g = s % sh.Hkv;
-  const bool fp16_split = sigma == a.splits;
-  const bool tq = sh.fmt == KVQ_FMT_TQ;
-  __shared__ Smem S;
+  const int s = blockIdx.x, j = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int D = sh.D, r = sh.Hq / sh.Hkv, b = s / sh.Hkv, g = s % sh.Hkv;
+  __shared__ float sc[MCH];
+  __shared__ float red[2 * MNT];
+  __shared__ float wq[65];
+  __shared__ int sinks[MAX_SINK], slots[MAX_SINK], nsinks;
+  __shared__ float Ls, Wf;
 
-  // query rows of the r heads; sinks of this batch element
-  for (int idx = tid; idx < r * D; idx += NT) {
-    const int j = idx / D, c = idx % D;
-    S.q[j][c] = ld_in(a.q, ((int64_t)b * sh.Hq + g * r + j) * D + c, sh.in_f32);
-  }
-  if (tid == 0) {
-    int n = 0;
-    if (sh.n_sink > 0) {
-      const int cnt = lv.sink_count[b];
-      for (int i = 0; i < cnt; ++i) {
-        const int p = lv.sink_pos[b * sh.n_sink + i];
-        if (p >= 0 && p < a.P) S.sinks[n++] = p;
-      }
-    }
-    S.nsinks = n;
-  }
-  if (tid < MAX_GQA) {
-    S.m[tid] = -INFINITY;
-    S.l[tid] = 0.f;
-  }
+  stage_sinks(a, b, sinks, slots, &nsinks);
   __syncthreads();
-  if (tq && !fp16_split) {  // rotate the query: q~ = c_d * FWHT(sigma * q)
-    const float cd = (float)(1.0 / __builtin_sqrt((double)D));
-    for (int j = tid >> 6; j < r; j += NT / 64) {
-      const bool act = 2 * lane < D;
-      float y0 = act ? S.q[j][2 * lane] * lv.tables->signs[2 * lane] : 0.f;
-      float y1 = act ? S.q[j][2 * lane + 1] * lv.tables->signs[2 * lane + 1] : 0.f;
-      wave_fwht(y0, y1, D, lane);
-      if (act) {
-        S.q[j][2 * lane] = y0 * cd;
-        S.q[j][2 * lane + 1] = y1 * cd;
-      }
-    }
-    __syncthreads();
-  }
+  const int64_t nwin = a.P - a.bulk_hi;
+  const int64_t n_fp = nwin + nsinks;
 
-  // score mapping: 32 rows x 8 channel slices; value mapping: D channels x (NT/D) row slices
-  const int st = tid >> 3, sl = tid & 7, cps = D / 8;
-  const int vc = tid % D, vs = tid / D, nvs = NT / D, rps = G / nvs;
-  float acc[MAX_GQA];
-  for (int j = 0; j < MAX_GQA; ++j) acc[j] = 0.f;
+  // query slice of this lane for the score mapping, in log2 units
+  const int lpr = D / 8, rpw = 64 / lpr, part = lane % lpr, rsub = lane / lpr;
+  const float mult = a.scale * LOG2E;
+  const int64_t qoff = ((int64_t)b * sh.Hq + (int64_t)g * r + j) * D + 8 * part;
+  float qv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) qv[k] = ld_in(a.q, qoff + k, sh.in_f32) * mult;
+  // value mapping: channel pair cp, row slice vsl
+  const int ncp = D / 2, cp = tid % ncp, vsl = tid / ncp, nvsl = MNT / ncp;
 
-  int nchunks;
-  int64_t fp_lo = 0, n_fp = 0;
-  if (fp16_split) {
-    fp_lo = a.bulk_hi;  // window rows [bulk_hi, P) minus sinks, then the sinks
-    n_fp = (a.P - fp_lo) + S.nsinks;
-    nchunks = (int)((n_fp + G - 1) / G);
-  } else {
-    const int first = sigma * a.blocks_per_split;
-    const int lastb = min(a.nblk, first + a.blocks_per_split);
-    nchunks = lastb - first;
-  }
-
-  for (int ch = 0; ch < nchunks; ++ch) {
-    int64_t blk = 0;
-    // stage the chunk
-    if (fp16_split) {
-      for (int idx = tid; idx < G * D; idx += NT) {
-        const int t = idx / D, c = idx % D;
-        const int64_t i = (int64_t)ch * G + t;
-        uint16_t kx = 0, vx = 0;
-        if (i < a.P - fp_lo) {
-          const int64_t p = fp_lo + i;
-          const int64_t wo = ((int64_t)s * sh.R + p % sh.R) * D + c;
-          kx = lv.win_k[wo];
-          vx = lv.win_v[wo];
-        } else if (i < n_fp) {
-          const int si = (int)(i - (a.P - fp_lo));
-          // sink pool slot of the si-th committed sink
-          int slot = -1, seen = 0;
-          const int cnt = sh.n_sink > 0 ? lv.sink_count[b] : 0;
-          for (int q = 0; q < cnt; ++q) {
-            const int p = lv.sink_pos[b * sh.n_sink + q];
-            if (p >= 0 && p < a.P) {
-              if (seen == si) slot = q;
-              ++seen;
-            }
-          }
-          if (slot >= 0) {
-            const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + c;
-            kx = lv.sink_k[so];
-            vx = lv.sink_v[so];
-          }
+  float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
+  for (int64_t c0 = 0; c0 < n_fp; c0 += MCH) {
+    const int n = (int)min((int64_t)MCH, n_fp - c0);
+    // scores of rows [c0, c0 + n)
+    for (int base = wv * rpw; base < n; base += (MNT / 64) * rpw) {
+      const int i = base + rsub;
+      float d = 0.f;
+      bool ok = i < n, snk = false;
+      if (ok) {
+        const int64_t off = fp16_row(a, s, c0 + i, nwin, slots, &snk) + 8 * part;
+        const uint4 w = *reinterpret_cast<const uint4*>((snk ? lv.sink_k : lv.win_k) + off);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          d = fmaf(qv[2 * k], f16_val((uint16_t)(ww[k] & 0xFFFFu)), d);
+          d = fmaf(qv[2 * k + 1], f16_val((uint16_t)(ww[k] >> 16)), d);
         }
-        S.rows_k[t][c] = kx;
-        S.rows_v[t][c] = vx;
-      }
-    } else {
-      blk = a.blk_first + (int64_t)sigma * a.blocks_per_split + ch;
-      const uint8_t* src = lv.bulk + ((int64_t)s * lv.cap_b + blk % lv.cap_b) * lv.rec;
-      for (int64_t o = tid * 16; o < lv.rec; o += NT * 16)
-        *reinterpret_cast<uint4*>(S.rec + o) = *reinterpret_cast<const uint4*>(src + o);
-    }
-    __syncthreads();
-
-    // scores
-    {
-      float part[MAX_GQA];
-      for (int j = 0; j < MAX_GQA; ++j) part[j] = 0.f;
-      for (int cc = 0; cc < cps; ++cc) {
-        const int c = sl * cps + cc;
-        const float kv = fp16_split ? f16_val(S.rows_k[st][c]) : k_val(sh, S.rec, lv, st, c);
-        for (int j = 0; j < r; ++j) part[j] = fmaf(S.q[j][c], kv, part[j]);
-      }
-      for (int j = 0; j < r; ++j) {
-        float v = part[j];
-        v = v + __shfl_xor(v, 1);
-        v = v + __shfl_xor(v, 2);
-        v = v + __shfl_xor(v, 4);
-        part[j] = v;
-      }
-      if (sl == 0) {
-        bool valid;
-        float mult = a.scale;
-        if (fp16_split) {
-          const int64_t i = (int64_t)ch * G + st;
-          valid = i < n_fp;
-          if (valid && i < a.P - fp_lo) {
-            const int64_t p = fp_lo + i;
-            for (int q = 0; q < S.nsinks; ++q) valid = valid && S.sinks[q] != p;
-          }
-        } else {
-          const int64_t p = blk * G + st;
-          valid = p >= a.bulk_lo && p < a.bulk_hi;
-          for (int q = 0; q < S.nsinks; ++q) valid = valid && S.sinks[q] != p;
-          if (tq) mult = mult * reinterpret_cast<const float*>(S.rec + lv.k_meta)[st];
+        if (!snk) {
+          const int64_t p = a.bulk_hi + c0 + i;
+          for (int q = 0; q < nsinks; ++q) ok = ok && sinks[q] != p;
         }
-        for (int j = 0; j < r; ++j) S.sc[j][st] = valid ? part[j] * mult : -INFINITY;
       }
+      for (int off = lpr / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      if (part == 0 && i < n) sc[i] = ok ? d : -INFINITY;
     }
     __syncthreads();
-    // online softmax, one thread per head
-    if (tid < r) {
-      const int j = tid;
-      float mx = -INFINITY;
-      for (int t = 0; t < G; ++t) mx = fmaxf(mx, S.sc[j][t]);
-      const float mold = S.m[j], mnew = fmaxf(mold, mx);
-      float f = 1.f, sum = 0.f;
-      if (mnew == -INFINITY) {
-        for (int t = 0; t < G; ++t) S.sc[j][t] = 0.f;
-      } else {
-        f = mold == -INFINITY ? 0.f : __expf(mold - mnew);
-        for (int t = 0; t < G; ++t) {
-          const float p = S.sc[j][t] == -INFINITY ? 0.f : __expf(S.sc[j][t] - mnew);
-          S.sc[j][t] = p;
-          sum += p;
-        }
-        S.m[j] = mnew;
-      }
-      S.l[j] = S.l[j] * f + sum;
-      S.fac[j] = f;
-    }
+    // chunk maximum (every wave reduces the whole chunk: no extra barrier)
+    float mx = -INFINITY;
+    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[i]);
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mnew = fmaxf(m, mx);
+    const float f = (m == -INFINITY) ? 0.f : exp2f(m - mnew);
     __syncthreads();
-    // values
-    for (int j = 0; j < r; ++j) acc[j] *= S.fac[j];
-    for (int tt = 0; tt < rps; ++tt) {
-      const int t = vs * rps + tt;
-      float vv;
-      if (fp16_split) vv = f16_val(S.rows_v[t][vc]);
-      else {
-        vv = v_val(sh, S.rec, lv, t, vc);
-        if (tq) vv = vv * reinterpret_cast<const float*>(S.rec + lv.v_meta)[t];
-      }
-      for (int j = 0; j < r; ++j) acc[j] = fmaf(S.sc[j][t], vv, acc[j]);
+    if (tid < n) sc[tid] = (sc[tid] == -INFINITY) ? 0.f : exp2f(sc[tid] - mnew);
+    __syncthreads();
+    float sum = 0.f;
+    for (int i = lane; i < n; i += 64) sum += sc[i];
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
+    if (mnew != -INFINITY) {
+      l = l * f + sum;
+      acc0 *= f;
+      acc1 *= f;
+      m = mnew;
+    }
+    for (int i = vsl; i < n; i += nvsl) {
+      bool snk;
+      const int64_t off = fp16_row(a, s, c0 + i, nwin, slots, &snk) + 2 * cp;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>((snk ? lv.sink_v : lv.win_v) + off);
+      const float p = sc[i];
+      acc0 = fmaf(p, f16_val((uint16_t)(w & 0xFFFFu)), acc0);
+      acc1 = fmaf(p, f16_val((uint16_t)(w >> 16)), acc1);
     }
     __syncthreads();
   }
+  red[2 * tid] = acc0;
+  red[2 * tid + 1] = acc1;
 
-  // reduce the value slices and write this workgroup's partial
-  for (int j = 0; j < r; ++j) S.red[tid][j] = acc[j];
-  __syncthreads();
-  const int total = a.splits + 1;
-  float* part = a.ws + ((int64_t)s * total + sigma) * r * (D + 2);
-  for (int idx = tid; idx < r * D; idx += NT) {
-    const int j = idx / D, c = idx % D;
-    float v = 0.f;
-    for (int q = 0; q < nvs; ++q) v += S.red[q * D + c][j];
-    part[j * (D + 2) + 2 + c] = v;
-  }
-  if (tid < r) {
-    part[tid * (D + 2)] = S.m[tid];
-    part[tid * (D + 2) + 1] = S.l[tid];
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const int prev = atomicAdd(&lv.counters[s], 1);
-    S.last = prev == total - 1;
-  }
-  __syncthreads();
-  if (!S.last) return;
-  __threadfence();
-  if (tid == 0) lv.counters[s] = 0;  // ready for the next call
-
-  // merge in fixed order; TurboQuant merges the rotated bulk first and rotates it back
-  const float* P0 = a.ws + (int64_t)s * total * r * (D + 2);
-  const int nbulk = a.splits;
-  float* fin = &S.q[0][0];  // reuse: merged bulk accumulator [r][D]
-  __shared__ float Mb[MAX_GQA], Lb[MAX_GQA];
-  if (tid < r) {
-    float M = -INFINITY;
-    for (int q = 0; q < (tq ? nbulk : total); ++q) M = fmaxf(M, P0[(q * r + tid) * (D + 2)]);
+  // weights of the bulk partials and of the fp16 rows
+  const int np = a.nparts;
+  const float* P0 = a.ws + (int64_t)s * np * r * (D + 2);
+  if (tid < 64) {
+    float M = m;
+    for (int q = tid; q < np; q += 64) M = fmaxf(M, P0[(q * r + j) * (D + 2)]);
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
     float L = 0.f;
-    for (int q = 0; q < (tq ? nbulk : total); ++q) {
-      const float mq = P0[(q * r + tid) * (D + 2)];
-      if (mq != -INFINITY) L += P0[(q * r + tid) * (D + 2) + 1] * __expf(mq - M);
-    }
-    Mb[tid] = M;
-    Lb[tid] = L;
-  }
-  __syncthreads();
-  for (int idx = tid; idx < r * D; idx += NT) {
-    const int j = idx / D, c = idx % D;
-    float v = 0.f;
-    for (int q = 0; q < (tq ? nbulk : total); ++q) {
+    for (int q = tid; q < np; q += 64) {
       const float mq = P0[(q * r + j) * (D + 2)];
-      if (mq != -INFINITY) v += P0[(q * r + j) * (D + 2) + 2 + c] * __expf(mq - Mb[j]);
+      const float w = mq == -INFINITY ? 0.f : exp2f(mq - M);
+      wq[q] = w;
+      L += P0[(q * r + j) * (D + 2) + 1] * w;
     }
-    fin[j * MAX_D + c] = v;
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (tid == 0) {
+      const float wf = m == -INFINITY ? 0.f : exp2f(m - M);
+      Wf = wf;
+      Ls = L + l * wf;
+    }
   }
   __syncthreads();
-  if (tq) {
-    // inverse rotation of the merged bulk accumulator: sigma * (c_d * FWHT(acc))
-    const float cd = (float)(1.0 / __builtin_sqrt((double)D));
-    for (int j = tid >> 6; j < r; j += NT / 64) {
-      const bool act = 2 * lane < D;
-      float y0 = act ? fin[j * MAX_D + 2 * lane] : 0.f;
-      float y1 = act ? fin[j * MAX_D + 2 * lane + 1] : 0.f;
-      wave_fwht(y0, y1, D, lane);
-      if (act) {
-        fin[j * MAX_D + 2 * lane] = lv.tables->signs[2 * lane] * (y0 * cd);
-        fin[j * MAX_D + 2 * lane + 1] = lv.tables->signs[2 * lane + 1] * (y1 * cd);
-      }
-    }
-    __syncthreads();
-    // merge with the fp16 partial (original domain)
-    if (tid < r) {
-      const float mf = P0[(nbulk * r + tid) * (D + 2)], lf = P0[(nbulk * r + tid) * (D + 2) + 1];
-      const float M = fmaxf(Mb[tid], mf);
-      const float wb = Mb[tid] == -INFINITY ? 0.f : __expf(Mb[tid] - M);
-      const float wf = mf == -INFINITY ? 0.f : __expf(mf - M);
-      S.fac[tid] = wb;
-      S.m[tid] = wf;
-      S.l[tid] = Lb[tid] * wb + lf * wf;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < r * D; idx += NT) {
-      const int j = idx / D, c = idx % D;
-      const float v = fin[j * MAX_D + c] * S.fac[j] + P0[(nbulk * r + j) * (D + 2) + 2 + c] * S.m[j];
-      a.out[((int64_t)b * sh.Hq + g * r + j) * D + c] = v / S.l[j];
-    }
-  } else {
-    for (int idx = tid; idx < r * D; idx += NT) {
-      const int j = idx / D, c = idx % D;
-      a.out[((int64_t)b * sh.Hq + g * r + j) * D + c] = fin[j * MAX_D + c] / Lb[j];
-    }
+  if (tid < D) {
+    float v = 0.f;
+#pragma unroll 4
+    for (int q = 0; q < np; ++q) v += wq[q] * P0[(q * r + j) * (D + 2) + 2 + tid];
+    // fp16 rows: sum the row slices of channel tid
+    const int c2 = tid >> 1, hi = tid & 1;
+    float fp = 0.f;
+    for (int q = 0; q < nvsl; ++q) fp += red[2 * (q * ncp + c2) + hi];
+    v += fp * Wf;
+    a.out[((int64_t)b * sh.Hq + g * r + j) * D + tid] = v / Ls;
   }
 }
 
 }  // namespace
 
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st);
+
+// Split-K decode: one kernel writes a partial (m, l, acc) per (split, stream) into the
+// workspace, a second merges them per stream in fixed order.  The kernel boundary orders the
+// two across the XCDs' separate L2 caches without device-scope fences inside a kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  dim3 grid(a.splits + 1, a.sh.B * a.sh.Hkv);
-  hipLaunchKernelGGL(k_decode, grid, dim3(NT), 0, st, a);
+  hipError_t e;
+  if (a.fast) {
+    e = launch_decode_fast(a, st);
+  } else if (a.nparts > 0) {
+    dim3 grid(a.nparts, a.sh.B * a.sh.Hkv);
+    hipLaunchKernelGGL(k_decode, grid, dim3(DNT), 0, st, a);
+    e = hipGetLastError();
+  } else {
+    e = hipSuccess;
+  }
+  if (e != hipSuccess) return e;
+  if (a.sh.fmt == KVQ_FMT_TQ)
+    hipLaunchKernelGGL(k_decode_merge, dim3(a.sh.B * a.sh.Hkv), dim3(DNT), 0, st, a);
+  else
+    hipLaunchKernelGGL(k_merge_heads, dim3(a.sh.B * a.sh.Hkv, a.sh.Hq / a.sh.Hkv), dim3(MNT), 0, st, a);
   return hipGetLastError();
 }
 

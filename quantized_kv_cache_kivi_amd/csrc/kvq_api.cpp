@@ -129,22 +129,31 @@ kvq_layout make_layout(const kvq_config& c) {
   off = align256(off + (uint64_t)c.batch * c.n_sink * 4);
   L.sink_count = off;
   off = align256(off + (uint64_t)c.batch * 4);
-  L.counters = off;
-  off = align256(off + S * 4);
   L.layer_stride = off;
   L.tables = (uint64_t)c.n_layers * L.layer_stride;
   L.total = L.tables + align256(sizeof(Tables));
   return L;
 }
 
-constexpr int TARGET_WGS = 2048;       // split-K target: many more workgroups than the 256 CUs
-constexpr int MIN_BLOCKS_PER_SPLIT = 2;
+// Shapes the MFMA decode path covers (the generic kernel takes the rest).
+bool fast_path(const kvq_config& c) {
+  const int r = c.n_q_heads / c.n_kv_heads;
+  return c.head_dim == 128 && (r == 1 || r == 2 || r == 4 || r == 8) &&
+         (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits));
+}
 
-int max_splits(const kvq_config& c) {
+// Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, at least 4 blocks per
+// wave, and enough workgroups (~1024) to cover the 256 CUs several times.  Generic path: ~2048
+// workgroups of >= 2 blocks.  Never more than 64 splits; monotone in nblk.
+int splits_for(const kvq_config& c, int nblk) {
   const int streams = c.batch * c.n_kv_heads;
-  int s = (TARGET_WGS + streams - 1) / streams;
+  int s;
+  if (fast_path(c)) s = std::min((nblk + 15) / 16, std::max(1, (1024 + streams - 1) / streams));
+  else s = std::min((nblk + 1) / 2, std::max(1, (2048 + streams - 1) / streams));
   return std::max(1, std::min(s, 64));
 }
+
+int max_splits(const kvq_config& c) { return splits_for(c, effective_capacity(c) / G); }
 
 }  // namespace
 
@@ -189,7 +198,6 @@ LayerView view_of(const kvq_cache* c, int layer) {
   v.sink_pos = (int32_t*)(b + L.sink_pos);
   v.sink_score = (float*)(b + L.sink_score);
   v.sink_count = (int32_t*)(b + L.sink_count);
-  v.counters = (int32_t*)(b + L.counters);
   v.tables = (const Tables*)(c->base + L.tables);
   v.rec = (int64_t)L.record_bytes;
   v.k_codes = (int64_t)L.rec_k_codes;
@@ -369,8 +377,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   if (a.bulk_hi > a.bulk_lo) {
     a.blk_first = a.bulk_lo / G;
     a.nblk = (int)((a.bulk_hi - 1) / G - a.blk_first + 1);
-    int s = std::min(max_splits(cf), (a.nblk + MIN_BLOCKS_PER_SPLIT - 1) / MIN_BLOCKS_PER_SPLIT);
-    s = std::max(1, s);
+    const int s = splits_for(cf, a.nblk);
     a.blocks_per_split = (a.nblk + s - 1) / s;
     a.splits = (a.nblk + a.blocks_per_split - 1) / a.blocks_per_split;
   } else {
@@ -379,6 +386,8 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
     a.splits = 0;
     a.blocks_per_split = 0;
   }
+  a.fast = fast_path(cf) && a.splits > 0;
+  a.nparts = a.splits + (cf.format == KVQ_FMT_TQ ? 1 : 0);
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;

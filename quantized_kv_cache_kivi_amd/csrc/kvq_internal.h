@@ -36,7 +36,6 @@ struct LayerView {
   int32_t* sink_pos;    // [B][n_sink]
   float* sink_score;    // [B][n_sink]
   int32_t* sink_count;  // [B]
-  int32_t* counters;    // [B*Hkv]
   const Tables* tables;
   int64_t rec, k_codes, v_codes, k_meta, v_meta;  // record size and section offsets
   int cap_b;
@@ -78,6 +77,8 @@ struct DecodeArgs {
   int nblk;                  // bulk blocks
   int splits;                // bulk splits S (the fp16 split is index S)
   int blocks_per_split;
+  int fast;                  // 1: MFMA path (head_dim 128, KIVI equal widths or q2k, GQA ratio 1/2/4/8)
+  int nparts;                // partials per stream in the workspace (splits, plus 1 for TurboQuant's fp16 rows)
 };
 
 struct DequantArgs {

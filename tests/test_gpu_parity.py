@@ -29,6 +29,14 @@ CASES = {
                  capacity=512, seed=0x5EED0004),
     "tq24_topk_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=2,
                           v_bits=4, sink_mode="topk", n_sink=2, window=128, residual=8, seed=77),
+    "fast_kivi4_r8_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="kivi", k_bits=4,
+                              v_bits=4, sink_mode="first_n", n_sink=4, window=160, residual=16),
+    "fast_kivi8_r2_topk": dict(n_layers=1, batch=2, n_kv_heads=3, n_q_heads=6, head_dim=128, fmt="kivi", k_bits=8,
+                               v_bits=8, sink_mode="topk", n_sink=5, residual=0, capacity=512),
+    "fast_kivi2_r1_win": dict(n_layers=1, batch=1, n_kv_heads=4, n_q_heads=4, head_dim=128, fmt="kivi", k_bits=2,
+                              v_bits=2, window=96, residual=0),
+    "fast_q2k_r8_topk": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="q2k", k_bits=2,
+                             v_bits=4, sink_mode="topk", n_sink=4, residual=40, capacity=512),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]
