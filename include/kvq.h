@@ -159,7 +159,9 @@ kvq_status kvq_select_sinks(kvq_cache* c, int32_t layer, const void* k, int32_t 
  * re-quantized from its staged rows until it is complete); sink rows are
  * excluded from calibration and copied to the fp16 sink pool ([KS] 2-3); the
  * last `residual` rows are copied to the fp16 window ring.  Fails with
- * KVQ_ECAPACITY if a written block slot still holds a live block. */
+ * KVQ_ECAPACITY if a written block slot still holds a live block, and with
+ * KVQ_ERANGE if a position would reach 2^31 (positions are int32 on the
+ * device). */
 kvq_status kvq_append(kvq_cache* c, int32_t layer, const void* k, const void* v, int32_t n, void* stream);
 
 /* StreamingLLM eviction of positions [sink, P - window) ([SK]

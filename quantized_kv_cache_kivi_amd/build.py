@@ -4,7 +4,8 @@
 
 Flags: -ffp-contract=off keeps every code-deciding fp32 expression one
 rounding per operation (the quantizer's codes must match a reference that
-computes the same way); packed fp32 math is switched off.
+computes the same way); packed fp32 math is switched off; MFMA accumulators
+are kept in ordinary VGPRs (no AGPR copies around the online-softmax rescale).
 """
 
 import os
@@ -18,6 +19,7 @@ SOURCES = ["kvq_api.cpp", "tables.cpp", "append.hip", "select.hip", "decode.hip"
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -35,139 +35,232 @@ __global__ __launch_bounds__(DNT) void k_decode_merge(DecodeArgs a) {
 }
 
 constexpr int MNT = 256;  // threads of a merge workgroup
-constexpr int MCH = 256;  // fp16 rows per chunk of the merge kernel
+constexpr int MNP = 8;    // fp16 row passes per chunk (a pass covers MNT / (D/8) rows)
+constexpr int MPF = 16;   // split partials a thread fetches before the fp16 rows are scored
 
-// Address (in fp16 elements) of fp16 row i of stream s: window rows [bulk_hi, P) first, then
-// the committed sinks in slot order.
-__device__ __forceinline__ int64_t fp16_row(const DecodeArgs& a, int s, int64_t i, int64_t nwin, const int* slot,
-                                            bool* is_sink) {
-  const int D = a.sh.D;
-  if (i < nwin) {
-    *is_sink = false;
-    const int64_t p = a.bulk_hi + i;
-    return ((int64_t)s * a.sh.R + p % a.sh.R) * D;
+typedef uint32_t mu4 __attribute__((ext_vector_type(4)));
+
+// q[0..7] . (8 fp16 values of w)
+__device__ __forceinline__ float dot8(const float* q, const mu4& w) {
+  const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+  float d = 0.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    d = fmaf(q[2 * k], f16_val((uint16_t)(ww[k] & 0xFFFFu)), d);
+    d = fmaf(q[2 * k + 1], f16_val((uint16_t)(ww[k] >> 16)), d);
   }
-  *is_sink = true;
-  return ((int64_t)s * a.sh.n_sink + slot[i - nwin]) * D;
+  return d;
 }
 
-// Merge for formats without a rotation: one workgroup per (stream, query head).  The fp16 rows
-// are scored (one row per D/8 lanes, 8 channels a lane), turned into weights chunk by chunk with
-// an online max, and accumulated (two channels a lane, rows strided over the row slices); the
-// bulk partials of the head are then folded in, in split order.
+// Online-softmax state of the fp16 rows of one (stream, head): m is block-uniform; l and the
+// 8-channel accumulator are per thread (rows of its row slot).
+struct FpState {
+  float m, l, acc[8];
+};
+
+// Folds a set of K scores (one per pass of this thread's row slot; -inf where masked) and their
+// V rows into the state.  The block-wide maximum takes two barriers.
+template <int K>
+__device__ __forceinline__ void fp_update(FpState& st, const float (&sc)[K], const mu4 (&v)[K], bool counts,
+                                          float* wred, int lane, int wv) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < K; ++k) mx = fmaxf(mx, sc[k]);
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) wred[wv] = mx;
+  lds_barrier();
+  float M = wred[0];
+#pragma unroll
+  for (int w = 1; w < MNT / 64; ++w) M = fmaxf(M, wred[w]);
+  lds_barrier();
+  const float mnew = fmaxf(st.m, M);
+  if (mnew == -INFINITY) return;  // nothing valid yet (uniform)
+  const float f = st.m == -INFINITY ? 0.f : exp2f(st.m - mnew);
+  float lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.acc[c] *= f;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const float w = sc[k] == -INFINITY ? 0.f : exp2f(sc[k] - mnew);
+    lsum += w;
+    const uint32_t vv[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      st.acc[2 * c] = fmaf(w, f16_val((uint16_t)(vv[c] & 0xFFFFu)), st.acc[2 * c]);
+      st.acc[2 * c + 1] = fmaf(w, f16_val((uint16_t)(vv[c] >> 16)), st.acc[2 * c + 1]);
+    }
+  }
+  st.l = st.l * f + (counts ? lsum : 0.f);  // one lane per row counts the row's weight
+  st.m = mnew;
+}
+
+// Window rows [c0, c0 + MNP * rpp) of this thread's row slot (rows past the window read row 0).
+__device__ __forceinline__ void load_window(mu4 (&kr)[MNP], mu4 (&vr)[MNP], const uint16_t* wk, const uint16_t* wv,
+                                            int c0, int rs, int rpp, int nwin, int slot0, int R, int D) {
+#pragma unroll
+  for (int k = 0; k < MNP; ++k) {
+    const int row = c0 + rs + k * rpp;
+    const int rr = row < nwin ? row : 0;  // clamped: the load is always in bounds
+    int sl = slot0 + rr;
+    if (sl >= R) sl -= R;
+    kr[k] = *reinterpret_cast<const mu4*>(wk + (int64_t)sl * D);
+    vr[k] = *reinterpret_cast<const mu4*>(wv + (int64_t)sl * D);
+  }
+}
+
+// Merge for formats without a rotation: one workgroup per (stream, query head).  Every load is
+// issued before any is used (sink slots, query slice, split partials, sink-pool rows, the first
+// chunk of window rows; clamped addresses instead of branches); the fp16 rows (window rows
+// [bulk_hi, P) minus committed sinks, then the sink pool in slot order) are scored with D/8 lanes
+// per row and folded in with an online maximum; the bulk partials of the head are then merged in
+// split order.
 __global__ __launch_bounds__(MNT) void k_merge_heads(DecodeArgs a) {
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int s = blockIdx.x, j = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int D = sh.D, r = sh.Hq / sh.Hkv, b = s / sh.Hkv, g = s % sh.Hkv;
-  __shared__ float sc[MCH];
-  __shared__ float red[2 * MNT];
+  const int D = sh.D, r = sh.Hq / sh.Hkv, b = s / sh.Hkv, g = s % sh.Hkv, ns = sh.n_sink;
+  const int lpr = D / 8, rpp = MNT / lpr, part = tid % lpr, rs = tid / lpr;
+  __shared__ int spos[MAX_SINK];  // position of each sink-pool slot; -1 unless a committed sink < P
+  __shared__ int wsk[MAX_SINK];   // window rows holding a committed sink (read from the pool instead)
+  __shared__ int nwsk;
+  __shared__ float wred[MNT / 64];
+  __shared__ float red[MNT * 8];
   __shared__ float wq[65];
-  __shared__ int sinks[MAX_SINK], slots[MAX_SINK], nsinks;
   __shared__ float Ls, Wf;
 
-  stage_sinks(a, b, sinks, slots, &nsinks);
-  __syncthreads();
-  const int64_t nwin = a.P - a.bulk_hi;
-  const int64_t n_fp = nwin + nsinks;
-
-  // query slice of this lane for the score mapping, in log2 units
-  const int lpr = D / 8, rpw = 64 / lpr, part = lane % lpr, rsub = lane / lpr;
-  const float mult = a.scale * LOG2E;
-  const int64_t qoff = ((int64_t)b * sh.Hq + (int64_t)g * r + j) * D + 8 * part;
-  float qv[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) qv[k] = ld_in(a.q, qoff + k, sh.in_f32) * mult;
-  // value mapping: channel pair cp, row slice vsl
-  const int ncp = D / 2, cp = tid % ncp, vsl = tid / ncp, nvsl = MNT / ncp;
-
-  float m = -INFINITY, l = 0.f, acc0 = 0.f, acc1 = 0.f;
-  for (int64_t c0 = 0; c0 < n_fp; c0 += MCH) {
-    const int n = (int)min((int64_t)MCH, n_fp - c0);
-    // scores of rows [c0, c0 + n)
-    for (int base = wv * rpw; base < n; base += (MNT / 64) * rpw) {
-      const int i = base + rsub;
-      float d = 0.f;
-      bool ok = i < n, snk = false;
-      if (ok) {
-        const int64_t off = fp16_row(a, s, c0 + i, nwin, slots, &snk) + 8 * part;
-        const uint4 w = *reinterpret_cast<const uint4*>((snk ? lv.sink_k : lv.win_k) + off);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          d = fmaf(qv[2 * k], f16_val((uint16_t)(ww[k] & 0xFFFFu)), d);
-          d = fmaf(qv[2 * k + 1], f16_val((uint16_t)(ww[k] >> 16)), d);
-        }
-        if (!snk) {
-          const int64_t p = a.bulk_hi + c0 + i;
-          for (int q = 0; q < nsinks; ++q) ok = ok && sinks[q] != p;
-        }
-      }
-      for (int off = lpr / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
-      if (part == 0 && i < n) sc[i] = ok ? d : -INFINITY;
-    }
-    __syncthreads();
-    // chunk maximum (every wave reduces the whole chunk: no extra barrier)
-    float mx = -INFINITY;
-    for (int i = lane; i < n; i += 64) mx = fmaxf(mx, sc[i]);
-    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float mnew = fmaxf(m, mx);
-    const float f = (m == -INFINITY) ? 0.f : exp2f(m - mnew);
-    __syncthreads();
-    if (tid < n) sc[tid] = (sc[tid] == -INFINITY) ? 0.f : exp2f(sc[tid] - mnew);
-    __syncthreads();
-    float sum = 0.f;
-    for (int i = lane; i < n; i += 64) sum += sc[i];
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off);
-    if (mnew != -INFINITY) {
-      l = l * f + sum;
-      acc0 *= f;
-      acc1 *= f;
-      m = mnew;
-    }
-    for (int i = vsl; i < n; i += nvsl) {
-      bool snk;
-      const int64_t off = fp16_row(a, s, c0 + i, nwin, slots, &snk) + 2 * cp;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>((snk ? lv.sink_v : lv.win_v) + off);
-      const float p = sc[i];
-      acc0 = fmaf(p, f16_val((uint16_t)(w & 0xFFFFu)), acc0);
-      acc1 = fmaf(p, f16_val((uint16_t)(w >> 16)), acc1);
-    }
-    __syncthreads();
-  }
-  red[2 * tid] = acc0;
-  red[2 * tid + 1] = acc1;
-
-  // weights of the bulk partials and of the fp16 rows
+  const int nwin = (int)(a.P - a.bulk_hi);  // positions fit in int32
   const int np = a.nparts;
   const float* P0 = a.ws + (int64_t)s * np * r * (D + 2);
-  if (tid < 64) {
-    float M = m;
-    for (int q = tid; q < np; q += 64) M = fmaxf(M, P0[(q * r + j) * (D + 2)]);
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float L = 0.f;
-    for (int q = tid; q < np; q += 64) {
-      const float mq = P0[(q * r + j) * (D + 2)];
-      const float w = mq == -INFINITY ? 0.f : exp2f(mq - M);
-      wq[q] = w;
-      L += P0[(q * r + j) * (D + 2) + 1] * w;
-    }
-    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
-    if (tid == 0) {
-      const float wf = m == -INFINITY ? 0.f : exp2f(m - M);
-      Wf = wf;
-      Ls = L + l * wf;
+
+  // ---- loads (branch-free: an empty source is replaced by an always-valid one and masked later) ----
+  const int cnt = lv.sink_count[b];
+  const int praw = *(ns > 0 ? lv.sink_pos + b * ns + min(tid, ns - 1) : lv.sink_count + b);
+  // query slice: one 16-byte load (fp16) or two (fp32)
+  const int64_t qo = ((int64_t)b * sh.Hq + (int64_t)g * r + j) * D + 8 * part;
+  const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qo * (sh.in_f32 ? 4 : 2);
+  const mu4 qw0 = *reinterpret_cast<const mu4*>(qp);
+  const mu4 qw1 = *reinterpret_cast<const mu4*>(qp + (sh.in_f32 ? 16 : 0));
+  const int npc = max(np, 1);  // the workspace always holds one partial per stream
+  float pm = P0[(min(tid, npc - 1) * r + j) * (D + 2)];
+  float pl = P0[(min(tid, npc - 1) * r + j) * (D + 2) + 1];
+  float pv[MPF];
+#pragma unroll
+  for (int q = 0; q < MPF; ++q) pv[q] = P0[(min(q, npc - 1) * r + j) * (D + 2) + 2 + min(tid, D - 1)];
+  const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + 8 * part;  // stand-in row source
+  const uint16_t* skp = ns > 0 ? lv.sink_k + ((int64_t)s * ns + min(rs, ns - 1)) * D + 8 * part : q16;
+  const uint16_t* svp = ns > 0 ? lv.sink_v + ((int64_t)s * ns + min(rs, ns - 1)) * D + 8 * part : q16;
+  const mu4 sk = *reinterpret_cast<const mu4*>(skp);
+  const mu4 svv = *reinterpret_cast<const mu4*>(svp);
+  const int slot0 = nwin > 0 ? (int)(a.bulk_hi % sh.R) : 0;
+  const int rring = max(sh.R, 1);
+  const uint16_t* wk = nwin > 0 ? lv.win_k + ((int64_t)s * sh.R) * D + 8 * part : q16;
+  const uint16_t* wvp = nwin > 0 ? lv.win_v + ((int64_t)s * sh.R) * D + 8 * part : q16;
+  mu4 kr[MNP], vr[MNP];
+  load_window(kr, vr, wk, wvp, 0, rs, rpp, nwin, slot0, rring, D);
+
+  // ---- uses ----
+  if (tid < ns) spos[tid] = (tid < min(cnt, ns) && praw >= 0 && praw < a.P) ? praw : -1;
+  if (tid >= np) {
+    pm = -INFINITY;
+    pl = 0.f;
+  }
+  if (np == 0) {
+#pragma unroll
+    for (int q = 0; q < MPF; ++q) pv[q] = 0.f;
+  }
+  const float mult = a.scale * LOG2E;
+  float qv[8];
+  if (sh.in_f32) {
+    const uint32_t ww[8] = {qw0.x, qw0.y, qw0.z, qw0.w, qw1.x, qw1.y, qw1.z, qw1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) qv[k] = __builtin_bit_cast(float, ww[k]);
+  } else {
+    const uint32_t ww[4] = {qw0.x, qw0.y, qw0.z, qw0.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      qv[2 * k] = f16_val((uint16_t)(ww[k] & 0xFFFFu));
+      qv[2 * k + 1] = f16_val((uint16_t)(ww[k] >> 16));
     }
   }
-  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < 8; ++k) qv[k] *= mult;
+  lds_barrier();
+  if (tid < 64) {  // committed sinks inside the window
+    const int p = lane < ns ? spos[lane] : -1;
+    const bool in = p >= 0 && p >= a.bulk_hi && p < a.P;
+    const uint64_t msk = __ballot(in);
+    if (in) wsk[__popcll(msk & ((1ull << lane) - 1ull))] = (int)(p - a.bulk_hi);
+    if (lane == 0) nwsk = __popcll(msk);
+  }
+  lds_barrier();
+  const int nw = nwsk;
+
+  FpState st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) st.acc[c] = 0.f;
+  // window rows, chunk by chunk
+  for (int c0 = 0; c0 < nwin; c0 += MNP * rpp) {
+    if (c0 > 0) load_window(kr, vr, wk, wvp, c0, rs, rpp, nwin, slot0, rring, D);
+#pragma unroll
+    for (int k = 0; k < MNP; ++k)
+      if (c0 + rs + k * rpp >= nwin) kr[k] = vr[k] = mu4{0, 0, 0, 0};
+    float sc[MNP];
+#pragma unroll
+    for (int k = 0; k < MNP; ++k) {
+      float d = dot8(qv, kr[k]);
+      for (int off = lpr / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      const int row = c0 + rs + k * rpp;
+      bool ok = row < nwin;
+      for (int q = 0; q < nw; ++q) ok = ok && wsk[q] != row;
+      sc[k] = ok ? d : -INFINITY;
+    }
+    fp_update(st, sc, vr, part == 0, wred, lane, wv);
+  }
+  // sink pool rows (slot order), one pass
+  {
+    float d = dot8(qv, sk);
+    for (int off = lpr / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+    const bool ok = rs < ns && spos[rs] >= 0;
+    const float sc1[1] = {ok ? d : -INFINITY};
+    const mu4 v1[1] = {ok ? svv : mu4{0, 0, 0, 0}};
+    fp_update(st, sc1, v1, part == 0, wred, lane, wv);
+  }
+
+  // ---- reduce the fp16 state over the row slots ----
+  float lt = st.l;
+  for (int off = 32; off >= 1; off >>= 1) lt += __shfl_xor(lt, off);
+  if (lane == 0) wred[wv] = lt;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) red[rs * D + 8 * part + c] = st.acc[c];
+  lds_barrier();
+  float lfp = 0.f;
+#pragma unroll
+  for (int w = 0; w < MNT / 64; ++w) lfp += wred[w];
+  // ---- weights of the bulk partials and of the fp16 rows ----
+  if (tid < 64) {
+    float M = fmaxf(st.m, pm);  // np <= 64: lane q holds split q
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float w = pm == -INFINITY ? 0.f : exp2f(pm - M);
+    if (tid < np) wq[tid] = w;
+    float L = pl * w;
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (tid == 0) {
+      const float wf = st.m == -INFINITY ? 0.f : exp2f(st.m - M);
+      Wf = wf;
+      Ls = L + lfp * wf;
+    }
+  }
+  lds_barrier();
   if (tid < D) {
     float v = 0.f;
-#pragma unroll 4
-    for (int q = 0; q < np; ++q) v += wq[q] * P0[(q * r + j) * (D + 2) + 2 + tid];
-    // fp16 rows: sum the row slices of channel tid
-    const int c2 = tid >> 1, hi = tid & 1;
+#pragma unroll
+    for (int q = 0; q < MPF; ++q)
+      if (q < np) v += wq[q] * pv[q];
+    for (int q = MPF; q < np; ++q) v += wq[q] * P0[(q * r + j) * (D + 2) + 2 + tid];
     float fp = 0.f;
-    for (int q = 0; q < nvsl; ++q) fp += red[2 * (q * ncp + c2) + hi];
+    for (int q = 0; q < rpp; ++q) fp += red[q * D + tid];
     v += fp * Wf;
     a.out[((int64_t)b * sh.Hq + g * r + j) * D + tid] = v / Ls;
   }

@@ -46,6 +46,13 @@ __device__ __forceinline__ void v_code_pos(int t, int c, int D, int b, int* word
 // Token of element e of V token group kg.
 __device__ __forceinline__ int v_tok(int kg, int e) { return 16 * (e >> 2) + 4 * kg + (e & 3); }
 
+// Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float wave_sum_xor(float a, int first_off) {
   for (int off = first_off; off >= 1; off >>= 1) a = a + __shfl_xor(a, off);
   return a;

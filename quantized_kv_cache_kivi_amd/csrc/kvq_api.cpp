@@ -2,6 +2,7 @@
 // launch glue.  Every compute step runs in the HIP kernels; this file only
 // checks arguments, tracks (P, lo) per layer and issues launches.
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -145,21 +146,48 @@ bool fast_path(const kvq_config& c) {
 // Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, at least 4 blocks per
 // wave, and enough workgroups (~1024) to cover the 256 CUs several times.  Generic path: ~2048
 // workgroups of >= 2 blocks.  Never more than 64 splits; monotone in nblk.
-int splits_for(const kvq_config& c, int nblk) {
+// Bulk splits of the MFMA path: whole rounds of the workgroups the device holds at once (`slots`),
+// at least 4 blocks (one per wave) per split, at most 64 splits.
+int fast_splits(int streams, int nblk, int slots) {
+  const int smax = std::max(1, std::min(64, nblk / 4));
+  if (slots <= 0) slots = 1024;
+  int best = 1;
+  double best_eff = -1.0;
+  for (int k = 1; k <= 8; ++k) {
+    int s = std::max(1, std::min(smax, (int)std::lround((double)k * slots / streams)));
+    const int bps = (nblk + s - 1) / s;
+    s = (nblk + bps - 1) / bps;
+    const long long items = (long long)streams * s, rounds = (items + slots - 1) / slots;
+    const double eff = (double)items / (double)(rounds * slots);
+    if (eff > best_eff + 1e-9) {
+      best_eff = eff;
+      best = s;
+    }
+    if (eff >= 0.9) break;
+  }
+  return best;
+}
+
+int splits_for(const kvq_config& c, int nblk, int slots) {
   const int streams = c.batch * c.n_kv_heads;
-  int s;
-  if (fast_path(c)) s = std::min((nblk + 15) / 16, std::max(1, (1024 + streams - 1) / streams));
-  else s = std::min((nblk + 1) / 2, std::max(1, (2048 + streams - 1) / streams));
+  if (fast_path(c)) return fast_splits(streams, nblk, slots);
+  const int s = std::min((nblk + 1) / 2, std::max(1, (2048 + streams - 1) / streams));
   return std::max(1, std::min(s, 64));
 }
 
-int max_splits(const kvq_config& c) { return splits_for(c, effective_capacity(c) / G); }
+// Upper bound of the splits of any decode call (sizes the workspace from the configuration alone).
+int max_splits(const kvq_config& c) {
+  const int nblk = effective_capacity(c) / G;
+  if (fast_path(c)) return std::max(1, std::min(64, nblk / 4));
+  return splits_for(c, nblk, 0);
+}
 
 }  // namespace
 
 struct kvq_cache {
   kvq_config cfg;
   kvq_layout lay;
+  int slots;  // workgroups of the MFMA decode kernel the device holds at once (0: generic path)
   uint8_t* base;
   std::vector<int64_t> P, lo, pend_P;
   std::vector<int32_t> pend_n;
@@ -263,6 +291,7 @@ kvq_status kvq_create(const kvq_config* cfg, void* dev_buf, size_t dev_bytes, vo
   c->pend_P.assign(cfg->n_layers, -1);
   c->pend_n.assign(cfg->n_layers, -1);
   make_tables(c->cfg, &c->tables);
+  c->slots = fast_path(c->cfg) ? fast_resident_slots(shape_of(c->cfg)) : 0;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemsetAsync(dev_buf, 0, lay.total, s);
   if (e != hipSuccess) {
@@ -319,6 +348,8 @@ kvq_status kvq_append(kvq_cache* c, int32_t layer, const void* k, const void* v,
   if (!k || !v || n < 1) return fail(KVQ_EINVAL, "k and v must not be NULL and n >= 1");
   const kvq_config& cf = c->cfg;
   const int64_t P = c->P[layer];
+  if (P + n > (int64_t)INT32_MAX)
+    return fail(KVQ_ERANGE, "append of %d rows at P=%lld: positions must stay below 2^31", n, (long long)P);
   if (cf.sink_mode == KVQ_SINK_TOPK && cf.n_sink > 0 && (c->pend_P[layer] != P || c->pend_n[layer] != n))
     return fail(KVQ_EORDER, "TOPK mode: call kvq_select_sinks on this chunk (P=%lld, n=%d) first", (long long)P, n);
   if (cf.window == 0) {
@@ -377,7 +408,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   if (a.bulk_hi > a.bulk_lo) {
     a.blk_first = a.bulk_lo / G;
     a.nblk = (int)((a.bulk_hi - 1) / G - a.blk_first + 1);
-    const int s = splits_for(cf, a.nblk);
+    const int s = splits_for(cf, a.nblk, c->slots);
     a.blocks_per_split = (a.nblk + s - 1) / s;
     a.splits = (a.nblk + a.blocks_per_split - 1) / a.blocks_per_split;
   } else {

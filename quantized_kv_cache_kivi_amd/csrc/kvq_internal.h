@@ -95,6 +95,10 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 
+// Workgroups of the MFMA decode kernel for this shape that the current device holds at once
+// (compute units x resident workgroups per unit); 0 if the shape has no MFMA kernel.
+int fast_resident_slots(const Shape& sh);
+
 // Host-side table generation (tables.cpp).
 void make_tables(const kvq_config& cfg, Tables* t);
 

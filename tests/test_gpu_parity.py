@@ -35,6 +35,8 @@ CASES = {
                                v_bits=8, sink_mode="topk", n_sink=5, residual=0, capacity=512),
     "fast_kivi2_r1_win": dict(n_layers=1, batch=1, n_kv_heads=4, n_q_heads=4, head_dim=128, fmt="kivi", k_bits=2,
                               v_bits=2, window=96, residual=0),
+    "fast_kivi2_topk_res200": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="kivi",
+                                   k_bits=2, v_bits=2, sink_mode="topk", n_sink=4, residual=200, capacity=512),
     "fast_q2k_r8_topk": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="q2k", k_bits=2,
                              v_bits=4, sink_mode="topk", n_sink=4, residual=40, capacity=512),
 }
