@@ -46,11 +46,12 @@
  *    k = 8*mu + e, the code of channel 16*mu + i of token
  *    T(kg, e) = 16*(e/4) + 4*kg + e%4  (kg 0..3, i 0..15, mu 0..D/16-1, e 0..7).
  *  * KIVI: K meta = scale fp16[D] then zero fp16[D]; V meta = scale
- *    fp16[32][D/32] then zero fp16[32][D/32].  Codes are unsigned offsets
+ *    fp16[16][D/32][2] then zero fp16[16][D/32][2] (token t, group g at
+ *    [t/2][g][t%2]: the two tokens of a pair are adjacent per group).  Codes are unsigned offsets
  *    u = rint((x - zero)/scale) clamped to [0, 2^b - 1], computed against the
  *    stored fp16 scale and zero ([SK] "Affine quantisation formula").
  *  * Q2K: K meta = block RMS fp16[D], K code = number of Gaussian Lloyd-Max
- *    thresholds <= x/rms; V meta = scale fp16[32][D/32], V code = q + 8 with
+ *    thresholds <= x/rms; V meta = scale fp16[16][D/32][2], V code = q + 8 with
  *    q = clamp(rint(x/scale), -8, 7), scale = absmax/7 ([Q2K] "Summary").
  *  * TQ: K meta = fp32 norm[32], V meta = fp32 norm[32] of the rotated row;
  *    codes are Lloyd-Max Beta(D/2, D/2) indices of the rotated, normalised

@@ -142,11 +142,11 @@ def block_records(cfg, qs):
     out[:, off["v_codes"]:off["v_codes"] + size["v_codes"]] = layout.pack_v_tiles(qs["v_codes"], cfg.v_bits)
     if cfg.fmt == "kivi":
         km = np.concatenate([qs["k_scale"], qs["k_zero"]], axis=-1).astype("<u2").view(np.uint8)
-        vm = np.concatenate([qs["v_scale"].reshape(nblk, -1), qs["v_zero"].reshape(nblk, -1)], axis=-1)
+        vm = np.concatenate([layout.pack_v_meta(qs["v_scale"]), layout.pack_v_meta(qs["v_zero"])], axis=-1)
         vm = vm.astype("<u2").view(np.uint8)
     elif cfg.fmt == "q2k":
         km = qs["k_rms"].astype("<u2").view(np.uint8)
-        vm = qs["v_scale"].reshape(nblk, -1).astype("<u2").view(np.uint8)
+        vm = layout.pack_v_meta(qs["v_scale"]).astype("<u2").view(np.uint8)
     else:
         km = qs["k_norm"].astype("<f4").view(np.uint8)
         vm = qs["v_norm"].astype("<f4").view(np.uint8)

@@ -26,10 +26,13 @@ density and changes only which bit a code lands in:
   ====== ======================================= ===================================
   format K meta                                  V meta
   ====== ======================================= ===================================
-  KIVI   scale fp16 [D], then zero fp16 [D]      scale fp16 [32][D/32], then zero
-  q2k    rms fp16 [D]                            scale fp16 [32][D/32]
+  KIVI   scale fp16 [D], then zero fp16 [D]      scale fp16 [16][D/32][2], then zero
+  q2k    rms fp16 [D]                            scale fp16 [16][D/32][2]
   TQ     K norm fp32 [32] (per token)            V norm fp32 [32] (per token)
   ====== ======================================= ===================================
+
+  The V scale (and zero) of token t and 32-channel group g sits at index
+  [t // 2][g][t % 2]: the two tokens of a pair are adjacent for every group.
 """
 
 import numpy as np
@@ -110,6 +113,21 @@ def unpack_v_tiles(data, D, bits):
     out = np.zeros(d.shape[:-1] + (G, D), dtype=np.uint8)
     out[..., tok, ch] = seq
     return out
+
+
+def pack_v_meta(meta):
+    """V metadata [..., 32, D/32] (token, group) -> [..., 32*D/32] in [t // 2][g][t % 2] order."""
+    m = np.asarray(meta)
+    ng = m.shape[-1]
+    pairs = m.reshape(m.shape[:-2] + (G // 2, 2, ng))
+    return np.swapaxes(pairs, -1, -2).reshape(m.shape[:-2] + (G * ng,))
+
+
+def unpack_v_meta(flat, ng):
+    """Inverse of pack_v_meta."""
+    f = np.asarray(flat)
+    pairs = f.reshape(f.shape[:-1] + (G // 2, ng, 2))
+    return np.swapaxes(pairs, -1, -2).reshape(f.shape[:-1] + (G, ng))
 
 
 def record_sections(fmt, D, k_bits, v_bits):

@@ -248,10 +248,10 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
     } else {
       uint16_t* vm = reinterpret_cast<uint16_t*>(rec + lv.v_meta);
       for (int idx = tid; idx < G * ng; idx += NT) {
-        const int t = idx / ng, g = idx % ng;
+        const int t = idx / ng, g = idx % ng, mi = v_meta_idx(t, g, ng);
         if (t < tnew0) continue;
-        vm[idx] = t < tend ? vmeta_s[t][g] : 0;
-        if (sh.fmt == KVQ_FMT_KIVI) vm[G * ng + idx] = t < tend ? vmeta_z[t][g] : 0;
+        vm[mi] = t < tend ? vmeta_s[t][g] : 0;
+        if (sh.fmt == KVQ_FMT_KIVI) vm[G * ng + mi] = t < tend ? vmeta_z[t][g] : 0;
       }
     }
   }

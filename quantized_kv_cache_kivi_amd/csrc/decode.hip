@@ -274,10 +274,9 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st);
 // workspace, a second merges them per stream in fixed order.  The kernel boundary orders the
 // two across the XCDs' separate L2 caches without device-scope fences inside a kernel.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  if (a.fast) return launch_decode_fast(a, st);  // split kernel (bulk and fp16 rows) and its merge
   hipError_t e;
-  if (a.fast) {
-    e = launch_decode_fast(a, st);
-  } else if (a.nparts > 0) {
+  if (a.nparts > 0) {
     dim3 grid(a.nparts, a.sh.B * a.sh.Hkv);
     hipLaunchKernelGGL(k_decode, grid, dim3(DNT), 0, st, a);
     e = hipGetLastError();

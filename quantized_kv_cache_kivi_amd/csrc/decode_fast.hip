@@ -1,35 +1,42 @@
-// MFMA decode attention over the packed bulk, head_dim 128 (gfx950).
+// MFMA decode attention, head_dim 128, fp16 query (gfx950).
 //
-// Writes the bulk split partials that the merge kernel of decode.hip combines
-// with the fp16 rows; it replaces the generic bulk workgroups for KIVI (equal
-// K/V widths 2, 4, 8) and q2k with GQA ratio 1, 2, 4 or 8.
+// One launch of k_decode_fast writes every partial of a decode call: the
+// workgroups with blockIdx.x < splits stream the packed bulk of one split of a
+// stream, the next ones score the fp16 rows (window rows minus committed sinks,
+// then the sink pool) of that stream, 64 rows each.  k_merge_parts then merges
+// the partials of each (stream, query head) in fixed order.
 //
-// Per 32-token block and wave ("StreamingLLM + KIVI — long-context decode
+// Bulk, per 32-token block and wave ("StreamingLLM + KIVI — long-context decode
 // without growing the KV cache", "Affine quantisation formula": k = u*s + z per
-// channel, v = u*s + z per token and 32-channel group; q2k pull-request page:
-// k = level(u)*rms, v = (u - 8)*s):
-//  * scores S^T[t][j] = sum_c u[t][c] * (q[j][c] s[c]) + sum_c z[c] q[j][c].
-//    The first sum runs on the 16x16x32 f16 MFMA: codes enter as exact fp16
-//    subnormals, masked in place inside their packed word (a code at bit
-//    position p of a 16-bit half is worth u * 2^(p-24); the query side carries
-//    the compensating power of two), and the per-block folded query q*s is
-//    split into fp16 hi + lo halves that occupy separate MFMA columns (head j
-//    hi in column j, lo in column R + j), so one MFMA keeps ~22 bits.  q2k
-//    splits level(u) = c0 + c1 b0 + c2 b1 over the two code bits (exact for a
-//    symmetric 4-level grid).  The zero-point sum is a 64-lane reduction.
+// channel, v = u*s + z per token and 32-channel group; q2k pull-request page,
+// "Summary": k = level(u)*rms, v = (u - 8)*s):
+//  * scores: S[t][j] = sum_c u[t][c] * (q[j][c] s[c]) + sum_c z[c] q[j][c].
+//    The first sum runs on the 16x16x32 f16 MFMA.  Codes enter as exact fp16
+//    subnormals masked in place inside their packed word (a code at bit p of a
+//    16-bit half is worth u * 2^(p-24)); the query side is the exact product
+//    q*s of two fp16 pairs split into an fp16 hi half (column j) and lo half
+//    (column R + j) with one packed multiply and one packed fma, both then
+//    scaled by 2^-p, so the MFMA keeps ~22 bits.  q2k splits level(u) = c0 + c1 b0 + c2 b1 over the
+//    two code bits (exact for a symmetric 4-level grid) into two accumulators
+//    that share the query operand.  The zero-point (q2k: c0) sum is a packed
+//    dot product per lane, summed over the wave through LDS.
 //  * online softmax in log2 units on 64 lanes (scores staged through LDS so
-//    every lane works on live (head, token) pairs).
+//    every lane holds one (head, token pair)); the row maximum is reduced only
+//    when some score exceeds the running maximum, and the denominators stay per
+//    lane until the end of the split.
 //  * out^T[c][j] += sum_t u[t][c] * (p[j][t] s[t][g]) on the MFMA (V codes are
-//    stored in this operand order), weights split hi/lo into columns as above;
-//    the zero-point term sum_t p z is accumulated in fp32.
-// Four waves per workgroup take interleaved blocks of the split and merge in
-// LDS; the workgroup writes one partial.
+//    stored in this operand order); the weights times the V scale are split
+//    hi/lo the same way (packed fp16 product of fp16 halves of p and the fp16
+//    scale); the zero-point term sum_t p z is a packed dot product per lane.
+// Four waves per workgroup take interleaved blocks of the split, each with the
+// next block in flight while it computes one, and merge in LDS; the workgroup
+// writes one partial.
 //
-// Rounding: only this file's device code may contract a*b+c into one FMA; the
-// result is within the same error budget (every product here feeds a sum).
-// Range: the fp16 halves hold q*s*scale*log2(e) times at most 2^7 and V scale
-// times at most 2^6; inputs whose products overflow fp16 there are outside the
-// domain of this path.
+// Rounding: this file may contract a*b+c into one fma (every product here
+// feeds a sum).  Range: the query operand holds q*s and the weight operand
+// p*s*2^(PV-p) (weights p <= 1, PV the largest V code position: 6 for 2-bit,
+// 4 for 4-bit, 0 for 8-bit codes), both in fp16: |q*s| must stay below 65504
+// and a V scale below 2^(16-PV).
 #include "decode_shared.h"
 
 #pragma clang fp contract(fast)
@@ -38,37 +45,48 @@ namespace kvq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 constexpr int FD = 128;       // head_dim of this path
 constexpr int NW = DNT / 64;  // waves per workgroup
+constexpr int FPR = 64;       // fp16 rows per fp16 workgroup
 
 __device__ __forceinline__ f4 mfma(const u4& a, const u4& b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0,
                                                 0, 0);
 }
+__device__ __forceinline__ h2 H2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+__device__ __forceinline__ uint32_t U32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 
-// Two fp32 values as fp16 hi halves (round toward zero) and the fp16 remainder.
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const half2 h = __builtin_bit_cast(half2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
-  const float r0 = x0 - (float)h.x, r1 = x1 - (float)h.y;
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
+// The exact product of two fp16 pairs as fp16 hi = rn(a*b) and lo = rn(a*b - hi).
+__device__ __forceinline__ void mul_split(h2 a, h2 b, uint32_t& hi, uint32_t& lo) {
+  const h2 h = a * b;
+  hi = U32(h);
+  lo = U32(__builtin_elementwise_fma(a, b, -h));
 }
+// (a*b) + c*b split the same way, for a value given as fp16 halves a + c.
+__device__ __forceinline__ void mul_split2(h2 a, h2 c, h2 b, uint32_t& hi, uint32_t& lo) {
+  const h2 h = a * b;
+  hi = U32(h);
+  lo = U32(__builtin_elementwise_fma(c, b, __builtin_elementwise_fma(a, b, -h)));
+}
+// a.x*b.x + a.y*b.y + acc in fp32.
+__device__ __forceinline__ float dot2(h2 a, h2 b, float acc) { return __builtin_amdgcn_fdot2(a, b, acc, false); }
 
 // fp16 half `hi` (0: bits 0..15, 1: bits 16..31) of a word, as fp32.
 __device__ __forceinline__ float h16(uint32_t w, int hi) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> (16 * hi)));
 }
 
-// 2^x on the transcendental unit (arguments here are <= 0; results below 2^-126 may flush to 0).
+// 2^x on the transcendental unit (results below 2^-126 may flush to 0; 2^-inf = 0).
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Row-of-16 all-reductions with DPP lane permutations (no LDS crossbar): quad xor 1, quad xor 2,
-// half-row mirror, row mirror.  Every lane of the row ends with the same value.
+// Row-of-16 all-reductions with DPP lane permutations: quad xor 1, quad xor 2, half-row mirror,
+// row mirror.  Every lane of the row ends with the same value.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
@@ -121,7 +139,7 @@ template <int B>
 constexpr int code_pos(int r) {
   return B == 2 ? 2 * r : B == 4 ? 4 * (r & 1) : 0;
 }
-// Single code bit `bit` (0 or 1) of 2-bit codes in place: element pair r sits at 2r + bit.
+// Single code bit BIT (0 or 1) of 2-bit codes in place: element pair r sits at bit 2r + BIT.
 template <int BIT>
 __device__ __forceinline__ u4 plane_a(const uint32_t* d, int k) {
   const uint32_t w = (k & 1) ? d[k >> 1] >> 8 : d[k >> 1];
@@ -133,168 +151,171 @@ __device__ __forceinline__ u4 plane_a(const uint32_t* d, int k) {
   return r;
 }
 
-template <int R, int NPLANE>
+template <int R>
 struct alignas(16) FastWave {
   static constexpr int NC = 2 * R;  // MFMA columns in use: hi halves of heads 0..R-1, then lo halves
   // Rows are padded by 16 bytes so that the 16 column lanes of an MFMA operand read (and the
   // 16-byte score stores) fall on distinct LDS banks.
   union {
-    uint32_t qb[NPLANE][NC][FD / 2 + 4];  // folded query: [code plane][column][channel pair]
-    float o[R][FD];                       // wave output for the workgroup merge
+    uint32_t qb[NC][FD / 2 + 4];  // query operand: [column][channel pair]
+    float o[R][FD];               // wave output for the workgroup merge
   } x;
-  float ps[NC][G + 4];                    // raw score columns of the current block
-  float kp[R][64 + 4];                    // zero-point term partials per head and compact lane
-  uint32_t ab[4][NC][4 * 4 + 4];          // weights x V scale: [group][column][4 * token group + pair]
+  float ps[NC][G + 4];            // raw score columns of the current block
+  float kp[R][64 + 4];            // zero-point (q2k: c0) term per head and lane
+  uint32_t ab[4][NC][4 * 4 + 4];  // weights x V scale: [group][column][4 * token group + pair]
   float f[R], zt[R][4], m[R], l[R];
 };
-template <int R, int NPLANE>
+template <int R>
 struct FastSmem {
-  FastWave<R, NPLANE> w[NW];
+  FastWave<R> w[NW];
   int sinks[MAX_SINK];  // committed sink positions (< P) of this batch element
   int nsinks;
 };
+// LDS of an fp16-row workgroup (shares the allocation of the bulk workgroups).
+template <int R>
+struct FpSmem {
+  uint32_t q[R][FD / 2];    // query, fp16 pairs
+  float sc[R][FPR];         // scores, then weights, of the workgroup's rows
+  float red[NW][R][FD];     // per row group value sums
+  float m[R], l[R];
+  int spos[MAX_SINK], sslot[MAX_SINK];
+  int nsink;
+};
+template <int R>
+union DecSmem {
+  FastSmem<R> bulk;
+  FpSmem<R> fp;
+};
 
-// 8 consecutive input elements (fp16 or fp32) starting at element i (a multiple of 8), as fp32.
-__device__ __forceinline__ void ld8(const void* p, int64_t i, int in_f32, float* o) {
-  if (in_f32) {
-    const f4* q = reinterpret_cast<const f4*>(static_cast<const float*>(p) + i);
-    const f4 x = q[0], y = q[1];
-    o[0] = x[0], o[1] = x[1], o[2] = x[2], o[3] = x[3], o[4] = y[0], o[5] = y[1], o[6] = y[2], o[7] = y[3];
-  } else {
-    const u4 w = *reinterpret_cast<const u4*>(static_cast<const _Float16*>(p) + i);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      o[2 * k] = h16(ww[k], 0);
-      o[2 * k + 1] = h16(ww[k], 1);
-    }
-  }
-}
-// 2 consecutive input elements starting at element i (even), as fp32.
-__device__ __forceinline__ void ld2(const void* p, int64_t i, int in_f32, float* o) {
-  if (in_f32) {
-    const float2 x = *reinterpret_cast<const float2*>(static_cast<const float*>(p) + i);
-    o[0] = x.x, o[1] = x.y;
-  } else {
-    const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(p) + i);
-    o[0] = h16(w, 0), o[1] = h16(w, 1);
-  }
-}
-
-// What one lane reads from a block record (K and V parts of the next block are in flight while
-// the current one is computed).
-template <int KB>
-struct KPart {
+// What one lane reads from a block record.
+template <int KB, int VB>
+struct Blk {
   uint32_t kd[2][KB];  // K code rows i16 and 16 + i16, channels 32*kg .. 32*kg + 31
   uint32_t ks, kz;     // K scale (q2k: rms) and zero of channels 2*lane, 2*lane + 1
-};
-template <int VB>
-struct VPart {
-  uint32_t vd[2 * VB];  // V code chunk `lane`
-  u4 vs, vz;            // V scale and zero of tokens 2*tp, 2*tp + 1, groups 0..3
+  uint32_t vd[2 * VB]; // V code chunk `lane`
+  u4 vs, vz;           // V scale and zero of tokens 2*i16, 2*i16 + 1: [group][token] fp16
 };
 
-template <bool Q2K, int KB>
-__device__ __forceinline__ void load_k(KPart<KB>& d, const uint8_t* rec, const LayerView& lv, int lane) {
+// Per-lane byte offsets, inside a block record, of what load_blk reads.
+struct BlkOffs {
+  uint32_t k[2], ks, kz, v, vs, vz;
+};
+template <int KB, int VB>
+__device__ __forceinline__ BlkOffs blk_offsets(const LayerView& lv, int lane) {
   const int i16 = lane & 15, kg = lane >> 4;
+  BlkOffs o;
+#pragma unroll
+  for (int tau = 0; tau < 2; ++tau) o.k[tau] = (uint32_t)(lv.k_codes + (16 * tau + i16) * (FD * KB / 8) + kg * 4 * KB);
+  o.ks = (uint32_t)(lv.k_meta + 4 * lane);
+  o.kz = (uint32_t)(lv.k_meta + 2 * FD + 4 * lane);
+  o.v = (uint32_t)(lv.v_codes + lane * 8 * VB);
+  o.vs = (uint32_t)(lv.v_meta + 16 * i16);
+  o.vz = (uint32_t)(lv.v_meta + 2 * G * (FD / 32) + 16 * i16);
+  return o;
+}
+
+// One block record into registers: buffer loads from the stream's ring with the record's byte
+// offset in a scalar register and fixed per-lane offsets (no address arithmetic per block).
+template <bool Q2K, int KB, int VB>
+__device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t rs, uint32_t rec_off,
+                                         const BlkOffs& o) {
+  // the loads of one record stay together and in this order (scheduling barriers), so the wait
+  // counts the compiler derives for each block are the count of loads issued after it
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    const uint8_t* src = rec + lv.k_codes + (16 * tau + i16) * (FD * KB / 8) + kg * 4 * KB;
     if constexpr (KB == 2) {
-      const u2 x = *reinterpret_cast<const u2*>(src);
+      const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k[tau], rec_off, 0);
       d.kd[tau][0] = x.x, d.kd[tau][1] = x.y;
     } else {
 #pragma unroll
       for (int k = 0; k < KB / 4; ++k) {
-        const u4 x = reinterpret_cast<const u4*>(src)[k];
+        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, o.k[tau] + 16 * k, rec_off, 0);
         d.kd[tau][4 * k] = x.x, d.kd[tau][4 * k + 1] = x.y, d.kd[tau][4 * k + 2] = x.z, d.kd[tau][4 * k + 3] = x.w;
       }
     }
   }
-  d.ks = reinterpret_cast<const uint32_t*>(rec + lv.k_meta)[lane];
-  d.kz = Q2K ? 0u : reinterpret_cast<const uint32_t*>(rec + lv.k_meta + 2 * FD)[lane];
-}
-
-template <bool Q2K, int VB>
-__device__ __forceinline__ void load_v(VPart<VB>& d, const uint8_t* rec, const LayerView& lv, int lane) {
-  const u4* src = reinterpret_cast<const u4*>(rec + lv.v_codes + lane * 8 * VB);
+  d.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, o.ks, rec_off, 0);
+  d.kz = Q2K ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rs, o.kz, rec_off, 0);
 #pragma unroll
   for (int k = 0; k < VB / 2; ++k) {
-    const u4 x = src[k];
+    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * k, rec_off, 0);
     d.vd[4 * k] = x.x, d.vd[4 * k + 1] = x.y, d.vd[4 * k + 2] = x.z, d.vd[4 * k + 3] = x.w;
   }
-  d.vs = *reinterpret_cast<const u4*>(rec + lv.v_meta + 16 * (lane & 15));
-  if constexpr (!Q2K) d.vz = *reinterpret_cast<const u4*>(rec + lv.v_meta + 2 * G * (FD / 32) + 16 * (lane & 15));
+  d.vs = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vs, rec_off, 0);
+  if constexpr (!Q2K) d.vz = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vz, rec_off, 0);
   else d.vz = u4{0, 0, 0, 0};
+  __builtin_amdgcn_sched_barrier(0);
 }
 
-// One 32-token block of the wave: scores, online softmax, value accumulation.
 template <int FMT, int KB, int VB, int R>
-struct BlockState {
+struct Fast {
   static constexpr bool Q2K = FMT == KVQ_FMT_Q2K;
-  static constexpr int NPLANE = Q2K ? 2 : 1;
+  static constexpr int NC = 2 * R;
   static constexpr int NPL = R <= 4 ? 1 : R / 4;  // (head, token pair) slots per lane in the compact phase
-  static constexpr int PK = Q2K ? 7 : code_pos<KB>(3);  // largest in-place K code position
-  static constexpr int PV = code_pos<VB>(3);            // largest in-place V code position
-  float qc[R][2];        // query channels 2*lane, 2*lane + 1 of every head, log2 units
-  float fa, fb;          // K fold factors of this lane (plane 0 / plane 1, q2k levels included)
-  float fv;              // V weight factor of this lane's token pair
-  float m_[NPL], l_[NPL], zacc[NPL][4];
+  static constexpr int NKA = Q2K ? 2 : 1;         // K accumulators per token tile (q2k: one per code bit)
+};
+
+// Per-lane state of a wave over its blocks.
+template <int FMT, int KB, int VB, int R>
+struct State {
+  using F = Fast<FMT, KB, VB, R>;
+  h2 q2[R];             // query channels 2*lane, 2*lane + 1 (fp16)
+  h2 fa2;               // 2^-pos of their K element pair
+  float cs, kc;         // score = fma(raw, cs, kappa * kc), log2 units
+  float lf, ifv;        // -log2 and 2^ of the V position factor of this lane's token pair
+  float m_[F::NPL], lfm[F::NPL], l_[F::NPL], zacc[F::NPL][4];
   f4 acc[8];
 };
 
 template <int FMT, int KB, int VB, int R>
-__device__ __forceinline__ void block_step(BlockState<FMT, KB, VB, R>& S,
-                                           FastWave<R, BlockState<FMT, KB, VB, R>::NPLANE>& W,
-                                           const int* sinks, const KPart<KB>& kc, const VPart<VB>& vp, int blk,
-                                           int blo, int bhi, int sblk, int nsink, float c0, int lane) {
-  using St = BlockState<FMT, KB, VB, R>;
-  constexpr bool Q2K = St::Q2K;
-  constexpr int NPL = St::NPL, NC = 2 * R;
-  constexpr float SK = (float)(1u << (24 - St::PK));
+__device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>& W, const int* sinks,
+                                           const Blk<KB, VB>& d, int blk, int blo, int bhi, int sblk, int nsink,
+                                           float q2k_w, int lane) {
+  using F = Fast<FMT, KB, VB, R>;
+  constexpr bool Q2K = F::Q2K;
+  constexpr int NPL = F::NPL;
   const int i16 = lane & 15, kg = lane >> 4, tp = i16;
-  // MFMA column of this lane; padding lanes repeat the last column, so their score stores repeat
-  // its values
-  const int col = i16 < NC ? i16 : NC - 1;
+  // MFMA column of this lane; padding lanes repeat the last column (identical values, identical stores)
+  const int col = i16 < F::NC ? i16 : F::NC - 1;
 
-  // ---- fold the per-channel K scale into the query (hi -> column j, lo -> column R + j) ----
+  // ---- query operand: the exact products q * s split hi (column j) / lo (R + j), times 2^-pos ----
   {
-    const float s0 = h16(kc.ks, 0), s1 = h16(kc.ks, 1);
-    const float z0 = Q2K ? c0 * s0 : h16(kc.kz, 0), z1 = Q2K ? c0 * s1 : h16(kc.kz, 1);
-    const float sa0 = s0 * S.fa, sa1 = s1 * S.fa;
+    const h2 s2 = H2(d.ks);
+    const h2 z2 = Q2K ? s2 : H2(d.kz);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       uint32_t h, l;
-      split2(S.qc[j][0] * sa0, S.qc[j][1] * sa1, h, l);
-      W.x.qb[0][j][lane] = h;
-      W.x.qb[0][R + j][lane] = l;
-      if constexpr (Q2K) {
-        split2(S.qc[j][0] * (s0 * S.fb), S.qc[j][1] * (s1 * S.fb), h, l);
-        W.x.qb[St::NPLANE - 1][j][lane] = h;
-        W.x.qb[St::NPLANE - 1][R + j][lane] = l;
-      }
-      W.kp[j][lane] = S.qc[j][0] * z0 + S.qc[j][1] * z1;
+      mul_split(S.q2[j], s2, h, l);
+      W.x.qb[j][lane] = U32(H2(h) * S.fa2);
+      W.x.qb[R + j][lane] = U32(H2(l) * S.fa2);
+      W.kp[j][lane] = dot2(S.q2[j], z2, 0.f);
     }
   }
   // ---- scores: raw MFMA columns to LDS ----
-  f4 c_[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+  {
+    f4 c0[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    f4 c1[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    const u4 b0 = *reinterpret_cast<const u4*>(&W.x.qb[0][col][16 * kg + 4 * st]);
-    if constexpr (Q2K) {
-      const u4 b1 = *reinterpret_cast<const u4*>(&W.x.qb[St::NPLANE - 1][col][16 * kg + 4 * st]);
+    for (int st = 0; st < 4; ++st) {
+      const u4 b = *reinterpret_cast<const u4*>(&W.x.qb[col][16 * kg + 4 * st]);
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
-        c_[tau] = mfma(plane_a<0>(kc.kd[tau], st), b0, c_[tau]);
-        c_[tau] = mfma(plane_a<1>(kc.kd[tau], st), b1, c_[tau]);
+        if constexpr (Q2K) {
+          c0[tau] = mfma(plane_a<0>(d.kd[tau], st), b, c0[tau]);
+          c1[tau] = mfma(plane_a<1>(d.kd[tau], st), b, c1[tau]);
+        } else {
+          c0[tau] = mfma(codes_a<KB>(d.kd[tau], st), b, c0[tau]);
+        }
       }
-    } else {
+    }
 #pragma unroll
-      for (int tau = 0; tau < 2; ++tau) c_[tau] = mfma(codes_a<KB>(kc.kd[tau], st), b0, c_[tau]);
+    for (int tau = 0; tau < 2; ++tau) {
+      f4 c = c0[tau];
+      if constexpr (Q2K) c = c0[tau] + c1[tau] * q2k_w;
+      *reinterpret_cast<f4*>(&W.ps[col][16 * tau + 4 * kg]) = c;
     }
   }
-#pragma unroll
-  for (int tau = 0; tau < 2; ++tau) *reinterpret_cast<f4*>(&W.ps[col][16 * tau + 4 * kg]) = c_[tau];
 
   // ---- compact online softmax and weights x V scale ----
   // tokens 2tp, 2tp+1 of the block; masked if outside [bulk_lo, bulk_hi) or a committed sink
@@ -310,79 +331,81 @@ __device__ __forceinline__ void block_step(BlockState<FMT, KB, VB, R>& S,
     }
   }
   const int t0 = 2 * tp, kgt = (t0 & 15) >> 2, et = ((t0 >> 4) << 2) | (t0 & 3);  // V operand position
-  bool resc = false;
-  float fp_[NPL], zb[NPL][4];  // rescale factor and this block's zero-point terms per slot
+  float y0[NPL], y1[NPL];
+  bool grow = false;
 #pragma unroll
   for (int p = 0; p < NPL; ++p) {
     const int jr = kg + 4 * p;
     const int j = jr < R ? jr : R - 1;  // lanes past the last head repeat it (identical stores)
     const f4 kq = *reinterpret_cast<const f4*>(&W.kp[j][4 * tp]);
-    const float kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3]));
-    const float2 hi = *reinterpret_cast<const float2*>(&W.ps[j][2 * tp]);
-    const float2 lo = *reinterpret_cast<const float2*>(&W.ps[R + j][2 * tp]);
-    const float sv0 = ok0 ? (hi.x + lo.x) * SK + kap : -INFINITY;
-    const float sv1 = ok1 ? (hi.y + lo.y) * SK + kap : -INFINITY;
-    const float mx = row_max16(fmaxf(sv0, sv1));
-    const float mold = S.m_[p];
-    const float mnew = fmaxf(mold, mx);
-    float f = 1.f, e0 = 0.f, e1 = 0.f;
-    if (mnew != -INFINITY) {
-      f = mold == -INFINITY ? 0.f : (mnew == mold ? 1.f : ex2(mold - mnew));
-      e0 = sv0 == -INFINITY ? 0.f : ex2(sv0 - mnew);
-      e1 = sv1 == -INFINITY ? 0.f : ex2(sv1 - mnew);
+    const float kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3])) * S.kc;
+    const f2 hi = *reinterpret_cast<const f2*>(&W.ps[j][2 * tp]);
+    const f2 lo = *reinterpret_cast<const f2*>(&W.ps[R + j][2 * tp]);
+    y0[p] = ok0 ? __builtin_fmaf(hi.x + lo.x, S.cs, kap) : -INFINITY;
+    y1[p] = ok1 ? __builtin_fmaf(hi.y + lo.y, S.cs, kap) : -INFINITY;
+    grow = grow || fmaxf(y0[p], y1[p]) > S.m_[p];
+  }
+  // a new running maximum somewhere in the wave: reduce the row maxima and rescale
+  const bool resc = __any(grow);
+  if (resc) {
+#pragma unroll
+    for (int p = 0; p < NPL; ++p) {
+      const int jr = kg + 4 * p;
+      const int j = jr < R ? jr : R - 1;
+      const float mold = S.m_[p];
+      const float mnew = fmaxf(mold, row_max16(fmaxf(y0[p], y1[p])));
+      const float f = mold == mnew ? 1.f : (mold == -INFINITY ? 0.f : ex2(mold - mnew));
+      S.m_[p] = mnew;
+      S.lfm[p] = mnew == -INFINITY ? 0.f : S.lf - mnew;
+      S.l_[p] *= f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) S.zacc[p][q] *= f;
+      if (tp == 0) W.f[j] = f;
     }
-    const float sum = row_sum16(e0 + e1);
-    S.l_[p] = S.l_[p] * f + sum;
-    S.m_[p] = mnew;
-    if (tp == 0) W.f[j] = f;
-    fp_[p] = f;
-    resc = resc || f != 1.f;
-    const float e0v = e0 * S.fv, e1v = e1 * S.fv;
+  }
+#pragma unroll
+  for (int p = 0; p < NPL; ++p) {
+    const int jr = kg + 4 * p;
+    const int j = jr < R ? jr : R - 1;
+    // weights times the V position factor of this token pair; masked tokens give 2^-inf = 0
+    const float e0 = ex2(y0[p] + S.lfm[p]), e1 = ex2(y1[p] + S.lfm[p]);
+    S.l_[p] = __builtin_fmaf(e0 + e1, S.ifv, S.l_[p]);
+    const h2 ph = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+    const h2 pl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(e0 - (float)ph.x, e1 - (float)ph.y));
+    const uint32_t vs[4] = {d.vs.x, d.vs.y, d.vs.z, d.vs.w};
+    const uint32_t vz[4] = {d.vz.x, d.vz.y, d.vz.z, d.vz.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      // vs / vz hold fp16 [t0: g0 g1 | g2 g3][t0+1: g0 g1 | g2 g3]
-      const float s_t0 = h16(q < 2 ? vp.vs.x : vp.vs.y, q & 1), s_t1 = h16(q < 2 ? vp.vs.z : vp.vs.w, q & 1);
+      const h2 s2 = H2(vs[q]);  // V scales of tokens t0, t0 + 1 in group q
       uint32_t h, l;
-      split2(e0v * s_t0, e1v * s_t1, h, l);
+      mul_split2(ph, pl, s2, h, l);
       W.ab[q][j][4 * kgt + (et >> 1)] = h;
       W.ab[q][R + j][4 * kgt + (et >> 1)] = l;
-      if constexpr (Q2K) {
-        zb[p][q] = -8.f * (e0 * s_t0 + e1 * s_t1);
-      } else {
-        const float z_t0 = h16(q < 2 ? vp.vz.x : vp.vz.y, q & 1);
-        const float z_t1 = h16(q < 2 ? vp.vz.z : vp.vz.w, q & 1);
-        zb[p][q] = e0 * z_t0 + e1 * z_t1;
-      }
+      const h2 z2 = Q2K ? s2 : H2(vz[q]);
+      S.zacc[p][q] = dot2(ph, z2, dot2(pl, z2, S.zacc[p][q]));
     }
   }
   // ---- values (rare: rescale the running sums to a new maximum first) ----
-  if (__any(resc)) {
-    const float fc = W.f[i16 & (R - 1)];
+  if (resc) {
+    const float fc = W.f[i16 % R];
 #pragma unroll
     for (int mu = 0; mu < 8; ++mu) S.acc[mu] *= fc;
-#pragma unroll
-    for (int p = 0; p < NPL; ++p)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) S.zacc[p][q] *= fp_[p];
   }
-#pragma unroll
-  for (int p = 0; p < NPL; ++p)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) S.zacc[p][q] += zb[p][q];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const u4 bq = *reinterpret_cast<const u4*>(&W.ab[q][col][4 * kg]);
 #pragma unroll
-    for (int mu = 2 * q; mu < 2 * q + 2; ++mu) S.acc[mu] = mfma(codes_a<VB>(vp.vd, mu), bq, S.acc[mu]);
+    for (int mu = 2 * q; mu < 2 * q + 2; ++mu) S.acc[mu] = mfma(codes_a<VB>(d.vd, mu), bq, S.acc[mu]);
   }
 }
 
 template <int FMT, int KB, int VB, int R>
-__device__ void fast_partial(const DecodeArgs& a, FastSmem<R, BlockState<FMT, KB, VB, R>::NPLANE>& F) {
-  using State = BlockState<FMT, KB, VB, R>;
-  constexpr bool Q2K = State::Q2K;
-  constexpr int NPL = State::NPL;
-  constexpr float SV = (float)(1u << (24 - State::PV));
+__device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
+  using Fc = Fast<FMT, KB, VB, R>;
+  using St = State<FMT, KB, VB, R>;
+  constexpr bool Q2K = Fc::Q2K;
+  constexpr int NPL = Fc::NPL;
+  constexpr int PV = code_pos<VB>(3);
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -391,37 +414,52 @@ __device__ void fast_partial(const DecodeArgs& a, FastSmem<R, BlockState<FMT, KB
   const int sigma = blockIdx.x, s = blockIdx.y, b = s / sh.Hkv, g = s % sh.Hkv;
   auto& W = F.w[wv];
 
-  const float qscale = a.scale * LOG2E;
-  const float c0 = Q2K ? lv.tables->q2k_lvl[0] : 1.f;
-  const float c1 = Q2K ? lv.tables->q2k_lvl[1] - lv.tables->q2k_lvl[0] : 1.f;
-  const float c2 = Q2K ? lv.tables->q2k_lvl[2] - lv.tables->q2k_lvl[0] : 1.f;
-  const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
-
+  const int first = sigma * a.blocks_per_split;
+  const int lastb = min(a.nblk, first + a.blocks_per_split);
+  const int blo = (int)a.bulk_lo, bhi = (int)a.bulk_hi;  // positions fit in int32 (checked on the host)
+  const int blkf = (int)a.blk_first;
+  const int slot0 = (int)(a.blk_first % lv.cap_b);  // ring slot of bulk block index 0
+  // the stream's ring as a buffer resource (every record offset fits in 32 bits: checked on the host)
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(lv.bulk + (int64_t)s * lv.cap_b * lv.rec), 0, (int)(lv.cap_b * lv.rec), 0x00020000);
+  const BlkOffs bo = blk_offsets<KB, VB>(lv, lane);
+  auto rec_of = [&](int bi) -> uint32_t {
+    bi = bi < lastb ? bi : lastb - 1;  // past the split: re-read its last block (a cache hit), never used
+    int sl = slot0 + bi;
+    if (sl >= lv.cap_b) sl -= lv.cap_b;
+    return (uint32_t)sl * (uint32_t)lv.rec;
+  };
   stage_sinks(a, b, F.sinks, nullptr, &F.nsinks);
-  State S;
-#pragma unroll
-  for (int j = 0; j < R; ++j) {
-    ld2(a.q, qrow + j * FD + 2 * lane, sh.in_f32, S.qc[j]);
-    S.qc[j][0] *= qscale;
-    S.qc[j][1] *= qscale;
+  St S;
+  const float al = a.scale * LOG2E;
+  float q2k_w = 0.f;
+  if constexpr (Q2K) {
+    const float c0 = lv.tables->q2k_lvl[0], c1 = lv.tables->q2k_lvl[1] - c0, c2 = lv.tables->q2k_lvl[2] - c0;
+    S.cs = ldexpf(c1 * al, 24);
+    S.kc = c0 * al;
+    q2k_w = c2 / (2.f * c1);  // the b1 accumulator carries an extra factor 2 (bit 2r + 1)
+  } else {
+    S.cs = ldexpf(al, 24);
+    S.kc = al;
   }
   {
-    // channels 2*lane, 2*lane+1 are element pair (lane & 3) of their K step; the V weights of tokens
-    // 2*i16, 2*i16+1 are element pair (et >> 1) of their token group
-    const int rk = lane & 3;
-    if constexpr (Q2K) {
-      S.fa = ldexpf(c1, State::PK - 2 * rk);
-      S.fb = ldexpf(c2, State::PK - 2 * rk - 1);
-    } else {
-      S.fa = ldexpf(1.f, State::PK - code_pos<KB>(rk));
-      S.fb = 0.f;
-    }
+    const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
+    const int pk = Q2K ? 2 * (lane & 3) : code_pos<KB>(lane & 3);
+    const _Float16 fa = (_Float16)ldexpf(1.f, -pk);
+    S.fa2 = h2{fa, fa};
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      S.q2[j] = H2(reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + j * FD)[lane]);
+    // weights carry 2^(PV - pv): the V codes of this lane's token pair sit at bit pv
     const int t0 = 2 * i16, et = ((t0 >> 4) << 2) | (t0 & 3);
-    S.fv = ldexpf(1.f, State::PV - code_pos<VB>(et >> 1));
+    const int pv = code_pos<VB>(et >> 1);
+    S.lf = (float)(PV - pv);
+    S.ifv = ldexpf(1.f, pv - PV);
   }
 #pragma unroll
   for (int p = 0; p < NPL; ++p) {
     S.m_[p] = -INFINITY;
+    S.lfm[p] = 0.f;
     S.l_[p] = 0.f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) S.zacc[p][q] = 0.f;
@@ -432,40 +470,26 @@ __device__ void fast_partial(const DecodeArgs& a, FastSmem<R, BlockState<FMT, KB
 
   const int nsink = __builtin_amdgcn_readfirstlane(F.nsinks);
   const int sblk = lane < nsink ? F.sinks[lane] / G : -1;  // block of sink `lane`
-  const int first = sigma * a.blocks_per_split;
-  const int lastb = min(a.nblk, first + a.blocks_per_split);
-  const int blo = (int)a.bulk_lo, bhi = (int)a.bulk_hi;  // positions fit in int32 (checked on the host)
-  const int blkf = (int)a.blk_first;
-  const int slot0 = (int)(a.blk_first % lv.cap_b);  // ring slot of bulk block index 0
-  const uint8_t* sbase = lv.bulk + (int64_t)s * lv.cap_b * lv.rec;
-  auto rec_of = [&](int bi) {
-    int sl = slot0 + bi;
-    if (sl >= lv.cap_b) sl -= lv.cap_b;
-    return sbase + (int64_t)sl * lv.rec;
-  };
 
-  // ping-pong buffers: the next block of this wave is in flight while the current one is computed
-  KPart<KB> k0, k1;
-  VPart<VB> v0, v1;
+  // Two register buffers: the next block of this wave is in flight while the current one is
+  // computed (a deeper ring costs the registers of a third wave per SIMD, which hides more).  The
+  // ring is primed only after every other load of the prologue has landed, so the loop is entered
+  // with exactly the loads in flight that its back edge carries (the compiler's wait counts then
+  // stay exact).
+  Blk<KB, VB> d0, d1;
   int bi = first + wv;
   if (bi < lastb) {
-    load_k<Q2K>(k0, rec_of(bi), lv, lane);
-    load_v<Q2K>(v0, rec_of(bi), lv, lane);
-  }
-  while (bi < lastb) {
-    if (bi + NW < lastb) {
-      load_k<Q2K>(k1, rec_of(bi + NW), lv, lane);
-      load_v<Q2K>(v1, rec_of(bi + NW), lv, lane);
+    load_blk<Q2K>(d0, rs, rec_of(bi), bo);
+    while (true) {
+      load_blk<Q2K>(d1, rs, rec_of(bi + NW), bo);
+      block_step(S, W, F.sinks, d0, blkf + bi, blo, bhi, sblk, nsink, q2k_w, lane);
+      bi += NW;
+      if (bi >= lastb) break;
+      load_blk<Q2K>(d0, rs, rec_of(bi + NW), bo);
+      block_step(S, W, F.sinks, d1, blkf + bi, blo, bhi, sblk, nsink, q2k_w, lane);
+      bi += NW;
+      if (bi >= lastb) break;
     }
-    block_step(S, W, F.sinks, k0, v0, blkf + bi, blo, bhi, sblk, nsink, c0, lane);
-    bi += NW;
-    if (bi >= lastb) break;
-    if (bi + NW < lastb) {
-      load_k<Q2K>(k0, rec_of(bi + NW), lv, lane);
-      load_v<Q2K>(v0, rec_of(bi + NW), lv, lane);
-    }
-    block_step(S, W, F.sinks, k1, v1, blkf + bi, blo, bhi, sblk, nsink, c0, lane);
-    bi += NW;
   }
 
   // ---- wave results: zero-point term, output (column j plus column R + j), (m, l) ----
@@ -473,16 +497,19 @@ __device__ void fast_partial(const DecodeArgs& a, FastSmem<R, BlockState<FMT, KB
 #pragma unroll
   for (int p = 0; p < NPL; ++p) {
     const int jr = kg + 4 * p;
+    const float lsum = row_sum16(S.l_[p]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float z = row_sum16(S.zacc[p][q]);
+      float z = row_sum16(S.zacc[p][q] * S.ifv);
+      if constexpr (Q2K) z = -8.f * z;
       if (jr < R && tp == 0) W.zt[jr][q] = z;
     }
     if (jr < R && tp == 0) {
       W.m[jr] = S.m_[p];
-      W.l[jr] = S.l_[p];
+      W.l[jr] = lsum;
     }
   }
+  const float SV = ldexpf(1.f, 24 - PV);  // V codes entered as u * 2^(pv - 24), the weights carried 2^(PV - pv)
 #pragma unroll
   for (int mu = 0; mu < 8; ++mu) {
     f4 lo;
@@ -506,7 +533,7 @@ __device__ void fast_partial(const DecodeArgs& a, FastSmem<R, BlockState<FMT, KB
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w)
-      if (F.w[w].m[j] != -INFINITY) v += F.w[w].x.o[j][c] * exp2f(F.w[w].m[j] - M);
+      if (F.w[w].m[j] != -INFINITY) v += F.w[w].x.o[j][c] * ex2(F.w[w].m[j] - M);
     part[j * (FD + 2) + 2 + c] = v;
   }
   if (tid < R) {
@@ -515,14 +542,123 @@ __device__ void fast_partial(const DecodeArgs& a, FastSmem<R, BlockState<FMT, KB
     for (int w = 0; w < NW; ++w) M = fmaxf(M, F.w[w].m[tid]);
 #pragma unroll
     for (int w = 0; w < NW; ++w)
-      if (F.w[w].m[tid] != -INFINITY) L += F.w[w].l[tid] * exp2f(F.w[w].m[tid] - M);
+      if (F.w[w].m[tid] != -INFINITY) L += F.w[w].l[tid] * ex2(F.w[w].m[tid] - M);
     part[tid * (FD + 2)] = M;
     part[tid * (FD + 2) + 1] = L;
   }
 }
 
-// Waves per SIMD the register allocation targets: 3 where the kernel fits 168 VGPRs without spilling
-// (2-bit K codes, at most 4 heads per KV head), else 2.
+// Partial of fp16 rows [64 f, 64 f + 64) of the stream's list: window rows [bulk_hi, P) (the ones
+// that are committed sinks masked: the pool holds them), then the committed sinks in slot order.
+// Scores: 4 lanes per row (32 channels each, packed fp16 dot products); weights per head over the
+// workgroup's rows; values: one channel pair per lane, rows split over the 4 waves.
+template <int R>
+__device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
+  const Shape sh = a.sh;
+  const LayerView lv = a.lv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int s = blockIdx.y, b = s / sh.Hkv, g = s % sh.Hkv;
+  const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
+  for (int idx = tid; idx < R * FD / 2; idx += DNT)
+    F.q[idx / (FD / 2)][idx % (FD / 2)] = reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow)[idx];
+  stage_sinks(a, b, F.spos, F.sslot, &F.nsink);
+  __syncthreads();
+  const int nwin = (int)(a.P - a.bulk_hi);  // positions fit in int32
+  const int nfp = nwin + F.nsink;
+  const int r0 = f * FPR, nr = max(0, min(FPR, nfp - r0));
+  const float al = a.scale * LOG2E;
+
+  auto row_ptr = [&](int i, bool v_side) -> const uint16_t* {  // fp16 row i of the list (i < nfp)
+    if (i < nwin) {
+      const int64_t p = a.bulk_hi + i;
+      return (v_side ? lv.win_v : lv.win_k) + ((int64_t)s * sh.R + p % sh.R) * FD;
+    }
+    return (v_side ? lv.sink_v : lv.sink_k) + ((int64_t)s * sh.n_sink + F.sslot[i - nwin]) * FD;
+  };
+  // ---- scores ----
+  {
+    const int lr = tid >> 2, qq = tid & 3, i = r0 + lr;
+    bool ok = lr < nr;
+    float acc[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[j] = 0.f;
+    if (ok) {
+      if (i < nwin)
+        for (int q = 0; q < F.nsink; ++q) ok = ok && F.spos[q] != a.bulk_hi + i;
+      const u4* kr = reinterpret_cast<const u4*>(row_ptr(i, false) + 32 * qq);
+      u4 kw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kw[k] = kr[k];
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u4 qw = *reinterpret_cast<const u4*>(&F.q[j][16 * qq + 4 * k]);
+          acc[j] = dot2(H2(qw.x), H2(kw[k].x), acc[j]);
+          acc[j] = dot2(H2(qw.y), H2(kw[k].y), acc[j]);
+          acc[j] = dot2(H2(qw.z), H2(kw[k].z), acc[j]);
+          acc[j] = dot2(H2(qw.w), H2(kw[k].w), acc[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float v = acc[j];
+      v += dpp<0xB1>(v);
+      v += dpp<0x4E>(v);
+      if (qq == 0) F.sc[j][lr] = ok ? v * al : -INFINITY;
+    }
+  }
+  __syncthreads();
+  // ---- weights per head ----
+  for (int j = wv; j < R; j += NW) {
+    const float x = F.sc[j][lane];
+    float M = x;
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float p = x == -INFINITY ? 0.f : ex2(x - M);
+    F.sc[j][lane] = p;
+    float L = p;
+    for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
+    if (lane == 0) {
+      F.m[j] = M;
+      F.l[j] = L;
+    }
+  }
+  __syncthreads();
+  // ---- values ----
+  {
+    float acc[R][2];
+#pragma unroll
+    for (int j = 0; j < R; ++j) acc[j][0] = acc[j][1] = 0.f;
+    for (int lr = wv; lr < nr; lr += NW) {
+      const uint32_t w = reinterpret_cast<const uint32_t*>(row_ptr(r0 + lr, true))[lane];
+      const float v0 = h16(w, 0), v1 = h16(w, 1);
+#pragma unroll
+      for (int j = 0; j < R; ++j) {
+        const float p = F.sc[j][lr];
+        acc[j][0] = __builtin_fmaf(p, v0, acc[j][0]);
+        acc[j][1] = __builtin_fmaf(p, v1, acc[j][1]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) *reinterpret_cast<f2*>(&F.red[wv][j][2 * lane]) = f2{acc[j][0], acc[j][1]};
+  }
+  __syncthreads();
+  float* part = a.ws + ((int64_t)s * a.nparts + a.splits + f) * R * (FD + 2);
+  for (int idx = tid; idx < R * FD; idx += DNT) {
+    const int j = idx / FD, c = idx % FD;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += F.red[w][j][c];
+    part[j * (FD + 2) + 2 + c] = v;
+  }
+  if (tid < R) {
+    part[tid * (FD + 2)] = F.m[tid];
+    part[tid * (FD + 2) + 1] = F.l[tid];
+  }
+}
+
+// Waves per SIMD the register allocation targets.
 template <int FMT, int KB, int VB, int R>
 constexpr int waves_target() {
   return (R <= 4 && KB == 2) ? 3 : 2;
@@ -531,19 +667,56 @@ constexpr int waves_target() {
 template <int FMT, int KB, int VB, int R>
 __global__ __launch_bounds__(DNT) __attribute__((amdgpu_waves_per_eu(waves_target<FMT, KB, VB, R>())))
 void k_decode_fast(DecodeArgs a) {
-  __shared__ FastSmem<R, BlockState<FMT, KB, VB, R>::NPLANE> S;
-  fast_partial<FMT, KB, VB, R>(a, S);
+  __shared__ DecSmem<R> S;
+  if ((int)blockIdx.x < a.splits) bulk_partial<FMT, KB, VB, R>(a, S.bulk);
+  else fp16_partial<R>(a, S.fp, (int)blockIdx.x - a.splits);
+}
+
+// Fixed-order merge of the partials of one (stream, query head): bulk splits, then fp16 groups.
+template <int R>
+__global__ __launch_bounds__(FD) void k_merge_parts(DecodeArgs a) {
+  const int s = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
+  const int b = s / a.sh.Hkv, g = s % a.sh.Hkv;
+  const float* P0 = a.ws + (int64_t)s * a.nparts * R * (FD + 2) + j * (FD + 2);
+  const int np = a.nparts;
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int q = 0; q < np; ++q) M = fmaxf(M, P0[(int64_t)q * R * (FD + 2)]);
+  float L = 0.f, v = 0.f;
+#pragma unroll 8
+  for (int q = 0; q < np; ++q) {
+    const float* pq = P0 + (int64_t)q * R * (FD + 2);
+    const float mq = pq[0];
+    const float w = mq == -INFINITY ? 0.f : ex2(mq - M);
+    L = __builtin_fmaf(pq[1], w, L);
+    v = __builtin_fmaf(pq[2 + c], w, v);
+  }
+  a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * FD + c] = v / L;
 }
 
 template <int FMT, int KB, int VB>
 hipError_t launch_r(const DecodeArgs& a, hipStream_t st) {
   const int r = a.sh.Hq / a.sh.Hkv;
-  dim3 grid(a.splits, a.sh.B * a.sh.Hkv);  // bulk splits only: the merge kernel reads the fp16 rows
+  const int S = a.sh.B * a.sh.Hkv;
+  dim3 grid(a.nparts, S);
+  dim3 mgrid(S, r);
   switch (r) {
-    case 1: hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 1>), grid, dim3(DNT), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 2>), grid, dim3(DNT), 0, st, a); break;
-    case 4: hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 4>), grid, dim3(DNT), 0, st, a); break;
-    case 8: hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 8>), grid, dim3(DNT), 0, st, a); break;
+    case 1:
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 1>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<1>), mgrid, dim3(FD), 0, st, a);
+      break;
+    case 2:
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 2>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<2>), mgrid, dim3(FD), 0, st, a);
+      break;
+    case 4:
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 4>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<4>), mgrid, dim3(FD), 0, st, a);
+      break;
+    case 8:
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 8>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<8>), mgrid, dim3(FD), 0, st, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -581,10 +754,13 @@ int fast_resident_slots(const Shape& sh) {
   return 0;
 }
 
-// Launches the MFMA kernel; the host only sets DecodeArgs::fast for shapes it covers.
+// Rows of fp16 partials one fp16 workgroup of the MFMA kernel scores.
+int fast_fp16_rows_per_group() { return FPR; }
+
+// Launches the MFMA kernel and its merge; the host only sets DecodeArgs::fast for shapes it covers.
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
-  if (sh.D != FD || a.splits == 0) return hipErrorInvalidValue;
+  if (sh.D != FD || a.nparts == 0 || sh.in_f32) return hipErrorInvalidValue;
   if (sh.fmt == KVQ_FMT_Q2K) return launch_r<KVQ_FMT_Q2K, 2, 4>(a, st);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2>(a, st);

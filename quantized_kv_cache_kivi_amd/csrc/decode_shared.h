@@ -71,8 +71,9 @@ __device__ __forceinline__ float v_val(const Shape& sh, const uint8_t* rec, cons
   const uint32_t u = code_at(rec + lv.v_codes, w, k, sh.vb);
   const uint16_t* vm = reinterpret_cast<const uint16_t*>(rec + lv.v_meta);
   const int ng = sh.D / 32, g = c >> 5;
-  if (sh.fmt == KVQ_FMT_KIVI) return (float)u * f16_val(vm[t * ng + g]) + f16_val(vm[G * ng + t * ng + g]);
-  if (sh.fmt == KVQ_FMT_Q2K) return ((float)u - 8.f) * f16_val(vm[t * ng + g]);
+  const int mi = v_meta_idx(t, g, ng);
+  if (sh.fmt == KVQ_FMT_KIVI) return (float)u * f16_val(vm[mi]) + f16_val(vm[G * ng + mi]);
+  if (sh.fmt == KVQ_FMT_Q2K) return ((float)u - 8.f) * f16_val(vm[mi]);
   return lv.tables->v_cen[u];
 }
 

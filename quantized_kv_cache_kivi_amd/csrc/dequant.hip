@@ -71,14 +71,15 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
     for (int e = 0; e < 2; ++e) {
       const int c = act ? 2 * lane + e : 0;
       if (sh.fmt == KVQ_FMT_KIVI) {
-        const float sc = is_k ? f16_val(m[c]) : f16_val(m[t * ng + (c >> 5)]);
-        const float z = is_k ? f16_val(m[D + c]) : f16_val(m[G * ng + t * ng + (c >> 5)]);
+        const int mi = v_meta_idx(t, c >> 5, ng);
+        const float sc = is_k ? f16_val(m[c]) : f16_val(m[mi]);
+        const float z = is_k ? f16_val(m[D + c]) : f16_val(m[G * ng + mi]);
         const float prod = (float)u[e] * sc;
         x[e] = prod + z;
       } else if (is_k) {
         x[e] = lv.tables->q2k_lvl[u[e]] * f16_val(m[c]);
       } else {
-        x[e] = ((float)u[e] - 8.f) * f16_val(m[t * ng + (c >> 5)]);
+        x[e] = ((float)u[e] - 8.f) * f16_val(m[v_meta_idx(t, c >> 5, ng)]);
       }
     }
   }

@@ -43,6 +43,10 @@ __device__ __forceinline__ void v_code_pos(int t, int c, int D, int b, int* word
   *word = q * (D * b / 64) + s / per;
   *k = s % per;
 }
+// Index (in fp16 units) of the V scale or zero of token t, channel group g inside its section:
+// [t / 2][g][t % 2], so both tokens of a pair sit side by side for every group.
+__device__ __forceinline__ int v_meta_idx(int t, int g, int ng) { return (t >> 1) * 2 * ng + 2 * g + (t & 1); }
+
 // Token of element e of V token group kg.
 __device__ __forceinline__ int v_tok(int kg, int e) { return 16 * (e >> 2) + 4 * kg + (e & 3); }
 

@@ -139,7 +139,7 @@ kvq_layout make_layout(const kvq_config& c) {
 // Shapes the MFMA decode path covers (the generic kernel takes the rest).
 bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
-  return c.head_dim == 128 && (r == 1 || r == 2 || r == 4 || r == 8) &&
+  return c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && (r == 1 || r == 2 || r == 4 || r == 8) &&
          (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits));
 }
 
@@ -180,6 +180,17 @@ int max_splits(const kvq_config& c) {
   const int nblk = effective_capacity(c) / G;
   if (fast_path(c)) return std::max(1, std::min(64, nblk / 4));
   return splits_for(c, nblk, 0);
+}
+
+// fp16-row partials of a decode call: the MFMA path scores the window rows and the sinks in groups
+// of fast_fp16_rows_per_group() rows; TurboQuant's generic kernel in one partial; other formats in
+// the merge kernel.
+int fp16_parts(const kvq_config& c, int64_t rows) {
+  if (fast_path(c)) {
+    const int per = fast_fp16_rows_per_group();
+    return (int)((rows + per - 1) / per);
+  }
+  return c.format == KVQ_FMT_TQ ? 1 : 0;
 }
 
 }  // namespace
@@ -269,7 +280,8 @@ size_t kvq_workspace_bytes(const kvq_config* cfg) {
   if (check(cfg) != KVQ_OK) return 0;
   const size_t streams = (size_t)cfg->batch * cfg->n_kv_heads;
   const size_t r = cfg->n_q_heads / cfg->n_kv_heads;
-  return streams * (size_t)(max_splits(*cfg) + 1) * r * (size_t)(cfg->head_dim + 2) * sizeof(float);
+  const int parts = max_splits(*cfg) + std::max(1, fp16_parts(*cfg, (int64_t)cfg->residual + cfg->n_sink));
+  return streams * (size_t)parts * r * (size_t)(cfg->head_dim + 2) * sizeof(float);
 }
 
 kvq_status kvq_create(const kvq_config* cfg, void* dev_buf, size_t dev_bytes, void* stream, kvq_cache** out) {
@@ -417,8 +429,11 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
     a.splits = 0;
     a.blocks_per_split = 0;
   }
-  a.fast = fast_path(cf) && a.splits > 0;
-  a.nparts = a.splits + (cf.format == KVQ_FMT_TQ ? 1 : 0);
+  a.fast = fast_path(cf);
+  // fp16 rows: window rows [bulk_hi, P) and at most min(n_sink, P) committed sinks (the kernels read
+  // the committed count; groups past it write empty partials)
+  const int64_t fp_rows = (P - a.bulk_hi) + std::min<int64_t>(cf.n_sink, P);
+  a.nparts = a.splits + fp16_parts(cf, fp_rows);
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;

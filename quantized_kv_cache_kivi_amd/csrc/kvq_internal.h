@@ -77,8 +77,9 @@ struct DecodeArgs {
   int nblk;                  // bulk blocks
   int splits;                // bulk splits S (the fp16 split is index S)
   int blocks_per_split;
-  int fast;                  // 1: MFMA path (head_dim 128, KIVI equal widths or q2k, GQA ratio 1/2/4/8)
-  int nparts;                // partials per stream in the workspace (splits, plus 1 for TurboQuant's fp16 rows)
+  int fast;                  // 1: MFMA path (head_dim 128, fp16 input, KIVI equal widths or q2k, GQA 1/2/4/8)
+  int nparts;                // partials per stream in the workspace: bulk splits, then the fp16-row groups
+                             // (MFMA path: ceil(rows / 64); TurboQuant: 1; other formats: 0)
 };
 
 struct DequantArgs {
@@ -98,6 +99,8 @@ hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 // Workgroups of the MFMA decode kernel for this shape that the current device holds at once
 // (compute units x resident workgroups per unit); 0 if the shape has no MFMA kernel.
 int fast_resident_slots(const Shape& sh);
+// fp16 rows (window and sinks) one fp16 workgroup of the MFMA decode kernel takes.
+int fast_fp16_rows_per_group();
 
 // Host-side table generation (tables.cpp).
 void make_tables(const kvq_config& cfg, Tables* t);

@@ -107,6 +107,20 @@ def test_v_tile_hand_position():
     # bits 16+8 .. 16+11 of word 1 = byte 3, low nibble
 
 
+def test_v_meta_order_hand_position_and_roundtrip():
+    # token 5, group 2 of D = 128 (4 groups): pair 2, group 2, second of the pair -> 2*8 + 2*2 + 1 = 21
+    meta = np.zeros((32, 4), np.uint16)
+    meta[5, 2] = 0xABCD
+    flat = layout.pack_v_meta(meta)
+    assert list(np.flatnonzero(flat)) == [21] and flat[21] == 0xABCD
+    rng = np.random.default_rng(4)
+    for ng in (1, 2, 4):
+        m = rng.integers(0, 1 << 16, size=(3, 32, ng)).astype(np.uint16)
+        f = layout.pack_v_meta(m)
+        assert sorted(f.reshape(3, -1)[0].tolist()) == sorted(m[0].reshape(-1).tolist())
+        assert np.array_equal(layout.unpack_v_meta(f, ng), m)
+
+
 def test_record_bytes_per_token():
     # bytes per token per KV head (codes + metadata amortised over the 32-token block)
     assert layout.record_sections("kivi", 128, 2, 2)[2] == 96 * 32
