@@ -20,6 +20,19 @@ namespace {
 constexpr int NT = 256;
 constexpr int XP = MAX_D + 1;  // padded LDS row (bank spread for per-row loops)
 
+// min / max over the 32 lanes of a half-wave (every lane of the half ends with the result)
+__device__ __forceinline__ float half_min(float x) {
+  for (int off = 1; off < 32; off <<= 1) x = fminf(x, __shfl_xor(x, off));
+  return x;
+}
+__device__ __forceinline__ float half_max(float x) {
+  for (int off = 1; off < 32; off <<= 1) x = fmaxf(x, __shfl_xor(x, off));
+  return x;
+}
+
+// Thread layout: channel c = tid % D and row group rg = tid / D hold rows t = rg + RG*i of the
+// block (RG = 256 / D row groups, i < 32 / RG), in registers.  The 32 channels of a V group
+// are the 32 lanes of one half-wave.
 __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
@@ -32,102 +45,205 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   const bool tq = sh.fmt == KVQ_FMT_TQ;
   uint8_t* rec = lv.bulk + ((int64_t)s * lv.cap_b + beta % lv.cap_b) * lv.rec;
   const int64_t in_row0 = ((int64_t)b * sh.Hkv + h) * a.n;  // row index base of this stream in the chunk
+  const int RG = NT / D, c = tid % D, rg = tid / D;
 
-  __shared__ float xk[G][XP];
-  __shared__ float xv[G][XP];
-  __shared__ uint8_t ck[G][MAX_D];
-  __shared__ uint8_t cv[G][MAX_D];
+  __shared__ float xk[G][XP];          // K rows (q2k sum of squares, TurboQuant rows)
+  __shared__ float xv[G][XP];          // V rows (TurboQuant rows)
+  __shared__ alignas(16) uint8_t ck[G][MAX_D];   // K codes [token][channel]
+  __shared__ alignas(16) uint8_t cvt[MAX_D][G];  // V codes [channel][token]
+  __shared__ float red0[NT / 32][MAX_D], red1[NT / 32][MAX_D];  // per row group partials
   __shared__ int sink_slot[G];
+  __shared__ uint32_t smask_s;
   __shared__ uint16_t vmeta_s[G][4], vmeta_z[G][4];
   __shared__ float knorm[G], vnorm[G];
 
-  // 1. sink membership of the block's rows
-  if (tid < G) {
-    const int64_t p = base + tid;
+  // Every global load of the kernel is issued before any of them is used (one memory round trip
+  // instead of one per loop iteration): the committed sink list, this thread's elements of the
+  // block's rows (new rows from the chunk, earlier rows of an open K block from staging) and the
+  // V code words that hold bits of rows appended by earlier calls.
+  constexpr int PER = G * MAX_D / NT;  // row elements per thread (at most)
+  const int nper = G * D / NT;         // row elements per thread
+  const int ng = D / 32;
+  const int wpc = D * sh.vb / 64;      // words per V code chunk
+  int sp[MAX_SINK];
+  int scount = 0;
+  if (tid < G && sh.n_sink > 0 && sh.sink_mode == KVQ_SINK_TOPK) {
+    scount = lv.sink_count[b];
+#pragma unroll
+    for (int i = 0; i < MAX_SINK; ++i) sp[i] = i < sh.n_sink ? lv.sink_pos[b * sh.n_sink + i] : -1;
+  }
+  float kx[PER], vx[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int t = rg + RG * i;
+    kx[i] = 0.f;
+    vx[i] = 0.f;
+    if (i < nper && t < tend) {
+      if (t >= tnew0) {
+        const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
+        kx[i] = ld_in(a.k, gi, sh.in_f32);
+        vx[i] = ld_in(a.v, gi, sh.in_f32);
+      } else if (!tq) {
+        kx[i] = ld_in(lv.staging, ((int64_t)s * G + t) * D + c, sh.in_f32);
+      }
+    }
+  }
+  constexpr int VW = 64 * (MAX_D * 8 / 64) / NT;  // V code words per thread (at most)
+  uint32_t oldv[VW];
+  {
+    const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
+#pragma unroll
+    for (int i = 0; i < VW; ++i) {
+      const int idx = tid + i * NT;
+      oldv[i] = (tnew0 > 0 && idx < 64 * wpc) ? vw[idx] : 0u;
+    }
+  }
+
+  // 1. sink membership of the block's rows (slots, and a bit mask of sink rows)
+  if (tid < 64) {
     int slot = -1;
-    if (tid < tend && sh.n_sink > 0) {
+    if (tid < G && tid < tend && sh.n_sink > 0) {
+      const int64_t p = base + tid;
       if (sh.sink_mode == KVQ_SINK_FIRST_N) {
         if (p < sh.n_sink) slot = (int)p;
       } else if (sh.sink_mode == KVQ_SINK_TOPK) {
-        const int cnt = lv.sink_count[b];
-        for (int i = 0; i < cnt; ++i)
-          if (lv.sink_pos[b * sh.n_sink + i] == p) slot = i;
+#pragma unroll
+        for (int i = 0; i < MAX_SINK; ++i)
+          if (i < scount && sp[i] == p) slot = i;
       }
     }
-    sink_slot[tid] = slot;
-    knorm[tid] = 0.f;
-    vnorm[tid] = 0.f;
+    const uint64_t m = __ballot(slot >= 0);
+    if (tid < G) {
+      sink_slot[tid] = slot;
+      knorm[tid] = 0.f;
+      vnorm[tid] = 0.f;
+    }
+    if (tid == 0) smask_s = (uint32_t)m;
   }
-  // 2. rows: new rows from the chunk, earlier rows of an open K block from staging
-  for (int idx = tid; idx < G * D; idx += NT) {
-    const int t = idx / D, c = idx % D;
-    float kx = 0.f, vx = 0.f;
-    if (t < tend) {
-      if (t >= tnew0) {
-        const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
-        kx = ld_in(a.k, gi, sh.in_f32);
-        vx = ld_in(a.v, gi, sh.in_f32);
-      } else if (!tq) {
-        kx = ld_in(lv.staging, ((int64_t)s * G + t) * D + c, sh.in_f32);
+  // 2. rows to LDS (the formats that read them across threads), codes cleared
+  if (tq || sh.fmt == KVQ_FMT_Q2K) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (i < nper) {
+        xk[rg + RG * i][c] = kx[i];
+        xv[rg + RG * i][c] = vx[i];
       }
-    }
-    xk[t][c] = kx;
-    xv[t][c] = vx;
-    ck[t][c] = 0;
-    cv[t][c] = 0;
+  }
+  for (int idx = tid; idx < G * MAX_D / 16; idx += NT) {
+    reinterpret_cast<uint4*>(&ck[0][0])[idx] = uint4{0, 0, 0, 0};
+    reinterpret_cast<uint4*>(&cvt[0][0])[idx] = uint4{0, 0, 0, 0};
   }
   __syncthreads();
+  const uint32_t smask = smask_s;
+  auto calib = [&](int t) { return t < tend && !((smask >> t) & 1u); };  // present, not a sink
 
-  // 3. K
+  // 3. K of a block format: per channel over the block's calibration rows, codes of every row
   if (!tq) {
-    for (int c = tid; c < D; c += NT) {
-      uint8_t* km = rec + lv.k_meta;
-      if (sh.fmt == KVQ_FMT_KIVI) {
-        float mn = INFINITY, mx = -INFINITY;
-        bool any = false;
-        for (int t = 0; t < tend; ++t)
-          if (sink_slot[t] < 0) {
-            mn = fminf(mn, xk[t][c]);
-            mx = fmaxf(mx, xk[t][c]);
-            any = true;
-          }
-        if (!any) mn = mx = 0.f;
-        mn = mn + 0.0f;
-        mx = mx + 0.0f;
-        const float L = (float)((1 << sh.kb) - 1);
-        const float s32 = fmaxf(EPS_SCALE, (mx - mn) / L);
-        const uint16_t s16 = f16_bits(s32), z16 = f16_bits(mn);
+    uint8_t* km = rec + lv.k_meta;
+    float sf = 0.f, zf = 0.f;
+    if (sh.fmt == KVQ_FMT_KIVI) {
+      float mn = INFINITY, mx = -INFINITY, any = 0.f;
+#pragma unroll
+      for (int i = 0; i < PER; ++i)
+        if (i < nper && calib(rg + RG * i)) {
+          mn = fminf(mn, kx[i]);
+          mx = fmaxf(mx, kx[i]);
+          any = 1.f;
+        }
+      red0[rg][c] = mn;
+      red1[rg][c] = any > 0.f ? mx : -INFINITY;
+      __syncthreads();
+      mn = INFINITY;
+      mx = -INFINITY;
+      for (int q = 0; q < RG; ++q) {
+        mn = fminf(mn, red0[q][c]);
+        mx = fmaxf(mx, red1[q][c]);
+      }
+      if (mx == -INFINITY) mn = mx = 0.f;  // no calibration row
+      mn = mn + 0.0f;
+      mx = mx + 0.0f;
+      const float L = (float)((1 << sh.kb) - 1);
+      const float s32 = fmaxf(EPS_SCALE, (mx - mn) / L);
+      const uint16_t s16 = f16_bits(s32), z16 = f16_bits(mn);
+      if (rg == 0) {
         reinterpret_cast<uint16_t*>(km)[c] = s16;
         reinterpret_cast<uint16_t*>(km)[D + c] = z16;
-        const float sf = f16_val(s16), zf = f16_val(z16);
-        for (int t = 0; t < tend; ++t)
-          if (sink_slot[t] < 0) {
-            const float u = rintf((xk[t][c] - zf) / sf);
-            ck[t][c] = (uint8_t)fminf(fmaxf(u, 0.f), L);
-          }
-      } else {  // Q2K
+      }
+      sf = f16_val(s16);
+      zf = f16_val(z16);
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int t = rg + RG * i;
+        if (i < nper && calib(t)) {
+          const float u = rintf((kx[i] - zf) / sf);
+          ck[t][c] = (uint8_t)fminf(fmaxf(u, 0.f), L);
+        }
+      }
+    } else {  // Q2K: block RMS summed in token order by one thread per channel
+      if (rg == 0) {
         float ss = 0.f;
         int n = 0;
         for (int t = 0; t < tend; ++t)
-          if (sink_slot[t] < 0) {
+          if (calib(t)) {
             ss = ss + xk[t][c] * xk[t][c];
             ++n;
           }
         const float r32 = n > 0 ? fmaxf(EPS_SCALE, sqrtf(ss / (float)n)) : EPS_SCALE;
         const uint16_t r16 = f16_bits(r32);
         reinterpret_cast<uint16_t*>(km)[c] = r16;
-        const float rf = f16_val(r16);
-        const float th0 = lv.tables->q2k_thr[0], th1 = lv.tables->q2k_thr[1], th2 = lv.tables->q2k_thr[2];
-        for (int t = 0; t < tend; ++t)
-          if (sink_slot[t] < 0) {
-            const float x = xk[t][c] / rf;
-            ck[t][c] = (uint8_t)((x >= th0) + (x >= th1) + (x >= th2));
-          }
+        red0[0][c] = f16_val(r16);
+      }
+      __syncthreads();
+      const float rf = red0[0][c];
+      const float th0 = lv.tables->q2k_thr[0], th1 = lv.tables->q2k_thr[1], th2 = lv.tables->q2k_thr[2];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int t = rg + RG * i;
+        if (i < nper && calib(t)) {
+          const float x = kx[i] / rf;
+          ck[t][c] = (uint8_t)((x >= th0) + (x >= th1) + (x >= th2));
+        }
       }
     }
-  }
-  // TQ rows (K and V) and the rotation: one wave per row
-  if (tq) {
+    // 3b. V of the new rows: per token and 32-channel group (one half-wave per group)
+    const int g = c >> 5;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int t = rg + RG * i;
+      if (i >= nper || t < tnew0 || t >= tend) continue;  // uniform over the half-wave
+      if ((smask >> t) & 1u) {
+        if ((c & 31) == 0) {
+          vmeta_s[t][g] = 0;
+          vmeta_z[t][g] = 0;
+        }
+        continue;
+      }
+      if (sh.fmt == KVQ_FMT_KIVI) {
+        const float mn = half_min(vx[i]) + 0.0f, mx = half_max(vx[i]) + 0.0f;
+        const float L = (float)((1 << sh.vb) - 1);
+        const float s32 = fmaxf(EPS_SCALE, (mx - mn) / L);
+        const uint16_t s16 = f16_bits(s32), z16 = f16_bits(mn);
+        const float vsf = f16_val(s16), vzf = f16_val(z16);
+        const float u = rintf((vx[i] - vzf) / vsf);
+        cvt[c][t] = (uint8_t)fminf(fmaxf(u, 0.f), L);
+        if ((c & 31) == 0) {
+          vmeta_s[t][g] = s16;
+          vmeta_z[t][g] = z16;
+        }
+      } else {  // Q2K: symmetric 4-bit, s = absmax / 7
+        const float am = half_max(fabsf(vx[i])) + 0.0f;
+        const uint16_t s16 = f16_bits(fmaxf(EPS_SCALE, am / 7.0f));
+        const float vsf = f16_val(s16);
+        const float q = fminf(fmaxf(rintf(vx[i] / vsf), -8.f), 7.f);
+        cvt[c][t] = (uint8_t)(q + 8.f);
+        if ((c & 31) == 0) {
+          vmeta_s[t][g] = s16;
+          vmeta_z[t][g] = 0;
+        }
+      }
+    }
+  } else {
+    // TQ rows (K and V) and the rotation: one wave per row
     const int lane = tid & 63, w = tid >> 6;
     const float cd = (float)(1.0 / __builtin_sqrt((double)D));
     const Tables* T = lv.tables;
@@ -151,93 +267,77 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
           u1 += t1 >= bnd[j];
         }
         if (act) {
-          uint8_t(*C)[MAX_D] = which ? cv : ck;
-          C[t][2 * lane] = (uint8_t)u0;
-          C[t][2 * lane + 1] = (uint8_t)u1;
+          if (which) {
+            cvt[2 * lane][t] = (uint8_t)u0;
+            cvt[2 * lane + 1][t] = (uint8_t)u1;
+          } else {
+            ck[t][2 * lane] = (uint8_t)u0;
+            ck[t][2 * lane + 1] = (uint8_t)u1;
+          }
         }
         if (lane == 0) (which ? vnorm : knorm)[t] = nrm;
-      }
-    }
-  } else {
-    // V per token and 32-channel group
-    const int ng = D / 32;
-    for (int idx = tid; idx < (tend - tnew0) * ng; idx += NT) {
-      const int t = tnew0 + idx / ng, g = idx % ng;
-      if (sink_slot[t] >= 0) {
-        vmeta_s[t][g] = 0;
-        vmeta_z[t][g] = 0;
-        continue;
-      }
-      if (sh.fmt == KVQ_FMT_KIVI) {
-        float mn = INFINITY, mx = -INFINITY;
-        for (int c = 0; c < 32; ++c) {
-          mn = fminf(mn, xv[t][32 * g + c]);
-          mx = fmaxf(mx, xv[t][32 * g + c]);
-        }
-        mn = mn + 0.0f;
-        mx = mx + 0.0f;
-        const float L = (float)((1 << sh.vb) - 1);
-        const float s32 = fmaxf(EPS_SCALE, (mx - mn) / L);
-        const uint16_t s16 = f16_bits(s32), z16 = f16_bits(mn);
-        vmeta_s[t][g] = s16;
-        vmeta_z[t][g] = z16;
-        const float sf = f16_val(s16), zf = f16_val(z16);
-        for (int c = 0; c < 32; ++c) {
-          const float u = rintf((xv[t][32 * g + c] - zf) / sf);
-          cv[t][32 * g + c] = (uint8_t)fminf(fmaxf(u, 0.f), L);
-        }
-      } else {  // Q2K: symmetric 4-bit, s = absmax / 7
-        float am = 0.f;
-        for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(xv[t][32 * g + c]));
-        am = am + 0.0f;
-        const uint16_t s16 = f16_bits(fmaxf(EPS_SCALE, am / 7.0f));
-        vmeta_s[t][g] = s16;
-        vmeta_z[t][g] = 0;
-        const float sf = f16_val(s16);
-        for (int c = 0; c < 32; ++c) {
-          const float q = fminf(fmaxf(rintf(xv[t][32 * g + c] / sf), -8.f), 7.f);
-          cv[t][32 * g + c] = (uint8_t)(q + 8.f);
-        }
       }
     }
   }
   __syncthreads();
 
-  // 4. K codes: token rows, word-interleaved.  Block formats rewrite the whole
-  //    block (rows not present are 0); TQ writes its new rows (and clears the
-  //    rest of a block it opens).
+  // 4. K codes: token rows, word-interleaved, from one vector LDS read of the word's codes.  Block
+  //    formats rewrite the whole block (rows not present are 0); TQ writes its new rows (and
+  //    clears the rest of a block it opens).
   {
     const int wpr = D * sh.kb / 32, per = 32 / sh.kb;
     uint32_t* kw = reinterpret_cast<uint32_t*>(rec + lv.k_codes);
     for (int idx = tid; idx < G * wpr; idx += NT) {
       const int t = idx / wpr, w = idx % wpr;
       if (tq && !((t >= tnew0 && t < tend) || (tnew0 == 0 && t >= tend))) continue;
+      uint32_t cw[4] = {0, 0, 0, 0};  // the word's codes, one byte each
+      const uint8_t* src = &ck[t][w * per];
+      if (per == 16) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        cw[0] = x.x, cw[1] = x.y, cw[2] = x.z, cw[3] = x.w;
+      } else if (per == 8) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        cw[0] = x.x, cw[1] = x.y;
+      } else {
+        cw[0] = *reinterpret_cast<const uint32_t*>(src);
+      }
       uint32_t word = 0;
-      for (int k = 0; k < per; ++k) word |= (uint32_t)ck[t][w * per + k] << code_shift(k, sh.kb);
+      for (int k = 0; k < per; ++k) word |= ((cw[k >> 2] >> (8 * (k & 3))) & 0xFFu) << code_shift(k, sh.kb);
       kw[idx] = word;
     }
   }
-  // 5. V codes: channel tiles; bits of rows appended earlier are kept, others rewritten
+  // 5. V codes: channel tiles; bits of rows appended earlier are kept, others rewritten.  The
+  //    tokens T(kg, e) of a channel for e = 0..3 and e = 4..7 are two 4-byte runs of cvt.
   {
-    const int wpc = D * sh.vb / 64, per = 32 / sh.vb;
+    const int per = 32 / sh.vb;
     uint32_t* vw = reinterpret_cast<uint32_t*>(rec + lv.v_codes);
     const uint32_t m1 = (1u << sh.vb) - 1;
-    for (int idx = tid; idx < 64 * wpc; idx += NT) {
+#pragma unroll
+    for (int ii = 0; ii < VW; ++ii) {
+      const int idx = tid + ii * NT;
+      if (idx >= 64 * wpc) break;
       const int q = idx / wpc, w = idx % wpc, kg = q >> 4, i = q & 15;
-      const uint32_t old = tnew0 > 0 ? vw[idx] : 0u;
+      const uint32_t old = oldv[ii];
       uint32_t word = 0;
+      uint32_t run[2] = {0, 0};
+      int mu_run = -1;
       for (int k = 0; k < per; ++k) {
         const int sq = w * per + k, mu = sq >> 3, e = sq & 7;
-        const int t = v_tok(kg, e), c = 16 * mu + i, sh_ = code_shift(k, sh.vb);
+        const int t = v_tok(kg, e), sh_ = code_shift(k, sh.vb);
+        if (mu != mu_run) {
+          const int cc = 16 * mu + i;
+          run[0] = *reinterpret_cast<const uint32_t*>(&cvt[cc][4 * kg]);
+          run[1] = *reinterpret_cast<const uint32_t*>(&cvt[cc][16 + 4 * kg]);
+          mu_run = mu;
+        }
         if (t < tnew0) word |= old & (m1 << sh_);
-        else if (t < tend) word |= (uint32_t)cv[t][c] << sh_;
+        else if (t < tend) word |= ((run[e >> 2] >> (8 * (e & 3))) & 0xFFu) << sh_;
       }
       vw[idx] = word;
     }
   }
   // 6. metadata of rows from tnew0 on (rows past tend cleared)
   {
-    const int ng = D / 32;
     if (tq) {
       float* kn = reinterpret_cast<float*>(rec + lv.k_meta);
       float* vn = reinterpret_cast<float*>(rec + lv.v_meta);
@@ -258,9 +358,9 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   // 7. staging of an open block (raw input rows; block formats only)
   if (!tq && tend < G) {
     for (int idx = tid; idx < (tend - tnew0) * D; idx += NT) {
-      const int t = tnew0 + idx / D, c = idx % D;
-      const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
-      const int64_t so = ((int64_t)s * G + t) * D + c;
+      const int t = tnew0 + idx / D, cc = idx % D;
+      const int64_t gi = (in_row0 + (base + t - a.P)) * D + cc;
+      const int64_t so = ((int64_t)s * G + t) * D + cc;
       if (sh.in_f32) reinterpret_cast<float*>(lv.staging)[so] = static_cast<const float*>(a.k)[gi];
       else reinterpret_cast<uint16_t*>(lv.staging)[so] = static_cast<const uint16_t*>(a.k)[gi];
     }
@@ -269,11 +369,11 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   if (sh.R > 0) {
     const int64_t wlo = (a.P + a.n - sh.R) > a.P ? (a.P + a.n - sh.R) : a.P;
     for (int idx = tid; idx < (tend - tnew0) * D; idx += NT) {
-      const int t = tnew0 + idx / D, c = idx % D;
+      const int t = tnew0 + idx / D, cc = idx % D;
       const int64_t p = base + t;
       if (p < wlo) continue;
-      const int64_t gi = (in_row0 + (p - a.P)) * D + c;
-      const int64_t wo = ((int64_t)s * sh.R + p % sh.R) * D + c;
+      const int64_t gi = (in_row0 + (p - a.P)) * D + cc;
+      const int64_t wo = ((int64_t)s * sh.R + p % sh.R) * D + cc;
       lv.win_k[wo] = ld_in_f16(a.k, gi, sh.in_f32);
       lv.win_v[wo] = ld_in_f16(a.v, gi, sh.in_f32);
     }
@@ -281,11 +381,11 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   // 9. fp16 sink pool
   if (sh.n_sink > 0) {
     for (int idx = tid; idx < (tend - tnew0) * D; idx += NT) {
-      const int t = tnew0 + idx / D, c = idx % D;
+      const int t = tnew0 + idx / D, cc = idx % D;
       const int slot = sink_slot[t];
       if (slot < 0) continue;
-      const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
-      const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + c;
+      const int64_t gi = (in_row0 + (base + t - a.P)) * D + cc;
+      const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + cc;
       lv.sink_k[so] = ld_in_f16(a.k, gi, sh.in_f32);
       lv.sink_v[so] = ld_in_f16(a.v, gi, sh.in_f32);
     }

@@ -76,6 +76,7 @@ def _load():
 
 
 lib = _load()
+_select, _append, _evict, _decode = lib.kvq_select_sinks, lib.kvq_append, lib.kvq_evict, lib.kvq_decode_attn
 
 
 def last_error():
@@ -122,8 +123,14 @@ def format_tables(cfg):
     return {k: list(v) for k, v in bufs.items()}
 
 
-def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(dev=None):
+    """Handle of the current HIP stream of device `dev` (default: the current device)."""
+    if _raw_stream is not None:
+        return _raw_stream(torch.cuda.current_device() if dev is None else dev)
+    return torch.cuda.current_stream(dev).cuda_stream
 
 
 def _ptr(t):
@@ -139,8 +146,10 @@ class Cache:
         nbytes = required_bytes(cfg)
         self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.ws = torch.empty(max(workspace_bytes(cfg), 16), dtype=torch.uint8, device=device)
+        self.dev = self.buf.device.index
+        self._ws = (self.ws.data_ptr(), self.ws.numel())
         h = ctypes.c_void_p()
-        _check(lib.kvq_create(ctypes.byref(cfg), _ptr(self.buf), nbytes, _stream(), ctypes.byref(h)))
+        _check(lib.kvq_create(ctypes.byref(cfg), _ptr(self.buf), nbytes, _stream(self.dev), ctypes.byref(h)))
         self.handle = h
 
     def __del__(self):
@@ -149,26 +158,26 @@ class Cache:
             lib.kvq_destroy(h)
             self.handle = None
 
-    # entry points, same names as the C ABI
+    # entry points, same names as the C ABI (launches go to the current stream of the cache's device)
     def kvq_select_sinks(self, layer, k):
-        _check(lib.kvq_select_sinks(self.handle, layer, _ptr(k), k.shape[2], _stream()))
+        _check(_select(self.handle, layer, k.data_ptr(), k.shape[2], _stream(self.dev)))
 
     def kvq_append(self, layer, k, v):
-        _check(lib.kvq_append(self.handle, layer, _ptr(k), _ptr(v), k.shape[2], _stream()))
+        _check(_append(self.handle, layer, k.data_ptr(), v.data_ptr(), k.shape[2], _stream(self.dev)))
 
     def kvq_evict(self, layer):
-        _check(lib.kvq_evict(self.handle, layer))
+        _check(_evict(self.handle, layer))
 
     def kvq_decode_attn(self, layer, q, out, scale=0.0):
-        _check(lib.kvq_decode_attn(self.handle, layer, _ptr(q), _ptr(out), scale, _ptr(self.ws),
-                                   self.ws.numel(), _stream()))
+        _check(_decode(self.handle, layer, q.data_ptr(), out.data_ptr(), scale, self._ws[0], self._ws[1],
+                       _stream(self.dev)))
 
     def kvq_dequant(self, layer, which, pos0, count, out):
-        _check(lib.kvq_dequant(self.handle, layer, which, pos0, count, _ptr(out), _stream()))
+        _check(lib.kvq_dequant(self.handle, layer, which, pos0, count, _ptr(out), _stream(self.dev)))
 
     def kvq_account(self, layer):
         b = kvq_bytes()
-        _check(lib.kvq_account(self.handle, layer, ctypes.byref(b), _stream()))
+        _check(lib.kvq_account(self.handle, layer, ctypes.byref(b), _stream(self.dev)))
         return {n: getattr(b, n) for n, _ in kvq_bytes._fields_}
 
     def kvq_get_state(self, layer):
