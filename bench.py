@@ -169,6 +169,105 @@ def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, b
                       f"decode-attention time (fp64, numpy, 1 BLAS thread)"}
 
 
+DECODE_SOURCES = ["decode_fast.hip", "decode.hip", "decode_shared.h", "device_common.h", "kvq_internal.h",
+                  "kvq_api.cpp"]
+DECODE_KERNELS = ("k_decode_fast", "k_merge_parts", "k_decode", "k_merge_heads", "k_decode_merge")
+PROFILES = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles")
+COPY_BYTES = 1 << 30  # calibration copy: 1 GiB read and 1 GiB written per launch
+
+
+def decode_fingerprint():
+    """sha256 of the sources that decide what the decode-attention kernels read and write."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "quantized_kv_cache_kivi_amd", "csrc")
+    for name in DECODE_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(cfgno):
+    return os.path.join(PROFILES, f"decode_traffic_{CONFIGS[cfgno]['name']}.json")
+
+
+def load_traffic(cfgno):
+    """HBM bytes per decode-attention call from hardware counters, if taken on the current kernels."""
+    try:
+        with open(traffic_file(cfgno)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t if t.get("fingerprint") == decode_fingerprint() else None
+
+
+def copy_calibration():
+    """A plain copy of known size (1 GiB read, 1 GiB written per launch) for the FETCH_SIZE /
+    WRITE_SIZE counter calibration."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] copy calibration: 4 copies of {COPY_BYTES} bytes")
+
+
+def _pmc_per_dispatch(d, counter, match):
+    """Mean per dispatch of `counter` (summed over its instances) for kernels whose name contains any
+    of `match`, per kernel base name, from a rocprofv3 --pmc output directory."""
+    import collections
+    import csv
+    import glob
+    per = collections.defaultdict(float)
+    names = {}
+    for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(fn)):
+            if r["Counter_Name"] != counter or not any(m in r["Kernel_Name"] for m in match):
+                continue
+            key = r["Dispatch_Id"]
+            per[key] += float(r["Counter_Value"])
+            names[key] = next(m for m in match if m in r["Kernel_Name"])
+    out = collections.defaultdict(list)
+    for key, v in per.items():
+        out[names[key]].append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}, {k: len(v) for k, v in out.items()}
+
+
+def summarize_pmc(cfgno, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, cmds):
+    """Decode-attention HBM bytes per call from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each
+    scaled by what the counter reads for the 1 GiB calibration copy; writes the JSON the bench
+    reads and a short markdown summary under profiles/."""
+    fk, nf = _pmc_per_dispatch(fetch_dir, "FETCH_SIZE", DECODE_KERNELS)
+    wk, nw = _pmc_per_dispatch(write_dir, "WRITE_SIZE", DECODE_KERNELS)
+    cf, _ = _pmc_per_dispatch(copy_fetch_dir, "FETCH_SIZE", ("copy", "elementwise"))
+    cw, _ = _pmc_per_dispatch(copy_write_dir, "WRITE_SIZE", ("copy", "elementwise"))
+    f_read = COPY_BYTES / (max(cf.values()) * 1024.0)
+    f_write = COPY_BYTES / (max(cw.values()) * 1024.0)
+    per_kernel = {k: {"fetch_kib": fk.get(k, 0.0), "write_kib": wk.get(k, 0.0), "dispatches": nf.get(k, 0)}
+                  for k in sorted(set(fk) | set(wk))}
+    traffic = sum(v["fetch_kib"] * 1024.0 * f_read + v["write_kib"] * 1024.0 * f_write for v in per_kernel.values())
+    t = {"workload": CONFIGS[cfgno]["name"], "fingerprint": decode_fingerprint(), "bytes_per_call": traffic,
+         "read_factor": f_read, "write_factor": f_write, "copy_fetch_kib": max(cf.values()),
+         "copy_write_kib": max(cw.values()), "per_kernel": per_kernel, "commands": cmds}
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(traffic_file(cfgno), "w") as f:
+        json.dump(t, f, indent=1)
+    lines = [f"# HBM traffic of one decode-attention call: {CONFIGS[cfgno]['name']}", "",
+             f"Workload: {CONFIGS[cfgno]['desc']}.", "", "Commands (MI355X, ROCm 7.2):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", "| kernel | FETCH_SIZE KiB / dispatch | WRITE_SIZE KiB / dispatch | dispatches |", "|---|---|---|---|"]
+    for k, v in per_kernel.items():
+        lines.append(f"| {k} | {v['fetch_kib']:.1f} | {v['write_kib']:.1f} | {v['dispatches']} |")
+    lines += ["", f"Calibration copy of {COPY_BYTES} bytes: FETCH_SIZE {max(cf.values()):.1f} KiB, WRITE_SIZE "
+              f"{max(cw.values()):.1f} KiB; read factor {f_read:.4f}, write factor {f_write:.4f}.", "",
+              f"HBM bytes per decode-attention call: {traffic / 1e6:.2f} MB (source fingerprint "
+              f"{t['fingerprint']}).", ""]
+    with open(os.path.join(PROFILES, f"decode_traffic_{CONFIGS[cfgno]['name']}.md"), "w") as f:
+        f.write("\n".join(lines))
+    print(json.dumps({"traffic_bytes_per_call": traffic, "per_kernel": per_kernel}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,7 +276,19 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="run the warmup and timed steps without timing or output (for rocprofv3 --pmc passes)")
+    ap.add_argument("--copy-calibration", action="store_true", help="run the 1 GiB calibration copy and exit")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="turn rocprofv3 --pmc outputs into profiles/decode_traffic_<workload>.{json,md}")
+    ap.add_argument("--pmc-commands", nargs="*", default=[], help="commands recorded with --summarize-pmc")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.config, *args.summarize_pmc, args.pmc_commands)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (every stream of the cache is "
@@ -261,6 +372,12 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if args.pmc_run:
+        for j in range(args.steps):
+            step(args.warmup + j)
+        torch.cuda.synchronize()
+        log(f"[bench] pmc run: {args.warmup + args.steps} steps")
+        return
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     nbytes, nctx = 0, 0
     t0 = time.perf_counter()
@@ -302,6 +419,8 @@ def main():
         warm = {"decode_attn_us": wms * 1e3, "GBps": wb / (wms * 1e-3) / 1e9,
                 "note": "same cache re-read back to back (served partly from the Infinity Cache)"}
 
+    tr = load_traffic(args.config)
+    traffic = tr["bytes_per_call"] if tr else None  # HBM bytes per decode-attention call (counters)
     res = {
         "metric": METRIC,
         "value": bytes_per_step / (ms_step * 1e-3) / 1e9,
@@ -322,7 +441,7 @@ def main():
                         "context_tokens_per_s": nctx / args.steps / (kern_ms * 1e-3),
                         "bytes_per_call": bytes_per_step / calls_per_step},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "warm_cache": warm,
     }
     if not args.no_cpu_baseline:
