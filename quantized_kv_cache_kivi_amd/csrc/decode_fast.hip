@@ -1,10 +1,11 @@
 // MFMA decode attention, head_dim 128, fp16 query (gfx950).
 //
-// One launch of k_decode_fast writes every partial of a decode call: the
-// workgroups with blockIdx.x < splits stream the packed bulk of one split of a
-// stream, the next ones score the fp16 rows (window rows minus committed sinks,
-// then the sink pool) of that stream, 64 rows each.  k_merge_parts then merges
-// the partials of each (stream, query head) in fixed order.
+// One launch of k_decode_fast writes every partial of a decode call: workgroup
+// (stream blockIdx.x, part blockIdx.y) streams the packed bulk of split
+// blockIdx.y of the stream when blockIdx.y < splits, else it scores 64 of the
+// stream's fp16 rows (window rows minus committed sinks, then the sink pool).
+// k_merge_parts then merges the partials of each (stream, query head) in fixed
+// order.
 //
 // Bulk, per 32-token block and wave ("StreamingLLM + KIVI — long-context decode
 // without growing the KV cache", "Affine quantisation formula": k = u*s + z per
@@ -411,7 +412,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform: keeps the loop scalar)
   const int i16 = lane & 15, kg = lane >> 4;
-  const int sigma = blockIdx.x, s = blockIdx.y, b = s / sh.Hkv, g = s % sh.Hkv;
+  const int sigma = blockIdx.y, s = blockIdx.x, b = s / sh.Hkv, g = s % sh.Hkv;
   auto& W = F.w[wv];
 
   const int first = sigma * a.blocks_per_split;
@@ -429,7 +430,14 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     if (sl >= lv.cap_b) sl -= lv.cap_b;
     return (uint32_t)sl * (uint32_t)lv.rec;
   };
-  stage_sinks(a, b, F.sinks, nullptr, &F.nsinks);
+  // Two register buffers: the next block of this wave is in flight while the current one is
+  // computed (a deeper ring costs the registers of a third wave per SIMD, which hides more).  The
+  // wave's first block is requested together with the prologue's loads, and the prologue ends by
+  // waiting for all of them, so the loop is entered with no load in flight and its back edge
+  // carries exactly one block (the compiler's wait counts inside the loop then stay exact).
+  Blk<KB, VB> d0, d1;
+  int bi = first + wv;
+  if (bi < lastb) load_blk<Q2K>(d0, rs, rec_of(bi), bo);
   St S;
   const float al = a.scale * LOG2E;
   float q2k_w = 0.f;
@@ -456,6 +464,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     S.lf = (float)(PV - pv);
     S.ifv = ldexpf(1.f, pv - PV);
   }
+  stage_sinks(a, b, F.sinks, nullptr, &F.nsinks);
 #pragma unroll
   for (int p = 0; p < NPL; ++p) {
     S.m_[p] = -INFINITY;
@@ -466,20 +475,13 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   }
 #pragma unroll
   for (int mu = 0; mu < 8; ++mu) S.acc[mu] = f4{0.f, 0.f, 0.f, 0.f};
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query, the sink list and the first block
   __syncthreads();
 
   const int nsink = __builtin_amdgcn_readfirstlane(F.nsinks);
   const int sblk = lane < nsink ? F.sinks[lane] / G : -1;  // block of sink `lane`
 
-  // Two register buffers: the next block of this wave is in flight while the current one is
-  // computed (a deeper ring costs the registers of a third wave per SIMD, which hides more).  The
-  // ring is primed only after every other load of the prologue has landed, so the loop is entered
-  // with exactly the loads in flight that its back edge carries (the compiler's wait counts then
-  // stay exact).
-  Blk<KB, VB> d0, d1;
-  int bi = first + wv;
   if (bi < lastb) {
-    load_blk<Q2K>(d0, rs, rec_of(bi), bo);
     while (true) {
       load_blk<Q2K>(d1, rs, rec_of(bi + NW), bo);
       block_step(S, W, F.sinks, d0, blkf + bi, blo, bhi, sblk, nsink, q2k_w, lane);
@@ -551,33 +553,59 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
 // Partial of fp16 rows [64 f, 64 f + 64) of the stream's list: window rows [bulk_hi, P) (the ones
 // that are committed sinks masked: the pool holds them), then the committed sinks in slot order.
 // Scores: 4 lanes per row (32 channels each, packed fp16 dot products); weights per head over the
-// workgroup's rows; values: one channel pair per lane, rows split over the 4 waves.
+// workgroup's rows; values: one channel pair per lane, rows split over the 4 waves.  Every row load
+// (the K quarter a thread scores and the V words its wave accumulates) is issued at once, right
+// after the sink list is known.
 template <int R>
 __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
+  constexpr int VPW = FPR / NW;  // rows per wave in the values phase
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int s = blockIdx.y, b = s / sh.Hkv, g = s % sh.Hkv;
+  const int s = blockIdx.x, b = s / sh.Hkv, g = s % sh.Hkv;
   const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
-  for (int idx = tid; idx < R * FD / 2; idx += DNT)
-    F.q[idx / (FD / 2)][idx % (FD / 2)] = reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow)[idx];
+  constexpr int QW = (R * FD / 2 + DNT - 1) / DNT;  // query words per thread
+  uint32_t qv[QW];
+#pragma unroll
+  for (int k = 0; k < QW; ++k) {
+    const int idx = tid + k * DNT;
+    qv[k] = idx < R * FD / 2 ? reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow)[idx] : 0u;
+  }
   stage_sinks(a, b, F.spos, F.sslot, &F.nsink);
+#pragma unroll
+  for (int k = 0; k < QW; ++k) {
+    const int idx = tid + k * DNT;
+    if (idx < R * FD / 2) F.q[idx / (FD / 2)][idx % (FD / 2)] = qv[k];
+  }
   __syncthreads();
   const int nwin = (int)(a.P - a.bulk_hi);  // positions fit in int32
   const int nfp = nwin + F.nsink;
   const int r0 = f * FPR, nr = max(0, min(FPR, nfp - r0));
   const float al = a.scale * LOG2E;
 
+  const int w0 = nwin > 0 ? (int)a.bulk_hi % sh.R : 0;  // window slot of row 0 (nwin <= R)
   auto row_ptr = [&](int i, bool v_side) -> const uint16_t* {  // fp16 row i of the list (i < nfp)
     if (i < nwin) {
-      const int64_t p = a.bulk_hi + i;
-      return (v_side ? lv.win_v : lv.win_k) + ((int64_t)s * sh.R + p % sh.R) * FD;
+      const int ws = w0 + i < sh.R ? w0 + i : w0 + i - sh.R;
+      return (v_side ? lv.win_v : lv.win_k) + ((int64_t)s * sh.R + ws) * FD;
     }
     return (v_side ? lv.sink_v : lv.sink_k) + ((int64_t)s * sh.n_sink + F.sslot[i - nwin]) * FD;
   };
+  const int lr = tid >> 2, qq = tid & 3, i = r0 + lr;
+  u4 kw[4];
+  if (lr < nr) {
+    const u4* kr = reinterpret_cast<const u4*>(row_ptr(i, false) + 32 * qq);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kw[k] = kr[k];
+  }
+  uint32_t vw[VPW];
+#pragma unroll
+  for (int k = 0; k < VPW; ++k) {
+    const int r = wv + NW * k;
+    vw[k] = r < nr ? reinterpret_cast<const uint32_t*>(row_ptr(r0 + r, true))[lane] : 0u;
+  }
   // ---- scores ----
   {
-    const int lr = tid >> 2, qq = tid & 3, i = r0 + lr;
     bool ok = lr < nr;
     float acc[R];
 #pragma unroll
@@ -585,10 +613,6 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
     if (ok) {
       if (i < nwin)
         for (int q = 0; q < F.nsink; ++q) ok = ok && F.spos[q] != a.bulk_hi + i;
-      const u4* kr = reinterpret_cast<const u4*>(row_ptr(i, false) + 32 * qq);
-      u4 kw[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) kw[k] = kr[k];
 #pragma unroll
       for (int j = 0; j < R; ++j) {
 #pragma unroll
@@ -630,14 +654,17 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
     float acc[R][2];
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[j][0] = acc[j][1] = 0.f;
-    for (int lr = wv; lr < nr; lr += NW) {
-      const uint32_t w = reinterpret_cast<const uint32_t*>(row_ptr(r0 + lr, true))[lane];
-      const float v0 = h16(w, 0), v1 = h16(w, 1);
 #pragma unroll
-      for (int j = 0; j < R; ++j) {
-        const float p = F.sc[j][lr];
-        acc[j][0] = __builtin_fmaf(p, v0, acc[j][0]);
-        acc[j][1] = __builtin_fmaf(p, v1, acc[j][1]);
+    for (int k = 0; k < VPW; ++k) {
+      const int r = wv + NW * k;
+      if (r < nr) {
+        const float v0 = h16(vw[k], 0), v1 = h16(vw[k], 1);
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          const float p = F.sc[j][r];
+          acc[j][0] = __builtin_fmaf(p, v0, acc[j][0]);
+          acc[j][1] = __builtin_fmaf(p, v1, acc[j][1]);
+        }
       }
     }
 #pragma unroll
@@ -668,28 +695,47 @@ template <int FMT, int KB, int VB, int R>
 __global__ __launch_bounds__(DNT) __attribute__((amdgpu_waves_per_eu(waves_target<FMT, KB, VB, R>())))
 void k_decode_fast(DecodeArgs a) {
   __shared__ DecSmem<R> S;
-  if ((int)blockIdx.x < a.splits) bulk_partial<FMT, KB, VB, R>(a, S.bulk);
-  else fp16_partial<R>(a, S.fp, (int)blockIdx.x - a.splits);
+  if ((int)blockIdx.y < a.splits) bulk_partial<FMT, KB, VB, R>(a, S.bulk);
+  else fp16_partial<R>(a, S.fp, (int)blockIdx.y - a.splits);
 }
 
 // Fixed-order merge of the partials of one (stream, query head): bulk splits, then fp16 groups.
+// The partials are read in chunks of MC, all loads of a chunk at once, with the running maximum
+// and sums rescaled between chunks (one memory round trip per chunk).
 template <int R>
 __global__ __launch_bounds__(FD) void k_merge_parts(DecodeArgs a) {
+  constexpr int MC = 16;
   const int s = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
   const int b = s / a.sh.Hkv, g = s % a.sh.Hkv;
   const float* P0 = a.ws + (int64_t)s * a.nparts * R * (FD + 2) + j * (FD + 2);
   const int np = a.nparts;
-  float M = -INFINITY;
-#pragma unroll 8
-  for (int q = 0; q < np; ++q) M = fmaxf(M, P0[(int64_t)q * R * (FD + 2)]);
-  float L = 0.f, v = 0.f;
-#pragma unroll 8
-  for (int q = 0; q < np; ++q) {
-    const float* pq = P0 + (int64_t)q * R * (FD + 2);
-    const float mq = pq[0];
-    const float w = mq == -INFINITY ? 0.f : ex2(mq - M);
-    L = __builtin_fmaf(pq[1], w, L);
-    v = __builtin_fmaf(pq[2 + c], w, v);
+  float M = -INFINITY, L = 0.f, v = 0.f;
+  for (int q0 = 0; q0 < np; q0 += MC) {
+    float mq[MC], lq[MC], vq[MC];
+#pragma unroll
+    for (int k = 0; k < MC; ++k) {
+      mq[k] = -INFINITY;
+      lq[k] = vq[k] = 0.f;
+      if (q0 + k < np) {
+        const float* pq = P0 + (int64_t)(q0 + k) * R * (FD + 2);
+        mq[k] = pq[0];
+        lq[k] = pq[1];
+        vq[k] = pq[2 + c];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < MC; ++k) Mn = fmaxf(Mn, mq[k]);
+    const float fo = M == -INFINITY ? 0.f : ex2(M - Mn);  // the sums so far are 0 while M = -inf
+    L *= fo;
+    v *= fo;
+#pragma unroll
+    for (int k = 0; k < MC; ++k) {
+      const float w = mq[k] == -INFINITY ? 0.f : ex2(mq[k] - Mn);
+      L = __builtin_fmaf(lq[k], w, L);
+      v = __builtin_fmaf(vq[k], w, v);
+    }
+    M = Mn;
   }
   a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * FD + c] = v / L;
 }
@@ -698,7 +744,8 @@ template <int FMT, int KB, int VB>
 hipError_t launch_r(const DecodeArgs& a, hipStream_t st) {
   const int r = a.sh.Hq / a.sh.Hkv;
   const int S = a.sh.B * a.sh.Hkv;
-  dim3 grid(a.nparts, S);
+  // parts vary slowest: the (short) fp16 workgroups are dispatched after every bulk split
+  dim3 grid(S, a.nparts);
   dim3 mgrid(S, r);
   switch (r) {
     case 1:

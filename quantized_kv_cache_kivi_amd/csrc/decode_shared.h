@@ -33,12 +33,15 @@ struct Smem {
 };
 
 // Committed sinks (position < P) of batch element b, compacted in slot order by wave 0:
-// positions, pool slots (if `slot` is not null) and their number.  Callers synchronize.
+// positions, pool slots (if `slot` is not null) and their number.  Callers synchronize.  The count
+// and the position slots are loaded together (one memory round trip), then masked by the count.
 __device__ inline void stage_sinks(const DecodeArgs& a, int b, int* pos, int* slot, int* count) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    const int cnt = a.sh.n_sink > 0 ? min(a.lv.sink_count[b], a.sh.n_sink) : 0;
-    const int p = lane < cnt ? a.lv.sink_pos[b * a.sh.n_sink + lane] : -1;
+    const int ns = a.sh.n_sink;
+    const int cnt = ns > 0 ? a.lv.sink_count[b] : 0;
+    const int praw = lane < ns ? a.lv.sink_pos[b * ns + lane] : -1;
+    const int p = lane < min(cnt, ns) ? praw : -1;
     const bool ok = p >= 0 && p < a.P;
     const uint64_t m = __ballot(ok);
     const int idx = __popcll(m & ((1ull << lane) - 1ull));

@@ -143,12 +143,13 @@ bool fast_path(const kvq_config& c) {
          (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits));
 }
 
-// Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, at least 4 blocks per
-// wave, and enough workgroups (~1024) to cover the 256 CUs several times.  Generic path: ~2048
-// workgroups of >= 2 blocks.  Never more than 64 splits; monotone in nblk.
-// Bulk splits of the MFMA path: whole rounds of the workgroups the device holds at once (`slots`),
-// at least 4 blocks (one per wave) per split, at most 64 splits.
-int fast_splits(int streams, int nblk, int slots) {
+// Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, whole rounds of the
+// workgroups the device holds at once (`slots`), at least 4 blocks (one per wave) per split, at most
+// 64 splits.  `extra` fp16-row workgroups per stream run in the same launch, dispatched after the
+// bulk: when the splits are short (<= 8 blocks per wave, about as long as an fp16 workgroup) they
+// are fitted into the same round, otherwise they fill the slots the first finished splits free.
+// Generic path: ~2048 workgroups of >= 2 blocks.  Never more than 64 splits.
+int fast_splits(int streams, int nblk, int slots, int extra) {
   const int smax = std::max(1, std::min(64, nblk / 4));
   if (slots <= 0) slots = 1024;
   int best = 1;
@@ -165,12 +166,20 @@ int fast_splits(int streams, int nblk, int slots) {
     }
     if (eff >= 0.9) break;
   }
+  const int bps = (nblk + best - 1) / best;
+  if (extra > 0 && bps <= 32 && (long long)streams * (best + extra) > slots) {
+    const int s2 = std::min(smax, slots / streams - extra);
+    if (s2 >= 1) {
+      const int b2 = (nblk + s2 - 1) / s2;
+      best = (nblk + b2 - 1) / b2;
+    }
+  }
   return best;
 }
 
-int splits_for(const kvq_config& c, int nblk, int slots) {
+int splits_for(const kvq_config& c, int nblk, int slots, int extra) {
   const int streams = c.batch * c.n_kv_heads;
-  if (fast_path(c)) return fast_splits(streams, nblk, slots);
+  if (fast_path(c)) return fast_splits(streams, nblk, slots, extra);
   const int s = std::min((nblk + 1) / 2, std::max(1, (2048 + streams - 1) / streams));
   return std::max(1, std::min(s, 64));
 }
@@ -179,7 +188,7 @@ int splits_for(const kvq_config& c, int nblk, int slots) {
 int max_splits(const kvq_config& c) {
   const int nblk = effective_capacity(c) / G;
   if (fast_path(c)) return std::max(1, std::min(64, nblk / 4));
-  return splits_for(c, nblk, 0);
+  return splits_for(c, nblk, 0, 0);
 }
 
 // fp16-row partials of a decode call: the MFMA path scores the window rows and the sinks in groups
@@ -417,10 +426,14 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   a.lo = lo;
   a.bulk_lo = lo;
   a.bulk_hi = std::max(lo, P - (int64_t)cf.residual);
+  // fp16 rows: window rows [bulk_hi, P) and at most min(n_sink, P) committed sinks (the kernels read
+  // the committed count; groups past it write empty partials)
+  const int64_t fp_rows = (P - a.bulk_hi) + std::min<int64_t>(cf.n_sink, P);
+  const int fparts = fp16_parts(cf, fp_rows);
   if (a.bulk_hi > a.bulk_lo) {
     a.blk_first = a.bulk_lo / G;
     a.nblk = (int)((a.bulk_hi - 1) / G - a.blk_first + 1);
-    const int s = splits_for(cf, a.nblk, c->slots);
+    const int s = splits_for(cf, a.nblk, c->slots, fparts);
     a.blocks_per_split = (a.nblk + s - 1) / s;
     a.splits = (a.nblk + a.blocks_per_split - 1) / a.blocks_per_split;
   } else {
@@ -430,10 +443,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
     a.blocks_per_split = 0;
   }
   a.fast = fast_path(cf);
-  // fp16 rows: window rows [bulk_hi, P) and at most min(n_sink, P) committed sinks (the kernels read
-  // the committed count; groups past it write empty partials)
-  const int64_t fp_rows = (P - a.bulk_hi) + std::min<int64_t>(cf.n_sink, P);
-  a.nparts = a.splits + fp16_parts(cf, fp_rows);
+  a.nparts = a.splits + fparts;
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;
