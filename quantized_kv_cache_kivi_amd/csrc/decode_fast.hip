@@ -61,6 +61,10 @@ __device__ __forceinline__ f4 mfma(const u4& a, const u4& b, f4 c) {
                                                 0, 0);
 }
 __device__ __forceinline__ h2 H2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+// Bits of a 32-bit word as fp32.  Vector components pass through this scalar parameter: with this
+// toolchain, __builtin_bit_cast applied directly to an ext_vector component (v.y) reads component 0.
+__device__ __forceinline__ float F32(uint32_t w) { return __builtin_bit_cast(float, w); }
+__device__ __forceinline__ uint32_t F32bits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ uint32_t U32(h2 x) { return __builtin_bit_cast(uint32_t, x); }
 
 // The exact product of two fp16 pairs as fp16 hi = rn(a*b) and lo = rn(a*b - hi).
@@ -152,6 +156,40 @@ __device__ __forceinline__ u4 plane_a(const uint32_t* d, int k) {
   return r;
 }
 
+// A operands (fp16 hi and lo halves) of the 8 TurboQuant K centroids coded in word w: element pair
+// r holds the codes at bits 4r and 16 + 4r (word-interleaved 4-bit codes).  The centroid of a code
+// is one dword (hi | lo << 16) of a 16-entry LDS table (a wave reads at most 16 distinct dwords).
+__device__ __forceinline__ void tq_cen_a(uint32_t w, const uint32_t* tab, u4& ah, u4& al) {
+  uint32_t hh[4], ll[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t e0 = tab[(w >> (4 * r)) & 0xFu], e1 = tab[(w >> (16 + 4 * r)) & 0xFu];
+    hh[r] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);  // low halves of e0, e1
+    ll[r] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);  // high halves of e0, e1
+  }
+  ah = u4{hh[0], hh[1], hh[2], hh[3]};
+  al = u4{ll[0], ll[1], ll[2], ll[3]};
+}
+
+// Signed plane of code bit BIT of 2-bit codes, from the complemented code words nd: every element
+// is s = 2 * bit - 1 as fp16 +-1.0 (`one16` = 0x3C003C00; the sign bit is set where the code bit is
+// 0).  Planes of +-1 keep a symmetric 4-level grid free of a constant term, so sums over many
+// tokens do not cancel; normal (not subnormal) operands keep the products with small weights exact
+// (products of two fp16 subnormals lose precision on the matrix cores).  `one16` is passed in as a
+// value (not a literal) so that the merge of sign and magnitude stays one and-or.
+template <int BIT>
+__device__ __forceinline__ u4 splane_a(const uint32_t* nd, int k, uint32_t one16) {
+  const int base = (k & 1) ? 8 : 0;
+  const uint32_t w = nd[k >> 1];
+  uint32_t o[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t sgn = w << (15 - (base + 2 * r + BIT));  // complemented bit -> bits 15 and 31
+    o[r] = (sgn & 0x80008000u) | one16;
+  }
+  return u4{o[0], o[1], o[2], o[3]};
+}
+
 template <int R>
 struct alignas(16) FastWave {
   static constexpr int NC = 2 * R;  // MFMA columns in use: hi halves of heads 0..R-1, then lo halves
@@ -171,6 +209,7 @@ struct FastSmem {
   FastWave<R> w[NW];
   int sinks[MAX_SINK];  // committed sink positions (< P) of this batch element
   int nsinks;
+  uint32_t tq_tab[16];  // TurboQuant K centroids: fp16 hi | fp16 lo << 16
 };
 // LDS of an fp16-row workgroup (shares the allocation of the bulk workgroups).
 template <int R>
@@ -193,33 +232,43 @@ template <int KB, int VB>
 struct Blk {
   uint32_t kd[2][KB];  // K code rows i16 and 16 + i16, channels 32*kg .. 32*kg + 31
   uint32_t ks, kz;     // K scale (q2k: rms) and zero of channels 2*lane, 2*lane + 1
+                       // (TurboQuant: fp32 K norms of tokens 2*i16, 2*i16 + 1)
   uint32_t vd[2 * VB]; // V code chunk `lane`
   u4 vs, vz;           // V scale and zero of tokens 2*i16, 2*i16 + 1: [group][token] fp16
+                       // (TurboQuant: vs.x, vs.y = fp32 V norms of tokens 2*i16, 2*i16 + 1)
 };
 
 // Per-lane byte offsets, inside a block record, of what load_blk reads.
 struct BlkOffs {
   uint32_t k[2], ks, kz, v, vs, vz;
 };
-template <int KB, int VB>
+template <int FMT, int KB, int VB>
 __device__ __forceinline__ BlkOffs blk_offsets(const LayerView& lv, int lane) {
   const int i16 = lane & 15, kg = lane >> 4;
   BlkOffs o;
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) o.k[tau] = (uint32_t)(lv.k_codes + (16 * tau + i16) * (FD * KB / 8) + kg * 4 * KB);
-  o.ks = (uint32_t)(lv.k_meta + 4 * lane);
-  o.kz = (uint32_t)(lv.k_meta + 2 * FD + 4 * lane);
+  if constexpr (FMT == KVQ_FMT_TQ) {  // per-token fp32 norms: tokens 2*i16, 2*i16 + 1
+    o.ks = (uint32_t)(lv.k_meta + 8 * i16);
+    o.kz = o.ks;
+    o.vs = (uint32_t)(lv.v_meta + 8 * i16);
+    o.vz = o.vs;
+  } else {
+    o.ks = (uint32_t)(lv.k_meta + 4 * lane);
+    o.kz = (uint32_t)(lv.k_meta + 2 * FD + 4 * lane);
+    o.vs = (uint32_t)(lv.v_meta + 16 * i16);
+    o.vz = (uint32_t)(lv.v_meta + 2 * G * (FD / 32) + 16 * i16);
+  }
   o.v = (uint32_t)(lv.v_codes + lane * 8 * VB);
-  o.vs = (uint32_t)(lv.v_meta + 16 * i16);
-  o.vz = (uint32_t)(lv.v_meta + 2 * G * (FD / 32) + 16 * i16);
   return o;
 }
 
 // One block record into registers: buffer loads from the stream's ring with the record's byte
 // offset in a scalar register and fixed per-lane offsets (no address arithmetic per block).
-template <bool Q2K, int KB, int VB>
+template <int FMT, int KB, int VB>
 __device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t rs, uint32_t rec_off,
                                          const BlkOffs& o) {
+  constexpr bool Q2K = FMT == KVQ_FMT_Q2K, TQ = FMT == KVQ_FMT_TQ;
   // the loads of one record stay together and in this order (scheduling barriers), so the wait
   // counts the compiler derives for each block are the count of loads issued after it
   __builtin_amdgcn_sched_barrier(0);
@@ -236,22 +285,34 @@ __device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t 
       }
     }
   }
-  d.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, o.ks, rec_off, 0);
-  d.kz = Q2K ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rs, o.kz, rec_off, 0);
+  if constexpr (TQ) {
+    const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, o.ks, rec_off, 0);
+    d.ks = x.x, d.kz = x.y;
+  } else {
+    d.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, o.ks, rec_off, 0);
+    d.kz = Q2K ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rs, o.kz, rec_off, 0);
+  }
 #pragma unroll
   for (int k = 0; k < VB / 2; ++k) {
     const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * k, rec_off, 0);
     d.vd[4 * k] = x.x, d.vd[4 * k + 1] = x.y, d.vd[4 * k + 2] = x.z, d.vd[4 * k + 3] = x.w;
   }
-  d.vs = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vs, rec_off, 0);
-  if constexpr (!Q2K) d.vz = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vz, rec_off, 0);
-  else d.vz = u4{0, 0, 0, 0};
+  if constexpr (TQ) {
+    const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, o.vs, rec_off, 0);
+    d.vs = u4{x.x, x.y, 0u, 0u};
+    d.vz = u4{0, 0, 0, 0};
+  } else {
+    d.vs = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vs, rec_off, 0);
+    if constexpr (!Q2K) d.vz = __builtin_amdgcn_raw_buffer_load_b128(rs, o.vz, rec_off, 0);
+    else d.vz = u4{0, 0, 0, 0};
+  }
   __builtin_amdgcn_sched_barrier(0);
 }
 
 template <int FMT, int KB, int VB, int R>
 struct Fast {
   static constexpr bool Q2K = FMT == KVQ_FMT_Q2K;
+  static constexpr bool TQ = FMT == KVQ_FMT_TQ;
   static constexpr int NC = 2 * R;
   static constexpr int NPL = R <= 4 ? 1 : R / 4;  // (head, token pair) slots per lane in the compact phase
   static constexpr int NKA = Q2K ? 2 : 1;         // K accumulators per token tile (q2k: one per code bit)
@@ -263,7 +324,9 @@ struct State {
   using F = Fast<FMT, KB, VB, R>;
   h2 q2[R];             // query channels 2*lane, 2*lane + 1 (fp16)
   h2 fa2;               // 2^-pos of their K element pair
-  float cs, kc;         // score = fma(raw, cs, kappa * kc), log2 units
+  float cs, kc;         // score = fma(raw, cs, kappa * kc), log2 units (TurboQuant: raw * cs * K norm)
+  float vb, vg;         // TurboQuant V level = cm + vb * s0 + vg * s1, s = 2 * bit - 1
+  uint32_t one16;       // TurboQuant: fp16 pair (1.0, 1.0)
   float lf, ifv;        // -log2 and 2^ of the V position factor of this lane's token pair
   float m_[F::NPL], lfm[F::NPL], l_[F::NPL], zacc[F::NPL][4];
   f4 acc[8];
@@ -272,16 +335,18 @@ struct State {
 template <int FMT, int KB, int VB, int R>
 __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>& W, const int* sinks,
                                            const Blk<KB, VB>& d, int blk, int blo, int bhi, int sblk, int nsink,
-                                           float q2k_w, int lane) {
+                                           float q2k_w, const uint32_t* tab, int lane) {
   using F = Fast<FMT, KB, VB, R>;
   constexpr bool Q2K = F::Q2K;
+  constexpr bool TQ = F::TQ;
   constexpr int NPL = F::NPL;
   const int i16 = lane & 15, kg = lane >> 4, tp = i16;
   // MFMA column of this lane; padding lanes repeat the last column (identical values, identical stores)
   const int col = i16 < F::NC ? i16 : F::NC - 1;
 
   // ---- query operand: the exact products q * s split hi (column j) / lo (R + j), times 2^-pos ----
-  {
+  // (TurboQuant: the rotated query, written once before the loop)
+  if constexpr (!TQ) {
     const h2 s2 = H2(d.ks);
     const h2 z2 = Q2K ? s2 : H2(d.kz);
 #pragma unroll
@@ -305,6 +370,11 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
         if constexpr (Q2K) {
           c0[tau] = mfma(plane_a<0>(d.kd[tau], st), b, c0[tau]);
           c1[tau] = mfma(plane_a<1>(d.kd[tau], st), b, c1[tau]);
+        } else if constexpr (TQ) {  // centroid hi halves, then lo halves, into one accumulator
+          u4 ah, al;
+          tq_cen_a(d.kd[tau][st], tab, ah, al);
+          c0[tau] = mfma(ah, b, c0[tau]);
+          c0[tau] = mfma(al, b, c0[tau]);
         } else {
           c0[tau] = mfma(codes_a<KB>(d.kd[tau], st), b, c0[tau]);
         }
@@ -338,12 +408,17 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
   for (int p = 0; p < NPL; ++p) {
     const int jr = kg + 4 * p;
     const int j = jr < R ? jr : R - 1;  // lanes past the last head repeat it (identical stores)
-    const f4 kq = *reinterpret_cast<const f4*>(&W.kp[j][4 * tp]);
-    const float kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3])) * S.kc;
     const f2 hi = *reinterpret_cast<const f2*>(&W.ps[j][2 * tp]);
     const f2 lo = *reinterpret_cast<const f2*>(&W.ps[R + j][2 * tp]);
-    y0[p] = ok0 ? __builtin_fmaf(hi.x + lo.x, S.cs, kap) : -INFINITY;
-    y1[p] = ok1 ? __builtin_fmaf(hi.y + lo.y, S.cs, kap) : -INFINITY;
+    if constexpr (TQ) {  // score = scale * K norm * (rotated query . centroids)
+      y0[p] = ok0 ? (hi.x + lo.x) * (S.cs * F32(d.ks)) : -INFINITY;
+      y1[p] = ok1 ? (hi.y + lo.y) * (S.cs * F32(d.kz)) : -INFINITY;
+    } else {
+      const f4 kq = *reinterpret_cast<const f4*>(&W.kp[j][4 * tp]);
+      const float kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3])) * S.kc;
+      y0[p] = ok0 ? __builtin_fmaf(hi.x + lo.x, S.cs, kap) : -INFINITY;
+      y1[p] = ok1 ? __builtin_fmaf(hi.y + lo.y, S.cs, kap) : -INFINITY;
+    }
     grow = grow || fmaxf(y0[p], y1[p]) > S.m_[p];
   }
   // a new running maximum somewhere in the wave: reduce the row maxima and rescale
@@ -371,6 +446,23 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
     // weights times the V position factor of this token pair; masked tokens give 2^-inf = 0
     const float e0 = ex2(y0[p] + S.lfm[p]), e1 = ex2(y1[p] + S.lfm[p]);
     S.l_[p] = __builtin_fmaf(e0 + e1, S.ifv, S.l_[p]);
+    if constexpr (TQ) {
+      // V level = cm + vb * s0 + vg * s1 (s = 2 * bit - 1) in the rotated domain, times the V
+      // norm: the two signed bit planes take the weights w * vb and w * vg (split hi/lo), the cm
+      // term is sum_t w (cm = 0 for the symmetric grids the library builds)
+      const float w0 = e0 * F32(d.vs.x), w1 = e1 * F32(d.vs.y);
+      S.zacc[p][0] += w0 + w1;
+      const float xb0 = w0 * S.vb, xb1 = w1 * S.vb, xg0 = w0 * S.vg, xg1 = w1 * S.vg;
+      const h2 bh = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xb0, xb1));
+      const h2 bl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xb0 - (float)bh.x, xb1 - (float)bh.y));
+      const h2 gh = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xg0, xg1));
+      const h2 gl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xg0 - (float)gh.x, xg1 - (float)gh.y));
+      W.ab[0][j][4 * kgt + (et >> 1)] = U32(bh);
+      W.ab[0][R + j][4 * kgt + (et >> 1)] = U32(bl);
+      W.ab[1][j][4 * kgt + (et >> 1)] = U32(gh);
+      W.ab[1][R + j][4 * kgt + (et >> 1)] = U32(gl);
+      continue;
+    }
     const h2 ph = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(e0, e1));
     const h2 pl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(e0 - (float)ph.x, e1 - (float)ph.y));
     const uint32_t vs[4] = {d.vs.x, d.vs.y, d.vs.z, d.vs.w};
@@ -392,11 +484,22 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
 #pragma unroll
     for (int mu = 0; mu < 8; ++mu) S.acc[mu] *= fc;
   }
+  if constexpr (TQ) {
+    const u4 b0 = *reinterpret_cast<const u4*>(&W.ab[0][col][4 * kg]);
+    const u4 b1 = *reinterpret_cast<const u4*>(&W.ab[1][col][4 * kg]);
+    const uint32_t nd[4] = {~d.vd[0], ~d.vd[1], ~d.vd[2], ~d.vd[3]};
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const u4 bq = *reinterpret_cast<const u4*>(&W.ab[q][col][4 * kg]);
+    for (int mu = 0; mu < 8; ++mu) {
+      S.acc[mu] = mfma(splane_a<0>(nd, mu, S.one16), b0, S.acc[mu]);
+      S.acc[mu] = mfma(splane_a<1>(nd, mu, S.one16), b1, S.acc[mu]);
+    }
+  } else {
 #pragma unroll
-    for (int mu = 2 * q; mu < 2 * q + 2; ++mu) S.acc[mu] = mfma(codes_a<VB>(d.vd, mu), bq, S.acc[mu]);
+    for (int q = 0; q < 4; ++q) {
+      const u4 bq = *reinterpret_cast<const u4*>(&W.ab[q][col][4 * kg]);
+#pragma unroll
+      for (int mu = 2 * q; mu < 2 * q + 2; ++mu) S.acc[mu] = mfma(codes_a<VB>(d.vd, mu), bq, S.acc[mu]);
+    }
   }
 }
 
@@ -405,6 +508,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   using Fc = Fast<FMT, KB, VB, R>;
   using St = State<FMT, KB, VB, R>;
   constexpr bool Q2K = Fc::Q2K;
+  constexpr bool TQ = Fc::TQ;
   constexpr int NPL = Fc::NPL;
   constexpr int PV = code_pos<VB>(3);
   const Shape sh = a.sh;
@@ -423,7 +527,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   // the stream's ring as a buffer resource (every record offset fits in 32 bits: checked on the host)
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(lv.bulk + (int64_t)s * lv.cap_b * lv.rec), 0, (int)(lv.cap_b * lv.rec), 0x00020000);
-  const BlkOffs bo = blk_offsets<KB, VB>(lv, lane);
+  const BlkOffs bo = blk_offsets<FMT, KB, VB>(lv, lane);
   auto rec_of = [&](int bi) -> uint32_t {
     bi = bi < lastb ? bi : lastb - 1;  // past the split: re-read its last block (a cache hit), never used
     int sl = slot0 + bi;
@@ -437,11 +541,30 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   // carries exactly one block (the compiler's wait counts inside the loop then stay exact).
   Blk<KB, VB> d0, d1;
   int bi = first + wv;
-  if (bi < lastb) load_blk<Q2K>(d0, rs, rec_of(bi), bo);
+  if (bi < lastb) load_blk<FMT>(d0, rs, rec_of(bi), bo);
   St S;
   const float al = a.scale * LOG2E;
-  float q2k_w = 0.f;
-  if constexpr (Q2K) {
+  float q2k_w = 0.f, tq_c0 = 0.f;
+  float sg0 = 0.f, sg1 = 0.f, kcen = 0.f;
+  if constexpr (TQ) {
+    // rotated-domain centroids enter the MFMA as real values: no code-position factor
+    S.cs = al;
+    S.kc = 0.f;
+    // level(u) = cm + vb * s0 + vg * s1 for u = b0 + 2 b1, s = 2b - 1: exact when the grid has
+    // c0 + c3 = c1 + c2 (the symmetric Lloyd-Max grid, where cm = 0)
+    const float c0 = lv.tables->v_cen[0], c3 = lv.tables->v_cen[3];
+    S.vb = 0.5f * (lv.tables->v_cen[1] - c0);
+    S.vg = 0.5f * (lv.tables->v_cen[2] - c0);
+    tq_c0 = 0.5f * (c0 + c3);
+    sg0 = lv.tables->signs[2 * lane];
+    sg1 = lv.tables->signs[2 * lane + 1];
+    // 1 in every lane, as a per-lane run-time value (bit 29 of the fp32 +-1 sign entries), so the
+    // fp16 pair (1.0, 1.0) lives in a vector register and each plane register is one shift plus one
+    // and-or
+    const uint32_t one = (F32bits(sg0) >> 29) & 1u;
+    S.one16 = one * 0x3C003C00u;
+    kcen = tid < 16 ? lv.tables->k_cen[tid] : 0.f;
+  } else if constexpr (Q2K) {
     const float c0 = lv.tables->q2k_lvl[0], c1 = lv.tables->q2k_lvl[1] - c0, c2 = lv.tables->q2k_lvl[2] - c0;
     S.cs = ldexpf(c1 * al, 24);
     S.kc = c0 * al;
@@ -458,9 +581,10 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
 #pragma unroll
     for (int j = 0; j < R; ++j)
       S.q2[j] = H2(reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + j * FD)[lane]);
-    // weights carry 2^(PV - pv): the V codes of this lane's token pair sit at bit pv
+    // weights carry 2^(PV - pv): the V codes of this lane's token pair sit at bit pv (TurboQuant's
+    // signed planes are +-1 at every position: no factor)
     const int t0 = 2 * i16, et = ((t0 >> 4) << 2) | (t0 & 3);
-    const int pv = code_pos<VB>(et >> 1);
+    const int pv = TQ ? PV : code_pos<VB>(et >> 1);
     S.lf = (float)(PV - pv);
     S.ifv = ldexpf(1.f, pv - PV);
   }
@@ -475,20 +599,43 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   }
 #pragma unroll
   for (int mu = 0; mu < 8; ++mu) S.acc[mu] = f4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (TQ) {
+    if (tid < 16) {  // K centroid table: fp16 hi and lo halves
+      const _Float16 h = (_Float16)kcen;
+      F.tq_tab[tid] = U32(h2{h, (_Float16)(kcen - (float)h)});
+    }
+  }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query, the sink list and the first block
   __syncthreads();
+  if constexpr (TQ) {
+    // rotated query q~ = c_d * FWHT(sigma * q) ("TurboQuant KV Cache Compression — Spec", "Step 1:
+    // Random Rotation"; "Optimization: Fused dequant-dot": scores in the rotated domain), split into
+    // fp16 hi (column j) and lo (column R + j): the K operand of every block of the call
+    const float cd = (float)(1.0 / __builtin_sqrt((double)FD));
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float y0 = (float)S.q2[j].x * sg0, y1 = (float)S.q2[j].y * sg1;
+      wave_fwht(y0, y1, FD, lane);
+      y0 *= cd;
+      y1 *= cd;
+      const h2 h = h2{(_Float16)y0, (_Float16)y1};
+      const h2 l = h2{(_Float16)(y0 - (float)h.x), (_Float16)(y1 - (float)h.y)};
+      W.x.qb[j][lane] = U32(h);
+      W.x.qb[R + j][lane] = U32(l);
+    }
+  }
 
   const int nsink = __builtin_amdgcn_readfirstlane(F.nsinks);
   const int sblk = lane < nsink ? F.sinks[lane] / G : -1;  // block of sink `lane`
 
   if (bi < lastb) {
     while (true) {
-      load_blk<Q2K>(d1, rs, rec_of(bi + NW), bo);
-      block_step(S, W, F.sinks, d0, blkf + bi, blo, bhi, sblk, nsink, q2k_w, lane);
+      load_blk<FMT>(d1, rs, rec_of(bi + NW), bo);
+      block_step(S, W, F.sinks, d0, blkf + bi, blo, bhi, sblk, nsink, q2k_w, F.tq_tab, lane);
       bi += NW;
       if (bi >= lastb) break;
-      load_blk<Q2K>(d0, rs, rec_of(bi + NW), bo);
-      block_step(S, W, F.sinks, d1, blkf + bi, blo, bhi, sblk, nsink, q2k_w, lane);
+      load_blk<FMT>(d0, rs, rec_of(bi + NW), bo);
+      block_step(S, W, F.sinks, d1, blkf + bi, blo, bhi, sblk, nsink, q2k_w, F.tq_tab, lane);
       bi += NW;
       if (bi >= lastb) break;
     }
@@ -502,8 +649,13 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     const float lsum = row_sum16(S.l_[p]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float z = row_sum16(S.zacc[p][q] * S.ifv);
-      if constexpr (Q2K) z = -8.f * z;
+      float z;
+      if constexpr (TQ) {  // cm * sum_t w (one value for every channel group)
+        z = tq_c0 * row_sum16(S.zacc[p][0] * S.ifv);
+      } else {
+        z = row_sum16(S.zacc[p][q] * S.ifv);
+        if constexpr (Q2K) z = -8.f * z;
+      }
       if (jr < R && tp == 0) W.zt[jr][q] = z;
     }
     if (jr < R && tp == 0) {
@@ -511,7 +663,8 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
       W.l[jr] = lsum;
     }
   }
-  const float SV = ldexpf(1.f, 24 - PV);  // V codes entered as u * 2^(pv - 24), the weights carried 2^(PV - pv)
+  // V codes entered as u * 2^(pv - 24), the weights carried 2^(PV - pv) (TurboQuant: +-1 planes)
+  const float SV = TQ ? 1.f : ldexpf(1.f, 24 - PV);
 #pragma unroll
   for (int mu = 0; mu < 8; ++mu) {
     f4 lo;
@@ -688,7 +841,7 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
 // Waves per SIMD the register allocation targets.
 template <int FMT, int KB, int VB, int R>
 constexpr int waves_target() {
-  return (R <= 4 && KB == 2) ? 3 : 2;
+  return (R <= 4 && (KB == 2 || FMT == KVQ_FMT_TQ)) ? 3 : 2;
 }
 
 template <int FMT, int KB, int VB, int R>
@@ -699,29 +852,22 @@ void k_decode_fast(DecodeArgs a) {
   else fp16_partial<R>(a, S.fp, (int)blockIdx.y - a.splits);
 }
 
-// Fixed-order merge of the partials of one (stream, query head): bulk splits, then fp16 groups.
-// The partials are read in chunks of MC, all loads of a chunk at once, with the running maximum
-// and sums rescaled between chunks (one memory round trip per chunk).
+// Online merge of partials [q0, q1) of one (stream, query head) into (M, L, v): the partials are read
+// in chunks of MC, all loads of a chunk at once, with the running maximum and sums rescaled
+// between chunks (one memory round trip per chunk).
 template <int R>
-__global__ __launch_bounds__(FD) void k_merge_parts(DecodeArgs a) {
+__device__ __forceinline__ void merge_range(const float* P0, int q0, int q1, int c, float& M, float& L, float& v) {
   constexpr int MC = 16;
-  const int s = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
-  const int b = s / a.sh.Hkv, g = s % a.sh.Hkv;
-  const float* P0 = a.ws + (int64_t)s * a.nparts * R * (FD + 2) + j * (FD + 2);
-  const int np = a.nparts;
-  float M = -INFINITY, L = 0.f, v = 0.f;
-  for (int q0 = 0; q0 < np; q0 += MC) {
+  for (int qb = q0; qb < q1; qb += MC) {
     float mq[MC], lq[MC], vq[MC];
 #pragma unroll
-    for (int k = 0; k < MC; ++k) {
-      mq[k] = -INFINITY;
-      lq[k] = vq[k] = 0.f;
-      if (q0 + k < np) {
-        const float* pq = P0 + (int64_t)(q0 + k) * R * (FD + 2);
-        mq[k] = pq[0];
-        lq[k] = pq[1];
-        vq[k] = pq[2 + c];
-      }
+    for (int k = 0; k < MC; ++k) {  // past the last part: re-read it (no branch between the loads), unused
+      const bool in = qb + k < q1;
+      const float* pq = P0 + (int64_t)(in ? qb + k : q1 - 1) * R * (FD + 2);
+      const float m = pq[0], l = pq[1], x = pq[2 + c];
+      mq[k] = in ? m : -INFINITY;
+      lq[k] = in ? l : 0.f;
+      vq[k] = in ? x : 0.f;
     }
     float Mn = M;
 #pragma unroll
@@ -737,6 +883,37 @@ __global__ __launch_bounds__(FD) void k_merge_parts(DecodeArgs a) {
     }
     M = Mn;
   }
+}
+
+// Fixed-order merge of the partials of one (stream, query head): bulk splits, then fp16 groups.
+// TurboQuant bulk partials live in the rotated domain: they are merged first and rotated back
+// (sigma * (c_d * FWHT(acc)); "TurboQuant KV Cache Compression — Spec", "Optimization: Fused
+// dequant-dot") before the fp16 groups, which are in the original domain, join the merge.
+template <int R, bool TQ>
+__global__ __launch_bounds__(FD) void k_merge_parts(DecodeArgs a) {
+  const int s = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
+  const int b = s / a.sh.Hkv, g = s % a.sh.Hkv;
+  const float* P0 = a.ws + (int64_t)s * a.nparts * R * (FD + 2) + j * (FD + 2);
+  const int np = a.nparts;
+  float M = -INFINITY, L = 0.f, v = 0.f;
+  if constexpr (TQ) {
+    __shared__ float rot[FD];
+    merge_range<R>(P0, 0, a.splits, c, M, L, v);
+    rot[c] = v;
+    __syncthreads();
+    if (c < 64) {
+      float y0 = rot[2 * c], y1 = rot[2 * c + 1];
+      wave_fwht(y0, y1, FD, c);
+      const float cd = (float)(1.0 / __builtin_sqrt((double)FD));
+      rot[2 * c] = a.lv.tables->signs[2 * c] * (y0 * cd);
+      rot[2 * c + 1] = a.lv.tables->signs[2 * c + 1] * (y1 * cd);
+    }
+    __syncthreads();
+    v = rot[c];
+    merge_range<R>(P0, a.splits, np, c, M, L, v);
+  } else {
+    merge_range<R>(P0, 0, np, c, M, L, v);
+  }
   a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * FD + c] = v / L;
 }
 
@@ -747,22 +924,23 @@ hipError_t launch_r(const DecodeArgs& a, hipStream_t st) {
   // parts vary slowest: the (short) fp16 workgroups are dispatched after every bulk split
   dim3 grid(S, a.nparts);
   dim3 mgrid(S, r);
+  constexpr bool TQ = FMT == KVQ_FMT_TQ;
   switch (r) {
     case 1:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 1>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<1>), mgrid, dim3(FD), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<1, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     case 2:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 2>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<2>), mgrid, dim3(FD), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<2, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     case 4:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 4>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<4>), mgrid, dim3(FD), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<4, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     case 8:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 8>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<8>), mgrid, dim3(FD), 0, st, a);
+      hipLaunchKernelGGL((k_merge_parts<8, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -793,6 +971,7 @@ int fast_resident_slots(const Shape& sh) {
   const int r = sh.Hq / sh.Hkv;
   if (sh.D != FD) return 0;
   if (sh.fmt == KVQ_FMT_Q2K) return slots_r<KVQ_FMT_Q2K, 2, 4>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return slots_r<KVQ_FMT_TQ, 4, 2>(r, cus);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return slots_r<KVQ_FMT_KIVI, 2, 2>(r, cus);
     if (sh.kb == 4) return slots_r<KVQ_FMT_KIVI, 4, 4>(r, cus);
@@ -809,6 +988,7 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
   if (sh.D != FD || a.nparts == 0 || sh.in_f32) return hipErrorInvalidValue;
   if (sh.fmt == KVQ_FMT_Q2K) return launch_r<KVQ_FMT_Q2K, 2, 4>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return launch_r<KVQ_FMT_TQ, 4, 2>(a, st);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2>(a, st);
     if (sh.kb == 4) return launch_r<KVQ_FMT_KIVI, 4, 4>(a, st);

@@ -140,7 +140,8 @@ kvq_layout make_layout(const kvq_config& c) {
 bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
   return c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && (r == 1 || r == 2 || r == 4 || r == 8) &&
-         (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits));
+         (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits) ||
+          (c.format == KVQ_FMT_TQ && c.k_bits == 4 && c.v_bits == 2));
 }
 
 // Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, whole rounds of the

@@ -39,6 +39,12 @@ CASES = {
                                    k_bits=2, v_bits=2, sink_mode="topk", n_sink=4, residual=200, capacity=512),
     "fast_q2k_r8_topk": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="q2k", k_bits=2,
                              v_bits=4, sink_mode="topk", n_sink=4, residual=40, capacity=512),
+    "fast_tq42_r8_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="tq", k_bits=4,
+                                  v_bits=2, sink_mode="topk", n_sink=3, residual=40, capacity=512, seed=11),
+    "fast_tq42_r1_win": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=128, fmt="tq", k_bits=4,
+                             v_bits=2, sink_mode="first_n", n_sink=4, window=96, residual=8, seed=12),
+    "fast_tq42_r2_ring_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128, fmt="tq", k_bits=4,
+                                  v_bits=2, window=160, residual=16, seed=13),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]
