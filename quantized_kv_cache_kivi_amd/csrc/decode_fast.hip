@@ -55,6 +55,11 @@ typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 constexpr int FD = 128;       // head_dim of this path
 constexpr int NW = DNT / 64;  // waves per workgroup
 constexpr int FPR = 64;       // fp16 rows per fp16 workgroup
+// The lo halves of the split query operand (all formats, times 2^9) and of TurboQuant's V weights
+// (times 2^11) are stored scaled up, in the range of the hi halves, and the lo columns are scaled
+// back when combined: products of two fp16 subnormals lose precision on the matrix cores.
+constexpr float LO_UP = 2048.f, LO_DOWN = 1.f / 2048.f;
+constexpr float LOK_UP = 512.f, LOK_DOWN = 1.f / 512.f;
 
 __device__ __forceinline__ f4 mfma(const u4& a, const u4& b, f4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0,
@@ -323,7 +328,7 @@ template <int FMT, int KB, int VB, int R>
 struct State {
   using F = Fast<FMT, KB, VB, R>;
   h2 q2[R];             // query channels 2*lane, 2*lane + 1 (fp16)
-  h2 fa2;               // 2^-pos of their K element pair
+  h2 fa2, fa2l;         // 2^-pos of their K element pair (lo halves: times 2^11)
   float cs, kc;         // score = fma(raw, cs, kappa * kc), log2 units (TurboQuant: raw * cs * K norm)
   float vb, vg;         // TurboQuant V level = cm + vb * s0 + vg * s1, s = 2 * bit - 1
   uint32_t one16;       // TurboQuant: fp16 pair (1.0, 1.0)
@@ -354,7 +359,7 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
       uint32_t h, l;
       mul_split(S.q2[j], s2, h, l);
       W.x.qb[j][lane] = U32(H2(h) * S.fa2);
-      W.x.qb[R + j][lane] = U32(H2(l) * S.fa2);
+      W.x.qb[R + j][lane] = U32(H2(l) * S.fa2l);
       W.kp[j][lane] = dot2(S.q2[j], z2, 0.f);
     }
   }
@@ -411,13 +416,13 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
     const f2 hi = *reinterpret_cast<const f2*>(&W.ps[j][2 * tp]);
     const f2 lo = *reinterpret_cast<const f2*>(&W.ps[R + j][2 * tp]);
     if constexpr (TQ) {  // score = scale * K norm * (rotated query . centroids)
-      y0[p] = ok0 ? (hi.x + lo.x) * (S.cs * F32(d.ks)) : -INFINITY;
-      y1[p] = ok1 ? (hi.y + lo.y) * (S.cs * F32(d.kz)) : -INFINITY;
+      y0[p] = ok0 ? __builtin_fmaf(lo.x, LOK_DOWN, hi.x) * (S.cs * F32(d.ks)) : -INFINITY;
+      y1[p] = ok1 ? __builtin_fmaf(lo.y, LOK_DOWN, hi.y) * (S.cs * F32(d.kz)) : -INFINITY;
     } else {
       const f4 kq = *reinterpret_cast<const f4*>(&W.kp[j][4 * tp]);
       const float kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3])) * S.kc;
-      y0[p] = ok0 ? __builtin_fmaf(hi.x + lo.x, S.cs, kap) : -INFINITY;
-      y1[p] = ok1 ? __builtin_fmaf(hi.y + lo.y, S.cs, kap) : -INFINITY;
+      y0[p] = ok0 ? __builtin_fmaf(__builtin_fmaf(lo.x, LOK_DOWN, hi.x), S.cs, kap) : -INFINITY;
+      y1[p] = ok1 ? __builtin_fmaf(__builtin_fmaf(lo.y, LOK_DOWN, hi.y), S.cs, kap) : -INFINITY;
     }
     grow = grow || fmaxf(y0[p], y1[p]) > S.m_[p];
   }
@@ -454,9 +459,11 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
       S.zacc[p][0] += w0 + w1;
       const float xb0 = w0 * S.vb, xb1 = w1 * S.vb, xg0 = w0 * S.vg, xg1 = w1 * S.vg;
       const h2 bh = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xb0, xb1));
-      const h2 bl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xb0 - (float)bh.x, xb1 - (float)bh.y));
+      const h2 bl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz((xb0 - (float)bh.x) * LO_UP,
+                                                                       (xb1 - (float)bh.y) * LO_UP));
       const h2 gh = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xg0, xg1));
-      const h2 gl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(xg0 - (float)gh.x, xg1 - (float)gh.y));
+      const h2 gl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz((xg0 - (float)gh.x) * LO_UP,
+                                                                       (xg1 - (float)gh.y) * LO_UP));
       W.ab[0][j][4 * kgt + (et >> 1)] = U32(bh);
       W.ab[0][R + j][4 * kgt + (et >> 1)] = U32(bl);
       W.ab[1][j][4 * kgt + (et >> 1)] = U32(gh);
@@ -578,6 +585,8 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     const int pk = Q2K ? 2 * (lane & 3) : code_pos<KB>(lane & 3);
     const _Float16 fa = (_Float16)ldexpf(1.f, -pk);
     S.fa2 = h2{fa, fa};
+    const _Float16 fal = (_Float16)ldexpf(1.f, 9 - pk);
+    S.fa2l = h2{fal, fal};
 #pragma unroll
     for (int j = 0; j < R; ++j)
       S.q2[j] = H2(reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + j * FD)[lane]);
@@ -619,7 +628,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
       y0 *= cd;
       y1 *= cd;
       const h2 h = h2{(_Float16)y0, (_Float16)y1};
-      const h2 l = h2{(_Float16)(y0 - (float)h.x), (_Float16)(y1 - (float)h.y)};
+      const h2 l = h2{(_Float16)((y0 - (float)h.x) * LOK_UP), (_Float16)((y1 - (float)h.y) * LOK_UP)};
       W.x.qb[j][lane] = U32(h);
       W.x.qb[R + j][lane] = U32(l);
     }
@@ -672,7 +681,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     for (int i = 0; i < 4; ++i) lo[i] = __shfl(S.acc[mu][i], lane + R);
     if (i16 < R) {
       const float zt = W.zt[i16][mu >> 1];
-      const f4 v = S.acc[mu] + lo;
+      const f4 v = S.acc[mu] + lo * (TQ ? LO_DOWN : 1.f);
       *reinterpret_cast<f4*>(&W.x.o[i16][16 * mu + 4 * kg]) =
           f4{v[0] * SV + zt, v[1] * SV + zt, v[2] * SV + zt, v[3] * SV + zt};
     }
