@@ -119,6 +119,9 @@ typedef struct { /* byte offsets inside the caller's device buffer */
   uint64_t sink_k, sink_v;        /* [batch][n_kv_heads][n_sink][head_dim] fp16 */
   uint64_t sink_pos, sink_score, sink_count; /* [batch][n_sink] int32, fp32; [batch] int32 */
   uint64_t tables;                /* once, not per layer: fp32 tables (TQ signs and codebooks, Q2K grid) */
+  uint64_t select_work;           /* once, not per layer (TOPK mode): [batch][64][n_sink] (fp32 score, int32
+                                     position) top-k lists of the workgroups of one sink-selection call;
+                                     contents between calls carry no state */
   uint64_t total;                 /* = kvq_required_bytes */
   int32_t cap_blocks;
   int32_t capacity;
@@ -150,8 +153,10 @@ kvq_status kvq_destroy(kvq_cache* c);
  * works", 1): per-token key L2 norm averaged over KV heads, folded into a
  * running top-k of absolute positions; new rows of that top-k join the
  * permanent sink set while it has room ([KS] "Fidelity to the paper": no
- * retroactive restore).  k: [batch][n_kv_heads][n][head_dim].  Required
- * before kvq_append in TOPK mode (else KVQ_EORDER); a no-op in other modes. */
+ * retroactive restore).  k: [batch][n_kv_heads][n][head_dim], 16-byte
+ * aligned in TOPK mode (else KVQ_EINVAL).  Required before kvq_append in TOPK
+ * mode (else KVQ_EORDER); a no-op in other modes.  Uses the cache's
+ * select_work area: calls on one cache must be ordered (one stream). */
 kvq_status kvq_select_sinks(kvq_cache* c, int32_t layer, const void* k, int32_t n, void* stream);
 
 /* Appends n rows of K and V at positions [P, P+n) of `layer` and quantizes

@@ -132,7 +132,9 @@ kvq_layout make_layout(const kvq_config& c) {
   off = align256(off + (uint64_t)c.batch * 4);
   L.layer_stride = off;
   L.tables = (uint64_t)c.n_layers * L.layer_stride;
-  L.total = L.tables + align256(sizeof(Tables));
+  L.select_work = L.tables + align256(sizeof(Tables));
+  const uint64_t sel = c.sink_mode == KVQ_SINK_TOPK ? (uint64_t)c.batch * SELECT_GMAX * c.n_sink * 8 : 0;
+  L.total = L.select_work + align256(sel);
   return L;
 }
 
@@ -353,10 +355,12 @@ kvq_status kvq_select_sinks(kvq_cache* c, int32_t layer, const void* k, int32_t 
   c->pend_P[layer] = c->P[layer];
   c->pend_n[layer] = n;
   if (c->cfg.sink_mode != KVQ_SINK_TOPK || c->cfg.n_sink == 0) return KVQ_OK;
+  if ((uintptr_t)k % 16 != 0) return fail(KVQ_EINVAL, "TOPK mode: k must be 16-byte aligned");
   SelectArgs a;
   a.sh = shape_of(c->cfg);
   a.lv = view_of(c, layer);
   a.k = k;
+  a.work = (int2*)(c->base + c->lay.select_work);
   a.P = c->P[layer];
   a.n = n;
   hipError_t e = launch_select(a, (hipStream_t)stream);

@@ -13,6 +13,8 @@ constexpr int G = 32;          // token block length and V channel-group length
 constexpr int MAX_SINK = 16;   // largest n_sink
 constexpr int MAX_GQA = 16;    // largest n_q_heads / n_kv_heads
 constexpr int MAX_D = 128;     // largest head_dim
+constexpr int SELECT_GMAX = 64;      // most workgroups per batch element of one sink-selection call
+constexpr int SELECT_MIN_ROWS = 64;  // rows a selection workgroup takes at least
 
 // fp32 tables written once into the device buffer (tables region).
 struct Tables {
@@ -59,7 +61,8 @@ struct AppendArgs {
 struct SelectArgs {
   Shape sh;
   LayerView lv;
-  const void* k;
+  const void* k;        // [B][Hkv][n][D] in_dtype, 16-byte aligned
+  int2* work;           // [B][SELECT_GMAX][n_sink] (fp32 score bits, position): per-workgroup top-k lists
   int64_t P;
   int n;
 };
@@ -93,6 +96,7 @@ struct DequantArgs {
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+int select_groups(int n);  // workgroups per batch element for an n-row selection call
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 

@@ -1,126 +1,154 @@
 // Sink selection ("KVSink-Adapted Sink Protection", "How it works", step 1,
 // and "Fidelity to the paper": key-norm proxy, prefill-dominant, no retroactive
-// restore).  One workgroup per batch element:
+// restore).  For each batch element b:
 //   score_t = (sum over KV heads, in order, of sqrt(canonical sumsq of K[b,h,t,:])) / Hkv
 // is folded into the running top-k (rank: score descending, position
 // ascending); new rows of the merged top-k join the permanent sink set while
 // it has room.  While the set is not full the running top-k equals it, so the
-// set and its scores are the whole state.  Sixteen waves take interleaved rows;
-// each wave requests the K rows of all heads of its next rows at once (up to
-// HB heads per round trip), keeps its own top-k, and thread 0 merges the wave
-// lists (the rank is a total order, so the merge order does not matter).
+// set and its scores are the whole state.
+//
+// Rows are read 16 bytes per lane: one load instruction covers 64 / LR
+// consecutive tokens of one head (LR lanes per row), and the canonical sum of
+// squares (pair products, then halving) is formed with in-row DPP moves for the
+// halvings that cross lanes and in-register adds for the rest, in exactly the
+// canonical order.  Each wave keeps its own sorted top-k in registers (entry i
+// in lane i).  A chunk of at most 64 rows takes one workgroup per batch element
+// that merges its wave lists with the committed set and commits; a longer chunk
+// is split over up to 64 workgroups per batch element, each writing its top-k to
+// the cache's selection work area, and a second kernel merges those lists.  The
+// rank is a total order, so the merge order never changes the result.
 #include "device_common.h"
 
 namespace kvq {
 namespace {
 
-constexpr int NT = 1024;
-constexpr int NW = NT / 64;
-constexpr int HB = 8;  // heads per round of loads
-constexpr int RB = 2;  // rows per round of loads
+constexpr int PNT = 256;       // threads of a row workgroup
+constexpr int PNW = PNT / 64;  // its waves
+constexpr int HB = 8;          // heads per round of loads
+constexpr int RB = 2;          // load instructions (token groups) per head per round
+constexpr int MNT = 1024;      // threads of the merge workgroup
+constexpr int EMPTY_P = 0x7FFFFFFF;
 
 struct Cand {
   float s;
   int p;
 };
-__device__ __forceinline__ bool before(const Cand& a, const Cand& b) {
-  return a.s > b.s || (a.s == b.s && a.p < b.p);
+__device__ __forceinline__ bool before(float as, int ap, float bs, int bp) {
+  return as > bs || (as == bs && ap < bp);
+}
+__device__ __forceinline__ bool before(const Cand& a, const Cand& b) { return before(a.s, a.p, b.s, b.p); }
+
+// Value of lane (l + M) for lanes l whose partner lies in the same row group (others: don't care).
+template <int M>
+__device__ __forceinline__ float from_up(float v) {
+  if constexpr (M < 16) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x100 + M, 0xF, 0xF,
+                                                                 false));  // row_shl:M
+  } else {
+    return __shfl_down(v, M);
+  }
 }
 
-__global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
-  const Shape sh = a.sh;
-  const LayerView lv = a.lv;
-  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int K = sh.n_sink, D = sh.D;
-  __shared__ Cand top[NW][MAX_SINK];
-  __shared__ int ntop[NW];
-  __shared__ int full;
-  if (tid == 0) full = lv.sink_count[b] >= K;
-  if (tid < NW) ntop[tid] = 0;
-  __syncthreads();
-  if (full) return;
+// Cross-lane halvings: lane offsets M, M/2, ..., 1 on the Q pair sums each lane holds.
+template <int M, int Q>
+__device__ __forceinline__ void cross_halvings(float (&a)[Q]) {
+  if constexpr (M >= 1) {
+#pragma unroll
+    for (int i = 0; i < Q; ++i) a[i] = a[i] + from_up<M>(a[i]);
+    cross_halvings<M / 2, Q>(a);
+  }
+}
 
-  // per-wave running top-K over rows w, w + NW, ...: RB rows per round trip
-  const bool act = 2 * lane < D;
-  for (int t0 = w; t0 < a.n; t0 += NW * RB) {
-    float acc[RB];
+// Canonical sum of squares of one row held 16 bytes per lane (E elements, Q = E/2 pairs per lane,
+// LR = D/E lanes per row).  Pair sums a_l for l = jQ .. jQ+Q-1 sit in lane j of the row group; the
+// halving a[l] + a[l + h] pairs lane j with lane j + h/Q while h >= Q and stays in the lane after.
+// Lane 0 of each row group ends with the sum.
+template <int ESZ, int D>
+__device__ __forceinline__ float row_sumsq(const uint4& w) {
+  constexpr int E = 16 / ESZ, Q = E / 2, LR = D / E;
+  float x[E];
+  if constexpr (ESZ == 2) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-    for (int r = 0; r < RB; ++r) acc[r] = 0.f;
-    for (int h0 = 0; h0 < sh.Hkv; h0 += HB) {
-      float x0[RB][HB], x1[RB][HB];
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {  // every load of the round first
-          const int h = h0 + hh, t = t0 + NW * r;
-          const bool ok = act && h < sh.Hkv && t < a.n;
-          const int64_t row = (((int64_t)b * sh.Hkv + h) * a.n + t) * D;
-          x0[r][hh] = ok ? ld_in(a.k, row + 2 * lane, sh.in_f32) : 0.f;
-          x1[r][hh] = ok ? ld_in(a.k, row + 2 * lane + 1, sh.in_f32) : 0.f;
-        }
-#pragma unroll
-      for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh)
-          if (h0 + hh < sh.Hkv) acc[r] = acc[r] + sqrtf(wave_sumsq(x0[r][hh], x1[r][hh], D));
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] & 0xFFFFu));
+      x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] >> 16));
     }
+  } else {
+    x[0] = __builtin_bit_cast(float, w.x);
+    x[1] = __builtin_bit_cast(float, w.y);
+    x[2] = __builtin_bit_cast(float, w.z);
+    x[3] = __builtin_bit_cast(float, w.w);
+  }
+  float a[Q];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) {
-      const int t = t0 + NW * r;
-      if (t >= a.n) break;
-      const Cand c{acc[r] / (float)sh.Hkv, (int)(a.P + t)};
-      if (lane == 0) {
-        int n = ntop[w];
-        int i = n < K ? n : K - 1;
-        if (n < K || before(c, top[w][K - 1])) {
-          // insertion into the sorted list
-          while (i > 0 && before(c, top[w][i - 1])) {
-            top[w][i] = top[w][i - 1];
-            --i;
-          }
-          top[w][i] = c;
-          if (n < K) ntop[w] = n + 1;
-        }
-      }
+  for (int i = 0; i < Q; ++i) {
+    const float p = x[2 * i] * x[2 * i];
+    const float q = x[2 * i + 1] * x[2 * i + 1];
+    a[i] = p + q;
+  }
+  cross_halvings<LR / 2, Q>(a);
+#pragma unroll
+  for (int hq = Q / 2; hq >= 1; hq >>= 1)
+#pragma unroll
+    for (int i = 0; i < hq; ++i) a[i] = a[i] + a[i + hq];
+  return a[0];
+}
+
+// Sorted per-wave top-k held one entry per lane (lanes >= n hold don't-care values).
+struct WaveTop {
+  float s;
+  int p;
+  int n;              // entries held (uniform)
+  float ks;           // k-th entry once n == K (uniform)
+  int kp;
+};
+
+__device__ __forceinline__ void wave_insert(WaveTop& T, float cs, int cp, bool offer, int K, int lane) {
+  uint64_t m = __ballot(offer && (T.n < K || before(cs, cp, T.ks, T.kp)));
+  while (m) {
+    const int src = __builtin_ctzll(m);
+    m &= m - 1;
+    const float s = __shfl(cs, src);
+    const int p = __shfl(cp, src);
+    if (T.n == K && !before(s, p, T.ks, T.kp)) continue;  // the k-th entry improved meanwhile
+    const int pos = __popcll(__ballot(lane < T.n && before(T.s, T.p, s, p)));
+    const float us = __shfl_up(T.s, 1);
+    const int up = __shfl_up(T.p, 1);
+    if (lane > pos) {
+      T.s = us;
+      T.p = up;
+    }
+    if (lane == pos) {
+      T.s = s;
+      T.p = p;
+    }
+    T.n = T.n < K ? T.n + 1 : K;
+    if (T.n == K) {
+      T.ks = __shfl(T.s, K - 1);
+      T.kp = __shfl(T.p, K - 1);
     }
   }
-  __syncthreads();
-  // merge: the committed set (with its scores) and the wave lists as one candidate array; every
-  // candidate's rank is the number of candidates before it (the rank order is total), the first K
-  // land in rank order, and thread 0 commits the new ones among them in that order
-  constexpr int NC = MAX_SINK * (NW + 1);
-  __shared__ Cand cand[NC];
-  __shared__ Cand best[MAX_SINK];
-  __shared__ int nbest;
-  const int cnt = lv.sink_count[b];
-  if (tid < NC) {
-    const int q = tid / MAX_SINK, i = tid % MAX_SINK;
-    Cand c{-INFINITY, 0x7FFFFFFF};  // empty slot: ranked after every real candidate
-    if (q < NW) {
-      if (i < ntop[q]) c = top[q][i];
-    } else if (i < cnt) {
-      c = Cand{lv.sink_score[b * K + i], lv.sink_pos[b * K + i]};
-    }
-    cand[tid] = c;
-  }
-  if (tid == 0) {
-    int nv = cnt;
-    for (int q = 0; q < NW; ++q) nv += ntop[q];
-    nbest = nv < K ? nv : K;  // ranks 0 .. nbest - 1 are taken
-  }
-  __syncthreads();
-  if (tid < NC && cand[tid].p != 0x7FFFFFFF) {
-    const Cand c = cand[tid];
+}
+
+// Rank merge of `nc` candidates in LDS (empty slots have p == EMPTY_P): the first K in rank order land
+// in best[0 .. nbest).  Every thread of the workgroup takes part.
+__device__ __forceinline__ void rank_merge(const Cand* cand, int nc, Cand* best, int K, int tid, int nt) {
+  for (int i = tid; i < nc; i += nt) {
+    const Cand c = cand[i];
+    if (c.p == EMPTY_P) continue;
     int r = 0;
-    for (int j = 0; j < NC; ++j) r += before(cand[j], c);
+    for (int j = 0; j < nc; ++j) r += before(cand[j], c);
     if (r < K) best[r] = c;
   }
-  __syncthreads();
-  if (tid != 0) return;
+}
+
+// Thread 0: the new rows (p >= P) among the first nbest ranks join the set in rank order while it has room.
+__device__ __forceinline__ void commit(const LayerView& lv, int b, int K, int cnt, const Cand* best, int nbest,
+                                       int64_t P) {
   int m = cnt;
-  const int nb = nbest;
-  for (int i = 0; i < nb; ++i) {
-    if (best[i].p >= a.P && m < K) {
+  for (int i = 0; i < nbest; ++i) {
+    if (best[i].p >= P && m < K) {
       lv.sink_pos[b * K + m] = best[i].p;
       lv.sink_score[b * K + m] = best[i].s;
       ++m;
@@ -129,11 +157,142 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a) {
   lv.sink_count[b] = m;
 }
 
+template <int ESZ, int D, bool FINAL>
+__global__ __launch_bounds__(PNT) void k_select_rows(SelectArgs a) {
+  constexpr int E = 16 / ESZ, LR = D / E, RPW = 64 / LR;
+  const Shape sh = a.sh;
+  const LayerView lv = a.lv;
+  const int b = blockIdx.x, g = blockIdx.y, G = gridDim.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int K = sh.n_sink, H = sh.Hkv;
+  const int cnt = lv.sink_count[b];
+  if (cnt >= K) return;  // the set is full: nothing more joins
+
+  // rows [tb, te) of the chunk for this workgroup
+  const int per = (a.n + G - 1) / G;
+  const int tb = g * per, te = min(a.n, tb + per);
+  const int j = lane % LR, rg = lane / LR;
+  const char* kb = static_cast<const char*>(a.k);
+
+  WaveTop T{-INFINITY, EMPTY_P, 0, -INFINITY, EMPTY_P};
+  for (int t0 = tb + w * RPW * RB; t0 < te; t0 += PNW * RPW * RB) {
+    float acc[RB];
+#pragma unroll
+    for (int r = 0; r < RB; ++r) acc[r] = 0.f;
+    for (int h0 = 0; h0 < H; h0 += HB) {
+      uint4 raw[RB][HB];
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {  // every load of the round first
+          const int h = h0 + hh, t = t0 + r * RPW + rg;
+          raw[r][hh] = make_uint4(0u, 0u, 0u, 0u);
+          if (h < H && t < te) {
+            const int64_t row = ((int64_t)b * H + h) * a.n + t;
+            raw[r][hh] = *reinterpret_cast<const uint4*>(kb + (row * D + j * E) * ESZ);
+          }
+        }
+#pragma unroll
+      for (int r = 0; r < RB; ++r)
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh)
+          if (h0 + hh < H) acc[r] = acc[r] + sqrtf(row_sumsq<ESZ, D>(raw[r][hh]));
+    }
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+      const int t = t0 + r * RPW + rg;
+      wave_insert(T, acc[r] / (float)H, (int)(a.P + t), j == 0 && t < te, K, lane);
+    }
+  }
+
+  // workgroup merge of the wave lists (and, for a single workgroup, of the committed set)
+  constexpr int NC = MAX_SINK * (PNW + 1);
+  __shared__ Cand cand[NC];
+  __shared__ Cand best[MAX_SINK];
+  for (int i = tid; i < NC; i += PNT) cand[i] = Cand{-INFINITY, EMPTY_P};
+  if (tid < MAX_SINK) best[tid] = Cand{-INFINITY, EMPTY_P};
+  __syncthreads();
+  if (lane < T.n) cand[w * MAX_SINK + lane] = Cand{T.s, T.p};
+  if (FINAL && tid < cnt) cand[PNW * MAX_SINK + tid] = Cand{lv.sink_score[b * K + tid], lv.sink_pos[b * K + tid]};
+  __syncthreads();
+  rank_merge(cand, NC, best, K, tid, PNT);
+  __syncthreads();
+  if (FINAL) {
+    if (tid == 0) {
+      int nv = 0;
+      for (int i = 0; i < NC; ++i) nv += cand[i].p != EMPTY_P;
+      commit(lv, b, K, cnt, best, nv < K ? nv : K, a.P);
+    }
+  } else if (tid < K) {
+    a.work[((int64_t)b * SELECT_GMAX + g) * K + tid] = make_int2(__builtin_bit_cast(int, best[tid].s), best[tid].p);
+  }
+}
+
+// Merge of the per-workgroup lists of a split chunk with the committed set.
+__global__ __launch_bounds__(MNT) void k_select_merge(SelectArgs a, int G) {
+  const LayerView lv = a.lv;
+  const int b = blockIdx.x, tid = threadIdx.x, K = a.sh.n_sink;
+  const int cnt = lv.sink_count[b];
+  if (cnt >= K) return;
+  constexpr int NC = MAX_SINK * (SELECT_GMAX + 1);
+  __shared__ Cand cand[NC];
+  __shared__ Cand best[MAX_SINK];
+  __shared__ int nvalid;
+  const int nc = K * (G + 1);
+  if (tid == 0) nvalid = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int i = tid; i < nc; i += MNT) {
+    Cand c{-INFINITY, EMPTY_P};
+    if (i < K * G) {
+      const int2 e = a.work[((int64_t)b * SELECT_GMAX + i / K) * K + i % K];
+      c = Cand{__builtin_bit_cast(float, e.x), e.y};
+    } else if (i - K * G < cnt) {
+      c = Cand{lv.sink_score[b * K + i - K * G], lv.sink_pos[b * K + i - K * G]};
+    }
+    cand[i] = c;
+    mine += c.p != EMPTY_P;
+  }
+  if (mine) atomicAdd(&nvalid, mine);
+  __syncthreads();
+  rank_merge(cand, nc, best, K, tid, MNT);
+  __syncthreads();
+  if (tid == 0) commit(lv, b, K, cnt, best, nvalid < K ? nvalid : K, a.P);
+}
+
+template <int ESZ, int D>
+hipError_t launch_rows(const SelectArgs& a, int G, hipStream_t st) {
+  if (G == 1) {
+    hipLaunchKernelGGL((k_select_rows<ESZ, D, true>), dim3(a.sh.B, 1), dim3(PNT), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_select_rows<ESZ, D, false>), dim3(a.sh.B, G), dim3(PNT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_select_merge, dim3(a.sh.B), dim3(MNT), 0, st, a, G);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+int select_groups(int n) {
+  const int g = (n + SELECT_MIN_ROWS - 1) / SELECT_MIN_ROWS;
+  return g < 1 ? 1 : (g > SELECT_GMAX ? SELECT_GMAX : g);
+}
+
 hipError_t launch_select(const SelectArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_select, dim3(a.sh.B), dim3(NT), 0, st, a);
-  return hipGetLastError();
+  const int G = select_groups(a.n);
+  const int D = a.sh.D;
+  if (a.sh.in_f32) {
+    if (D == 32) return launch_rows<4, 32>(a, G, st);
+    if (D == 64) return launch_rows<4, 64>(a, G, st);
+    if (D == 128) return launch_rows<4, 128>(a, G, st);
+  } else {
+    if (D == 32) return launch_rows<2, 32>(a, G, st);
+    if (D == 64) return launch_rows<2, 64>(a, G, st);
+    if (D == 128) return launch_rows<2, 128>(a, G, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace kvq

@@ -43,7 +43,7 @@ class kvq_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "layer_stride", "bulk", "record_bytes", "rec_k_codes", "rec_v_codes", "rec_k_meta", "rec_v_meta",
         "staging", "win_k", "win_v", "sink_k", "sink_v", "sink_pos", "sink_score", "sink_count",
-        "tables", "total")] + [("cap_blocks", ctypes.c_int32), ("capacity", ctypes.c_int32)]
+        "tables", "select_work", "total")] + [("cap_blocks", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
 def _load():
@@ -152,10 +152,10 @@ class Cache:
         _check(lib.kvq_create(ctypes.byref(cfg), _ptr(self.buf), nbytes, _stream(self.dev), ctypes.byref(h)))
         self.handle = h
 
-    def __del__(self):
+    def __del__(self, _destroy=lib.kvq_destroy):  # bound early: module globals may be gone at exit
         h = getattr(self, "handle", None)
         if h:
-            lib.kvq_destroy(h)
+            _destroy(h)
             self.handle = None
 
     # entry points, same names as the C ABI (launches go to the current stream of the cache's device)
