@@ -144,6 +144,28 @@ def key_multipliers(cfgno, kw, seed, device):
     return None
 
 
+def prefill_bytes(kw, P, n):
+    """Bytes one sink-selection call and one append call of n rows at position P must move.
+
+    Selection reads the K rows.  Append reads K and V and the staged rows of an open first block,
+    and writes the packed codes and V metadata of the new rows, the K metadata of every touched
+    block, the fp16 window rows among the new rows and the staged rows of an open last block
+    (sink rows, at most n_sink per batch element, are not counted)."""
+    D, H, B = kw["head_dim"], kw["n_kv_heads"], kw["batch"]
+    R = kw.get("residual", 0)
+    fmt, kb, vb = kw.get("fmt", "kivi"), kw.get("k_bits", 2), kw.get("v_bits", 2)
+    esz = 4 if kw.get("in_dtype") == "f32" else 2
+    kmeta_blk, vmeta_tok = {"kivi": (4 * D, 4 * (D // 32)), "q2k": (2 * D, 2 * (D // 32))}.get(fmt, (0, 8))
+    S = B * H
+    sel = S * n * D * esz if kw.get("sink_mode") == "topk" and kw.get("n_sink", 0) > 0 else 0
+    nblk = (P + n - 1) // 32 - P // 32 + 1
+    staged_in = (P % 32) * D * esz if fmt != "tq" else 0
+    staged_out = ((P + n) % 32) * D * esz if fmt != "tq" else 0
+    app = S * (2 * n * D * esz + staged_in + n * (D * (kb + vb) // 8 + vmeta_tok) + nblk * kmeta_blk
+               + min(n, R) * 2 * D * 2 + staged_out)
+    return sel, app
+
+
 def algorithmic_bytes(kw, P, lo, sinks_per_b):
     """Bytes one decode-attention call must move (valid tokens only)."""
     D, H, Hq, B = kw["head_dim"], kw["n_kv_heads"], kw["n_q_heads"], kw["batch"]
@@ -377,6 +399,8 @@ def main():
     pre_k = pre_v = None
     if T0 > 0:
         pre_k, pre_v = make_rows(args.config, kw, T0, seed, 100, dev, kmult, planted)
+    pstream = torch.cuda.current_stream().cuda_stream
+    pre_t = []  # (P, n, select timer, append timer) of every prefill chunk
     for r in range(nrep):
         c = kvq.Cache(cfg)
         for layer in range(L):
@@ -385,11 +409,33 @@ def main():
                 for s0 in range(0, T0, chunk):
                     k = pre_k[:, :, s0:s0 + chunk].contiguous()
                     v = pre_v[:, :, s0:s0 + chunk].contiguous()
+                    ts, ta = HipTimer(), HipTimer()
+                    ts.record(0, pstream)
                     c.kvq_select_sinks(layer, k)
+                    ts.record(1, pstream)
+                    ta.record(0, pstream)
                     c.kvq_append(layer, k, v)
+                    ta.record(1, pstream)
                     c.kvq_evict(layer)
+                    pre_t.append((s0, k.shape[2], ts, ta))
         reps.append(c)
     torch.cuda.synchronize()
+    prefill = None
+    if pre_t:
+        sel_b = app_b = sel_ms = app_ms = 0.0
+        for P_, n_, ts, ta in pre_t:
+            b_sel, b_app = prefill_bytes(kw, P_, n_)
+            sel_b += b_sel
+            app_b += b_app
+            sel_ms += ts.ms()
+            app_ms += ta.ms()
+        k_ = len(pre_t)
+        prefill = {"chunk_rows": min(4096, T0), "calls": k_,
+                   "select_us": sel_ms * 1e3 / k_, "select_GBps": (sel_b / (sel_ms * 1e-3) / 1e9) if sel_b else None,
+                   "append_us": app_ms * 1e3 / k_, "append_GBps": app_b / (app_ms * 1e-3) / 1e9,
+                   "note": "prefill chunks of every replica, HIP timing events around each call; bytes from "
+                           "bench.prefill_bytes (select: K read; append: K+V read, codes, metadata, fp16 rows written)"}
+        del pre_t
     sinks_per_b = [[] for _ in range(kw["batch"])]
     if kw.get("n_sink", 0) > 0:
         n = kw["batch"] * kw["n_sink"]
@@ -492,6 +538,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "warm_cache": warm,
+        "prefill": prefill,
     }
     if not args.no_cpu_baseline:
         try:

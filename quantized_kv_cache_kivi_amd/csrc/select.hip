@@ -12,11 +12,13 @@
 // squares (pair products, then halving) is formed with in-row DPP moves for the
 // halvings that cross lanes and in-register adds for the rest, in exactly the
 // canonical order.  Each wave keeps its own sorted top-k in registers (entry i
-// in lane i).  A chunk of at most 64 rows takes one workgroup per batch element
-// that merges its wave lists with the committed set and commits; a longer chunk
-// is split over up to 64 workgroups per batch element, each writing its top-k to
-// the cache's selection work area, and a second kernel merges those lists.  The
-// rank is a total order, so the merge order never changes the result.
+// in lane i; k <= 16, so the list is one DPP row), and every merge is more
+// insertions into such a list.  A chunk of at most 64 rows takes one workgroup
+// per batch element, whose first wave merges the other waves' lists and the
+// committed set and commits; a longer chunk is split over up to 64 workgroups
+// per batch element, each writing its top-k to the cache's selection work area,
+// and a one-wave kernel per batch element merges those lists.  The rank is a
+// total order, so the merge order never changes the result.
 #include "device_common.h"
 
 namespace kvq {
@@ -26,7 +28,6 @@ constexpr int PNT = 256;       // threads of a row workgroup
 constexpr int PNW = PNT / 64;  // its waves
 constexpr int HB = 8;          // heads per round of loads
 constexpr int RB = 2;          // load instructions (token groups) per head per round
-constexpr int MNT = 1024;      // threads of the merge workgroup
 constexpr int EMPTY_P = 0x7FFFFFFF;
 
 struct Cand {
@@ -104,17 +105,27 @@ struct WaveTop {
   int kp;
 };
 
+__device__ __forceinline__ float rdl(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+// Value of lane l - 1 in lane l of each 16-lane row (row_shr:1; lane 0 of a row keeps its own).
+__device__ __forceinline__ int row_up(int v) { return __builtin_amdgcn_update_dpp(v, v, 0x111, 0xF, 0xF, false); }
+__device__ __forceinline__ float row_up(float v) { return __builtin_bit_cast(float, row_up(__builtin_bit_cast(int, v))); }
+
+// Inserts the offered candidates (cs, cp) of the lanes with `offer` into the wave's list, in lane
+// order (the result does not depend on it): a ballot keeps the ones that beat the k-th entry, and
+// each is placed by one ballot (its rank) and one in-row shift of the entries behind it.
 __device__ __forceinline__ void wave_insert(WaveTop& T, float cs, int cp, bool offer, int K, int lane) {
   uint64_t m = __ballot(offer && (T.n < K || before(cs, cp, T.ks, T.kp)));
   while (m) {
     const int src = __builtin_ctzll(m);
     m &= m - 1;
-    const float s = __shfl(cs, src);
-    const int p = __shfl(cp, src);
+    const float s = rdl(cs, src);
+    const int p = __builtin_amdgcn_readlane(cp, src);
     if (T.n == K && !before(s, p, T.ks, T.kp)) continue;  // the k-th entry improved meanwhile
     const int pos = __popcll(__ballot(lane < T.n && before(T.s, T.p, s, p)));
-    const float us = __shfl_up(T.s, 1);
-    const int up = __shfl_up(T.p, 1);
+    const float us = row_up(T.s);
+    const int up = row_up(T.p);
     if (lane > pos) {
       T.s = us;
       T.p = up;
@@ -125,36 +136,29 @@ __device__ __forceinline__ void wave_insert(WaveTop& T, float cs, int cp, bool o
     }
     T.n = T.n < K ? T.n + 1 : K;
     if (T.n == K) {
-      T.ks = __shfl(T.s, K - 1);
-      T.kp = __shfl(T.p, K - 1);
+      T.ks = rdl(T.s, K - 1);
+      T.kp = __builtin_amdgcn_readlane(T.p, K - 1);
     }
   }
 }
 
-// Rank merge of `nc` candidates in LDS (empty slots have p == EMPTY_P): the first K in rank order land
-// in best[0 .. nbest).  Every thread of the workgroup takes part.
-__device__ __forceinline__ void rank_merge(const Cand* cand, int nc, Cand* best, int K, int tid, int nt) {
-  for (int i = tid; i < nc; i += nt) {
-    const Cand c = cand[i];
-    if (c.p == EMPTY_P) continue;
-    int r = 0;
-    for (int j = 0; j < nc; ++j) r += before(cand[j], c);
-    if (r < K) best[r] = c;
-  }
-}
-
-// Thread 0: the new rows (p >= P) among the first nbest ranks join the set in rank order while it has room.
-__device__ __forceinline__ void commit(const LayerView& lv, int b, int K, int cnt, const Cand* best, int nbest,
-                                       int64_t P) {
+// The new rows (p >= P) of the merged list join the set in rank order while it has room (lane 0
+// stores).
+__device__ __forceinline__ void commit(const LayerView& lv, int b, int K, int cnt, const WaveTop& T, int64_t P,
+                                       int lane) {
   int m = cnt;
-  for (int i = 0; i < nbest; ++i) {
-    if (best[i].p >= P && m < K) {
-      lv.sink_pos[b * K + m] = best[i].p;
-      lv.sink_score[b * K + m] = best[i].s;
+  for (int i = 0; i < T.n; ++i) {
+    const float s = rdl(T.s, i);
+    const int p = __builtin_amdgcn_readlane(T.p, i);
+    if (p >= P && m < K) {
+      if (lane == 0) {
+        lv.sink_pos[b * K + m] = p;
+        lv.sink_score[b * K + m] = s;
+      }
       ++m;
     }
   }
-  lv.sink_count[b] = m;
+  if (lane == 0) lv.sink_count[b] = m;
 }
 
 template <int ESZ, int D, bool FINAL>
@@ -205,59 +209,55 @@ __global__ __launch_bounds__(PNT) void k_select_rows(SelectArgs a) {
     }
   }
 
-  // workgroup merge of the wave lists (and, for a single workgroup, of the committed set)
-  constexpr int NC = MAX_SINK * (PNW + 1);
-  __shared__ Cand cand[NC];
-  __shared__ Cand best[MAX_SINK];
-  for (int i = tid; i < NC; i += PNT) cand[i] = Cand{-INFINITY, EMPTY_P};
-  if (tid < MAX_SINK) best[tid] = Cand{-INFINITY, EMPTY_P};
+  // workgroup merge: the first wave inserts the other waves' lists (and, for a single workgroup, the
+  // committed set) into its own
+  __shared__ Cand lists[PNW - 1][MAX_SINK];
+  __shared__ int nlist[PNW - 1];
+  if (w > 0) {
+    if (lane < T.n) lists[w - 1][lane] = Cand{T.s, T.p};
+    if (lane == 0) nlist[w - 1] = T.n;
+  }
   __syncthreads();
-  if (lane < T.n) cand[w * MAX_SINK + lane] = Cand{T.s, T.p};
-  if (FINAL && tid < cnt) cand[PNW * MAX_SINK + tid] = Cand{lv.sink_score[b * K + tid], lv.sink_pos[b * K + tid]};
-  __syncthreads();
-  rank_merge(cand, NC, best, K, tid, PNT);
-  __syncthreads();
+  if (w > 0) return;
+  {
+    const int q = lane / MAX_SINK, i = lane % MAX_SINK;  // lanes 0 .. 47: the three other lists
+    const bool ok = q < PNW - 1 && i < nlist[q < PNW - 1 ? q : 0];
+    const Cand c = ok ? lists[q < PNW - 1 ? q : 0][i] : Cand{-INFINITY, EMPTY_P};
+    wave_insert(T, c.s, c.p, ok, K, lane);
+  }
   if (FINAL) {
-    if (tid == 0) {
-      int nv = 0;
-      for (int i = 0; i < NC; ++i) nv += cand[i].p != EMPTY_P;
-      commit(lv, b, K, cnt, best, nv < K ? nv : K, a.P);
-    }
-  } else if (tid < K) {
-    a.work[((int64_t)b * SELECT_GMAX + g) * K + tid] = make_int2(__builtin_bit_cast(int, best[tid].s), best[tid].p);
+    const bool ok = lane < cnt;
+    const float cs = ok ? lv.sink_score[b * K + lane] : -INFINITY;
+    const int cp = ok ? lv.sink_pos[b * K + lane] : EMPTY_P;
+    wave_insert(T, cs, cp, ok, K, lane);
+    commit(lv, b, K, cnt, T, a.P, lane);
+  } else if (lane < K) {
+    a.work[((int64_t)b * SELECT_GMAX + g) * K + lane] =
+        lane < T.n ? make_int2(__builtin_bit_cast(int, T.s), T.p)
+                   : make_int2(__builtin_bit_cast(int, -INFINITY), EMPTY_P);
   }
 }
 
-// Merge of the per-workgroup lists of a split chunk with the committed set.
-__global__ __launch_bounds__(MNT) void k_select_merge(SelectArgs a, int G) {
+// Merge of the per-workgroup lists of a split chunk with the committed set: one wave per batch
+// element inserts every list entry (64 per round), then the committed set, and commits.
+__global__ __launch_bounds__(64) void k_select_merge(SelectArgs a, int G) {
   const LayerView lv = a.lv;
-  const int b = blockIdx.x, tid = threadIdx.x, K = a.sh.n_sink;
+  const int b = blockIdx.x, lane = threadIdx.x, K = a.sh.n_sink;
   const int cnt = lv.sink_count[b];
   if (cnt >= K) return;
-  constexpr int NC = MAX_SINK * (SELECT_GMAX + 1);
-  __shared__ Cand cand[NC];
-  __shared__ Cand best[MAX_SINK];
-  __shared__ int nvalid;
-  const int nc = K * (G + 1);
-  if (tid == 0) nvalid = 0;
-  __syncthreads();
-  int mine = 0;
-  for (int i = tid; i < nc; i += MNT) {
-    Cand c{-INFINITY, EMPTY_P};
-    if (i < K * G) {
-      const int2 e = a.work[((int64_t)b * SELECT_GMAX + i / K) * K + i % K];
-      c = Cand{__builtin_bit_cast(float, e.x), e.y};
-    } else if (i - K * G < cnt) {
-      c = Cand{lv.sink_score[b * K + i - K * G], lv.sink_pos[b * K + i - K * G]};
-    }
-    cand[i] = c;
-    mine += c.p != EMPTY_P;
+  WaveTop T{-INFINITY, EMPTY_P, 0, -INFINITY, EMPTY_P};
+  const int nc = K * G;
+  for (int i0 = 0; i0 < nc; i0 += 64) {
+    const int i = i0 + lane;
+    int2 e = make_int2(0, EMPTY_P);
+    if (i < nc) e = a.work[((int64_t)b * SELECT_GMAX + i / K) * K + i % K];
+    wave_insert(T, __builtin_bit_cast(float, e.x), e.y, e.y != EMPTY_P, K, lane);
   }
-  if (mine) atomicAdd(&nvalid, mine);
-  __syncthreads();
-  rank_merge(cand, nc, best, K, tid, MNT);
-  __syncthreads();
-  if (tid == 0) commit(lv, b, K, cnt, best, nvalid < K ? nvalid : K, a.P);
+  const bool ok = lane < cnt;
+  const float cs = ok ? lv.sink_score[b * K + lane] : -INFINITY;
+  const int cp = ok ? lv.sink_pos[b * K + lane] : EMPTY_P;
+  wave_insert(T, cs, cp, ok, K, lane);
+  commit(lv, b, K, cnt, T, a.P, lane);
 }
 
 template <int ESZ, int D>
@@ -269,7 +269,7 @@ hipError_t launch_rows(const SelectArgs& a, int G, hipStream_t st) {
   hipLaunchKernelGGL((k_select_rows<ESZ, D, false>), dim3(a.sh.B, G), dim3(PNT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_select_merge, dim3(a.sh.B), dim3(MNT), 0, st, a, G);
+  hipLaunchKernelGGL(k_select_merge, dim3(a.sh.B), dim3(64), 0, st, a, G);
   return hipGetLastError();
 }
 
