@@ -1,4 +1,6 @@
-// Append / quantize kernel: one workgroup per (touched 32-token block, stream).
+// Append / quantize kernels: whole blocks of a chunk, one wave per (block, stream); partial
+// blocks, one workgroup per (block, stream, 32-channel group); TurboQuant and other shapes, one
+// workgroup per (block, stream).
 //
 // Follows "StreamingLLM + KIVI — long-context decode without growing the KV
 // cache" ("KIVI", "Affine quantisation formula": K per channel, V per token,
@@ -682,19 +684,400 @@ hipError_t launch_cs_k(const AppendArgs& a, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Whole blocks of a prefill chunk (fp16 input, block formats): one wave per (block, stream), four
+// waves per workgroup working independently.  Lane (j, r) holds channels 8j .. 8j+7 of rows
+// NI*r .. NI*r + NI-1 (one 16-byte load per row and tensor; LR = D/8 lanes per row, so one load
+// instruction reads 64/LR whole rows).  K statistics per channel reduce over the lane's rows and
+// then across the row groups; V statistics per (row, 32 channels) reduce over four neighbouring
+// lanes.  K code words are assembled in registers; V codes pass through a wave-private LDS tile
+// [token][channel] so that each lane can gather the chunk of the matrix-core tile order it writes.
+// q2k's block RMS sums each channel in token order from a wave-private copy of the K rows.  The
+// arithmetic that decides a code is the per-element arithmetic of k_append_cs, operation for
+// operation.
+constexpr int FW = 4;  // waves (blocks) per workgroup of k_append_full
+
+template <int FMT, int D>
+struct FullSmem {
+  static constexpr int Q = FMT == KVQ_FMT_Q2K;
+  alignas(16) uint8_t vc[FW][G][D + 8];       // V codes [token][channel] (rows padded: bank spread)
+  alignas(16) _Float16 kr[Q ? FW : 1][Q ? G : 1][D + 8];  // q2k: K rows
+  float rf[Q ? FW : 1][D];                    // q2k: fp16 block RMS as fp32
+};
+
+__device__ __forceinline__ void h8(const uint4& w, float (&x)[8]) {
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] & 0xFFFFu));
+    x[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(u[i] >> 16));
+  }
+}
+
+template <int FMT, int KB, int VB, int D>
+__global__ __launch_bounds__(64 * FW) void k_append_full(AppendArgs a, int64_t fb0, int nfull) {
+  constexpr bool Q2K = FMT == KVQ_FMT_Q2K;
+  constexpr int LR = D / 8, RPI = 64 / LR, NI = G / RPI, NG = D / 32;
+  constexpr int KPW = 32 / KB, VPW = 32 / VB, WPC = D * VB / 64;
+  const Shape sh = a.sh;
+  const LayerView lv = a.lv;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int fb = blockIdx.x * FW + wv;
+  if (fb >= nfull) return;  // waves never meet at a barrier: an idle wave may leave
+  const int s = blockIdx.y, b = s / sh.Hkv, h = s % sh.Hkv;
+  const int64_t beta = fb0 + fb, base = beta * G;
+  const int j = lane % LR, r = lane / LR;
+  uint8_t* rec = lv.bulk + ((int64_t)s * lv.cap_b + beta % lv.cap_b) * lv.rec;
+  __shared__ FullSmem<FMT, D> sm;
+
+  // every global load first: the block's K and V rows, the sink list
+  const int64_t row0 = ((int64_t)b * sh.Hkv + h) * a.n + (base - a.P);  // input row of token 0
+  const uint16_t* kin = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vin = static_cast<const uint16_t*>(a.v);
+  uint4 kw[NI], vw[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int64_t off = (row0 + NI * r + i) * D + 8 * j;
+    kw[i] = *reinterpret_cast<const uint4*>(kin + off);
+    vw[i] = *reinterpret_cast<const uint4*>(vin + off);
+  }
+  // sink rows of the block: lane t < 32 finds the slot of position base + t
+  int myslot = -1;
+  if (sh.n_sink > 0) {
+    const int64_t p = base + (lane & 31);
+    if (sh.sink_mode == KVQ_SINK_FIRST_N) {
+      if (p < sh.n_sink) myslot = (int)p;
+    } else if (sh.sink_mode == KVQ_SINK_TOPK) {
+      const int cnt = lv.sink_count[b];
+      const int sp = lane < sh.n_sink ? lv.sink_pos[b * sh.n_sink + lane] : -1;
+      for (int i = 0; i < sh.n_sink; ++i) {
+        const int pi = __builtin_amdgcn_readlane(sp, i);
+        if (i < cnt && pi == p) myslot = i;
+      }
+    }
+  }
+  const uint32_t smask = (uint32_t)__ballot(lane < 32 && myslot >= 0);
+  auto calib = [&](int t) { return !((smask >> t) & 1u); };
+
+  // ---- K: statistics per channel, then codes ----
+  uint8_t* km = rec + lv.k_meta;
+  uint32_t kcode[NI][2];  // the lane's 8 codes of each row, bytes 0..3 and 4..7
+  if constexpr (!Q2K) {
+    float mn[8], mx[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      mn[c] = INFINITY;
+      mx[c] = -INFINITY;
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      if (!calib(NI * r + i)) continue;
+      float x[8];
+      h8(kw[i], x);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        mn[c] = fminf(mn[c], x[c]);
+        mx[c] = fmaxf(mx[c], x[c]);
+      }
+    }
+#pragma unroll
+    for (int off = LR; off < 64; off <<= 1)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        mn[c] = fminf(mn[c], __shfl_xor(mn[c], off));
+        mx[c] = fmaxf(mx[c], __shfl_xor(mx[c], off));
+      }
+    constexpr float L = (float)((1 << KB) - 1);
+    float sf[8], zf[8];
+    uint16_t s16[8], z16[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float lo = mn[c], hi = mx[c];
+      if (hi == -INFINITY) lo = hi = 0.f;  // no calibration row
+      lo = lo + 0.0f;
+      hi = hi + 0.0f;
+      const float s32 = fmaxf(EPS_SCALE, (hi - lo) / L);
+      s16[c] = f16_bits(s32);
+      z16[c] = f16_bits(lo);
+      sf[c] = f16_val(s16[c]);
+      zf[c] = f16_val(z16[c]);
+    }
+    if (r == 0) {
+      uint32_t sw[4], zw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sw[q] = (uint32_t)s16[2 * q] | ((uint32_t)s16[2 * q + 1] << 16);
+        zw[q] = (uint32_t)z16[2 * q] | ((uint32_t)z16[2 * q + 1] << 16);
+      }
+      *reinterpret_cast<uint4*>(km + 2 * 8 * j) = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+      *reinterpret_cast<uint4*>(km + 2 * (D + 8 * j)) = make_uint4(zw[0], zw[1], zw[2], zw[3]);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float x[8];
+      h8(kw[i], x);
+      const bool cal = calib(NI * r + i);
+      uint32_t u8[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float u = rintf((x[c] - zf[c]) / sf[c]);
+        u8[c] = cal ? (uint32_t)fminf(fmaxf(u, 0.f), L) : 0u;
+      }
+      kcode[i][0] = u8[0] | (u8[1] << 8) | (u8[2] << 16) | (u8[3] << 24);
+      kcode[i][1] = u8[4] | (u8[5] << 8) | (u8[6] << 16) | (u8[7] << 24);
+    }
+  } else {
+    // block RMS per channel, summed in token order over the calibration rows
+#pragma unroll
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<uint4*>(&sm.kr[wv][NI * r + i][8 * j]) = kw[i];
+    __builtin_amdgcn_wave_barrier();
+    const int ncal = G - __popc(smask);
+    if (lane < D / 2) {
+      float ss0 = 0.f, ss1 = 0.f;
+      for (int t = 0; t < G; ++t) {
+        if (!calib(t)) continue;
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(&sm.kr[wv][t][2 * lane]);
+        const float x0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+        const float x1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+        ss0 = ss0 + x0 * x0;
+        ss1 = ss1 + x1 * x1;
+      }
+      const float r0 = ncal > 0 ? fmaxf(EPS_SCALE, sqrtf(ss0 / (float)ncal)) : EPS_SCALE;
+      const float r1 = ncal > 0 ? fmaxf(EPS_SCALE, sqrtf(ss1 / (float)ncal)) : EPS_SCALE;
+      const uint16_t b0 = f16_bits(r0), b1 = f16_bits(r1);
+      reinterpret_cast<uint32_t*>(km)[lane] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+      sm.rf[wv][2 * lane] = f16_val(b0);
+      sm.rf[wv][2 * lane + 1] = f16_val(b1);
+    }
+    __builtin_amdgcn_wave_barrier();
+    float rf[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) rf[c] = sm.rf[wv][8 * j + c];
+    const float th0 = lv.tables->q2k_thr[0], th1 = lv.tables->q2k_thr[1], th2 = lv.tables->q2k_thr[2];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float x[8];
+      h8(kw[i], x);
+      const bool cal = calib(NI * r + i);
+      uint32_t u8[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float y = x[c] / rf[c];
+        u8[c] = cal ? (uint32_t)((y >= th0) + (y >= th1) + (y >= th2)) : 0u;
+      }
+      kcode[i][0] = u8[0] | (u8[1] << 8) | (u8[2] << 16) | (u8[3] << 24);
+      kcode[i][1] = u8[4] | (u8[5] << 8) | (u8[6] << 16) | (u8[7] << 24);
+    }
+  }
+  // K code words: word W of a row holds channels KPW*W .. KPW*W + KPW-1, code k at bit
+  // 16*(k%2) + KB*(k/2)
+  uint32_t* kdst = reinterpret_cast<uint32_t*>(rec + lv.k_codes);
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = NI * r + i;
+    uint32_t u[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) u[c] = (kcode[i][c >> 2] >> (8 * (c & 3))) & 0xFFu;
+    if constexpr (KB == 2) {  // one word per lane pair: this lane's codes are k = 8*(j%2) + c
+      uint32_t part = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) part |= u[c] << (16 * (c & 1) + 8 * (j & 1) + 2 * (c >> 1));
+      part |= __shfl_xor(part, 1);
+      if ((j & 1) == 0) kdst[t * (D * KB / 32) + (j >> 1)] = part;
+    } else if constexpr (KB == 4) {  // one word per lane
+      uint32_t wd = 0;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) wd |= u[c] << (16 * (c & 1) + 4 * (c >> 1));
+      kdst[t * (D * KB / 32) + j] = wd;
+    } else {  // two words per lane
+      uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        w0 |= u[c] << (16 * (c & 1) + 8 * (c >> 1));
+        w1 |= u[4 + c] << (16 * (c & 1) + 8 * (c >> 1));
+      }
+      *reinterpret_cast<uint2*>(&kdst[t * (D * KB / 32) + 2 * j]) = make_uint2(w0, w1);
+    }
+  }
+
+  // ---- V: statistics per (row, 32-channel group) over four neighbouring lanes, codes to LDS ----
+  uint16_t* vm = reinterpret_cast<uint16_t*>(rec + lv.v_meta);
+  const int g = j >> 2;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = NI * r + i;
+    float x[8];
+    h8(vw[i], x);
+    uint32_t u8[8];
+    uint16_t vs16 = 0, vz16 = 0;
+    if constexpr (!Q2K) {
+      float lo = x[0], hi = x[0];
+#pragma unroll
+      for (int c = 1; c < 8; ++c) {
+        lo = fminf(lo, x[c]);
+        hi = fmaxf(hi, x[c]);
+      }
+      lo = fminf(lo, __shfl_xor(lo, 1));
+      hi = fmaxf(hi, __shfl_xor(hi, 1));
+      lo = fminf(lo, __shfl_xor(lo, 2));
+      hi = fmaxf(hi, __shfl_xor(hi, 2));
+      lo = lo + 0.0f;
+      hi = hi + 0.0f;
+      constexpr float L = (float)((1 << VB) - 1);
+      const float s32 = fmaxf(EPS_SCALE, (hi - lo) / L);
+      vs16 = f16_bits(s32);
+      vz16 = f16_bits(lo);
+      const float vsf = f16_val(vs16), vzf = f16_val(vz16);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float u = rintf((x[c] - vzf) / vsf);
+        u8[c] = (uint32_t)fminf(fmaxf(u, 0.f), L);
+      }
+    } else {  // symmetric 4-bit, s = absmax / 7
+      float am = fabsf(x[0]);
+#pragma unroll
+      for (int c = 1; c < 8; ++c) am = fmaxf(am, fabsf(x[c]));
+      am = fmaxf(am, __shfl_xor(am, 1));
+      am = fmaxf(am, __shfl_xor(am, 2));
+      am = am + 0.0f;
+      vs16 = f16_bits(fmaxf(EPS_SCALE, am / 7.0f));
+      const float vsf = f16_val(vs16);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float q = fminf(fmaxf(rintf(x[c] / vsf), -8.f), 7.f);
+        u8[c] = (uint32_t)(q + 8.f);
+      }
+    }
+    const bool cal = calib(t);  // sink rows: zero codes and zero metadata
+    const uint32_t c0 = u8[0] | (u8[1] << 8) | (u8[2] << 16) | (u8[3] << 24);
+    const uint32_t c1 = u8[4] | (u8[5] << 8) | (u8[6] << 16) | (u8[7] << 24);
+    *reinterpret_cast<uint2*>(&sm.vc[wv][t][8 * j]) = cal ? make_uint2(c0, c1) : make_uint2(0u, 0u);
+    if ((j & 3) == 0) {
+      const int mi = v_meta_idx(t, g, NG);
+      vm[mi] = cal ? vs16 : (uint16_t)0;
+      if constexpr (!Q2K) vm[G * NG + mi] = cal ? vz16 : (uint16_t)0;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // V code words in the matrix-core order: chunk q = lane (token group kg = q/16, channel i = q%16)
+  // holds, for channel tile mu, codes of tokens v_tok(kg, e), e = 0..7, of channel 16*mu + i
+  {
+    const int kg = lane >> 4, i = lane & 15;
+    uint32_t* vdst = reinterpret_cast<uint32_t*>(rec + lv.v_codes) + lane * WPC;
+    uint32_t words[WPC];
+#pragma unroll
+    for (int w = 0; w < WPC; ++w) words[w] = 0u;
+#pragma unroll
+    for (int mu = 0; mu < D / 16; ++mu)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t code = sm.vc[wv][v_tok(kg, e)][16 * mu + i];
+        const int sq = 8 * mu + e, w = sq / VPW, k = sq % VPW;
+        words[w] |= code << (16 * (k & 1) + VB * (k >> 1));
+      }
+#pragma unroll
+    for (int w = 0; w < WPC; ++w) vdst[w] = words[w];
+  }
+
+  // ---- fp16 window ring (rows p in [max(P, P+n-R), P+n)) and sink pool: the lanes of a row copy
+  // their 16 bytes ----
+  const int64_t wlo = (a.P + a.n - sh.R) > a.P ? (a.P + a.n - sh.R) : a.P;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int t = NI * r + i;
+    const int64_t p = base + t;
+    if (sh.R > 0 && p >= wlo) {
+      const int64_t wo = ((int64_t)s * sh.R + p % sh.R) * D + 8 * j;
+      *reinterpret_cast<uint4*>(lv.win_k + wo) = kw[i];
+      *reinterpret_cast<uint4*>(lv.win_v + wo) = vw[i];
+    }
+    const int slot = __shfl(myslot, t);
+    if (slot >= 0) {
+      const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + 8 * j;
+      *reinterpret_cast<uint4*>(lv.sink_k + so) = kw[i];
+      *reinterpret_cast<uint4*>(lv.sink_v + so) = vw[i];
+    }
+  }
+  // first-N commits (block 0 of a chunk at P = 0): positions and count, once per batch element
+  if (sh.n_sink > 0 && sh.sink_mode == KVQ_SINK_FIRST_N && h == 0 && beta == 0) {
+    const int64_t P1 = a.P + a.n;
+    if (lane < sh.n_sink && lane < P1) lv.sink_pos[b * sh.n_sink + lane] = lane;
+    if (lane == 0) lv.sink_count[b] = (int)(P1 < sh.n_sink ? P1 : sh.n_sink);
+  }
+}
+
+template <int FMT, int KB, int VB>
+hipError_t launch_full_kv(const AppendArgs& a, int64_t fb0, int nfull, hipStream_t st) {
+  const dim3 grid((nfull + FW - 1) / FW, a.sh.B * a.sh.Hkv);
+  switch (a.sh.D) {
+    case 32: hipLaunchKernelGGL((k_append_full<FMT, KB, VB, 32>), grid, dim3(64 * FW), 0, st, a, fb0, nfull); break;
+    case 64: hipLaunchKernelGGL((k_append_full<FMT, KB, VB, 64>), grid, dim3(64 * FW), 0, st, a, fb0, nfull); break;
+    case 128: hipLaunchKernelGGL((k_append_full<FMT, KB, VB, 128>), grid, dim3(64 * FW), 0, st, a, fb0, nfull); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int KB>
+hipError_t launch_full_k(const AppendArgs& a, int64_t fb0, int nfull, hipStream_t st) {
+  switch (a.sh.vb) {
+    case 2: return launch_full_kv<KVQ_FMT_KIVI, KB, 2>(a, fb0, nfull, st);
+    case 4: return launch_full_kv<KVQ_FMT_KIVI, KB, 4>(a, fb0, nfull, st);
+    case 8: return launch_full_kv<KVQ_FMT_KIVI, KB, 8>(a, fb0, nfull, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_full(const AppendArgs& a, int64_t fb0, int nfull, hipStream_t st) {
+  const Shape& sh = a.sh;
+  if (sh.fmt == KVQ_FMT_Q2K) return launch_full_kv<KVQ_FMT_Q2K, 2, 4>(a, fb0, nfull, st);
+  switch (sh.kb) {
+    case 2: return launch_full_k<2>(a, fb0, nfull, st);
+    case 4: return launch_full_k<4>(a, fb0, nfull, st);
+    case 8: return launch_full_k<8>(a, fb0, nfull, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cs(const AppendArgs& a, hipStream_t st) {
+  const Shape& sh = a.sh;
+  dim3 grid(a.nblk, sh.B * sh.Hkv, sh.D / 32);
+  if (sh.fmt == KVQ_FMT_Q2K) return launch_cs_k<KVQ_FMT_Q2K, 2>(a, grid, st);
+  switch (sh.kb) {
+    case 2: return launch_cs_k<KVQ_FMT_KIVI, 2>(a, grid, st);
+    case 4: return launch_cs_k<KVQ_FMT_KIVI, 4>(a, grid, st);
+    case 8: return launch_cs_k<KVQ_FMT_KIVI, 8>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
-  if (sh.fmt != KVQ_FMT_TQ && sh.D % 32 == 0) {  // block formats: one workgroup per 32-channel group
-    dim3 grid(a.nblk, sh.B * sh.Hkv, sh.D / 32);
-    if (sh.fmt == KVQ_FMT_Q2K) return launch_cs_k<KVQ_FMT_Q2K, 2>(a, grid, st);
-    switch (sh.kb) {
-      case 2: return launch_cs_k<KVQ_FMT_KIVI, 2>(a, grid, st);
-      case 4: return launch_cs_k<KVQ_FMT_KIVI, 4>(a, grid, st);
-      case 8: return launch_cs_k<KVQ_FMT_KIVI, 8>(a, grid, st);
-      default: return hipErrorInvalidValue;
+  if (sh.fmt != KVQ_FMT_TQ && sh.D % 32 == 0) {  // block formats
+    // whole blocks of fp16 input: one wave per (block, stream); the partial blocks at either end
+    // (an open block re-quantized from its staged rows, a block left open): one workgroup per
+    // (block, stream, 32-channel group)
+    const int64_t fb0 = (a.P + G - 1) / G, fb1 = (a.P + a.n) / G;
+    const bool aligned = (reinterpret_cast<uintptr_t>(a.k) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.v) % 16 == 0);
+    if (!sh.in_f32 && aligned && fb1 > fb0) {
+      hipError_t e = launch_full(a, fb0, (int)(fb1 - fb0), st);
+      if (e != hipSuccess) return e;
+      if (a.P % G != 0) {
+        AppendArgs e0 = a;
+        e0.blk0 = a.P / G;
+        e0.nblk = 1;
+        if ((e = launch_cs(e0, st)) != hipSuccess) return e;
+      }
+      if ((a.P + a.n) % G != 0) {
+        AppendArgs e1 = a;
+        e1.blk0 = fb1;
+        e1.nblk = 1;
+        if ((e = launch_cs(e1, st)) != hipSuccess) return e;
+      }
+      return hipSuccess;
     }
+    return launch_cs(a, st);
   }
   dim3 grid(a.nblk, sh.B * sh.Hkv);
   hipLaunchKernelGGL(k_append, grid, dim3(NT), 0, st, a);

@@ -43,6 +43,10 @@ CASES = {
                                   v_bits=2, sink_mode="topk", n_sink=3, residual=40, capacity=512, seed=11),
     "fast_tq42_r1_win": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=128, fmt="tq", k_bits=4,
                              v_bits=2, sink_mode="first_n", n_sink=4, window=96, residual=8, seed=12),
+    "kivi28_d32_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=32, fmt="kivi", k_bits=2,
+                                v_bits=8, sink_mode="topk", n_sink=3, residual=8, capacity=512),
+    "kivi84_d64_firstn_win": dict(n_layers=1, batch=2, n_kv_heads=3, n_q_heads=3, head_dim=64, fmt="kivi", k_bits=8,
+                                  v_bits=4, sink_mode="first_n", n_sink=4, window=128, residual=4),
     "fast_tq42_r2_ring_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128, fmt="tq", k_bits=4,
                                   v_bits=2, window=160, residual=16, seed=13),
 }
