@@ -155,8 +155,10 @@ kvq_status kvq_destroy(kvq_cache* c);
  * permanent sink set while it has room ([KS] "Fidelity to the paper": no
  * retroactive restore).  k: [batch][n_kv_heads][n][head_dim], 16-byte
  * aligned in TOPK mode (else KVQ_EINVAL).  Required before kvq_append in TOPK
- * mode (else KVQ_EORDER); a no-op in other modes.  Uses the cache's
- * select_work area: calls on one cache must be ordered (one stream). */
+ * mode (else KVQ_EORDER); a no-op in other modes.  Each call commits
+ * min(n_sink - |C|, n) rows, so |C| = min(n_sink, P) and a call at
+ * P >= n_sink launches nothing.  Uses the cache's select_work area: calls on
+ * one cache must be ordered (one stream). */
 kvq_status kvq_select_sinks(kvq_cache* c, int32_t layer, const void* k, int32_t n, void* stream);
 
 /* Appends n rows of K and V at positions [P, P+n) of `layer` and quantizes

@@ -356,6 +356,10 @@ kvq_status kvq_select_sinks(kvq_cache* c, int32_t layer, const void* k, int32_t 
   c->pend_n[layer] = n;
   if (c->cfg.sink_mode != KVQ_SINK_TOPK || c->cfg.n_sink == 0) return KVQ_OK;
   if ((uintptr_t)k % 16 != 0) return fail(KVQ_EINVAL, "TOPK mode: k must be 16-byte aligned");
+  // Every call commits min(n_sink - |C|, n) rows (the merged top-k holds at least that many new
+  // rows, and new rows join only while the set has room), so |C| = min(n_sink, P): once n_sink rows
+  // have arrived the set is full for good and the call has nothing to do.
+  if (c->P[layer] >= c->cfg.n_sink) return KVQ_OK;
   SelectArgs a;
   a.sh = shape_of(c->cfg);
   a.lv = view_of(c, layer);

@@ -32,6 +32,22 @@ def test_rows_one_per_call_fill_in_arrival_order_and_are_never_restored():
     assert [p for p, _ in C] == [0, 1, 2]  # a full set is permanent: later high-norm rows stay quantized
 
 
+def test_committed_count_is_min_of_n_sink_and_rows_seen():
+    # |C'| = |C| + min(n_sink - |C|, new rows in the merged top-k) and the merged top-k holds at least
+    # min(n_sink, |C| + n) - |C| new rows, so |C| = min(n_sink, P) after every call: the set is full
+    # (and every later call a no-op) exactly once n_sink rows have arrived
+    rng = np.random.default_rng(43)
+    for trial in range(200):
+        K = int(rng.integers(1, 17))
+        C, P = [], 0
+        for _ in range(int(rng.integers(1, 8))):
+            n = int(rng.integers(1, 9))
+            sc = rng.integers(0, 4, size=n).astype(np.float32)  # ties with the committed scores too
+            C = sinks.topk_commit(C, range(P, P + n), sc, K)
+            P += n
+            assert len(C) == min(K, P), (trial, K, P, len(C))
+
+
 def test_displaced_row_rule():
     # C = {a}; a later call with 10 stronger rows commits 4 of them (in rank order) and C is full
     C = sinks.topk_commit([], [0], [1.0], 5)
