@@ -1,4 +1,5 @@
-"""Dequantization and single-query decode attention reference (test infrastructure only).
+"""Dequantization, single-query decode attention and causal prefill attention references (test
+infrastructure only).
 
 Dequantization follows the StreamingLLM + KIVI page ("Affine quantisation
 formula"; "The bug class the previous attempt hit": scales cast to fp32, K and
@@ -116,6 +117,43 @@ def decode_attention(model, layer, q, scale=None, batches=None, heads=None):
             s = s - s.max()
             w = np.exp(s)
             out[bi, hi] = (w @ vh) / w.sum()
+    return out
+
+
+def prefill_attention(model, layer, q, scale=None, batches=None, heads=None, queries=None):
+    """Reference multi-query attention of a prefill chunk over the cache, causal.
+
+    q: [B, Hq, n, D] are the queries of the last n appended positions P-n .. P-1.  Query i attends
+    the valid positions p (the cache as it stands: sinks, window, bulk, read priority applied) with
+    p <= P - n + i; a query with no such position yields zeros.  Readings: the valid set
+    is the cache after the chunk's append and eviction; alpha and the GQA mapping are the decode
+    ones.  Returns fp64 [len(batches), len(heads), len(queries), D].
+    """
+    cfg = model.cfg
+    D, r = cfg.head_dim, cfg.gqa
+    P = model.P[layer]
+    q64 = np.asarray(q).astype(np.float64)
+    n = q64.shape[2]
+    assert 1 <= n <= P, "the queries are the last n appended positions"
+    alpha = 1.0 / np.sqrt(float(D)) if not scale else float(np.float32(scale))
+    batches = range(cfg.batch) if batches is None else batches
+    heads = range(cfg.n_q_heads) if heads is None else heads
+    queries = range(n) if queries is None else queries
+    out = np.zeros((len(batches), len(heads), len(queries), D), dtype=np.float64)
+    for bi, b in enumerate(batches):
+        pos = np.array(sorted(model.valid(layer, b).keys()), dtype=np.int64)
+        cache = {}
+        for hi, j in enumerate(heads):
+            g = j // r
+            if g not in cache:
+                cache[g] = (stream_values(model, layer, b, g, "k", list(pos)),
+                            stream_values(model, layer, b, g, "v", list(pos)))
+            kh, vh = cache[g]
+            for qi, i in enumerate(queries):
+                sel = pos <= P - n + i
+                if not sel.any():
+                    continue
+                out[bi, hi, qi] = softmax_attention(q64[b, j, i], kh[sel], vh[sel], alpha)
     return out
 
 
