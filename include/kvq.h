@@ -189,6 +189,20 @@ kvq_status kvq_evict(kvq_cache* c, int32_t layer);
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Causal multi-query attention of a prefill chunk over `layer` (the "next"
+ * step after append in prefill: [Q2K] "Summary" reads prefill through the
+ * same q2k cache; [TQ] "API" attention over the cached rows).  q: the
+ * queries of the last n appended positions P-n .. P-1, [batch][n_q_heads][n]
+ * [head_dim] fp16, 16-byte aligned; out: [batch][n_q_heads][n][head_dim]
+ * fp32, 16-byte aligned.  Query i attends the valid positions p <= P-n+i
+ * (sinks, window, bulk; the same values decode attention reads) with
+ * softmax(scale * q . k) weights; a query with no such position gets zeros.
+ * scale <= 0 means 1/sqrt(head_dim).  KIVI and q2k caches, head_dim 32, 64
+ * or 128 (else KVQ_EINVAL); 1 <= n <= P (else KVQ_ERANGE).  One kernel
+ * launch, no workspace; deterministic. */
+kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t n, float* out, float scale,
+                            void* stream);
+
 /* Materialises fp16 values of positions [pos0, pos0+count) of `layer`
  * (which: 0 = K, 1 = V), read priority sink > window > bulk, bulk values
  * computed in fp32 as the format's dequant formula and rounded once to fp16

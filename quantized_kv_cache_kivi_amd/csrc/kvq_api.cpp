@@ -458,6 +458,36 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   return KVQ_OK;
 }
 
+kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t n, float* out, float scale,
+                            void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!q || !out) return fail(KVQ_EINVAL, "q and out must not be NULL");
+  const kvq_config& cf = c->cfg;
+  const int64_t P = c->P[layer], lo = c->lo[layer];
+  if (n < 1 || n > P)
+    return fail(KVQ_ERANGE, "prefill attention of n=%d queries needs 1 <= n <= P=%lld (the last n positions)", n,
+                (long long)P);
+  if (cf.format == KVQ_FMT_TQ) return fail(KVQ_EINVAL, "prefill attention supports the KIVI and q2k formats");
+  if (cf.in_dtype != KVQ_IN_F16) return fail(KVQ_EINVAL, "prefill attention needs fp16 queries");
+  if (cf.head_dim != 32 && cf.head_dim != 64 && cf.head_dim != 128)
+    return fail(KVQ_EINVAL, "prefill attention needs head_dim 32, 64 or 128");
+  if ((uintptr_t)q % 16 != 0 || (uintptr_t)out % 16 != 0) return fail(KVQ_EINVAL, "q and out must be 16-byte aligned");
+  PrefillArgs a;
+  a.sh = shape_of(cf);
+  a.lv = view_of(c, layer);
+  a.q = q;
+  a.out = out;
+  a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)cf.head_dim);
+  a.P = P;
+  a.lo = lo;
+  a.bulk_hi = std::max(lo, P - (int64_t)cf.residual);
+  a.n = n;
+  hipError_t e = launch_prefill(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
+  return KVQ_OK;
+}
+
 kvq_status kvq_dequant(kvq_cache* c, int32_t layer, int32_t which, int64_t pos0, int32_t count, uint16_t* out,
                        void* stream) {
   kvq_status st = check_layer(c, layer);

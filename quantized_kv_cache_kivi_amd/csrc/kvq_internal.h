@@ -85,6 +85,16 @@ struct DecodeArgs {
                              // (MFMA path: ceil(rows / 64); TurboQuant: 1; other formats: 0)
 };
 
+struct PrefillArgs {
+  Shape sh;
+  LayerView lv;
+  const void* q;        // [B][Hq][n][D] fp16, 16-byte aligned: queries of positions P-n .. P-1
+  float* out;           // [B][Hq][n][D]
+  float scale;
+  int64_t P, lo, bulk_hi;  // valid range [lo, P) (plus sinks); bulk rows below bulk_hi
+  int n;
+};
+
 struct DequantArgs {
   Shape sh;
   LayerView lv;
@@ -99,6 +109,8 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 int select_groups(int n);  // workgroups per batch element for an n-row selection call
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+int prefill_queries_per_tile(int r);  // queries of one prefill-attention workgroup for GQA ratio r
 
 // Workgroups of the MFMA decode kernel for this shape that the current device holds at once
 // (compute units x resident workgroups per unit); 0 if the shape has no MFMA kernel.

@@ -1,0 +1,351 @@
+// Causal multi-query attention of a prefill chunk over the quantized cache: the queries of the last
+// n appended positions P-n .. P-1 attend the valid positions (sinks, fp16 window, quantized bulk,
+// read priority as in decode attention) that are not after their own position.  Dequantization
+// follows "StreamingLLM + KIVI" ("Affine quantisation formula") and the q2k page ("Summary": Gaussian
+// Lloyd-Max K levels times the block RMS, symmetric 4-bit V); the attention itself is the plain
+// softmax attention of decode, with a causal limit per query.
+//
+// One workgroup per (stream, tile of queries); its four waves each own two tiles of 16 MFMA columns
+// (16 / r queries times the r query heads of the KV head).  Key/value rows are taken 32 at a time
+// ("row blocks": a bulk block, or up to 32 fp16 window rows, or the sinks): the workgroup
+// dequantizes a row block once into LDS (K and V as fp16 hi + lo halves whose sum is the fp32
+// value, V transposed into the matrix-core token order), then every wave runs
+//   scores = K . q  (v_mfma_f32_16x16x32_f16, hi and lo halves into one accumulator),
+// the online softmax of its columns in registers (log2 units), and
+//   acc += V^T . p  (the weights, split into fp16 hi + lo, enter as the B operand straight from the
+//                    score registers: the score lane layout is the token order of the V tile;
+//                    V_hi p_hi + V_hi p_lo + V_lo p_hi).
+// Row blocks after a tile's last query are skipped; within a row block every column masks the rows
+// after its own position.
+#include "device_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int PNW = 4;    // waves per workgroup
+constexpr int PT = 2;     // 16-column tiles per wave
+constexpr int PNT = 64 * PNW;
+constexpr float PLOG2E = 1.4426950408889634f;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma(const u4& a, const u4& b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0, 0,
+                                                0);
+}
+__device__ __forceinline__ uint32_t pk2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
+__device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+
+template <int D>
+struct PfSmem {
+  alignas(16) _Float16 khi[G][D + 8];  // K rows of the row block: fp16 hi halves
+  alignas(16) _Float16 klo[G][D + 8];  // fp16 lo halves (value - hi)
+  alignas(16) _Float16 vt[D][G + 8];   // V transposed: [channel][slot], slot 8*kq + e <-> row v_tok(kq, e)
+  alignas(16) _Float16 vtl[D][G + 8];  // its fp16 lo halves
+  int pos[G];                          // position of each row (-1: not attended)
+  int spos[MAX_SINK], sslot[MAX_SINK];
+  int nsink;
+};
+
+// Value of K code (row t, channel c) and of V code (row t, channel c) of a bulk record.
+template <int FMT, int KB, int D>
+__device__ __forceinline__ float k_deq(const uint8_t* rec, const LayerView& lv, int t, int c, float lv0, float lv1,
+                                       float lv2, float lv3) {
+  constexpr int per = 32 / KB;
+  const uint32_t w = reinterpret_cast<const uint32_t*>(rec + lv.k_codes)[t * (D * KB / 32) + c / per];
+  const int k = c % per;
+  const uint32_t u = (w >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
+  const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + lv.k_meta);
+  if constexpr (FMT == KVQ_FMT_KIVI) return (float)u * f16_val(km[c]) + f16_val(km[D + c]);
+  const float lvl = u == 0 ? lv0 : (u == 1 ? lv1 : (u == 2 ? lv2 : lv3));
+  return lvl * f16_val(km[c]);
+}
+
+template <int FMT, int KB, int VB, int D>
+__global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
+  constexpr int NST = D / 32, NMU = D / 16, NG = D / 32;
+  constexpr int VPW = 32 / VB, WPC = D * VB / 64;
+  const Shape sh = a.sh;
+  const LayerView lv = a.lv;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i16 = lane & 15, kg = lane >> 4;
+  const int s = blockIdx.y, b = s / sh.Hkv, g = s % sh.Hkv;
+  const int R = sh.Hq / sh.Hkv, qpt = 16 / R;          // queries per 16-column tile
+  const int QT = PNW * PT * qpt;                        // queries per workgroup
+  const int tile = (int)gridDim.x - 1 - (int)blockIdx.x;  // the longest tiles start first
+  const int q0 = tile * QT;
+  const int qlast = min(a.n - 1, q0 + QT - 1);
+  const int64_t pbase = a.P - a.n;  // position of query 0
+  const int64_t qmax = pbase + qlast;
+  __shared__ PfSmem<D> S;
+
+  // ---- queries of this wave's columns as the B operand (K-dimension slots 8*kg .. of chunk st) ----
+  u4 bq[PT][NST];
+  int qpos[PT];  // position of the lane's column query (-1: no query)
+  int qidx[PT], head[PT];
+#pragma unroll
+  for (int tt = 0; tt < PT; ++tt) {
+    const int qi = i16 / R, jj = i16 % R;
+    const int qq = q0 + (wv * PT + tt) * qpt + qi;
+    const bool ok = qi < qpt && qq < a.n;
+    qidx[tt] = qq;
+    head[tt] = g * R + jj;
+    qpos[tt] = ok ? (int)(pbase + qq) : -1;
+    const int64_t qrow = (((int64_t)b * sh.Hq + head[tt]) * a.n + qq) * D;
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      u4 v = u4{0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u4*>(static_cast<const _Float16*>(a.q) + qrow + 32 * st + 8 * kg);
+      bq[tt][st] = v;
+    }
+  }
+  if (tid < 64) {  // committed sinks already appended, with their pool slots
+    const int ns = sh.n_sink;
+    const int cnt = ns > 0 ? lv.sink_count[b] : 0;
+    const int praw = lane < ns ? lv.sink_pos[b * ns + lane] : -1;
+    const int p = lane < min(cnt, ns) ? praw : -1;
+    const bool ok = p >= 0 && p < a.P;
+    const uint64_t m = __ballot(ok);
+    const int idx = __popcll(m & ((1ull << lane) - 1ull));
+    if (ok) {
+      S.spos[idx] = p;
+      S.sslot[idx] = lane;
+    }
+    if (lane == 0) S.nsink = __popcll(m);
+  }
+  __syncthreads();
+  const int nsink = S.nsink;
+  auto is_sink = [&](int64_t p) {
+    bool r = false;
+    for (int q = 0; q < nsink; ++q) r = r || S.spos[q] == p;
+    return r;
+  };
+
+  float m_[PT], l_[PT];
+  f4 acc[PT][NMU];
+#pragma unroll
+  for (int tt = 0; tt < PT; ++tt) {
+    m_[tt] = -INFINITY;
+    l_[tt] = 0.f;
+#pragma unroll
+    for (int mu = 0; mu < NMU; ++mu) acc[tt][mu] = f4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float al = a.scale * PLOG2E;
+  const float lv0 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[0] : 0.f;
+  const float lv1 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[1] : 0.f;
+  const float lv2 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[2] : 0.f;
+  const float lv3 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[3] : 0.f;
+
+  // row blocks: bulk blocks, then fp16 window rows in groups of 32, then the sinks
+  const int64_t bhi = a.bulk_hi < qmax + 1 ? a.bulk_hi : qmax + 1;  // bulk rows [lo, bhi)
+  const int64_t blk0 = a.lo / G;
+  const int nbulk = bhi > a.lo ? (int)((bhi - 1) / G - blk0 + 1) : 0;
+  const int64_t whi = a.P < qmax + 1 ? a.P : qmax + 1;  // window rows [bulk_hi, whi)
+  const int nwin = whi > a.bulk_hi ? (int)(whi - a.bulk_hi) : 0;
+  const int nwblk = (nwin + G - 1) / G;
+  const int nrb = nbulk + nwblk + (nsink > 0 ? 1 : 0);
+
+  for (int rb = 0; rb < nrb; ++rb) {
+    __syncthreads();  // the previous row block is consumed
+    // ---- stage the row block: thread (row t, channel slice) for K; chunk-wise for V ----
+    if (rb < nbulk) {
+      const int64_t beta = blk0 + rb;
+      const uint8_t* rec = lv.bulk + ((int64_t)s * lv.cap_b + beta % lv.cap_b) * lv.rec;
+      {
+        constexpr int CPT = D / 8;  // channels per thread
+        const int t = tid >> 3, c0 = (tid & 7) * CPT;
+#pragma unroll
+        for (int c = c0; c < c0 + CPT; c += 2) {
+          const float x0 = k_deq<FMT, KB, D>(rec, lv, t, c, lv0, lv1, lv2, lv3);
+          const float x1 = k_deq<FMT, KB, D>(rec, lv, t, c + 1, lv0, lv1, lv2, lv3);
+          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+          *reinterpret_cast<uint32_t*>(&S.khi[t][c]) = (uint32_t)h16(x0) | ((uint32_t)h16(x1) << 16);
+          *reinterpret_cast<uint32_t*>(&S.klo[t][c]) =
+              (uint32_t)h16(x0 - (float)h0) | ((uint32_t)h16(x1 - (float)h1) << 16);
+        }
+        if (tid < G) {
+          const int64_t p = beta * G + tid;
+          S.pos[tid] = (p >= a.lo && p < bhi && !is_sink(p)) ? (int)p : -1;
+        }
+      }
+      {  // V: chunk q = 16*kq + i holds, for channel tile mu, rows v_tok(kq, e) of channel 16*mu + i
+        const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
+        const uint16_t* vm = reinterpret_cast<const uint16_t*>(rec + lv.v_meta);
+        const int q = tid & 63, kq = q >> 4, i = q & 15;
+        for (int wi = tid >> 6; wi < WPC; wi += PNW) {
+          const uint32_t w = vw[q * WPC + wi];
+#pragma unroll
+          for (int k = 0; k < VPW; ++k) {
+            const int sq = wi * VPW + k, mu = sq >> 3, e = sq & 7;
+            const int t = v_tok(kq, e), c = 16 * mu + i;
+            const uint32_t u = (w >> (16 * (k & 1) + VB * (k >> 1))) & ((1u << VB) - 1u);
+            const int mi = v_meta_idx(t, c >> 5, NG);
+            float x;
+            if constexpr (FMT == KVQ_FMT_KIVI) x = (float)u * f16_val(vm[mi]) + f16_val(vm[G * NG + mi]);
+            else x = ((float)u - 8.f) * f16_val(vm[mi]);
+            const _Float16 h = (_Float16)x;
+            S.vt[c][8 * kq + e] = h;
+            S.vtl[c][8 * kq + e] = (_Float16)(x - (float)h);
+          }
+        }
+      }
+    } else {
+      // fp16 rows: window rows bulk_hi + 32*w0 .. (sinks excluded: read from the pool), or the sinks
+      const bool sinks = rb >= nbulk + nwblk;
+      const int r0 = (rb - nbulk) * G;
+      constexpr int CPT = D / 8;
+      const int t = tid >> 3, c0 = (tid & 7) * CPT;
+      int64_t p = -1;
+      const uint16_t *kr = nullptr, *vr = nullptr;
+      if (!sinks) {
+        if (r0 + t < nwin) {
+          p = a.bulk_hi + r0 + t;
+          const int64_t ws = (int64_t)s * sh.R + p % sh.R;
+          kr = lv.win_k + ws * D;
+          vr = lv.win_v + ws * D;
+          if (is_sink(p)) p = -1;
+        }
+      } else if (t < nsink && S.spos[t] <= qmax) {
+        p = S.spos[t];
+        const int64_t so = (int64_t)s * sh.n_sink + S.sslot[t];
+        kr = lv.sink_k + so * D;
+        vr = lv.sink_v + so * D;
+      }
+      // rows of this thread's V transpose: row t goes to slot 8*kq + e with v_tok(kq, e) = t
+      const int kq = (t & 15) >> 2, e = ((t >> 4) << 2) | (t & 3);
+#pragma unroll
+      for (int c = c0; c < c0 + CPT; c += 2) {
+        uint32_t kw2 = 0u, vw2 = 0u;
+        if (kr) {
+          kw2 = *reinterpret_cast<const uint32_t*>(kr + c);
+          vw2 = *reinterpret_cast<const uint32_t*>(vr + c);
+        }
+        *reinterpret_cast<uint32_t*>(&S.khi[t][c]) = kw2;
+        *reinterpret_cast<uint32_t*>(&S.klo[t][c]) = 0u;
+        S.vt[c][8 * kq + e] = __builtin_bit_cast(_Float16, (uint16_t)(vw2 & 0xFFFFu));
+        S.vt[c + 1][8 * kq + e] = __builtin_bit_cast(_Float16, (uint16_t)(vw2 >> 16));
+        S.vtl[c][8 * kq + e] = (_Float16)0.f;
+        S.vtl[c + 1][8 * kq + e] = (_Float16)0.f;
+      }
+      if ((tid & 7) == 0) S.pos[t] = (int)p;
+    }
+    __syncthreads();
+
+    // ---- every tile of this wave against the row block ----
+#pragma unroll
+    for (int tt = 0; tt < PT; ++tt) {
+      f4 c[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau) {
+          const u4 ah = *reinterpret_cast<const u4*>(&S.khi[16 * tau + i16][32 * st + 8 * kg]);
+          const u4 alo = *reinterpret_cast<const u4*>(&S.klo[16 * tau + i16][32 * st + 8 * kg]);
+          c[tau] = mfma(ah, bq[tt][st], c[tau]);
+          c[tau] = mfma(alo, bq[tt][st], c[tau]);
+        }
+      // lane (column i16, group kg) holds rows 16*tau + 4*kg + e
+      float y[8];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int p = S.pos[16 * tau + 4 * kg + e];
+          const bool ok = p >= 0 && qpos[tt] >= 0 && p <= qpos[tt];
+          y[4 * tau + e] = ok ? c[tau][e] * al : -INFINITY;
+          mb = fmaxf(mb, y[4 * tau + e]);
+        }
+      mb = fmaxf(mb, __shfl_xor(mb, 16));
+      mb = fmaxf(mb, __shfl_xor(mb, 32));
+      const float mnew = fmaxf(m_[tt], mb);
+      if (__any(mnew > m_[tt])) {
+        const float f = mnew == m_[tt] ? 1.f : (m_[tt] == -INFINITY ? 0.f : exp2f(m_[tt] - mnew));
+        l_[tt] *= f;
+#pragma unroll
+        for (int mu = 0; mu < NMU; ++mu) acc[tt][mu] *= f;
+        m_[tt] = mnew;
+      }
+      float pw[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        pw[k] = mnew == -INFINITY ? 0.f : exp2f(y[k] - mnew);
+        l_[tt] += pw[k];
+      }
+      // weights as fp16 hi + lo halves (the pair is exact to ~2^-22 of the weight)
+      float ph[8], pl[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        ph[k] = (float)(_Float16)pw[k];
+        pl[k] = pw[k] - ph[k];
+      }
+      const u4 bph = u4{pk2(ph[0], ph[1]), pk2(ph[2], ph[3]), pk2(ph[4], ph[5]), pk2(ph[6], ph[7])};
+      const u4 bpl = u4{pk2(pl[0], pl[1]), pk2(pl[2], pl[3]), pk2(pl[4], pl[5]), pk2(pl[6], pl[7])};
+#pragma unroll
+      for (int mu = 0; mu < NMU; ++mu) {  // V_hi p_hi + V_hi p_lo + V_lo p_hi
+        const u4 avh = *reinterpret_cast<const u4*>(&S.vt[16 * mu + i16][8 * kg]);
+        const u4 avl = *reinterpret_cast<const u4*>(&S.vtl[16 * mu + i16][8 * kg]);
+        acc[tt][mu] = mfma(avh, bph, acc[tt][mu]);
+        acc[tt][mu] = mfma(avh, bpl, acc[tt][mu]);
+        acc[tt][mu] = mfma(avl, bph, acc[tt][mu]);
+      }
+    }
+  }
+
+  // ---- outputs: lane (column i16, group kg) holds channels 16*mu + 4*kg .. + 3 ----
+#pragma unroll
+  for (int tt = 0; tt < PT; ++tt) {
+    float l = l_[tt];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (qpos[tt] < 0) continue;
+    const float il = l > 0.f ? 1.f / l : 0.f;
+    float* o = a.out + (((int64_t)b * sh.Hq + head[tt]) * a.n + qidx[tt]) * D;
+#pragma unroll
+    for (int mu = 0; mu < NMU; ++mu) *reinterpret_cast<f4*>(o + 16 * mu + 4 * kg) = acc[tt][mu] * il;
+  }
+}
+
+template <int FMT, int KB, int VB>
+hipError_t launch_d(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.sh.D) {
+    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32>), grid, dim3(PNT), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64>), grid, dim3(PNT), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128>), grid, dim3(PNT), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+template <int KB>
+hipError_t launch_kivi(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  switch (a.sh.vb) {
+    case 2: return launch_d<KVQ_FMT_KIVI, KB, 2>(a, grid, st);
+    case 4: return launch_d<KVQ_FMT_KIVI, KB, 4>(a, grid, st);
+    case 8: return launch_d<KVQ_FMT_KIVI, KB, 8>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int prefill_queries_per_tile(int r) { return PNW * PT * (16 / r); }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
+  const Shape& sh = a.sh;
+  const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv);
+  const dim3 grid((a.n + QT - 1) / QT, sh.B * sh.Hkv);
+  if (sh.fmt == KVQ_FMT_Q2K) return launch_d<KVQ_FMT_Q2K, 2, 4>(a, grid, st);
+  if (sh.fmt != KVQ_FMT_KIVI) return hipErrorInvalidValue;
+  switch (sh.kb) {
+    case 2: return launch_kivi<2>(a, grid, st);
+    case 4: return launch_kivi<4>(a, grid, st);
+    case 8: return launch_kivi<8>(a, grid, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace kvq
