@@ -32,6 +32,7 @@ import time
 
 METRIC = "decode-attn HBM GB/s (% of peak) + context tokens/s over quantized KV cache"
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak
 
 CONFIGS = {
     1: dict(name="tiny-streaming-int8", kw=dict(n_layers=12, batch=1, n_kv_heads=8, n_q_heads=8, head_dim=32,
@@ -164,6 +165,51 @@ def prefill_bytes(kw, P, n):
     app = S * (2 * n * D * esz + staged_in + n * (D * (kb + vb) // 8 + vmeta_tok) + nblk * kmeta_blk
                + min(n, R) * 2 * D * 2 + staged_out)
     return sel, app
+
+
+def prefill_attention_flops(kw, P, lo, n, sinks_per_b):
+    """Algorithmic FLOPs of one causal prefill-attention call: 4*D per (query head, query, attended
+    row), the attended rows of query i being the valid positions (sinks, [lo, P)) up to P-n+i."""
+    D, Hq = kw["head_dim"], kw["n_q_heads"]
+    total = 0
+    for b in range(kw["batch"]):
+        early = sorted(p for p in sinks_per_b[b] if p < lo)
+        for i in range(n):
+            pos = P - n + i
+            total += max(0, pos - lo + 1) + sum(1 for p in early if p <= pos)
+    return 4 * D * Hq * total
+
+
+def prefill_attention_figure(kw, cache, P, sinks_per_b, seed, dev, stream, max_flops=5e13):
+    """kvq_prefill_attn of the queries of the last min(4096, P) positions on one replica right after
+    its prefill: median of three calls (HIP timing events) against the fp16 matrix-core peak."""
+    import torch
+    from quantized_kv_cache_kivi_amd import synth
+    if P == 0 or kw.get("fmt") == "tq" or kw.get("in_dtype") == "f32":
+        return None
+    n = min(4096, P)
+    _, lo = cache.kvq_get_state(0)
+    flops = prefill_attention_flops(kw, P, lo, n, sinks_per_b)
+    if flops > max_flops:
+        return {"skipped": f"{flops / 1e12:.0f} TFLOP per call exceeds the bench budget"}
+    q = synth.normal((kw["batch"], kw["n_q_heads"], n, kw["head_dim"]), seed, 60_000, dev).half().contiguous()
+    out = torch.empty((kw["batch"], kw["n_q_heads"], n, kw["head_dim"]), dtype=torch.float32, device=dev)
+    cache.kvq_prefill_attn(0, q, out)
+    ts = []
+    for _ in range(3):
+        e = HipTimer()
+        e.record(0, stream)
+        cache.kvq_prefill_attn(0, q, out)
+        e.record(1, stream)
+        torch.cuda.synchronize()
+        ts.append(e.ms())
+    t = sorted(ts)[1]
+    achieved = flops / (t * 1e-3) / 1e12
+    return {"queries": n, "P": P, "us": t * 1e3, "TFLOP_per_call": flops / 1e12,
+            "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / MFMA_F16_PEAK_TFLOPS},
+            "note": "algorithmic FLOPs (4*D per query head, query and attended row); the kernel issues 2.5x "
+                    "that on the matrix cores (K and V, weights as fp16 hi + lo pairs)"}
 
 
 def algorithmic_bytes(kw, P, lo, sinks_per_b):
@@ -440,6 +486,7 @@ def main():
         pos = reps[0].region(0, "sink_pos", n * 4).cpu().view(torch.int32).reshape(kw["batch"], kw["n_sink"])
         sinks_per_b = [[int(p) for p in row if p >= 0] for row in pos.tolist()]
     log(f"[bench] prefill done; sinks of b=0: {sinks_per_b[0]}")
+    prefill_attn = prefill_attention_figure(kw, reps[0], T0, sinks_per_b, seed, dev, pstream)
 
     # per-step inputs, resident on the GPU before timing
     step_kv = [make_rows(args.config, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(total_steps)]
@@ -537,6 +584,7 @@ def main():
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "warm_cache": warm,
         "prefill": prefill,
+        "prefill_attn": prefill_attn,
     }
     if not args.no_cpu_baseline:
         try:

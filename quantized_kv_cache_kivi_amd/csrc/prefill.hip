@@ -235,29 +235,40 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
     }
     __syncthreads();
 
-    // ---- every tile of this wave against the row block ----
+    // ---- the wave's tiles against the row block: every LDS operand read feeds all tiles ----
+    f4 c[PT][2];
+#pragma unroll
+    for (int tt = 0; tt < PT; ++tt) c[tt][0] = c[tt][1] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NST; ++st)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const u4 ah = *reinterpret_cast<const u4*>(&S.khi[16 * tau + i16][32 * st + 8 * kg]);
+        const u4 alo = *reinterpret_cast<const u4*>(&S.klo[16 * tau + i16][32 * st + 8 * kg]);
+#pragma unroll
+        for (int tt = 0; tt < PT; ++tt) {
+          c[tt][tau] = mfma(ah, bq[tt][st], c[tt][tau]);
+          c[tt][tau] = mfma(alo, bq[tt][st], c[tt][tau]);
+        }
+      }
+    // lane (column i16, group kg) holds rows 16*tau + 4*kg + e
+    int rp[8];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rp[4 * tau + e] = S.pos[16 * tau + 4 * kg + e];
+    u4 bph[PT], bpl[PT];
 #pragma unroll
     for (int tt = 0; tt < PT; ++tt) {
-      f4 c[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int st = 0; st < NST; ++st)
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-          const u4 ah = *reinterpret_cast<const u4*>(&S.khi[16 * tau + i16][32 * st + 8 * kg]);
-          const u4 alo = *reinterpret_cast<const u4*>(&S.klo[16 * tau + i16][32 * st + 8 * kg]);
-          c[tau] = mfma(ah, bq[tt][st], c[tau]);
-          c[tau] = mfma(alo, bq[tt][st], c[tau]);
-        }
-      // lane (column i16, group kg) holds rows 16*tau + 4*kg + e
       float y[8];
       float mb = -INFINITY;
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int p = S.pos[16 * tau + 4 * kg + e];
+          const int p = rp[4 * tau + e];
           const bool ok = p >= 0 && qpos[tt] >= 0 && p <= qpos[tt];
-          y[4 * tau + e] = ok ? c[tau][e] * al : -INFINITY;
+          y[4 * tau + e] = ok ? c[tt][tau][e] * al : -INFINITY;
           mb = fmaxf(mb, y[4 * tau + e]);
         }
       mb = fmaxf(mb, __shfl_xor(mb, 16));
@@ -270,28 +281,27 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         for (int mu = 0; mu < NMU; ++mu) acc[tt][mu] *= f;
         m_[tt] = mnew;
       }
-      float pw[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        pw[k] = mnew == -INFINITY ? 0.f : exp2f(y[k] - mnew);
-        l_[tt] += pw[k];
-      }
       // weights as fp16 hi + lo halves (the pair is exact to ~2^-22 of the weight)
       float ph[8], pl[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        ph[k] = (float)(_Float16)pw[k];
-        pl[k] = pw[k] - ph[k];
+        const float pw = mnew == -INFINITY ? 0.f : exp2f(y[k] - mnew);
+        l_[tt] += pw;
+        ph[k] = (float)(_Float16)pw;
+        pl[k] = pw - ph[k];
       }
-      const u4 bph = u4{pk2(ph[0], ph[1]), pk2(ph[2], ph[3]), pk2(ph[4], ph[5]), pk2(ph[6], ph[7])};
-      const u4 bpl = u4{pk2(pl[0], pl[1]), pk2(pl[2], pl[3]), pk2(pl[4], pl[5]), pk2(pl[6], pl[7])};
+      bph[tt] = u4{pk2(ph[0], ph[1]), pk2(ph[2], ph[3]), pk2(ph[4], ph[5]), pk2(ph[6], ph[7])};
+      bpl[tt] = u4{pk2(pl[0], pl[1]), pk2(pl[2], pl[3]), pk2(pl[4], pl[5]), pk2(pl[6], pl[7])};
+    }
 #pragma unroll
-      for (int mu = 0; mu < NMU; ++mu) {  // V_hi p_hi + V_hi p_lo + V_lo p_hi
-        const u4 avh = *reinterpret_cast<const u4*>(&S.vt[16 * mu + i16][8 * kg]);
-        const u4 avl = *reinterpret_cast<const u4*>(&S.vtl[16 * mu + i16][8 * kg]);
-        acc[tt][mu] = mfma(avh, bph, acc[tt][mu]);
-        acc[tt][mu] = mfma(avh, bpl, acc[tt][mu]);
-        acc[tt][mu] = mfma(avl, bph, acc[tt][mu]);
+    for (int mu = 0; mu < NMU; ++mu) {  // V_hi p_hi + V_hi p_lo + V_lo p_hi
+      const u4 avh = *reinterpret_cast<const u4*>(&S.vt[16 * mu + i16][8 * kg]);
+      const u4 avl = *reinterpret_cast<const u4*>(&S.vtl[16 * mu + i16][8 * kg]);
+#pragma unroll
+      for (int tt = 0; tt < PT; ++tt) {
+        acc[tt][mu] = mfma(avh, bph[tt], acc[tt][mu]);
+        acc[tt][mu] = mfma(avh, bpl[tt], acc[tt][mu]);
+        acc[tt][mu] = mfma(avl, bph[tt], acc[tt][mu]);
       }
     }
   }
