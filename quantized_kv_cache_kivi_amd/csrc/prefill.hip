@@ -51,20 +51,6 @@ struct PfSmem {
   int nsink;
 };
 
-// Value of K code (row t, channel c) and of V code (row t, channel c) of a bulk record.
-template <int FMT, int KB, int D>
-__device__ __forceinline__ float k_deq(const uint8_t* rec, const LayerView& lv, int t, int c, float lv0, float lv1,
-                                       float lv2, float lv3) {
-  constexpr int per = 32 / KB;
-  const uint32_t w = reinterpret_cast<const uint32_t*>(rec + lv.k_codes)[t * (D * KB / 32) + c / per];
-  const int k = c % per;
-  const uint32_t u = (w >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
-  const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + lv.k_meta);
-  if constexpr (FMT == KVQ_FMT_KIVI) return (float)u * f16_val(km[c]) + f16_val(km[D + c]);
-  const float lvl = u == 0 ? lv0 : (u == 1 ? lv1 : (u == 2 ? lv2 : lv3));
-  return lvl * f16_val(km[c]);
-}
-
 template <int FMT, int KB, int VB, int D>
 __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   constexpr int NST = D / 32, NMU = D / 16, NG = D / 32;
@@ -148,24 +134,49 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   const int nwin = whi > a.bulk_hi ? (int)(whi - a.bulk_hi) : 0;
   const int nwblk = (nwin + G - 1) / G;
   const int nrb = nbulk + nwblk + (nsink > 0 ? 1 : 0);
+  const int slot0 = (int)(blk0 % lv.cap_b);                        // ring slot of the first bulk block
+  const int wslot0 = nwin > 0 ? (int)(a.bulk_hi % sh.R) : 0;        // window slot of row bulk_hi
+  const uint8_t* sbase = lv.bulk + (int64_t)s * lv.cap_b * lv.rec;  // this stream's ring
 
   for (int rb = 0; rb < nrb; ++rb) {
     __syncthreads();  // the previous row block is consumed
     // ---- stage the row block: thread (row t, channel slice) for K; chunk-wise for V ----
+    constexpr int CPT = D / 8;  // channels per thread
+    const int t = tid >> 3, c0 = (tid & 7) * CPT;
     if (rb < nbulk) {
       const int64_t beta = blk0 + rb;
-      const uint8_t* rec = lv.bulk + ((int64_t)s * lv.cap_b + beta % lv.cap_b) * lv.rec;
-      {
-        constexpr int CPT = D / 8;  // channels per thread
-        const int t = tid >> 3, c0 = (tid & 7) * CPT;
+      int slot = slot0 + rb;
+      if (slot >= lv.cap_b) slot -= lv.cap_b;
+      const uint8_t* rec = sbase + (int64_t)slot * lv.rec;
+      {  // K: codes of row t, channels c0 .. c0 + CPT - 1, with their metadata
+        constexpr int per = 32 / KB;
+        const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + lv.k_codes) + t * (D * KB / 32);
+        const uint32_t* km = reinterpret_cast<const uint32_t*>(rec + lv.k_meta);
+        uint32_t sc[CPT / 2], zc[CPT / 2];
 #pragma unroll
-        for (int c = c0; c < c0 + CPT; c += 2) {
-          const float x0 = k_deq<FMT, KB, D>(rec, lv, t, c, lv0, lv1, lv2, lv3);
-          const float x1 = k_deq<FMT, KB, D>(rec, lv, t, c + 1, lv0, lv1, lv2, lv3);
-          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-          *reinterpret_cast<uint32_t*>(&S.khi[t][c]) = (uint32_t)h16(x0) | ((uint32_t)h16(x1) << 16);
-          *reinterpret_cast<uint32_t*>(&S.klo[t][c]) =
-              (uint32_t)h16(x0 - (float)h0) | ((uint32_t)h16(x1 - (float)h1) << 16);
+        for (int i = 0; i < CPT / 2; ++i) {
+          sc[i] = km[c0 / 2 + i];
+          zc[i] = FMT == KVQ_FMT_KIVI ? km[D / 2 + c0 / 2 + i] : 0u;
+        }
+#pragma unroll
+        for (int i = 0; i < CPT / 2; ++i) {
+          float x[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int c = c0 + 2 * i + h, k = c % per;
+            const uint32_t u = (kw[c / per] >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
+            const float sf = f16_val((uint16_t)(sc[i] >> (16 * h)));
+            if constexpr (FMT == KVQ_FMT_KIVI) {
+              x[h] = (float)u * sf + f16_val((uint16_t)(zc[i] >> (16 * h)));
+            } else {
+              const float lvl = u == 0 ? lv0 : (u == 1 ? lv1 : (u == 2 ? lv2 : lv3));
+              x[h] = lvl * sf;
+            }
+          }
+          const _Float16 h0 = (_Float16)x[0], h1 = (_Float16)x[1];
+          *reinterpret_cast<uint32_t*>(&S.khi[t][c0 + 2 * i]) = (uint32_t)h16(x[0]) | ((uint32_t)h16(x[1]) << 16);
+          *reinterpret_cast<uint32_t*>(&S.klo[t][c0 + 2 * i]) =
+              (uint32_t)h16(x[0] - (float)h0) | ((uint32_t)h16(x[1] - (float)h1) << 16);
         }
         if (tid < G) {
           const int64_t p = beta * G + tid;
@@ -174,39 +185,65 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       }
       {  // V: chunk q = 16*kq + i holds, for channel tile mu, rows v_tok(kq, e) of channel 16*mu + i
         const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
-        const uint16_t* vm = reinterpret_cast<const uint16_t*>(rec + lv.v_meta);
+        const uint32_t* vm = reinterpret_cast<const uint32_t*>(rec + lv.v_meta);
         const int q = tid & 63, kq = q >> 4, i = q & 15;
+        constexpr int EPW = VPW < 8 ? VPW : 8;  // row slots of one channel a word covers
         for (int wi = tid >> 6; wi < WPC; wi += PNW) {
           const uint32_t w = vw[q * WPC + wi];
 #pragma unroll
-          for (int k = 0; k < VPW; ++k) {
-            const int sq = wi * VPW + k, mu = sq >> 3, e = sq & 7;
-            const int t = v_tok(kq, e), c = 16 * mu + i;
-            const uint32_t u = (w >> (16 * (k & 1) + VB * (k >> 1))) & ((1u << VB) - 1u);
-            const int mi = v_meta_idx(t, c >> 5, NG);
-            float x;
-            if constexpr (FMT == KVQ_FMT_KIVI) x = (float)u * f16_val(vm[mi]) + f16_val(vm[G * NG + mi]);
-            else x = ((float)u - 8.f) * f16_val(vm[mi]);
-            const _Float16 h = (_Float16)x;
-            S.vt[c][8 * kq + e] = h;
-            S.vtl[c][8 * kq + e] = (_Float16)(x - (float)h);
+          for (int k0 = 0; k0 < VPW; k0 += EPW) {
+            const int sq0 = wi * VPW + k0, mu = sq0 >> 3, e0 = sq0 & 7, c = 16 * mu + i, gq = c >> 5;
+            // metadata of the word's rows: token pairs (t, t+1) share a dword in each section
+            float hv[EPW], lvv[EPW];
+#pragma unroll
+            for (int ee = 0; ee < EPW; ee += 2) {
+              const int e = e0 + ee, tk = v_tok(kq, e);  // tk even, tk + 1 = v_tok(kq, e + 1)
+              const int mi = v_meta_idx(tk, gq, NG) >> 1;
+              const uint32_t sw = vm[mi];
+              const uint32_t zw = FMT == KVQ_FMT_KIVI ? vm[G * NG / 2 + mi] : 0u;
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const int k = k0 + ee + h;
+                const uint32_t u = (w >> (16 * (k & 1) + VB * (k >> 1))) & ((1u << VB) - 1u);
+                const float sf = f16_val((uint16_t)(sw >> (16 * h)));
+                float x;
+                if constexpr (FMT == KVQ_FMT_KIVI) x = (float)u * sf + f16_val((uint16_t)(zw >> (16 * h)));
+                else x = ((float)u - 8.f) * sf;
+                const _Float16 hx = (_Float16)x;
+                hv[ee + h] = (float)hx;
+                lvv[ee + h] = x - (float)hx;
+              }
+            }
+            uint32_t ph[EPW / 2], pl[EPW / 2];
+#pragma unroll
+            for (int m = 0; m < EPW / 2; ++m) {
+              ph[m] = (uint32_t)h16(hv[2 * m]) | ((uint32_t)h16(hv[2 * m + 1]) << 16);
+              pl[m] = (uint32_t)h16(lvv[2 * m]) | ((uint32_t)h16(lvv[2 * m + 1]) << 16);
+            }
+            if constexpr (EPW == 8) {
+              *reinterpret_cast<u4*>(&S.vt[c][8 * kq]) = u4{ph[0], ph[1], ph[2], ph[3]};
+              *reinterpret_cast<u4*>(&S.vtl[c][8 * kq]) = u4{pl[0], pl[1], pl[2], pl[3]};
+            } else {
+              *reinterpret_cast<uint2*>(&S.vt[c][8 * kq + e0]) = make_uint2(ph[0], ph[1]);
+              *reinterpret_cast<uint2*>(&S.vtl[c][8 * kq + e0]) = make_uint2(pl[0], pl[1]);
+            }
           }
         }
       }
     } else {
-      // fp16 rows: window rows bulk_hi + 32*w0 .. (sinks excluded: read from the pool), or the sinks
+      // fp16 rows: window rows bulk_hi + r0 + t (sinks excluded: read from the pool), or the sinks
       const bool sinks = rb >= nbulk + nwblk;
       const int r0 = (rb - nbulk) * G;
-      constexpr int CPT = D / 8;
-      const int t = tid >> 3, c0 = (tid & 7) * CPT;
       int64_t p = -1;
       const uint16_t *kr = nullptr, *vr = nullptr;
       if (!sinks) {
         if (r0 + t < nwin) {
           p = a.bulk_hi + r0 + t;
-          const int64_t ws = (int64_t)s * sh.R + p % sh.R;
-          kr = lv.win_k + ws * D;
-          vr = lv.win_v + ws * D;
+          int ws = wslot0 + r0 + t;  // nwin <= R, so one wrap at most
+          if (ws >= sh.R) ws -= sh.R;
+          const int64_t wo = (int64_t)s * sh.R + ws;
+          kr = lv.win_k + wo * D;
+          vr = lv.win_v + wo * D;
           if (is_sink(p)) p = -1;
         }
       } else if (t < nsink && S.spos[t] <= qmax) {
@@ -275,7 +312,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       mb = fmaxf(mb, __shfl_xor(mb, 32));
       const float mnew = fmaxf(m_[tt], mb);
       if (__any(mnew > m_[tt])) {
-        const float f = mnew == m_[tt] ? 1.f : (m_[tt] == -INFINITY ? 0.f : exp2f(m_[tt] - mnew));
+        const float f = mnew == m_[tt] ? 1.f : (m_[tt] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_[tt] - mnew));
         l_[tt] *= f;
 #pragma unroll
         for (int mu = 0; mu < NMU; ++mu) acc[tt][mu] *= f;
@@ -285,7 +322,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       float ph[8], pl[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float pw = mnew == -INFINITY ? 0.f : exp2f(y[k] - mnew);
+        const float pw = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(y[k] - mnew);
         l_[tt] += pw;
         ph[k] = (float)(_Float16)pw;
         pl[k] = pw - ph[k];
