@@ -25,6 +25,7 @@ namespace {
 constexpr int PNW = 4;    // waves per workgroup
 constexpr int PT = 2;     // 16-column tiles per wave
 constexpr int PNT = 64 * PNW;
+constexpr int SL = PNT / G;  // staging threads per row
 constexpr float PLOG2E = 1.4426950408889634f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -141,8 +142,8 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   for (int rb = 0; rb < nrb; ++rb) {
     __syncthreads();  // the previous row block is consumed
     // ---- stage the row block: thread (row t, channel slice) for K; chunk-wise for V ----
-    constexpr int CPT = D / 8;  // channels per thread
-    const int t = tid >> 3, c0 = (tid & 7) * CPT;
+    constexpr int CPT = D / SL;  // channels per staging thread
+    const int t = tid / SL, c0 = (tid % SL) * CPT;
     if (rb < nbulk) {
       const int64_t beta = blk0 + rb;
       int slot = slot0 + rb;
@@ -268,7 +269,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         S.vtl[c][8 * kq + e] = (_Float16)0.f;
         S.vtl[c + 1][8 * kq + e] = (_Float16)0.f;
       }
-      if ((tid & 7) == 0) S.pos[t] = (int)p;
+      if (tid % SL == 0) S.pos[t] = (int)p;
     }
     __syncthreads();
 
