@@ -185,7 +185,7 @@ def prefill_attention_figure(kw, cache, P, sinks_per_b, seed, dev, stream, max_f
     its prefill: median of three calls (HIP timing events) against the fp16 matrix-core peak."""
     import torch
     from quantized_kv_cache_kivi_amd import synth
-    if P == 0 or kw.get("fmt") == "tq" or kw.get("in_dtype") == "f32":
+    if P == 0 or kw.get("in_dtype") == "f32":
         return None
     n = min(4096, P)
     _, lo = cache.kvq_get_state(0)
@@ -209,7 +209,8 @@ def prefill_attention_figure(kw, cache, P, sinks_per_b, seed, dev, stream, max_f
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": achieved / MFMA_F16_PEAK_TFLOPS},
             "note": "algorithmic FLOPs (4*D per query head, query and attended row); the kernel issues 2.5x "
-                    "that on the matrix cores (K and V, weights as fp16 hi + lo pairs)"}
+                    "that on the matrix cores (K and V, weights as fp16 hi + lo pairs; 3x for TurboQuant, "
+                    "whose rotated queries are hi + lo pairs too)"}
 
 
 def algorithmic_bytes(kw, P, lo, sinks_per_b):

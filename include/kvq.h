@@ -197,9 +197,10 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
  * fp32, 16-byte aligned.  Query i attends the valid positions p <= P-n+i
  * (sinks, window, bulk; the same values decode attention reads) with
  * softmax(scale * q . k) weights; a query with no such position gets zeros.
- * scale <= 0 means 1/sqrt(head_dim).  KIVI and q2k caches, head_dim 32, 64
- * or 128 (else KVQ_EINVAL); 1 <= n <= P (else KVQ_ERANGE).  One kernel
- * launch, no workspace; deterministic. */
+ * scale <= 0 means 1/sqrt(head_dim).  Every cache format (TurboQuant in the
+ * rotated domain: queries rotated once, outputs rotated back); fp16 input
+ * caches only, head_dim 32, 64 or 128 (else KVQ_EINVAL); 1 <= n <= P (else
+ * KVQ_ERANGE).  One kernel launch, no workspace; deterministic. */
 kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t n, float* out, float scale,
                             void* stream);
 

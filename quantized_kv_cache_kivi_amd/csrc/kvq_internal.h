@@ -110,7 +110,7 @@ int select_groups(int n);  // workgroups per batch element for an n-row selectio
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
-int prefill_queries_per_tile(int r);  // queries of one prefill-attention workgroup for GQA ratio r
+int prefill_queries_per_tile(int r, int fmt);  // queries of one prefill-attention workgroup
 
 // Workgroups of the MFMA decode kernel for this shape that the current device holds at once
 // (compute units x resident workgroups per unit); 0 if the shape has no MFMA kernel.

@@ -20,10 +20,10 @@
 #include "device_common.h"
 
 namespace kvq {
+constexpr int PT = 2;     // 16-column tiles per wave (block formats)
 namespace {
 
 constexpr int PNW = 4;    // waves per workgroup
-constexpr int PT = 2;     // 16-column tiles per wave
 constexpr int PNT = 64 * PNW;
 constexpr int SL = PNT / G;  // staging threads per row
 constexpr float PLOG2E = 1.4426950408889634f;
@@ -50,10 +50,16 @@ struct PfSmem {
   int pos[G];                          // position of each row (-1: not attended)
   int spos[MAX_SINK], sslot[MAX_SINK];
   int nsink;
+  float kcen[16], vcen[16];  // TurboQuant centroids (rotated domain)
 };
 
 template <int FMT, int KB, int VB, int D>
 __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
+  // TurboQuant works in the rotated domain ("TurboQuant KV Cache Compression — Spec", "Optimization:
+  // Fused dequant-dot"): queries rotated once (fp16 hi + lo, a third score product), bulk rows are
+  // norm times centroid, fp16 window and sink rows are rotated while staged, outputs rotated back
+  constexpr bool TQ = FMT == KVQ_FMT_TQ;
+  constexpr int PT = TQ ? 1 : ::kvq::PT;  // column tiles per wave
   constexpr int NST = D / 32, NMU = D / 16, NG = D / 32;
   constexpr int VPW = 32 / VB, WPC = D * VB / 64;
   const Shape sh = a.sh;
@@ -71,23 +77,73 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   __shared__ PfSmem<D> S;
 
   // ---- queries of this wave's columns as the B operand (K-dimension slots 8*kg .. of chunk st) ----
-  u4 bq[PT][NST];
+  u4 bq[PT][NST], bql[TQ ? PT : 1][TQ ? NST : 1];
   int qpos[PT];  // position of the lane's column query (-1: no query)
   int qidx[PT], head[PT];
+  const float cd = (float)(1.0 / __builtin_sqrt((double)D));
+  float sg0 = 0.f, sg1 = 0.f;  // TurboQuant signs of channels 2*lane, 2*lane + 1
+  if constexpr (TQ) {
+    sg0 = 2 * lane < D ? lv.tables->signs[2 * lane] : 0.f;
+    sg1 = 2 * lane < D ? lv.tables->signs[2 * lane + 1] : 0.f;
+    if (tid < 16) S.kcen[tid] = lv.tables->k_cen[tid & ((1 << KB) - 1)];
+    if (tid >= 16 && tid < 32) S.vcen[tid - 16] = lv.tables->v_cen[(tid - 16) & ((1 << VB) - 1)];
+  }
+  auto col_query = [&](int tt, int col, int* qq_out, int* head_out) {
+    const int qi = col / R, jj = col % R;
+    const int qq = q0 + (wv * PT + tt) * qpt + qi;
+    *qq_out = qq;
+    *head_out = g * R + jj;
+    return qi < qpt && qq < a.n;
+  };
 #pragma unroll
   for (int tt = 0; tt < PT; ++tt) {
-    const int qi = i16 / R, jj = i16 % R;
-    const int qq = q0 + (wv * PT + tt) * qpt + qi;
-    const bool ok = qi < qpt && qq < a.n;
+    int qq, hd;
+    const bool ok = col_query(tt, i16, &qq, &hd);
     qidx[tt] = qq;
-    head[tt] = g * R + jj;
+    head[tt] = hd;
     qpos[tt] = ok ? (int)(pbase + qq) : -1;
-    const int64_t qrow = (((int64_t)b * sh.Hq + head[tt]) * a.n + qq) * D;
+    if constexpr (!TQ) {
+      const int64_t qrow = (((int64_t)b * sh.Hq + hd) * a.n + qq) * D;
 #pragma unroll
-    for (int st = 0; st < NST; ++st) {
-      u4 v = u4{0u, 0u, 0u, 0u};
-      if (ok) v = *reinterpret_cast<const u4*>(static_cast<const _Float16*>(a.q) + qrow + 32 * st + 8 * kg);
-      bq[tt][st] = v;
+      for (int st = 0; st < NST; ++st) {
+        u4 v = u4{0u, 0u, 0u, 0u};
+        if (ok) v = *reinterpret_cast<const u4*>(static_cast<const _Float16*>(a.q) + qrow + 32 * st + 8 * kg);
+        bq[tt][st] = v;
+      }
+    } else {
+      // rotate the wave's 16 column queries one by one (lane l holds channels 2l, 2l + 1) into a
+      // wave-private LDS tile, then read each lane's B-operand slice back as fp16 hi + lo
+      float* qs = reinterpret_cast<float*>(&S.khi[0][0]) + wv * 16 * D;
+      for (int col = 0; col < 16; ++col) {
+        int cq, ch;
+        const bool cok = col_query(tt, col, &cq, &ch);
+        float y0 = 0.f, y1 = 0.f;
+        if (cok && 2 * lane < D) {
+          const uint32_t w =
+              reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + (((int64_t)b * sh.Hq + ch) * a.n + cq) * D)[lane];
+          y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)) * sg0;
+          y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) * sg1;
+        }
+        wave_fwht(y0, y1, D, lane);
+        if (2 * lane < D) {
+          qs[col * D + 2 * lane] = y0 * cd;
+          qs[col * D + 2 * lane + 1] = y1 * cd;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int st = 0; st < NST; ++st) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const float x0 = qs[i16 * D + 32 * st + 8 * kg + 2 * m], x1 = qs[i16 * D + 32 * st + 8 * kg + 2 * m + 1];
+          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+          hw[m] = (uint32_t)h16(x0) | ((uint32_t)h16(x1) << 16);
+          lw[m] = (uint32_t)h16(x0 - (float)h0) | ((uint32_t)h16(x1 - (float)h1) << 16);
+        }
+        bq[tt][st] = u4{hw[0], hw[1], hw[2], hw[3]};
+        bql[tt][st] = u4{lw[0], lw[1], lw[2], lw[3]};
+      }
     }
   }
   if (tid < 64) {  // committed sinks already appended, with their pool slots
@@ -154,10 +210,15 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + lv.k_codes) + t * (D * KB / 32);
         const uint32_t* km = reinterpret_cast<const uint32_t*>(rec + lv.k_meta);
         uint32_t sc[CPT / 2], zc[CPT / 2];
+        float nk = 0.f;  // TurboQuant: the row's K norm
+        if constexpr (TQ) {
+          nk = reinterpret_cast<const float*>(rec + lv.k_meta)[t];
+        } else {
 #pragma unroll
-        for (int i = 0; i < CPT / 2; ++i) {
-          sc[i] = km[c0 / 2 + i];
-          zc[i] = FMT == KVQ_FMT_KIVI ? km[D / 2 + c0 / 2 + i] : 0u;
+          for (int i = 0; i < CPT / 2; ++i) {
+            sc[i] = km[c0 / 2 + i];
+            zc[i] = FMT == KVQ_FMT_KIVI ? km[D / 2 + c0 / 2 + i] : 0u;
+          }
         }
 #pragma unroll
         for (int i = 0; i < CPT / 2; ++i) {
@@ -166,10 +227,13 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
           for (int h = 0; h < 2; ++h) {
             const int c = c0 + 2 * i + h, k = c % per;
             const uint32_t u = (kw[c / per] >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
-            const float sf = f16_val((uint16_t)(sc[i] >> (16 * h)));
-            if constexpr (FMT == KVQ_FMT_KIVI) {
+            if constexpr (TQ) {
+              x[h] = nk * S.kcen[u];
+            } else if constexpr (FMT == KVQ_FMT_KIVI) {
+              const float sf = f16_val((uint16_t)(sc[i] >> (16 * h)));
               x[h] = (float)u * sf + f16_val((uint16_t)(zc[i] >> (16 * h)));
             } else {
+              const float sf = f16_val((uint16_t)(sc[i] >> (16 * h)));
               const float lvl = u == 0 ? lv0 : (u == 1 ? lv1 : (u == 2 ? lv2 : lv3));
               x[h] = lvl * sf;
             }
@@ -200,15 +264,21 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
             for (int ee = 0; ee < EPW; ee += 2) {
               const int e = e0 + ee, tk = v_tok(kq, e);  // tk even, tk + 1 = v_tok(kq, e + 1)
               const int mi = v_meta_idx(tk, gq, NG) >> 1;
-              const uint32_t sw = vm[mi];
+              const uint32_t sw = TQ ? 0u : vm[mi];
               const uint32_t zw = FMT == KVQ_FMT_KIVI ? vm[G * NG / 2 + mi] : 0u;
+              float nv[2] = {0.f, 0.f};  // TurboQuant: V norms of rows tk, tk + 1
+              if constexpr (TQ) {
+                nv[0] = reinterpret_cast<const float*>(rec + lv.v_meta)[tk];
+                nv[1] = reinterpret_cast<const float*>(rec + lv.v_meta)[tk + 1];
+              }
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
                 const int k = k0 + ee + h;
                 const uint32_t u = (w >> (16 * (k & 1) + VB * (k >> 1))) & ((1u << VB) - 1u);
                 const float sf = f16_val((uint16_t)(sw >> (16 * h)));
                 float x;
-                if constexpr (FMT == KVQ_FMT_KIVI) x = (float)u * sf + f16_val((uint16_t)(zw >> (16 * h)));
+                if constexpr (TQ) x = nv[h] * S.vcen[u];
+                else if constexpr (FMT == KVQ_FMT_KIVI) x = (float)u * sf + f16_val((uint16_t)(zw >> (16 * h)));
                 else x = ((float)u - 8.f) * sf;
                 const _Float16 hx = (_Float16)x;
                 hv[ee + h] = (float)hx;
@@ -235,41 +305,82 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       // fp16 rows: window rows bulk_hi + r0 + t (sinks excluded: read from the pool), or the sinks
       const bool sinks = rb >= nbulk + nwblk;
       const int r0 = (rb - nbulk) * G;
-      int64_t p = -1;
-      const uint16_t *kr = nullptr, *vr = nullptr;
-      if (!sinks) {
-        if (r0 + t < nwin) {
-          p = a.bulk_hi + r0 + t;
-          int ws = wslot0 + r0 + t;  // nwin <= R, so one wrap at most
-          if (ws >= sh.R) ws -= sh.R;
-          const int64_t wo = (int64_t)s * sh.R + ws;
-          kr = lv.win_k + wo * D;
-          vr = lv.win_v + wo * D;
-          if (is_sink(p)) p = -1;
+      auto row_src = [&](int tr, int64_t* pp, const uint16_t** kp, const uint16_t** vp) {
+        *pp = -1;
+        *kp = *vp = nullptr;
+        if (!sinks) {
+          if (r0 + tr < nwin) {
+            *pp = a.bulk_hi + r0 + tr;
+            int ws = wslot0 + r0 + tr;  // nwin <= R, so one wrap at most
+            if (ws >= sh.R) ws -= sh.R;
+            const int64_t wo = (int64_t)s * sh.R + ws;
+            *kp = lv.win_k + wo * D;
+            *vp = lv.win_v + wo * D;
+            if (is_sink(*pp)) *pp = -1;
+          }
+        } else if (tr < nsink && S.spos[tr] <= qmax) {
+          *pp = S.spos[tr];
+          const int64_t so = (int64_t)s * sh.n_sink + S.sslot[tr];
+          *kp = lv.sink_k + so * D;
+          *vp = lv.sink_v + so * D;
         }
-      } else if (t < nsink && S.spos[t] <= qmax) {
-        p = S.spos[t];
-        const int64_t so = (int64_t)s * sh.n_sink + S.sslot[t];
-        kr = lv.sink_k + so * D;
-        vr = lv.sink_v + so * D;
-      }
-      // rows of this thread's V transpose: row t goes to slot 8*kq + e with v_tok(kq, e) = t
-      const int kq = (t & 15) >> 2, e = ((t >> 4) << 2) | (t & 3);
+      };
+      if constexpr (TQ) {  // one row per wave pass, rotated: lane l holds channels 2l, 2l + 1
+        for (int rr = 0; rr < G / PNW; ++rr) {
+          const int tr = wv + PNW * rr;
+          int64_t p;
+          const uint16_t *kr, *vr;
+          row_src(tr, &p, &kr, &vr);
+          float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
+          if (kr && 2 * lane < D) {
+            const uint32_t kw2 = reinterpret_cast<const uint32_t*>(kr)[lane];
+            const uint32_t vw2 = reinterpret_cast<const uint32_t*>(vr)[lane];
+            k0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(kw2 & 0xFFFFu)) * sg0;
+            k1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(kw2 >> 16)) * sg1;
+            v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw2 & 0xFFFFu)) * sg0;
+            v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw2 >> 16)) * sg1;
+          }
+          wave_fwht(k0, k1, D, lane);
+          wave_fwht(v0, v1, D, lane);
+          k0 *= cd;
+          k1 *= cd;
+          v0 *= cd;
+          v1 *= cd;
+          if (2 * lane < D) {
+            const _Float16 hk0 = (_Float16)k0, hk1 = (_Float16)k1, hv0 = (_Float16)v0, hv1 = (_Float16)v1;
+            *reinterpret_cast<uint32_t*>(&S.khi[tr][2 * lane]) = (uint32_t)h16(k0) | ((uint32_t)h16(k1) << 16);
+            *reinterpret_cast<uint32_t*>(&S.klo[tr][2 * lane]) =
+                (uint32_t)h16(k0 - (float)hk0) | ((uint32_t)h16(k1 - (float)hk1) << 16);
+            const int kq = (tr & 15) >> 2, e = ((tr >> 4) << 2) | (tr & 3);
+            S.vt[2 * lane][8 * kq + e] = hv0;
+            S.vt[2 * lane + 1][8 * kq + e] = hv1;
+            S.vtl[2 * lane][8 * kq + e] = (_Float16)(v0 - (float)hv0);
+            S.vtl[2 * lane + 1][8 * kq + e] = (_Float16)(v1 - (float)hv1);
+          }
+          if (lane == 0) S.pos[tr] = (int)p;
+        }
+      } else {
+        int64_t p;
+        const uint16_t *kr, *vr;
+        row_src(t, &p, &kr, &vr);
+        // rows of this thread's V transpose: row t goes to slot 8*kq + e with v_tok(kq, e) = t
+        const int kq = (t & 15) >> 2, e = ((t >> 4) << 2) | (t & 3);
 #pragma unroll
-      for (int c = c0; c < c0 + CPT; c += 2) {
-        uint32_t kw2 = 0u, vw2 = 0u;
-        if (kr) {
-          kw2 = *reinterpret_cast<const uint32_t*>(kr + c);
-          vw2 = *reinterpret_cast<const uint32_t*>(vr + c);
+        for (int c = c0; c < c0 + CPT; c += 2) {
+          uint32_t kw2 = 0u, vw2 = 0u;
+          if (kr) {
+            kw2 = *reinterpret_cast<const uint32_t*>(kr + c);
+            vw2 = *reinterpret_cast<const uint32_t*>(vr + c);
+          }
+          *reinterpret_cast<uint32_t*>(&S.khi[t][c]) = kw2;
+          *reinterpret_cast<uint32_t*>(&S.klo[t][c]) = 0u;
+          S.vt[c][8 * kq + e] = __builtin_bit_cast(_Float16, (uint16_t)(vw2 & 0xFFFFu));
+          S.vt[c + 1][8 * kq + e] = __builtin_bit_cast(_Float16, (uint16_t)(vw2 >> 16));
+          S.vtl[c][8 * kq + e] = (_Float16)0.f;
+          S.vtl[c + 1][8 * kq + e] = (_Float16)0.f;
         }
-        *reinterpret_cast<uint32_t*>(&S.khi[t][c]) = kw2;
-        *reinterpret_cast<uint32_t*>(&S.klo[t][c]) = 0u;
-        S.vt[c][8 * kq + e] = __builtin_bit_cast(_Float16, (uint16_t)(vw2 & 0xFFFFu));
-        S.vt[c + 1][8 * kq + e] = __builtin_bit_cast(_Float16, (uint16_t)(vw2 >> 16));
-        S.vtl[c][8 * kq + e] = (_Float16)0.f;
-        S.vtl[c + 1][8 * kq + e] = (_Float16)0.f;
+        if (tid % SL == 0) S.pos[t] = (int)p;
       }
-      if (tid % SL == 0) S.pos[t] = (int)p;
     }
     __syncthreads();
 
@@ -287,6 +398,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         for (int tt = 0; tt < PT; ++tt) {
           c[tt][tau] = mfma(ah, bq[tt][st], c[tt][tau]);
           c[tt][tau] = mfma(alo, bq[tt][st], c[tt][tau]);
+          if constexpr (TQ) c[tt][tau] = mfma(ah, bql[tt][st], c[tt][tau]);
         }
       }
     // lane (column i16, group kg) holds rows 16*tau + 4*kg + e
@@ -345,16 +457,37 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   }
 
   // ---- outputs: lane (column i16, group kg) holds channels 16*mu + 4*kg .. + 3 ----
+  if constexpr (TQ) __syncthreads();  // the LDS tiles become the rotation scratch
 #pragma unroll
   for (int tt = 0; tt < PT; ++tt) {
     float l = l_[tt];
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
-    if (qpos[tt] < 0) continue;
     const float il = l > 0.f ? 1.f / l : 0.f;
-    float* o = a.out + (((int64_t)b * sh.Hq + head[tt]) * a.n + qidx[tt]) * D;
+    if constexpr (!TQ) {
+      if (qpos[tt] < 0) continue;
+      float* o = a.out + (((int64_t)b * sh.Hq + head[tt]) * a.n + qidx[tt]) * D;
 #pragma unroll
-    for (int mu = 0; mu < NMU; ++mu) *reinterpret_cast<f4*>(o + 16 * mu + 4 * kg) = acc[tt][mu] * il;
+      for (int mu = 0; mu < NMU; ++mu) *reinterpret_cast<f4*>(o + 16 * mu + 4 * kg) = acc[tt][mu] * il;
+    } else {
+      // rotated-domain rows to a wave-private LDS tile, then o = sigma * (c_d * FWHT(row)) per column
+      float* os = reinterpret_cast<float*>(&S.khi[0][0]) + wv * 16 * D;
+#pragma unroll
+      for (int mu = 0; mu < NMU; ++mu) *reinterpret_cast<f4*>(os + i16 * D + 16 * mu + 4 * kg) = acc[tt][mu] * il;
+      __builtin_amdgcn_wave_barrier();
+      for (int col = 0; col < 16; ++col) {
+        int cq, ch;
+        const bool cok = col_query(tt, col, &cq, &ch);
+        float y0 = 2 * lane < D ? os[col * D + 2 * lane] : 0.f;
+        float y1 = 2 * lane < D ? os[col * D + 2 * lane + 1] : 0.f;
+        wave_fwht(y0, y1, D, lane);
+        if (cok && 2 * lane < D) {
+          float* o = a.out + (((int64_t)b * sh.Hq + ch) * a.n + cq) * D;
+          *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(sg0 * (y0 * cd), sg1 * (y1 * cd));
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
   }
 }
 
@@ -380,13 +513,20 @@ hipError_t launch_kivi(const PrefillArgs& a, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-int prefill_queries_per_tile(int r) { return PNW * PT * (16 / r); }
+int prefill_queries_per_tile(int r, int fmt) { return PNW * (fmt == KVQ_FMT_TQ ? 1 : PT) * (16 / r); }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
-  const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv);
+  const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv, sh.fmt);
   const dim3 grid((a.n + QT - 1) / QT, sh.B * sh.Hkv);
   if (sh.fmt == KVQ_FMT_Q2K) return launch_d<KVQ_FMT_Q2K, 2, 4>(a, grid, st);
+  if (sh.fmt == KVQ_FMT_TQ) {
+    if (sh.kb == 4 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 4, 2>(a, grid, st);
+    if (sh.kb == 2 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 2, 2>(a, grid, st);
+    if (sh.kb == 4 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 4, 4>(a, grid, st);
+    if (sh.kb == 2 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 2, 4>(a, grid, st);
+    return hipErrorInvalidValue;
+  }
   if (sh.fmt != KVQ_FMT_KIVI) return hipErrorInvalidValue;
   switch (sh.kb) {
     case 2: return launch_kivi<2>(a, grid, st);

@@ -2,8 +2,9 @@
 
 Bar: for every (b, query head, query) row, ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3 (the decode
 attention bar); rows whose query has no valid position are zeros on both sides, exactly.  Cases
-cover GQA ratios 1, 2, 3 (padding columns), 4 and 8, head_dim 32, 64 and 128, KIVI widths and q2k,
-top-k and first-n sinks, the fp16 window, an evicting ring (early queries whose own rows are gone),
+cover GQA ratios 1, 2, 3 (padding columns), 4 and 8, head_dim 32, 64 and 128, KIVI widths, q2k and
+TurboQuant (every K/V width pair: rotated queries, rotated fp16 rows, outputs rotated back), top-k
+and first-n sinks, the fp16 window, an evicting ring (early queries whose own rows are gone),
 several query tiles per stream and a chunk that starts inside an open block.
 """
 import numpy as np
@@ -29,6 +30,14 @@ CASES = {
                           residual=0, capacity=1024), [300, 45]),
     "kivi24_r3_topk": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=6, head_dim=128, fmt="kivi", k_bits=2,
                             v_bits=4, sink_mode="topk", n_sink=5, residual=0, capacity=1024), [90, 250]),
+    "tq42_r4_topk_res16": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=4,
+                                v_bits=2, sink_mode="topk", n_sink=3, residual=16, capacity=1024), [70, 100, 1, 33]),
+    "tq22_r2_d64_ring": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=2,
+                              v_bits=2, sink_mode="first_n", n_sink=2, window=32, residual=8), [60, 20, 33]),
+    "tq44_r1_d32": (dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="tq", k_bits=4, v_bits=4,
+                         residual=0, capacity=1024), [150, 45]),
+    "tq24_r8_firstn": (dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=8, head_dim=128, fmt="tq", k_bits=2,
+                            v_bits=4, sink_mode="first_n", n_sink=4, residual=40, capacity=1024), [200, 7]),
 }
 
 
@@ -83,9 +92,8 @@ def test_prefill_rejects_bad_calls():
     with pytest.raises(kvq.KvqError) as e:
         pair.gpu.kvq_prefill_attn(0, q, out)  # more queries than appended positions
     assert e.value.status == -2
-    tq = Pair(data_seed=3, n_layers=1, batch=1, n_kv_heads=1, n_q_heads=4, head_dim=128, fmt="tq", k_bits=4,
-              v_bits=2, capacity=256)
-    tq.push(0, 10)
+    buf = torch.zeros(c.batch * c.n_q_heads * 10 * c.head_dim + 1, dtype=torch.float16, device="cuda")
+    qmis = buf[1:].view(c.batch, c.n_q_heads, 10, c.head_dim)  # 2-byte aligned only
     with pytest.raises(kvq.KvqError) as e:
-        tq.gpu.kvq_prefill_attn(0, q[:1, :4, :10].contiguous(), out[:1, :4, :10].contiguous())
+        pair.gpu.kvq_prefill_attn(0, qmis, out[:, :, :10].contiguous())
     assert e.value.status == -1
