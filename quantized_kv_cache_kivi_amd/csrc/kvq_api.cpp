@@ -31,6 +31,19 @@ kvq_status fail(kvq_status st, const char* fmt, ...) {
 
 uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
+}  // namespace
+
+namespace kvq {
+// The calling thread's error text, shared with the whole-T cache's entry points.
+kvq_status set_error(kvq_status st, const char* msg) {
+  g_err = msg;
+  return st;
+}
+void clear_error() { g_err.clear(); }
+}  // namespace kvq
+
+namespace {
+
 struct RecordSections {
   uint64_t kc, vc, km, vm, rec;
 };

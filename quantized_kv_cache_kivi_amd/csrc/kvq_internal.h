@@ -118,6 +118,10 @@ int fast_resident_slots(const Shape& sh);
 // fp16 rows (window and sinks) one fp16 workgroup of the MFMA decode kernel takes.
 int fast_fp16_rows_per_group();
 
+// The calling thread's error text (kvq_last_error), for every entry point of the library.
+kvq_status set_error(kvq_status st, const char* msg);
+void clear_error();
+
 // Host-side table generation (tables.cpp).
 void make_tables(const kvq_config& cfg, Tables* t);
 

@@ -1,0 +1,477 @@
+// Kernels of the whole-T KIVI cache (kvq_whole.h), following "StreamingLLM + KIVI — long-context
+// decode without growing the KV cache": "KIVI — int8/int4 KV cache with greedy-lossless decode"
+// (K per channel over every stored token, re-computed on each append; V per token), "Affine
+// quantisation formula" (scale = max(1e-5, range / (qMax - qMin)), zero = min, signed codes),
+// "Storage layout" (int8 rows, fp16 per-channel K and per-row V metadata) and "Caveats" (the
+// whole stored K is re-quantised on every append).
+//
+// Every kernel streams int8 rows: a thread owns 8 channels of a row (one 8-byte code load, one
+// 16- or 32-byte input load), D/8 neighbouring lanes cover a row, and a wave walks 512/D rows at
+// a time.  Per-row reductions (V min/max, scores) are xor shuffles inside the D/8-lane group.
+//   append   k_stats:   per tile of 256 stored + new rows, the channel min/max of the stored K
+//                       (dequantised with the current metadata) and of the new rows; the new V rows
+//                       are quantised and stored on the way;
+//            k_requant: every tile reduces the per-tile extremes to the new metadata and codes its
+//                       rows again (stored rows from their dequantised values, new rows from the
+//                       input); tile 0 writes the metadata.  The previous metadata is read from the
+//                       copy k_stats left in the workspace, so no tile sees a half-written table.
+//   decode   k_decode:  split-K over the stored rows: the query is folded with the K scales once
+//                       per workgroup (q'_c = q_c s_c, kappa = sum_c q_c z_c), score = q'.u + kappa,
+//                       online softmax per row group, V rows dequantised in fp32; one partial
+//                       (acc, m, l) per split and head;
+//            k_merge:   the partials of a (b, query head) in fixed split order.
+#include "whole_internal.h"
+
+namespace kvqw {
+namespace {
+
+constexpr int NT = 256;
+constexpr float EPS = 1e-5f;
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+__device__ __forceinline__ float f16_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ float lo16(uint32_t w) { return f16_val((uint16_t)(w & 0xFFFFu)); }
+__device__ __forceinline__ float hi16(uint32_t w) { return f16_val((uint16_t)(w >> 16)); }
+
+// Slot of stored row j (sinks first, then the ring rows).
+__device__ __forceinline__ int row_slot(const Rows& r, int j) {
+  if (j < r.nsk) return j;
+  int t = r.rs0 + (j - r.nsk);
+  if (t >= r.ring) t -= r.ring;
+  return r.n_sink + t;
+}
+
+// Slot of new row i of an append.
+__device__ __forceinline__ int new_slot(const AppendArgs& a, int i) {
+  if (i < a.nsk_new) return a.old.nsk + i;  // positions below n_sink: every earlier row is a sink
+  int t = a.ps0 + (i - a.nsk_new);
+  if (t >= a.old.ring) t -= a.old.ring;
+  return a.old.n_sink + t;
+}
+
+// 8 consecutive input elements (fp16 or fp32), 16-byte aligned.
+template <bool F32>
+__device__ __forceinline__ void ld8(const void* p, int64_t i, float* x) {
+  if constexpr (F32) {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i);
+    const uint4 b = *reinterpret_cast<const uint4*>(static_cast<const float*>(p) + i + 4);
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __builtin_bit_cast(float, w[e]);
+  } else {
+    const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      x[2 * m] = lo16(w[m]);
+      x[2 * m + 1] = hi16(w[m]);
+    }
+  }
+}
+
+// u = q - qMin of 8 signed codes, as fp32 (exact).
+__device__ __forceinline__ void codes8(uint2 w, int qmin, float* u) {
+  const uint32_t ww[2] = {w.x, w.y};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) u[e] = (float)((int)(int8_t)(uint8_t)(ww[e >> 2] >> (8 * (e & 3))) - qmin);
+}
+
+// Signed codes of 8 values against fp32 scale and zero: u = clamp(rint((x - z)/s), 0, L), q = u + qMin.
+__device__ __forceinline__ uint2 quant8(const float* x, const float* s, const float* z, float L, int qmin) {
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float u = fminf(fmaxf(rintf((x[e] - z[e]) / s[e]), 0.f), L);
+    w[e >> 2] |= ((uint32_t)((int)u + qmin) & 0xFFu) << (8 * (e & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+__device__ __forceinline__ void ld_meta8(const uint16_t* p, float* x) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    x[2 * m] = lo16(w[m]);
+    x[2 * m + 1] = hi16(w[m]);
+  }
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
+  constexpr int CG = D / 8, RP = NT / CG;
+  const Shape sh = a.sh;
+  const int s = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+  const int cg = tid % CG, rl = tid / CG;
+  const int qmin = sh.bits == 8 ? -128 : -8;
+  const float L = (float)((1 << sh.bits) - 1);
+  const int nold = a.old.nsk + a.old.nring, ntot = nold + a.n;
+  const int j0 = tile * RPT, j1 = min(ntot, j0 + RPT);
+  __shared__ float smn[RP * D], smx[RP * D];
+  float so[8], zo[8];
+  ld_meta8(a.v.ks + (int64_t)s * D + 8 * cg, so);
+  ld_meta8(a.v.kz + (int64_t)s * D + 8 * cg, zo);
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = INFINITY;
+    mx[e] = -INFINITY;
+  }
+  const int64_t in0 = (int64_t)s * a.n;
+  for (int j = j0 + rl; j < j1; j += RP) {
+    float x[8];
+    if (j < nold) {
+      const int sl = row_slot(a.old, j);
+      codes8(*reinterpret_cast<const uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg), qmin, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * so[e] + zo[e];  // two roundings (no contraction)
+    } else {
+      const int i = j - nold;
+      ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
+      // the new V row: per-token min/max over all channels, final at append
+      float v[8];
+      ld8<F32>(a.vin, (in0 + i) * D + 8 * cg, v);
+      float vmn = v[0], vmx = v[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) {
+        vmn = fminf(vmn, v[e]);
+        vmx = fmaxf(vmx, v[e]);
+      }
+#pragma unroll
+      for (int o = CG / 2; o >= 1; o >>= 1) {
+        vmn = fminf(vmn, __shfl_xor(vmn, o));
+        vmx = fmaxf(vmx, __shfl_xor(vmx, o));
+      }
+      vmn = vmn + 0.f;
+      vmx = vmx + 0.f;
+      const uint16_t s16 = f16_bits(fmaxf(EPS, (vmx - vmn) / L)), z16 = f16_bits(vmn);
+      float sv[8], zv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        sv[e] = f16_val(s16);
+        zv[e] = f16_val(z16);
+      }
+      const int sl = new_slot(a, i);
+      const int64_t ro = (int64_t)s * sh.cap + sl;
+      *reinterpret_cast<uint2*>(a.v.vc + ro * D + 8 * cg) = quant8(v, sv, zv, L, qmin);
+      if (cg == 0) {
+        a.v.vs[ro] = s16;
+        a.v.vz[ro] = z16;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = fminf(mn[e], x[e]);
+      mx[e] = fmaxf(mx[e], x[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    smn[rl * D + 8 * cg + e] = mn[e];
+    smx[rl * D + 8 * cg + e] = mx[e];
+  }
+  __syncthreads();
+  if (tid < D) {
+    float m0 = INFINITY, m1 = -INFINITY;
+    for (int r = 0; r < RP; ++r) {
+      m0 = fminf(m0, smn[r * D + tid]);
+      m1 = fmaxf(m1, smx[r * D + tid]);
+    }
+    float* pp = a.part + ((int64_t)s * a.tiles + tile) * 2 * D;
+    pp[tid] = m0;
+    pp[D + tid] = m1;
+    if (tile == 0) {
+      a.oldm[(int64_t)s * 2 * D + tid] = a.v.ks[(int64_t)s * D + tid];
+      a.oldm[(int64_t)s * 2 * D + D + tid] = a.v.kz[(int64_t)s * D + tid];
+    }
+  }
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) void k_requant(AppendArgs a) {
+  constexpr int CG = D / 8, RP = NT / CG;
+  const Shape sh = a.sh;
+  const int s = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
+  const int cg = tid % CG, rl = tid / CG;
+  const int qmin = sh.bits == 8 ? -128 : -8;
+  const float L = (float)((1 << sh.bits) - 1);
+  const int nold = a.old.nsk + a.old.nring, ntot = nold + a.n;
+  const int j0 = tile * RPT, j1 = min(ntot, j0 + RPT);
+  __shared__ float sns[D], snz[D], sos[D], soz[D];
+  if (tid < D) {
+    // channel min/max over every row: the per-tile extremes, reduced in tile order
+    float m0 = INFINITY, m1 = -INFINITY;
+    const float* pp = a.part + (int64_t)s * a.tiles * 2 * D;
+    for (int t = 0; t < a.tiles; ++t) {
+      m0 = fminf(m0, pp[t * 2 * D + tid]);
+      m1 = fmaxf(m1, pp[t * 2 * D + D + tid]);
+    }
+    m0 = m0 + 0.f;
+    m1 = m1 + 0.f;
+    const uint16_t s16 = f16_bits(fmaxf(EPS, (m1 - m0) / L)), z16 = f16_bits(m0);
+    sns[tid] = f16_val(s16);
+    snz[tid] = f16_val(z16);
+    sos[tid] = f16_val(a.oldm[(int64_t)s * 2 * D + tid]);
+    soz[tid] = f16_val(a.oldm[(int64_t)s * 2 * D + D + tid]);
+    if (tile == 0) {
+      a.v.ks[(int64_t)s * D + tid] = s16;
+      a.v.kz[(int64_t)s * D + tid] = z16;
+    }
+  }
+  __syncthreads();
+  float ns[8], nz[8], so[8], zo[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    ns[e] = sns[8 * cg + e];
+    nz[e] = snz[8 * cg + e];
+    so[e] = sos[8 * cg + e];
+    zo[e] = soz[8 * cg + e];
+  }
+  const int64_t in0 = (int64_t)s * a.n;
+  for (int j = j0 + rl; j < j1; j += RP) {
+    float x[8];
+    int sl;
+    if (j < nold) {
+      sl = row_slot(a.old, j);
+      codes8(*reinterpret_cast<const uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg), qmin, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = x[e] * so[e] + zo[e];
+    } else {
+      const int i = j - nold;
+      sl = new_slot(a, i);
+      ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
+    }
+    *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg) = quant8(x, ns, nz, L, qmin);
+  }
+}
+
+template <int D, int R, bool F32>
+__global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
+  constexpr int CG = D / 8, TPI = 64 / CG, NW = NT / 64;
+  const Shape sh = a.sh;
+  const int s = blockIdx.y, split = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int b = s / sh.H, g = s % sh.H;
+  const int cg = lane % CG, tau = lane / CG;
+  const int qmin = sh.bits == 8 ? -128 : -8;
+  __shared__ float sq[R][D], skap[R];
+  __shared__ float smw[NW][R], slw[NW][R];
+  __shared__ float sacc[NW][R][D];
+  auto qval = [&](int h, int c) {
+    const int64_t i = ((int64_t)b * sh.Hq + g * R + h) * D + c;
+    return F32 ? static_cast<const float*>(a.q)[i] : f16_val(static_cast<const uint16_t*>(a.q)[i]);
+  };
+  for (int i = tid; i < R * D; i += NT) {
+    const int h = i / D, c = i % D;
+    sq[h][c] = qval(h, c) * f16_val(a.v.ks[(int64_t)s * D + c]);
+  }
+  if (tid < R) {
+    float k = 0.f;
+    for (int c = 0; c < D; ++c) k = k + qval(tid, c) * f16_val(a.v.kz[(int64_t)s * D + c]);
+    skap[tid] = k;
+  }
+  __syncthreads();
+  float qf[R][8], kap[R], m[R], l[R], acc[R][8];
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      qf[h][e] = sq[h][8 * cg + e];
+      acc[h][e] = 0.f;
+    }
+    kap[h] = skap[h];
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+  }
+  const float al = a.scale * LOG2E;
+  const int nst = a.rows.nsk + a.rows.nring;
+  const int j0 = split * a.rows_per_split, j1 = min(nst, j0 + a.rows_per_split);
+  for (int j = j0 + wv * TPI + tau; j < j1; j += NW * TPI) {
+    const int64_t ro = (int64_t)s * sh.cap + row_slot(a.rows, j);
+    float uk[8], uv[8];
+    codes8(*reinterpret_cast<const uint2*>(a.v.kc + ro * D + 8 * cg), qmin, uk);
+    codes8(*reinterpret_cast<const uint2*>(a.v.vc + ro * D + 8 * cg), qmin, uv);
+    const float vsf = f16_val(a.v.vs[ro]), vzf = f16_val(a.v.vz[ro]);
+    float xv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xv[e] = uv[e] * vsf + vzf;
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p = p + qf[h][e] * uk[e];
+#pragma unroll
+      for (int o = CG / 2; o >= 1; o >>= 1) p = p + __shfl_xor(p, o);
+      const float sc = (p + kap[h]) * al;
+      const float mn = fmaxf(m[h], sc);
+      const float corr = __builtin_amdgcn_exp2f(m[h] - mn);  // 0 while m is -inf
+      const float pw = __builtin_amdgcn_exp2f(sc - mn);
+      l[h] = l[h] * corr + pw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * corr + pw * xv[e];
+      m[h] = mn;
+    }
+  }
+  // row groups of the wave (lanes cg + CG*tau), then the waves through LDS
+#pragma unroll
+  for (int h = 0; h < R; ++h) {
+    float M = m[h];
+#pragma unroll
+    for (int o = CG; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float w = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - M);
+    float lw = l[h] * w;
+#pragma unroll
+    for (int o = CG; o < 64; o <<= 1) lw = lw + __shfl_xor(lw, o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float aw = acc[h][e] * w;
+#pragma unroll
+      for (int o = CG; o < 64; o <<= 1) aw = aw + __shfl_xor(aw, o);
+      acc[h][e] = aw;
+    }
+    m[h] = M;
+    l[h] = lw;
+  }
+  if (tau == 0) {
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sacc[wv][h][8 * cg + e] = acc[h][e];
+      if (cg == 0) {
+        smw[wv][h] = m[h];
+        slw[wv][h] = l[h];
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < R * D; i += NT) {
+    const int h = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, smw[w][h]);
+    float av = 0.f, lv = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = smw[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(smw[w][h] - M);
+      av = av + sacc[w][h][c] * wt;
+      lv = lv + slw[w][h] * wt;
+    }
+    float* pp = a.part + (((int64_t)s * a.splits + split) * R + h) * (D + 2);
+    pp[c] = av;
+    if (c == 0) {
+      pp[D] = M;
+      pp[D + 1] = lv;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
+  const Shape sh = a.sh;
+  const int bj = blockIdx.x, R = sh.Hq / sh.H;
+  const int b = bj / sh.Hq, jq = bj % sh.Hq, g = jq / R, h = jq % R, s = b * sh.H + g;
+  const int c = threadIdx.x;
+  const int64_t stride = (int64_t)R * (D + 2);
+  const float* base = a.part + ((int64_t)s * a.splits * R + h) * (D + 2);
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[sp * stride + D]);
+  float av = 0.f, lv = 0.f;
+  for (int sp = 0; sp < a.splits; ++sp) {
+    const float ms = base[sp * stride + D];
+    const float wt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+    av = av + base[sp * stride + c] * wt;
+    lv = lv + base[sp * stride + D + 1] * wt;
+  }
+  a.out[(int64_t)bj * D + c] = lv > 0.f ? av / lv : 0.f;
+}
+
+__global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
+  const Shape sh = a.sh;
+  const int D = sh.D, CG = D / 8;
+  const int s = blockIdx.y;
+  const int idx = blockIdx.x * NT + threadIdx.x;
+  const int row = idx / CG, cg = idx % CG;
+  if (row >= a.count) return;
+  const int64_t p = a.pos0 + row;
+  const int sl = p < a.n_sink ? (int)p : a.n_sink + (int)((p - a.n_sink) % a.ring);
+  const int64_t ro = (int64_t)s * sh.cap + sl;
+  const int qmin = sh.bits == 8 ? -128 : -8;
+  float u[8];
+  codes8(*reinterpret_cast<const uint2*>((a.which == 0 ? a.v.kc : a.v.vc) + ro * D + 8 * cg), qmin, u);
+  uint16_t* o = a.out + ((int64_t)s * a.count + row) * D + 8 * cg;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int c = 8 * cg + e;
+    const float sc = a.which == 0 ? f16_val(a.v.ks[(int64_t)s * D + c]) : f16_val(a.v.vs[ro]);
+    const float z = a.which == 0 ? f16_val(a.v.kz[(int64_t)s * D + c]) : f16_val(a.v.vz[ro]);
+    o[e] = f16_bits(u[e] * sc + z);
+  }
+}
+
+template <int D, bool F32>
+hipError_t append_d(const AppendArgs& a, hipStream_t st) {
+  const dim3 grid(a.tiles, a.sh.B * a.sh.H);
+  hipLaunchKernelGGL((k_stats<D, F32>), grid, dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_requant<D, F32>), grid, dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, int R, bool F32>
+hipError_t decode_r(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_decode<D, R, F32>), dim3(a.splits, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_merge<D>), dim3(a.sh.B * a.sh.Hq), dim3(D), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D, bool F32>
+hipError_t decode_d(const DecodeArgs& a, hipStream_t st) {
+  switch (a.sh.Hq / a.sh.H) {
+    case 1: return decode_r<D, 1, F32>(a, st);
+    case 2: return decode_r<D, 2, F32>(a, st);
+    case 4: return decode_r<D, 4, F32>(a, st);
+    case 8: return decode_r<D, 8, F32>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool F32>
+hipError_t decode_f(const DecodeArgs& a, hipStream_t st) {
+  switch (a.sh.D) {
+    case 32: return decode_d<32, F32>(a, st);
+    case 64: return decode_d<64, F32>(a, st);
+    case 128: return decode_d<128, F32>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool F32>
+hipError_t append_f(const AppendArgs& a, hipStream_t st) {
+  switch (a.sh.D) {
+    case 32: return append_d<32, F32>(a, st);
+    case 64: return append_d<64, F32>(a, st);
+    case 128: return append_d<128, F32>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
+  return a.sh.in_f32 ? append_f<true>(a, st) : append_f<false>(a, st);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  return a.sh.in_f32 ? decode_f<true>(a, st) : decode_f<false>(a, st);
+}
+
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t st) {
+  const int per = a.count * (a.sh.D / 8);
+  hipLaunchKernelGGL(k_dequant, dim3((per + NT - 1) / NT, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace kvqw

@@ -46,12 +46,30 @@ class kvq_layout(ctypes.Structure):
         "tables", "select_work", "total")] + [("cap_blocks", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 
+class kvqw_config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "batch", "n_kv_heads", "n_q_heads", "head_dim", "bits", "n_sink", "window", "capacity",
+        "in_dtype")]
+
+
+class kvqw_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in (
+        "layer_stride", "k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "total")] + [
+        ("capacity", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
+class kvqw_bytes(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "n_stored", "current_length", "code_bytes", "meta_bytes", "packed_int4_bytes", "bf16_bytes")]
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with `python -m quantized_kv_cache_kivi_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, F32, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     cfgp = ctypes.POINTER(kvq_config)
+    wcfgp = ctypes.POINTER(kvqw_config)
     sig = {
         "kvq_config_check": (I32, [cfgp]),
         "kvq_required_bytes": (SZ, [cfgp]),
@@ -69,6 +87,18 @@ def _load():
         "kvq_get_state": (I32, [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
         "kvq_format_tables": (I32, [cfgp, P, P, P, P, P, P, P]),
         "kvq_last_error": (ctypes.c_char_p, []),
+        "kvqw_config_check": (I32, [wcfgp]),
+        "kvqw_required_bytes": (SZ, [wcfgp]),
+        "kvqw_get_layout": (I32, [wcfgp, ctypes.POINTER(kvqw_layout)]),
+        "kvqw_workspace_bytes": (SZ, [wcfgp]),
+        "kvqw_create": (I32, [wcfgp, P, SZ, P, ctypes.POINTER(P)]),
+        "kvqw_destroy": (I32, [P]),
+        "kvqw_append": (I32, [P, I32, P, P, I32, P, SZ, P]),
+        "kvqw_evict": (I32, [P, I32]),
+        "kvqw_decode_attn": (I32, [P, I32, P, P, F32, P, SZ, P]),
+        "kvqw_dequant": (I32, [P, I32, I32, I64, I32, P, P]),
+        "kvqw_account": (I32, [P, I32, ctypes.POINTER(kvqw_bytes)]),
+        "kvqw_get_state": (I32, [P, I32, ctypes.POINTER(I64), ctypes.POINTER(I64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -190,6 +220,81 @@ class Cache:
         return P.value, lo.value
 
     # raw views of the documented storage regions (for tests)
+    def region(self, layer, name, nbytes):
+        off = layer * self.layout.layer_stride + getattr(self.layout, name)
+        return self.buf[off: off + nbytes]
+
+
+# ---- the whole-T KIVI cache (include/kvq_whole.h) ----
+
+def make_whole_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, bits=8, n_sink=0, window=0, capacity=0,
+                      in_dtype="f16"):
+    return kvqw_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, bits, n_sink, window, capacity,
+                       IN_DTYPE[in_dtype])
+
+
+def whole_config_check(cfg):
+    return lib.kvqw_config_check(ctypes.byref(cfg))
+
+
+def whole_required_bytes(cfg):
+    return lib.kvqw_required_bytes(ctypes.byref(cfg))
+
+
+def whole_workspace_bytes(cfg):
+    return lib.kvqw_workspace_bytes(ctypes.byref(cfg))
+
+
+def whole_layout(cfg):
+    lay = kvqw_layout()
+    _check(lib.kvqw_get_layout(ctypes.byref(cfg), ctypes.byref(lay)))
+    return lay
+
+
+class WholeCache:
+    """A whole-T KIVI cache bound to a torch-allocated device buffer, with its workspace."""
+
+    def __init__(self, cfg, device="cuda"):
+        self.cfg = cfg
+        self.layout = whole_layout(cfg)
+        nbytes = whole_required_bytes(cfg)
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(max(whole_workspace_bytes(cfg), 16), dtype=torch.uint8, device=device)
+        self.dev = self.buf.device.index
+        h = ctypes.c_void_p()
+        _check(lib.kvqw_create(ctypes.byref(cfg), _ptr(self.buf), nbytes, _stream(self.dev), ctypes.byref(h)))
+        self.handle = h
+
+    def __del__(self, _destroy=lib.kvqw_destroy):
+        h = getattr(self, "handle", None)
+        if h:
+            _destroy(h)
+            self.handle = None
+
+    def kvqw_append(self, layer, k, v):
+        _check(lib.kvqw_append(self.handle, layer, _ptr(k), _ptr(v), k.shape[2], _ptr(self.ws), self.ws.numel(),
+                               _stream(self.dev)))
+
+    def kvqw_evict(self, layer):
+        _check(lib.kvqw_evict(self.handle, layer))
+
+    def kvqw_decode_attn(self, layer, q, out, scale=0.0):
+        _check(lib.kvqw_decode_attn(self.handle, layer, _ptr(q), _ptr(out), scale, _ptr(self.ws), self.ws.numel(),
+                                    _stream(self.dev)))
+
+    def kvqw_dequant(self, layer, which, pos0, count, out):
+        _check(lib.kvqw_dequant(self.handle, layer, which, pos0, count, _ptr(out), _stream(self.dev)))
+
+    def kvqw_account(self, layer):
+        b = kvqw_bytes()
+        _check(lib.kvqw_account(self.handle, layer, ctypes.byref(b)))
+        return {n: getattr(b, n) for n, _ in kvqw_bytes._fields_}
+
+    def kvqw_get_state(self, layer):
+        P, lo = ctypes.c_int64(), ctypes.c_int64()
+        _check(lib.kvqw_get_state(self.handle, layer, ctypes.byref(P), ctypes.byref(lo)))
+        return P.value, lo.value
+
     def region(self, layer, name, nbytes):
         off = layer * self.layout.layer_stride + getattr(self.layout, name)
         return self.buf[off: off + nbytes]

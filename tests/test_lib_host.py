@@ -22,13 +22,14 @@ def kvq():
     return m
 
 
-def test_exports_every_declared_symbol(kvq):
-    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
-    names = sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", hdr)))
-    assert len(names) >= 15
+@pytest.mark.parametrize("header,prefix,least", [("kvq.h", "kvq_", 15), ("kvq_whole.h", "kvqw_", 12)])
+def test_exports_every_declared_symbol(kvq, header, prefix, least):
+    hdr = open(os.path.join(ROOT, "include", header)).read()
+    names = sorted(set(re.findall(r"\b(" + prefix + r"[a-z_]+)\s*\(", hdr)))
+    assert len(names) >= least
     so = ctypes.CDLL(kvq.LIB_PATH)
     for n in names:
-        assert hasattr(so, n), f"{n} declared in kvq.h but not exported"
+        assert hasattr(so, n), f"{n} declared in {header} but not exported"
 
 
 def test_config_validation(kvq):
@@ -99,3 +100,28 @@ def test_product_does_not_use_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(from|import)\s+oracle\b", text, re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_whole_config_validation_and_layout(kvq):
+    from oracle import kivi_whole as okw
+    ok = kvq.make_whole_config(12, 1, 8, 8, 32, 8, 4, 256, 0, "f32")
+    assert kvq.whole_config_check(ok) == 0
+    lay = kvq.whole_layout(ok)
+    assert lay.capacity == okw.default_capacity(4, 256)
+    S, D, cap = 8, 32, lay.capacity
+    assert lay.v_codes - lay.k_codes >= S * cap * D and lay.k_zero - lay.k_scale >= S * D * 2
+    assert lay.v_zero - lay.v_scale >= S * cap * 2 and lay.layer_stride >= lay.v_zero + S * cap * 2
+    assert kvq.whole_required_bytes(ok) == 12 * lay.layer_stride
+    assert kvq.whole_workspace_bytes(ok) > 0
+    bad = [
+        kvq.make_whole_config(1, 1, 2, 6, 64, 8, 0, 0, 64),      # GQA ratio 3
+        kvq.make_whole_config(1, 1, 2, 2, 96, 8, 0, 0, 64),      # head_dim
+        kvq.make_whole_config(1, 1, 2, 2, 64, 2, 0, 0, 64),      # bits
+        kvq.make_whole_config(1, 1, 2, 2, 64, 8, 0, 0, 0),       # no capacity, no window
+        kvq.make_whole_config(1, 1, 2, 2, 64, 8, 4, 60, 64),     # capacity - n_sink <= window
+        kvq.make_whole_config(1, 1, 2, 2, 64, 8, 64, 0, 64),     # capacity <= n_sink
+        kvq.make_whole_config(1, 1, 2, 2, 64, 8, 0, 0, 40),      # not a multiple of 32
+    ]
+    for cfg in bad:
+        assert kvq.whole_config_check(cfg) == -1 and kvq.last_error() != ""
+        assert kvq.whole_required_bytes(cfg) == 0
