@@ -213,6 +213,115 @@ def prefill_attention_figure(kw, cache, P, sinks_per_b, seed, dev, stream, max_f
                     "whose rotated queries are hi + lo pairs too)"}
 
 
+def whole_decode_bytes(wk, n_stored, esz):
+    """Algorithmic bytes of one whole-T decode-attention call: every stored row's K and V codes and its
+    V scale and zero, the K scales and zeros, q and out."""
+    S, D, r = wk["batch"] * wk["n_kv_heads"], wk["head_dim"], wk["n_q_heads"] // wk["n_kv_heads"]
+    return S * (n_stored * (2 * D + 4) + 4 * D + r * D * esz + r * D * 4)
+
+
+def whole_append_bytes(wk, n_old, n, esz):
+    """Algorithmic bytes of one whole-T append of n rows over n_old stored rows: the stored K codes read
+    and written back re-quantised (the page's O(T*D) recompute), the new K and V rows read, their codes
+    and V metadata written, the K metadata read and written."""
+    S, D = wk["batch"] * wk["n_kv_heads"], wk["head_dim"]
+    return S * (n_old * D + (n_old + n) * D + 2 * n * D * esz + n * (D + 4) + 8 * D)
+
+
+def whole_figure(dev, stream):
+    """The StreamingLLM + KIVI page's own KIVI cache (K scales over the whole stored T), two workloads:
+    the page's model shape (12 layers, 8 heads, d=32, int8, sink 4 + window 256, fp32 K/V, a 4-token
+    prompt then 500 decode steps of append + evict + attention per layer), and one layer at batch 8,
+    8 KV / 32 q heads, d=128, int8, T=4096 for the kernels' bandwidth."""
+    import torch
+    from quantized_kv_cache_kivi_amd import kvq, synth
+    res = {}
+    med = lambda v: sorted(v)[len(v) // 2]
+    # the page's model: every step is 12 x (append 1 row, evict, decode attention)
+    pk = dict(n_layers=12, batch=1, n_kv_heads=8, n_q_heads=8, head_dim=32, bits=8, n_sink=4, window=256,
+              in_dtype="f32")
+    c = kvq.WholeCache(kvq.make_whole_config(**pk))
+    seed = 0x5EED0006
+    shp = lambda n: (1, 8, n, 32)
+    k0, v0 = synth.normal(shp(4), seed, 1, dev).float(), synth.normal(shp(4), seed, 2, dev).float()
+    steps = 500
+    ks = synth.normal((steps,) + shp(1), seed, 3, dev).float()
+    vs = synth.normal((steps,) + shp(1), seed, 4, dev).float()
+    qs = synth.normal((steps, 1, 8, 32), seed, 5, dev).float()
+    out = torch.empty((1, 8, 32), dtype=torch.float32, device=dev)
+    for layer in range(12):
+        c.kvqw_append(layer, k0.contiguous(), v0.contiguous())
+        c.kvqw_evict(layer)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        for layer in range(12):
+            c.kvqw_append(layer, ks[i], vs[i])
+            c.kvqw_evict(layer)
+            c.kvqw_decode_attn(layer, qs[i], out)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    stored = c.kvqw_account(0)["n_stored"]
+    ev_a, ev_d = [HipTimer() for _ in range(24)], [HipTimer() for _ in range(24)]
+    for j in range(24):
+        ev_a[j].record(0, stream)
+        c.kvqw_append(0, ks[j], vs[j])
+        ev_a[j].record(1, stream)
+        c.kvqw_evict(0)
+        ev_d[j].record(0, stream)
+        c.kvqw_decode_attn(0, qs[j], out)
+        ev_d[j].record(1, stream)
+    torch.cuda.synchronize()
+    ta, td = med([e.ms() for e in ev_a[4:]]) * 1e3, med([e.ms() for e in ev_d[4:]]) * 1e3
+    res["page_model"] = {
+        "workload": "12 layers, batch 1, 8 heads, d=32, int8, sink 4, window 256, fp32 K/V, 4-token prompt + "
+                    f"{steps} decode steps (append 1 row + evict + decode attention per layer)",
+        "tokens_per_s": steps / el, "us_per_step": el / steps * 1e6, "stored_rows": stored,
+        "append_us": ta, "decode_attn_us": td,
+        "cache_bytes_12_layers": 12 * c.kvqw_account(0)["code_bytes"] + 12 * c.kvqw_account(0)["meta_bytes"],
+        "note": "launch-bound: 4 kernel launches per layer and step over 8 x 260 rows of 68 bytes"}
+    del c
+    # bandwidth workload
+    wk = dict(n_layers=1, batch=8, n_kv_heads=8, n_q_heads=32, head_dim=128, bits=8, n_sink=0, window=0,
+              capacity=4096 + 64, in_dtype="f16")
+    c = kvq.WholeCache(kvq.make_whole_config(**wk))
+    T = 4096
+    k = synth.normal((8, 8, T, 128), seed, 6, dev) * synth.channel_multipliers(8, 128, 6.0, seed, 7, dev)[None, :, None, :]
+    v = synth.normal((8, 8, T, 128), seed, 8, dev)
+    c.kvqw_append(0, k.half().contiguous(), v.half().contiguous())
+    del k, v
+    n_steps = 24
+    sk = [synth.normal((8, 8, 1, 128), seed, 100 + i, dev).half().contiguous() for i in range(n_steps)]
+    sv = [synth.normal((8, 8, 1, 128), seed, 200 + i, dev).half().contiguous() for i in range(n_steps)]
+    q = synth.normal((8, 32, 128), seed, 300, dev).half().contiguous()
+    out = torch.empty((8, 32, 128), dtype=torch.float32, device=dev)
+    ev_a, ev_d = [HipTimer() for _ in range(n_steps)], [HipTimer() for _ in range(n_steps)]
+    for j in range(n_steps):
+        ev_a[j].record(0, stream)
+        c.kvqw_append(0, sk[j], sv[j])
+        ev_a[j].record(1, stream)
+        ev_d[j].record(0, stream)
+        c.kvqw_decode_attn(0, q, out)
+        ev_d[j].record(1, stream)
+    torch.cuda.synchronize()
+    ta, td = med([e.ms() for e in ev_a[4:]]), med([e.ms() for e in ev_d[4:]])
+    n_mid = T + n_steps // 2
+    ba, bd = whole_append_bytes(wk, n_mid, 1, 2), whole_decode_bytes(wk, n_mid + 1, 2)
+    res["bandwidth"] = {
+        "workload": "1 layer, batch 8, 8 KV / 32 q heads, d=128, int8, fp16 K/V with 6x channel spread, T=4096 "
+                    "(+1 row per step), no eviction",
+        "decode_attn": {"us": td * 1e3, "bytes": bd, "GBps": bd / (td * 1e-3) / 1e9,
+                        "roofline": {"bound": "hbm", "achieved": bd / (td * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                                     "unit": "GB/s", "frac": bd / (td * 1e-3) / 1e9 / HBM_PEAK_GBPS}},
+        "append": {"us": ta * 1e3, "bytes": ba, "GBps": ba / (ta * 1e-3) / 1e9,
+                   "roofline": {"bound": "hbm", "achieved": ba / (ta * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                                "unit": "GB/s", "frac": ba / (ta * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                   "note": "one row appended re-quantises all 4096 stored K rows (read twice: min/max, then "
+                           "codes; algorithmic bytes count one read and one write)"},
+        "note": "median of 20 calls, HIP timing events"}
+    return res
+
+
 def algorithmic_bytes(kw, P, lo, sinks_per_b):
     """Bytes one decode-attention call must move (valid tokens only)."""
     D, H, Hq, B = kw["head_dim"], kw["n_kv_heads"], kw["n_q_heads"], kw["batch"]
@@ -488,6 +597,7 @@ def main():
         sinks_per_b = [[int(p) for p in row if p >= 0] for row in pos.tolist()]
     log(f"[bench] prefill done; sinks of b=0: {sinks_per_b[0]}")
     prefill_attn = prefill_attention_figure(kw, reps[0], T0, sinks_per_b, seed, dev, pstream)
+    kivi_whole = whole_figure(dev, pstream) if not args.pmc_run else None
 
     # per-step inputs, resident on the GPU before timing
     step_kv = [make_rows(args.config, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(total_steps)]
@@ -586,6 +696,7 @@ def main():
         "warm_cache": warm,
         "prefill": prefill,
         "prefill_attn": prefill_attn,
+        "kivi_whole": kivi_whole,
     }
     if not args.no_cpu_baseline:
         try:

@@ -70,11 +70,15 @@ __device__ __forceinline__ void ld8(const void* p, int64_t i, float* x) {
   }
 }
 
-// u = q - qMin of 8 signed codes, as fp32 (exact).
+// u = q - qMin of 8 signed codes, as fp32 (exact).  For a two's-complement byte b of q, q + 128 is
+// b ^ 0x80 (int8) and q + 8 is (b ^ 0x08) & 0x0F (int4, q in [-8, 7]): one or two bit operations per
+// word, then a byte-to-float conversion per code.
 __device__ __forceinline__ void codes8(uint2 w, int qmin, float* u) {
-  const uint32_t ww[2] = {w.x, w.y};
+  uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) u[e] = (float)((int)(int8_t)(uint8_t)(ww[e >> 2] >> (8 * (e & 3))) - qmin);
+  for (int m = 0; m < 2; ++m) ww[m] = qmin == -128 ? ww[m] ^ 0x80808080u : (ww[m] ^ 0x08080808u) & 0x0F0F0F0Fu;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) u[e] = (float)((ww[e >> 2] >> (8 * (e & 3))) & 0xFFu);
 }
 
 // Signed codes of 8 values against fp32 scale and zero: u = clamp(rint((x - z)/s), 0, L), q = u + qMin.
@@ -119,14 +123,23 @@ __global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
     mx[e] = -INFINITY;
   }
   const int64_t in0 = (int64_t)s * a.n;
-  for (int j = j0 + rl; j < j1; j += RP) {
+  const int jo = min(j1, nold);
+#pragma unroll 4
+  for (int j = j0 + rl; j < jo; j += RP) {  // stored rows
     float x[8];
-    if (j < nold) {
-      const int sl = row_slot(a.old, j);
-      codes8(*reinterpret_cast<const uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg), qmin, x);
+    const int sl = row_slot(a.old, j);
+    codes8(*reinterpret_cast<const uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg), qmin, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * so[e] + zo[e];  // two roundings (no contraction)
-    } else {
+    for (int e = 0; e < 8; ++e) {
+      x[e] = x[e] * so[e] + zo[e];  // two roundings (no contraction)
+      mn[e] = fminf(mn[e], x[e]);
+      mx[e] = fmaxf(mx[e], x[e]);
+    }
+  }
+  for (int j = j0 + rl; j < j1; j += RP) {  // new rows
+    if (j < nold) continue;
+    float x[8];
+    {
       const int i = j - nold;
       ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
       // the new V row: per-token min/max over all channels, final at append
@@ -199,13 +212,29 @@ __global__ __launch_bounds__(NT) void k_requant(AppendArgs a) {
   const int nold = a.old.nsk + a.old.nring, ntot = nold + a.n;
   const int j0 = tile * RPT, j1 = min(ntot, j0 + RPT);
   __shared__ float sns[D], snz[D], sos[D], soz[D];
-  if (tid < D) {
-    // channel min/max over every row: the per-tile extremes, reduced in tile order
+  constexpr int TG = NT / D;  // threads per channel for the tile reduction
+  __shared__ float rmn[TG][D], rmx[TG][D];
+  {
+    // channel min/max over every row: the per-tile extremes (min and max are exact, so the
+    // reduction order does not matter)
+    const int c = tid % D, tg = tid / D;
     float m0 = INFINITY, m1 = -INFINITY;
     const float* pp = a.part + (int64_t)s * a.tiles * 2 * D;
-    for (int t = 0; t < a.tiles; ++t) {
-      m0 = fminf(m0, pp[t * 2 * D + tid]);
-      m1 = fmaxf(m1, pp[t * 2 * D + D + tid]);
+#pragma unroll 4
+    for (int t = tg; t < a.tiles; t += TG) {
+      m0 = fminf(m0, pp[t * 2 * D + c]);
+      m1 = fmaxf(m1, pp[t * 2 * D + D + c]);
+    }
+    rmn[tg][c] = m0;
+    rmx[tg][c] = m1;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float m0 = rmn[0][tid], m1 = rmx[0][tid];
+#pragma unroll
+    for (int t = 1; t < TG; ++t) {
+      m0 = fminf(m0, rmn[t][tid]);
+      m1 = fmaxf(m1, rmx[t][tid]);
     }
     m0 = m0 + 0.f;
     m1 = m1 + 0.f;
@@ -229,54 +258,75 @@ __global__ __launch_bounds__(NT) void k_requant(AppendArgs a) {
     zo[e] = soz[8 * cg + e];
   }
   const int64_t in0 = (int64_t)s * a.n;
-  for (int j = j0 + rl; j < j1; j += RP) {
+  const int jo = min(j1, nold);
+#pragma unroll 4
+  for (int j = j0 + rl; j < jo; j += RP) {  // stored rows, coded again in place
     float x[8];
-    int sl;
-    if (j < nold) {
-      sl = row_slot(a.old, j);
-      codes8(*reinterpret_cast<const uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg), qmin, x);
+    int8_t* row = a.v.kc + ((int64_t)s * sh.cap + row_slot(a.old, j)) * D + 8 * cg;
+    codes8(*reinterpret_cast<const uint2*>(row), qmin, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = x[e] * so[e] + zo[e];
-    } else {
-      const int i = j - nold;
-      sl = new_slot(a, i);
-      ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
-    }
-    *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg) = quant8(x, ns, nz, L, qmin);
+    for (int e = 0; e < 8; ++e) x[e] = x[e] * so[e] + zo[e];
+    *reinterpret_cast<uint2*>(row) = quant8(x, ns, nz, L, qmin);
+  }
+  for (int j = j0 + rl; j < j1; j += RP) {  // new rows
+    if (j < nold) continue;
+    float x[8];
+    const int i = j - nold;
+    ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
+    *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + new_slot(a, i)) * D + 8 * cg) =
+        quant8(x, ns, nz, L, qmin);
   }
 }
 
+// u = q - qMin of N codes held in N/4 words (see codes8).
+template <int N>
+__device__ __forceinline__ void codes_n(const uint32_t* w, int qmin, float* u) {
+#pragma unroll
+  for (int m = 0; m < N / 4; ++m) {
+    const uint32_t x = qmin == -128 ? w[m] ^ 0x80808080u : (w[m] ^ 0x08080808u) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[4 * m + e] = (float)((x >> (8 * e)) & 0xFFu);
+  }
+}
+
+// CPL = 8 channels per lane (one 8-byte code load per row and operand); 16 channels per lane
+// (16-byte loads, fewer shuffles) measured slower on the batch-8, T=4096, GQA-4 workload.
 template <int D, int R, bool F32>
 __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
-  constexpr int CG = D / 8, TPI = 64 / CG, NW = NT / 64;
+  constexpr int CPL = 8;
+  constexpr int CG = D / CPL, TPI = 64 / CG, NW = NT / 64, NWD = CPL / 4;
   const Shape sh = a.sh;
   const int s = blockIdx.y, split = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int b = s / sh.H, g = s % sh.H;
   const int cg = lane % CG, tau = lane / CG;
   const int qmin = sh.bits == 8 ? -128 : -8;
-  __shared__ float sq[R][D], skap[R];
+  __shared__ float sq[R][D], sqz[R][D], skap[R];
   __shared__ float smw[NW][R], slw[NW][R];
   __shared__ float sacc[NW][R][D];
-  auto qval = [&](int h, int c) {
-    const int64_t i = ((int64_t)b * sh.Hq + g * R + h) * D + c;
-    return F32 ? static_cast<const float*>(a.q)[i] : f16_val(static_cast<const uint16_t*>(a.q)[i]);
-  };
   for (int i = tid; i < R * D; i += NT) {
     const int h = i / D, c = i % D;
-    sq[h][c] = qval(h, c) * f16_val(a.v.ks[(int64_t)s * D + c]);
-  }
-  if (tid < R) {
-    float k = 0.f;
-    for (int c = 0; c < D; ++c) k = k + qval(tid, c) * f16_val(a.v.kz[(int64_t)s * D + c]);
-    skap[tid] = k;
+    const int64_t qi = ((int64_t)b * sh.Hq + g * R + h) * D + c;
+    const float qv = F32 ? static_cast<const float*>(a.q)[qi] : f16_val(static_cast<const uint16_t*>(a.q)[qi]);
+    sq[h][c] = qv * f16_val(a.v.ks[(int64_t)s * D + c]);
+    sqz[h][c] = qv * f16_val(a.v.kz[(int64_t)s * D + c]);
   }
   __syncthreads();
-  float qf[R][8], kap[R], m[R], l[R], acc[R][8];
+  if (wv == 0) {  // kappa_h = sum_c q_hc z_c: two channels per lane, then a wave sum
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float k = (lane < D ? sqz[h][lane] : 0.f) + (lane + 64 < D ? sqz[h][lane + 64] : 0.f);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) k = k + __shfl_xor(k, o);
+      if (lane == 0) skap[h] = k;
+    }
+  }
+  __syncthreads();
+  float qf[R][CPL], kap[R], m[R], l[R], acc[R][CPL];
 #pragma unroll
   for (int h = 0; h < R; ++h) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      qf[h][e] = sq[h][8 * cg + e];
+    for (int e = 0; e < CPL; ++e) {
+      qf[h][e] = sq[h][CPL * cg + e];
       acc[h][e] = 0.f;
     }
     kap[h] = skap[h];
@@ -286,30 +336,63 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
   const float al = a.scale * LOG2E;
   const int nst = a.rows.nsk + a.rows.nring;
   const int j0 = split * a.rows_per_split, j1 = min(nst, j0 + a.rows_per_split);
-  for (int j = j0 + wv * TPI + tau; j < j1; j += NW * TPI) {
-    const int64_t ro = (int64_t)s * sh.cap + row_slot(a.rows, j);
-    float uk[8], uv[8];
-    codes8(*reinterpret_cast<const uint2*>(a.v.kc + ro * D + 8 * cg), qmin, uk);
-    codes8(*reinterpret_cast<const uint2*>(a.v.vc + ro * D + 8 * cg), qmin, uv);
-    const float vsf = f16_val(a.v.vs[ro]), vzf = f16_val(a.v.vz[ro]);
-    float xv[8];
+  // NB rows per lane in flight: every row's codes are requested before the first is scored
+  constexpr int STEP = NW * TPI, NB = 2;
+  auto ld_codes = [&](const int8_t* p, uint32_t* w) {
+    if constexpr (NWD == 4) {
+      const uint4 x = *reinterpret_cast<const uint4*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+      w[2] = x.z;
+      w[3] = x.w;
+    } else {
+      const uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x;
+      w[1] = x.y;
+    }
+  };
+  for (int j = j0 + wv * TPI + tau; j < j1; j += NB * STEP) {
+    uint32_t kw[NB][NWD], vw[NB][NWD];
+    uint16_t vsb[NB], vzb[NB];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xv[e] = uv[e] * vsf + vzf;
+    for (int r = 0; r < NB; ++r) {
+      const int jr = j + r * STEP < j1 ? j + r * STEP : j;  // past the end: reload row j, unused
+      const int64_t ro = (int64_t)s * sh.cap + row_slot(a.rows, jr);
+      ld_codes(a.v.kc + ro * D + CPL * cg, kw[r]);
+      ld_codes(a.v.vc + ro * D + CPL * cg, vw[r]);
+      vsb[r] = a.v.vs[ro];
+      vzb[r] = a.v.vz[ro];
+    }
 #pragma unroll
-    for (int h = 0; h < R; ++h) {
-      float p = 0.f;
+    for (int r = 0; r < NB; ++r) {
+      if (j + r * STEP >= j1) break;  // uniform over the row's lanes
+      float uk[CPL], uv[CPL];
+      codes_n<CPL>(kw[r], qmin, uk);
+      codes_n<CPL>(vw[r], qmin, uv);
+      const float vsf = f16_val(vsb[r]), vzf = f16_val(vzb[r]);
+      float xv[CPL];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) p = p + qf[h][e] * uk[e];
+      for (int e = 0; e < CPL; ++e) xv[e] = __builtin_fmaf(uv[e], vsf, vzf);
 #pragma unroll
-      for (int o = CG / 2; o >= 1; o >>= 1) p = p + __shfl_xor(p, o);
-      const float sc = (p + kap[h]) * al;
-      const float mn = fmaxf(m[h], sc);
-      const float corr = __builtin_amdgcn_exp2f(m[h] - mn);  // 0 while m is -inf
-      const float pw = __builtin_amdgcn_exp2f(sc - mn);
-      l[h] = l[h] * corr + pw;
+      for (int h = 0; h < R; ++h) {
+        float p = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = acc[h][e] * corr + pw * xv[e];
-      m[h] = mn;
+        for (int e = 0; e < CPL; ++e) p = __builtin_fmaf(qf[h][e], uk[e], p);
+#pragma unroll
+        for (int o = CG / 2; o >= 1; o >>= 1) p = p + __shfl_xor(p, o);
+        const float sc = (p + kap[h]) * al;
+        if (sc > m[h]) {  // uniform over the row's lanes
+          const float corr = __builtin_amdgcn_exp2f(m[h] - sc);  // 0 while m is -inf
+          l[h] *= corr;
+#pragma unroll
+          for (int e = 0; e < CPL; ++e) acc[h][e] *= corr;
+          m[h] = sc;
+        }
+        const float pw = __builtin_amdgcn_exp2f(sc - m[h]);
+        l[h] += pw;
+#pragma unroll
+        for (int e = 0; e < CPL; ++e) acc[h][e] = __builtin_fmaf(pw, xv[e], acc[h][e]);
+      }
     }
   }
   // row groups of the wave (lanes cg + CG*tau), then the waves through LDS
@@ -323,7 +406,7 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int o = CG; o < 64; o <<= 1) lw = lw + __shfl_xor(lw, o);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < CPL; ++e) {
       float aw = acc[h][e] * w;
 #pragma unroll
       for (int o = CG; o < 64; o <<= 1) aw = aw + __shfl_xor(aw, o);
@@ -336,7 +419,7 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
 #pragma unroll
     for (int h = 0; h < R; ++h) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sacc[wv][h][8 * cg + e] = acc[h][e];
+      for (int e = 0; e < CPL; ++e) sacc[wv][h][CPL * cg + e] = acc[h][e];
       if (cg == 0) {
         smw[wv][h] = m[h];
         slw[wv][h] = l[h];
@@ -373,14 +456,22 @@ __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
   const int c = threadIdx.x;
   const int64_t stride = (int64_t)R * (D + 2);
   const float* base = a.part + ((int64_t)s * a.splits * R + h) * (D + 2);
+  __shared__ float sm[MAX_SPLITS], sw[MAX_SPLITS], sl[MAX_SPLITS];
+  for (int sp = c; sp < a.splits; sp += D) {  // every split's (m, l) at once, then the weights
+    sm[sp] = base[sp * stride + D];
+    sl[sp] = base[sp * stride + D + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[sp * stride + D]);
+  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, sm[sp]);
+  __syncthreads();
+  for (int sp = c; sp < a.splits; sp += D) sw[sp] = sm[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[sp] - M);
+  __syncthreads();
   float av = 0.f, lv = 0.f;
+#pragma unroll 8
   for (int sp = 0; sp < a.splits; ++sp) {
-    const float ms = base[sp * stride + D];
-    const float wt = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-    av = av + base[sp * stride + c] * wt;
-    lv = lv + base[sp * stride + D + 1] * wt;
+    av = av + base[sp * stride + c] * sw[sp];
+    lv = lv + sl[sp] * sw[sp];
   }
   a.out[(int64_t)bj * D + c] = lv > 0.f ? av / lv : 0.f;
 }
