@@ -24,4 +24,4 @@ against something other than itself (a closed form, a textbook value, a value
 printed on a page, brute force, or an invariant).
 """
 
-from . import numerics, layout, kivi, q2k, turboquant, sinks, cache, attention, accounting, kivi_whole  # noqa: F401
+from . import numerics, layout, kivi, q2k, turboquant, sinks, cache, attention, accounting, kivi_whole, rope  # noqa: F401

@@ -23,7 +23,7 @@ rotated-domain identity q . R^T k = (R q) . k in tests/test_oracle_attention.py.
 
 import numpy as np
 
-from . import kivi, q2k, turboquant
+from . import kivi, q2k, rope, turboquant
 from .cache import G, quantize_stream
 from .numerics import from_f16_bits, to_f16_bits
 
@@ -111,9 +111,15 @@ def decode_attention(model, layer, q, scale=None, batches=None, heads=None):
         for hi, j in enumerate(heads):
             g = j // r
             if g not in cache:
-                cache[g] = (stream_values(model, layer, b, g, "k", pos), stream_values(model, layer, b, g, "v", pos))
+                kk = stream_values(model, layer, b, g, "k", pos)
+                if cfg.rope:  # keys turned by their index in the compressed cache
+                    kk = rope.rotate(kk, np.arange(len(pos)), cfg.rope_base)
+                cache[g] = (kk, stream_values(model, layer, b, g, "v", pos))
             kh, vh = cache[g]
-            s = alpha * (kh @ q64[b, j])
+            qv = q64[b, j]
+            if cfg.rope:  # the query sits at the last index (its own row is the last valid one)
+                qv = rope.rotate(qv, rope.index_of(pos, model.P[layer] - 1), cfg.rope_base)
+            s = alpha * (kh @ qv)
             s = s - s.max()
             w = np.exp(s)
             out[bi, hi] = (w @ vh) / w.sum()
@@ -146,14 +152,19 @@ def prefill_attention(model, layer, q, scale=None, batches=None, heads=None, que
         for hi, j in enumerate(heads):
             g = j // r
             if g not in cache:
-                cache[g] = (stream_values(model, layer, b, g, "k", list(pos)),
-                            stream_values(model, layer, b, g, "v", list(pos)))
+                kk = stream_values(model, layer, b, g, "k", list(pos))
+                if cfg.rope:
+                    kk = rope.rotate(kk, np.arange(len(pos)), cfg.rope_base)
+                cache[g] = (kk, stream_values(model, layer, b, g, "v", list(pos)))
             kh, vh = cache[g]
             for qi, i in enumerate(queries):
                 sel = pos <= P - n + i
                 if not sel.any():
                     continue
-                out[bi, hi, qi] = softmax_attention(q64[b, j, i], kh[sel], vh[sel], alpha)
+                qv = q64[b, j, i]
+                if cfg.rope:  # the query's index: valid positions before its own
+                    qv = rope.rotate(qv, rope.index_of(pos, P - n + i), cfg.rope_base)
+                out[bi, hi, qi] = softmax_attention(qv, kh[sel], vh[sel], alpha)
     return out
 
 

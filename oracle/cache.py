@@ -59,6 +59,8 @@ class Config:
     capacity: int = 0          # slots per stream (multiple of 32)
     in_dtype: str = "f16"      # 'f16' | 'f32'
     seed: int = 0
+    rope: bool = False         # K and q handed over before RoPE, rotated on read (oracle/rope.py)
+    rope_base: float = 10000.0
 
     @property
     def cap_blocks(self):
