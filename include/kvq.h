@@ -102,6 +102,12 @@ typedef struct {
   int32_t capacity;   /* block slots * 32 per stream; 0 = library default (needs window > 0) */
   int32_t in_dtype;   /* KVQ_IN_F16 or KVQ_IN_F32 for K, V and q */
   uint64_t seed;      /* TQ sign-diagonal seed ([TQ] "Step 1") */
+  int32_t rope;       /* 1: K and q are handed over before RoPE and attention turns them on read by their
+                         index in the compressed cache ([SK] "RoPE caveat", "Caveats": StreamingLLM's
+                         re-positioning); 0: off.  Not with TQ. */
+  float rope_base;    /* RoPE base (<= 0: 10000); channel c < head_dim/2 pairs with c + head_dim/2 and turns
+                         by idx * base^(-2c/head_dim), idx = the number of valid positions before the row
+                         (a query: before its own position) */
 } kvq_config;
 
 typedef struct {

@@ -284,7 +284,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
     e = hipSuccess;
   }
   if (e != hipSuccess) return e;
-  if (a.sh.fmt == KVQ_FMT_TQ)
+  if (a.sh.fmt == KVQ_FMT_TQ || a.sh.rope)
     hipLaunchKernelGGL(k_decode_merge, dim3(a.sh.B * a.sh.Hkv), dim3(DNT), 0, st, a);
   else
     hipLaunchKernelGGL(k_merge_heads, dim3(a.sh.B * a.sh.Hkv, a.sh.Hq / a.sh.Hkv), dim3(MNT), 0, st, a);

@@ -25,6 +25,7 @@ struct Smem {
   int sinks[MAX_SINK];      // committed sink positions (< P) of this batch element
   int sink_slot[MAX_SINK];  // their sink-pool slots
   int nsinks;
+  int rk[G];                // RoPE on read: index in the compressed cache of each row of the chunk
   union {
     alignas(16) uint8_t rec[MAX_REC];                       // staged block record (bulk)
     struct { uint16_t k[G][MAX_D], v[G][MAX_D]; } rows;     // fp16 rows of the current chunk
@@ -81,8 +82,8 @@ __device__ __forceinline__ float v_val(const Shape& sh, const uint8_t* rec, cons
 }
 
 
-// Partial of this workgroup: bulk blocks of split `sigma`, or (sigma == splits, TurboQuant only)
-// the fp16 rows.
+// Partial of this workgroup: bulk blocks of split `sigma`, or (sigma == splits, TurboQuant and
+// RoPE-on-read caches) the fp16 rows.
 __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
 
   const Shape sh = a.sh;
@@ -103,6 +104,25 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
     S.l[tid] = 0.f;
   }
   __syncthreads();
+  if (sh.rope) {  // the query turns by its own index: the last valid position, P - 1
+    const int qi = cache_index(S.sinks, S.nsinks, a.lo, a.P - 1);
+    const int h = D / 2;
+    float qa[MAX_GQA * MAX_D / 2 / DNT + 1], qb[MAX_GQA * MAX_D / 2 / DNT + 1];
+    int n = 0;
+    for (int idx = tid; idx < r * h; idx += DNT, ++n) {
+      const int j = idx / h, c = idx % h;
+      qa[n] = rope_val(S.q[j][c], S.q[j][c + h], c, D, qi, lv.tables->rope_inv);
+      qb[n] = rope_val(S.q[j][c + h], S.q[j][c], c + h, D, qi, lv.tables->rope_inv);
+    }
+    __syncthreads();
+    n = 0;
+    for (int idx = tid; idx < r * h; idx += DNT, ++n) {
+      const int j = idx / h, c = idx % h;
+      S.q[j][c] = qa[n];
+      S.q[j][c + h] = qb[n];
+    }
+    __syncthreads();
+  }
   if (tq && !fp16_split) {  // rotate the query: q~ = c_d * FWHT(sigma * q)
     const float cd = (float)(1.0 / __builtin_sqrt((double)D));
     for (int j = tid >> 6; j < r; j += DNT / 64) {
@@ -164,6 +184,16 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
       for (int64_t o = tid * 16; o < lv.rec; o += DNT * 16)
         *reinterpret_cast<uint4*>(S.u.rec + o) = *reinterpret_cast<const uint4*>(src + o);
     }
+    if (sh.rope && tid < G) {  // index in the compressed cache of each row of the chunk
+      int64_t p;
+      if (fp16_split) {
+        const int64_t i = (int64_t)ch * G + tid;
+        p = i < a.P - fp_lo ? fp_lo + i : (i < n_fp ? S.sinks[(int)(i - (a.P - fp_lo))] : 0);
+      } else {
+        p = blk * G + tid;
+      }
+      S.rk[tid] = cache_index(S.sinks, S.nsinks, a.lo, p);
+    }
     __syncthreads();
 
     // scores
@@ -172,7 +202,12 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
       for (int j = 0; j < MAX_GQA; ++j) part[j] = 0.f;
       for (int cc = 0; cc < cps; ++cc) {
         const int c = sl * cps + cc;
-        const float kv = fp16_split ? f16_val(S.u.rows.k[st][c]) : k_val(sh, S.u.rec, lv, st, c);
+        float kv = fp16_split ? f16_val(S.u.rows.k[st][c]) : k_val(sh, S.u.rec, lv, st, c);
+        if (sh.rope) {  // the key turns by its row's index in the compressed cache
+          const int pc = c < D / 2 ? c + D / 2 : c - D / 2;
+          const float kp = fp16_split ? f16_val(S.u.rows.k[st][pc]) : k_val(sh, S.u.rec, lv, st, pc);
+          kv = rope_val(kv, kp, c, D, S.rk[st], lv.tables->rope_inv);
+        }
         for (int j = 0; j < r; ++j) part[j] = fmaf(S.q[j][c], kv, part[j]);
       }
       for (int j = 0; j < r; ++j) {

@@ -50,6 +50,24 @@ __device__ __forceinline__ int v_meta_idx(int t, int g, int ng) { return (t >> 1
 // Token of element e of V token group kg.
 __device__ __forceinline__ int v_tok(int kg, int e) { return 16 * (e >> 2) + 4 * kg + (e & 3); }
 
+// RoPE on read ("StreamingLLM + KIVI", "RoPE caveat"): the index of position p in the compressed
+// cache, i.e. the number of valid positions (committed sinks, [lo, P)) before p.
+__device__ __forceinline__ int cache_index(const int* sinks, int nsinks, int64_t lo, int64_t p) {
+  const int64_t lim = p < lo ? p : lo;
+  int n = 0;
+  for (int q = 0; q < nsinks; ++q) n += sinks[q] < lim ? 1 : 0;
+  return n + (int)(p > lo ? p - lo : 0);
+}
+
+// Rotate-half RoPE of channel c given its partner channel (c +- D/2): x' = x cos - y sin for
+// c < D/2, x' = x cos + y sin above, with the angle fp32(idx) * theta_{c mod D/2}.
+__device__ __forceinline__ float rope_val(float x, float partner, int c, int D, int idx, const float* inv) {
+  const int h = D >> 1, f = c < h ? c : c - h;
+  float sn, cs;
+  sincosf((float)idx * inv[f], &sn, &cs);
+  return c < h ? x * cs - partner * sn : x * cs + partner * sn;
+}
+
 // Workgroup barrier that orders LDS only: outstanding global loads stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");

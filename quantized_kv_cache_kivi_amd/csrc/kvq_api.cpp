@@ -101,6 +101,8 @@ kvq_status check(const kvq_config* c) {
   if (c->sink_mode == KVQ_SINK_NONE && c->n_sink != 0) return fail(KVQ_EINVAL, "n_sink > 0 needs a sink mode");
   if (c->window < 0 || c->residual < 0) return fail(KVQ_EINVAL, "window and residual must be >= 0");
   if (c->in_dtype != KVQ_IN_F16 && c->in_dtype != KVQ_IN_F32) return fail(KVQ_EINVAL, "in_dtype must be 0 or 1");
+  if (c->rope != 0 && c->rope != 1) return fail(KVQ_EINVAL, "rope must be 0 or 1");
+  if (c->rope && c->format == KVQ_FMT_TQ) return fail(KVQ_EINVAL, "rope on read is not available with TQ");
   if (c->capacity < 0 || c->capacity % G != 0) return fail(KVQ_EINVAL, "capacity must be a multiple of 32");
   const int32_t cap = effective_capacity(*c);
   if (cap < G) return fail(KVQ_EINVAL, "capacity must be given (>= 32) when window = 0");
@@ -154,7 +156,7 @@ kvq_layout make_layout(const kvq_config& c) {
 // Shapes the MFMA decode path covers (the generic kernel takes the rest).
 bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
-  return c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && (r == 1 || r == 2 || r == 4 || r == 8) &&
+  return c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope && (r == 1 || r == 2 || r == 4 || r == 8) &&
          (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits) ||
           (c.format == KVQ_FMT_TQ && c.k_bits == 4 && c.v_bits == 2));
 }
@@ -215,7 +217,7 @@ int fp16_parts(const kvq_config& c, int64_t rows) {
     const int per = fast_fp16_rows_per_group();
     return (int)((rows + per - 1) / per);
   }
-  return c.format == KVQ_FMT_TQ ? 1 : 0;
+  return c.format == KVQ_FMT_TQ || c.rope ? 1 : 0;
 }
 
 }  // namespace
@@ -246,6 +248,7 @@ Shape shape_of(const kvq_config& c) {
   s.W = c.window;
   s.R = c.residual;
   s.in_f32 = c.in_dtype == KVQ_IN_F32;
+  s.rope = c.rope;
   return s;
 }
 

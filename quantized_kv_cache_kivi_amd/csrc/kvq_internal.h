@@ -25,6 +25,7 @@ struct Tables {
   float v_cen[16];      // TQ V centroids
   float q2k_thr[4];     // Gaussian 4-level Lloyd-Max thresholds (3 used)
   float q2k_lvl[4];     // Gaussian 4-level Lloyd-Max levels
+  float rope_inv[MAX_D / 2];  // RoPE theta_c = base^(-2c/D), rounded to fp32 (rope mode)
 };
 
 // Everything a kernel needs to address one layer of the cache.
@@ -44,7 +45,7 @@ struct LayerView {
 };
 
 struct Shape {
-  int B, Hkv, Hq, D, fmt, kb, vb, sink_mode, n_sink, W, R, in_f32;
+  int B, Hkv, Hq, D, fmt, kb, vb, sink_mode, n_sink, W, R, in_f32, rope;
 };
 
 struct AppendArgs {
@@ -110,7 +111,7 @@ int select_groups(int n);  // workgroups per batch element for an n-row selectio
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
-int prefill_queries_per_tile(int r, int fmt);  // queries of one prefill-attention workgroup
+int prefill_queries_per_tile(int r, int fmt, int rope);  // queries of one prefill-attention workgroup
 
 // Workgroups of the MFMA decode kernel for this shape that the current device holds at once
 // (compute units x resident workgroups per unit); 0 if the shape has no MFMA kernel.

@@ -53,13 +53,16 @@ struct PfSmem {
   float kcen[16], vcen[16];  // TurboQuant centroids (rotated domain)
 };
 
-template <int FMT, int KB, int VB, int D>
+template <int FMT, int KB, int VB, int D, bool RP>
 __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   // TurboQuant works in the rotated domain ("TurboQuant KV Cache Compression — Spec", "Optimization:
   // Fused dequant-dot"): queries rotated once (fp16 hi + lo, a third score product), bulk rows are
   // norm times centroid, fp16 window and sink rows are rotated while staged, outputs rotated back
+  // RoPE on read ("StreamingLLM + KIVI", "RoPE caveat"): queries and staged keys turn by their
+  // index in the compressed cache; the turned queries are fp16 hi + lo pairs like TurboQuant's
   constexpr bool TQ = FMT == KVQ_FMT_TQ;
-  constexpr int PT = TQ ? 1 : ::kvq::PT;  // column tiles per wave
+  constexpr bool SQ = TQ || RP;            // queries split into fp16 hi + lo (third score product)
+  constexpr int PT = SQ ? 1 : ::kvq::PT;  // column tiles per wave
   constexpr int NST = D / 32, NMU = D / 16, NG = D / 32;
   constexpr int VPW = 32 / VB, WPC = D * VB / 64;
   const Shape sh = a.sh;
@@ -76,8 +79,23 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   const int64_t qmax = pbase + qlast;
   __shared__ PfSmem<D> S;
 
+  if (tid < 64) {  // committed sinks already appended, with their pool slots
+    const int ns = sh.n_sink;
+    const int cnt = ns > 0 ? lv.sink_count[b] : 0;
+    const int praw = lane < ns ? lv.sink_pos[b * ns + lane] : -1;
+    const int p = lane < min(cnt, ns) ? praw : -1;
+    const bool ok = p >= 0 && p < a.P;
+    const uint64_t m = __ballot(ok);
+    const int idx = __popcll(m & ((1ull << lane) - 1ull));
+    if (ok) {
+      S.spos[idx] = p;
+      S.sslot[idx] = lane;
+    }
+    if (lane == 0) S.nsink = __popcll(m);
+  }
+  __syncthreads();
   // ---- queries of this wave's columns as the B operand (K-dimension slots 8*kg .. of chunk st) ----
-  u4 bq[PT][NST], bql[TQ ? PT : 1][TQ ? NST : 1];
+  u4 bq[PT][NST], bql[SQ ? PT : 1][SQ ? NST : 1];
   int qpos[PT];  // position of the lane's column query (-1: no query)
   int qidx[PT], head[PT];
   const float cd = (float)(1.0 / __builtin_sqrt((double)D));
@@ -102,7 +120,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
     qidx[tt] = qq;
     head[tt] = hd;
     qpos[tt] = ok ? (int)(pbase + qq) : -1;
-    if constexpr (!TQ) {
+    if constexpr (!SQ) {
       const int64_t qrow = (((int64_t)b * sh.Hq + hd) * a.n + qq) * D;
 #pragma unroll
       for (int st = 0; st < NST; ++st) {
@@ -121,13 +139,26 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         if (cok && 2 * lane < D) {
           const uint32_t w =
               reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + (((int64_t)b * sh.Hq + ch) * a.n + cq) * D)[lane];
-          y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu)) * sg0;
-          y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16)) * sg1;
+          y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+          y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
         }
-        wave_fwht(y0, y1, D, lane);
+        if constexpr (TQ) {
+          y0 *= sg0;
+          y1 *= sg1;
+          wave_fwht(y0, y1, D, lane);
+          y0 *= cd;
+          y1 *= cd;
+        } else {  // RoPE: channel 2l pairs with 2l + D/2, held by lane l ^ (D/4)
+          const float p0 = __shfl_xor(y0, D / 4), p1 = __shfl_xor(y1, D / 4);
+          const int qi = cache_index(S.spos, S.nsink, a.lo, pbase + cq);
+          const float r0 = rope_val(y0, p0, 2 * lane, D, qi, lv.tables->rope_inv);
+          const float r1 = rope_val(y1, p1, 2 * lane + 1, D, qi, lv.tables->rope_inv);
+          y0 = r0;
+          y1 = r1;
+        }
         if (2 * lane < D) {
-          qs[col * D + 2 * lane] = y0 * cd;
-          qs[col * D + 2 * lane + 1] = y1 * cd;
+          qs[col * D + 2 * lane] = y0;
+          qs[col * D + 2 * lane + 1] = y1;
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -146,21 +177,6 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       }
     }
   }
-  if (tid < 64) {  // committed sinks already appended, with their pool slots
-    const int ns = sh.n_sink;
-    const int cnt = ns > 0 ? lv.sink_count[b] : 0;
-    const int praw = lane < ns ? lv.sink_pos[b * ns + lane] : -1;
-    const int p = lane < min(cnt, ns) ? praw : -1;
-    const bool ok = p >= 0 && p < a.P;
-    const uint64_t m = __ballot(ok);
-    const int idx = __popcll(m & ((1ull << lane) - 1ull));
-    if (ok) {
-      S.spos[idx] = p;
-      S.sslot[idx] = lane;
-    }
-    if (lane == 0) S.nsink = __popcll(m);
-  }
-  __syncthreads();
   const int nsink = S.nsink;
   auto is_sink = [&](int64_t p) {
     bool r = false;
@@ -383,6 +399,25 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       }
     }
     __syncthreads();
+    if constexpr (RP) {  // the staged keys turn by their rows' indices in the compressed cache
+      constexpr int H = D / 2;
+      for (int idx = tid; idx < G * H; idx += PNT) {
+        const int t = idx / H, c = idx % H;
+        const int p = S.pos[t];
+        if (p < 0) continue;
+        const int ri = cache_index(S.spos, nsink, a.lo, p);
+        const float x0 = (float)S.khi[t][c] + (float)S.klo[t][c];
+        const float x1 = (float)S.khi[t][c + H] + (float)S.klo[t][c + H];
+        const float y0 = rope_val(x0, x1, c, D, ri, lv.tables->rope_inv);
+        const float y1 = rope_val(x1, x0, c + H, D, ri, lv.tables->rope_inv);
+        const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
+        S.khi[t][c] = h0;
+        S.klo[t][c] = (_Float16)(y0 - (float)h0);
+        S.khi[t][c + H] = h1;
+        S.klo[t][c + H] = (_Float16)(y1 - (float)h1);
+      }
+      __syncthreads();
+    }
 
     // ---- the wave's tiles against the row block: every LDS operand read feeds all tiles ----
     f4 c[PT][2];
@@ -398,7 +433,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         for (int tt = 0; tt < PT; ++tt) {
           c[tt][tau] = mfma(ah, bq[tt][st], c[tt][tau]);
           c[tt][tau] = mfma(alo, bq[tt][st], c[tt][tau]);
-          if constexpr (TQ) c[tt][tau] = mfma(ah, bql[tt][st], c[tt][tau]);
+          if constexpr (SQ) c[tt][tau] = mfma(ah, bql[tt][st], c[tt][tau]);
         }
       }
     // lane (column i16, group kg) holds rows 16*tau + 4*kg + e
@@ -491,15 +526,20 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   }
 }
 
-template <int FMT, int KB, int VB>
-hipError_t launch_d(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+template <int FMT, int KB, int VB, bool RP>
+hipError_t launch_dr(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   switch (a.sh.D) {
-    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32>), grid, dim3(PNT), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64>), grid, dim3(PNT), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128>), grid, dim3(PNT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, RP>), grid, dim3(PNT), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, RP>), grid, dim3(PNT), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, RP>), grid, dim3(PNT), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+template <int FMT, int KB, int VB>
+hipError_t launch_d(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (FMT == KVQ_FMT_TQ) return launch_dr<FMT, KB, VB, false>(a, grid, st);  // no RoPE with TQ
+  else return a.sh.rope ? launch_dr<FMT, KB, VB, true>(a, grid, st) : launch_dr<FMT, KB, VB, false>(a, grid, st);
 }
 template <int KB>
 hipError_t launch_kivi(const PrefillArgs& a, dim3 grid, hipStream_t st) {
@@ -513,11 +553,13 @@ hipError_t launch_kivi(const PrefillArgs& a, dim3 grid, hipStream_t st) {
 
 }  // namespace
 
-int prefill_queries_per_tile(int r, int fmt) { return PNW * (fmt == KVQ_FMT_TQ ? 1 : PT) * (16 / r); }
+int prefill_queries_per_tile(int r, int fmt, int rope) {
+  return PNW * (fmt == KVQ_FMT_TQ || rope ? 1 : PT) * (16 / r);
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
-  const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv, sh.fmt);
+  const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv, sh.fmt, sh.rope);
   const dim3 grid((a.n + QT - 1) / QT, sh.B * sh.Hkv);
   if (sh.fmt == KVQ_FMT_Q2K) return launch_d<KVQ_FMT_Q2K, 2, 4>(a, grid, st);
   if (sh.fmt == KVQ_FMT_TQ) {

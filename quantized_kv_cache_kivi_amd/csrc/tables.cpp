@@ -148,6 +148,8 @@ void make_tables(const kvq_config& cfg, Tables* t) {
     beta_lloyd_max(cfg.head_dim, cfg.v_bits, t->v_bnd, t->v_cen);
   }
   gaussian_lloyd_max4(t->q2k_thr, t->q2k_lvl);
+  const double base = cfg.rope_base > 0.f ? (double)cfg.rope_base : 10000.0;
+  for (int c = 0; c < cfg.head_dim / 2; ++c) t->rope_inv[c] = (float)std::pow(base, -2.0 * c / cfg.head_dim);
 }
 
 }  // namespace kvq

@@ -45,6 +45,7 @@ def test_config_validation(kvq):
         kvq.make_config(1, 2, 2, 8, 128, capacity=48),                       # not a multiple of 32
         kvq.make_config(1, 2, 2, 8, 128, window=256, capacity=256),          # no spare block
         kvq.make_config(1, 2, 2, 8, 128, "kivi", 2, 2, "topk", 17, capacity=64),
+        kvq.make_config(1, 2, 2, 8, 128, "tq", 4, 2, capacity=64, rope=True),   # RoPE on read with TQ
     ]
     for cfg in bad:
         assert kvq.config_check(cfg) == -1
