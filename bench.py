@@ -322,6 +322,47 @@ def whole_figure(dev, stream):
     return res
 
 
+def rope_figure(cfgno, kw, pre_k, pre_v, sinks_per_b, seed, dev, stream):
+    """The same workload with RoPE on read (keys and queries turned by their index in the compressed
+    cache): one replica, its prefill, then decode attention (generic split kernel) and prefill
+    attention of the last 4096 queries, medians of HIP timing events."""
+    import torch
+    from quantized_kv_cache_kivi_amd import kvq, synth
+    if pre_k is None or kw.get("fmt") == "tq":
+        return None
+    rk = dict(kw, rope=True)
+    c = kvq.Cache(kvq.make_config(**rk))
+    T0 = pre_k.shape[2]
+    for s0 in range(0, T0, 4096):
+        k = pre_k[:, :, s0:s0 + 4096].contiguous()
+        v = pre_v[:, :, s0:s0 + 4096].contiguous()
+        c.kvq_select_sinks(0, k)
+        c.kvq_append(0, k, v)
+        c.kvq_evict(0)
+    dt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
+    q = synth.normal((kw["batch"], kw["n_q_heads"], kw["head_dim"]), seed, 61_000, dev).to(dt).contiguous()
+    out = torch.empty((kw["batch"], kw["n_q_heads"], kw["head_dim"]), dtype=torch.float32, device=dev)
+    evs = [HipTimer() for _ in range(20)]
+    for e in evs:
+        e.record(0, stream)
+        c.kvq_decode_attn(0, q, out)
+        e.record(1, stream)
+    torch.cuda.synchronize()
+    t = sorted(e.ms() for e in evs[4:])[8]
+    P, lo = c.kvq_get_state(0)
+    nb, _ = algorithmic_bytes(kw, P, lo, sinks_per_b)
+    res = {"decode_attn": {"us": t * 1e3, "bytes": nb, "GBps": nb / (t * 1e-3) / 1e9,
+                           "roofline": {"bound": "hbm", "achieved": nb / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
+                                        "unit": "GB/s", "frac": nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+                           "note": "generic split kernel (the matrix-core decode path keeps the per-block "
+                                   "query fold, which a per-row rotation breaks)"}}
+    pa = prefill_attention_figure(kw, c, T0, sinks_per_b, seed, dev, stream)
+    if pa is not None:
+        pa["note"] = "matrix-core kernel; staged keys turned in LDS, queries as fp16 hi + lo (3 score products)"
+    res["prefill_attn"] = pa
+    return res
+
+
 def algorithmic_bytes(kw, P, lo, sinks_per_b):
     """Bytes one decode-attention call must move (valid tokens only)."""
     D, H, Hq, B = kw["head_dim"], kw["n_kv_heads"], kw["n_q_heads"], kw["batch"]
@@ -598,6 +639,8 @@ def main():
     log(f"[bench] prefill done; sinks of b=0: {sinks_per_b[0]}")
     prefill_attn = prefill_attention_figure(kw, reps[0], T0, sinks_per_b, seed, dev, pstream)
     kivi_whole = whole_figure(dev, pstream) if not args.pmc_run else None
+    rope_on_read = rope_figure(args.config, kw, pre_k, pre_v, sinks_per_b, seed, dev, pstream) \
+        if not args.pmc_run else None
 
     # per-step inputs, resident on the GPU before timing
     step_kv = [make_rows(args.config, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(total_steps)]
@@ -697,6 +740,7 @@ def main():
         "prefill": prefill,
         "prefill_attn": prefill_attn,
         "kivi_whole": kivi_whole,
+        "rope_on_read": rope_on_read,
     }
     if not args.no_cpu_baseline:
         try:
