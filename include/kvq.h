@@ -55,7 +55,8 @@
  *    q = clamp(rint(x/scale), -8, 7), scale = absmax/7 ([Q2K] "Summary").
  *  * TQ: K meta = fp32 norm[32], V meta = fp32 norm[32] of the rotated row;
  *    codes are Lloyd-Max Beta(D/2, D/2) indices of the rotated, normalised
- *    coordinates ([TQ] "As-Built Notes", "Step 1", "Step 2").
+ *    coordinates ([TQ] "As-Built Notes", "Step 1", "Step 2"); 3-bit codes sit
+ *    in 4-bit slots (b = 4 above: two per byte, two bits unused, [TQ] "Step 3").
  *  * Sink rows and rows not yet appended hold code 0 and V metadata 0.
  *  Per-stream extras: K staging rows of the open block (in_dtype, KIVI and
  *  Q2K), fp16 window ring [residual][D] for K and V (slot p % residual), fp16
@@ -93,7 +94,8 @@ typedef struct {
   int32_t n_kv_heads; /* >= 1 */
   int32_t n_q_heads;  /* multiple of n_kv_heads, ratio <= 16 */
   int32_t head_dim;   /* 32, 64 or 128 */
-  int32_t format;     /* KVQ_FMT_*: KIVI bits (k,v) each in {2,4,8}; Q2K (2,4); TQ (4,2) or (2,2),(4,4),(2,4) */
+  int32_t format;     /* KVQ_FMT_*: KIVI bits (k,v) each in {2,4,8}; Q2K (2,4); TQ each in {2,3,4} (3-bit codes
+                         two per byte with two bits unused, [TQ] "Step 3: Packing": stored as 4-bit slots) */
   int32_t k_bits, v_bits;
   int32_t sink_mode;  /* KVQ_SINK_*; n_sink = 0 means no sinks in any mode */
   int32_t n_sink;     /* 0 .. 16 */

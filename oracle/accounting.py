@@ -15,7 +15,7 @@ Parity: pinned by enumeration and by the page figures of the q2k page
 tests/test_oracle_cache.py.
 """
 
-from .layout import record_sections
+from .layout import record_sections, slot_bits
 
 
 def bytes_per_token_head(fmt, D, k_bits, v_bits, G=32):
@@ -40,7 +40,7 @@ def account(model, layer, b):
     return {
         "n_valid": len(src), "n_compressed": n_q, "n_sink": n_sink, "n_residual": n_res,
         "current_length": model.P[layer],
-        "compressed_bytes": n_q * H * D * (cfg.k_bits + cfg.v_bits) // 8 + meta,
+        "compressed_bytes": n_q * H * D * (slot_bits(cfg.k_bits) + slot_bits(cfg.v_bits)) // 8 + meta,
         "sink_fp16_bytes": n_sink * H * D * 2 * 2,
         "residual_fp16_bytes": n_res * H * D * 2 * 2,
     }

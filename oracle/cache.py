@@ -140,8 +140,9 @@ def block_records(cfg, qs):
     off, size, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits)
     nblk = qs["nblk"]
     out = np.zeros((nblk, rec), dtype=np.uint8)
-    out[:, off["k_codes"]:off["k_codes"] + size["k_codes"]] = layout.pack_k_rows(qs["k_codes"], cfg.k_bits)
-    out[:, off["v_codes"]:off["v_codes"] + size["v_codes"]] = layout.pack_v_tiles(qs["v_codes"], cfg.v_bits)
+    kb, vb = layout.slot_bits(cfg.k_bits), layout.slot_bits(cfg.v_bits)
+    out[:, off["k_codes"]:off["k_codes"] + size["k_codes"]] = layout.pack_k_rows(qs["k_codes"], kb)
+    out[:, off["v_codes"]:off["v_codes"] + size["v_codes"]] = layout.pack_v_tiles(qs["v_codes"], vb)
     if cfg.fmt == "kivi":
         km = np.concatenate([qs["k_scale"], qs["k_zero"]], axis=-1).astype("<u2").view(np.uint8)
         vm = np.concatenate([layout.pack_v_meta(qs["v_scale"]), layout.pack_v_meta(qs["v_zero"])], axis=-1)

@@ -33,6 +33,10 @@ density and changes only which bit a code lands in:
 
   The V scale (and zero) of token t and 32-channel group g sits at index
   [t // 2][g][t % 2]: the two tokens of a pair are adjacent for every group.
+
+* **3-bit TurboQuant codes** use the page's per-byte packing, two codes per
+  byte with two bits unused ("Step 3: Packing"): they are stored in 4-bit
+  slots, b = 4 above.
 """
 
 import numpy as np
@@ -130,10 +134,15 @@ def unpack_v_meta(flat, ng):
     return np.swapaxes(pairs, -1, -2).reshape(f.shape[:-1] + (G, ng))
 
 
+def slot_bits(bits):
+    """Bits a code occupies in storage (3-bit codes: two per byte, two bits unused)."""
+    return 4 if bits == 3 else bits
+
+
 def record_sections(fmt, D, k_bits, v_bits):
     """Byte sizes of the four sections of one block record, and their offsets."""
-    kc = G * D * k_bits // 8
-    vc = G * D * v_bits // 8
+    kc = G * D * slot_bits(k_bits) // 8
+    vc = G * D * slot_bits(v_bits) // 8
     if fmt == "kivi":
         km, vm = 2 * 2 * D, 2 * 2 * G * (D // 32)
     elif fmt == "q2k":

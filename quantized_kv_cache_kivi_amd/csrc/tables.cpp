@@ -146,6 +146,10 @@ void make_tables(const kvq_config& cfg, Tables* t) {
   if (cfg.format == KVQ_FMT_TQ) {
     beta_lloyd_max(cfg.head_dim, cfg.k_bits, t->k_bnd, t->k_cen);
     beta_lloyd_max(cfg.head_dim, cfg.v_bits, t->v_bnd, t->v_cen);
+    // boundaries past a narrower codebook never count (3-bit codes live in 4-bit slots, whose
+    // quantizer counts 15 boundaries); centroids past it are never read
+    for (int j = (1 << cfg.k_bits) - 1; j < 15; ++j) t->k_bnd[j] = INFINITY;
+    for (int j = (1 << cfg.v_bits) - 1; j < 15; ++j) t->v_bnd[j] = INFINITY;
   }
   gaussian_lloyd_max4(t->q2k_thr, t->q2k_lvl);
   const double base = cfg.rope_base > 0.f ? (double)cfg.rope_base : 10000.0;

@@ -49,6 +49,14 @@ CASES = {
                                   v_bits=4, sink_mode="first_n", n_sink=4, window=128, residual=4),
     "fast_tq42_r2_ring_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128, fmt="tq", k_bits=4,
                                   v_bits=2, window=160, residual=16, seed=13),
+    # 3-bit TurboQuant codes (two per byte, two bits unused): K3/V2 on the matrix-core path, K4/V3 and
+    # K3/V3 on the generic one
+    "fast_tq32_r4_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=3,
+                                  v_bits=2, sink_mode="topk", n_sink=3, residual=24, capacity=512, seed=14),
+    "tq43_d64_firstn_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=4,
+                                v_bits=3, sink_mode="first_n", n_sink=2, window=128, residual=8, seed=15),
+    "tq33_d32_f32": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="tq", k_bits=3, v_bits=3,
+                         capacity=512, in_dtype="f32", seed=16),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]

@@ -7,6 +7,7 @@ from scipy import integrate
 from scipy.linalg import hadamard
 from scipy.stats import beta as beta_dist
 
+from oracle import layout
 from oracle import turboquant as tq
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
@@ -46,7 +47,7 @@ def _cell_moments(a, lo, hi):
 
 def test_codebook_fixed_point_by_quadrature_and_symmetry():
     d = 128
-    for bits in (2, 4):
+    for bits in (2, 3, 4):
         b, c, _ = tq.beta_lloyd_max(d, bits)
         L = 1 << bits
         edges = [0.0] + list(b) + [1.0]
@@ -59,7 +60,7 @@ def test_codebook_fixed_point_by_quadrature_and_symmetry():
 
 
 def test_codebook_unique_from_another_start():
-    for bits in (2, 4):
+    for bits in (2, 3, 4):
         L = 1 << bits
         b1, c1, _ = tq.beta_lloyd_max(128, bits)
         init = beta_dist.ppf((np.arange(L) + 0.5) / L, 64, 64)  # quantile start
@@ -81,7 +82,7 @@ def test_roundtrip_mse_matches_distortion():
     rng = np.random.default_rng(31)
     sg = tq.signs(7, d)
     x = rng.standard_normal((4000, d)).astype(np.float32)
-    for bits in (2, 4):
+    for bits in (2, 3, 4):
         kb, kc = tq.codebook(d, bits)
         b, c, _ = tq.beta_lloyd_max(d, bits)
         edges = [0.0] + list(b) + [1.0]
@@ -139,3 +140,15 @@ def test_turboquant_code_bytes_per_token():
         # metadata: one fp32 norm each for K and V per head (the page's two range floats each)
         assert (size["k_meta"] + size["v_meta"]) // 32 * row["heads"] * 2 == row["range_metadata_bytes"]
     assert 128 * 7 == g["rotation_flops_d128"]  # d log2 d butterflies
+
+
+def test_three_bit_codes_take_the_per_byte_packing():
+    """[TQ] "Step 3: Packing": 3-bit codes go two per byte with two bits unused, so K3 keys of 16
+    heads at dim 128 take 16 * 128 / 2 = 1024 bytes per token (the page's 768 B row assumes the
+    dense 8-in-3 alternative it mentions), the same as 4-bit keys."""
+    _, s3, _ = layout.record_sections("tq", 128, 3, 2)
+    _, s4, _ = layout.record_sections("tq", 128, 4, 2)
+    assert s3["k_codes"] == s4["k_codes"] and 16 * s3["k_codes"] // 32 == 1024
+    codes = np.arange(8, dtype=np.uint8)[None, :].repeat(4, 0).reshape(1, 32)
+    assert np.array_equal(layout.unpack_words(layout.pack_words(codes, layout.slot_bits(3)), 4), codes)
+    assert layout.pack_words(codes, 4).size == 16  # 32 codes in 16 bytes: two per byte
