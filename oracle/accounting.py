@@ -31,7 +31,7 @@ def account(model, layer, b):
     n_res = sum(1 for s in src.values() if s == "window")
     n_q = sum(1 for s in src.values() if s == "bulk")
     H, D = cfg.n_kv_heads, cfg.head_dim
-    _, size, _ = record_sections(cfg.fmt, D, cfg.k_bits, cfg.v_bits)
+    _, size, _ = record_sections(cfg.fmt, D, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
     blocks = {p // 32 for p, s in src.items() if s == "bulk"}
     if cfg.fmt == "tq":
         meta = n_q * 8 * H
@@ -40,7 +40,8 @@ def account(model, layer, b):
     return {
         "n_valid": len(src), "n_compressed": n_q, "n_sink": n_sink, "n_residual": n_res,
         "current_length": model.P[layer],
-        "compressed_bytes": n_q * H * D * (slot_bits(cfg.k_bits) + slot_bits(cfg.v_bits)) // 8 + meta,
+        "compressed_bytes": n_q * H * D * (slot_bits(cfg.k_bits, cfg.tq_dense3) +
+                                           slot_bits(cfg.v_bits, cfg.tq_dense3)) // 8 + meta,
         "sink_fp16_bytes": n_sink * H * D * 2 * 2,
         "residual_fp16_bytes": n_res * H * D * 2 * 2,
     }

@@ -61,6 +61,7 @@ class Config:
     seed: int = 0
     rope: bool = False         # K and q handed over before RoPE, rotated on read (oracle/rope.py)
     rope_base: float = 10000.0
+    tq_dense3: bool = False    # 3-bit TurboQuant codes as a dense 8-in-3 stream (else two per byte)
 
     @property
     def cap_blocks(self):
@@ -137,10 +138,10 @@ def quantize_stream(cfg, K, V, sink_pos, P, tq=None):
 
 def block_records(cfg, qs):
     """Packed block records [nblk, record_bytes] from quantize_stream output."""
-    off, size, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits)
+    off, size, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
     nblk = qs["nblk"]
     out = np.zeros((nblk, rec), dtype=np.uint8)
-    kb, vb = layout.slot_bits(cfg.k_bits), layout.slot_bits(cfg.v_bits)
+    kb, vb = layout.slot_bits(cfg.k_bits, cfg.tq_dense3), layout.slot_bits(cfg.v_bits, cfg.tq_dense3)
     out[:, off["k_codes"]:off["k_codes"] + size["k_codes"]] = layout.pack_k_rows(qs["k_codes"], kb)
     out[:, off["v_codes"]:off["v_codes"] + size["v_codes"]] = layout.pack_v_tiles(qs["v_codes"], vb)
     if cfg.fmt == "kivi":
@@ -165,7 +166,7 @@ def stream_image(cfg, K, V, sink_list, P, tq=None):
     sink_k/sink_v uint16 [n_sink, D], staging fp32 [P % 32, D] (the open
     block's raw rows; staging rows beyond P % 32 are not defined).
     """
-    _, _, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits)
+    _, _, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
     cap_b = cfg.cap_blocks
     D = cfg.head_dim
     bulk = np.zeros((cap_b, rec), dtype=np.uint8)

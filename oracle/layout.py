@@ -36,7 +36,10 @@ density and changes only which bit a code lands in:
 
 * **3-bit TurboQuant codes** use the page's per-byte packing, two codes per
   byte with two bits unused ("Step 3: Packing"): they are stored in 4-bit
-  slots, b = 4 above.
+  slots, b = 4 above.  With the dense option (the page's "8 values into 3
+  bytes") they are a plain little-endian bit stream instead: code i of a
+  section's sequence (K: row-major token rows; V: the 64 chunks above, one
+  after another) occupies bits [3i, 3i + 3), least significant bit first.
 """
 
 import numpy as np
@@ -75,14 +78,18 @@ def unpack_words(data, bits):
 
 
 def pack_k_rows(codes, bits):
-    """K codes [..., 32, D] -> bytes [..., 32*D*bits/8] (token rows)."""
+    """K codes [..., 32, D] -> bytes [..., 32*D*bits/8] (token rows; bits = 3: the dense stream)."""
     c = np.asarray(codes)
+    if bits == 3:
+        return pack_bits3(c.reshape(c.shape[:-2] + (-1,)))
     packed = pack_words(c, bits)  # [..., 32, D*bits/8]
     return packed.reshape(c.shape[:-2] + (-1,))
 
 
 def unpack_k_rows(data, D, bits):
     d = np.asarray(data)
+    if bits == 3:
+        return unpack_bits3(d, G * D).reshape(d.shape[:-1] + (G, D))
     rows = d.reshape(d.shape[:-1] + (G, D * bits // 8))
     return unpack_words(rows, bits)
 
@@ -105,14 +112,19 @@ def pack_v_tiles(codes, bits):
     D = c.shape[-1]
     tok, ch = _v_tile_order(D)
     seq = c[..., tok, ch]  # [..., 64, D/2]
+    if bits == 3:
+        return pack_bits3(seq.reshape(seq.shape[:-2] + (-1,)))
     packed = pack_words(seq, bits)  # [..., 64, D*bits/16]
     return packed.reshape(c.shape[:-2] + (-1,))
 
 
 def unpack_v_tiles(data, D, bits):
     d = np.asarray(data)
-    chunks = d.reshape(d.shape[:-1] + (64, D * bits // 16))
-    seq = unpack_words(chunks, bits)  # [..., 64, D/2]
+    if bits == 3:
+        seq = unpack_bits3(d, 64 * D // 2).reshape(d.shape[:-1] + (64, D // 2))
+    else:
+        chunks = d.reshape(d.shape[:-1] + (64, D * bits // 16))
+        seq = unpack_words(chunks, bits)  # [..., 64, D/2]
     tok, ch = _v_tile_order(D)
     out = np.zeros(d.shape[:-1] + (G, D), dtype=np.uint8)
     out[..., tok, ch] = seq
@@ -134,15 +146,32 @@ def unpack_v_meta(flat, ng):
     return np.swapaxes(pairs, -1, -2).reshape(f.shape[:-1] + (G, ng))
 
 
-def slot_bits(bits):
-    """Bits a code occupies in storage (3-bit codes: two per byte, two bits unused)."""
-    return 4 if bits == 3 else bits
+def slot_bits(bits, dense3=False):
+    """Bits a code occupies in storage (3-bit codes: two per byte with two bits unused, or 3 when dense)."""
+    if bits == 3:
+        return 3 if dense3 else 4
+    return bits
 
 
-def record_sections(fmt, D, k_bits, v_bits):
+def pack_bits3(codes):
+    """Dense 3-bit stream of codes [..., n] (3n a multiple of 8): code i at bits [3i, 3i+3), LSB first."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert np.all(c < 8), "code out of range"
+    bits = ((c[..., :, None] >> np.arange(3, dtype=np.uint8)) & 1).reshape(c.shape[:-1] + (-1,))
+    return np.packbits(bits, axis=-1, bitorder="little")
+
+
+def unpack_bits3(data, n):
+    """Inverse of pack_bits3: the first n codes of a dense 3-bit stream."""
+    bits = np.unpackbits(np.asarray(data, dtype=np.uint8), axis=-1, bitorder="little")
+    b = bits[..., : 3 * n].reshape(bits.shape[:-1] + (n, 3)).astype(np.uint8)
+    return b[..., 0] | (b[..., 1] << 1) | (b[..., 2] << 2)
+
+
+def record_sections(fmt, D, k_bits, v_bits, dense3=False):
     """Byte sizes of the four sections of one block record, and their offsets."""
-    kc = G * D * slot_bits(k_bits) // 8
-    vc = G * D * slot_bits(v_bits) // 8
+    kc = G * D * slot_bits(k_bits, dense3) // 8
+    vc = G * D * slot_bits(v_bits, dense3) // 8
     if fmt == "kivi":
         km, vm = 2 * 2 * D, 2 * 2 * G * (D // 32)
     elif fmt == "q2k":

@@ -152,3 +152,22 @@ def test_three_bit_codes_take_the_per_byte_packing():
     codes = np.arange(8, dtype=np.uint8)[None, :].repeat(4, 0).reshape(1, 32)
     assert np.array_equal(layout.unpack_words(layout.pack_words(codes, layout.slot_bits(3)), 4), codes)
     assert layout.pack_words(codes, 4).size == 16  # 32 codes in 16 bytes: two per byte
+
+
+def test_dense_three_bit_stream():
+    """The page's "8 values into 3 bytes": K3/V2 keys of 16 heads at dim 128 take 768 bytes per token
+    ([TQ] "Memory per token per layer"), and the stream puts code i at bits 3i..3i+2, LSB first."""
+    _, s3, _ = layout.record_sections("tq", 128, 3, 2, dense3=True)
+    assert 16 * s3["k_codes"] // 32 == 768
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 8, size=(5, 64)).astype(np.uint8)
+    packed = layout.pack_bits3(codes)
+    assert packed.shape == (5, 24)
+    big = int.from_bytes(packed[2].tobytes(), "little")
+    assert all(((big >> (3 * i)) & 7) == codes[2, i] for i in range(64))
+    assert np.array_equal(layout.unpack_bits3(packed, 64), codes)
+    for D in (32, 64, 128):
+        k = rng.integers(0, 8, size=(2, 32, D)).astype(np.uint8)
+        assert np.array_equal(layout.unpack_k_rows(layout.pack_k_rows(k, 3), D, 3), k)
+        assert np.array_equal(layout.unpack_v_tiles(layout.pack_v_tiles(k, 3), D, 3), k)
+        assert layout.pack_k_rows(k, 3).shape[-1] == 32 * D * 3 // 8
