@@ -56,7 +56,9 @@
  *  * TQ: K meta = fp32 norm[32], V meta = fp32 norm[32] of the rotated row;
  *    codes are Lloyd-Max Beta(D/2, D/2) indices of the rotated, normalised
  *    coordinates ([TQ] "As-Built Notes", "Step 1", "Step 2"); 3-bit codes sit
- *    in 4-bit slots (b = 4 above: two per byte, two bits unused, [TQ] "Step 3").
+ *    in 4-bit slots (b = 4 above: two per byte, two bits unused, [TQ] "Step 3"),
+ *    or with tq_dense3 form one little-endian 3-bit stream per section (K: the
+ *    token rows in order; V: the 64 chunks in order; code i at bits 3i..3i+2).
  *  * Sink rows and rows not yet appended hold code 0 and V metadata 0.
  *  Per-stream extras: K staging rows of the open block (in_dtype, KIVI and
  *  Q2K), fp16 window ring [residual][D] for K and V (slot p % residual), fp16
@@ -110,6 +112,9 @@ typedef struct {
   float rope_base;    /* RoPE base (<= 0: 10000); channel c < head_dim/2 pairs with c + head_dim/2 and turns
                          by idx * base^(-2c/head_dim), idx = the number of valid positions before the row
                          (a query: before its own position) */
+  int32_t tq_dense3;  /* TQ with a 3-bit side: 1 stores 3-bit codes as a dense stream, 8 codes in 3 bytes
+                         ([TQ] "Step 3: Packing"; code i of a section's sequence at bits 3i .. 3i+2, LSB
+                         first); 0 (default) two per byte in 4-bit slots */
 } kvq_config;
 
 typedef struct {

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   constexpr int PER = G * MAX_D / NT;  // row elements per thread (at most)
   const int nper = G * D / NT;         // row elements per thread
   const int ng = D / 32;
-  const int wpc = D * sh.vb / 64;      // words per V code chunk
+  const int wpc = D * sh.vb / 64;      // words per V code chunk (word-interleaved widths)
+  const int nvw = D * sh.vb;           // words of the V code section
   int sp[MAX_SINK];
   int scount = 0;
   if (tid < G && sh.n_sink > 0 && sh.sink_mode == KVQ_SINK_TOPK) {
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
 #pragma unroll
     for (int i = 0; i < VW; ++i) {
       const int idx = tid + i * NT;
-      oldv[i] = (tnew0 > 0 && idx < 64 * wpc) ? vw[idx] : 0u;
+      oldv[i] = (tnew0 > 0 && idx < nvw) ? vw[idx] : 0u;
     }
   }
 
@@ -292,6 +293,13 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
     for (int idx = tid; idx < G * wpr; idx += NT) {
       const int t = idx / wpr, w = idx % wpr;
       if (tq && !((t >= tnew0 && t < tend) || (tnew0 == 0 && t >= tend))) continue;
+      if (sh.kb == 3) {  // dense 3-bit stream: rows are whole words, a word holds codes c0 .. c1 of row t
+        uint32_t word = 0;
+        const int c0 = (32 * w) / 3, c1 = min(D - 1, (32 * w + 31) / 3);
+        for (int cc = c0; cc <= c1; ++cc) word |= code3_in_word(ck[t][cc], 3 * cc, w);
+        kw[idx] = word;
+        continue;
+      }
       uint32_t cw[4] = {0, 0, 0, 0};  // the word's codes, one byte each
       const uint8_t* src = &ck[t][w * per];
       if (per == 16) {
@@ -317,7 +325,20 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
 #pragma unroll
     for (int ii = 0; ii < VW; ++ii) {
       const int idx = tid + ii * NT;
-      if (idx >= 64 * wpc) break;
+      if (idx >= nvw) break;
+      if (sh.vb == 3) {  // dense 3-bit stream: codes g0 .. g1 of the tile sequence touch word idx
+        const uint32_t old = oldv[ii];
+        uint32_t word = 0;
+        const int half = D / 2, g0 = (32 * idx) / 3, g1 = min(64 * half - 1, (32 * idx + 31) / 3);
+        for (int g = g0; g <= g1; ++g) {
+          const int q = g / half, k = g % half, kg = q >> 4, i = q & 15;
+          const int t = v_tok(kg, k & 7), cc = 16 * (k >> 3) + i;
+          if (t < tnew0) word |= old & code3_in_word(7u, 3 * g, idx);
+          else if (t < tend) word |= code3_in_word(cvt[cc][t], 3 * g, idx);
+        }
+        vw[idx] = word;
+        continue;
+      }
       const int q = idx / wpc, w = idx % wpc, kg = q >> 4, i = q & 15;
       const uint32_t old = oldv[ii];
       uint32_t word = 0;

@@ -63,7 +63,7 @@ __device__ __forceinline__ uint32_t code_at(const uint8_t* sec, int word, int k,
 __device__ __forceinline__ float k_val(const Shape& sh, const uint8_t* rec, const LayerView& lv, int t, int c) {
   int w, k;
   k_code_pos(t, c, sh.D, sh.kb, &w, &k);
-  const uint32_t u = code_at(rec + lv.k_codes, w, k, sh.kb);
+  const uint32_t u = sh.kb == 3 ? code3_at(rec + lv.k_codes, k_bit3(t, c, sh.D)) : code_at(rec + lv.k_codes, w, k, sh.kb);
   const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + lv.k_meta);
   if (sh.fmt == KVQ_FMT_KIVI) return (float)u * f16_val(km[c]) + f16_val(km[sh.D + c]);
   if (sh.fmt == KVQ_FMT_Q2K) return lv.tables->q2k_lvl[u] * f16_val(km[c]);
@@ -72,7 +72,7 @@ __device__ __forceinline__ float k_val(const Shape& sh, const uint8_t* rec, cons
 __device__ __forceinline__ float v_val(const Shape& sh, const uint8_t* rec, const LayerView& lv, int t, int c) {
   int w, k;
   v_code_pos(t, c, sh.D, sh.vb, &w, &k);
-  const uint32_t u = code_at(rec + lv.v_codes, w, k, sh.vb);
+  const uint32_t u = sh.vb == 3 ? code3_at(rec + lv.v_codes, v_bit3(t, c, sh.D)) : code_at(rec + lv.v_codes, w, k, sh.vb);
   const uint16_t* vm = reinterpret_cast<const uint16_t*>(rec + lv.v_meta);
   const int ng = sh.D / 32, g = c >> 5;
   const int mi = v_meta_idx(t, g, ng);

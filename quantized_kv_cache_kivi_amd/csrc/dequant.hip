@@ -53,6 +53,10 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
   for (int e = 0; e < 2; ++e) {
     const int c = act ? 2 * lane + e : 0;
     int wd, k;
+    if (nb == 3) {  // dense 3-bit stream
+      u[e] = code3_at(codes, is_k ? k_bit3(t, c, D) : v_bit3(t, c, D));
+      continue;
+    }
     if (is_k) k_code_pos(t, c, D, nb, &wd, &k);
     else v_code_pos(t, c, D, nb, &wd, &k);
     u[e] = (reinterpret_cast<const uint32_t*>(codes)[wd] >> code_shift(k, nb)) & ((1u << nb) - 1u);

@@ -47,6 +47,29 @@ __device__ __forceinline__ void v_code_pos(int t, int c, int D, int b, int* word
 // [t / 2][g][t % 2], so both tokens of a pair sit side by side for every group.
 __device__ __forceinline__ int v_meta_idx(int t, int g, int ng) { return (t >> 1) * 2 * ng + 2 * g + (t & 1); }
 
+// Dense 3-bit stream ("TurboQuant KV Cache Compression — Spec", "Step 3: Packing", 8 values in 3
+// bytes): code i of a section's sequence at bits [3i, 3i + 3), least significant bit first; the K
+// sequence is row-major token rows, the V sequence the 64 chunks of the tile order one after another.
+__device__ __forceinline__ int k_bit3(int t, int c, int D) { return 3 * (t * D + c); }
+__device__ __forceinline__ int v_bit3(int t, int c, int D) {
+  const int kg = (t & 15) >> 2, e = ((t >> 4) << 2) | (t & 3);
+  return 3 * ((16 * kg + (c & 15)) * (D / 2) + 8 * (c >> 4) + e);
+}
+// A code of a dense stream: one word, or two when it straddles a word boundary (the next word is
+// inside the section: the code ends there).
+__device__ __forceinline__ uint32_t code3_at(const uint8_t* sec, int bit) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(sec);
+  const int wi = bit >> 5, o = bit & 31;
+  uint32_t x = w[wi] >> o;
+  if (o > 29) x |= w[wi + 1] << (32 - o);
+  return x & 7u;
+}
+// Bits of code `code` (3 bits at stream bit `bit`) that fall in word `wi` of the stream, in place.
+__device__ __forceinline__ uint32_t code3_in_word(uint32_t code, int bit, int wi) {
+  const int s = bit - 32 * wi;  // -2 .. 31
+  return s >= 0 ? code << s : code >> (-s);
+}
+
 // Token of element e of V token group kg.
 __device__ __forceinline__ int v_tok(int kg, int e) { return 16 * (e >> 2) + 4 * kg + (e & 3); }
 

@@ -50,13 +50,13 @@ struct RecordSections {
 
 // Bits a code occupies in storage: 3-bit TurboQuant codes use the page's per-byte packing, two
 // codes per byte with two bits unused ([TQ] "Step 3: Packing"), i.e. 4-bit slots.
-int slot_bits(int bits) { return bits == 3 ? 4 : bits; }
+int slot_bits(int bits, int dense3 = 0) { return bits == 3 ? (dense3 ? 3 : 4) : bits; }
 
 RecordSections record_sections(const kvq_config& c) {
   RecordSections r;
   const uint64_t D = c.head_dim;
-  r.kc = G * D * slot_bits(c.k_bits) / 8;
-  r.vc = G * D * slot_bits(c.v_bits) / 8;
+  r.kc = G * D * slot_bits(c.k_bits, c.tq_dense3) / 8;
+  r.vc = G * D * slot_bits(c.v_bits, c.tq_dense3) / 8;
   if (c.format == KVQ_FMT_KIVI) {
     r.km = 2 * 2 * D;
     r.vm = 2 * 2 * G * (D / 32);
@@ -107,6 +107,9 @@ kvq_status check(const kvq_config* c) {
   if (c->in_dtype != KVQ_IN_F16 && c->in_dtype != KVQ_IN_F32) return fail(KVQ_EINVAL, "in_dtype must be 0 or 1");
   if (c->rope != 0 && c->rope != 1) return fail(KVQ_EINVAL, "rope must be 0 or 1");
   if (c->rope && c->format == KVQ_FMT_TQ) return fail(KVQ_EINVAL, "rope on read is not available with TQ");
+  if (c->tq_dense3 != 0 && c->tq_dense3 != 1) return fail(KVQ_EINVAL, "tq_dense3 must be 0 or 1");
+  if (c->tq_dense3 && (c->format != KVQ_FMT_TQ || (c->k_bits != 3 && c->v_bits != 3)))
+    return fail(KVQ_EINVAL, "tq_dense3 needs TQ with 3-bit K or V");
   if (c->capacity < 0 || c->capacity % G != 0) return fail(KVQ_EINVAL, "capacity must be a multiple of 32");
   const int32_t cap = effective_capacity(*c);
   if (cap < G) return fail(KVQ_EINVAL, "capacity must be given (>= 32) when window = 0");
@@ -162,7 +165,7 @@ bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
   return c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope && (r == 1 || r == 2 || r == 4 || r == 8) &&
          (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits) ||
-          (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || c.k_bits == 3) && c.v_bits == 2));
+          (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || (c.k_bits == 3 && !c.tq_dense3)) && c.v_bits == 2));
 }
 
 // Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, whole rounds of the
@@ -245,8 +248,8 @@ Shape shape_of(const kvq_config& c) {
   s.Hq = c.n_q_heads;
   s.D = c.head_dim;
   s.fmt = c.format;
-  s.kb = slot_bits(c.k_bits);  // kernels address codes by their storage slots
-  s.vb = slot_bits(c.v_bits);
+  s.kb = slot_bits(c.k_bits, c.tq_dense3);  // kernels address codes by their storage slots
+  s.vb = slot_bits(c.v_bits, c.tq_dense3);
   s.sink_mode = c.n_sink > 0 ? c.sink_mode : KVQ_SINK_NONE;
   s.n_sink = c.n_sink;
   s.W = c.window;
@@ -579,7 +582,8 @@ kvq_status kvq_account(kvq_cache* c, int32_t layer, kvq_bytes* out, void* stream
     out->n_valid += n_s + n_win + n_bulk;
     int64_t meta = cf.format == KVQ_FMT_TQ ? n_bulk * 8 * H
                                            : nblocks * (int64_t)rs.km * H + n_bulk * (int64_t)(rs.vm / G) * H;
-    out->compressed_bytes += n_bulk * H * D * (slot_bits(cf.k_bits) + slot_bits(cf.v_bits)) / 8 + meta;
+    out->compressed_bytes +=
+        n_bulk * H * D * (slot_bits(cf.k_bits, cf.tq_dense3) + slot_bits(cf.v_bits, cf.tq_dense3)) / 8 + meta;
     out->sink_fp16_bytes += n_s * H * D * 2 * 2;
     out->residual_fp16_bytes += n_win * H * D * 2 * 2;
   }

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       if (slot >= lv.cap_b) slot -= lv.cap_b;
       const uint8_t* rec = sbase + (int64_t)slot * lv.rec;
       {  // K: codes of row t, channels c0 .. c0 + CPT - 1, with their metadata
-        constexpr int per = 32 / KB;
+        constexpr int per = KB == 3 ? 1 : 32 / KB;  // (3-bit codes: the dense stream, read per code)
         const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + lv.k_codes) + t * (D * KB / 32);
         const uint32_t* km = reinterpret_cast<const uint32_t*>(rec + lv.k_meta);
         uint32_t sc[CPT / 2], zc[CPT / 2];
@@ -242,7 +242,8 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int c = c0 + 2 * i + h, k = c % per;
-            const uint32_t u = (kw[c / per] >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
+            const uint32_t u = KB == 3 ? code3_at(rec + lv.k_codes, k_bit3(t, c, D))
+                                       : (kw[c / per] >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
             if constexpr (TQ) {
               x[h] = nk * S.kcen[u];
             } else if constexpr (FMT == KVQ_FMT_KIVI) {
@@ -264,7 +265,17 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
           S.pos[tid] = (p >= a.lo && p < bhi && !is_sink(p)) ? (int)p : -1;
         }
       }
-      {  // V: chunk q = 16*kq + i holds, for channel tile mu, rows v_tok(kq, e) of channel 16*mu + i
+      if constexpr (VB == 3) {  // V from the dense 3-bit stream, one element per thread and pass
+        const float* vn = reinterpret_cast<const float*>(rec + lv.v_meta);
+        for (int idx = tid; idx < G * D; idx += PNT) {
+          const int tv = idx % G, c = idx / G;
+          const float x = vn[tv] * S.vcen[code3_at(rec + lv.v_codes, v_bit3(tv, c, D))];
+          const int kq = (tv & 15) >> 2, e = ((tv >> 4) << 2) | (tv & 3);
+          const _Float16 hx = (_Float16)x;
+          S.vt[c][8 * kq + e] = hx;
+          S.vtl[c][8 * kq + e] = (_Float16)(x - (float)hx);
+        }
+      } else {  // V: chunk q = 16*kq + i holds, for channel tile mu, rows v_tok(kq, e) of channel 16*mu + i
         const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
         const uint32_t* vm = reinterpret_cast<const uint32_t*>(rec + lv.v_meta);
         const int q = tid & 63, kq = q >> 4, i = q & 15;
@@ -567,6 +578,12 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
     if (sh.kb == 2 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 2, 2>(a, grid, st);
     if (sh.kb == 4 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 4, 4>(a, grid, st);
     if (sh.kb == 2 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 2, 4>(a, grid, st);
+    // dense 3-bit streams
+    if (sh.kb == 3 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 3, 2>(a, grid, st);
+    if (sh.kb == 3 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 3, 3>(a, grid, st);
+    if (sh.kb == 3 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 3, 4>(a, grid, st);
+    if (sh.kb == 2 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 2, 3>(a, grid, st);
+    if (sh.kb == 4 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 4, 3>(a, grid, st);
     return hipErrorInvalidValue;
   }
   if (sh.fmt != KVQ_FMT_KIVI) return hipErrorInvalidValue;

@@ -31,7 +31,8 @@ class kvq_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "batch", "n_kv_heads", "n_q_heads", "head_dim", "format", "k_bits", "v_bits",
         "sink_mode", "n_sink", "window", "residual", "capacity", "in_dtype")] + [
-        ("seed", ctypes.c_uint64), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float)]
+        ("seed", ctypes.c_uint64), ("rope", ctypes.c_int32), ("rope_base", ctypes.c_float),
+        ("tq_dense3", ctypes.c_int32)]
 
 
 class kvq_bytes(ctypes.Structure):
@@ -122,9 +123,10 @@ def _check(status):
 
 def make_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, fmt="kivi", k_bits=2, v_bits=2,
                 sink_mode="none", n_sink=0, window=0, residual=0, capacity=0, in_dtype="f16", seed=0, rope=False,
-                rope_base=0.0):
+                rope_base=0.0, tq_dense3=False):
     return kvq_config(n_layers, batch, n_kv_heads, n_q_heads, head_dim, FMT[fmt], k_bits, v_bits, SINK[sink_mode],
-                      n_sink, window, residual, capacity, IN_DTYPE[in_dtype], seed, int(rope), rope_base)
+                      n_sink, window, residual, capacity, IN_DTYPE[in_dtype], seed, int(rope), rope_base,
+                      int(tq_dense3))
 
 
 def config_check(cfg):

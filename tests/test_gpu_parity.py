@@ -57,6 +57,15 @@ CASES = {
                                 v_bits=3, sink_mode="first_n", n_sink=2, window=128, residual=8, seed=15),
     "tq33_d32_f32": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="tq", k_bits=3, v_bits=3,
                          capacity=512, in_dtype="f32", seed=16),
+    # the dense 8-in-3 stream (codes straddle words; V chunks are not word-aligned at head_dim 32)
+    "tq32_dense_r4_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=3,
+                                   v_bits=2, sink_mode="topk", n_sink=3, residual=24, capacity=512, seed=17,
+                                   tq_dense3=True),
+    "tq43_dense_d64_firstn_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=4,
+                                      v_bits=3, sink_mode="first_n", n_sink=2, window=128, residual=8, seed=18,
+                                      tq_dense3=True),
+    "tq33_dense_d32_f32": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="tq", k_bits=3,
+                               v_bits=3, capacity=512, in_dtype="f32", seed=19, tq_dense3=True),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]

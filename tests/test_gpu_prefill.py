@@ -40,6 +40,11 @@ CASES = {
                           sink_mode="topk", n_sink=3, residual=16, capacity=1024), [70, 33]),
     "tq43_r2_d64": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=4, v_bits=3,
                          residual=8, capacity=1024), [90, 20]),
+    "tq33_dense_r2_d64": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=3,
+                               v_bits=3, sink_mode="first_n", n_sink=2, residual=8, capacity=1024, tq_dense3=True),
+                          [90, 20]),
+    "tq32_dense_r4_d32": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=8, head_dim=32, fmt="tq", k_bits=3,
+                               v_bits=2, residual=0, capacity=1024, tq_dense3=True), [70, 33]),
     "tq24_r8_firstn": (dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=8, head_dim=128, fmt="tq", k_bits=2,
                             v_bits=4, sink_mode="first_n", n_sink=4, residual=40, capacity=1024), [200, 7]),
 }

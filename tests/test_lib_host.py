@@ -126,3 +126,14 @@ def test_whole_config_validation_and_layout(kvq):
     for cfg in bad:
         assert kvq.whole_config_check(cfg) == -1 and kvq.last_error() != ""
         assert kvq.whole_required_bytes(cfg) == 0
+
+
+def test_dense_three_bit_config_and_layout(kvq):
+    ok = kvq.make_config(1, 2, 2, 8, 128, "tq", 3, 2, capacity=64, tq_dense3=True)
+    assert kvq.config_check(ok) == 0
+    off, size, rec = olayout.record_sections("tq", 128, 3, 2, dense3=True)
+    lay = kvq.get_layout(ok)
+    assert lay.record_bytes == rec and lay.rec_v_codes == size["k_codes"] == 32 * 128 * 3 // 8
+    for bad in (kvq.make_config(1, 2, 2, 8, 128, "tq", 4, 2, capacity=64, tq_dense3=True),
+                kvq.make_config(1, 2, 2, 8, 128, "kivi", 2, 2, capacity=64, tq_dense3=True)):
+        assert kvq.config_check(bad) == -1 and "tq_dense3" in kvq.last_error()
