@@ -544,6 +544,8 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=sorted(CONFIGS))
     ap.add_argument("--replicas", type=int, default=0, help="cache replicas (0: enough to exceed 1 GB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-figures", action="store_true",
+                    help="skip the whole-T cache and RoPE-on-read figures (profiling runs of the other kernels)")
     ap.add_argument("--pmc-run", action="store_true",
                     help="run the warmup and timed steps without timing or output (for rocprofv3 --pmc passes)")
     ap.add_argument("--copy-calibration", action="store_true", help="run the 1 GiB calibration copy and exit")
@@ -637,10 +639,11 @@ def main():
         pos = reps[0].region(0, "sink_pos", n * 4).cpu().view(torch.int32).reshape(kw["batch"], kw["n_sink"])
         sinks_per_b = [[int(p) for p in row if p >= 0] for row in pos.tolist()]
     log(f"[bench] prefill done; sinks of b=0: {sinks_per_b[0]}")
-    prefill_attn = prefill_attention_figure(kw, reps[0], T0, sinks_per_b, seed, dev, pstream)
-    kivi_whole = whole_figure(dev, pstream) if not args.pmc_run else None
-    rope_on_read = rope_figure(args.config, kw, pre_k, pre_v, sinks_per_b, seed, dev, pstream) \
+    prefill_attn = prefill_attention_figure(kw, reps[0], T0, sinks_per_b, seed, dev, pstream) \
         if not args.pmc_run else None
+    extras = not (args.pmc_run or args.no_extra_figures)
+    kivi_whole = whole_figure(dev, pstream) if extras else None
+    rope_on_read = rope_figure(args.config, kw, pre_k, pre_v, sinks_per_b, seed, dev, pstream) if extras else None
 
     # per-step inputs, resident on the GPU before timing
     step_kv = [make_rows(args.config, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(total_steps)]
