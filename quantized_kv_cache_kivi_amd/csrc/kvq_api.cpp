@@ -216,6 +216,12 @@ int max_splits(const kvq_config& c) {
   return splits_for(c, nblk, 0, 0);
 }
 
+// RoPE caches with fp16 queries decode on the prefill kernel (split over row blocks).
+constexpr int ROPE_MAX_SPLITS = 64;
+bool rope_decode_on_prefill(const kvq_config& c) {
+  return c.rope && c.in_dtype == KVQ_IN_F16 && c.format != KVQ_FMT_TQ;
+}
+
 // fp16-row partials of a decode call: the MFMA path scores the window rows and the sinks in groups
 // of fast_fp16_rows_per_group() rows; TurboQuant's generic kernel in one partial; other formats in
 // the merge kernel.
@@ -316,7 +322,10 @@ size_t kvq_workspace_bytes(const kvq_config* cfg) {
   const size_t streams = (size_t)cfg->batch * cfg->n_kv_heads;
   const size_t r = cfg->n_q_heads / cfg->n_kv_heads;
   const int parts = max_splits(*cfg) + std::max(1, fp16_parts(*cfg, (int64_t)cfg->residual + cfg->n_sink));
-  return streams * (size_t)parts * r * (size_t)(cfg->head_dim + 2) * sizeof(float);
+  size_t bytes = streams * (size_t)parts * r * (size_t)(cfg->head_dim + 2) * sizeof(float);
+  if (rope_decode_on_prefill(*cfg))  // row-block partials of the prefill kernel: up to 64 splits
+    bytes = std::max(bytes, streams * r * (size_t)ROPE_MAX_SPLITS * (cfg->head_dim + 4) * sizeof(float));
+  return bytes;
 }
 
 kvq_status kvq_create(const kvq_config* cfg, void* dev_buf, size_t dev_bytes, void* stream, kvq_cache** out) {
@@ -462,6 +471,30 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   // the committed count; groups past it write empty partials)
   const int64_t fp_rows = (P - a.bulk_hi) + std::min<int64_t>(cf.n_sink, P);
   const int fparts = fp16_parts(cf, fp_rows);
+  if (rope_decode_on_prefill(cf)) {
+    // RoPE on read with fp16 queries: the decode query is a one-query prefill chunk (its index is
+    // that of position P - 1), run on the matrix-core prefill kernel split over row blocks
+    if ((uintptr_t)q % 16 != 0 || (uintptr_t)out % 16 != 0 || (uintptr_t)ws % 16 != 0)
+      return fail(KVQ_EINVAL, "RoPE decode: q, out and ws must be 16-byte aligned");
+    PrefillArgs pa;
+    pa.sh = a.sh;
+    pa.lv = a.lv;
+    pa.q = q;
+    pa.out = out;
+    pa.scale = a.scale;
+    pa.P = P;
+    pa.lo = lo;
+    pa.bulk_hi = a.bulk_hi;
+    pa.n = 1;
+    pa.part = (float*)ws;
+    const int nrb = prefill_row_blocks(pa);
+    const int streams = cf.batch * cf.n_kv_heads;
+    const int want = std::max(1, (2048 + streams - 1) / streams);  // ~2048 workgroups
+    pa.splits = std::max(1, std::min({ROPE_MAX_SPLITS, want, nrb}));
+    hipError_t e = launch_prefill(pa, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode (RoPE) launch");
+    return KVQ_OK;
+  }
   if (a.bulk_hi > a.bulk_lo) {
     a.blk_first = a.bulk_lo / G;
     a.nblk = (int)((a.bulk_hi - 1) / G - a.blk_first + 1);
@@ -505,6 +538,8 @@ kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t 
   a.lo = lo;
   a.bulk_hi = std::max(lo, P - (int64_t)cf.residual);
   a.n = n;
+  a.splits = 1;
+  a.part = nullptr;
   hipError_t e = launch_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "prefill attention launch");
   return KVQ_OK;

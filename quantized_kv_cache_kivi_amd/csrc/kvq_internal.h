@@ -94,6 +94,8 @@ struct PrefillArgs {
   float scale;
   int64_t P, lo, bulk_hi;  // valid range [lo, P) (plus sinks); bulk rows below bulk_hi
   int n;
+  int splits;           // row-block splits per query tile (1: outputs written directly; > 1: not TQ)
+  float* part;          // splits > 1: [B][Hq][n][splits][D + 4] partials (acc[D], m, l), merged afterwards
 };
 
 struct DequantArgs {
@@ -112,6 +114,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t s);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 int prefill_queries_per_tile(int r, int fmt, int rope);  // queries of one prefill-attention workgroup
+int prefill_row_blocks(const PrefillArgs& a);            // row blocks the last query tile reads
 
 // Workgroups of the MFMA decode kernel for this shape that the current device holds at once
 // (compute units x resident workgroups per unit); 0 if the shape has no MFMA kernel.

@@ -211,7 +211,10 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   const int wslot0 = nwin > 0 ? (int)(a.bulk_hi % sh.R) : 0;        // window slot of row bulk_hi
   const uint8_t* sbase = lv.bulk + (int64_t)s * lv.cap_b * lv.rec;  // this stream's ring
 
-  for (int rb = 0; rb < nrb; ++rb) {
+  // split over row blocks (decode-sized calls): this workgroup reads row blocks [rb_lo, rb_hi)
+  const int split = blockIdx.z;
+  const int rb_lo = (int)((int64_t)nrb * split / a.splits), rb_hi = (int)((int64_t)nrb * (split + 1) / a.splits);
+  for (int rb = rb_lo; rb < rb_hi; ++rb) {
     __syncthreads();  // the previous row block is consumed
     // ---- stage the row block: thread (row t, channel slice) for K; chunk-wise for V ----
     constexpr int CPT = D / SL;  // channels per staging thread
@@ -510,6 +513,17 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     const float il = l > 0.f ? 1.f / l : 0.f;
+    if (!TQ && a.splits > 1) {  // un-normalised partial (acc, m, l) of this split
+      if (qpos[tt] < 0) continue;
+      float* pp = a.part + ((((int64_t)b * sh.Hq + head[tt]) * a.n + qidx[tt]) * a.splits + split) * (D + 4);
+#pragma unroll
+      for (int mu = 0; mu < NMU; ++mu) *reinterpret_cast<f4*>(pp + 16 * mu + 4 * kg) = acc[tt][mu];
+      if (kg == 0) {
+        pp[D] = m_[tt];
+        pp[D + 1] = l;
+      }
+      continue;
+    }
     if constexpr (!TQ) {
       if (qpos[tt] < 0) continue;
       float* o = a.out + (((int64_t)b * sh.Hq + head[tt]) * a.n + qidx[tt]) * D;
@@ -537,6 +551,27 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   }
 }
 
+// Fixed-order merge of the row-block splits of one (b, head, query): o = sum 2^(m_i - M) acc_i /
+// sum 2^(m_i - M) l_i; a query without valid rows in any split gets zeros.
+template <int D>
+__global__ __launch_bounds__(D) void k_prefill_merge(PrefillArgs a) {
+  const int64_t idx = blockIdx.x;  // (b * Hq + head) * n + query
+  const int c = threadIdx.x;
+  const float* base = a.part + idx * a.splits * (D + 4);
+  float M = -INFINITY;
+  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[sp * (D + 4) + D]);
+  float av = 0.f, lv = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float ms = base[sp * (D + 4) + D];
+      const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+      av = av + base[sp * (D + 4) + c] * w;
+      lv = lv + base[sp * (D + 4) + D + 1] * w;
+    }
+  }
+  a.out[idx * D + c] = lv > 0.f ? av / lv : 0.f;
+}
+
 template <int FMT, int KB, int VB, bool RP>
 hipError_t launch_dr(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   switch (a.sh.D) {
@@ -544,6 +579,14 @@ hipError_t launch_dr(const PrefillArgs& a, dim3 grid, hipStream_t st) {
     case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, RP>), grid, dim3(PNT), 0, st, a); break;
     case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, RP>), grid, dim3(PNT), 0, st, a); break;
     default: return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits <= 1) return e;
+  const dim3 mg((unsigned)((int64_t)a.sh.B * a.sh.Hq * a.n));
+  switch (a.sh.D) {
+    case 32: hipLaunchKernelGGL(k_prefill_merge<32>, mg, dim3(32), 0, st, a); break;
+    case 64: hipLaunchKernelGGL(k_prefill_merge<64>, mg, dim3(64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL(k_prefill_merge<128>, mg, dim3(128), 0, st, a); break;
   }
   return hipGetLastError();
 }
@@ -568,10 +611,18 @@ int prefill_queries_per_tile(int r, int fmt, int rope) {
   return PNW * (fmt == KVQ_FMT_TQ || rope ? 1 : PT) * (16 / r);
 }
 
+int prefill_row_blocks(const PrefillArgs& a) {
+  // the last tile's rows: every valid position (its last query is position P - 1)
+  const int64_t nb = a.bulk_hi > a.lo ? (a.bulk_hi - 1) / G - a.lo / G + 1 : 0;
+  const int64_t nw = a.P - a.bulk_hi;
+  return (int)(nb + (nw + G - 1) / G + (a.sh.n_sink > 0 ? 1 : 0));
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
   const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv, sh.fmt, sh.rope);
-  const dim3 grid((a.n + QT - 1) / QT, sh.B * sh.Hkv);
+  if (a.splits > 1 && (sh.fmt == KVQ_FMT_TQ || !a.part)) return hipErrorInvalidValue;
+  const dim3 grid((a.n + QT - 1) / QT, sh.B * sh.Hkv, a.splits > 1 ? a.splits : 1);
   if (sh.fmt == KVQ_FMT_Q2K) return launch_d<KVQ_FMT_Q2K, 2, 4>(a, grid, st);
   if (sh.fmt == KVQ_FMT_TQ) {
     if (sh.kb == 4 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 4, 2>(a, grid, st);
