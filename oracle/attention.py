@@ -10,7 +10,7 @@ then the inverse rotation).
 Attention has a plain definition, written out here in fp64:
 o = sum_p softmax_p(alpha * q . k_p) v_p over the valid positions p, with the
 keys and values dequantized exactly (fp64 products of the stored fp16/fp32
-metadata, no intermediate rounding).  Readings (DESIGN.md): alpha = 1/sqrt(D)
+metadata, no intermediate rounding).  Readings: alpha = 1/sqrt(D)
 unless given; query head j reads KV head j // (Hq/Hkv).
 
 ``dequant16`` is the materialisation the library's kvq_dequant returns:
@@ -131,7 +131,7 @@ def prefill_attention(model, layer, q, scale=None, batches=None, heads=None, que
 
     q: [B, Hq, n, D] are the queries of the last n appended positions P-n .. P-1.  Query i attends
     the valid positions p (the cache as it stands: sinks, window, bulk, read priority applied) with
-    p <= P - n + i; a query with no such position yields zeros.  Readings (DESIGN.md): the valid set
+    p <= P - n + i; a query with no such position yields zeros.  Readings: the valid set
     is the cache after the chunk's append and eviction; alpha and the GQA mapping are the decode
     ones.  Returns fp64 [len(batches), len(heads), len(queries), D].
     """

@@ -8,7 +8,7 @@ the quantized bulk, read exact) and the kivi_sink page ("How it works": sink
 rows fp16 and never quantized, excluded from calibration; the fp16 residual
 window composes with them).
 
-Readings (DESIGN.md):
+Readings:
 
 * Positions are absolute.  After ``evict`` the valid set is
   C u [lo, P) with lo = max(lo, P - W) (lo = 0 when W = 0), C the committed

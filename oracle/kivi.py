@@ -6,7 +6,7 @@ codes from rounding (x - zero)/scale, dequant (q - qMin)*scale + zero.  K is
 grouped per channel (here over 32-token blocks, the group-size freezing the
 page's "Caveats" section names), V per token (here over 32-channel groups).
 
-Readings where the page is silent (each listed in the design doc):
+Readings where the page is silent:
 
 * qMax - qMin = 2^b - 1 for b = 8, 4 (the page's -128/127 and -8/7) and 2
   (the kivi_sink page runs b = 2; the page itself has no int2).

@@ -20,7 +20,7 @@ Follows the StreamingLLM + KIVI page:
 * "Caveats": a new token can move a channel's min/max, so the whole K block is
   re-quantised on every append (O(T*D) per step).
 
-Readings (each listed in the design doc):
+Readings:
 
 * Stored bytes are the signed code q = u + qMin (two's complement int8), with
   u = clamp(rint((x - zero)/scale), 0, qMax - qMin) against the stored fp16

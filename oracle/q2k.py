@@ -6,7 +6,7 @@ Lloyd-Max codebook over the block RMS, fitted to the Gaussian grid; V at 4
 bits per token in 32-element blocks with one fp16 scale each; 448 bytes per
 cell at 2 KV heads x 256 channels.
 
-Readings (the page names the formats but does not define them; DESIGN.md):
+Readings (the page names the formats but does not define them):
 
 * 448 B/cell fixes the metadata as one fp16 scale per K (channel, 32-token
   block) and one per V (token, 32-channel group), with no zero points.

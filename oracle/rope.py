@@ -7,7 +7,7 @@ compressed cache rather than of its original position, which needs the keys stor
 the rotation applied when they are read.  Storing K before RoPE also keeps the per-channel K
 quantisation on a stable basis ("The bug class the previous attempt hit", 5).
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
 
 * The rotation is the rotary embedding in its rotate-half form: channel c < D/2 pairs with
   c + D/2, and the pair (x_c, x_{c+D/2}) turns by the angle idx * theta_c with

@@ -8,7 +8,7 @@ token quantized in an earlier call is never restored later.  The static mode
 keeps the first N tokens (StreamingLLM + KIVI page, "StreamingLLM — why
 softmax needs an anchor").
 
-Readings (DESIGN.md):
+Readings:
 
 * score_t = (sum over heads h, in order, of sqrt(canonical sumsq of K[b,h,t,:]))
   / n_kv_heads, in fp32.

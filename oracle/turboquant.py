@@ -7,7 +7,7 @@ before the Walsh-Hadamard transform; normalisation by the vector L2 norm),
 stages 1, 2, 4, ...; scale by 1/sqrt(d) after the transform), and
 "Optimization: Fused dequant-dot" for the rotated-domain decode identity.
 
-Readings (the design doc lists them):
+Readings:
 
 * Signs: sigma_i = -1 when bit 63 of the i-th output of splitmix64 (the
   generator of Steele, Lea and Flood, 2014) seeded with ``seed`` is set,
