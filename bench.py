@@ -228,7 +228,7 @@ def whole_append_bytes(wk, n_old, n, esz):
     return S * (n_old * D + (n_old + n) * D + 2 * n * D * esz + n * (D + 4) + 8 * D)
 
 
-def whole_figure(dev, stream):
+def whole_figure(dev, stream, with_oracle=False):
     """The StreamingLLM + KIVI page's own KIVI cache (K scales over the whole stored T), two workloads:
     the page's model shape (12 layers, 8 heads, d=32, int8, sink 4 + window 256, fp32 K/V, a 4-token
     prompt then 500 decode steps of append + evict + attention per layer), and one layer at batch 8,
@@ -280,6 +280,32 @@ def whole_figure(dev, stream):
         "append_us": ta, "decode_attn_us": td,
         "cache_bytes_12_layers": 12 * c.kvqw_account(0)["code_bytes"] + 12 * c.kvqw_account(0)["meta_bytes"],
         "note": "launch-bound: 4 kernel launches per layer and step over 8 x 260 rows of 68 bytes"}
+    if with_oracle:  # the oracle on one layer of the same model, steady state (260 stored rows), 1 thread
+        from threadpoolctl import threadpool_limits
+
+        from oracle import kivi_whole as okw
+        with threadpool_limits(limits=1):
+            om = okw.WholeCache(okw.WholeConfig(1, 1, 8, 8, 32, bits=8, n_sink=4, window=256, in_dtype="f32"))
+            om.append(0, k0.cpu().numpy(), v0.cpu().numpy())
+            om.evict(0)
+            kc, vc, qc = ks.cpu().numpy(), vs.cpu().numpy(), qs.cpu().numpy()
+            for i in range(260):
+                om.append(0, kc[i], vc[i])
+                om.evict(0)
+            t0 = time.perf_counter()
+            n_or = 0
+            for i in range(260, steps):
+                om.append(0, kc[i], vc[i])
+                om.evict(0)
+                om.decode_attention(0, qc[i])
+                n_or += 1
+                if time.perf_counter() - t0 > 10.0:
+                    break
+            t_or = time.perf_counter() - t0
+        res["page_model"]["cpu_baseline"] = {
+            "value": n_or / t_or / 12, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_or} decode steps of one layer at 260 stored rows (append + evict + attention), "
+                      "scaled to the 12 layers of a step"}
     del c
     # bandwidth workload
     wk = dict(n_layers=1, batch=8, n_kv_heads=8, n_q_heads=32, head_dim=128, bits=8, n_sink=0, window=0,
@@ -431,11 +457,45 @@ def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, b
             nbytes += algorithmic_bytes(sub, m.P[0], m.lo[0], sinks)[0]
             if time.perf_counter() - t0 > budget_s:
                 break
+        # causal prefill attention of the same model: a few queries of one query head per KV head
+        extra = {}
+        if prefill_k.shape[2] > 0 and kw.get("in_dtype") != "f32":
+            import torch
+            from quantized_kv_cache_kivi_amd import synth
+            P = m.P[0]
+            nq = 8
+            heads = list(range(0, kw["n_q_heads"], kw["n_q_heads"] // kw["n_kv_heads"]))
+            qp = synth.normal((1, kw["n_q_heads"], nq, kw["head_dim"]), 7, 62_000).to(torch.float16).numpy()
+            t1 = time.perf_counter()
+            oattn.prefill_attention(m, 0, qp, heads=heads)
+            tp = time.perf_counter() - t1
+            _, lo = m.P[0], m.lo[0]
+            early = [p for p, _ in m.sink_list(0, 0) if p < lo]
+            rows = sum(max(0, P - nq + i - lo + 1) + sum(1 for p in early if p <= P - nq + i) for i in range(nq))
+            flops = 4 * kw["head_dim"] * len(heads) * rows
+            extra["prefill_attn"] = {"value": flops / tp / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+                                     "sample": f"batch element 0, {len(heads)} query heads (one per KV head), the "
+                                               f"last {nq} of {P} positions as queries; algorithmic FLOPs / oracle "
+                                               f"time (fp64, numpy, 1 BLAS thread)"}
+            if kw.get("fmt") != "tq":  # the same cache read with RoPE on read
+                mr = ocache.CacheModel(m.cfg.with_(rope=True), reserve=P)
+                mr.select(0, k0)
+                mr.append(0, k0, v0)
+                mr.evict(0)
+                qd = qp[:, :, -1]
+                t1 = time.perf_counter()
+                oattn.decode_attention(mr, 0, qd)
+                td = time.perf_counter() - t1
+                nb_r = algorithmic_bytes(sub, mr.P[0], mr.lo[0], [[p for p, _ in mr.sink_list(0, 0)]])[0]
+                extra["rope_decode_attn"] = {"value": nb_r / td / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                                             "sample": f"batch element 0 after the {mr.P[0]}-row prefill, every "
+                                                       f"query head, one decode call with RoPE on read (fp64, "
+                                                       f"numpy, 1 BLAS thread)"}
     return {"value": nbytes / t_attn / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"batch element 0 of the workload ({kw['n_kv_heads']} KV heads, {kw['n_q_heads']} query "
                       f"heads): prefill of {prefill_k.shape[2]} rows ({t_prefill:.1f} s), then {calls} decode "
                       f"steps; value = algorithmic decode-attention bytes of that batch element / oracle "
-                      f"decode-attention time (fp64, numpy, 1 BLAS thread)"}
+                      f"decode-attention time (fp64, numpy, 1 BLAS thread)", "rows": extra}
 
 
 DECODE_SOURCES = ["decode_fast.hip", "decode.hip", "decode_shared.h", "device_common.h", "kvq_internal.h",
@@ -643,7 +703,7 @@ def main():
     prefill_attn = prefill_attention_figure(kw, reps[0], T0, sinks_per_b, seed, dev, pstream) \
         if not args.pmc_run else None
     extras = not (args.pmc_run or args.no_extra_figures)
-    kivi_whole = whole_figure(dev, pstream) if extras else None
+    kivi_whole = whole_figure(dev, pstream, with_oracle=not args.no_cpu_baseline) if extras else None
     rope_on_read = rope_figure(args.config, kw, pre_k, pre_v, sinks_per_b, seed, dev, pstream) if extras else None
 
     # per-step inputs, resident on the GPU before timing
@@ -753,6 +813,11 @@ def main():
                                                step_kv[0][0][:, :, :0], pre_v if pre_v is not None else
                                                step_kv[0][1][:, :, :0], step_kv[:n_cpu], qs[:n_cpu],
                                                kw.get("sink_mode") == "topk")
+            rows = res["cpu_baseline"].pop("rows", {})
+            if res.get("prefill_attn") and "prefill_attn" in rows:
+                res["prefill_attn"]["cpu_baseline"] = rows["prefill_attn"]
+            if res.get("rope_on_read") and "rope_decode_attn" in rows:
+                res["rope_on_read"]["decode_attn"]["cpu_baseline"] = rows["rope_decode_attn"]
         except Exception as e:  # the baseline is a report, never a reason to lose the GPU line
             res["cpu_baseline"] = {"value": None, "unit": "GB/s", "cores": 1, "kind": "oracle",
                                    "sample": f"failed: {e!r}"}
