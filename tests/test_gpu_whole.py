@@ -168,3 +168,19 @@ def test_whole_rejects_bad_calls():
     assert acc["code_bytes"] + acc["meta_bytes"] == okw.stored_bytes(pair.ocfg, 32)
     assert acc["packed_int4_bytes"] == okw.stored_bytes(pair.ocfg, 32, packed_int4=True)
     assert acc["bf16_bytes"] == okw.dense_bytes(pair.ocfg, 32, 2)
+
+
+def test_whole_bench_bandwidth_size():
+    """The bench's bandwidth workload (batch 8, 8 KV / 32 q heads, d=128, int8, T=4096 then single
+    rows, no eviction), in the launch configuration bench.py times: codes and metadata of every
+    stream bit-exact, decode attention within 1e-3."""
+    pair = WPair(seed=21, n_layers=1, batch=8, n_kv_heads=8, n_q_heads=32, head_dim=128, bits=8,
+                 capacity=4096 + 64)
+    pair.push(0, 4096, False)
+    pair.compare_bytes(0)
+    err = pair.compare_attention(0, 1)
+    for i in range(3):
+        pair.push(0, 1, False)
+    pair.compare_bytes(0)
+    err = max(err, pair.compare_attention(0, 2))
+    _log(f"[whole bench size] P={pair.model.P[0]}: bytes exact, attention rel err {err:.2e}")
