@@ -489,7 +489,7 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
     pa.part = (float*)ws;
     const int nrb = prefill_row_blocks(pa);
     const int streams = cf.batch * cf.n_kv_heads;
-    const int want = std::max(1, (2048 + streams - 1) / streams);  // ~2048 workgroups
+    const int want = std::max(1, (2048 + streams - 1) / streams);  // ~2048 workgroups (1024: 147 us, 4096: 155 us)
     pa.splits = std::max(1, std::min({ROPE_MAX_SPLITS, want, nrb}));
     hipError_t e = launch_prefill(pa, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode (RoPE) launch");

@@ -136,7 +136,14 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         int cq, ch;
         const bool cok = col_query(tt, col, &cq, &ch);
         float y0 = 0.f, y1 = 0.f;
-        if (cok && 2 * lane < D) {
+        if (!cok) {  // a padding column (uniform over the wave): zeros, nothing to turn
+          if (2 * lane < D) {
+            qs[col * D + 2 * lane] = 0.f;
+            qs[col * D + 2 * lane + 1] = 0.f;
+          }
+          continue;
+        }
+        if (2 * lane < D) {
           const uint32_t w =
               reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + (((int64_t)b * sh.Hq + ch) * a.n + cq) * D)[lane];
           y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
@@ -214,6 +221,10 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   // split over row blocks (decode-sized calls): this workgroup reads row blocks [rb_lo, rb_hi)
   const int split = blockIdx.z;
   const int rb_lo = (int)((int64_t)nrb * split / a.splits), rb_hi = (int)((int64_t)nrb * (split + 1) / a.splits);
+  bool anyq = false;
+#pragma unroll
+  for (int tt = 0; tt < PT; ++tt) anyq = anyq || qpos[tt] >= 0;
+  const bool live = __any(anyq);
   for (int rb = rb_lo; rb < rb_hi; ++rb) {
     __syncthreads();  // the previous row block is consumed
     // ---- stage the row block: thread (row t, channel slice) for K; chunk-wise for V ----
@@ -434,6 +445,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
     }
 
     // ---- the wave's tiles against the row block: every LDS operand read feeds all tiles ----
+    if (!live) continue;  // a wave without queries (a short chunk) only helps to stage
     f4 c[PT][2];
 #pragma unroll
     for (int tt = 0; tt < PT; ++tt) c[tt][0] = c[tt][1] = f4{0.f, 0.f, 0.f, 0.f};
@@ -558,16 +570,21 @@ __global__ __launch_bounds__(D) void k_prefill_merge(PrefillArgs a) {
   const int64_t idx = blockIdx.x;  // (b * Hq + head) * n + query
   const int c = threadIdx.x;
   const float* base = a.part + idx * a.splits * (D + 4);
+  __shared__ float sm[64], sl[64], sw[64];  // splits <= 64: every split's (m, l) loaded at once
+  for (int sp = c; sp < a.splits; sp += D) {
+    sm[sp] = base[sp * (D + 4) + D];
+    sl[sp] = base[sp * (D + 4) + D + 1];
+  }
+  __syncthreads();
   float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, base[sp * (D + 4) + D]);
+  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, sm[sp]);
+  for (int sp = c; sp < a.splits; sp += D) sw[sp] = sm[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[sp] - M);
+  __syncthreads();
   float av = 0.f, lv = 0.f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < a.splits; ++sp) {
-      const float ms = base[sp * (D + 4) + D];
-      const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-      av = av + base[sp * (D + 4) + c] * w;
-      lv = lv + base[sp * (D + 4) + D + 1] * w;
-    }
+#pragma unroll 8
+  for (int sp = 0; sp < a.splits; ++sp) {
+    av = av + base[sp * (D + 4) + c] * sw[sp];
+    lv = lv + sl[sp] * sw[sp];
   }
   a.out[idx * D + c] = lv > 0.f ? av / lv : 0.f;
 }
