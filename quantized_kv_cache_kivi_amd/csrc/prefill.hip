@@ -433,8 +433,9 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         const int ri = cache_index(S.spos, nsink, a.lo, p);
         const float x0 = (float)S.khi[t][c] + (float)S.klo[t][c];
         const float x1 = (float)S.khi[t][c + H] + (float)S.klo[t][c + H];
-        const float y0 = rope_val(x0, x1, c, D, ri, lv.tables->rope_inv);
-        const float y1 = rope_val(x1, x0, c + H, D, ri, lv.tables->rope_inv);
+        float sn, cs;  // one angle per pair: both channels turn by idx * theta_c
+        sincosf((float)ri * lv.tables->rope_inv[c], &sn, &cs);
+        const float y0 = x0 * cs - x1 * sn, y1 = x1 * cs + x0 * sn;
         const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
         S.khi[t][c] = h0;
         S.klo[t][c] = (_Float16)(y0 - (float)h0);
