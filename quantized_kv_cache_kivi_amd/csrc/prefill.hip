@@ -53,7 +53,7 @@ struct PfSmem {
   float kcen[16], vcen[16];  // TurboQuant centroids (rotated domain)
 };
 
-template <int FMT, int KB, int VB, int D, bool RP>
+template <int FMT, int KB, int VB, int D, bool RP, int PTT>
 __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   // TurboQuant works in the rotated domain ("TurboQuant KV Cache Compression — Spec", "Optimization:
   // Fused dequant-dot"): queries rotated once (fp16 hi + lo, a third score product), bulk rows are
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   // index in the compressed cache; the turned queries are fp16 hi + lo pairs like TurboQuant's
   constexpr bool TQ = FMT == KVQ_FMT_TQ;
   constexpr bool SQ = TQ || RP;            // queries split into fp16 hi + lo (third score product)
-  constexpr int PT = SQ ? 1 : ::kvq::PT;  // column tiles per wave
+  constexpr int PT = PTT;  // column tiles per wave
   constexpr int NST = D / 32, NMU = D / 16, NG = D / 32;
   constexpr int VPW = 32 / VB, WPC = D * VB / 64;
   const Shape sh = a.sh;
@@ -590,15 +590,34 @@ __global__ __launch_bounds__(D) void k_prefill_merge(PrefillArgs a) {
   a.out[idx * D + c] = lv > 0.f ? av / lv : 0.f;
 }
 
-template <int FMT, int KB, int VB, bool RP>
-hipError_t launch_dr(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+// Column tiles per wave: TurboQuant 1 (the rotated queries' lo halves take a second tile's
+// registers); RoPE 1 for short chunks (a decode query: fewer idle columns, more waves per SIMD) and 2
+// for long ones; otherwise 2.
+int tiles_per_wave(const PrefillArgs& a) {
+  if (a.sh.fmt == KVQ_FMT_TQ) return 1;
+  if (a.sh.rope && a.n < 256) return 1;
+  return PT;
+}
+
+template <int FMT, int KB, int VB, bool RP, int PTT>
+hipError_t launch_drp(const PrefillArgs& a, hipStream_t st) {
+  const int QT = PNW * PTT * (16 / (a.sh.Hq / a.sh.Hkv));
+  const dim3 grid((a.n + QT - 1) / QT, a.sh.B * a.sh.Hkv, a.splits > 1 ? a.splits : 1);
   switch (a.sh.D) {
-    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, RP>), grid, dim3(PNT), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, RP>), grid, dim3(PNT), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, RP>), grid, dim3(PNT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, RP, PTT>), grid, dim3(PNT), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, RP, PTT>), grid, dim3(PNT), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, RP, PTT>), grid, dim3(PNT), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
+  return hipGetLastError();
+}
+
+template <int FMT, int KB, int VB, bool RP>
+hipError_t launch_dr(const PrefillArgs& a, hipStream_t st) {
+  hipError_t e;
+  if constexpr (FMT == KVQ_FMT_TQ) e = launch_drp<FMT, KB, VB, RP, 1>(a, st);
+  else if constexpr (RP) e = tiles_per_wave(a) == 1 ? launch_drp<FMT, KB, VB, RP, 1>(a, st) : launch_drp<FMT, KB, VB, RP, PT>(a, st);
+  else e = launch_drp<FMT, KB, VB, RP, PT>(a, st);
   if (e != hipSuccess || a.splits <= 1) return e;
   const dim3 mg((unsigned)((int64_t)a.sh.B * a.sh.Hq * a.n));
   switch (a.sh.D) {
@@ -609,24 +628,25 @@ hipError_t launch_dr(const PrefillArgs& a, dim3 grid, hipStream_t st) {
   return hipGetLastError();
 }
 template <int FMT, int KB, int VB>
-hipError_t launch_d(const PrefillArgs& a, dim3 grid, hipStream_t st) {
-  if constexpr (FMT == KVQ_FMT_TQ) return launch_dr<FMT, KB, VB, false>(a, grid, st);  // no RoPE with TQ
-  else return a.sh.rope ? launch_dr<FMT, KB, VB, true>(a, grid, st) : launch_dr<FMT, KB, VB, false>(a, grid, st);
+hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
+  if constexpr (FMT == KVQ_FMT_TQ) return launch_dr<FMT, KB, VB, false>(a, st);  // no RoPE with TQ
+  else return a.sh.rope ? launch_dr<FMT, KB, VB, true>(a, st) : launch_dr<FMT, KB, VB, false>(a, st);
 }
 template <int KB>
-hipError_t launch_kivi(const PrefillArgs& a, dim3 grid, hipStream_t st) {
+hipError_t launch_kivi(const PrefillArgs& a, hipStream_t st) {
   switch (a.sh.vb) {
-    case 2: return launch_d<KVQ_FMT_KIVI, KB, 2>(a, grid, st);
-    case 4: return launch_d<KVQ_FMT_KIVI, KB, 4>(a, grid, st);
-    case 8: return launch_d<KVQ_FMT_KIVI, KB, 8>(a, grid, st);
+    case 2: return launch_d<KVQ_FMT_KIVI, KB, 2>(a, st);
+    case 4: return launch_d<KVQ_FMT_KIVI, KB, 4>(a, st);
+    case 8: return launch_d<KVQ_FMT_KIVI, KB, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int prefill_queries_per_tile(int r, int fmt, int rope) {
-  return PNW * (fmt == KVQ_FMT_TQ || rope ? 1 : PT) * (16 / r);
+int prefill_queries_per_tile(int r, int fmt, int rope) {  // (long chunks)
+  (void)rope;
+  return PNW * (fmt == KVQ_FMT_TQ ? 1 : PT) * (16 / r);
 }
 
 int prefill_row_blocks(const PrefillArgs& a) {
@@ -638,28 +658,26 @@ int prefill_row_blocks(const PrefillArgs& a) {
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
-  const int QT = prefill_queries_per_tile(sh.Hq / sh.Hkv, sh.fmt, sh.rope);
   if (a.splits > 1 && (sh.fmt == KVQ_FMT_TQ || !a.part)) return hipErrorInvalidValue;
-  const dim3 grid((a.n + QT - 1) / QT, sh.B * sh.Hkv, a.splits > 1 ? a.splits : 1);
-  if (sh.fmt == KVQ_FMT_Q2K) return launch_d<KVQ_FMT_Q2K, 2, 4>(a, grid, st);
+  if (sh.fmt == KVQ_FMT_Q2K) return launch_d<KVQ_FMT_Q2K, 2, 4>(a, st);
   if (sh.fmt == KVQ_FMT_TQ) {
-    if (sh.kb == 4 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 4, 2>(a, grid, st);
-    if (sh.kb == 2 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 2, 2>(a, grid, st);
-    if (sh.kb == 4 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 4, 4>(a, grid, st);
-    if (sh.kb == 2 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 2, 4>(a, grid, st);
+    if (sh.kb == 4 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 4, 2>(a, st);
+    if (sh.kb == 2 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 2, 2>(a, st);
+    if (sh.kb == 4 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 4, 4>(a, st);
+    if (sh.kb == 2 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 2, 4>(a, st);
     // dense 3-bit streams
-    if (sh.kb == 3 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 3, 2>(a, grid, st);
-    if (sh.kb == 3 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 3, 3>(a, grid, st);
-    if (sh.kb == 3 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 3, 4>(a, grid, st);
-    if (sh.kb == 2 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 2, 3>(a, grid, st);
-    if (sh.kb == 4 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 4, 3>(a, grid, st);
+    if (sh.kb == 3 && sh.vb == 2) return launch_d<KVQ_FMT_TQ, 3, 2>(a, st);
+    if (sh.kb == 3 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 3, 3>(a, st);
+    if (sh.kb == 3 && sh.vb == 4) return launch_d<KVQ_FMT_TQ, 3, 4>(a, st);
+    if (sh.kb == 2 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 2, 3>(a, st);
+    if (sh.kb == 4 && sh.vb == 3) return launch_d<KVQ_FMT_TQ, 4, 3>(a, st);
     return hipErrorInvalidValue;
   }
   if (sh.fmt != KVQ_FMT_KIVI) return hipErrorInvalidValue;
   switch (sh.kb) {
-    case 2: return launch_kivi<2>(a, grid, st);
-    case 4: return launch_kivi<4>(a, grid, st);
-    case 8: return launch_kivi<8>(a, grid, st);
+    case 2: return launch_kivi<2>(a, st);
+    case 4: return launch_kivi<4>(a, st);
+    case 8: return launch_kivi<8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,7 +6,8 @@ LDS, queries as fp16 hi + lo pairs) turn them by their index in the compressed c
 over (b, query head[, query]) of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3.  Cases: KIVI-2, KIVI-4,
 KIVI-8 and q2k; head_dim 32, 64, 128; GQA 1, 2, 4, 8; top-k and first-N sinks; an evicting window
 (indices re-packed after eviction) and no eviction (indices = positions); fp16 and fp32 input;
-a RoPE base other than the default.  Storage is unchanged by the flag (bytes compared once).
+a RoPE base other than the default; chunks below and above 256 rows (one and two column tiles per
+wave in the prefill kernel).  Storage is unchanged by the flag (bytes compared once).
 """
 import numpy as np
 import pytest
@@ -29,7 +30,7 @@ CASES = {
                                            k_bits=4, v_bits=4, sink_mode="first_n", n_sink=2, window=40, residual=8,
                                            in_dtype="f32", rope=True, rope_base=500000.0), [60, 20, 1, 1, 1]),
     "kivi8_d32_r1_plain_positions": (dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="kivi",
-                                          k_bits=8, v_bits=8, capacity=256, rope=True), [100, 1, 45]),
+                                          k_bits=8, v_bits=8, capacity=512, rope=True), [300, 1, 45]),
 }
 
 
