@@ -185,14 +185,15 @@ def prefill_attention_figure(kw, cache, P, sinks_per_b, seed, dev, stream, max_f
     its prefill: median of three calls (HIP timing events) against the fp16 matrix-core peak."""
     import torch
     from quantized_kv_cache_kivi_amd import synth
-    if P == 0 or kw.get("in_dtype") == "f32":
+    if P == 0:
         return None
     n = min(4096, P)
     _, lo = cache.kvq_get_state(0)
     flops = prefill_attention_flops(kw, P, lo, n, sinks_per_b)
     if flops > max_flops:
         return {"skipped": f"{flops / 1e12:.0f} TFLOP per call exceeds the bench budget"}
-    q = synth.normal((kw["batch"], kw["n_q_heads"], n, kw["head_dim"]), seed, 60_000, dev).half().contiguous()
+    qdt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
+    q = synth.normal((kw["batch"], kw["n_q_heads"], n, kw["head_dim"]), seed, 60_000, dev).to(qdt).contiguous()
     out = torch.empty((kw["batch"], kw["n_q_heads"], n, kw["head_dim"]), dtype=torch.float32, device=dev)
     cache.kvq_prefill_attn(0, q, out)
     ts = []
@@ -459,13 +460,14 @@ def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, b
                 break
         # causal prefill attention of the same model: a few queries of one query head per KV head
         extra = {}
-        if prefill_k.shape[2] > 0 and kw.get("in_dtype") != "f32":
+        if prefill_k.shape[2] > 0:
             import torch
             from quantized_kv_cache_kivi_amd import synth
             P = m.P[0]
             nq = 8
             heads = list(range(0, kw["n_q_heads"], kw["n_q_heads"] // kw["n_kv_heads"]))
-            qp = synth.normal((1, kw["n_q_heads"], nq, kw["head_dim"]), 7, 62_000).to(torch.float16).numpy()
+            qdt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
+            qp = synth.normal((1, kw["n_q_heads"], nq, kw["head_dim"]), 7, 62_000).to(qdt).numpy()
             t1 = time.perf_counter()
             oattn.prefill_attention(m, 0, qp, heads=heads)
             tp = time.perf_counter() - t1

@@ -206,13 +206,14 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
  * step after append in prefill: [Q2K] "Summary" reads prefill through the
  * same q2k cache; [TQ] "API" attention over the cached rows).  q: the
  * queries of the last n appended positions P-n .. P-1, [batch][n_q_heads][n]
- * [head_dim] fp16, 16-byte aligned; out: [batch][n_q_heads][n][head_dim]
+ * [head_dim] in_dtype, 16-byte aligned; out: [batch][n_q_heads][n][head_dim]
  * fp32, 16-byte aligned.  Query i attends the valid positions p <= P-n+i
  * (sinks, window, bulk; the same values decode attention reads) with
  * softmax(scale * q . k) weights; a query with no such position gets zeros.
  * scale <= 0 means 1/sqrt(head_dim).  Every cache format (TurboQuant in the
- * rotated domain: queries rotated once, outputs rotated back); fp16 input
- * caches only, head_dim 32, 64 or 128 (else KVQ_EINVAL); 1 <= n <= P (else
+ * rotated domain: queries rotated once, outputs rotated back); fp32
+ * queries enter the matrix cores as fp16 hi + lo pairs; head_dim 32, 64 or
+ * 128 (else KVQ_EINVAL); 1 <= n <= P (else
  * KVQ_ERANGE).  One kernel launch, no workspace; deterministic. */
 kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t n, float* out, float scale,
                             void* stream);

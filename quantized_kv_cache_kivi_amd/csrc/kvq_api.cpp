@@ -524,7 +524,6 @@ kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t 
   if (n < 1 || n > P)
     return fail(KVQ_ERANGE, "prefill attention of n=%d queries needs 1 <= n <= P=%lld (the last n positions)", n,
                 (long long)P);
-  if (cf.in_dtype != KVQ_IN_F16) return fail(KVQ_EINVAL, "prefill attention needs fp16 queries");
   if (cf.head_dim != 32 && cf.head_dim != 64 && cf.head_dim != 128)
     return fail(KVQ_EINVAL, "prefill attention needs head_dim 32, 64 or 128");
   if ((uintptr_t)q % 16 != 0 || (uintptr_t)out % 16 != 0) return fail(KVQ_EINVAL, "q and out must be 16-byte aligned");

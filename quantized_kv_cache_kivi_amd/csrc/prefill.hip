@@ -53,15 +53,16 @@ struct PfSmem {
   float kcen[16], vcen[16];  // TurboQuant centroids (rotated domain)
 };
 
-template <int FMT, int KB, int VB, int D, bool RP, int PTT>
+template <int FMT, int KB, int VB, int D, bool LQ, int PTT>
 __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
   // TurboQuant works in the rotated domain ("TurboQuant KV Cache Compression — Spec", "Optimization:
   // Fused dequant-dot"): queries rotated once (fp16 hi + lo, a third score product), bulk rows are
   // norm times centroid, fp16 window and sink rows are rotated while staged, outputs rotated back
   // RoPE on read ("StreamingLLM + KIVI", "RoPE caveat"): queries and staged keys turn by their
-  // index in the compressed cache; the turned queries are fp16 hi + lo pairs like TurboQuant's
+  // index in the compressed cache; the turned queries are fp16 hi + lo pairs like TurboQuant's.
+  // LQ: queries staged through LDS as fp16 hi + lo, for RoPE (sh.rope) or fp32 queries (sh.in_f32).
   constexpr bool TQ = FMT == KVQ_FMT_TQ;
-  constexpr bool SQ = TQ || RP;            // queries split into fp16 hi + lo (third score product)
+  constexpr bool SQ = TQ || LQ;            // queries split into fp16 hi + lo (third score product)
   constexpr int PT = PTT;  // column tiles per wave
   constexpr int NST = D / 32, NMU = D / 16, NG = D / 32;
   constexpr int VPW = 32 / VB, WPC = D * VB / 64;
@@ -144,10 +145,16 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
           continue;
         }
         if (2 * lane < D) {
-          const uint32_t w =
-              reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + (((int64_t)b * sh.Hq + ch) * a.n + cq) * D)[lane];
-          y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-          y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+          const int64_t qrow = (((int64_t)b * sh.Hq + ch) * a.n + cq) * D;
+          if (sh.in_f32) {
+            const float2 w = reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qrow)[lane];
+            y0 = w.x;
+            y1 = w.y;
+          } else {
+            const uint32_t w = reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow)[lane];
+            y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+            y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+          }
         }
         if constexpr (TQ) {
           y0 *= sg0;
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
           wave_fwht(y0, y1, D, lane);
           y0 *= cd;
           y1 *= cd;
-        } else {  // RoPE: channel 2l pairs with 2l + D/2, held by lane l ^ (D/4)
+        } else if (sh.rope) {  // RoPE: channel 2l pairs with 2l + D/2, held by lane l ^ (D/4)
           const float p0 = __shfl_xor(y0, D / 4), p1 = __shfl_xor(y1, D / 4);
           const int qi = cache_index(S.spos, S.nsink, a.lo, pbase + cq);
           const float r0 = rope_val(y0, p0, 2 * lane, D, qi, lv.tables->rope_inv);
@@ -424,7 +431,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
       }
     }
     __syncthreads();
-    if constexpr (RP) {  // the staged keys turn by their rows' indices in the compressed cache
+    if (LQ && sh.rope) {  // the staged keys turn by their rows' indices in the compressed cache
       constexpr int H = D / 2;
       for (int idx = tid; idx < G * H; idx += PNT) {
         const int t = idx / H, c = idx % H;
@@ -591,33 +598,33 @@ __global__ __launch_bounds__(D) void k_prefill_merge(PrefillArgs a) {
 }
 
 // Column tiles per wave: TurboQuant 1 (the rotated queries' lo halves take a second tile's
-// registers); RoPE 1 for short chunks (a decode query: fewer idle columns, more waves per SIMD) and 2
-// for long ones; otherwise 2.
+// registers); queries staged through LDS (RoPE, fp32) 1 for short chunks (a decode query: fewer idle
+// columns, more waves per SIMD) and 2 for long ones; otherwise 2.
 int tiles_per_wave(const PrefillArgs& a) {
   if (a.sh.fmt == KVQ_FMT_TQ) return 1;
-  if (a.sh.rope && a.n < 256) return 1;
+  if ((a.sh.rope || a.sh.in_f32) && a.n < 256) return 1;
   return PT;
 }
 
-template <int FMT, int KB, int VB, bool RP, int PTT>
+template <int FMT, int KB, int VB, bool LQ, int PTT>
 hipError_t launch_drp(const PrefillArgs& a, hipStream_t st) {
   const int QT = PNW * PTT * (16 / (a.sh.Hq / a.sh.Hkv));
   const dim3 grid((a.n + QT - 1) / QT, a.sh.B * a.sh.Hkv, a.splits > 1 ? a.splits : 1);
   switch (a.sh.D) {
-    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, RP, PTT>), grid, dim3(PNT), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, RP, PTT>), grid, dim3(PNT), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, RP, PTT>), grid, dim3(PNT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, LQ, PTT>), grid, dim3(PNT), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, LQ, PTT>), grid, dim3(PNT), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, LQ, PTT>), grid, dim3(PNT), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, int KB, int VB, bool RP>
+template <int FMT, int KB, int VB, bool LQ>
 hipError_t launch_dr(const PrefillArgs& a, hipStream_t st) {
   hipError_t e;
-  if constexpr (FMT == KVQ_FMT_TQ) e = launch_drp<FMT, KB, VB, RP, 1>(a, st);
-  else if constexpr (RP) e = tiles_per_wave(a) == 1 ? launch_drp<FMT, KB, VB, RP, 1>(a, st) : launch_drp<FMT, KB, VB, RP, PT>(a, st);
-  else e = launch_drp<FMT, KB, VB, RP, PT>(a, st);
+  if constexpr (FMT == KVQ_FMT_TQ) e = launch_drp<FMT, KB, VB, LQ, 1>(a, st);
+  else if constexpr (LQ) e = tiles_per_wave(a) == 1 ? launch_drp<FMT, KB, VB, LQ, 1>(a, st) : launch_drp<FMT, KB, VB, LQ, PT>(a, st);
+  else e = launch_drp<FMT, KB, VB, LQ, PT>(a, st);
   if (e != hipSuccess || a.splits <= 1) return e;
   const dim3 mg((unsigned)((int64_t)a.sh.B * a.sh.Hq * a.n));
   switch (a.sh.D) {
@@ -629,8 +636,10 @@ hipError_t launch_dr(const PrefillArgs& a, hipStream_t st) {
 }
 template <int FMT, int KB, int VB>
 hipError_t launch_d(const PrefillArgs& a, hipStream_t st) {
-  if constexpr (FMT == KVQ_FMT_TQ) return launch_dr<FMT, KB, VB, false>(a, st);  // no RoPE with TQ
-  else return a.sh.rope ? launch_dr<FMT, KB, VB, true>(a, st) : launch_dr<FMT, KB, VB, false>(a, st);
+  // TurboQuant stages its queries through LDS already (and has no RoPE); the block formats take the
+  // LDS query prologue for RoPE or fp32 queries
+  if constexpr (FMT == KVQ_FMT_TQ) return launch_dr<FMT, KB, VB, false>(a, st);
+  else return a.sh.rope || a.sh.in_f32 ? launch_dr<FMT, KB, VB, true>(a, st) : launch_dr<FMT, KB, VB, false>(a, st);
 }
 template <int KB>
 hipError_t launch_kivi(const PrefillArgs& a, hipStream_t st) {

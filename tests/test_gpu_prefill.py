@@ -47,6 +47,17 @@ CASES = {
                                v_bits=2, residual=0, capacity=1024, tq_dense3=True), [70, 33]),
     "tq24_r8_firstn": (dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=8, head_dim=128, fmt="tq", k_bits=2,
                             v_bits=4, sink_mode="first_n", n_sink=4, residual=40, capacity=1024), [200, 7]),
+    # fp32 input: queries staged through LDS as fp16 hi + lo
+    "kivi2_r4_topk_f32": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="kivi", k_bits=2,
+                               v_bits=2, sink_mode="topk", n_sink=3, residual=16, capacity=1024, in_dtype="f32"),
+                          [70, 300, 1, 33]),
+    "kivi8_r1_d32_f32_ring": (dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="kivi", k_bits=8,
+                                   v_bits=8, sink_mode="first_n", n_sink=2, window=64, residual=8, in_dtype="f32"),
+                              [60, 20, 33]),
+    "q2k_r2_d64_f32": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="q2k", k_bits=2,
+                            v_bits=4, residual=40, capacity=1024, in_dtype="f32"), [100, 7]),
+    "tq42_r4_f32": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=4, v_bits=2,
+                         sink_mode="first_n", n_sink=2, residual=16, capacity=1024, in_dtype="f32"), [90, 20]),
 }
 
 
@@ -56,7 +67,8 @@ def _log(*a):
 
 def _check(pair, n, seed):
     c = pair.ocfg
-    q = synth.normal((c.batch, c.n_q_heads, n, c.head_dim), pair.seed, 70_000 + seed, "cuda").half().contiguous()
+    q = synth.normal((c.batch, c.n_q_heads, n, c.head_dim), pair.seed, 70_000 + seed, "cuda")
+    q = (q.float() if c.in_dtype == "f32" else q.half()).contiguous()
     out = torch.full((c.batch, c.n_q_heads, n, c.head_dim), float("nan"), dtype=torch.float32, device="cuda")
     pair.gpu.kvq_prefill_attn(0, q, out)
     torch.cuda.synchronize()

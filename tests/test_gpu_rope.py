@@ -40,7 +40,7 @@ def _log(*a):
 
 def _prefill_err(pair, n, tag):
     c = pair.ocfg
-    q = synth.normal((c.batch, c.n_q_heads, n, c.head_dim), pair.seed, 71_000 + tag, "cuda").half().contiguous()
+    q = synth.normal((c.batch, c.n_q_heads, n, c.head_dim), pair.seed, 71_000 + tag, "cuda").to(pair.tdtype).contiguous()
     out = torch.full((c.batch, c.n_q_heads, n, c.head_dim), float("nan"), dtype=torch.float32, device="cuda")
     pair.gpu.kvq_prefill_attn(0, q, out)
     torch.cuda.synchronize()
@@ -63,8 +63,7 @@ def test_rope_decode_and_prefill(name):
         pair.push(0, n)
         err, _ = pair.compare_attention(0)
         worst_d = max(worst_d, err)
-        if kw.get("in_dtype", "f16") == "f16":  # prefill attention takes fp16 queries
-            worst_p = max(worst_p, _prefill_err(pair, n, step))
+        worst_p = max(worst_p, _prefill_err(pair, n, step))
         if step == 0:
             assert pair.compare_bytes(0) > 0
         _log(f"[{name}] step {step} n={n} P={pair.model.P[0]}: decode {err:.2e}, prefill worst {worst_p:.2e}")
