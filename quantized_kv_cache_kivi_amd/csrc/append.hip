@@ -654,37 +654,36 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
     vm[mi] = tid < tend ? vms[tid] : 0;
     if constexpr (!Q2K) vm[G * ng + mi] = tid < tend ? vmz[tid] : 0;
   }
-  // 7. staging of an open block (raw K input rows)
-  if (tend < G) {
-    for (int t = tnew0 + rg; t < tend; t += RGS) {
-      const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
+  // 7-9. the new rows' raw copies, from the values this thread loaded in the first phase (its rows
+  //      rg + RGS i; fp16 input round-trips through fp32 exactly): staging of an open block, the
+  //      fp16 window ring (rows p in [max(P, P+n-R), P+n)) and the fp16 sink pool
+  const int64_t wlo = (a.P + a.n - sh.R) > a.P ? (a.P + a.n - sh.R) : a.P;
+#pragma unroll
+  for (int i = 0; i < PR; ++i) {
+    const int t = rg + RGS * i;
+    if (t < tnew0 || t >= tend) continue;
+    const int64_t p = base + t;
+    const uint16_t k16 = f16_bits(kx[i]), v16 = f16_bits(vx[i]);
+    if (tend < G) {
       const int64_t so = ((int64_t)s * G + t) * D + c;
-      if (sh.in_f32) reinterpret_cast<float*>(lv.staging)[so] = static_cast<const float*>(a.k)[gi];
-      else reinterpret_cast<uint16_t*>(lv.staging)[so] = static_cast<const uint16_t*>(a.k)[gi];
+      if (sh.in_f32) reinterpret_cast<float*>(lv.staging)[so] = kx[i];
+      else reinterpret_cast<uint16_t*>(lv.staging)[so] = k16;
     }
-  }
-  // 8. fp16 window ring: rows p in [max(P, P+n-R), P+n)
-  if (sh.R > 0) {
-    const int64_t wlo = (a.P + a.n - sh.R) > a.P ? (a.P + a.n - sh.R) : a.P;
-    for (int t = tnew0 + rg; t < tend; t += RGS) {
-      const int64_t p = base + t;
-      if (p < wlo) continue;
-      const int64_t gi = (in_row0 + (p - a.P)) * D + c;
+    if (sh.R > 0 && p >= wlo) {
       const int64_t wo = ((int64_t)s * sh.R + p % sh.R) * D + c;
-      lv.win_k[wo] = ld_in_f16(a.k, gi, sh.in_f32);
-      lv.win_v[wo] = ld_in_f16(a.v, gi, sh.in_f32);
+      lv.win_k[wo] = k16;
+      lv.win_v[wo] = v16;
+    }
+    if (sh.n_sink > 0) {
+      const int slot = sink_slot[t];
+      if (slot >= 0) {
+        const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + c;
+        lv.sink_k[so] = k16;
+        lv.sink_v[so] = v16;
+      }
     }
   }
-  // 9. fp16 sink pool
   if (sh.n_sink > 0) {
-    for (int t = tnew0 + rg; t < tend; t += RGS) {
-      const int slot = sink_slot[t];
-      if (slot < 0) continue;
-      const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
-      const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + c;
-      lv.sink_k[so] = ld_in_f16(a.k, gi, sh.in_f32);
-      lv.sink_v[so] = ld_in_f16(a.v, gi, sh.in_f32);
-    }
     // first-N commits: positions and count, by one workgroup per batch element
     if (sh.sink_mode == KVQ_SINK_FIRST_N && h == 0 && blockIdx.x == 0 && grp == 0) {
       const int64_t P1 = a.P + a.n;
