@@ -10,9 +10,12 @@ Counts per (layer, b) are taken by enumerating the valid positions and their
 read source, never from a formula, so the partition pin is independent of the
 library's arithmetic.
 
-Parity: pinned by enumeration and by the page figures of the q2k page
-("Memory math": 448 B per cell at 2 x 256 channels) in
-tests/test_oracle_cache.py.
+Parity: pinned by hand-counted cases (KIVI and q2k with partially evicted
+blocks, top-k sinks inside blocks, a block whose valid rows are all sinks, a
+window covering every valid row, TurboQuant after eviction) and by
+position-by-position enumeration in tests/test_oracle_accounting.py, and by the
+page figures of the q2k page ("Memory math": 448 B per cell at 2 x 256
+channels) in tests/test_oracle_q2k.py.
 """
 
 from .layout import record_sections, slot_bits

@@ -18,7 +18,12 @@ the fp32 formulas above rounded once to fp16.
 
 Parity: pinned by brute force on hand-sized caches (one token gives o = v;
 equal keys give the mean of V; two tokens give a sigmoid weight) and by the
-rotated-domain identity q . R^T k = (R q) . k in tests/test_oracle_attention.py.
+rotated-domain identity q . R^T k = (R q) . k in tests/test_oracle_attention.py;
+the cache-level dequantization (``stream_values``, both paths) by on-grid rows
+of every format appended across blocks, sinks, an evicting window and a
+wrapping ring, which must come back exactly (KIVI, q2k V), on their planted
+level times the block's fp16 RMS (q2k K) or as |c[u]| times the row
+(TurboQuant, fp64 inverse) in tests/test_oracle_cache_grid.py.
 """
 
 import numpy as np

@@ -160,10 +160,14 @@ kvq_layout make_layout(const kvq_config& c) {
   return L;
 }
 
-// Shapes the MFMA decode path covers (the generic kernel takes the rest).
+// Shapes the MFMA decode path covers (the generic kernel takes the rest).  The MFMA kernel reads a
+// stream's ring through a buffer resource with 32-bit record offsets and a 31-bit size, so a ring of
+// 2 GiB or more per stream goes to the generic kernel, which addresses with 64-bit pointers.
 bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
-  return c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope && (r == 1 || r == 2 || r == 4 || r == 8) &&
+  const uint64_t ring = (uint64_t)(effective_capacity(c) / G) * record_sections(c).rec;
+  return ring < (uint64_t(1) << 31) && c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope &&
+         (r == 1 || r == 2 || r == 4 || r == 8) &&
          (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits) ||
           (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || (c.k_bits == 3 && !c.tq_dense3)) && c.v_bits == 2));
 }

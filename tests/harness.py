@@ -5,6 +5,8 @@ as the same buffers (the oracle gets a host copy of exactly what the library
 read).  Nothing here computes any step of the method.
 """
 
+import zlib
+
 import numpy as np
 import torch
 
@@ -13,6 +15,12 @@ from oracle import cache as ocache
 from quantized_kv_cache_kivi_amd import synth
 
 TOL_ATTN = 1e-3  # max over (b, j) of ||o_gpu - o_ref||_inf / ||o_ref||_inf
+
+
+def stable_seed(name, mod=1000):
+    """Data seed of a named case: a CRC-32 of the name, the same in every process (Python's str hash is
+    salted per process, so a seed taken from it would not reproduce a failure)."""
+    return zlib.crc32(name.encode()) % mod
 
 
 def rel_attn_err(out_gpu, out_ref):

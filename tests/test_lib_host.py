@@ -137,3 +137,21 @@ def test_dense_three_bit_config_and_layout(kvq):
     for bad in (kvq.make_config(1, 2, 2, 8, 128, "tq", 4, 2, capacity=64, tq_dense3=True),
                 kvq.make_config(1, 2, 2, 8, 128, "kivi", 2, 2, capacity=64, tq_dense3=True)):
         assert kvq.config_check(bad) == -1 and "tq_dense3" in kvq.last_error()
+
+
+def test_rings_of_two_gib_or_more_leave_the_matrix_core_decode(kvq):
+    """The matrix-core decode kernel reads a stream's ring with 32-bit buffer offsets; a ring of 2 GiB or
+    more per stream is decoded by the generic kernel (64-bit addressing).  The two kernels size their
+    split partials differently (at 512 streams: up to 64 splits against 4), which shows the routing."""
+    rec = olayout.record_sections("kivi", 128, 8, 8)[2]
+    below = (2 ** 31 - 1) // rec          # largest ring (in blocks) under 2 GiB
+    above = below + 1
+    assert below * rec < 2 ** 31 <= above * rec
+    ws = {}
+    for name, blocks in (("below", below), ("above", above)):
+        cfg = kvq.make_config(1, 64, 8, 32, 128, "kivi", 8, 8, capacity=32 * blocks)
+        assert kvq.config_check(cfg) == 0
+        ws[name] = kvq.workspace_bytes(cfg)
+    per_part = 64 * 8 * 4 * (128 + 2) * 4
+    assert ws["below"] == (64 + 1) * per_part
+    assert ws["above"] == (4 + 1) * per_part
