@@ -202,6 +202,23 @@ kvq_status kvq_evict(kvq_cache* c, int32_t layer);
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Size of the static decode workspace kvq_decode_attn_nomalloc uses: 32 MiB of device memory per GPU,
+ * held from the library's first use on that GPU until the process ends. */
+#define KVQ_STATIC_WS_BYTES ((size_t)32 << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc): kvq_decode_attn with the split partials in a workspace the library
+ * holds in static device memory (KVQ_STATIC_WS_BYTES per GPU) instead of a caller's `ws`.  Same
+ * arguments, kernels and results as kvq_decode_attn; allocates nothing.  Run it with the cache's device
+ * current.  Fails with KVQ_ECAPACITY, launching nothing, when the call's split partials need more than
+ * KVQ_STATIC_WS_BYTES (streams x (splits + fp16-row groups) x (n_q_heads / n_kv_heads) x
+ * (head_dim + 2) x 4 bytes; with RoPE on read, batch x n_q_heads x splits x (head_dim + 4) x 4).
+ * Every call on one GPU shares that GPU's workspace: calls that overlap in time on one GPU (different
+ * streams, or different host threads without ordering) race and give wrong results.  Nothing in it
+ * needs clearing between calls (each call writes every partial it reads). */
+kvq_status kvq_decode_attn_nomalloc(kvq_cache* c, int32_t layer, const void* q, float* out, float scale,
+                                    void* stream);
+
 /* Causal multi-query attention of a prefill chunk over `layer` (the "next"
  * step after append in prefill: [Q2K] "Summary" reads prefill through the
  * same q2k cache; [TQ] "API" attention over the cached rows).  q: the

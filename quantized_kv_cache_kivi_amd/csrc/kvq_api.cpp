@@ -352,6 +352,11 @@ kvq_status kvq_create(const kvq_config* cfg, void* dev_buf, size_t dev_bytes, vo
   c->pend_n.assign(cfg->n_layers, -1);
   make_tables(c->cfg, &c->tables);
   c->slots = fast_path(c->cfg) ? fast_resident_slots(shape_of(c->cfg)) : 0;
+  st = static_ws_prepare();  // device address of the static decode workspace, once per device
+  if (st != KVQ_OK) {
+    delete c;
+    return st;
+  }
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipMemsetAsync(dev_buf, 0, lay.total, s);
   if (e != hipSuccess) {
@@ -455,9 +460,23 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
                            size_t ws_bytes, void* stream) {
   kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
-  if (!q || !out || !ws) return fail(KVQ_EINVAL, "q, out and ws must not be NULL");
   if (ws_bytes < kvq_workspace_bytes(&c->cfg)) return fail(KVQ_EINVAL, "ws_bytes too small");
+  return kvq::decode_attn_ws(c, layer, q, out, scale, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace kvq {
+
+// Decode attention with the split partials in ws (ws_bytes long): fails with KVQ_ECAPACITY, launching
+// nothing, if this call's partials do not fit.
+kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
+                          size_t ws_bytes, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!q || !out || !ws) return fail(KVQ_EINVAL, "q, out and ws must not be NULL");
   const kvq_config& cf = c->cfg;
+  const size_t streams = (size_t)cf.batch * cf.n_kv_heads, r = cf.n_q_heads / cf.n_kv_heads;
   const int64_t P = c->P[layer], lo = c->lo[layer];
   if (P == 0) return fail(KVQ_ERANGE, "layer %d is empty", layer);
   DecodeArgs a;
@@ -495,6 +514,9 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
     const int streams = cf.batch * cf.n_kv_heads;
     const int want = std::max(1, (2048 + streams - 1) / streams);  // ~2048 workgroups (1024: 147 us, 4096: 155 us)
     pa.splits = std::max(1, std::min({ROPE_MAX_SPLITS, want, nrb}));
+    const size_t need = streams * r * (size_t)pa.splits * (cf.head_dim + 4) * sizeof(float);
+    if (need > ws_bytes)
+      return fail(KVQ_ECAPACITY, "decode attention needs %zu workspace bytes; %zu given", need, ws_bytes);
     hipError_t e = launch_prefill(pa, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "decode (RoPE) launch");
     return KVQ_OK;
@@ -513,10 +535,17 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   }
   a.fast = fast_path(cf);
   a.nparts = a.splits + fparts;
+  const size_t need = streams * (size_t)std::max(1, a.nparts) * r * (cf.head_dim + 2) * sizeof(float);
+  if (need > ws_bytes)
+    return fail(KVQ_ECAPACITY, "decode attention needs %zu workspace bytes; %zu given", need, ws_bytes);
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;
 }
+
+}  // namespace kvq
+
+extern "C" {
 
 kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t n, float* out, float scale,
                             void* stream) {

@@ -129,4 +129,13 @@ void clear_error();
 // Host-side table generation (tables.cpp).
 void make_tables(const kvq_config& cfg, Tables* t);
 
+// Decode attention with its split partials in ws (ws_bytes device bytes); KVQ_ECAPACITY, with nothing
+// launched, when this call's partials need more.  Shared by kvq_decode_attn (caller's workspace) and
+// kvq_decode_attn_nomalloc (the library's static workspace).
+kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
+                          size_t ws_bytes, void* stream);
+// Takes the current device's address of the static decode workspace once per device (kvq_create
+// calls it so that the address is known before any allocation-free call).
+kvq_status static_ws_prepare();
+
 }  // namespace kvq

@@ -83,6 +83,7 @@ def _load():
         "kvq_append": (I32, [P, I32, P, P, I32, P]),
         "kvq_evict": (I32, [P, I32]),
         "kvq_decode_attn": (I32, [P, I32, P, P, F32, P, SZ, P]),
+        "kvq_decode_attn_nomalloc": (I32, [P, I32, P, P, F32, P]),
         "kvq_dequant": (I32, [P, I32, I32, I64, I32, P, P]),
         "kvq_prefill_attn": (I32, [P, I32, P, I32, P, F32, P]),
         "kvq_account": (I32, [P, I32, ctypes.POINTER(kvq_bytes), P]),
@@ -206,6 +207,10 @@ class Cache:
     def kvq_decode_attn(self, layer, q, out, scale=0.0):
         _check(_decode(self.handle, layer, q.data_ptr(), out.data_ptr(), scale, self._ws[0], self._ws[1],
                        _stream(self.dev)))
+
+    def kvq_decode_attn_nomalloc(self, layer, q, out, scale=0.0):
+        _check(lib.kvq_decode_attn_nomalloc(self.handle, layer, q.data_ptr(), out.data_ptr(), scale,
+                                            _stream(self.dev)))
 
     def kvq_prefill_attn(self, layer, q, out, scale=0.0):
         _check(lib.kvq_prefill_attn(self.handle, layer, _ptr(q), q.shape[2], _ptr(out), scale, _stream(self.dev)))
