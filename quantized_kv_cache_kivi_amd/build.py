@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.cpp", "tables.cpp", "append.hip", "select.hip", "decode.hip", "decode_fast.hip", "dequant.hip", "prefill.hip",
-           "kvqw_api.cpp", "whole.hip", "static_ws.hip"]
+           "kvqw_api.cpp", "whole.hip", "static_ws.hip", "stream_read.hip"]
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

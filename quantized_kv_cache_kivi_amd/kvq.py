@@ -84,6 +84,7 @@ def _load():
         "kvq_evict": (I32, [P, I32]),
         "kvq_decode_attn": (I32, [P, I32, P, P, F32, P, SZ, P]),
         "kvq_decode_attn_nomalloc": (I32, [P, I32, P, P, F32, P]),
+        "kvq_stream_read": (I32, [P, ctypes.c_uint64, P, P]),
         "kvq_dequant": (I32, [P, I32, I32, I64, I32, P, P]),
         "kvq_prefill_attn": (I32, [P, I32, P, I32, P, F32, P]),
         "kvq_account": (I32, [P, I32, ctypes.POINTER(kvq_bytes), P]),
@@ -157,6 +158,11 @@ def format_tables(cfg):
             "q2k_thr": (ctypes.c_float * 3)(), "q2k_lvl": (ctypes.c_float * 4)()}
     _check(lib.kvq_format_tables(ctypes.byref(cfg), *[ctypes.cast(b, ctypes.c_void_p) for b in bufs.values()]))
     return {k: list(v) for k, v in bufs.items()}
+
+
+def kvq_stream_read(buf, nbytes, out):
+    """Plain streaming read of the first nbytes of device tensor `buf` (include/kvq_bench.h)."""
+    _check(lib.kvq_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), _stream(buf.device.index)))
 
 
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)

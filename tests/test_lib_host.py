@@ -22,7 +22,8 @@ def kvq():
     return m
 
 
-@pytest.mark.parametrize("header,prefix,least", [("kvq.h", "kvq_", 15), ("kvq_whole.h", "kvqw_", 12)])
+@pytest.mark.parametrize("header,prefix,least", [("kvq.h", "kvq_", 15), ("kvq_whole.h", "kvqw_", 12),
+                                                 ("kvq_bench.h", "kvq_stream", 1)])
 def test_exports_every_declared_symbol(kvq, header, prefix, least):
     hdr = open(os.path.join(ROOT, "include", header)).read()
     names = sorted(set(re.findall(r"\b(" + prefix + r"[a-z_]+)\s*\(", hdr)))
