@@ -391,6 +391,94 @@ def rope_figure(cfgno, kw, pre_k, pre_v, sinks_per_b, seed, dev, stream):
     return res
 
 
+def decode_figure(cfgno, dev, stream, ncalls=40):
+    """Decode attention of one workload on its full-size cache, cold: the cache is replicated until the
+    replicas exceed 1 GB and consecutive calls read different replicas.  Reports the call's duration (HIP
+    events on its stream, median), algorithmic GB/s and the fraction of the 8 TB/s peak, and next to it a
+    plain streaming read (kvq_stream_read) of the same number of bytes from the same replicas: the
+    bandwidth this GPU delivers to a read of that size, and the decode call's fraction of it.  Windowed
+    workloads also time the per-step append (1 row) + evict."""
+    import torch
+    from quantized_kv_cache_kivi_amd import kvq, synth
+    C = CONFIGS[cfgno]
+    kw = dict(C["kw"])
+    seed, T0 = SEEDS[cfgno], C["prefill"]
+    if kw.get("window", 0) == 0:
+        kw["capacity"] = 32 * math.ceil((T0 + 32 + 64) / 32)
+    cfg = kvq.make_config(**kw)
+    per_rep = kvq.required_bytes(cfg)
+    nrep = max(1, min(64, math.ceil(1.0e9 / max(per_rep, 1))))
+    kmult = key_multipliers(cfgno, kw, seed, dev)
+    planted = synth.planted_positions(kw["batch"], kw["n_sink"], T0, seed, 11) \
+        if kw.get("sink_mode") == "topk" else None
+    chunk = 4096
+    chunks = []
+    for i, s0 in enumerate(range(0, T0, chunk)):
+        n = min(chunk, T0 - s0)
+        pl = None if planted is None else [[p - s0 for p in row if s0 <= p < s0 + n] for row in planted]
+        chunks.append(make_rows(cfgno, kw, n, seed, 100 + 7 * i, dev, kmult, pl))
+    reps = []
+    for _ in range(nrep):
+        c = kvq.Cache(cfg)
+        for k, v in chunks:
+            c.kvq_select_sinks(0, k)
+            c.kvq_append(0, k, v)
+            c.kvq_evict(0)
+        reps.append(c)
+    del chunks
+    torch.cuda.synchronize()
+    sinks_per_b = [[] for _ in range(kw["batch"])]
+    if kw.get("n_sink", 0) > 0:
+        pos = reps[0].region(0, "sink_pos", kw["batch"] * kw["n_sink"] * 4).cpu().view(torch.int32)
+        sinks_per_b = [[int(p) for p in row if p >= 0] for row in pos.reshape(kw["batch"], -1).tolist()]
+    dt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
+    q = synth.normal((kw["batch"], kw["n_q_heads"], kw["head_dim"]), seed, 50_000, dev).to(dt).contiguous()
+    out = torch.empty((kw["batch"], kw["n_q_heads"], kw["head_dim"]), dtype=torch.float32, device=dev)
+    P, lo = reps[0].kvq_get_state(0)
+    nbytes, nctx = algorithmic_bytes(kw, P, lo, sinks_per_b)
+
+    def timed(fn, n):
+        for i in range(5):
+            fn(i)
+        evs = [HipTimer() for _ in range(n)]
+        for i in range(n):
+            evs[i].record(0, stream)
+            fn(5 + i)
+            evs[i].record(1, stream)
+        torch.cuda.synchronize()
+        t = sorted(e.ms() * 1e3 for e in evs)
+        return t[len(t) // 2], sum(t) / len(t)
+
+    dec_med, dec_mean = timed(lambda i: reps[i % nrep].kvq_decode_attn(0, q, out), ncalls)
+    rd_bytes = (min(nbytes, per_rep) // 16) * 16
+    word = torch.zeros(4, dtype=torch.int32, device=dev)
+    rd_med, rd_mean = timed(lambda i: kvq.kvq_stream_read(reps[i % nrep].buf, rd_bytes, word), ncalls)
+    gbps = nbytes / dec_med / 1e3
+    read_gbps = rd_bytes / rd_med / 1e3
+    tr = load_traffic(cfgno)
+    fig = {"workload": f"{C['name']}: {C['desc']}", "P": P, "lo": lo, "cache_replicas": nrep,
+           "bytes_per_call": nbytes, "us_per_call": dec_med, "us_per_call_mean": dec_mean, "GBps": gbps,
+           "frac_of_peak": gbps / HBM_PEAK_GBPS, "context_tokens_per_s": nctx / (dec_med * 1e-6),
+           "stream_read": {"bytes": rd_bytes, "us": rd_med, "GBps": read_gbps, "frac_of_peak": read_gbps / HBM_PEAK_GBPS},
+           "frac_of_stream_read": gbps / read_gbps,
+           "traffic_bytes_per_call": tr["bytes_per_call"] if tr else None}
+    if kw.get("window", 0) > 0:  # per-step append of one row + evict, on the one replica it advances
+        steps = [make_rows(cfgno, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(ncalls + 5)]
+        c = reps[0]
+
+        def app(i):
+            k, v = steps[i]
+            c.kvq_select_sinks(0, k)
+            c.kvq_append(0, k, v)
+            c.kvq_evict(0)
+
+        a_med, a_mean = timed(app, ncalls)
+        fig["append_evict_us"] = a_med
+    del reps
+    torch.cuda.empty_cache()
+    return fig
+
+
 def algorithmic_bytes(kw, P, lo, sinks_per_b):
     """Bytes one decode-attention call must move (valid tokens only)."""
     D, H, Hq, B = kw["head_dim"], kw["n_kv_heads"], kw["n_q_heads"], kw["batch"]
@@ -422,68 +510,103 @@ def algorithmic_bytes(kw, P, lo, sinks_per_b):
     return total, n_ctx
 
 
-def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, budget_s=20.0):
-    """The oracle as it stands, timed on the host on a bounded sample of the same workload."""
-    import numpy as np
-    from threadpoolctl import threadpool_limits
+def host_threads():
+    """Threads the C oracle runs on: this process's CPU affinity, capped by OMP_NUM_THREADS when set."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS")
+    if cap and cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
-    from oracle import attention as oattn
+
+def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, budget_s=20.0):
+    """The plain-C oracle as it stands (oracle/c: fp64 decode attention over the cache it dequantizes from
+    its own stored rows), timed on the host on a bounded sample of the same workload, on every host core
+    this process may use (OpenMP over the streams) and on one thread."""
+    import numpy as np
+
     from oracle import cache as ocache
-    sub = dict(kw)
-    nb = 1  # one batch element (all its KV and query heads) of the workload
-    sub["batch"] = nb
-    ocfg = ocache.Config(**{**sub, "capacity": sub.get("capacity", 0)})
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        m = ocache.CacheModel(ocfg.with_(capacity=ocache.default_capacity(kw.get("window", 0),
-                                                                           prefill_k.shape[2] + 64)),
-                              reserve=prefill_k.shape[2] + 64)
-        k0 = prefill_k[:nb].cpu().numpy()
-        v0 = prefill_v[:nb].cpu().numpy()
-        m.select(0, k0)
-        m.append(0, k0, v0)
+    from oracle import c_model
+    ocfg = ocache.Config(**{**kw, "capacity": ocache.default_capacity(kw.get("window", 0),
+                                                                      prefill_k.shape[2] + 64 + len(steps_kv))})
+    threads = host_threads()
+    t0 = time.perf_counter()
+    m = c_model.CModel(ocfg)
+    k0, v0 = prefill_k.cpu().numpy(), prefill_v.cpu().numpy()
+    for s0 in range(0, k0.shape[2], 4096):
+        kc, vc = k0[:, :, s0:s0 + 4096], v0[:, :, s0:s0 + 4096]
+        m.select(0, kc)
+        m.append(0, kc, vc)
         m.evict(0)
-        t_prefill = time.perf_counter() - t0
-        calls, t_attn, nbytes = 0, 0.0, 0
-        for (k, v), qq in zip(steps_kv, q):
-            kk, vv = k[:nb].cpu().numpy(), v[:nb].cpu().numpy()
-            m.select(0, kk)
-            m.append(0, kk, vv)
-            m.evict(0)
+    t_prefill = time.perf_counter() - t0
+    calls, t_n, t_1, nbytes, nbytes1 = 0, 0.0, 0.0, 0, 0
+    for (k, v), qq in zip(steps_kv, q):
+        kk, vv = k.cpu().numpy(), v.cpu().numpy()
+        m.select(0, kk)
+        m.append(0, kk, vv)
+        m.evict(0)
+        qn = qq.cpu().numpy()
+        P, lo = m.state(0)
+        pos, _, cnt = m.sink_state(0)
+        sinks = [[int(p) for p in row[:c] if p >= 0] for row, c in zip(pos, cnt)]
+        b_ = algorithmic_bytes(kw, P, lo, sinks)[0]
+        t1 = time.perf_counter()
+        m.decode_attention(0, qn, threads=threads)
+        t_n += time.perf_counter() - t1
+        nbytes += b_
+        if calls < 2:  # the same call on one thread (first two steps)
             t1 = time.perf_counter()
-            oattn.decode_attention(m, 0, qq[:nb].cpu().numpy())
-            t_attn += time.perf_counter() - t1
-            calls += 1
-            sinks = [[p for p, _ in m.sink_list(0, 0)]]
-            nbytes += algorithmic_bytes(sub, m.P[0], m.lo[0], sinks)[0]
-            if time.perf_counter() - t0 > budget_s:
-                break
-        # causal prefill attention of the same model: a few queries of one query head per KV head
-        extra = {}
-        if prefill_k.shape[2] > 0:
-            import torch
-            from quantized_kv_cache_kivi_amd import synth
-            P = m.P[0]
+            m.decode_attention(0, qn, threads=1)
+            t_1 += time.perf_counter() - t1
+            nbytes1 += b_
+        calls += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    res = {"value": nbytes / t_n / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "one_thread": {"value": nbytes1 / t_1 / 1e9, "unit": "GB/s", "cores": 1},
+           "sample": f"the whole workload ({kw['batch']} x {kw['n_kv_heads']} streams, {kw['n_q_heads']} query "
+                     f"heads): the plain-C oracle replays the {prefill_k.shape[2]}-row prefill ({t_prefill:.1f} s) "
+                     f"and {calls} decode steps; value = algorithmic decode-attention bytes / oracle decode-"
+                     f"attention time (fp64 over the cache it dequantizes from its stored rows; OpenMP over the "
+                     f"streams on {threads} threads; one_thread: the first two calls again on one thread)"}
+    extra = {}
+    # rows beyond the decode hot path keep the numpy oracle: causal prefill attention and RoPE on read
+    if prefill_k.shape[2] > 0:
+        import torch
+        from threadpoolctl import threadpool_limits
+
+        from oracle import attention as oattn
+        from quantized_kv_cache_kivi_amd import synth
+        sub = dict(kw)
+        sub["batch"] = 1
+        with threadpool_limits(limits=1):
+            mn = ocache.CacheModel(ocache.Config(**{**sub, "capacity": ocfg.capacity}), reserve=prefill_k.shape[2] + 64)
+            kb, vb = k0[:1], v0[:1]
+            for s0 in range(0, kb.shape[2], 4096):
+                mn.select(0, kb[:, :, s0:s0 + 4096])
+                mn.append(0, kb[:, :, s0:s0 + 4096], vb[:, :, s0:s0 + 4096])
+                mn.evict(0)
+            P, lo = mn.P[0], mn.lo[0]
             nq = 8
             heads = list(range(0, kw["n_q_heads"], kw["n_q_heads"] // kw["n_kv_heads"]))
             qdt = torch.float32 if kw.get("in_dtype") == "f32" else torch.float16
             qp = synth.normal((1, kw["n_q_heads"], nq, kw["head_dim"]), 7, 62_000).to(qdt).numpy()
             t1 = time.perf_counter()
-            oattn.prefill_attention(m, 0, qp, heads=heads)
+            oattn.prefill_attention(mn, 0, qp, heads=heads)
             tp = time.perf_counter() - t1
-            _, lo = m.P[0], m.lo[0]
-            early = [p for p, _ in m.sink_list(0, 0) if p < lo]
+            early = [p for p, _ in mn.sink_list(0, 0) if p < lo]
             rows = sum(max(0, P - nq + i - lo + 1) + sum(1 for p in early if p <= P - nq + i) for i in range(nq))
             flops = 4 * kw["head_dim"] * len(heads) * rows
             extra["prefill_attn"] = {"value": flops / tp / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
                                      "sample": f"batch element 0, {len(heads)} query heads (one per KV head), the "
                                                f"last {nq} of {P} positions as queries; algorithmic FLOPs / oracle "
-                                               f"time (fp64, numpy, 1 BLAS thread)"}
+                                               f"time (numpy oracle, fp64, 1 BLAS thread)"}
             if kw.get("fmt") != "tq":  # the same cache read with RoPE on read
-                mr = ocache.CacheModel(m.cfg.with_(rope=True), reserve=P)
-                mr.select(0, k0)
-                mr.append(0, k0, v0)
-                mr.evict(0)
+                mr = ocache.CacheModel(mn.cfg.with_(rope=True), reserve=P)
+                for s0 in range(0, kb.shape[2], 4096):
+                    mr.select(0, kb[:, :, s0:s0 + 4096])
+                    mr.append(0, kb[:, :, s0:s0 + 4096], vb[:, :, s0:s0 + 4096])
+                    mr.evict(0)
                 qd = qp[:, :, -1]
                 t1 = time.perf_counter()
                 oattn.decode_attention(mr, 0, qd)
@@ -491,13 +614,10 @@ def cpu_baseline(cfgno, kw, prefill_k, prefill_v, steps_kv, q, sink_mode_topk, b
                 nb_r = algorithmic_bytes(sub, mr.P[0], mr.lo[0], [[p for p, _ in mr.sink_list(0, 0)]])[0]
                 extra["rope_decode_attn"] = {"value": nb_r / td / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                                              "sample": f"batch element 0 after the {mr.P[0]}-row prefill, every "
-                                                       f"query head, one decode call with RoPE on read (fp64, "
-                                                       f"numpy, 1 BLAS thread)"}
-    return {"value": nbytes / t_attn / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"batch element 0 of the workload ({kw['n_kv_heads']} KV heads, {kw['n_q_heads']} query "
-                      f"heads): prefill of {prefill_k.shape[2]} rows ({t_prefill:.1f} s), then {calls} decode "
-                      f"steps; value = algorithmic decode-attention bytes of that batch element / oracle "
-                      f"decode-attention time (fp64, numpy, 1 BLAS thread)", "rows": extra}
+                                                       f"query head, one decode call with RoPE on read (numpy "
+                                                       f"oracle, fp64, 1 BLAS thread)"}
+    res["rows"] = extra
+    return res
 
 
 DECODE_SOURCES = ["decode_fast.hip", "decode.hip", "decode_shared.h", "device_common.h", "kvq_internal.h",
@@ -615,6 +735,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="turn rocprofv3 --pmc outputs into profiles/decode_traffic_<workload>.{json,md}")
     ap.add_argument("--pmc-commands", nargs="*", default=[], help="commands recorded with --summarize-pmc")
+    ap.add_argument("--by-config", default="2,3,4,5",
+                    help="workloads whose full-size decode attention is timed beside the headline ('' for none)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.config, *args.summarize_pmc, args.pmc_commands)
@@ -808,6 +930,14 @@ def main():
         "kivi_whole": kivi_whole,
         "rope_on_read": rope_on_read,
     }
+    by_cfg = [int(x) for x in args.by_config.split(",") if x.strip()]
+    if by_cfg:
+        del reps
+        torch.cuda.empty_cache()
+        res["decode_attn_by_config"] = {}
+        for cn in by_cfg:
+            log(f"[bench] decode attention of config {cn} at full size")
+            res["decode_attn_by_config"][str(cn)] = decode_figure(cn, dev, stream)
     if not args.no_cpu_baseline:
         try:
             n_cpu = min(args.steps, 16)
