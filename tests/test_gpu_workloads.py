@@ -2,8 +2,10 @@
 configuration bench.py times (same library entry points, same shapes, same split policy).
 
 The GPU cache holds every batch element; the oracle replays the same calls for sampled batch
-elements (the first and the last) on exactly the rows the library received, so each comparison
-is element by element on those streams:
+elements (the first, one in the middle and the last) on exactly the rows the library received, so
+each comparison is element by element on those streams.  The large workloads (q2k, TurboQuant, the
+long int4 stream) replay on the plain-C oracle (oracle/c, bit-exact with the numpy oracle), which
+makes their full decode schedules affordable; the others on the numpy oracle:
 
 * stored bytes of every sampled stream (packed codes, metadata, fp16 window, sink pool), sink
   positions / scores / count: bit-exact;
@@ -22,6 +24,7 @@ import torch
 import bench
 from harness import TOL_ATTN, rel_attn_err
 from oracle import attention as oattn
+from oracle import c_model
 from oracle import cache as ocache
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +37,7 @@ def _log(*a):
 class Workload:
     """GPU cache for all batch elements plus oracle models for the sampled ones."""
 
-    def __init__(self, cfgno, capacity_extra=512, **extra):
+    def __init__(self, cfgno, capacity_extra=512, oracle="numpy", **extra):
         from quantized_kv_cache_kivi_amd import kvq, synth
         self.kvq, self.synth = kvq, synth
         C = bench.CONFIGS[cfgno]
@@ -43,11 +46,15 @@ class Workload:
             self.kw["capacity"] = 32 * ((self.T0 + capacity_extra + 31) // 32)
         self.gpu = kvq.Cache(kvq.make_config(**self.kw))
         self.B = self.kw["batch"]
-        self.bs = sorted({0, self.B - 1})
+        self.bs = sorted({0, self.B // 2, self.B - 1})
         okw = dict(self.kw)
         okw["batch"] = 1
         okw["capacity"] = self.gpu.layout.capacity
-        self.models = {b: ocache.CacheModel(ocache.Config(**okw), reserve=self.T0 + 64) for b in self.bs}
+        self.c_oracle = oracle == "c"
+        if self.c_oracle:
+            self.models = {b: c_model.CModel(ocache.Config(**okw)) for b in self.bs}
+        else:
+            self.models = {b: ocache.CacheModel(ocache.Config(**okw), reserve=self.T0 + 64) for b in self.bs}
         self.kmult = bench.key_multipliers(cfgno, self.kw, self.seed, "cuda")
         self.L = self.kw["n_layers"]
 
@@ -75,6 +82,10 @@ class Workload:
                 self.push(layer, k, v)
             _log(f"  prefill rows [{s0}, {s0 + n})")
 
+    def state(self, b, layer=0):
+        m = self.models[b]
+        return m.state(layer) if self.c_oracle else (m.P[layer], m.lo[layer])
+
     def query(self, tag):
         dt = torch.float32 if self.kw.get("in_dtype") == "f32" else torch.float16
         return self.synth.normal((self.B, self.kw["n_q_heads"], self.kw["head_dim"]), self.seed, tag,
@@ -87,7 +98,10 @@ class Workload:
         got, qh = out.cpu().numpy(), q.cpu().numpy()
         worst = 0.0
         for b, m in self.models.items():
-            ref = oattn.decode_attention(m, layer, qh[b:b + 1])
+            if self.c_oracle:
+                ref = m.decode_attention(layer, qh[b:b + 1], threads=bench.host_threads())
+            else:
+                ref = oattn.decode_attention(m, layer, qh[b:b + 1])
             worst = max(worst, rel_attn_err(got[b:b + 1], ref))
         assert worst <= TOL_ATTN, f"attention rel err {worst:.3e}"
         return worst
@@ -130,7 +144,9 @@ class Workload:
                 got = out.cpu().numpy().view(np.uint16)
                 for b, m in self.models.items():
                     for h in range(H):
-                        ref = oattn.dequant16(m, layer, 0, h, "k" if which == 0 else "v", list(range(p0, p0 + cnt)))
+                        wk, pos = "k" if which == 0 else "v", list(range(p0, p0 + cnt))
+                        ref = m.values(layer, 0, h, wk, pos)[1] if self.c_oracle else \
+                            oattn.dequant16(m, layer, 0, h, wk, pos)
                         d = np.abs(got[b, h].astype(np.int32) - ref.astype(np.int32))
                         same = (got[b, h] >> 15) == (ref >> 15)
                         d = np.where(same, d, np.where((got[b, h] & 0x7FFF) + (ref & 0x7FFF) == 0, 0, 99))
@@ -188,7 +204,7 @@ def test_workload_tiny_streaming_int8():
             P, lo = w.gpu.kvq_get_state(0)
             assert w.gpu.kvq_account(0)["n_valid"] == min(P, 4 + 256) * w.B
             _log(f"[tiny] step {i}: P={P} lo={lo} ok (worst {worst:.2e})")
-    w.check_dequant(0, [(w.models[0].lo[0], 16), (499, 1)])
+    w.check_dequant(0, [(w.state(0)[1], 16), (499, 1)])
 
 
 def test_workload_kivi2_dynamic_sinks():
@@ -223,32 +239,40 @@ def test_workload_kivi2_dynamic_sinks_rope_on_read():
 
 
 def test_workload_q2k_32k():
-    """q2k, batch 16, T = 32768, 4 first sinks, fp16 window 128."""
-    w = Workload(3)
+    """q2k, batch 16, T = 32768, 4 first sinks, fp16 window 128; then 34 decode steps, so the first
+    block opened by decoding completes (step 31) and freezes; bytes after the prefill and at the end."""
+    w = Workload(3, oracle="c")
     w.prefill()
     w.check_bytes(0)
     w.check_attention(0, w.query(1))
-    _decode_steps(w, 2, {0, 1}, 0)
-    w.check_dequant(0, [(0, 40), (32768 - 200, 200)])
+    _decode_steps(w, 34, {0, 1, 30, 31, 32, 33}, 0)
+    w.check_bytes(0)
+    w.check_dequant(0, [(0, 40), (32768 - 200, 234)])
 
 
 def test_workload_turboquant_16k():
-    """TurboQuant K4/V2, batch 8, T = 16384 (AR(1) channels)."""
-    w = Workload(4)
+    """TurboQuant K4/V2, batch 8, T = 16384 (AR(1) channels); then 34 decode steps (a block completes)."""
+    w = Workload(4, oracle="c")
     w.prefill()
     w.check_bytes(0)
     w.check_attention(0, w.query(1))
-    _decode_steps(w, 1, {0}, 0)
-    w.check_dequant(0, [(0, 33), (16384 - 31, 32)])
+    _decode_steps(w, 34, {0, 1, 31, 32, 33}, 0)
+    w.check_bytes(0)
+    w.check_dequant(0, [(0, 33), (16384 - 31, 65)])
 
 
 def test_workload_long_streaming_int4():
-    """Batch 64, full 65540-token cache (sink 4, W = 65536), then append + evict + attention steps."""
-    w = Workload(5)
+    """Batch 64, full 65540-token cache (sink 4, W = 65536), then 256 steps of append + evict + attention.
+    The ring (2050 blocks, 65600 slots) wraps at step 60; attention at steps 0, 1, 2, 31, 32, 33, 127,
+    128 and 255 and every stored byte of the sampled streams after the prefill and after step 255."""
+    w = Workload(5, oracle="c")
     w.prefill()
+    w.check_bytes(0)
     w.check_attention(0, w.query(1))
-    _decode_steps(w, 3, {0, 2}, 0)
+    _decode_steps(w, 256, {0, 1, 2, 31, 32, 33, 127, 128, 255}, 0)
     w.check_bytes(0)
     P, lo = w.gpu.kvq_get_state(0)
-    assert P - lo == 65536 and w.gpu.kvq_account(0)["n_valid"] == (65536 + 4) * w.B
+    assert (P, lo) == (65540 + 256, 65540 + 256 - 65536) and P > w.gpu.layout.capacity
+    assert w.gpu.kvq_account(0)["n_valid"] == (65536 + 4) * w.B
+    assert (P, lo) == w.state(0)
     w.check_dequant(0, [(lo, 64), (P - 130, 130)])
