@@ -131,6 +131,8 @@ typedef struct { /* byte offsets inside the caller's device buffer */
   uint64_t win_k, win_v;          /* [batch][n_kv_heads][residual][head_dim] fp16 */
   uint64_t sink_k, sink_v;        /* [batch][n_kv_heads][n_sink][head_dim] fp16 */
   uint64_t sink_pos, sink_score, sink_count; /* [batch][n_sink] int32, fp32; [batch] int32 */
+  uint64_t decode_sync;           /* [batch][n_kv_heads] uint32: arrival counters of the decode workgroups
+                                     of one call (the last to arrive merges the stream); zero between calls */
   uint64_t tables;                /* once, not per layer: fp32 tables (TQ signs and codebooks, Q2K grid) */
   uint64_t select_work;           /* once, not per layer (TOPK mode): [batch][64][n_sink] (fp32 score, int32
                                      position) top-k lists of the workgroups of one sink-selection call;
@@ -197,7 +199,10 @@ kvq_status kvq_evict(kvq_cache* c, int32_t layer);
  * "Optimization: Fused dequant-dot": TQ scores and values are accumulated in
  * the rotated domain and the output is rotated back once).  scale <= 0 means
  * 1/sqrt(head_dim).  ws: >= kvq_workspace_bytes device bytes (split partials).
- * Two kernel launches (split-K partials, then a fixed-order merge per stream);
+ * Split-K: every workgroup writes one online-softmax partial; on the matrix-core
+ * path (head_dim 128, fp16 queries) the last workgroup of a stream to finish
+ * merges the stream's partials in fixed order in the same launch (counters in
+ * the cache's decode_sync region), elsewhere a second launch merges them;
  * results are deterministic. */
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
                            size_t ws_bytes, void* stream);

@@ -1,11 +1,15 @@
 // MFMA decode attention, head_dim 128, fp16 query (gfx950).
 //
-// One launch of k_decode_fast writes every partial of a decode call: workgroup
-// (stream blockIdx.x, part blockIdx.y) streams the packed bulk of split
-// blockIdx.y of the stream when blockIdx.y < splits, else it scores 64 of the
-// stream's fp16 rows (window rows minus committed sinks, then the sink pool).
-// k_merge_parts then merges the partials of each (stream, query head) in fixed
-// order.
+// One launch of k_decode_fast does a whole decode call: workgroup (stream
+// blockIdx.x, part blockIdx.y) streams the packed bulk of split blockIdx.y of
+// the stream when blockIdx.y < splits, else it scores 64 of the stream's fp16
+// rows (window rows minus committed sinks, then the sink pool), and writes one
+// online-softmax partial.  The partials are stored with device-scope atomic
+// stores (they reach the point of coherence of every XCD), the workgroup waits
+// for its stores, then counts itself in the stream's arrival counter; the
+// workgroup that arrives last merges the stream's partials in fixed order
+// (device-scope loads) and writes the output, so no second launch is needed.
+// The counter is reset by that workgroup (zero between calls).
 //
 // Bulk, per 32-token block and wave ("StreamingLLM + KIVI — long-context decode
 // without growing the KV cache", "Affine quantisation formula": k = u*s + z per
@@ -66,6 +70,15 @@ __device__ __forceinline__ f4 mfma(const u4& a, const u4& b, f4 c) {
                                                 0, 0);
 }
 __device__ __forceinline__ h2 H2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+// Partials are written, and read back by the merging workgroup, with device-scope relaxed atomics:
+// those accesses are coherent across the XCDs' L2 caches, and the counter increment that publishes
+// a partial is issued only after its stores have completed (vmcnt(0)).
+__device__ __forceinline__ void st_part(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_part(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 // Bits of a 32-bit word as fp32.  Vector components pass through this scalar parameter: with this
 // toolchain, __builtin_bit_cast applied directly to an ext_vector component (v.y) reads component 0.
 __device__ __forceinline__ float F32(uint32_t w) { return __builtin_bit_cast(float, w); }
@@ -230,6 +243,7 @@ template <int R>
 union DecSmem {
   FastSmem<R> bulk;
   FpSmem<R> fp;
+  float rot[2][FD];  // the merging workgroup: TurboQuant outputs rotated back, two heads at a time
 };
 
 // What one lane reads from a block record.
@@ -698,7 +712,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       if (F.w[w].m[j] != -INFINITY) v += F.w[w].x.o[j][c] * ex2(F.w[w].m[j] - M);
-    part[j * (FD + 2) + 2 + c] = v;
+    st_part(&part[j * (FD + 2) + 2 + c], v);
   }
   if (tid < R) {
     float M = -INFINITY, L = 0.f;
@@ -707,8 +721,8 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
 #pragma unroll
     for (int w = 0; w < NW; ++w)
       if (F.w[w].m[tid] != -INFINITY) L += F.w[w].l[tid] * ex2(F.w[w].m[tid] - M);
-    part[tid * (FD + 2)] = M;
-    part[tid * (FD + 2) + 1] = L;
+    st_part(&part[tid * (FD + 2)], M);
+    st_part(&part[tid * (FD + 2) + 1], L);
   }
 }
 
@@ -839,11 +853,11 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += F.red[w][j][c];
-    part[j * (FD + 2) + 2 + c] = v;
+    st_part(&part[j * (FD + 2) + 2 + c], v);
   }
   if (tid < R) {
-    part[tid * (FD + 2)] = F.m[tid];
-    part[tid * (FD + 2) + 1] = F.l[tid];
+    st_part(&part[tid * (FD + 2)], F.m[tid]);
+    st_part(&part[tid * (FD + 2) + 1], F.l[tid]);
   }
 }
 
@@ -851,14 +865,6 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
 template <int FMT, int KB, int VB, int R>
 constexpr int waves_target() {
   return (R <= 4 && (KB == 2 || FMT == KVQ_FMT_TQ)) ? 3 : 2;
-}
-
-template <int FMT, int KB, int VB, int R>
-__global__ __launch_bounds__(DNT) __attribute__((amdgpu_waves_per_eu(waves_target<FMT, KB, VB, R>())))
-void k_decode_fast(DecodeArgs a) {
-  __shared__ DecSmem<R> S;
-  if ((int)blockIdx.y < a.splits) bulk_partial<FMT, KB, VB, R>(a, S.bulk);
-  else fp16_partial<R>(a, S.fp, (int)blockIdx.y - a.splits);
 }
 
 // Online merge of partials [q0, q1) of one (stream, query head) into (M, L, v): the partials are read
@@ -873,7 +879,7 @@ __device__ __forceinline__ void merge_range(const float* P0, int q0, int q1, int
     for (int k = 0; k < MC; ++k) {  // past the last part: re-read it (no branch between the loads), unused
       const bool in = qb + k < q1;
       const float* pq = P0 + (int64_t)(in ? qb + k : q1 - 1) * R * (FD + 2);
-      const float m = pq[0], l = pq[1], x = pq[2 + c];
+      const float m = ld_part(pq), l = ld_part(pq + 1), x = ld_part(pq + 2 + c);
       mq[k] = in ? m : -INFINITY;
       lq[k] = in ? l : 0.f;
       vq[k] = in ? x : 0.f;
@@ -894,36 +900,60 @@ __device__ __forceinline__ void merge_range(const float* P0, int q0, int q1, int
   }
 }
 
-// Fixed-order merge of the partials of one (stream, query head): bulk splits, then fp16 groups.
-// TurboQuant bulk partials live in the rotated domain: they are merged first and rotated back
-// (sigma * (c_d * FWHT(acc)); "TurboQuant KV Cache Compression — Spec", "Optimization: Fused
-// dequant-dot") before the fp16 groups, which are in the original domain, join the merge.
+// Fixed-order merge of every query head of stream s by its last workgroup: bulk splits, then fp16
+// groups, two heads at a time (128 threads, one channel each, per head).  TurboQuant bulk partials live
+// in the rotated domain: they are merged first and rotated back (sigma * (c_d * FWHT(acc));
+// "TurboQuant KV Cache Compression — Spec", "Optimization: Fused dequant-dot") before the fp16
+// groups, which are in the original domain, join the merge.
 template <int R, bool TQ>
-__global__ __launch_bounds__(FD) void k_merge_parts(DecodeArgs a) {
-  const int s = blockIdx.x, j = blockIdx.y, c = threadIdx.x;
+__device__ void merge_stream(const DecodeArgs& a, int s, float (*rot)[FD]) {
+  const int tid = threadIdx.x, half = tid >> 7, c = tid & (FD - 1);
   const int b = s / a.sh.Hkv, g = s % a.sh.Hkv;
-  const float* P0 = a.ws + (int64_t)s * a.nparts * R * (FD + 2) + j * (FD + 2);
-  const int np = a.nparts;
-  float M = -INFINITY, L = 0.f, v = 0.f;
-  if constexpr (TQ) {
-    __shared__ float rot[FD];
-    merge_range<R>(P0, 0, a.splits, c, M, L, v);
-    rot[c] = v;
-    __syncthreads();
-    if (c < 64) {
-      float y0 = rot[2 * c], y1 = rot[2 * c + 1];
-      wave_fwht(y0, y1, FD, c);
-      const float cd = (float)(1.0 / __builtin_sqrt((double)FD));
-      rot[2 * c] = a.lv.tables->signs[2 * c] * (y0 * cd);
-      rot[2 * c + 1] = a.lv.tables->signs[2 * c + 1] * (y1 * cd);
+  for (int j0 = 0; j0 < R; j0 += 2) {
+    const int j = j0 + half, jj = j < R ? j : R - 1;
+    const float* P0 = a.ws + (int64_t)s * a.nparts * R * (FD + 2) + jj * (FD + 2);
+    float M = -INFINITY, L = 0.f, v = 0.f;
+    if constexpr (TQ) {
+      merge_range<R>(P0, 0, a.splits, c, M, L, v);
+      rot[half][c] = v;
+      __syncthreads();
+      if (c < 64) {  // one wave per head: v = sigma * (c_d * FWHT(v))
+        float y0 = rot[half][2 * c], y1 = rot[half][2 * c + 1];
+        wave_fwht(y0, y1, FD, c);
+        const float cd = (float)(1.0 / __builtin_sqrt((double)FD));
+        rot[half][2 * c] = a.lv.tables->signs[2 * c] * (y0 * cd);
+        rot[half][2 * c + 1] = a.lv.tables->signs[2 * c + 1] * (y1 * cd);
+      }
+      __syncthreads();
+      v = rot[half][c];
+      __syncthreads();
+      merge_range<R>(P0, a.splits, a.nparts, c, M, L, v);
+    } else {
+      merge_range<R>(P0, 0, a.nparts, c, M, L, v);
     }
-    __syncthreads();
-    v = rot[c];
-    merge_range<R>(P0, a.splits, np, c, M, L, v);
-  } else {
-    merge_range<R>(P0, 0, np, c, M, L, v);
+    if (j < R) a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * FD + c] = v / L;
   }
-  a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * FD + c] = v / L;
+}
+
+template <int FMT, int KB, int VB, int R>
+__global__ __launch_bounds__(DNT) __attribute__((amdgpu_waves_per_eu(waves_target<FMT, KB, VB, R>())))
+void k_decode_fast(DecodeArgs a) {
+  __shared__ DecSmem<R> S;
+  __shared__ int last;
+  if ((int)blockIdx.y < a.splits) bulk_partial<FMT, KB, VB, R>(a, S.bulk);
+  else fp16_partial<R>(a, S.fp, (int)blockIdx.y - a.splits);
+  // publish the partial: its stores complete before the arrival is counted
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  const int s = blockIdx.x;
+  if (threadIdx.x == 0) {
+    const uint32_t n = __hip_atomic_fetch_add(&a.lv.decode_sync[s], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = n == (uint32_t)(a.nparts - 1);
+    if (last) __hip_atomic_store(&a.lv.decode_sync[s], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  merge_stream<R, FMT == KVQ_FMT_TQ>(a, s, S.rot);
 }
 
 template <int FMT, int KB, int VB>
@@ -932,24 +962,18 @@ hipError_t launch_r(const DecodeArgs& a, hipStream_t st) {
   const int S = a.sh.B * a.sh.Hkv;
   // parts vary slowest: the (short) fp16 workgroups are dispatched after every bulk split
   dim3 grid(S, a.nparts);
-  dim3 mgrid(S, r);
-  constexpr bool TQ = FMT == KVQ_FMT_TQ;
   switch (r) {
     case 1:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 1>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<1, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     case 2:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 2>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<2, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     case 4:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 4>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<4, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     case 8:
       hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 8>), grid, dim3(DNT), 0, st, a);
-      hipLaunchKernelGGL((k_merge_parts<8, TQ>), mgrid, dim3(FD), 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }

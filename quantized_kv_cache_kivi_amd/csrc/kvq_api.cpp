@@ -152,6 +152,8 @@ kvq_layout make_layout(const kvq_config& c) {
   off = align256(off + (uint64_t)c.batch * c.n_sink * 4);
   L.sink_count = off;
   off = align256(off + (uint64_t)c.batch * 4);
+  L.decode_sync = off;
+  off = align256(off + S * 4);
   L.layer_stride = off;
   L.tables = (uint64_t)c.n_layers * L.layer_stride;
   L.select_work = L.tables + align256(sizeof(Tables));
@@ -282,6 +284,7 @@ LayerView view_of(const kvq_cache* c, int layer) {
   v.sink_pos = (int32_t*)(b + L.sink_pos);
   v.sink_score = (float*)(b + L.sink_score);
   v.sink_count = (int32_t*)(b + L.sink_count);
+  v.decode_sync = (uint32_t*)(b + L.decode_sync);
   v.tables = (const Tables*)(c->base + L.tables);
   v.rec = (int64_t)L.record_bytes;
   v.k_codes = (int64_t)L.rec_k_codes;

@@ -39,6 +39,7 @@ struct LayerView {
   int32_t* sink_pos;    // [B][n_sink]
   float* sink_score;    // [B][n_sink]
   int32_t* sink_count;  // [B]
+  uint32_t* decode_sync;  // [S] arrival counters of one decode call's workgroups (zero between calls)
   const Tables* tables;
   int64_t rec, k_codes, v_codes, k_meta, v_meta;  // record size and section offsets
   int cap_b;

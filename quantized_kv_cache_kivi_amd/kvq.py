@@ -44,7 +44,7 @@ class kvq_bytes(ctypes.Structure):
 class kvq_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "layer_stride", "bulk", "record_bytes", "rec_k_codes", "rec_v_codes", "rec_k_meta", "rec_v_meta",
-        "staging", "win_k", "win_v", "sink_k", "sink_v", "sink_pos", "sink_score", "sink_count",
+        "staging", "win_k", "win_v", "sink_k", "sink_v", "sink_pos", "sink_score", "sink_count", "decode_sync",
         "tables", "select_work", "total")] + [("cap_blocks", ctypes.c_int32), ("capacity", ctypes.c_int32)]
 
 

@@ -67,7 +67,7 @@ def test_layout_matches_documented_format(kvq, fmt, kb, vb, D):
     S = 2 * 4
     regions = [("bulk", S * lay.cap_blocks * rec), ("win_k", S * 16 * D * 2), ("win_v", S * 16 * D * 2),
                ("sink_k", S * 5 * D * 2), ("sink_v", S * 5 * D * 2), ("sink_pos", 2 * 5 * 4),
-               ("sink_score", 2 * 5 * 4), ("sink_count", 2 * 4)]
+               ("sink_score", 2 * 5 * 4), ("sink_count", 2 * 4), ("decode_sync", S * 4)]
     if fmt != "tq":
         regions.append(("staging", S * 32 * D * 2))
     spans = sorted((getattr(lay, n), getattr(lay, n) + sz, n) for n, sz in regions)
