@@ -33,7 +33,7 @@ def account(model, layer, b):
     n_sink = sum(1 for s in src.values() if s == "sink")
     n_res = sum(1 for s in src.values() if s == "window")
     n_q = sum(1 for s in src.values() if s == "bulk")
-    H, D = cfg.n_kv_heads, cfg.head_dim
+    H, D = cfg.n_kv_heads, cfg.store_dim  # stored width (TurboQuant pads a non-power-of-two head_dim)
     _, size, _ = record_sections(cfg.fmt, D, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
     blocks = {p // 32 for p, s in src.items() if s == "bulk"}
     if cfg.fmt == "tq":

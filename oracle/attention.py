@@ -50,7 +50,8 @@ def _bulk_values(cfg, qs, which, positions, tq, exact):
                 return q2k.LEVELS[u.astype(np.intp)].astype(np.float64) * from_f16_bits(r).astype(np.float64)
             return q2k.k_dequant32(u, r)
         n = qs["k_norm"][blk, row]
-        return (turboquant.dequant64 if exact else turboquant.dequant32)(u, n, tq.kc, tq.signs)
+        # the inverse rotation over the padded width, then the caller's head_dim channels
+        return (turboquant.dequant64 if exact else turboquant.dequant32)(u, n, tq.kc, tq.signs)[:, :cfg.head_dim]
     u = qs["v_codes"][blk, row]
     D = u.shape[1]
     if cfg.fmt == "kivi":
@@ -65,8 +66,8 @@ def _bulk_values(cfg, qs, which, positions, tq, exact):
             return (u.astype(np.float64) - 8.0) * from_f16_bits(s).astype(np.float64)
         return q2k.v_dequant32(u, s)
     n = qs["v_norm"][blk, row]
-    assert D == cfg.head_dim
-    return (turboquant.dequant64 if exact else turboquant.dequant32)(u, n, tq.vc, tq.signs)
+    assert D == cfg.store_dim
+    return (turboquant.dequant64 if exact else turboquant.dequant32)(u, n, tq.vc, tq.signs)[:, :cfg.head_dim]
 
 
 def stream_values(model, layer, b, h, which, positions, exact=True):

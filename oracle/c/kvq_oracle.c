@@ -15,7 +15,7 @@
 #endif
 
 #define G 32           /* token-block length and V channel-group length */
-#define MAXD 128
+#define MAXD 256       /* widest stored row: TurboQuant head_dim 160 padded to 256 */
 #define MAXSINK 16
 #define EPS 1e-5f      /* eps of the affine scale: StreamingLLM + KIVI page, "Affine quantisation formula" */
 
@@ -216,6 +216,7 @@ typedef struct {
 
 struct ko_model {
   ko_config c;
+  int dp;                                  /* stored width: TurboQuant pads head_dim to a power of two */
   int kslot, vslot;                        /* bits a stored code occupies */
   int kc, vc, km, vm, rec;                 /* record section sizes */
   int cap_b;
@@ -235,7 +236,9 @@ ko_model* ko_create(const ko_config* cfg) {
   const ko_config c = *cfg;
   if (c.n_layers < 1 || c.batch < 1 || c.n_kv_heads < 1 || c.n_q_heads < 1) return NULL;
   if (c.n_q_heads % c.n_kv_heads) return NULL;
-  if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128) return NULL;
+  if (c.head_dim != 32 && c.head_dim != 64 && c.head_dim != 128 &&
+      !(c.fmt == 2 && (c.head_dim == 96 || c.head_dim == 160)))
+    return NULL;
   if (c.n_sink < 0 || c.n_sink > MAXSINK || c.capacity < G || c.capacity % G) return NULL;
   if (c.fmt == 0) {
     if ((c.k_bits != 2 && c.k_bits != 4 && c.k_bits != 8) || (c.v_bits != 2 && c.v_bits != 4 && c.v_bits != 8))
@@ -250,7 +253,11 @@ ko_model* ko_create(const ko_config* cfg) {
   ko_model* m = (ko_model*)calloc(1, sizeof(ko_model));
   if (!m) return NULL;
   m->c = c;
-  const int D = c.head_dim;
+  int dp = c.head_dim;
+  if (c.fmt == 2)
+    while (dp & (dp - 1)) dp += dp & -dp;  /* next power of two (TurboQuant spec, "Hadamard Transform Detail") */
+  m->dp = dp;
+  const int D = dp;
   const int dense = c.fmt == 2 && c.tq_dense3;
   m->kslot = slot_bits(c.k_bits, dense);
   m->vslot = slot_bits(c.v_bits, dense);
@@ -268,10 +275,10 @@ ko_model* ko_create(const ko_config* cfg) {
   }
   m->rec = m->kc + m->vc + m->km + m->vm;
   m->cap_b = c.capacity / G;
-  if (c.fmt == 2) {
-    ko_tq_signs(c.seed, D, m->signs);
-    ko_tq_codebook(D, c.k_bits, m->kbnd, m->kcen);
-    ko_tq_codebook(D, c.v_bits, m->vbnd, m->vcen);
+  if (c.fmt == 2) {  /* one sign per stored coordinate; codebooks of Beta(head_dim/2, head_dim/2) */
+    ko_tq_signs(c.seed, dp, m->signs);
+    ko_tq_codebook(c.head_dim, c.k_bits, m->kbnd, m->kcen);
+    ko_tq_codebook(c.head_dim, c.v_bits, m->vbnd, m->vcen);
   }
   ko_q2k_grid(m->q2k_th, m->q2k_lv);
   const int L = c.n_layers, B = c.batch, H = c.n_kv_heads;
@@ -525,10 +532,10 @@ static void fwht64(double* x, int d) {
 
 /* TurboQuant row: y = c_d * FWHT(sigma * x); n = sqrt(sumsq(y)); code = #{boundaries <= y / n}. */
 static void tq_row(const ko_model* m, const float* x, const float* bnd, int bits, uint8_t* code, float* norm) {
-  const int D = m->c.head_dim;
+  const int D = m->dp, Din = m->c.head_dim;  /* the row, zero-padded from Din to D channels */
   const float cd = (float)(1.0 / sqrt((double)D));
   float y[MAXD];
-  for (int i = 0; i < D; ++i) y[i] = x[i] * m->signs[i];
+  for (int i = 0; i < D; ++i) y[i] = (i < Din ? x[i] : 0.0f) * m->signs[i];
   fwht32(y, D);
   for (int i = 0; i < D; ++i) y[i] = y[i] * cd;
   const float n = sqrtf(sumsq(y, D));
@@ -686,7 +693,7 @@ static void put_code(uint8_t* sec, int64_t seq, int slot, uint32_t code) {
 static void put_f16(uint8_t* p, uint16_t h) { memcpy(p, &h, 2); }
 
 static void pack_record(const ko_model* m, const Block* o, uint8_t* rec) {
-  const int D = m->c.head_dim, ng = D / 32;
+  const int D = m->dp, ng = D / 32;
   memset(rec, 0, m->rec);
   uint8_t* kc = rec;
   uint8_t* vc = rec + m->kc;
@@ -734,7 +741,7 @@ int ko_stream_image(ko_model* m, int layer, int b, int h, uint8_t* bulk, uint16_
                     uint16_t* sink_k, uint16_t* sink_v) {
   if (!m || layer < 0 || layer >= m->c.n_layers || b < 0 || b >= m->c.batch || h < 0 || h >= m->c.n_kv_heads)
     return -1;
-  const int D = m->c.head_dim, R = m->c.residual;
+  const int D = m->dp, Din = m->c.head_dim, R = m->c.residual;  /* fp16 rows stored padded to D */
   const int64_t P = m->P[layer];
   const Rows* r = rows_of(m, layer, b, h);
   if (bulk) {
@@ -754,16 +761,16 @@ int ko_stream_image(ko_model* m, int layer, int b, int h, uint8_t* bulk, uint16_
   for (int rho = 0; rho < R; ++rho) {
     const int64_t p = rho <= P - 1 ? rho + R * ((P - 1 - rho) / R) : -1;
     for (int ch = 0; ch < D; ++ch) {
-      if (win_k) win_k[rho * D + ch] = p >= 0 ? f16_bits(r->k[p * D + ch]) : 0;
-      if (win_v) win_v[rho * D + ch] = p >= 0 ? f16_bits(r->v[p * D + ch]) : 0;
+      if (win_k) win_k[rho * D + ch] = p >= 0 && ch < Din ? f16_bits(r->k[p * Din + ch]) : 0;
+      if (win_v) win_v[rho * D + ch] = p >= 0 && ch < Din ? f16_bits(r->v[p * Din + ch]) : 0;
     }
   }
   int64_t s[MAXSINK];
   const int ns = sinks_of(m, layer, b, s);
   for (int i = 0; i < m->c.n_sink; ++i)
     for (int ch = 0; ch < D; ++ch) {
-      if (sink_k) sink_k[i * D + ch] = i < ns ? f16_bits(r->k[s[i] * D + ch]) : 0;
-      if (sink_v) sink_v[i * D + ch] = i < ns ? f16_bits(r->v[s[i] * D + ch]) : 0;
+      if (sink_k) sink_k[i * D + ch] = i < ns && ch < Din ? f16_bits(r->k[s[i] * Din + ch]) : 0;
+      if (sink_v) sink_v[i * D + ch] = i < ns && ch < Din ? f16_bits(r->v[s[i] * Din + ch]) : 0;
     }
   return 0;
 }
@@ -809,17 +816,18 @@ static void bulk_row(const ko_model* m, const Block* o, int t, int which, double
      * transform first, then the signs) */
     const float* cen = which ? m->vcen : m->kcen;
     const float n = which ? o->vn[t] : o->kn[t];
+    const int Dp = m->dp;  /* the inverse over every stored coordinate, then the first head_dim channels */
     if (x64) {
       double w[MAXD];
-      for (int ch = 0; ch < D; ++ch) w[ch] = (double)n * (double)cen[u[ch]];
-      fwht64(w, D);
-      for (int ch = 0; ch < D; ++ch) x64[ch] = (double)m->signs[ch] * (w[ch] / sqrt((double)D));
+      for (int ch = 0; ch < Dp; ++ch) w[ch] = (double)n * (double)cen[u[ch]];
+      fwht64(w, Dp);
+      for (int ch = 0; ch < D; ++ch) x64[ch] = (double)m->signs[ch] * (w[ch] / sqrt((double)Dp));
     }
     if (x32) {
-      const float cd = (float)(1.0 / sqrt((double)D));
+      const float cd = (float)(1.0 / sqrt((double)Dp));
       float w[MAXD];
-      for (int ch = 0; ch < D; ++ch) w[ch] = n * cen[u[ch]];
-      fwht32(w, D);
+      for (int ch = 0; ch < Dp; ++ch) w[ch] = n * cen[u[ch]];
+      fwht32(w, Dp);
       for (int ch = 0; ch < D; ++ch) x32[ch] = m->signs[ch] * (w[ch] * cd);
     }
   }
@@ -996,7 +1004,7 @@ int ko_account(const ko_model* m, int layer, int b, int64_t* out8) {
       }
     }
   }
-  const int64_t H = m->c.n_kv_heads, D = m->c.head_dim;
+  const int64_t H = m->c.n_kv_heads, D = m->dp;  /* stored width */
   const int64_t meta = m->c.fmt == 2 ? n_q * 8 * H : nblk * m->km * H + n_q * (m->vm / G) * H;
   out8[0] = n_s + n_w + n_q;
   out8[1] = n_q;

@@ -152,7 +152,7 @@ class CModel:
 
     def image(self, layer, b, h):
         c = self.cfg
-        D, R, ns = c.head_dim, c.residual, c.n_sink
+        D, R, ns = c.store_dim, c.residual, c.n_sink  # fp16 rows are stored at the padded width
         out = {"bulk": np.zeros((self.cap_blocks, self.record_bytes), np.uint8),
                "win_k": np.zeros((R, D), np.uint16), "win_v": np.zeros((R, D), np.uint16),
                "sink_k": np.zeros((ns, D), np.uint16), "sink_v": np.zeros((ns, D), np.uint16)}

@@ -68,6 +68,15 @@ class Config:
         return self.capacity // G
 
     @property
+    def store_dim(self):
+        """Width rows are stored and rotated at: TurboQuant pads a head_dim that is not a power of two
+        with zeros to the next power of two (TurboQuant spec, "Hadamard Transform Detail") and keeps
+        every rotated coordinate; other formats store head_dim."""
+        if self.fmt == "tq":
+            return 1 << (self.head_dim - 1).bit_length()
+        return self.head_dim
+
+    @property
     def gqa(self):
         return self.n_q_heads // self.n_kv_heads
 
@@ -84,8 +93,8 @@ def default_capacity(window, max_len=0):
 
 class TQTables:
     def __init__(self, cfg):
-        self.signs = turboquant.signs(cfg.seed, cfg.head_dim)
-        self.kb, self.kc = turboquant.codebook(cfg.head_dim, cfg.k_bits)
+        self.signs = turboquant.signs(cfg.seed, cfg.store_dim)        # one per stored coordinate
+        self.kb, self.kc = turboquant.codebook(cfg.head_dim, cfg.k_bits)  # Beta(head_dim/2, head_dim/2)
         self.vb, self.vc = turboquant.codebook(cfg.head_dim, cfg.v_bits)
 
 
@@ -138,7 +147,7 @@ def quantize_stream(cfg, K, V, sink_pos, P, tq=None):
 
 def block_records(cfg, qs):
     """Packed block records [nblk, record_bytes] from quantize_stream output."""
-    off, size, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
+    off, size, rec = layout.record_sections(cfg.fmt, cfg.store_dim, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
     nblk = qs["nblk"]
     out = np.zeros((nblk, rec), dtype=np.uint8)
     kb, vb = layout.slot_bits(cfg.k_bits, cfg.tq_dense3), layout.slot_bits(cfg.v_bits, cfg.tq_dense3)
@@ -166,9 +175,9 @@ def stream_image(cfg, K, V, sink_list, P, tq=None):
     sink_k/sink_v uint16 [n_sink, D], staging fp32 [P % 32, D] (the open
     block's raw rows; staging rows beyond P % 32 are not defined).
     """
-    _, _, rec = layout.record_sections(cfg.fmt, cfg.head_dim, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
+    _, _, rec = layout.record_sections(cfg.fmt, cfg.store_dim, cfg.k_bits, cfg.v_bits, cfg.tq_dense3)
     cap_b = cfg.cap_blocks
-    D = cfg.head_dim
+    D = cfg.store_dim  # fp16 rows are stored at the padded width (zeros past head_dim)
     bulk = np.zeros((cap_b, rec), dtype=np.uint8)
     if P > 0:
         qs = quantize_stream(cfg, K, V, [p for p, _ in sink_list], P, tq)
@@ -181,16 +190,17 @@ def stream_image(cfg, K, V, sink_list, P, tq=None):
     R = cfg.residual
     win_k = np.zeros((R, D), dtype=np.uint16)
     win_v = np.zeros((R, D), dtype=np.uint16)
+    Din = cfg.head_dim
     for rho in range(R):
         if rho <= P - 1:
             p = rho + R * ((P - 1 - rho) // R)
-            win_k[rho] = to_f16_bits(K[p])
-            win_v[rho] = to_f16_bits(V[p])
+            win_k[rho, :Din] = to_f16_bits(K[p])
+            win_v[rho, :Din] = to_f16_bits(V[p])
     sk = np.zeros((cfg.n_sink, D), dtype=np.uint16)
     sv = np.zeros((cfg.n_sink, D), dtype=np.uint16)
     for i, (p, _) in enumerate(sink_list):
-        sk[i] = to_f16_bits(K[p])
-        sv[i] = to_f16_bits(V[p])
+        sk[i, :Din] = to_f16_bits(K[p])
+        sv[i, :Din] = to_f16_bits(V[p])
     nst = P % G
     staging = np.array(K[P - nst:P], dtype=np.float32) if cfg.fmt != "tq" else np.zeros((0, D), np.float32)
     return {"bulk": bulk, "win_k": win_k, "win_v": win_v, "sink_k": sk, "sink_v": sv, "staging": staging}

@@ -142,9 +142,20 @@ def codes_from_t(t, boundaries):
     return u
 
 
+def pad(x, dp):
+    """Rows [..., d] zero-padded to [..., dp] (the rotation width, a power of two)."""
+    x = f32(x)
+    if x.shape[-1] == dp:
+        return x
+    out = np.zeros(x.shape[:-1] + (dp,), np.float32)
+    out[..., :x.shape[-1]] = x
+    return out
+
+
 def quantize_rows(x, sgn, boundaries, quantized=None):
-    """Rows [n, d] -> (codes uint8 [n, d], norms fp32 [n]).  Rows with quantized=False get code 0, norm 0."""
-    y = rotate(x, sgn)
+    """Rows [n, d] -> (codes uint8 [n, dp], norms fp32 [n]) with dp = len(sgn) >= d: rows are zero-padded
+    to dp and every rotated coordinate is coded.  Rows with quantized=False get code 0, norm 0."""
+    y = rotate(pad(x, len(sgn)), sgn)
     nrm = np.sqrt(sumsq_canonical(y))
     safe = np.where(nrm > 0, nrm, np.float32(1.0))
     t = np.where(nrm[:, None] > 0, y / safe[:, None], np.float32(0.0))

@@ -83,9 +83,11 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
     vx[i] = 0.f;
     if (i < nper && t < tend) {
       if (t >= tnew0) {
-        const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
-        kx[i] = ld_in(a.k, gi, sh.in_f32);
-        vx[i] = ld_in(a.v, gi, sh.in_f32);
+        if (c < sh.Din) {  // input rows hold Din channels; the rest of a padded row is zero
+          const int64_t gi = (in_row0 + (base + t - a.P)) * sh.Din + c;
+          kx[i] = ld_in(a.k, gi, sh.in_f32);
+          vx[i] = ld_in(a.v, gi, sh.in_f32);
+        }
       } else if (!tq) {
         kx[i] = ld_in(lv.staging, ((int64_t)s * G + t) * D + c, sh.in_f32);
       }
@@ -395,10 +397,10 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
       const int t = tnew0 + idx / D, cc = idx % D;
       const int64_t p = base + t;
       if (p < wlo) continue;
-      const int64_t gi = (in_row0 + (p - a.P)) * D + cc;
+      const int64_t gi = (in_row0 + (p - a.P)) * sh.Din + cc;
       const int64_t wo = ((int64_t)s * sh.R + p % sh.R) * D + cc;
-      lv.win_k[wo] = ld_in_f16(a.k, gi, sh.in_f32);
-      lv.win_v[wo] = ld_in_f16(a.v, gi, sh.in_f32);
+      lv.win_k[wo] = cc < sh.Din ? ld_in_f16(a.k, gi, sh.in_f32) : (uint16_t)0;
+      lv.win_v[wo] = cc < sh.Din ? ld_in_f16(a.v, gi, sh.in_f32) : (uint16_t)0;
     }
   }
   // 9. fp16 sink pool
@@ -407,10 +409,10 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
       const int t = tnew0 + idx / D, cc = idx % D;
       const int slot = sink_slot[t];
       if (slot < 0) continue;
-      const int64_t gi = (in_row0 + (base + t - a.P)) * D + cc;
+      const int64_t gi = (in_row0 + (base + t - a.P)) * sh.Din + cc;
       const int64_t so = ((int64_t)s * sh.n_sink + slot) * D + cc;
-      lv.sink_k[so] = ld_in_f16(a.k, gi, sh.in_f32);
-      lv.sink_v[so] = ld_in_f16(a.v, gi, sh.in_f32);
+      lv.sink_k[so] = cc < sh.Din ? ld_in_f16(a.k, gi, sh.in_f32) : (uint16_t)0;
+      lv.sink_v[so] = cc < sh.Din ? ld_in_f16(a.v, gi, sh.in_f32) : (uint16_t)0;
     }
     // first-N commits: positions and count, by one workgroup per batch element
     if (sh.sink_mode == KVQ_SINK_FIRST_N && h == 0 && blockIdx.x == 0) {

@@ -136,7 +136,7 @@ __global__ __launch_bounds__(MNT) void k_merge_heads(DecodeArgs a) {
   const int cnt = lv.sink_count[b];
   const int praw = *(ns > 0 ? lv.sink_pos + b * ns + min(tid, ns - 1) : lv.sink_count + b);
   // query slice: one 16-byte load (fp16) or two (fp32)
-  const int64_t qo = ((int64_t)b * sh.Hq + (int64_t)g * r + j) * D + 8 * part;
+  const int64_t qo = ((int64_t)b * sh.Hq + (int64_t)g * r + j) * sh.Din + 8 * part;  // Din = D here (not TQ)
   const uint8_t* qp = static_cast<const uint8_t*>(a.q) + qo * (sh.in_f32 ? 4 : 2);
   const mu4 qw0 = *reinterpret_cast<const mu4*>(qp);
   const mu4 qw1 = *reinterpret_cast<const mu4*>(qp + (sh.in_f32 ? 16 : 0));
@@ -262,7 +262,7 @@ __global__ __launch_bounds__(MNT) void k_merge_heads(DecodeArgs a) {
     float fp = 0.f;
     for (int q = 0; q < rpp; ++q) fp += red[q * D + tid];
     v += fp * Wf;
-    a.out[((int64_t)b * sh.Hq + g * r + j) * D + tid] = v / Ls;
+    a.out[((int64_t)b * sh.Hq + g * r + j) * sh.Din + tid] = v / Ls;
   }
 }
 

@@ -595,7 +595,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     S.kc = al;
   }
   {
-    const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
+    const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * sh.Din;  // query rows of Din channels
     const int pk = Q2K ? 2 * (lane & 3) : code_pos<KB>(lane & 3);
     const _Float16 fa = (_Float16)ldexpf(1.f, -pk);
     S.fa2 = h2{fa, fa};
@@ -603,7 +603,9 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     S.fa2l = h2{fal, fal};
 #pragma unroll
     for (int j = 0; j < R; ++j)
-      S.q2[j] = H2(reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + j * FD)[lane]);
+      S.q2[j] = H2(2 * lane < sh.Din
+                       ? *reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + j * sh.Din + 2 * lane)
+                       : 0u);  // channels past Din are the zero padding
     // weights carry 2^(PV - pv): the V codes of this lane's token pair sit at bit pv (TurboQuant's
     // signed planes are +-1 at every position: no factor)
     const int t0 = 2 * i16, et = ((t0 >> 4) << 2) | (t0 & 3);
@@ -739,13 +741,15 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
   const LayerView lv = a.lv;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int s = blockIdx.x, b = s / sh.Hkv, g = s % sh.Hkv;
-  const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
+  const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * sh.Din;  // query rows of Din channels
   constexpr int QW = (R * FD / 2 + DNT - 1) / DNT;  // query words per thread
   uint32_t qv[QW];
 #pragma unroll
   for (int k = 0; k < QW; ++k) {
-    const int idx = tid + k * DNT;
-    qv[k] = idx < R * FD / 2 ? reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow)[idx] : 0u;
+    const int idx = tid + k * DNT, j = idx / (FD / 2), w = idx % (FD / 2);
+    qv[k] = idx < R * FD / 2 && 2 * w < sh.Din
+                ? *reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + j * sh.Din + 2 * w)
+                : 0u;
   }
   stage_sinks(a, b, F.spos, F.sslot, &F.nsink);
 #pragma unroll
@@ -931,7 +935,7 @@ __device__ void merge_stream(const DecodeArgs& a, int s, float (*rot)[FD]) {
     } else {
       merge_range<R>(P0, 0, a.nparts, c, M, L, v);
     }
-    if (j < R) a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * FD + c] = v / L;
+    if (j < R && c < a.sh.Din) a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * a.sh.Din + c] = v / L;
   }
 }
 

@@ -96,7 +96,7 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
   // query rows of the r heads; sinks of this batch element
   for (int idx = tid; idx < r * D; idx += DNT) {
     const int j = idx / D, c = idx % D;
-    S.q[j][c] = ld_in(a.q, ((int64_t)b * sh.Hq + g * r + j) * D + c, sh.in_f32);
+    S.q[j][c] = c < sh.Din ? ld_in(a.q, ((int64_t)b * sh.Hq + g * r + j) * sh.Din + c, sh.in_f32) : 0.f;
   }
   stage_sinks(a, b, S.sinks, S.sink_slot, &S.nsinks);
   if (tid < MAX_GQA) {
@@ -353,12 +353,12 @@ __device__ inline void merge_partials(const DecodeArgs& a, Smem& S) {
     for (int idx = tid; idx < r * D; idx += DNT) {
       const int j = idx / D, c = idx % D;
       const float v = fin[j * MAX_D + c] * S.fac[j] + P0[(nbulk * r + j) * (D + 2) + 2 + c] * S.m[j];
-      a.out[((int64_t)b * sh.Hq + g * r + j) * D + c] = v / S.l[j];
+      if (c < sh.Din) a.out[((int64_t)b * sh.Hq + g * r + j) * sh.Din + c] = v / S.l[j];
     }
   } else {
     for (int idx = tid; idx < r * D; idx += DNT) {
       const int j = idx / D, c = idx % D;
-      a.out[((int64_t)b * sh.Hq + g * r + j) * D + c] = fin[j * MAX_D + c] / S.Lb[j];
+      if (c < sh.Din) a.out[((int64_t)b * sh.Hq + g * r + j) * sh.Din + c] = fin[j * MAX_D + c] / S.Lb[j];
     }
   }
 }

@@ -25,8 +25,9 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
   if (i >= a.count) return;
   const int64_t p = a.pos0 + i;
   const bool is_k = a.which == 0;
-  uint16_t* out = a.out + ((int64_t)s * a.count + i) * D;
+  uint16_t* out = a.out + ((int64_t)s * a.count + i) * sh.Din;  // rows of the caller's Din channels
   const bool act = 2 * lane < D;
+  const bool wr = 2 * lane < sh.Din;  // Din is even: a lane writes both of its channels or neither
   // sink pool
   int slot = -1;
   if (sh.n_sink > 0) {
@@ -37,7 +38,7 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
   if (slot >= 0 || p >= a.P - sh.R) {
     const uint16_t* src = slot >= 0 ? (is_k ? lv.sink_k : lv.sink_v) + ((int64_t)s * sh.n_sink + slot) * D
                                     : (is_k ? lv.win_k : lv.win_v) + ((int64_t)s * sh.R + p % sh.R) * D;
-    if (act) {
+    if (wr) {
       out[2 * lane] = src[2 * lane];
       out[2 * lane + 1] = src[2 * lane + 1];
     }
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
       }
     }
   }
-  if (act) {
+  if (wr) {
     out[2 * lane] = f16_bits(x[0]);
     out[2 * lane + 1] = f16_bits(x[1]);
   }

@@ -42,6 +42,13 @@ kvq_status set_error(kvq_status st, const char* msg) {
 void clear_error() { g_err.clear(); }
 }  // namespace kvq
 
+namespace kvq {
+// Width a row is stored and computed at: TurboQuant pads a head_dim that is not a power of two (96)
+// with zeros to the next power of two, so the fast Walsh-Hadamard rotation applies ("TurboQuant KV
+// Cache Compression — Spec", "Hadamard Transform Detail"), and keeps every rotated coordinate.
+int stored_dim(const kvq_config& c) { return c.format == KVQ_FMT_TQ && c.head_dim == 96 ? 128 : c.head_dim; }
+}  // namespace kvq
+
 namespace {
 
 struct RecordSections {
@@ -54,7 +61,7 @@ int slot_bits(int bits, int dense3 = 0) { return bits == 3 ? (dense3 ? 3 : 4) : 
 
 RecordSections record_sections(const kvq_config& c) {
   RecordSections r;
-  const uint64_t D = c.head_dim;
+  const uint64_t D = stored_dim(c);
   r.kc = G * D * slot_bits(c.k_bits, c.tq_dense3) / 8;
   r.vc = G * D * slot_bits(c.v_bits, c.tq_dense3) / 8;
   if (c.format == KVQ_FMT_KIVI) {
@@ -83,8 +90,10 @@ kvq_status check(const kvq_config* c) {
     return fail(KVQ_EINVAL, "n_layers, batch, n_kv_heads and n_q_heads must be >= 1");
   if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > MAX_GQA)
     return fail(KVQ_EINVAL, "n_q_heads must be a multiple of n_kv_heads with ratio <= %d", MAX_GQA);
-  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
-    return fail(KVQ_EINVAL, "head_dim must be 32, 64 or 128 (got %d)", c->head_dim);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && !(c->head_dim == 96 && c->format == KVQ_FMT_TQ))
+    return fail(KVQ_EINVAL, "head_dim must be 32, 64 or 128, or 96 with TQ (got %d)", c->head_dim);
+  if (c->head_dim == 96 && c->sink_mode == KVQ_SINK_TOPK && c->n_sink > 0)
+    return fail(KVQ_EINVAL, "top-k sink selection needs head_dim 32, 64 or 128");
   auto okb = [](int b) { return b == 2 || b == 4 || b == 8; };
   switch (c->format) {
     case KVQ_FMT_KIVI:
@@ -124,7 +133,7 @@ kvq_layout make_layout(const kvq_config& c) {
   kvq_layout L;
   std::memset(&L, 0, sizeof(L));
   const RecordSections rs = record_sections(c);
-  const uint64_t S = (uint64_t)c.batch * c.n_kv_heads, D = c.head_dim;
+  const uint64_t S = (uint64_t)c.batch * c.n_kv_heads, D = stored_dim(c);
   const uint64_t esz = c.in_dtype == KVQ_IN_F32 ? 4 : 2;
   L.capacity = effective_capacity(c);
   L.cap_blocks = L.capacity / G;
@@ -168,7 +177,7 @@ kvq_layout make_layout(const kvq_config& c) {
 bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
   const uint64_t ring = (uint64_t)(effective_capacity(c) / G) * record_sections(c).rec;
-  return ring < (uint64_t(1) << 31) && c.head_dim == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope &&
+  return ring < (uint64_t(1) << 31) && stored_dim(c) == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope &&
          (r == 1 || r == 2 || r == 4 || r == 8) &&
          (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits) ||
           (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || (c.k_bits == 3 && !c.tq_dense3)) && c.v_bits == 2));
@@ -258,7 +267,8 @@ Shape shape_of(const kvq_config& c) {
   s.B = c.batch;
   s.Hkv = c.n_kv_heads;
   s.Hq = c.n_q_heads;
-  s.D = c.head_dim;
+  s.D = stored_dim(c);
+  s.Din = c.head_dim;
   s.fmt = c.format;
   s.kb = slot_bits(c.k_bits, c.tq_dense3);  // kernels address codes by their storage slots
   s.vb = slot_bits(c.v_bits, c.tq_dense3);
@@ -329,9 +339,9 @@ size_t kvq_workspace_bytes(const kvq_config* cfg) {
   const size_t streams = (size_t)cfg->batch * cfg->n_kv_heads;
   const size_t r = cfg->n_q_heads / cfg->n_kv_heads;
   const int parts = max_splits(*cfg) + std::max(1, fp16_parts(*cfg, (int64_t)cfg->residual + cfg->n_sink));
-  size_t bytes = streams * (size_t)parts * r * (size_t)(cfg->head_dim + 2) * sizeof(float);
+  size_t bytes = streams * (size_t)parts * r * (size_t)(stored_dim(*cfg) + 2) * sizeof(float);
   if (rope_decode_on_prefill(*cfg))  // row-block partials of the prefill kernel: up to 64 splits
-    bytes = std::max(bytes, streams * r * (size_t)ROPE_MAX_SPLITS * (cfg->head_dim + 4) * sizeof(float));
+    bytes = std::max(bytes, streams * r * (size_t)ROPE_MAX_SPLITS * (stored_dim(*cfg) + 4) * sizeof(float));
   return bytes;
 }
 
@@ -517,7 +527,7 @@ kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out
     const int streams = cf.batch * cf.n_kv_heads;
     const int want = std::max(1, (2048 + streams - 1) / streams);  // ~2048 workgroups (1024: 147 us, 4096: 155 us)
     pa.splits = std::max(1, std::min({ROPE_MAX_SPLITS, want, nrb}));
-    const size_t need = streams * r * (size_t)pa.splits * (cf.head_dim + 4) * sizeof(float);
+    const size_t need = streams * r * (size_t)pa.splits * (stored_dim(cf) + 4) * sizeof(float);
     if (need > ws_bytes)
       return fail(KVQ_ECAPACITY, "decode attention needs %zu workspace bytes; %zu given", need, ws_bytes);
     hipError_t e = launch_prefill(pa, (hipStream_t)stream);
@@ -538,7 +548,7 @@ kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out
   }
   a.fast = fast_path(cf);
   a.nparts = a.splits + fparts;
-  const size_t need = streams * (size_t)std::max(1, a.nparts) * r * (cf.head_dim + 2) * sizeof(float);
+  const size_t need = streams * (size_t)std::max(1, a.nparts) * r * (stored_dim(cf) + 2) * sizeof(float);
   if (need > ws_bytes)
     return fail(KVQ_ECAPACITY, "decode attention needs %zu workspace bytes; %zu given", need, ws_bytes);
   hipError_t e = launch_decode(a, (hipStream_t)stream);
@@ -560,8 +570,8 @@ kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t 
   if (n < 1 || n > P)
     return fail(KVQ_ERANGE, "prefill attention of n=%d queries needs 1 <= n <= P=%lld (the last n positions)", n,
                 (long long)P);
-  if (cf.head_dim != 32 && cf.head_dim != 64 && cf.head_dim != 128)
-    return fail(KVQ_EINVAL, "prefill attention needs head_dim 32, 64 or 128");
+  if (stored_dim(cf) != 32 && stored_dim(cf) != 64 && stored_dim(cf) != 128)
+    return fail(KVQ_EINVAL, "prefill attention needs head_dim 32, 64, 96 (TQ) or 128");
   if ((uintptr_t)q % 16 != 0 || (uintptr_t)out % 16 != 0) return fail(KVQ_EINVAL, "q and out must be 16-byte aligned");
   PrefillArgs a;
   a.sh = shape_of(cf);
@@ -619,7 +629,7 @@ kvq_status kvq_account(kvq_cache* c, int32_t layer, kvq_bytes* out, void* stream
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "account copy");
   const int64_t P = c->P[layer], lo = c->lo[layer], R = cf.residual;
-  const int64_t H = cf.n_kv_heads, D = cf.head_dim;
+  const int64_t H = cf.n_kv_heads, D = stored_dim(cf);  // stored rows (TurboQuant pads 96 to 128)
   const RecordSections rs = record_sections(cf);
   std::memset(out, 0, sizeof(*out));
   const int64_t wlo = std::max(lo, P - R);
@@ -676,7 +686,7 @@ kvq_status kvq_format_tables(const kvq_config* cfg, float* signs, float* k_bnd, 
   Tables t;
   make_tables(*cfg, &t);
   const int kl = 1 << cfg->k_bits, vl = 1 << cfg->v_bits;
-  if (signs) std::memcpy(signs, t.signs, sizeof(float) * cfg->head_dim);
+  if (signs) std::memcpy(signs, t.signs, sizeof(float) * stored_dim(*cfg));
   if (cfg->format == KVQ_FMT_TQ) {
     if (k_bnd) std::memcpy(k_bnd, t.k_bnd, sizeof(float) * (kl - 1));
     if (k_cen) std::memcpy(k_cen, t.k_cen, sizeof(float) * kl);

@@ -47,6 +47,8 @@ struct LayerView {
 
 struct Shape {
   int B, Hkv, Hq, D, fmt, kb, vb, sink_mode, n_sink, W, R, in_f32, rope;
+  int Din;  // channels of the caller's rows (q, K, V, outputs); D is the stored and computed width
+            // (TurboQuant pads a head_dim that is not a power of two to the next one, zeros in the pad)
 };
 
 struct AppendArgs {
@@ -129,6 +131,8 @@ void clear_error();
 
 // Host-side table generation (tables.cpp).
 void make_tables(const kvq_config& cfg, Tables* t);
+// Width rows are stored and computed at (TurboQuant: head_dim 96 padded to 128; else head_dim).
+int stored_dim(const kvq_config& c);
 
 // Decode attention with its split partials in ws (ws_bytes device bytes); KVQ_ECAPACITY, with nothing
 // launched, when this call's partials need more.  Shared by kvq_decode_attn (caller's workspace) and

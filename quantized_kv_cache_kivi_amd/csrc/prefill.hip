@@ -144,14 +144,14 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
           }
           continue;
         }
-        if (2 * lane < D) {
-          const int64_t qrow = (((int64_t)b * sh.Hq + ch) * a.n + cq) * D;
+        if (2 * lane < sh.Din) {  // query rows of Din channels (TurboQuant pads the rest with zeros)
+          const int64_t qrow = (((int64_t)b * sh.Hq + ch) * a.n + cq) * sh.Din;
           if (sh.in_f32) {
-            const float2 w = reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qrow)[lane];
+            const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qrow + 2 * lane);
             y0 = w.x;
             y1 = w.y;
           } else {
-            const uint32_t w = reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow)[lane];
+            const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + 2 * lane);
             y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
             y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
           }
@@ -561,8 +561,8 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         float y0 = 2 * lane < D ? os[col * D + 2 * lane] : 0.f;
         float y1 = 2 * lane < D ? os[col * D + 2 * lane + 1] : 0.f;
         wave_fwht(y0, y1, D, lane);
-        if (cok && 2 * lane < D) {
-          float* o = a.out + (((int64_t)b * sh.Hq + ch) * a.n + cq) * D;
+        if (cok && 2 * lane < sh.Din) {
+          float* o = a.out + (((int64_t)b * sh.Hq + ch) * a.n + cq) * sh.Din;
           *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(sg0 * (y0 * cd), sg1 * (y1 * cd));
         }
       }

@@ -142,7 +142,8 @@ void gaussian_lloyd_max4(float* thr, float* lvl) {
 void make_tables(const kvq_config& cfg, Tables* t) {
   std::memset(t, 0, sizeof(*t));
   uint64_t x = cfg.seed;
-  for (int i = 0; i < cfg.head_dim; ++i) t->signs[i] = (splitmix64_next(x) >> 63) ? -1.0f : 1.0f;
+  // one sign per stored (padded) coordinate; the codebooks follow Beta(head_dim/2, head_dim/2)
+  for (int i = 0; i < stored_dim(cfg); ++i) t->signs[i] = (splitmix64_next(x) >> 63) ? -1.0f : 1.0f;
   if (cfg.format == KVQ_FMT_TQ) {
     beta_lloyd_max(cfg.head_dim, cfg.k_bits, t->k_bnd, t->k_cen);
     beta_lloyd_max(cfg.head_dim, cfg.v_bits, t->v_bnd, t->v_cen);

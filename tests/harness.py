@@ -88,7 +88,7 @@ class Pair:
     # -- comparisons ----------------------------------------------------------------------------
     def gpu_regions(self, layer):
         c, L = self.ocfg, self.gpu.layout
-        S, D = c.batch * c.n_kv_heads, c.head_dim
+        S, D = c.batch * c.n_kv_heads, c.store_dim  # stored rows (TurboQuant pads head_dim 96 to 128)
         torch.cuda.synchronize()
         reg = lambda name, n: self.gpu.region(layer, name, n).cpu().numpy()  # noqa: E731
         out = {"bulk": reg("bulk", S * L.cap_blocks * L.record_bytes).reshape(S, L.cap_blocks, L.record_bytes)}

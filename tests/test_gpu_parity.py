@@ -66,6 +66,16 @@ CASES = {
                                       tq_dense3=True),
     "tq33_dense_d32_f32": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="tq", k_bits=3,
                                v_bits=3, capacity=512, in_dtype="f32", seed=19, tq_dense3=True),
+    # head_dim 96: rows zero-padded to 128 for the Walsh-Hadamard rotation, every rotated coordinate
+    # coded, Beta(48, 48) codebooks; K4/V2 on the matrix-core path, the others on the generic one
+    "fast_tq42_d96_r4_firstn_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=96, fmt="tq",
+                                        k_bits=4, v_bits=2, sink_mode="first_n", n_sink=3, residual=24,
+                                        capacity=512, seed=20),
+    "tq44_d96_f32_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=96, fmt="tq", k_bits=4,
+                             v_bits=4, sink_mode="first_n", n_sink=2, window=128, residual=8, in_dtype="f32",
+                             seed=21),
+    "tq32_dense_d96": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=6, head_dim=96, fmt="tq", k_bits=3,
+                           v_bits=2, capacity=512, seed=22, tq_dense3=True),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]

@@ -58,6 +58,11 @@ CASES = {
                             v_bits=4, residual=40, capacity=1024, in_dtype="f32"), [100, 7]),
     "tq42_r4_f32": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=4, v_bits=2,
                          sink_mode="first_n", n_sink=2, residual=16, capacity=1024, in_dtype="f32"), [90, 20]),
+    # head_dim 96: queries and outputs of 96 channels, rows padded to 128 for the rotation
+    "tq42_r4_d96": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=96, fmt="tq", k_bits=4, v_bits=2,
+                         sink_mode="first_n", n_sink=2, residual=16, capacity=1024, seed=23), [70, 33]),
+    "tq44_r2_d96_f32_ring": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=96, fmt="tq", k_bits=4,
+                                  v_bits=4, window=64, residual=8, in_dtype="f32", seed=24), [60, 20, 33]),
 }
 
 

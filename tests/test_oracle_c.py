@@ -26,7 +26,7 @@ def test_fp16_conversion_matches_ieee_round_to_nearest_even():
         assert np.array_equal(c_model.f32_to_f16(x), x.astype(np.float16).view(np.uint16))
 
 
-@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 160])
 def test_tables_equal_the_numpy_oracle(d):
     for bits in (2, 3, 4):
         nb, nc = turboquant.codebook(d, bits)
@@ -58,6 +58,10 @@ CASES = {
                                       tq_dense3=True, seed=5),
     "tq_k3v3_d32": dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=2, head_dim=32, fmt="tq", k_bits=3, v_bits=3,
                         seed=9, in_dtype="f32"),
+    "tq_k4v2_d96_window": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=96, fmt="tq", k_bits=4,
+                               v_bits=2, sink_mode="first_n", n_sink=2, window=70, residual=8, seed=31),
+    "tq_k4v4_d160_f32": dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=2, head_dim=160, fmt="tq", k_bits=4,
+                             v_bits=4, residual=4, in_dtype="f32", seed=32),
 }
 SCHEDULE = [70, 1, 1, 33, 1, 20, 2, 31, 1, 17, 1]
 
