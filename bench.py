@@ -381,9 +381,9 @@ def rope_figure(cfgno, kw, pre_k, pre_v, sinks_per_b, seed, dev, stream):
     res = {"decode_attn": {"us": t * 1e3, "bytes": nb, "GBps": nb / (t * 1e-3) / 1e9,
                            "roofline": {"bound": "hbm", "achieved": nb / (t * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS,
                                         "unit": "GB/s", "frac": nb / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS},
-                           "note": "one-query prefill-attention kernel split over row blocks, then a merge "
-                                   "(the matrix-core decode path keeps a per-block query fold, which a per-row "
-                                   "rotation breaks)"}}
+                           "note": "matrix-core decode kernel (one launch): keys dequantized in fp32 and turned "
+                                   "by their row in the 16-token tile, the query turned per tile by the position "
+                                   "difference; fp16 window and sink rows turned by index difference"}}
     pa = prefill_attention_figure(kw, c, T0, sinks_per_b, seed, dev, stream)
     if pa is not None:
         pa["note"] = "matrix-core kernel; staged keys turned in LDS, queries as fp16 hi + lo (3 score products)"

@@ -110,8 +110,11 @@ typedef struct {
                          index in the compressed cache ([SK] "RoPE caveat", "Caveats": StreamingLLM's
                          re-positioning); 0: off.  Not with TQ. */
   float rope_base;    /* RoPE base (<= 0: 10000); channel c < head_dim/2 pairs with c + head_dim/2 and turns
-                         by idx * base^(-2c/head_dim), idx = the number of valid positions before the row
-                         (a query: before its own position) */
+                         by the exact angle idx * theta_c, theta_c = base^(-2c/head_dim) rounded to fp32,
+                         idx = the number of valid positions before the row (a query: before its own
+                         position); capacity + n_sink must stay below 2^24.  On the matrix-core decode path
+                         (head_dim 128, fp16, KIVI with k_bits = v_bits) the turned keys enter the matrix
+                         cores as fp16 pairs and must stay below 65504 in magnitude. */
   int32_t tq_dense3;  /* TQ with a 3-bit side: 1 stores 3-bit codes as a dense stream, 8 codes in 3 bytes
                          ([TQ] "Step 3: Packing"; code i of a section's sequence at bits 3i .. 3i+2, LSB
                          first); 0 (default) two per byte in 4-bit slots */

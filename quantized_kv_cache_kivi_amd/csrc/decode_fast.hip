@@ -208,23 +208,28 @@ __device__ __forceinline__ u4 splane_a(const uint32_t* nd, int k, uint32_t one16
   return u4{o[0], o[1], o[2], o[3]};
 }
 
-template <int R>
+template <int R, bool RP>
 struct alignas(16) FastWave {
   static constexpr int NC = 2 * R;  // MFMA columns in use: hi halves of heads 0..R-1, then lo halves
+  static constexpr int QV = RP ? 2 : 1;  // query operands: RoPE keeps one per 16-token row tile
   // Rows are padded by 16 bytes so that the 16 column lanes of an MFMA operand read (and the
   // 16-byte score stores) fall on distinct LDS banks.
   union {
-    uint32_t qb[NC][FD / 2 + 4];  // query operand: [column][channel pair]
-    float o[R][FD];               // wave output for the workgroup merge
+    uint32_t qb[QV][NC][FD / 2 + 4];  // query operand: [row tile][column][channel pair]
+    float o[R][FD];                   // wave output for the workgroup merge
   } x;
   float ps[NC][G + 4];            // raw score columns of the current block
-  float kp[R][64 + 4];            // zero-point (q2k: c0) term per head and lane
+  float kp[RP ? 1 : R][64 + 4];   // zero-point (q2k: c0) term per head and lane (not with RoPE)
+  uint32_t km[RP ? 2 : 1][RP ? 64 : 1];  // RoPE: the block's K scales and zeros, channel pairs
   uint32_t ab[4][NC][4 * 4 + 4];  // weights x V scale: [group][column][4 * token group + pair]
   float f[R], zt[R][4], m[R], l[R];
 };
-template <int R>
+template <int R, bool RP>
 struct FastSmem {
-  FastWave<R> w[NW];
+  FastWave<R, RP> w[NW];
+  // RoPE: cos, sin of i * theta_f for rows i < 16, [i][2 f + (0: cos, 1: sin)], rows padded by 16
+  // bytes (the 16 row lanes of a read fall on distinct banks)
+  float rk[RP ? 16 : 1][RP ? 2 * 64 + 4 : 1];
   int sinks[MAX_SINK];  // committed sink positions (< P) of this batch element
   int nsinks;
   uint32_t tq_tab[16];  // TurboQuant K centroids: fp16 hi | fp16 lo << 16
@@ -239,9 +244,9 @@ struct FpSmem {
   int spos[MAX_SINK], sslot[MAX_SINK];
   int nsink;
 };
-template <int R>
+template <int R, bool RP>
 union DecSmem {
-  FastSmem<R> bulk;
+  FastSmem<R, RP> bulk;
   FpSmem<R> fp;
   float rot[2][FD];  // the merging workgroup: TurboQuant outputs rotated back, two heads at a time
 };
@@ -249,7 +254,8 @@ union DecSmem {
 // What one lane reads from a block record.
 template <int KB, int VB>
 struct Blk {
-  uint32_t kd[2][KB];  // K code rows i16 and 16 + i16, channels 32*kg .. 32*kg + 31
+  uint32_t kd[2][KB];  // K code rows i16 and 16 + i16, channels 32*kg .. 32*kg + 31 (RoPE: channels
+                       // 16*kg .. 16*kg + 15 in kd[.][0, KB/2), their partners + 64 in kd[.][KB/2, KB))
   uint32_t ks, kz;     // K scale (q2k: rms) and zero of channels 2*lane, 2*lane + 1
                        // (TurboQuant: fp32 K norms of tokens 2*i16, 2*i16 + 1)
   uint32_t vd[2 * VB]; // V code chunk `lane`
@@ -261,12 +267,13 @@ struct Blk {
 struct BlkOffs {
   uint32_t k[2], ks, kz, v, vs, vz;
 };
-template <int FMT, int KB, int VB>
+template <int FMT, int KB, int VB, bool RP>
 __device__ __forceinline__ BlkOffs blk_offsets(const LayerView& lv, int lane) {
   const int i16 = lane & 15, kg = lane >> 4;
   BlkOffs o;
 #pragma unroll
-  for (int tau = 0; tau < 2; ++tau) o.k[tau] = (uint32_t)(lv.k_codes + (16 * tau + i16) * (FD * KB / 8) + kg * 4 * KB);
+  for (int tau = 0; tau < 2; ++tau)  // a code row is FD * KB / 8 bytes; RoPE: 16 channels are 2 * KB bytes
+    o.k[tau] = (uint32_t)(lv.k_codes + (16 * tau + i16) * (FD * KB / 8) + kg * (RP ? 2 : 4) * KB);
   if constexpr (FMT == KVQ_FMT_TQ) {  // per-token fp32 norms: tokens 2*i16, 2*i16 + 1
     o.ks = (uint32_t)(lv.k_meta + 8 * i16);
     o.kz = o.ks;
@@ -284,7 +291,7 @@ __device__ __forceinline__ BlkOffs blk_offsets(const LayerView& lv, int lane) {
 
 // One block record into registers: buffer loads from the stream's ring with the record's byte
 // offset in a scalar register and fixed per-lane offsets (no address arithmetic per block).
-template <int FMT, int KB, int VB>
+template <int FMT, int KB, int VB, bool RP>
 __device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t rs, uint32_t rec_off,
                                          const BlkOffs& o) {
   constexpr bool Q2K = FMT == KVQ_FMT_Q2K, TQ = FMT == KVQ_FMT_TQ;
@@ -293,7 +300,21 @@ __device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t 
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int tau = 0; tau < 2; ++tau) {
-    if constexpr (KB == 2) {
+    if constexpr (RP) {  // channels 16*kg .. 16*kg + 15 and the same + 64 (8 * KB bytes further)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const uint32_t off = o.k[tau] + hf * 8 * KB;
+        if constexpr (KB == 2) {
+          d.kd[tau][hf] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, rec_off, 0);
+        } else if constexpr (KB == 4) {
+          const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, off, rec_off, 0);
+          d.kd[tau][2 * hf] = x.x, d.kd[tau][2 * hf + 1] = x.y;
+        } else {
+          const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, rec_off, 0);
+          d.kd[tau][4 * hf] = x.x, d.kd[tau][4 * hf + 1] = x.y, d.kd[tau][4 * hf + 2] = x.z, d.kd[tau][4 * hf + 3] = x.w;
+        }
+      }
+    } else if constexpr (KB == 2) {
       const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k[tau], rec_off, 0);
       d.kd[tau][0] = x.x, d.kd[tau][1] = x.y;
     } else {
@@ -337,6 +358,41 @@ struct Fast {
   static constexpr int NKA = Q2K ? 2 : 1;         // K accumulators per token tile (q2k: one per code bit)
 };
 
+// RoPE on read ("StreamingLLM + KIVI — long-context decode without growing the KV cache", "RoPE
+// caveat"): a bulk row at position p (>= lo, like the query's own position P - 1) has index
+// (sinks below lo) + p - lo, so q(P-1) . k(p) = q R((P-1-p) theta) . k: the query turns by
+// (P - 1 - p0 - 16 tau) theta per 16-token row tile tau of a block at p0 (the MFMA column operand of
+// that tile), the key of row i16 of the tile by i16 theta (a per-lane constant), dequantized in
+// fp32 and split into fp16 hi + lo halves for the MFMA.  Per-lane state of a wave:
+template <int R>
+struct RopeLane {
+  h2 ql[R], qh[R];           // query channels fp, fp + 1 and fp + 64, fp + 65 (fp = 2 * (lane & 31))
+  float c[2], s[2];          // cos, sin of the current block's query angle, frequencies fp, fp + 1
+  float cst[2], sst[2];      // cos, sin of one wave step (NW blocks) at those frequencies
+  const float* rk;           // cos, sin of i16 * theta_f, f = 16 * kg + 0..15 (LDS)
+};
+
+// Dword index, inside a query operand row, of the channel pair (c, c + 1) (c even) in the RoPE
+// K order: step st < 2 takes channels 16 kg + 8 st .. + 7, step st >= 2 the same + 64.
+__device__ __forceinline__ int rope_qpair(int c) {
+  const int h = c >> 6, x = c & 63;
+  return 16 * (x >> 4) + 4 * (2 * h + ((x >> 3) & 1)) + ((x >> 1) & 3);
+}
+// KB-bit code of channel 8 sp + 2 r + e of half hf (channels 16 kg .. + 15, or + 64) of a RoPE
+// code row: a dword holds the 16 / KB channel pairs i at bits KB i (even) and 16 + KB i (odd).
+template <int KB>
+__device__ __forceinline__ uint32_t rope_code(const uint32_t* kd, int hf, int sp, int r, int e) {
+  constexpr int PPD = 16 / KB;  // channel pairs per dword
+  const int pi = 4 * sp + r;
+  return (kd[hf * (KB / 2) + pi / PPD] >> (KB * (pi % PPD) + 16 * e)) & ((1u << KB) - 1u);
+}
+// fp16 hi = rz(a), rz(b) and lo = rz((x - hi) * up) of two fp32 values, packed pairs.
+__device__ __forceinline__ void split16(float a, float b, float up, uint32_t& hi, uint32_t& lo) {
+  const h2 h = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));
+  hi = U32(h);
+  lo = U32(__builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz((a - (float)h.x) * up, (b - (float)h.y) * up)));
+}
+
 // Per-lane state of a wave over its blocks.
 template <int FMT, int KB, int VB, int R>
 struct State {
@@ -351,10 +407,10 @@ struct State {
   f4 acc[8];
 };
 
-template <int FMT, int KB, int VB, int R>
-__device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>& W, const int* sinks,
-                                           const Blk<KB, VB>& d, int blk, int blo, int bhi, int sblk, int nsink,
-                                           float q2k_w, const uint32_t* tab, int lane) {
+template <int FMT, int KB, int VB, int R, bool RP>
+__device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R, RP>& W, const RopeLane<R>& Q,
+                                           const int* sinks, const Blk<KB, VB>& d, int blk, int blo, int bhi,
+                                           int sblk, int nsink, float q2k_w, const uint32_t* tab, int lane) {
   using F = Fast<FMT, KB, VB, R>;
   constexpr bool Q2K = F::Q2K;
   constexpr bool TQ = F::TQ;
@@ -364,26 +420,90 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
   const int col = i16 < F::NC ? i16 : F::NC - 1;
 
   // ---- query operand: the exact products q * s split hi (column j) / lo (R + j), times 2^-pos ----
-  // (TurboQuant: the rotated query, written once before the loop)
-  if constexpr (!TQ) {
+  // (TurboQuant: the rotated query, written once before the loop; RoPE: the turned query of each
+  // row tile, and the block's K scales and zeros for the dequantization)
+  if constexpr (RP) {
+    W.km[0][lane] = d.ks;
+    W.km[1][lane] = d.kz;
+    const int tq = lane >> 5, fp = 2 * (lane & 31);
+    const int il = rope_qpair(fp), ih = rope_qpair(64 + fp);
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float x0 = (float)Q.ql[j].x, x1 = (float)Q.ql[j].y, y0 = (float)Q.qh[j].x, y1 = (float)Q.qh[j].y;
+      uint32_t h, l;
+      split16(x0 * Q.c[0] - y0 * Q.s[0], x1 * Q.c[1] - y1 * Q.s[1], LOK_UP, h, l);
+      W.x.qb[tq][j][il] = h;
+      W.x.qb[tq][R + j][il] = l;
+      split16(y0 * Q.c[0] + x0 * Q.s[0], y1 * Q.c[1] + x1 * Q.s[1], LOK_UP, h, l);
+      W.x.qb[tq][j][ih] = h;
+      W.x.qb[tq][R + j][ih] = l;
+    }
+  } else if constexpr (!TQ) {
     const h2 s2 = H2(d.ks);
     const h2 z2 = Q2K ? s2 : H2(d.kz);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       uint32_t h, l;
       mul_split(S.q2[j], s2, h, l);
-      W.x.qb[j][lane] = U32(H2(h) * S.fa2);
-      W.x.qb[R + j][lane] = U32(H2(l) * S.fa2l);
+      W.x.qb[0][j][lane] = U32(H2(h) * S.fa2);
+      W.x.qb[0][R + j][lane] = U32(H2(l) * S.fa2l);
       W.kp[j][lane] = dot2(S.q2[j], z2, 0.f);
     }
   }
   // ---- scores: raw MFMA columns to LDS ----
-  {
+  if constexpr (RP) {
+    // keys k = u s + z per channel (fp32), turned by i16 theta in (f, f + 64) pairs, split into fp16
+    // hi and lo * 2^11 (two MFMA products per step; the lo product enters at 2^-11)
+    f4 c0[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    f4 c1[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+      const u4 sl = *reinterpret_cast<const u4*>(&W.km[0][8 * kg + 4 * sp]);
+      const u4 zl = *reinterpret_cast<const u4*>(&W.km[1][8 * kg + 4 * sp]);
+      const u4 sh = *reinterpret_cast<const u4*>(&W.km[0][32 + 8 * kg + 4 * sp]);
+      const u4 zh = *reinterpret_cast<const u4*>(&W.km[1][32 + 8 * kg + 4 * sp]);
+      const uint32_t slv[4] = {sl.x, sl.y, sl.z, sl.w}, zlv[4] = {zl.x, zl.y, zl.z, zl.w};
+      const uint32_t shv[4] = {sh.x, sh.y, sh.z, sh.w}, zhv[4] = {zh.x, zh.y, zh.z, zh.w};
+      float kc[8], ks[8];  // frequencies 16 kg + 8 sp + 0..7
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f4 t = *reinterpret_cast<const f4*>(Q.rk + 16 * sp + 4 * m);
+        kc[2 * m] = t[0], ks[2 * m] = t[1], kc[2 * m + 1] = t[2], ks[2 * m + 1] = t[3];
+      }
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        uint32_t ahl[4], all[4], ahh[4], alh[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float rl[2], rh[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float kl = __builtin_fmaf((float)rope_code<KB>(d.kd[tau], 0, sp, r, e), h16(slv[r], e), h16(zlv[r], e));
+            const float kh = __builtin_fmaf((float)rope_code<KB>(d.kd[tau], 1, sp, r, e), h16(shv[r], e), h16(zhv[r], e));
+            const int fi = 2 * r + e;
+            rl[e] = kl * kc[fi] - kh * ks[fi];
+            rh[e] = kh * kc[fi] + kl * ks[fi];
+          }
+          split16(rl[0], rl[1], LO_UP, ahl[r], all[r]);
+          split16(rh[0], rh[1], LO_UP, ahh[r], alh[r]);
+        }
+        const u4 bl = *reinterpret_cast<const u4*>(&W.x.qb[tau][col][16 * kg + 4 * sp]);
+        const u4 bh = *reinterpret_cast<const u4*>(&W.x.qb[tau][col][16 * kg + 4 * (sp + 2)]);
+        c0[tau] = mfma(u4{ahl[0], ahl[1], ahl[2], ahl[3]}, bl, c0[tau]);
+        c0[tau] = mfma(u4{ahh[0], ahh[1], ahh[2], ahh[3]}, bh, c0[tau]);
+        c1[tau] = mfma(u4{all[0], all[1], all[2], all[3]}, bl, c1[tau]);
+        c1[tau] = mfma(u4{alh[0], alh[1], alh[2], alh[3]}, bh, c1[tau]);
+      }
+    }
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+      *reinterpret_cast<f4*>(&W.ps[col][16 * tau + 4 * kg]) = c0[tau] + c1[tau] * LO_DOWN;
+  } else {
     f4 c0[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
     f4 c1[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      const u4 b = *reinterpret_cast<const u4*>(&W.x.qb[col][16 * kg + 4 * st]);
+      const u4 b = *reinterpret_cast<const u4*>(&W.x.qb[0][col][16 * kg + 4 * st]);
 #pragma unroll
       for (int tau = 0; tau < 2; ++tau) {
         if constexpr (Q2K) {
@@ -433,8 +553,11 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
       y0[p] = ok0 ? __builtin_fmaf(lo.x, LOK_DOWN, hi.x) * (S.cs * F32(d.ks)) : -INFINITY;
       y1[p] = ok1 ? __builtin_fmaf(lo.y, LOK_DOWN, hi.y) * (S.cs * F32(d.kz)) : -INFINITY;
     } else {
-      const f4 kq = *reinterpret_cast<const f4*>(&W.kp[j][4 * tp]);
-      const float kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3])) * S.kc;
+      float kap = 0.f;  // RoPE: the zeros are inside the dequantized keys
+      if constexpr (!RP) {
+        const f4 kq = *reinterpret_cast<const f4*>(&W.kp[j][4 * tp]);
+        kap = row_sum16((kq[0] + kq[1]) + (kq[2] + kq[3])) * S.kc;
+      }
       y0[p] = ok0 ? __builtin_fmaf(__builtin_fmaf(lo.x, LOK_DOWN, hi.x), S.cs, kap) : -INFINITY;
       y1[p] = ok1 ? __builtin_fmaf(__builtin_fmaf(lo.y, LOK_DOWN, hi.y), S.cs, kap) : -INFINITY;
     }
@@ -524,8 +647,8 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R>
   }
 }
 
-template <int FMT, int KB, int VB, int R>
-__device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
+template <int FMT, int KB, int VB, int R, bool RP>
+__device__ void bulk_partial(const DecodeArgs& a, FastSmem<R, RP>& F, int sigma) {
   using Fc = Fast<FMT, KB, VB, R>;
   using St = State<FMT, KB, VB, R>;
   constexpr bool Q2K = Fc::Q2K;
@@ -537,7 +660,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform: keeps the loop scalar)
   const int i16 = lane & 15, kg = lane >> 4;
-  const int sigma = blockIdx.y, s = blockIdx.x, b = s / sh.Hkv, g = s % sh.Hkv;
+  const int s = blockIdx.x, b = s / sh.Hkv, g = s % sh.Hkv;
   auto& W = F.w[wv];
 
   const int first = sigma * a.blocks_per_split;
@@ -548,7 +671,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   // the stream's ring as a buffer resource (every record offset fits in 32 bits: checked on the host)
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(lv.bulk + (int64_t)s * lv.cap_b * lv.rec), 0, (int)(lv.cap_b * lv.rec), 0x00020000);
-  const BlkOffs bo = blk_offsets<FMT, KB, VB>(lv, lane);
+  const BlkOffs bo = blk_offsets<FMT, KB, VB, RP>(lv, lane);
   auto rec_of = [&](int bi) -> uint32_t {
     bi = bi < lastb ? bi : lastb - 1;  // past the split: re-read its last block (a cache hit), never used
     int sl = slot0 + bi;
@@ -562,7 +685,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
   // carries exactly one block (the compiler's wait counts inside the loop then stay exact).
   Blk<KB, VB> d0, d1;
   int bi = first + wv;
-  if (bi < lastb) load_blk<FMT>(d0, rs, rec_of(bi), bo);
+  if (bi < lastb) load_blk<FMT, KB, VB, RP>(d0, rs, rec_of(bi), bo);
   St S;
   const float al = a.scale * LOG2E;
   float q2k_w = 0.f, tq_c0 = 0.f;
@@ -590,10 +713,54 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
     S.cs = ldexpf(c1 * al, 24);
     S.kc = c0 * al;
     q2k_w = c2 / (2.f * c1);  // the b1 accumulator carries an extra factor 2 (bit 2r + 1)
-  } else {
-    S.cs = ldexpf(al, 24);
-    S.kc = al;
+  } else {  // codes enter as u * 2^(pos - 24) (RoPE: as dequantized keys)
+    S.cs = RP ? al : ldexpf(al, 24);
+    S.kc = RP ? 0.f : al;
   }
+  RopeLane<R> Q;
+  int kq = 0;  // RoPE: P - 1 - p0 - 16 tau of the wave's current block (tau = lane >> 5)
+  if constexpr (RP) {
+    const int fp = 2 * (lane & 31);
+    const _Float16* qs = static_cast<const _Float16*>(a.q) + ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      Q.ql[j] = H2(*reinterpret_cast<const uint32_t*>(qs + j * FD + fp));
+      Q.qh[j] = H2(*reinterpret_cast<const uint32_t*>(qs + j * FD + 64 + fp));
+    }
+    for (int idx = tid; idx < 16 * 64; idx += DNT) {
+      const int i = idx >> 6, f = idx & 63;
+      F.rk[i][2 * f] = lv.tables->rope_row[i][f][0];
+      F.rk[i][2 * f + 1] = lv.tables->rope_row[i][f][1];
+    }
+    Q.rk = &F.rk[i16][2 * 16 * kg];
+    kq = (int)(a.P - 1 - (int64_t)(blkf + bi) * G) - 16 * (lane >> 5);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float th = lv.tables->rope_inv[fp + e];
+      rope_cs(kq, th, Q.c[e], Q.s[e]);
+      rope_cs(NW * G, th, Q.cst[e], Q.sst[e]);
+    }
+  }
+  // next block of the wave: the query angle steps back by NW * G positions (a rotation; every 16th
+  // step recomputed from the index, so rounding does not accumulate)
+  int nstep = 0;
+  auto rope_next = [&]() {
+    if constexpr (RP) {
+      kq -= NW * G;
+      if ((++nstep & 15) == 0) {
+        const int fp = 2 * (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) rope_cs(kq, lv.tables->rope_inv[fp + e], Q.c[e], Q.s[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float c = Q.c[e], sn = Q.s[e];
+          Q.c[e] = __builtin_fmaf(c, Q.cst[e], sn * Q.sst[e]);
+          Q.s[e] = __builtin_fmaf(sn, Q.cst[e], -c * Q.sst[e]);
+        }
+      }
+    }
+  };
   {
     const int64_t qrow = ((int64_t)b * sh.Hq + (int64_t)g * R) * sh.Din;  // query rows of Din channels
     const int pk = Q2K ? 2 * (lane & 3) : code_pos<KB>(lane & 3);
@@ -645,8 +812,8 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
       y1 *= cd;
       const h2 h = h2{(_Float16)y0, (_Float16)y1};
       const h2 l = h2{(_Float16)((y0 - (float)h.x) * LOK_UP), (_Float16)((y1 - (float)h.y) * LOK_UP)};
-      W.x.qb[j][lane] = U32(h);
-      W.x.qb[R + j][lane] = U32(l);
+      W.x.qb[0][j][lane] = U32(h);
+      W.x.qb[0][R + j][lane] = U32(l);
     }
   }
 
@@ -655,12 +822,14 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
 
   if (bi < lastb) {
     while (true) {
-      load_blk<FMT>(d1, rs, rec_of(bi + NW), bo);
-      block_step(S, W, F.sinks, d0, blkf + bi, blo, bhi, sblk, nsink, q2k_w, F.tq_tab, lane);
+      load_blk<FMT, KB, VB, RP>(d1, rs, rec_of(bi + NW), bo);
+      block_step(S, W, Q, F.sinks, d0, blkf + bi, blo, bhi, sblk, nsink, q2k_w, F.tq_tab, lane);
+      rope_next();
       bi += NW;
       if (bi >= lastb) break;
-      load_blk<FMT>(d0, rs, rec_of(bi + NW), bo);
-      block_step(S, W, F.sinks, d1, blkf + bi, blo, bhi, sblk, nsink, q2k_w, F.tq_tab, lane);
+      load_blk<FMT, KB, VB, RP>(d0, rs, rec_of(bi + NW), bo);
+      block_step(S, W, Q, F.sinks, d1, blkf + bi, blo, bhi, sblk, nsink, q2k_w, F.tq_tab, lane);
+      rope_next();
       bi += NW;
       if (bi >= lastb) break;
     }
@@ -734,7 +903,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R>& F) {
 // workgroup's rows; values: one channel pair per lane, rows split over the 4 waves.  Every row load
 // (the K quarter a thread scores and the V words its wave accumulates) is issued at once, right
 // after the sink list is known.
-template <int R>
+template <int R, bool RP>
 __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
   constexpr int VPW = FPR / NW;  // rows per wave in the values phase
   const Shape sh = a.sh;
@@ -772,7 +941,7 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
     return (v_side ? lv.sink_v : lv.sink_k) + ((int64_t)s * sh.n_sink + F.sslot[i - nwin]) * FD;
   };
   const int lr = tid >> 2, qq = tid & 3, i = r0 + lr;
-  u4 kw[4];
+  u4 kw[4] = {u4{0, 0, 0, 0}, u4{0, 0, 0, 0}, u4{0, 0, 0, 0}, u4{0, 0, 0, 0}};
   if (lr < nr) {
     const u4* kr = reinterpret_cast<const u4*>(row_ptr(i, false) + 32 * qq);
 #pragma unroll
@@ -790,9 +959,58 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
     float acc[R];
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[j] = 0.f;
-    if (ok) {
-      if (i < nwin)
-        for (int q = 0; q < F.nsink; ++q) ok = ok && F.spos[q] != a.bulk_hi + i;
+    if (ok && i < nwin)
+      for (int q = 0; q < F.nsink; ++q) ok = ok && F.spos[q] != a.bulk_hi + i;
+    if constexpr (RP) {
+      // RoPE: q(m) . k(n) = q . R((n - m) theta) k with m the query's index: the row turns by its
+      // index minus the query's, the query is used as handed over.  This thread's channels 32 qq ..
+      // 32 qq + 31 pair with those of thread tid ^ 2 (channels -+ 64, one DPP step): each of the two
+      // computes the cos and sin of half of their 32 shared frequencies.
+      const int qi = cache_index(F.spos, F.nsink, a.lo, a.P - 1);
+      int dn = 0;
+      if (lr < nr) dn = cache_index(F.spos, F.nsink, a.lo, i < nwin ? a.bulk_hi + i : (int64_t)F.spos[i - nwin]) - qi;
+      const int f0 = 32 * (qq & 1), hsel = qq >> 1;
+      float cw[16], sw[16];  // frequencies f0 + 16 hsel + k
+#pragma unroll
+      for (int k = 0; k < 16; ++k) rope_cs(dn, a.lv.tables->rope_inv[f0 + 16 * hsel + k], cw[k], sw[k]);
+      const uint32_t xw[16] = {kw[0].x, kw[0].y, kw[0].z, kw[0].w, kw[1].x, kw[1].y, kw[1].z, kw[1].w,
+                               kw[2].x, kw[2].y, kw[2].z, kw[2].w, kw[3].x, kw[3].y, kw[3].z, kw[3].w};
+      uint32_t kh[16], kl[16];  // turned key, fp16 hi and lo * 2^11, channel pairs 32 qq + 2 w
+#pragma unroll
+      for (int w = 0; w < 16; ++w) {
+        const uint32_t yw = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)xw[w], 0x4E, 0xF, 0xF, false);
+        const bool mine = hsel == (w >> 3);
+        float rr[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int k = 2 * (w & 7) + e;
+          // the partner's values are read in every lane (a DPP read from a lane outside the active
+          // mask would return 0), then selected
+          const float cp = dpp<0x4E>(cw[k]), spn = dpp<0x4E>(sw[k]);
+          const float cs = mine ? cw[k] : cp, sn = mine ? sw[k] : spn;
+          const float x = h16(xw[w], e), y = h16(yw, e);
+          rr[e] = qq < 2 ? x * cs - y * sn : x * cs + y * sn;
+        }
+        split16(rr[0], rr[1], LO_UP, kh[w], kl[w]);
+      }
+      if (ok) {
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          float ah = 0.f, alo = 0.f;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const u4 qw = *reinterpret_cast<const u4*>(&F.q[j][16 * qq + 4 * k]);
+            const uint32_t qv[4] = {qw.x, qw.y, qw.z, qw.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              ah = dot2(H2(qv[t]), H2(kh[4 * k + t]), ah);
+              alo = dot2(H2(qv[t]), H2(kl[4 * k + t]), alo);
+            }
+          }
+          acc[j] = __builtin_fmaf(alo, LO_DOWN, ah);
+        }
+      }
+    } else if (ok) {
 #pragma unroll
       for (int j = 0; j < R; ++j) {
 #pragma unroll
@@ -866,9 +1084,9 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
 }
 
 // Waves per SIMD the register allocation targets.
-template <int FMT, int KB, int VB, int R>
+template <int FMT, int KB, int VB, int R, bool RP>
 constexpr int waves_target() {
-  return (R <= 4 && (KB == 2 || FMT == KVQ_FMT_TQ)) ? 3 : 2;
+  return (!RP && R <= 4 && (KB == 2 || FMT == KVQ_FMT_TQ)) ? 3 : 2;
 }
 
 // Online merge of partials [q0, q1) of one (stream, query head) into (M, L, v): the partials are read
@@ -939,13 +1157,16 @@ __device__ void merge_stream(const DecodeArgs& a, int s, float (*rot)[FD]) {
   }
 }
 
-template <int FMT, int KB, int VB, int R>
-__global__ __launch_bounds__(DNT) __attribute__((amdgpu_waves_per_eu(waves_target<FMT, KB, VB, R>())))
+// RoPE workgroups: the fp16-row groups come first in the grid (each of their rows takes its own
+// rotation, which makes them longer than a bulk split's share), then the bulk splits.
+template <int FMT, int KB, int VB, int R, bool RP>
+__global__ __launch_bounds__(DNT) __attribute__((amdgpu_waves_per_eu(waves_target<FMT, KB, VB, R, RP>())))
 void k_decode_fast(DecodeArgs a) {
-  __shared__ DecSmem<R> S;
+  __shared__ DecSmem<R, RP> S;
   __shared__ int last;
-  if ((int)blockIdx.y < a.splits) bulk_partial<FMT, KB, VB, R>(a, S.bulk);
-  else fp16_partial<R>(a, S.fp, (int)blockIdx.y - a.splits);
+  const int y = blockIdx.y, nfp = a.nparts - a.splits;
+  if (RP ? y >= nfp : y < a.splits) bulk_partial<FMT, KB, VB, R, RP>(a, S.bulk, RP ? y - nfp : y);
+  else fp16_partial<R, RP>(a, S.fp, RP ? y : y - a.splits);
   // publish the partial: its stores complete before the arrival is counted
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
@@ -960,39 +1181,40 @@ void k_decode_fast(DecodeArgs a) {
   merge_stream<R, FMT == KVQ_FMT_TQ>(a, s, S.rot);
 }
 
-template <int FMT, int KB, int VB>
+template <int FMT, int KB, int VB, bool RP>
 hipError_t launch_r(const DecodeArgs& a, hipStream_t st) {
   const int r = a.sh.Hq / a.sh.Hkv;
   const int S = a.sh.B * a.sh.Hkv;
-  // parts vary slowest: the (short) fp16 workgroups are dispatched after every bulk split
+  // parts vary slowest: the (short) fp16 workgroups are dispatched after every bulk split (RoPE:
+  // before them)
   dim3 grid(S, a.nparts);
   switch (r) {
     case 1:
-      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 1>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 1, RP>), grid, dim3(DNT), 0, st, a);
       break;
     case 2:
-      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 2>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 2, RP>), grid, dim3(DNT), 0, st, a);
       break;
     case 4:
-      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 4>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 4, RP>), grid, dim3(DNT), 0, st, a);
       break;
     case 8:
-      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 8>), grid, dim3(DNT), 0, st, a);
+      hipLaunchKernelGGL((k_decode_fast<FMT, KB, VB, 8, RP>), grid, dim3(DNT), 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int FMT, int KB, int VB>
+template <int FMT, int KB, int VB, bool RP>
 int slots_r(int r, int per_cu) {
   int nb = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (r) {
-    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 1>, DNT, 0); break;
-    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 2>, DNT, 0); break;
-    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 4>, DNT, 0); break;
-    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 8>, DNT, 0); break;
+    case 1: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 1, RP>, DNT, 0); break;
+    case 2: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 2, RP>, DNT, 0); break;
+    case 4: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 4, RP>, DNT, 0); break;
+    case 8: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, k_decode_fast<FMT, KB, VB, 8, RP>, DNT, 0); break;
     default: break;
   }
   return e == hipSuccess ? nb * per_cu : 0;
@@ -1007,12 +1229,20 @@ int fast_resident_slots(const Shape& sh) {
     return 0;
   const int r = sh.Hq / sh.Hkv;
   if (sh.D != FD) return 0;
-  if (sh.fmt == KVQ_FMT_Q2K) return slots_r<KVQ_FMT_Q2K, 2, 4>(r, cus);
-  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return slots_r<KVQ_FMT_TQ, 4, 2>(r, cus);
+  if (sh.rope) {
+    if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
+      if (sh.kb == 2) return slots_r<KVQ_FMT_KIVI, 2, 2, true>(r, cus);
+      if (sh.kb == 4) return slots_r<KVQ_FMT_KIVI, 4, 4, true>(r, cus);
+      if (sh.kb == 8) return slots_r<KVQ_FMT_KIVI, 8, 8, true>(r, cus);
+    }
+    return 0;
+  }
+  if (sh.fmt == KVQ_FMT_Q2K) return slots_r<KVQ_FMT_Q2K, 2, 4, false>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return slots_r<KVQ_FMT_TQ, 4, 2, false>(r, cus);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
-    if (sh.kb == 2) return slots_r<KVQ_FMT_KIVI, 2, 2>(r, cus);
-    if (sh.kb == 4) return slots_r<KVQ_FMT_KIVI, 4, 4>(r, cus);
-    if (sh.kb == 8) return slots_r<KVQ_FMT_KIVI, 8, 8>(r, cus);
+    if (sh.kb == 2) return slots_r<KVQ_FMT_KIVI, 2, 2, false>(r, cus);
+    if (sh.kb == 4) return slots_r<KVQ_FMT_KIVI, 4, 4, false>(r, cus);
+    if (sh.kb == 8) return slots_r<KVQ_FMT_KIVI, 8, 8, false>(r, cus);
   }
   return 0;
 }
@@ -1024,12 +1254,20 @@ int fast_fp16_rows_per_group() { return FPR; }
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
   if (sh.D != FD || a.nparts == 0 || sh.in_f32) return hipErrorInvalidValue;
-  if (sh.fmt == KVQ_FMT_Q2K) return launch_r<KVQ_FMT_Q2K, 2, 4>(a, st);
-  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return launch_r<KVQ_FMT_TQ, 4, 2>(a, st);
+  if (sh.rope) {
+    if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
+      if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2, true>(a, st);
+      if (sh.kb == 4) return launch_r<KVQ_FMT_KIVI, 4, 4, true>(a, st);
+      if (sh.kb == 8) return launch_r<KVQ_FMT_KIVI, 8, 8, true>(a, st);
+    }
+    return hipErrorInvalidValue;
+  }
+  if (sh.fmt == KVQ_FMT_Q2K) return launch_r<KVQ_FMT_Q2K, 2, 4, false>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return launch_r<KVQ_FMT_TQ, 4, 2, false>(a, st);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
-    if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2>(a, st);
-    if (sh.kb == 4) return launch_r<KVQ_FMT_KIVI, 4, 4>(a, st);
-    if (sh.kb == 8) return launch_r<KVQ_FMT_KIVI, 8, 8>(a, st);
+    if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2, false>(a, st);
+    if (sh.kb == 4) return launch_r<KVQ_FMT_KIVI, 4, 4, false>(a, st);
+    if (sh.kb == 8) return launch_r<KVQ_FMT_KIVI, 8, 8, false>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -82,12 +82,30 @@ __device__ __forceinline__ int cache_index(const int* sinks, int nsinks, int64_t
   return n + (int)(p > lo ? p - lo : 0);
 }
 
+// cos and sin of the exact angle idx * th (|idx| < 2^24, so fp32(idx) is exact): a = fp32(idx * th)
+// plus its exact residual e = idx * th - a (one fma); cos(a + e) and sin(a + e) from sincosf(a) and
+// the Taylor terms of e (|e| < 2^-5: error below 1e-7), or sincosf(e) for larger e (angles above 2^19).
+__device__ __forceinline__ void rope_cs(int idx, float th, float& cs, float& sn) {
+  const float x = (float)idx, a = x * th, e = __builtin_fmaf(x, th, -a);
+  float sa, ca, se, ce;
+  sincosf(a, &sa, &ca);
+  if (fabsf(e) < 0.03125f) {
+    const float e2 = e * e;
+    ce = __builtin_fmaf(-0.5f, e2, 1.f);
+    se = __builtin_fmaf(e * e2, -1.f / 6.f, e);
+  } else {
+    sincosf(e, &se, &ce);
+  }
+  cs = __builtin_fmaf(ca, ce, -sa * se);
+  sn = __builtin_fmaf(sa, ce, ca * se);
+}
+
 // Rotate-half RoPE of channel c given its partner channel (c +- D/2): x' = x cos - y sin for
-// c < D/2, x' = x cos + y sin above, with the angle fp32(idx) * theta_{c mod D/2}.
+// c < D/2, x' = x cos + y sin above, with the angle idx * theta_{c mod D/2}.
 __device__ __forceinline__ float rope_val(float x, float partner, int c, int D, int idx, const float* inv) {
   const int h = D >> 1, f = c < h ? c : c - h;
   float sn, cs;
-  sincosf((float)idx * inv[f], &sn, &cs);
+  rope_cs(idx, inv[f], cs, sn);
   return c < h ? x * cs - partner * sn : x * cs + partner * sn;
 }
 

@@ -125,6 +125,8 @@ kvq_status check(const kvq_config* c) {
   if (c->window > 0 && cap < G * ((c->window + G - 1) / G + 1))
     return fail(KVQ_EINVAL, "capacity %d too small for window %d (needs one spare block)", cap, c->window);
   if (c->residual > cap) return fail(KVQ_EINVAL, "residual larger than capacity");
+  if (c->rope && (int64_t)cap + c->n_sink >= (int64_t(1) << 24))
+    return fail(KVQ_EINVAL, "RoPE on read needs capacity + n_sink below 2^24 (indices exact in fp32)");
   g_err.clear();
   return KVQ_OK;
 }
@@ -171,16 +173,19 @@ kvq_layout make_layout(const kvq_config& c) {
   return L;
 }
 
-// Shapes the MFMA decode path covers (the generic kernel takes the rest).  The MFMA kernel reads a
-// stream's ring through a buffer resource with 32-bit record offsets and a 31-bit size, so a ring of
-// 2 GiB or more per stream goes to the generic kernel, which addresses with 64-bit pointers.
+// Shapes the MFMA decode path covers (the generic kernel takes the rest; RoPE on read: KIVI with
+// equal K and V widths).  The MFMA kernel reads a stream's ring through a buffer resource with
+// 32-bit record offsets and a 31-bit size, so a ring of 2 GiB or more per stream goes to the generic
+// kernel, which addresses with 64-bit pointers.
 bool fast_path(const kvq_config& c) {
   const int r = c.n_q_heads / c.n_kv_heads;
   const uint64_t ring = (uint64_t)(effective_capacity(c) / G) * record_sections(c).rec;
-  return ring < (uint64_t(1) << 31) && stored_dim(c) == 128 && c.in_dtype == KVQ_IN_F16 && !c.rope &&
+  const bool kivi_eq = c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits;
+  return ring < (uint64_t(1) << 31) && stored_dim(c) == 128 && c.in_dtype == KVQ_IN_F16 &&
          (r == 1 || r == 2 || r == 4 || r == 8) &&
-         (c.format == KVQ_FMT_Q2K || (c.format == KVQ_FMT_KIVI && c.k_bits == c.v_bits) ||
-          (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || (c.k_bits == 3 && !c.tq_dense3)) && c.v_bits == 2));
+         (c.rope ? kivi_eq
+                 : (c.format == KVQ_FMT_Q2K || kivi_eq ||
+                    (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || (c.k_bits == 3 && !c.tq_dense3)) && c.v_bits == 2)));
 }
 
 // Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, whole rounds of the
@@ -231,10 +236,11 @@ int max_splits(const kvq_config& c) {
   return splits_for(c, nblk, 0, 0);
 }
 
-// RoPE caches with fp16 queries decode on the prefill kernel (split over row blocks).
+// RoPE caches with fp16 queries that the MFMA decode kernel does not cover decode on the prefill
+// kernel (split over row blocks).
 constexpr int ROPE_MAX_SPLITS = 64;
 bool rope_decode_on_prefill(const kvq_config& c) {
-  return c.rope && c.in_dtype == KVQ_IN_F16 && c.format != KVQ_FMT_TQ;
+  return c.rope && c.in_dtype == KVQ_IN_F16 && c.format != KVQ_FMT_TQ && !fast_path(c);
 }
 
 // fp16-row partials of a decode call: the MFMA path scores the window rows and the sinks in groups

@@ -26,6 +26,7 @@ struct Tables {
   float q2k_thr[4];     // Gaussian 4-level Lloyd-Max thresholds (3 used)
   float q2k_lvl[4];     // Gaussian 4-level Lloyd-Max levels
   float rope_inv[MAX_D / 2];  // RoPE theta_c = base^(-2c/D), rounded to fp32 (rope mode)
+  float rope_row[16][MAX_D / 2][2];  // RoPE (cos, sin) of the exact angles i * theta_c, i < 16 (rope mode)
 };
 
 // Everything a kernel needs to address one layer of the cache.

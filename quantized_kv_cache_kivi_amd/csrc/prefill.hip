@@ -441,7 +441,7 @@ __global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
         const float x0 = (float)S.khi[t][c] + (float)S.klo[t][c];
         const float x1 = (float)S.khi[t][c + H] + (float)S.klo[t][c + H];
         float sn, cs;  // one angle per pair: both channels turn by idx * theta_c
-        sincosf((float)ri * lv.tables->rope_inv[c], &sn, &cs);
+        rope_cs(ri, lv.tables->rope_inv[c], cs, sn);
         const float y0 = x0 * cs - x1 * sn, y1 = x1 * cs + x0 * sn;
         const _Float16 h0 = (_Float16)y0, h1 = (_Float16)y1;
         S.khi[t][c] = h0;

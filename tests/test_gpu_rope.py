@@ -1,8 +1,10 @@
 """GPU parity of RoPE on read (kvq_config.rope = 1) against the oracle, through the C ABI.
 
-Keys and queries are handed over before RoPE; decode attention (generic split kernel, bulk
-splits plus one fp16-row split) and prefill attention (matrix-core kernel, staged keys turned in
-LDS, queries as fp16 hi + lo pairs) turn them by their index in the compressed cache.  Bar: max
+Keys and queries are handed over before RoPE; decode attention (head_dim 128 fp16 KIVI with equal
+widths: the matrix-core decode kernel, keys dequantized and turned in registers, the query turned
+per row tile; q2k and other head_dims: the prefill kernel split over row blocks; fp32: the generic
+split kernel) and prefill attention (matrix-core kernel, staged keys turned in LDS, queries as
+fp16 hi + lo pairs) turn them by their index in the compressed cache.  Bar: max
 over (b, query head[, query]) of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3.  Cases: KIVI-2, KIVI-4,
 KIVI-8 and q2k; head_dim 32, 64, 128; GQA 1, 2, 4, 8; top-k and first-N sinks; an evicting window
 (indices re-packed after eviction) and no eviction (indices = positions); fp16 and fp32 input;
@@ -31,6 +33,17 @@ CASES = {
                                            in_dtype="f32", rope=True, rope_base=500000.0), [60, 20, 1, 1, 1]),
     "kivi8_d32_r1_plain_positions": (dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="kivi",
                                           k_bits=8, v_bits=8, capacity=512, rope=True), [300, 1, 45]),
+    # the matrix-core decode kernel (head_dim 128, fp16, KIVI with equal widths): several blocks per
+    # wave, evicting windows, both sink modes, GQA 1 / 2 / 8
+    "kivi4_d128_r2_firstn_win200_res24": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128,
+                                               fmt="kivi", k_bits=4, v_bits=4, sink_mode="first_n", n_sink=4,
+                                               window=200, residual=24, capacity=384, rope=True), [230, 1, 70, 1, 1]),
+    "kivi8_d128_r8_topk_res8": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="kivi",
+                                     k_bits=8, v_bits=8, sink_mode="topk", n_sink=6, residual=8, capacity=1024,
+                                     rope=True), [500, 1, 33]),
+    "kivi2_d128_r1_long_plain": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=2, head_dim=128, fmt="kivi",
+                                      k_bits=2, v_bits=2, residual=0, capacity=2560, rope=True,
+                                      rope_base=500000.0), [2200, 1, 64]),
 }
 
 

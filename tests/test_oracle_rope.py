@@ -2,7 +2,8 @@
 
 Against closed forms: each channel pair turns as the complex number x_c + i x_{c+D/2} times
 e^{i idx theta_c}; zero angle is the identity; norms are kept; q(i) . k(j) depends on j - i only
-(up to the fp32 rounding of the angles); theta_c is geometric with ratio base^(-2/D).  Against the
+(to fp64 rounding: the angle is the exact product idx * theta_c, also at indices where an fp32 product
+would move it by milliradians); theta_c is geometric with ratio base^(-2/D).  Against the
 StreamingLLM + KIVI page ("RoPE caveat", "Implementation"): after eviction the sinks hold indices
 0.., the window follows them without a gap, and a decode query sits at index n_sink + window - 1
 however long the stream is.
@@ -34,15 +35,26 @@ def test_scores_depend_on_relative_position_only():
     q, k = rng.standard_normal(D), rng.standard_normal(D)
     for i, j in [(10, 3), (100, 0), (259, 4)]:
         base = rope.rotate(q, i) @ rope.rotate(k, j)
-        for t in (1, 7, 1000):
+        for t in (1, 7, 1000, 3 * 65536 + 5):  # the last: an fp32 product would be off by 1e-2 rad
             shifted = rope.rotate(q, i + t) @ rope.rotate(k, j + t)
-            assert abs(shifted - base) <= 1e-4 * np.abs(q).sum() * np.abs(k).max()
+            assert abs(shifted - base) <= 1e-10 * np.abs(q).sum() * np.abs(k).max()
     # and q(i) . k(j) = q . k(j - i) exactly in the angle algebra (fp64 angles)
     th = rope.inv_freq(D).astype(np.float64)
     def rot64(x, ang):
         a, b = x[: D // 2], x[D // 2:]
         return np.concatenate([a * np.cos(ang) - b * np.sin(ang), b * np.cos(ang) + a * np.sin(ang)])
     assert abs(rot64(q, 9 * th) @ rot64(k, 4 * th) - q @ rot64(k, -5 * th)) < 1e-12
+
+
+def test_angle_is_the_exact_product():
+    """idx * theta_c to fp64 rounding: at index 65537 the fp32 product would differ by ~4e-3 rad."""
+    th = rope.inv_freq(128).astype(np.float64)
+    ang = rope.angles(np.array([65537, 12345678]), 128)
+    for r, i in enumerate((65537, 12345678)):
+        exact = np.array([float(i) * t for t in th])
+        assert np.array_equal(ang[r], exact)
+    f32 = (np.float32(65537) * rope.inv_freq(128)).astype(np.float64)
+    assert np.abs(f32 - ang[0]).max() > 1e-3
 
 
 def test_theta_is_geometric():
@@ -73,7 +85,7 @@ def test_indices_after_eviction():
 
 def test_decode_attention_with_rope_equals_relative_form():
     """With W = 0 and no sinks the query sits at P-1 and row p at p, so the score of row p is
-    q . R(p - (P-1)) k_p (fp64 angle algebra, within the fp32 angle rounding)."""
+    q . R(p - (P-1)) k_p (fp64 angle algebra)."""
     cfg = ocache.Config(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=2, head_dim=64, fmt="kivi", k_bits=8,
                         v_bits=8, capacity=128, in_dtype="f32", rope=True)
     m = ocache.CacheModel(cfg)
@@ -91,7 +103,7 @@ def test_decode_attention_with_rope_equals_relative_form():
             kh[p, 32:] * np.cos((p - 39) * th) + kh[p, :32] * np.sin((p - 39) * th)]) for p in pos]) / 8.0
         w = np.exp(s - s.max())
         ref = (w @ vh) / w.sum()
-        assert np.allclose(out[0, j], ref, rtol=0, atol=1e-4 * np.abs(ref).max())
+        assert np.allclose(out[0, j], ref, rtol=0, atol=1e-12 * np.abs(ref).max())
     # the same rows without RoPE on read give another answer: the rotation is applied
     m2 = ocache.CacheModel(cfg.with_(rope=False))
     m2.append(0, m.K[0][:, :, :40], m.V[0][:, :, :40])
