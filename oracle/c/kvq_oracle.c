@@ -240,6 +240,7 @@ ko_model* ko_create(const ko_config* cfg) {
       !(c.fmt == 2 && (c.head_dim == 96 || c.head_dim == 160)))
     return NULL;
   if (c.n_sink < 0 || c.n_sink > MAXSINK || c.capacity < G || c.capacity % G) return NULL;
+  if (c.rope && c.fmt == 2) return NULL;
   if (c.fmt == 0) {
     if ((c.k_bits != 2 && c.k_bits != 4 && c.k_bits != 8) || (c.v_bits != 2 && c.v_bits != 4 && c.v_bits != 8))
       return NULL;
@@ -901,6 +902,17 @@ static Valid valid_positions(const ko_model* m, int layer, int b) {
   return v;
 }
 
+/* RoPE on read: row x [D] turned by the exact angles idx * theta_c (rotate-half pairs). */
+static void rope_turn(double* x, int D, int64_t idx, const float* theta) {
+  const int h = D / 2;
+  for (int f = 0; f < h; ++f) {
+    const double a = (double)idx * (double)theta[f], cs = cos(a), sn = sin(a);
+    const double x0 = x[f], x1 = x[f + h];
+    x[f] = x0 * cs - x1 * sn;
+    x[f + h] = x1 * cs + x0 * sn;
+  }
+}
+
 /* One stream (b, g): scores of its r query heads over every valid position, then the weighted values. */
 static int attend_stream(ko_model* m, int layer, int b, int g, const void* q, double alpha, double* out) {
   const ko_config* c = &m->c;
@@ -924,6 +936,14 @@ static int attend_stream(ko_model* m, int layer, int b, int g, const void* q, do
       const int64_t qi = ((int64_t)b * c->n_q_heads + (int64_t)g * r + j) * D + ch;
       qv[j][ch] = c->in_f32 ? (double)((const float*)q)[qi] : (double)f16_val(((const uint16_t*)q)[qi]);
     }
+  float theta[MAXD / 2];
+  if (c->rope) {  /* the query's index: valid positions before its own, P - 1 (the last valid one) */
+    const double base = c->rope_base > 0.f ? (double)c->rope_base : 10000.0;
+    for (int f = 0; f < D / 2; ++f) theta[f] = (float)pow(base, -2.0 * f / D);
+    int64_t qidx = 0;
+    while (qidx < v.n && v.pos[qidx] < m->P[layer] - 1) ++qidx;
+    for (int j = 0; j < r; ++j) rope_turn(qv[j], D, qidx, theta);
+  }
   for (int pass = 0; pass < 2; ++pass) {  /* pass 0: K and scores; pass 1: V and the output */
     int64_t have = -1;
     double acc[16][MAXD], wsum[16], mx[16];
@@ -950,6 +970,7 @@ static int attend_stream(ko_model* m, int layer, int b, int g, const void* q, do
         }
         bulk_row(m, o, (int)(p % G), pass, x, NULL);
       }
+      if (c->rope && pass == 0) rope_turn(x, D, i, theta);  /* row i of the ascending valid list has index i */
       for (int j = 0; j < r; ++j) {
         if (pass == 0) {
           double d = 0.0;

@@ -19,7 +19,10 @@
  *   - StreamingLLM eviction of [sink, P - window) as a validity range with an fp16 overlay for sinks and
  *     the recent window (StreamingLLM + KIVI page, "Implementation"; q2k page, "Summary");
  *   - the stored bytes of every ring slot in the documented storage format (include/kvq.h);
- *   - single-query decode attention in fp64 over the exactly dequantized cache (plain definition).
+ *   - single-query decode attention in fp64 over the exactly dequantized cache (plain definition),
+ *     optionally with RoPE on read: rotate-half pairs (c, c + D/2) turned by the exact angle idx * theta_c,
+ *     theta_c = base^(-2c/D) rounded to fp32, idx = the number of valid positions before the row or the
+ *     query's own position ("StreamingLLM + KIVI" page, "RoPE caveat"; the readings of oracle/rope.py).
  *
  * Every code-deciding expression is fp32, one rounding per operation (built with -ffp-contract=off
  * -fno-fast-math), rintf rounding half to even, min/max results canonicalised with + 0.0f; fp32 -> fp16 is
@@ -47,6 +50,8 @@ typedef struct {
   int32_t in_f32;      /* 0: inputs are fp16 bit patterns, 1: fp32 */
   int32_t tq_dense3;   /* TurboQuant 3-bit codes as a dense stream (else 4-bit slots) */
   uint64_t seed;       /* TurboQuant sign seed */
+  int32_t rope;        /* 1: decode attention turns keys and queries by their index (not with TurboQuant) */
+  float rope_base;     /* RoPE base (<= 0: 10000) */
 } ko_config;
 
 typedef struct ko_model ko_model;

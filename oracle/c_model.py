@@ -39,7 +39,9 @@ def build_library(verbose=False):
 class _Cfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "batch", "n_kv_heads", "n_q_heads", "head_dim", "fmt",
                                                "k_bits", "v_bits", "sink_mode", "n_sink", "window", "residual",
-                                               "capacity", "in_f32", "tq_dense3")] + [("seed", ctypes.c_uint64)]
+                                               "capacity", "in_f32", "tq_dense3")] + [("seed", ctypes.c_uint64),
+                                                                                       ("rope", ctypes.c_int32),
+                                                                                       ("rope_base", ctypes.c_float)]
 
 
 _lib = None
@@ -109,8 +111,7 @@ class CModel:
         self.cfg = cfg
         c = _Cfg(cfg.n_layers, cfg.batch, cfg.n_kv_heads, cfg.n_q_heads, cfg.head_dim, FMT[cfg.fmt], cfg.k_bits,
                  cfg.v_bits, SINK[cfg.sink_mode], cfg.n_sink, cfg.window, cfg.residual, cfg.capacity,
-                 int(cfg.in_dtype == "f32"), int(cfg.tq_dense3), cfg.seed)
-        assert not cfg.rope, "the C oracle covers the decode hot path without RoPE on read"
+                 int(cfg.in_dtype == "f32"), int(cfg.tq_dense3), cfg.seed, int(cfg.rope), float(cfg.rope_base))
         self.h = lib().ko_create(ctypes.byref(c))
         if not self.h:
             raise ValueError("C oracle rejected the configuration")

@@ -9,8 +9,8 @@ makes their full decode schedules affordable; the others on the numpy oracle:
 
 * stored bytes of every sampled stream (packed codes, metadata, fp16 window, sink pool), sink
   positions / scores / count: bit-exact;
-* decode attention of the sampled batch elements: max over heads of
-  ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3;
+* decode attention of the sampled batch elements (also with RoPE on read at the KIVI-2 and int4
+  sizes): max over heads of ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3;
 * kvq_dequant of sampled positions: within 1 fp16 ulp.
 
 Workload recipes (seeded, synthetic) follow bench.CONFIGS: the tiny 12-layer StreamingLLM + KIVI
@@ -226,7 +226,7 @@ def test_workload_kivi2_dynamic_sinks():
 
 
 def test_workload_kivi2_dynamic_sinks_rope_on_read():
-    """The same workload with RoPE on read: decode attention (the split prefill kernel) and prefill
+    """The same workload with RoPE on read: decode attention (the matrix-core decode kernel) and prefill
     attention of the 4096 prefill queries, sampled against the oracle."""
     from quantized_kv_cache_kivi_amd import synth
     w = Workload(2, rope=True)
@@ -276,3 +276,15 @@ def test_workload_long_streaming_int4():
     assert w.gpu.kvq_account(0)["n_valid"] == (65536 + 4) * w.B
     assert (P, lo) == w.state(0)
     w.check_dequant(0, [(lo, 64), (P - 130, 130)])
+
+
+def test_workload_long_streaming_int4_rope_on_read():
+    """The long int4 stream with RoPE on read, against the C oracle: indices up to 65539 (where an fp32
+    product of the angle would be off by up to 3.9e-3 rad) and 2050 bulk blocks per stream, so each wave
+    of the matrix-core kernel walks hundreds of blocks with its query angle stepped per block and
+    recomputed every 16th.  Attention after the prefill and at decode steps 0, 1 and 60 (the ring wraps)."""
+    w = Workload(5, oracle="c", rope=True)
+    w.prefill()
+    w.check_attention(0, w.query(1))
+    _decode_steps(w, 61, {0, 1, 60}, 0)
+    assert w.gpu.kvq_get_state(0) == w.state(0)

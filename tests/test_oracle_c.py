@@ -1,6 +1,6 @@
 """The plain-C99 oracle (oracle/c) against the numpy oracle: the same call sequences give the same
 stored bytes, committed sinks, byte accounting and values bit for bit, the same format tables bit for
-bit, and decode attention equal to fp64 rounding (the two sum in different orders).  Together with the
+bit, and decode attention equal to fp64 rounding (the two sum in different orders), RoPE on read included.  Together with the
 pins of the numpy oracle (tests/test_oracle_*.py) this pins the C oracle."""
 import numpy as np
 import pytest
@@ -62,6 +62,12 @@ CASES = {
                                v_bits=2, sink_mode="first_n", n_sink=2, window=70, residual=8, seed=31),
     "tq_k4v4_d160_f32": dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=2, head_dim=160, fmt="tq", k_bits=4,
                              v_bits=4, residual=4, in_dtype="f32", seed=32),
+    "kivi2_topk_window_rope": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="kivi",
+                                   k_bits=2, v_bits=2, sink_mode="topk", n_sink=3, window=100, residual=16,
+                                   rope=True),
+    "q2k_first_n_rope_base": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="q2k", k_bits=2,
+                                  v_bits=4, sink_mode="first_n", n_sink=4, residual=8, rope=True,
+                                  rope_base=500000.0),
 }
 SCHEDULE = [70, 1, 1, 33, 1, 20, 2, 31, 1, 17, 1]
 
