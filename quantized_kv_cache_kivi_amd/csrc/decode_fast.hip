@@ -366,7 +366,7 @@ struct Fast {
 // fp32 and split into fp16 hi + lo halves for the MFMA.  Per-lane state of a wave:
 template <int R>
 struct RopeLane {
-  h2 ql[R], qh[R];           // query channels fp, fp + 1 and fp + 64, fp + 65 (fp = 2 * (lane & 31))
+  f2 ql[R], qh[R];           // query channels fp, fp + 1 and fp + 64, fp + 65 (fp = 2 * (lane & 31))
   float c[2], s[2];          // cos, sin of the current block's query angle, frequencies fp, fp + 1
   float cst[2], sst[2];      // cos, sin of one wave step (NW blocks) at those frequencies
   const float* rk;           // cos, sin of i16 * theta_f, f = 16 * kg + 0..15 (LDS)
@@ -378,19 +378,42 @@ __device__ __forceinline__ int rope_qpair(int c) {
   const int h = c >> 6, x = c & 63;
   return 16 * (x >> 4) + 4 * (2 * h + ((x >> 3) & 1)) + ((x >> 1) & 3);
 }
-// KB-bit code of channel 8 sp + 2 r + e of half hf (channels 16 kg .. + 15, or + 64) of a RoPE
-// code row: a dword holds the 16 / KB channel pairs i at bits KB i (even) and 16 + KB i (odd).
+// Codes of the channel pair (8 sp + 2 r, + 1) of half hf (channels 16 kg .. + 15, or + 64) of a
+// RoPE code row, masked in place as two fp16 subnormals u * 2^(p - 24), p = rope_pos<KB>(r) (a dword
+// holds the 16 / KB channel pairs i at bits KB i (even channel) and 16 + KB i (odd); codes above bit
+// 7 of a half are shifted down first).
 template <int KB>
-__device__ __forceinline__ uint32_t rope_code(const uint32_t* kd, int hf, int sp, int r, int e) {
-  constexpr int PPD = 16 / KB;  // channel pairs per dword
-  const int pi = 4 * sp + r;
-  return (kd[hf * (KB / 2) + pi / PPD] >> (KB * (pi % PPD) + 16 * e)) & ((1u << KB) - 1u);
+constexpr int rope_pos(int r) {
+  return KB == 2 ? 2 * r : KB == 4 ? 4 * (r & 1) : 0;
 }
-// fp16 hi = rz(a), rz(b) and lo = rz((x - hi) * up) of two fp32 values, packed pairs.
+template <int KB>
+__device__ __forceinline__ uint32_t rope_codes(const uint32_t* kd, int hf, int sp, int r) {
+  if constexpr (KB == 2) {
+    const uint32_t w = sp ? kd[hf] >> 8 : kd[hf];
+    return w & (0x00030003u << (2 * r));
+  } else if constexpr (KB == 4) {
+    const uint32_t w = kd[2 * hf + sp];
+    return (r >= 2 ? w >> 8 : w) & (0x000F000Fu << (4 * (r & 1)));
+  } else {
+    const uint32_t w = kd[4 * hf + 2 * sp + (r >> 1)];
+    return ((r & 1) ? w >> 8 : w) & 0x00FF00FFu;
+  }
+}
+// fp16 hi = rn(a), rn(b) and lo = rn((x - hi) * up) of two fp32 values, packed pairs (the lo halves
+// as one mixed-precision fma each: exact product hi * up, one rounding).
 __device__ __forceinline__ void split16(float a, float b, float up, uint32_t& hi, uint32_t& lo) {
-  const h2 h = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));
+  const h2 h = h2{(_Float16)a, (_Float16)b};
   hi = U32(h);
-  lo = U32(__builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz((a - (float)h.x) * up, (b - (float)h.y) * up)));
+  const _Float16 l0 = (_Float16)__builtin_fmaf((float)h.x, -up, a * up);
+  const _Float16 l1 = (_Float16)__builtin_fmaf((float)h.y, -up, b * up);
+  lo = U32(h2{l0, l1});
+}
+// The same without scaling, hi rounded toward zero: lo = rn(x - hi).  nm1 is -1 held in a register (an fma by a literal -1
+// would be rewritten as a subtraction, which the mixed-precision fma does not cover).
+__device__ __forceinline__ void split16u(float a, float b, float nm1, uint32_t& hi, uint32_t& lo) {
+  const h2 h = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(a, b));  // one instruction per pair
+  hi = U32(h);
+  lo = U32(h2{(_Float16)__builtin_fmaf((float)h.x, nm1, a), (_Float16)__builtin_fmaf((float)h.y, nm1, b)});
 }
 
 // Per-lane state of a wave over its blocks.
@@ -429,7 +452,7 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
     const int il = rope_qpair(fp), ih = rope_qpair(64 + fp);
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      const float x0 = (float)Q.ql[j].x, x1 = (float)Q.ql[j].y, y0 = (float)Q.qh[j].x, y1 = (float)Q.qh[j].y;
+      const float x0 = Q.ql[j].x, x1 = Q.ql[j].y, y0 = Q.qh[j].x, y1 = Q.qh[j].y;
       uint32_t h, l;
       split16(x0 * Q.c[0] - y0 * Q.s[0], x1 * Q.c[1] - y1 * Q.s[1], LOK_UP, h, l);
       W.x.qb[tq][j][il] = h;
@@ -453,9 +476,11 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
   // ---- scores: raw MFMA columns to LDS ----
   if constexpr (RP) {
     // keys k = u s + z per channel (fp32), turned by i16 theta in (f, f + 64) pairs, split into fp16
-    // hi and lo * 2^11 (two MFMA products per step; the lo product enters at 2^-11)
+    // hi and lo halves (two MFMA products per step into one accumulator; a lo half below the fp16
+    // normal range keeps its absolute precision, 2^-25, and meets a normal query half)
     f4 c0[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
-    f4 c1[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
+    float nm1 = -1.f;
+    asm("" : "+v"(nm1));  // opaque to the optimizer (no instruction)
 #pragma unroll
     for (int sp = 0; sp < 2; ++sp) {
       const u4 sl = *reinterpret_cast<const u4*>(&W.km[0][8 * kg + 4 * sp]);
@@ -464,6 +489,17 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
       const u4 zh = *reinterpret_cast<const u4*>(&W.km[1][32 + 8 * kg + 4 * sp]);
       const uint32_t slv[4] = {sl.x, sl.y, sl.z, sl.w}, zlv[4] = {zl.x, zl.y, zl.z, zl.w};
       const uint32_t shv[4] = {sh.x, sh.y, sh.z, sh.w}, zhv[4] = {zh.x, zh.y, zh.z, zh.w};
+      // scales times 2^(24 - p): the codes enter as fp16 subnormals u * 2^(p - 24)
+      float sls[4][2], shs[4][2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          constexpr float one = 1.f;
+          const float f = __builtin_ldexpf(one, 24 - rope_pos<KB>(r));
+          sls[r][e] = h16(slv[r], e) * f;
+          shs[r][e] = h16(shv[r], e) * f;
+        }
       float kc[8], ks[8];  // frequencies 16 kg + 8 sp + 0..7
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -478,26 +514,26 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
           float rl[2], rh[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const float kl = __builtin_fmaf((float)rope_code<KB>(d.kd[tau], 0, sp, r, e), h16(slv[r], e), h16(zlv[r], e));
-            const float kh = __builtin_fmaf((float)rope_code<KB>(d.kd[tau], 1, sp, r, e), h16(shv[r], e), h16(zhv[r], e));
+            const float kl = __builtin_fmaf(h16(rope_codes<KB>(d.kd[tau], 0, sp, r), e), sls[r][e], h16(zlv[r], e));
+            const float kh = __builtin_fmaf(h16(rope_codes<KB>(d.kd[tau], 1, sp, r), e), shs[r][e], h16(zhv[r], e));
             const int fi = 2 * r + e;
             rl[e] = kl * kc[fi] - kh * ks[fi];
             rh[e] = kh * kc[fi] + kl * ks[fi];
           }
-          split16(rl[0], rl[1], LO_UP, ahl[r], all[r]);
-          split16(rh[0], rh[1], LO_UP, ahh[r], alh[r]);
+          split16u(rl[0], rl[1], nm1, ahl[r], all[r]);
+          split16u(rh[0], rh[1], nm1, ahh[r], alh[r]);
         }
         const u4 bl = *reinterpret_cast<const u4*>(&W.x.qb[tau][col][16 * kg + 4 * sp]);
         const u4 bh = *reinterpret_cast<const u4*>(&W.x.qb[tau][col][16 * kg + 4 * (sp + 2)]);
         c0[tau] = mfma(u4{ahl[0], ahl[1], ahl[2], ahl[3]}, bl, c0[tau]);
         c0[tau] = mfma(u4{ahh[0], ahh[1], ahh[2], ahh[3]}, bh, c0[tau]);
-        c1[tau] = mfma(u4{all[0], all[1], all[2], all[3]}, bl, c1[tau]);
-        c1[tau] = mfma(u4{alh[0], alh[1], alh[2], alh[3]}, bh, c1[tau]);
+        c0[tau] = mfma(u4{all[0], all[1], all[2], all[3]}, bl, c0[tau]);
+        c0[tau] = mfma(u4{alh[0], alh[1], alh[2], alh[3]}, bh, c0[tau]);
       }
     }
 #pragma unroll
     for (int tau = 0; tau < 2; ++tau)
-      *reinterpret_cast<f4*>(&W.ps[col][16 * tau + 4 * kg]) = c0[tau] + c1[tau] * LO_DOWN;
+      *reinterpret_cast<f4*>(&W.ps[col][16 * tau + 4 * kg]) = c0[tau];
   } else {
     f4 c0[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
     f4 c1[2] = {f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f}};
@@ -724,8 +760,10 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R, RP>& F, int sigma)
     const _Float16* qs = static_cast<const _Float16*>(a.q) + ((int64_t)b * sh.Hq + (int64_t)g * R) * FD;
 #pragma unroll
     for (int j = 0; j < R; ++j) {
-      Q.ql[j] = H2(*reinterpret_cast<const uint32_t*>(qs + j * FD + fp));
-      Q.qh[j] = H2(*reinterpret_cast<const uint32_t*>(qs + j * FD + 64 + fp));
+      const h2 lo2 = H2(*reinterpret_cast<const uint32_t*>(qs + j * FD + fp));
+      const h2 hi2 = H2(*reinterpret_cast<const uint32_t*>(qs + j * FD + 64 + fp));
+      Q.ql[j] = f2{(float)lo2.x, (float)lo2.y};
+      Q.qh[j] = f2{(float)hi2.x, (float)hi2.y};
     }
     for (int idx = tid; idx < 16 * 64; idx += DNT) {
       const int i = idx >> 6, f = idx & 63;
