@@ -210,6 +210,20 @@ kvq_status kvq_evict(kvq_cache* c, int32_t layer);
 kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* One decode step of `layer` for one new row: kvq_select_sinks (top-k mode), kvq_append (1 row), kvq_evict
+ * and kvq_decode_attn, in this order ([SK] "Implementation": per layer and step, append, evict, attend;
+ * [KS] "How it works"), with the same results, stored bytes and state as those four calls.  k, v:
+ * [batch][n_kv_heads][1][head_dim] in_dtype; q, out, scale, ws, ws_bytes as in kvq_decode_attn.  When the
+ * row changes no sink (the committed set already holds min(n_sink, P) rows and n_sink <= P), completes
+ * no block, the cache defers open blocks (block formats, fp16 input, residual >= 32) and the shape has
+ * the matrix-core decode kernel (k and v 16-byte aligned), the step is one launch: the decode kernel's
+ * first fp16-row workgroup of each stream copies the row into the staging rows and the fp16 window
+ * (and zeroes the record of a block the row opens) while the row is scored straight from k and v.
+ * Otherwise the four calls run as separate launches.  Errors as in those calls; on an error nothing is
+ * launched and the state is unchanged. */
+kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k, const void* v, const void* q, float* out,
+                           float scale, void* ws, size_t ws_bytes, void* stream);
+
 /* Size of the static decode workspace kvq_decode_attn_nomalloc uses: 32 MiB of device memory per GPU,
  * held from the library's first use on that GPU until the process ends. */
 #define KVQ_STATIC_WS_BYTES ((size_t)32 << 20)

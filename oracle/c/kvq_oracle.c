@@ -738,6 +738,12 @@ static void pack_record(const ko_model* m, const Block* o, uint8_t* rec) {
   }
 }
 
+/* Block formats with fp16 input and residual >= 32 quantize a block once, when its last row arrives (KIVI
+ * groups keys per channel over full groups of tokens; while a block is open all its rows are in the fp16
+ * window, which serves every read of them): an open block's record holds zero bytes until then.  Otherwise
+ * an open block's record holds its rows so far, re-quantized on every append. */
+static int defers_open_block(const ko_config* c) { return c->fmt != 2 && !c->in_f32 && c->residual >= G; }
+
 int ko_stream_image(ko_model* m, int layer, int b, int h, uint8_t* bulk, uint16_t* win_k, uint16_t* win_v,
                     uint16_t* sink_k, uint16_t* sink_v) {
   if (!m || layer < 0 || layer >= m->c.n_layers || b < 0 || b >= m->c.batch || h < 0 || h >= m->c.n_kv_heads)
@@ -753,6 +759,7 @@ int ko_stream_image(ko_model* m, int layer, int b, int h, uint8_t* bulk, uint16_
       const int64_t last = (P - 1) / G;
       for (int64_t slot = 0; slot < m->cap_b && slot <= last; ++slot) {
         const int64_t beta = slot + m->cap_b * ((last - slot) / m->cap_b); /* the latest block in the slot */
+        if (beta == last && P % G != 0 && defers_open_block(&m->c)) continue;  /* open block: zero bytes */
         quantize_block(m, layer, b, h, beta, o);
         pack_record(m, o, bulk + slot * m->rec);
       }

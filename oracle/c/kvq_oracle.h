@@ -18,7 +18,8 @@
  *     Detail", "As-Built Notes");
  *   - StreamingLLM eviction of [sink, P - window) as a validity range with an fp16 overlay for sinks and
  *     the recent window (StreamingLLM + KIVI page, "Implementation"; q2k page, "Summary");
- *   - the stored bytes of every ring slot in the documented storage format (include/kvq.h);
+ *   - the stored bytes of every ring slot in the documented storage format (include/kvq.h; block formats
+ *     with fp16 input and residual >= 32 leave an open block's record zero until the block completes);
  *   - single-query decode attention in fp64 over the exactly dequantized cache (plain definition),
  *     optionally with RoPE on read: rotate-half pairs (c, c + D/2) turned by the exact angle idx * theta_c,
  *     theta_c = base^(-2c/D) rounded to fp32, idx = the number of valid positions before the row or the

@@ -80,6 +80,16 @@ class Config:
     def gqa(self):
         return self.n_q_heads // self.n_kv_heads
 
+    @property
+    def defers_open_block(self):
+        """Block formats with fp16 input and an fp16 window of at least one block (residual >= 32)
+        quantize a block once, when its last row arrives, the way KIVI groups keys per channel only
+        over full groups of tokens: while a block is open every row of it is in the fp16 window,
+        which serves every read of it, and its record holds zero bytes from the append that opens
+        it.  Otherwise (fp32 input, a shorter window, TurboQuant's per-token rows) an open block's
+        record holds its rows so far, re-quantized on every append."""
+        return self.fmt in ("kivi", "q2k") and self.in_dtype == "f16" and self.residual >= G
+
     def with_(self, **kw):
         return replace(self, **kw)
 
@@ -187,6 +197,8 @@ def stream_image(cfg, K, V, sink_list, P, tq=None):
             if slot <= last:
                 beta = slot + cap_b * ((last - slot) // cap_b)
                 bulk[slot] = recs[beta]
+        if cfg.defers_open_block and P % G:
+            bulk[last % cap_b] = 0  # the open block's record: zero until the block completes
     R = cfg.residual
     win_k = np.zeros((R, D), dtype=np.uint16)
     win_v = np.zeros((R, D), dtype=np.uint16)

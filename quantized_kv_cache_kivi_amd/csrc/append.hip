@@ -451,6 +451,13 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
   uint8_t* rec = lv.bulk + ((int64_t)s * lv.cap_b + beta % lv.cap_b) * lv.rec;
   const int64_t in_row0 = ((int64_t)b * sh.Hkv + h) * a.n;
   const int wpc = D * VB / 64;  // V words per chunk
+  // a.defer (block formats, fp16 input, fp16 window of >= 32 rows): a block is quantized once, when
+  // its last row arrives; a block left open by this call only gets its rows copied (and a zero
+  // record when this call opens it), and a block completed by this call takes the V of its earlier
+  // rows from the fp16 window, where all of them still are.  Otherwise an open block is re-quantized
+  // on every call and the V codes of earlier rows are kept.
+  const bool open_mode = a.defer && tend < G;
+  const int vt0 = a.defer ? 0 : tnew0;  // first row whose V this call quantizes
 
   __shared__ float xk[G][33];               // q2k: rows for the per-channel sum of squares
   __shared__ alignas(16) uint8_t ck[G][32];   // K codes [token][channel of the group]
@@ -479,14 +486,15 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
         const int64_t gi = (in_row0 + (base + t - a.P)) * D + c;
         kx[i] = ld_in(a.k, gi, sh.in_f32);
         vx[i] = ld_in(a.v, gi, sh.in_f32);
-      } else {
+      } else if (!open_mode) {
         kx[i] = ld_in(lv.staging, ((int64_t)s * G + t) * D + c, sh.in_f32);
+        if (a.defer) vx[i] = f16_val(lv.win_v[((int64_t)s * sh.R + (base + t) % sh.R) * D + c]);
       }
     }
   }
   uint32_t oldv = 0;  // word (chunk tid / VWG, group word tid % VWG), for tid < 64 * VWG
   const uint32_t* vwords = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
-  if (tnew0 > 0 && tid < 64 * VWG) oldv = vwords[(tid / VWG) * wpc + grp * VWG + tid % VWG];
+  if (vt0 > 0 && tid < 64 * VWG) oldv = vwords[(tid / VWG) * wpc + grp * VWG + tid % VWG];
 
   // 1. sink membership of the block's rows
   if (tid < 64) {
@@ -520,6 +528,15 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
   const uint32_t smask = smask_s;
   auto calib = [&](int t) { return t < tend && !((smask >> t) & 1u); };  // present, not a sink
 
+  if (open_mode) {
+    // a block opened by this call and left open: its record is zero until it completes (this
+    // group's quarter of the record words)
+    if (tnew0 == 0) {
+      const int words = (int)(lv.rec / 4), per = (words + 3) / 4;
+      uint32_t* rw = reinterpret_cast<uint32_t*>(rec);
+      for (int i = grp * per + tid; i < min(words, (grp + 1) * per); i += NT) rw[i] = 0u;
+    }
+  } else {
   // 3. K: per channel over the block's calibration rows, codes of every row
   uint8_t* km = rec + lv.k_meta;
   if constexpr (!Q2K) {
@@ -586,11 +603,11 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
       }
     }
   }
-  // 3b. V of the new rows: the group of one row is one half-wave
+  // 3b. V of the rows from vt0 on: the group of one row is one half-wave
 #pragma unroll
   for (int i = 0; i < PR; ++i) {
     const int t = rg + RGS * i;
-    if (t < tnew0 || t >= tend || ((smask >> t) & 1u)) continue;  // uniform over the half-wave
+    if (t < vt0 || t >= tend || ((smask >> t) & 1u)) continue;  // uniform over the half-wave
     if constexpr (!Q2K) {
       const float mn = half_min(vx[i]) + 0.0f, mx = half_max(vx[i]) + 0.0f;
       constexpr float L = (float)((1 << VB) - 1);
@@ -634,7 +651,7 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
     reinterpret_cast<uint32_t*>(rec + lv.k_codes)[t * (D * KB / 32) + KB * grp + w] = word;
   }
   // 5. V code words of the group: chunk q = 16 kg + i, group word w; its codes are channels
-  //    16 mu + i (mu = 2 grp, 2 grp + 1) of tokens T(kg, e); bits of rows before tnew0 are kept
+  //    16 mu + i (mu = 2 grp, 2 grp + 1) of tokens T(kg, e); bits of rows before vt0 are kept
   if (tid < 64 * VWG) {
     const int q = tid / VWG, w = tid % VWG, kg = q >> 4, i = q & 15;
     constexpr uint32_t m1 = (1u << VB) - 1;
@@ -644,18 +661,19 @@ __global__ __launch_bounds__(NT) void k_append_cs(AppendArgs a) {
       const int sq = (VWG * grp + w) * VPW + k, mu = sq >> 3, e = sq & 7;
       const int t = v_tok(kg, e), shf = 16 * (k & 1) + VB * (k >> 1);
       const int lc = 16 * (mu - 2 * grp) + i;
-      if (t < tnew0) word |= oldv & (m1 << shf);
+      if (t < vt0) word |= oldv & (m1 << shf);
       else if (t < tend) word |= (uint32_t)cvt[lc][t] << shf;
     }
     reinterpret_cast<uint32_t*>(rec + lv.v_codes)[q * wpc + VWG * grp + w] = word;
   }
-  // 6. V metadata of rows from tnew0 on (rows past tend cleared)
-  if (tid >= tnew0 && tid < G) {
+  // 6. V metadata of rows from vt0 on (rows past tend cleared)
+  if (tid >= vt0 && tid < G) {
     const int ng = D / 32, mi = v_meta_idx(tid, grp, ng);
     uint16_t* vm = reinterpret_cast<uint16_t*>(rec + lv.v_meta);
     vm[mi] = tid < tend ? vms[tid] : 0;
     if constexpr (!Q2K) vm[G * ng + mi] = tid < tend ? vmz[tid] : 0;
   }
+  }  // !open_mode
   // 7-9. the new rows' raw copies, from the values this thread loaded in the first phase (its rows
   //      rg + RGS i; fp16 input round-trips through fp32 exactly): staging of an open block, the
   //      fp16 window ring (rows p in [max(P, P+n-R), P+n)) and the fp16 sink pool
@@ -1077,21 +1095,24 @@ hipError_t launch_cs(const AppendArgs& a, hipStream_t st) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
   const Shape& sh = a.sh;
   if (sh.fmt != KVQ_FMT_TQ && sh.D % 32 == 0) {  // block formats
-    // whole blocks of fp16 input: one wave per (block, stream); the partial blocks at either end
-    // (an open block re-quantized from its staged rows, a block left open): one workgroup per
-    // (block, stream, 32-channel group)
-    const int64_t fb0 = (a.P + G - 1) / G, fb1 = (a.P + a.n) / G;
+    // The block the chunk starts inside (an open block: re-quantized from its staged rows, or with
+    // deferral completed from its staged K and fp16-window V rows) runs first and alone: later rows
+    // of the chunk overwrite staging and window slots it reads.  Then whole blocks of fp16 input: one
+    // wave per (block, stream); the block left open at the end and everything else: one workgroup
+    // per (block, stream, 32-channel group).
+    hipError_t e;
+    const int64_t end = a.P + a.n, fb0 = (a.P + G - 1) / G, fb1 = end / G, last = (end - 1) / G;
+    if (a.P % G != 0) {
+      AppendArgs e0 = a;
+      e0.blk0 = a.P / G;
+      e0.nblk = 1;
+      if ((e = launch_cs(e0, st)) != hipSuccess) return e;
+      if (end <= fb0 * G) return hipSuccess;  // the chunk ends inside that block
+    }
     const bool aligned = (reinterpret_cast<uintptr_t>(a.k) % 16 == 0) && (reinterpret_cast<uintptr_t>(a.v) % 16 == 0);
     if (!sh.in_f32 && aligned && fb1 > fb0) {
-      hipError_t e = launch_full(a, fb0, (int)(fb1 - fb0), st);
-      if (e != hipSuccess) return e;
-      if (a.P % G != 0) {
-        AppendArgs e0 = a;
-        e0.blk0 = a.P / G;
-        e0.nblk = 1;
-        if ((e = launch_cs(e0, st)) != hipSuccess) return e;
-      }
-      if ((a.P + a.n) % G != 0) {
+      if ((e = launch_full(a, fb0, (int)(fb1 - fb0), st)) != hipSuccess) return e;
+      if (end % G != 0) {
         AppendArgs e1 = a;
         e1.blk0 = fb1;
         e1.nblk = 1;
@@ -1099,7 +1120,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
       }
       return hipSuccess;
     }
-    return launch_cs(a, st);
+    AppendArgs e2 = a;
+    e2.blk0 = fb0;
+    e2.nblk = (int)(last - fb0 + 1);
+    return launch_cs(e2, st);
   }
   dim3 grid(a.nblk, sh.B * sh.Hkv);
   hipLaunchKernelGGL(k_append, grid, dim3(NT), 0, st, a);

@@ -959,6 +959,25 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
                 : 0u;
   }
   stage_sinks(a, b, F.spos, F.sslot, &F.nsink);
+  if (a.k1 != nullptr && f == 0) {
+    // fused decode step: the stream's appended row (position P - 1) goes to the staging rows and the
+    // fp16 window ring, and the block it opens gets a zero record.  Nothing in this launch reads
+    // either: the row is scored from k1 / v1, its window slot held a row below the window, and an
+    // open block lies inside the fp16 window.
+    const int64_t p = a.P - 1;
+    if (tid < FD / 2) {
+      const uint32_t kw = reinterpret_cast<const uint32_t*>(a.k1)[(int64_t)s * (FD / 2) + tid];
+      const uint32_t vw = reinterpret_cast<const uint32_t*>(a.v1)[(int64_t)s * (FD / 2) + tid];
+      const int64_t ws = (int64_t)s * sh.R + p % sh.R;
+      reinterpret_cast<uint32_t*>(lv.staging)[((int64_t)s * G + p % G) * (FD / 2) + tid] = kw;
+      reinterpret_cast<uint32_t*>(lv.win_k)[ws * (FD / 2) + tid] = kw;
+      reinterpret_cast<uint32_t*>(lv.win_v)[ws * (FD / 2) + tid] = vw;
+    }
+    if (a.open_new) {
+      uint32_t* rw = reinterpret_cast<uint32_t*>(lv.bulk + ((int64_t)s * lv.cap_b + (p / G) % lv.cap_b) * lv.rec);
+      for (int i = tid; i < (int)(lv.rec / 4); i += DNT) rw[i] = 0u;
+    }
+  }
 #pragma unroll
   for (int k = 0; k < QW; ++k) {
     const int idx = tid + k * DNT;
@@ -973,6 +992,8 @@ __device__ void fp16_partial(const DecodeArgs& a, FpSmem<R>& F, int f) {
   const int w0 = nwin > 0 ? (int)a.bulk_hi % sh.R : 0;  // window slot of row 0 (nwin <= R)
   auto row_ptr = [&](int i, bool v_side) -> const uint16_t* {  // fp16 row i of the list (i < nfp)
     if (i < nwin) {
+      if (a.k1 != nullptr && i == nwin - 1)  // fused step: the appended row, from the input
+        return static_cast<const uint16_t*>(v_side ? a.v1 : a.k1) + (int64_t)s * FD;
       const int ws = w0 + i < sh.R ? w0 + i : w0 + i - sh.R;
       return (v_side ? lv.win_v : lv.win_k) + ((int64_t)s * sh.R + ws) * FD;
     }

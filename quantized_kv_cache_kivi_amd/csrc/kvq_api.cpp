@@ -229,6 +229,13 @@ int splits_for(const kvq_config& c, int nblk, int slots, int extra) {
   return std::max(1, std::min(s, 64));
 }
 
+// Block formats with fp16 input and an fp16 window of at least one block quantize a block once, when
+// its last row arrives (KIVI groups keys per channel over full groups of tokens): while a block is
+// open all its rows are in the fp16 window, which serves every read of them, and its record is zero.
+bool defers_open_block(const kvq_config& c) {
+  return c.format != KVQ_FMT_TQ && c.in_dtype == KVQ_IN_F16 && c.residual >= G;
+}
+
 // Upper bound of the splits of any decode call (sizes the workspace from the configuration alone).
 int max_splits(const kvq_config& c) {
   const int nblk = effective_capacity(c) / G;
@@ -460,6 +467,7 @@ kvq_status kvq_append(kvq_cache* c, int32_t layer, const void* k, const void* v,
   a.n = n;
   a.blk0 = P / G;
   a.nblk = (int)((P + n - 1) / G - a.blk0 + 1);
+  a.defer = defers_open_block(cf) ? 1 : 0;
   hipError_t e = launch_append(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "append launch");
   c->P[layer] = P + n;
@@ -483,6 +491,47 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   return kvq::decode_attn_ws(c, layer, q, out, scale, ws, ws_bytes, stream);
 }
 
+kvq_status kvq_decode_step(kvq_cache* c, int32_t layer, const void* k, const void* v, const void* q, float* out,
+                           float scale, void* ws, size_t ws_bytes, void* stream) {
+  kvq_status st = check_layer(c, layer);
+  if (st != KVQ_OK) return st;
+  if (!k || !v || !q || !out || !ws) return fail(KVQ_EINVAL, "k, v, q, out and ws must not be NULL");
+  if (ws_bytes < kvq_workspace_bytes(&c->cfg)) return fail(KVQ_EINVAL, "ws_bytes too small");
+  const kvq_config& cf = c->cfg;
+  const int64_t P = c->P[layer], lo = c->lo[layer];
+  // One launch when the row changes no sink (the committed set is min(n_sink, P) rows: full, or
+  // static), completes no block, and the decode kernel reads neither the open block's record (the
+  // fp16 window covers it) nor the row's window slot (the row is scored from k and v).
+  const bool aligned = (reinterpret_cast<uintptr_t>(k) % 16 == 0) && (reinterpret_cast<uintptr_t>(v) % 16 == 0);
+  const bool fuse = c->slots > 0 && fast_path(cf) && defers_open_block(cf) && aligned && (P + 1) % G != 0 &&
+                    (cf.n_sink == 0 || P >= cf.n_sink) && P + 1 <= (int64_t)INT32_MAX;
+  if (!fuse) {
+    if (cf.sink_mode == KVQ_SINK_TOPK && cf.n_sink > 0 && (st = kvq_select_sinks(c, layer, k, 1, stream)) != KVQ_OK)
+      return st;
+    if ((st = kvq_append(c, layer, k, v, 1, stream)) != KVQ_OK) return st;
+    if ((st = kvq_evict(c, layer)) != KVQ_OK) return st;
+    return kvq::decode_attn_ws(c, layer, q, out, scale, ws, ws_bytes, stream);
+  }
+  // the checks kvq_append makes
+  if (cf.window == 0) {
+    if (P + 1 > cf.capacity) return fail(KVQ_ECAPACITY, "append of 1 row at P=%lld exceeds capacity %d", (long long)P, cf.capacity);
+  } else if ((P / G - c->lay.cap_blocks + 1) * G > lo) {
+    return fail(KVQ_ECAPACITY, "append of 1 row at P=%lld would overwrite a live block (lo=%lld); evict first",
+                (long long)P, (long long)lo);
+  }
+  c->P[layer] = P + 1;
+  if (cf.window > 0) c->lo[layer] = std::max(lo, P + 1 - (int64_t)cf.window);
+  st = kvq::decode_attn_ws(c, layer, q, out, scale, ws, ws_bytes, stream, k, v, P % G == 0 ? 1 : 0);
+  if (st != KVQ_OK) {  // nothing launched: the call leaves the state as it found it
+    c->P[layer] = P;
+    c->lo[layer] = lo;
+    return st;
+  }
+  c->pend_P[layer] = -1;
+  c->pend_n[layer] = -1;
+  return KVQ_OK;
+}
+
 }  // extern "C"
 
 namespace kvq {
@@ -490,7 +539,7 @@ namespace kvq {
 // Decode attention with the split partials in ws (ws_bytes long): fails with KVQ_ECAPACITY, launching
 // nothing, if this call's partials do not fit.
 kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
-                          size_t ws_bytes, void* stream) {
+                          size_t ws_bytes, void* stream, const void* k1, const void* v1, int open_new) {
   kvq_status st = check_layer(c, layer);
   if (st != KVQ_OK) return st;
   if (!q || !out || !ws) return fail(KVQ_EINVAL, "q, out and ws must not be NULL");
@@ -507,6 +556,9 @@ kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)cf.head_dim);
   a.P = P;
   a.lo = lo;
+  a.k1 = k1;
+  a.v1 = v1;
+  a.open_new = open_new;
   a.bulk_lo = lo;
   a.bulk_hi = std::max(lo, P - (int64_t)cf.residual);
   // fp16 rows: window rows [bulk_hi, P) and at most min(n_sink, P) committed sinks (the kernels read

@@ -61,6 +61,7 @@ struct AppendArgs {
   int n;                // rows in this call
   int64_t blk0;         // first block touched
   int nblk;             // blocks touched
+  int defer;            // 1: blocks are quantized when they complete (block formats, fp16 input, residual >= 32)
 };
 
 struct SelectArgs {
@@ -88,6 +89,9 @@ struct DecodeArgs {
   int fast;                  // 1: MFMA path (head_dim 128, fp16 input, KIVI equal widths or q2k, GQA 1/2/4/8)
   int nparts;                // partials per stream in the workspace: bulk splits, then the fp16-row groups
                              // (MFMA path: ceil(rows / 64); TurboQuant: 1; other formats: 0)
+  const void* k1;            // fused decode step: the row appended at P - 1, [B][Hkv][1][D] fp16 (else NULL);
+  const void* v1;            // scored from here, copied to staging and window by fp16 group 0
+  int open_new;              // fused step whose row opens a block: that block's record is zeroed
 };
 
 struct PrefillArgs {
@@ -139,7 +143,8 @@ int stored_dim(const kvq_config& c);
 // launched, when this call's partials need more.  Shared by kvq_decode_attn (caller's workspace) and
 // kvq_decode_attn_nomalloc (the library's static workspace).
 kvq_status decode_attn_ws(kvq_cache* c, int32_t layer, const void* q, float* out, float scale, void* ws,
-                          size_t ws_bytes, void* stream);
+                          size_t ws_bytes, void* stream, const void* k1 = nullptr, const void* v1 = nullptr,
+                          int open_new = 0);
 // Takes the current device's address of the static decode workspace once per device (kvq_create
 // calls it so that the address is known before any allocation-free call).
 kvq_status static_ws_prepare();

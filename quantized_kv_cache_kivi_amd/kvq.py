@@ -84,6 +84,7 @@ def _load():
         "kvq_evict": (I32, [P, I32]),
         "kvq_decode_attn": (I32, [P, I32, P, P, F32, P, SZ, P]),
         "kvq_decode_attn_nomalloc": (I32, [P, I32, P, P, F32, P]),
+        "kvq_decode_step": (I32, [P, I32, P, P, P, P, F32, P, SZ, P]),
         "kvq_stream_read": (I32, [P, ctypes.c_uint64, P, P]),
         "kvq_dequant": (I32, [P, I32, I32, I64, I32, P, P]),
         "kvq_prefill_attn": (I32, [P, I32, P, I32, P, F32, P]),
@@ -213,6 +214,11 @@ class Cache:
     def kvq_decode_attn(self, layer, q, out, scale=0.0):
         _check(_decode(self.handle, layer, q.data_ptr(), out.data_ptr(), scale, self._ws[0], self._ws[1],
                        _stream(self.dev)))
+
+    def kvq_decode_step(self, layer, k, v, q, out, scale=0.0):
+        """select_sinks + append(1 row) + evict + decode_attn for the row k, v ([B][Hkv][1][D])."""
+        _check(lib.kvq_decode_step(self.handle, layer, _ptr(k), _ptr(v), q.data_ptr(), out.data_ptr(), scale,
+                                   self._ws[0], self._ws[1], _stream(self.dev)))
 
     def kvq_decode_attn_nomalloc(self, layer, q, out, scale=0.0):
         _check(lib.kvq_decode_attn_nomalloc(self.handle, layer, q.data_ptr(), out.data_ptr(), scale,

@@ -62,6 +62,8 @@ CASES = {
                                v_bits=2, sink_mode="first_n", n_sink=2, window=70, residual=8, seed=31),
     "tq_k4v4_d160_f32": dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=2, head_dim=160, fmt="tq", k_bits=4,
                              v_bits=4, residual=4, in_dtype="f32", seed=32),
+    "kivi4_first_n_res40_window": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="kivi",
+                                       k_bits=4, v_bits=4, sink_mode="first_n", n_sink=4, window=90, residual=40),
     "kivi2_topk_window_rope": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="kivi",
                                    k_bits=2, v_bits=2, sink_mode="topk", n_sink=3, window=100, residual=16,
                                    rope=True),
