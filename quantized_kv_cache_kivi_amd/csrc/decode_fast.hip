@@ -1186,6 +1186,57 @@ __device__ __forceinline__ void merge_range(const float* P0, int q0, int q1, int
 // in the rotated domain: they are merged first and rotated back (sigma * (c_d * FWHT(acc));
 // "TurboQuant KV Cache Compression — Spec", "Optimization: Fused dequant-dot") before the fp16
 // groups, which are in the original domain, join the merge.
+// The same for every head at once (no rotation): thread (half, c) merges channel c of heads half,
+// half + 2, ..., with the loads of all its heads for a chunk of partials issued together, so the
+// merge takes one memory round trip per chunk instead of one per head pair.
+template <int R>
+__device__ void merge_heads(const DecodeArgs& a, int s) {
+  constexpr int NH = (R + 1) / 2, MC = NH <= 2 ? 16 : 8;
+  const int tid = threadIdx.x, half = tid >> 7, c = tid & (FD - 1);
+  const int b = s / a.sh.Hkv, g = s % a.sh.Hkv;
+  const float* base = a.ws + (int64_t)s * a.nparts * R * (FD + 2);
+  float M[NH], L[NH], v[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) M[h] = -INFINITY, L[h] = 0.f, v[h] = 0.f;
+  for (int qb = 0; qb < a.nparts; qb += MC) {
+    float mq[NH][MC], lq[NH][MC], vq[NH][MC];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const int j = half + 2 * h, jj = j < R ? j : R - 1;
+#pragma unroll
+      for (int k = 0; k < MC; ++k) {  // past the last part: re-read it (no branch between the loads), unused
+        const bool in = qb + k < a.nparts;
+        const float* pq = base + (int64_t)(in ? qb + k : a.nparts - 1) * R * (FD + 2) + jj * (FD + 2);
+        const float m = ld_part(pq), l = ld_part(pq + 1), x = ld_part(pq + 2 + c);
+        mq[h][k] = in ? m : -INFINITY;
+        lq[h][k] = in ? l : 0.f;
+        vq[h][k] = in ? x : 0.f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float Mn = M[h];
+#pragma unroll
+      for (int k = 0; k < MC; ++k) Mn = fmaxf(Mn, mq[h][k]);
+      const float fo = M[h] == -INFINITY ? 0.f : ex2(M[h] - Mn);  // the sums so far are 0 while M = -inf
+      L[h] *= fo;
+      v[h] *= fo;
+#pragma unroll
+      for (int k = 0; k < MC; ++k) {
+        const float w = mq[h][k] == -INFINITY ? 0.f : ex2(mq[h][k] - Mn);
+        L[h] = __builtin_fmaf(lq[h][k], w, L[h]);
+        v[h] = __builtin_fmaf(vq[h][k], w, v[h]);
+      }
+      M[h] = Mn;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int j = half + 2 * h;
+    if (j < R && c < a.sh.Din) a.out[((int64_t)b * a.sh.Hq + (int64_t)g * R + j) * a.sh.Din + c] = v[h] / L[h];
+  }
+}
+
 template <int R, bool TQ>
 __device__ void merge_stream(const DecodeArgs& a, int s, float (*rot)[FD]) {
   const int tid = threadIdx.x, half = tid >> 7, c = tid & (FD - 1);
@@ -1237,7 +1288,8 @@ void k_decode_fast(DecodeArgs a) {
   }
   __syncthreads();
   if (!last) return;
-  merge_stream<R, FMT == KVQ_FMT_TQ>(a, s, S.rot);
+  if constexpr (FMT == KVQ_FMT_TQ) merge_stream<R, true>(a, s, S.rot);
+  else merge_heads<R>(a, s);
 }
 
 template <int FMT, int KB, int VB, bool RP>

@@ -23,9 +23,11 @@ namespace kvq {
 constexpr int PT = 2;     // 16-column tiles per wave (block formats)
 namespace {
 
-constexpr int PNW = 4;    // waves per workgroup
-constexpr int PNT = 64 * PNW;
-constexpr int SL = PNT / G;  // staging threads per row
+// Waves per workgroup (a template parameter of the kernel): 4.  With 8 (one staged row block feeding
+// 8 waves, half the staging work per column) the config-2 prefill took 5.6 ms instead of 4.9: one
+// 8-wave workgroup per CU leaves no second workgroup to compute while one stages.  Queries staged
+// through LDS (TurboQuant, RoPE, fp32) need 4: their staging tile holds 16 columns per wave.
+constexpr int PNW_DIRECT = 4, PNW_LDS = 4;
 constexpr float PLOG2E = 1.4426950408889634f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -53,8 +55,9 @@ struct PfSmem {
   float kcen[16], vcen[16];  // TurboQuant centroids (rotated domain)
 };
 
-template <int FMT, int KB, int VB, int D, bool LQ, int PTT>
-__global__ __launch_bounds__(PNT) void k_prefill_attn(PrefillArgs a) {
+template <int FMT, int KB, int VB, int D, bool LQ, int PTT, int PW>
+__global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
+  constexpr int PNW = PW, PNT = 64 * PW, SL = PNT / G;  // waves and threads per workgroup, staging threads per row
   // TurboQuant works in the rotated domain ("TurboQuant KV Cache Compression — Spec", "Optimization:
   // Fused dequant-dot"): queries rotated once (fp16 hi + lo, a third score product), bulk rows are
   // norm times centroid, fp16 window and sink rows are rotated while staged, outputs rotated back
@@ -608,12 +611,13 @@ int tiles_per_wave(const PrefillArgs& a) {
 
 template <int FMT, int KB, int VB, bool LQ, int PTT>
 hipError_t launch_drp(const PrefillArgs& a, hipStream_t st) {
-  const int QT = PNW * PTT * (16 / (a.sh.Hq / a.sh.Hkv));
+  constexpr int PW = (FMT == KVQ_FMT_TQ || LQ) ? PNW_LDS : PNW_DIRECT;
+  const int QT = PW * PTT * (16 / (a.sh.Hq / a.sh.Hkv));
   const dim3 grid((a.n + QT - 1) / QT, a.sh.B * a.sh.Hkv, a.splits > 1 ? a.splits : 1);
   switch (a.sh.D) {
-    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, LQ, PTT>), grid, dim3(PNT), 0, st, a); break;
-    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, LQ, PTT>), grid, dim3(PNT), 0, st, a); break;
-    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, LQ, PTT>), grid, dim3(PNT), 0, st, a); break;
+    case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -653,9 +657,8 @@ hipError_t launch_kivi(const PrefillArgs& a, hipStream_t st) {
 
 }  // namespace
 
-int prefill_queries_per_tile(int r, int fmt, int rope) {  // (long chunks)
-  (void)rope;
-  return PNW * (fmt == KVQ_FMT_TQ ? 1 : PT) * (16 / r);
+int prefill_queries_per_tile(int r, int fmt, int rope) {  // (long chunks, fp16 queries)
+  return fmt == KVQ_FMT_TQ ? PNW_LDS * (16 / r) : (rope ? PNW_LDS : PNW_DIRECT) * PT * (16 / r);
 }
 
 int prefill_row_blocks(const PrefillArgs& a) {
