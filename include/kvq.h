@@ -95,7 +95,10 @@ typedef struct {
   int32_t batch;      /* >= 1 */
   int32_t n_kv_heads; /* >= 1 */
   int32_t n_q_heads;  /* multiple of n_kv_heads, ratio <= 16 */
-  int32_t head_dim;   /* 32, 64 or 128 */
+  int32_t head_dim;   /* 32, 64 or 128; with TQ also 96 or 160, stored zero-padded to the next power of two
+                         (128, 256: [TQ] "Hadamard Transform Detail", every rotated coordinate kept), so
+                         every per-row width of the layout is that stored width; top-k sinks need head_dim
+                         32, 64 or 128 */
   int32_t format;     /* KVQ_FMT_*: KIVI bits (k,v) each in {2,4,8}; Q2K (2,4); TQ each in {2,3,4} (3-bit codes
                          two per byte with two bits unused, [TQ] "Step 3: Packing": stored as 4-bit slots) */
   int32_t k_bits, v_bits;
@@ -252,7 +255,7 @@ kvq_status kvq_decode_attn_nomalloc(kvq_cache* c, int32_t layer, const void* q, 
  * scale <= 0 means 1/sqrt(head_dim).  Every cache format (TurboQuant in the
  * rotated domain: queries rotated once, outputs rotated back); fp32
  * queries enter the matrix cores as fp16 hi + lo pairs; head_dim 32, 64 or
- * 128 (else KVQ_EINVAL); 1 <= n <= P (else
+ * 128, or TQ's padded 96 and 160 (else KVQ_EINVAL); 1 <= n <= P (else
  * KVQ_ERANGE).  One kernel launch, no workspace; deterministic. */
 kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t n, float* out, float scale,
                             void* stream);
@@ -274,7 +277,7 @@ kvq_status kvq_account(kvq_cache* c, int32_t layer, kvq_bytes* out, void* stream
 /* Host state of `layer`: appended length P and eviction boundary lo. */
 kvq_status kvq_get_state(const kvq_cache* c, int32_t layer, int64_t* P, int64_t* lo);
 
-/* Host copies of the tables kvq_create writes: signs[head_dim], K boundaries
+/* Host copies of the tables kvq_create writes: signs[stored width], K boundaries
  * [2^k_bits - 1], K centroids [2^k_bits], V boundaries, V centroids (TQ, in
  * the t = 2u - 1 space), and the Q2K thresholds[3] and levels[4].  Any
  * pointer may be NULL. */

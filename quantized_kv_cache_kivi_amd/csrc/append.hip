@@ -20,7 +20,6 @@ namespace kvq {
 namespace {
 
 constexpr int NT = 256;
-constexpr int XP = MAX_D + 1;  // padded LDS row (bank spread for per-row loops)
 
 // min / max over the 32 lanes of a half-wave (every lane of the half ends with the result)
 __device__ __forceinline__ float half_min(float x) {
@@ -34,8 +33,11 @@ __device__ __forceinline__ float half_max(float x) {
 
 // Thread layout: channel c = tid % D and row group rg = tid / D hold rows t = rg + RG*i of the
 // block (RG = 256 / D row groups, i < 32 / RG), in registers.  The 32 channels of a V group
-// are the 32 lanes of one half-wave.
+// are the 32 lanes of one half-wave.  MD: the widest stored row the instance takes (128, or 256
+// for TurboQuant rows of head_dim 160).
+template <int MD>
 __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
+  constexpr int XP = MD + 1;  // padded LDS row (bank spread for per-row loops)
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int D = sh.D, tid = threadIdx.x;
@@ -51,9 +53,9 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
 
   __shared__ float xk[G][XP];          // K rows (q2k sum of squares, TurboQuant rows)
   __shared__ float xv[G][XP];          // V rows (TurboQuant rows)
-  __shared__ alignas(16) uint8_t ck[G][MAX_D];   // K codes [token][channel]
-  __shared__ alignas(16) uint8_t cvt[MAX_D][G];  // V codes [channel][token]
-  __shared__ float red0[NT / 32][MAX_D], red1[NT / 32][MAX_D];  // per row group partials
+  __shared__ alignas(16) uint8_t ck[G][MD];   // K codes [token][channel]
+  __shared__ alignas(16) uint8_t cvt[MD][G];  // V codes [channel][token]
+  __shared__ float red0[NT / 32][MD], red1[NT / 32][MD];  // per row group partials
   __shared__ int sink_slot[G];
   __shared__ uint32_t smask_s;
   __shared__ uint16_t vmeta_s[G][4], vmeta_z[G][4];
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
   // instead of one per loop iteration): the committed sink list, this thread's elements of the
   // block's rows (new rows from the chunk, earlier rows of an open K block from staging) and the
   // V code words that hold bits of rows appended by earlier calls.
-  constexpr int PER = G * MAX_D / NT;  // row elements per thread (at most)
+  constexpr int PER = G * MD / NT;  // row elements per thread (at most)
   const int nper = G * D / NT;         // row elements per thread
   const int ng = D / 32;
   const int wpc = D * sh.vb / 64;      // words per V code chunk (word-interleaved widths)
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
       }
     }
   }
-  constexpr int VW = 64 * (MAX_D * 8 / 64) / NT;  // V code words per thread (at most)
+  constexpr int VW = 64 * (MD * 8 / 64) / NT;  // V code words per thread (at most)
   uint32_t oldv[VW];
   {
     const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
         xv[rg + RG * i][c] = vx[i];
       }
   }
-  for (int idx = tid; idx < G * MAX_D / 16; idx += NT) {
+  for (int idx = tid; idx < G * MD / 16; idx += NT) {
     reinterpret_cast<uint4*>(&ck[0][0])[idx] = uint4{0, 0, 0, 0};
     reinterpret_cast<uint4*>(&cvt[0][0])[idx] = uint4{0, 0, 0, 0};
   }
@@ -248,7 +250,8 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
       }
     }
   } else {
-    // TQ rows (K and V) and the rotation: one wave per row
+    // TQ rows (K and V) and the rotation: one wave per row, MD / 64 channels per lane
+    constexpr int NK = MD / 64;
     const int lane = tid & 63, w = tid >> 6;
     const float cd = (float)(1.0 / __builtin_sqrt((double)D));
     const Tables* T = lv.tables;
@@ -258,26 +261,25 @@ __global__ __launch_bounds__(NT) void k_append(AppendArgs a) {
         float (*X)[XP] = which ? xv : xk;
         const int nb = which ? sh.vb : sh.kb;
         const float* bnd = which ? T->v_bnd : T->k_bnd;
-        const bool act = 2 * lane < D;
-        float y0 = act ? X[t][2 * lane] * T->signs[2 * lane] : 0.f;
-        float y1 = act ? X[t][2 * lane + 1] * T->signs[2 * lane + 1] : 0.f;
-        wave_fwht(y0, y1, D, lane);
-        y0 = y0 * cd;
-        y1 = y1 * cd;
-        const float nrm = sqrtf(wave_sumsq(y0, y1, D));
-        const float t0 = nrm > 0.f ? y0 / nrm : 0.f, t1 = nrm > 0.f ? y1 / nrm : 0.f;
-        int u0 = 0, u1 = 0;
-        for (int j = 0; j < (1 << nb) - 1; ++j) {
-          u0 += t0 >= bnd[j];
-          u1 += t1 >= bnd[j];
+        float y[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const int cc = row_chan(lane, k);
+          y[k] = cc < D ? X[t][cc] * T->signs[cc] : 0.f;
         }
-        if (act) {
-          if (which) {
-            cvt[2 * lane][t] = (uint8_t)u0;
-            cvt[2 * lane + 1][t] = (uint8_t)u1;
-          } else {
-            ck[t][2 * lane] = (uint8_t)u0;
-            ck[t][2 * lane + 1] = (uint8_t)u1;
+        row_fwht<MD>(y, D, lane);
+#pragma unroll
+        for (int k = 0; k < NK; ++k) y[k] = y[k] * cd;
+        const float nrm = sqrtf(row_sumsq<MD>(y, D));
+#pragma unroll
+        for (int k = 0; k < NK; ++k) {
+          const int cc = row_chan(lane, k);
+          const float tv = nrm > 0.f ? y[k] / nrm : 0.f;
+          int u = 0;
+          for (int j = 0; j < (1 << nb) - 1; ++j) u += tv >= bnd[j];
+          if (cc < D) {
+            if (which) cvt[cc][t] = (uint8_t)u;
+            else ck[t][cc] = (uint8_t)u;
           }
         }
         if (lane == 0) (which ? vnorm : knorm)[t] = nrm;
@@ -1126,7 +1128,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t st) {
     return launch_cs(e2, st);
   }
   dim3 grid(a.nblk, sh.B * sh.Hkv);
-  hipLaunchKernelGGL(k_append, grid, dim3(NT), 0, st, a);
+  if (sh.D > MAX_D) hipLaunchKernelGGL(k_append<MAX_SD>, grid, dim3(NT), 0, st, a);
+  else hipLaunchKernelGGL(k_append<MAX_D>, grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 

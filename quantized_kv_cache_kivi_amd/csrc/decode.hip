@@ -24,14 +24,17 @@
 namespace kvq {
 namespace {
 
+// MD: the widest stored row the instance takes (128, or 256 for TurboQuant rows of head_dim 160).
+template <int MD>
 __global__ __launch_bounds__(DNT) void k_decode(DecodeArgs a) {
-  __shared__ Smem S;
-  generic_partial(a, S);
+  __shared__ Smem<MD> S;
+  generic_partial<MD>(a, S);
 }
 
+template <int MD>
 __global__ __launch_bounds__(DNT) void k_decode_merge(DecodeArgs a) {
-  __shared__ Smem S;
-  merge_partials(a, S);
+  __shared__ Smem<MD> S;
+  merge_partials<MD>(a, S);
 }
 
 constexpr int MNT = 256;  // threads of a merge workgroup
@@ -278,14 +281,17 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   hipError_t e;
   if (a.nparts > 0) {
     dim3 grid(a.nparts, a.sh.B * a.sh.Hkv);
-    hipLaunchKernelGGL(k_decode, grid, dim3(DNT), 0, st, a);
+    if (a.sh.D > MAX_D) hipLaunchKernelGGL(k_decode<MAX_SD>, grid, dim3(DNT), 0, st, a);
+    else hipLaunchKernelGGL(k_decode<MAX_D>, grid, dim3(DNT), 0, st, a);
     e = hipGetLastError();
   } else {
     e = hipSuccess;
   }
   if (e != hipSuccess) return e;
-  if (a.sh.fmt == KVQ_FMT_TQ || a.sh.rope)
-    hipLaunchKernelGGL(k_decode_merge, dim3(a.sh.B * a.sh.Hkv), dim3(DNT), 0, st, a);
+  if (a.sh.D > MAX_D)
+    hipLaunchKernelGGL(k_decode_merge<MAX_SD>, dim3(a.sh.B * a.sh.Hkv), dim3(DNT), 0, st, a);
+  else if (a.sh.fmt == KVQ_FMT_TQ || a.sh.rope)
+    hipLaunchKernelGGL(k_decode_merge<MAX_D>, dim3(a.sh.B * a.sh.Hkv), dim3(DNT), 0, st, a);
   else
     hipLaunchKernelGGL(k_merge_heads, dim3(a.sh.B * a.sh.Hkv, a.sh.Hq / a.sh.Hkv), dim3(MNT), 0, st, a);
   return hipGetLastError();

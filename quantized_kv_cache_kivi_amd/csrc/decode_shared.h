@@ -14,10 +14,13 @@ namespace kvq {
 constexpr float LOG2E = 1.4426950408889634f;
 
 constexpr int DNT = 256;  // threads of a decode workgroup
-constexpr int MAX_REC = 2 * G * MAX_D + 4 * MAX_D + 4 * G * 4;  // 8-bit K and V, KIVI metadata
 
+// Shared memory of the generic decode kernels for rows of at most MD stored channels (128, or 256 for
+// TurboQuant rows of head_dim 160).
+template <int MD>
 struct Smem {
-  float q[MAX_GQA][MAX_D];       // query (rotated for TurboQuant bulk); merged output in merge_partials()
+  static constexpr int MAX_REC = 2 * G * MD + 4 * MD + 4 * G * 4;  // 8-bit K and V, KIVI metadata
+  float q[MAX_GQA][MD];          // query (rotated for TurboQuant bulk); merged output in merge_partials()
   float sc[MAX_GQA][G];          // scores, then weights, of the current 32 rows
   float fac[MAX_GQA];            // rescale factors of the current step
   float m[MAX_GQA], l[MAX_GQA];  // running max and denominator
@@ -28,7 +31,7 @@ struct Smem {
   int rk[G];                // RoPE on read: index in the compressed cache of each row of the chunk
   union {
     alignas(16) uint8_t rec[MAX_REC];                       // staged block record (bulk)
-    struct { uint16_t k[G][MAX_D], v[G][MAX_D]; } rows;     // fp16 rows of the current chunk
+    struct { uint16_t k[G][MD], v[G][MD]; } rows;           // fp16 rows of the current chunk
     float red[DNT][MAX_GQA];                                 // cross-slice reduction (after the loop)
   } u;
 };
@@ -84,7 +87,8 @@ __device__ __forceinline__ float v_val(const Shape& sh, const uint8_t* rec, cons
 
 // Partial of this workgroup: bulk blocks of split `sigma`, or (sigma == splits, TurboQuant and
 // RoPE-on-read caches) the fp16 rows.
-__device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
+template <int MD>
+__device__ inline void generic_partial(const DecodeArgs& a, Smem<MD>& S) {
 
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
@@ -107,7 +111,7 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
   if (sh.rope) {  // the query turns by its own index: the last valid position, P - 1
     const int qi = cache_index(S.sinks, S.nsinks, a.lo, a.P - 1);
     const int h = D / 2;
-    float qa[MAX_GQA * MAX_D / 2 / DNT + 1], qb[MAX_GQA * MAX_D / 2 / DNT + 1];
+    float qa[MAX_GQA * MD / 2 / DNT + 1], qb[MAX_GQA * MD / 2 / DNT + 1];
     int n = 0;
     for (int idx = tid; idx < r * h; idx += DNT, ++n) {
       const int j = idx / h, c = idx % h;
@@ -124,15 +128,20 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
     __syncthreads();
   }
   if (tq && !fp16_split) {  // rotate the query: q~ = c_d * FWHT(sigma * q)
+    constexpr int NK = MD / 64;
     const float cd = (float)(1.0 / __builtin_sqrt((double)D));
     for (int j = tid >> 6; j < r; j += DNT / 64) {
-      const bool act = 2 * lane < D;
-      float y0 = act ? S.q[j][2 * lane] * lv.tables->signs[2 * lane] : 0.f;
-      float y1 = act ? S.q[j][2 * lane + 1] * lv.tables->signs[2 * lane + 1] : 0.f;
-      wave_fwht(y0, y1, D, lane);
-      if (act) {
-        S.q[j][2 * lane] = y0 * cd;
-        S.q[j][2 * lane + 1] = y1 * cd;
+      float y[NK];
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int c = row_chan(lane, k);
+        y[k] = c < D ? S.q[j][c] * lv.tables->signs[c] : 0.f;
+      }
+      row_fwht<MD>(y, D, lane);
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int c = row_chan(lane, k);
+        if (c < D) S.q[j][c] = y[k] * cd;
       }
     }
     __syncthreads();
@@ -292,7 +301,8 @@ __device__ inline void generic_partial(const DecodeArgs& a, Smem& S) {
 
 // Fixed-order merge of the split partials of stream blockIdx.x and the output
 // (runs in its own kernel, after every split has written its partial).
-__device__ inline void merge_partials(const DecodeArgs& a, Smem& S) {
+template <int MD>
+__device__ inline void merge_partials(const DecodeArgs& a, Smem<MD>& S) {
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int D = sh.D, r = sh.Hq / sh.Hkv, tid = threadIdx.x, lane = tid & 63;
@@ -322,20 +332,25 @@ __device__ inline void merge_partials(const DecodeArgs& a, Smem& S) {
       const float mq = P0[(q * r + j) * (D + 2)];
       if (mq != -INFINITY) v += P0[(q * r + j) * (D + 2) + 2 + c] * exp2f(mq - S.Mb[j]);
     }
-    fin[j * MAX_D + c] = v;
+    fin[j * MD + c] = v;
   }
   __syncthreads();
   if (tq) {
     // inverse rotation of the merged bulk accumulator: sigma * (c_d * FWHT(acc))
+    constexpr int NK = MD / 64;
     const float cd = (float)(1.0 / __builtin_sqrt((double)D));
     for (int j = tid >> 6; j < r; j += DNT / 64) {
-      const bool act = 2 * lane < D;
-      float y0 = act ? fin[j * MAX_D + 2 * lane] : 0.f;
-      float y1 = act ? fin[j * MAX_D + 2 * lane + 1] : 0.f;
-      wave_fwht(y0, y1, D, lane);
-      if (act) {
-        fin[j * MAX_D + 2 * lane] = lv.tables->signs[2 * lane] * (y0 * cd);
-        fin[j * MAX_D + 2 * lane + 1] = lv.tables->signs[2 * lane + 1] * (y1 * cd);
+      float y[NK];
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int c = row_chan(lane, k);
+        y[k] = c < D ? fin[j * MD + c] : 0.f;
+      }
+      row_fwht<MD>(y, D, lane);
+#pragma unroll
+      for (int k = 0; k < NK; ++k) {
+        const int c = row_chan(lane, k);
+        if (c < D) fin[j * MD + c] = lv.tables->signs[c] * (y[k] * cd);
       }
     }
     __syncthreads();
@@ -352,13 +367,13 @@ __device__ inline void merge_partials(const DecodeArgs& a, Smem& S) {
     __syncthreads();
     for (int idx = tid; idx < r * D; idx += DNT) {
       const int j = idx / D, c = idx % D;
-      const float v = fin[j * MAX_D + c] * S.fac[j] + P0[(nbulk * r + j) * (D + 2) + 2 + c] * S.m[j];
+      const float v = fin[j * MD + c] * S.fac[j] + P0[(nbulk * r + j) * (D + 2) + 2 + c] * S.m[j];
       if (c < sh.Din) a.out[((int64_t)b * sh.Hq + g * r + j) * sh.Din + c] = v / S.l[j];
     }
   } else {
     for (int idx = tid; idx < r * D; idx += DNT) {
       const int j = idx / D, c = idx % D;
-      if (c < sh.Din) a.out[((int64_t)b * sh.Hq + g * r + j) * sh.Din + c] = fin[j * MAX_D + c] / S.Lb[j];
+      if (c < sh.Din) a.out[((int64_t)b * sh.Hq + g * r + j) * sh.Din + c] = fin[j * MD + c] / S.Lb[j];
     }
   }
 }

@@ -16,7 +16,11 @@ namespace {
 
 constexpr int NT = 256;
 
+// MD: the widest stored row the instance takes (128, or 256 for TurboQuant rows of head_dim 160);
+// lane l holds channels 128h + 2l + e in x[2h + e].
+template <int MD>
 __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
+  constexpr int NK = MD / 64;
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int D = sh.D, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -26,8 +30,7 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
   const int64_t p = a.pos0 + i;
   const bool is_k = a.which == 0;
   uint16_t* out = a.out + ((int64_t)s * a.count + i) * sh.Din;  // rows of the caller's Din channels
-  const bool act = 2 * lane < D;
-  const bool wr = 2 * lane < sh.Din;  // Din is even: a lane writes both of its channels or neither
+  // Din is even: a lane writes both channels of a pair or neither
   // sink pool
   int slot = -1;
   if (sh.n_sink > 0) {
@@ -38,9 +41,10 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
   if (slot >= 0 || p >= a.P - sh.R) {
     const uint16_t* src = slot >= 0 ? (is_k ? lv.sink_k : lv.sink_v) + ((int64_t)s * sh.n_sink + slot) * D
                                     : (is_k ? lv.win_k : lv.win_v) + ((int64_t)s * sh.R + p % sh.R) * D;
-    if (wr) {
-      out[2 * lane] = src[2 * lane];
-      out[2 * lane + 1] = src[2 * lane + 1];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = row_chan(lane, k);
+      if (c < sh.Din) out[c] = src[c];
     }
     return;
   }
@@ -49,48 +53,56 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
   const uint8_t* rec = lv.bulk + ((int64_t)s * lv.cap_b + blk % lv.cap_b) * lv.rec;
   const int nb = is_k ? sh.kb : sh.vb;
   const uint8_t* codes = rec + (is_k ? lv.k_codes : lv.v_codes);
-  float x[2];
-  uint32_t u[2];
-  for (int e = 0; e < 2; ++e) {
-    const int c = act ? 2 * lane + e : 0;
-    int wd, k;
+  float x[NK];
+  uint32_t u[NK];
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int c0 = row_chan(lane, k), c = c0 < D ? c0 : 0;
+    int wd, kk;
     if (nb == 3) {  // dense 3-bit stream
-      u[e] = code3_at(codes, is_k ? k_bit3(t, c, D) : v_bit3(t, c, D));
+      u[k] = code3_at(codes, is_k ? k_bit3(t, c, D) : v_bit3(t, c, D));
       continue;
     }
-    if (is_k) k_code_pos(t, c, D, nb, &wd, &k);
-    else v_code_pos(t, c, D, nb, &wd, &k);
-    u[e] = (reinterpret_cast<const uint32_t*>(codes)[wd] >> code_shift(k, nb)) & ((1u << nb) - 1u);
+    if (is_k) k_code_pos(t, c, D, nb, &wd, &kk);
+    else v_code_pos(t, c, D, nb, &wd, &kk);
+    u[k] = (reinterpret_cast<const uint32_t*>(codes)[wd] >> code_shift(kk, nb)) & ((1u << nb) - 1u);
   }
   if (sh.fmt == KVQ_FMT_TQ) {
     const float nrm = reinterpret_cast<const float*>(rec + (is_k ? lv.k_meta : lv.v_meta))[t];
     const float* cen = is_k ? lv.tables->k_cen : lv.tables->v_cen;
-    float y0 = act ? nrm * cen[u[0]] : 0.f, y1 = act ? nrm * cen[u[1]] : 0.f;
-    wave_fwht(y0, y1, D, lane);
+    float y[NK];
+#pragma unroll
+    for (int k = 0; k < NK; ++k) y[k] = row_chan(lane, k) < D ? nrm * cen[u[k]] : 0.f;
+    row_fwht<MD>(y, D, lane);
     const float cd = (float)(1.0 / __builtin_sqrt((double)D));
-    x[0] = act ? lv.tables->signs[2 * lane] * (y0 * cd) : 0.f;
-    x[1] = act ? lv.tables->signs[2 * lane + 1] * (y1 * cd) : 0.f;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c = row_chan(lane, k);
+      x[k] = c < D ? lv.tables->signs[c] * (y[k] * cd) : 0.f;
+    }
   } else {
     const uint16_t* m = reinterpret_cast<const uint16_t*>(rec + (is_k ? lv.k_meta : lv.v_meta));
     const int ng = D / 32;
-    for (int e = 0; e < 2; ++e) {
-      const int c = act ? 2 * lane + e : 0;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) {
+      const int c0 = row_chan(lane, k), c = c0 < D ? c0 : 0;
       if (sh.fmt == KVQ_FMT_KIVI) {
         const int mi = v_meta_idx(t, c >> 5, ng);
         const float sc = is_k ? f16_val(m[c]) : f16_val(m[mi]);
         const float z = is_k ? f16_val(m[D + c]) : f16_val(m[G * ng + mi]);
-        const float prod = (float)u[e] * sc;
-        x[e] = prod + z;
+        const float prod = (float)u[k] * sc;
+        x[k] = prod + z;
       } else if (is_k) {
-        x[e] = lv.tables->q2k_lvl[u[e]] * f16_val(m[c]);
+        x[k] = lv.tables->q2k_lvl[u[k]] * f16_val(m[c]);
       } else {
-        x[e] = ((float)u[e] - 8.f) * f16_val(m[v_meta_idx(t, c >> 5, ng)]);
+        x[k] = ((float)u[k] - 8.f) * f16_val(m[v_meta_idx(t, c >> 5, ng)]);
       }
     }
   }
-  if (wr) {
-    out[2 * lane] = f16_bits(x[0]);
-    out[2 * lane + 1] = f16_bits(x[1]);
+#pragma unroll
+  for (int k = 0; k < NK; ++k) {
+    const int c = row_chan(lane, k);
+    if (c < sh.Din) out[c] = f16_bits(x[k]);
   }
 }
 
@@ -98,7 +110,8 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
 
 hipError_t launch_dequant(const DequantArgs& a, hipStream_t st) {
   dim3 grid((a.count + NT / 64 - 1) / (NT / 64), a.sh.B * a.sh.Hkv);
-  hipLaunchKernelGGL(k_dequant, grid, dim3(NT), 0, st, a);
+  if (a.sh.D > MAX_D) hipLaunchKernelGGL(k_dequant<MAX_SD>, grid, dim3(NT), 0, st, a);
+  else hipLaunchKernelGGL(k_dequant<MAX_D>, grid, dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 

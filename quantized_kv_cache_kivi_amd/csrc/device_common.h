@@ -150,4 +150,43 @@ __device__ __forceinline__ float wave_sumsq(float y0, float y1, int D) {
   return wave_sum_xor(p + q, D >> 2);
 }
 
+// A row of up to MD channels (MD = 128 or 256) held by one wave, MD / 64 values per lane: y[2h + e]
+// is channel 128h + 2l + e of lane l (h = 1 only for rows of 256 channels; a row of D <= 128
+// channels uses y[0], y[1] of lanes l < D/2).
+__device__ __forceinline__ int row_chan(int lane, int k) { return 128 * (k >> 1) + 2 * lane + (k & 1); }
+
+// The D-point transform (D a power of two, 2 <= D <= MD) of such a row, stages len = 1, 2, ..., D/2
+// as in wave_fwht.  For 256 channels the stages below 128 pair channels inside one 128-channel half
+// (each half transforms alone) and the last stage pairs channel c with c + 128, in the lane.
+template <int MD>
+__device__ __forceinline__ void row_fwht(float (&y)[MD / 64], int D, int lane) {
+  if constexpr (MD > 128) {
+    if (D > 128) {
+      wave_fwht(y[0], y[1], 128, lane);
+      wave_fwht(y[2], y[3], 128, lane);
+      const float a0 = y[0] + y[2], a1 = y[1] + y[3], b0 = y[0] - y[2], b1 = y[1] - y[3];
+      y[0] = a0;
+      y[1] = a1;
+      y[2] = b0;
+      y[3] = b1;
+      return;
+    }
+  }
+  wave_fwht(y[0], y[1], D, lane);
+}
+
+// Canonical fp32 sum of squares of such a row (the tree of wave_sumsq).  For 256 channels the pair
+// sums a_l (l < 128) sit two per lane, a_l and a_{l+64}, so the first halving is the in-lane add.
+template <int MD>
+__device__ __forceinline__ float row_sumsq(const float (&y)[MD / 64], int D) {
+  if constexpr (MD > 128) {
+    if (D > 128) {
+      const float p0 = y[0] * y[0], q0 = y[1] * y[1], p1 = y[2] * y[2], q1 = y[3] * y[3];
+      const float lo = p0 + q0, hi = p1 + q1;
+      return wave_sum_xor(lo + hi, 32);
+    }
+  }
+  return wave_sumsq(y[0], y[1], D);
+}
+
 }  // namespace kvq

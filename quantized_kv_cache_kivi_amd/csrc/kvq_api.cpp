@@ -43,10 +43,15 @@ void clear_error() { g_err.clear(); }
 }  // namespace kvq
 
 namespace kvq {
-// Width a row is stored and computed at: TurboQuant pads a head_dim that is not a power of two (96)
-// with zeros to the next power of two, so the fast Walsh-Hadamard rotation applies ("TurboQuant KV
-// Cache Compression — Spec", "Hadamard Transform Detail"), and keeps every rotated coordinate.
-int stored_dim(const kvq_config& c) { return c.format == KVQ_FMT_TQ && c.head_dim == 96 ? 128 : c.head_dim; }
+// Width a row is stored and computed at: TurboQuant pads a head_dim that is not a power of two (96,
+// 160) with zeros to the next power of two (128, 256), so the fast Walsh-Hadamard rotation applies
+// ("TurboQuant KV Cache Compression — Spec", "Hadamard Transform Detail"), and keeps every rotated
+// coordinate.
+int stored_dim(const kvq_config& c) {
+  if (c.format == KVQ_FMT_TQ && c.head_dim == 96) return 128;
+  if (c.format == KVQ_FMT_TQ && c.head_dim == 160) return 256;
+  return c.head_dim;
+}
 }  // namespace kvq
 
 namespace {
@@ -90,9 +95,10 @@ kvq_status check(const kvq_config* c) {
     return fail(KVQ_EINVAL, "n_layers, batch, n_kv_heads and n_q_heads must be >= 1");
   if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > MAX_GQA)
     return fail(KVQ_EINVAL, "n_q_heads must be a multiple of n_kv_heads with ratio <= %d", MAX_GQA);
-  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && !(c->head_dim == 96 && c->format == KVQ_FMT_TQ))
-    return fail(KVQ_EINVAL, "head_dim must be 32, 64 or 128, or 96 with TQ (got %d)", c->head_dim);
-  if (c->head_dim == 96 && c->sink_mode == KVQ_SINK_TOPK && c->n_sink > 0)
+  const bool tq_pad = c->format == KVQ_FMT_TQ && (c->head_dim == 96 || c->head_dim == 160);
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && !tq_pad)
+    return fail(KVQ_EINVAL, "head_dim must be 32, 64 or 128, or 96 or 160 with TQ (got %d)", c->head_dim);
+  if (tq_pad && c->sink_mode == KVQ_SINK_TOPK && c->n_sink > 0)
     return fail(KVQ_EINVAL, "top-k sink selection needs head_dim 32, 64 or 128");
   auto okb = [](int b) { return b == 2 || b == 4 || b == 8; };
   switch (c->format) {
@@ -628,8 +634,9 @@ kvq_status kvq_prefill_attn(kvq_cache* c, int32_t layer, const void* q, int32_t 
   if (n < 1 || n > P)
     return fail(KVQ_ERANGE, "prefill attention of n=%d queries needs 1 <= n <= P=%lld (the last n positions)", n,
                 (long long)P);
-  if (stored_dim(cf) != 32 && stored_dim(cf) != 64 && stored_dim(cf) != 128)
-    return fail(KVQ_EINVAL, "prefill attention needs head_dim 32, 64, 96 (TQ) or 128");
+  const int sd = stored_dim(cf);
+  if (sd != 32 && sd != 64 && sd != 128 && !(sd == 256 && cf.format == KVQ_FMT_TQ))
+    return fail(KVQ_EINVAL, "prefill attention needs head_dim 32, 64, 96 (TQ), 128 or 160 (TQ)");
   if ((uintptr_t)q % 16 != 0 || (uintptr_t)out % 16 != 0) return fail(KVQ_EINVAL, "q and out must be 16-byte aligned");
   PrefillArgs a;
   a.sh = shape_of(cf);
@@ -687,7 +694,7 @@ kvq_status kvq_account(kvq_cache* c, int32_t layer, kvq_bytes* out, void* stream
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "account copy");
   const int64_t P = c->P[layer], lo = c->lo[layer], R = cf.residual;
-  const int64_t H = cf.n_kv_heads, D = stored_dim(cf);  // stored rows (TurboQuant pads 96 to 128)
+  const int64_t H = cf.n_kv_heads, D = stored_dim(cf);  // stored rows (TurboQuant pads 96 to 128, 160 to 256)
   const RecordSections rs = record_sections(cf);
   std::memset(out, 0, sizeof(*out));
   const int64_t wlo = std::max(lo, P - R);

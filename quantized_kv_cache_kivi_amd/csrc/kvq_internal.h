@@ -12,13 +12,14 @@ namespace kvq {
 constexpr int G = 32;          // token block length and V channel-group length
 constexpr int MAX_SINK = 16;   // largest n_sink
 constexpr int MAX_GQA = 16;    // largest n_q_heads / n_kv_heads
-constexpr int MAX_D = 128;     // largest head_dim
+constexpr int MAX_D = 128;     // largest head_dim of the block formats (and of RoPE on read)
+constexpr int MAX_SD = 256;    // widest stored row: TurboQuant head_dim 160 padded to 256
 constexpr int SELECT_GMAX = 64;      // most workgroups per batch element of one sink-selection call
 constexpr int SELECT_MIN_ROWS = 64;  // rows a selection workgroup takes at least
 
 // fp32 tables written once into the device buffer (tables region).
 struct Tables {
-  float signs[MAX_D];   // TQ sign diagonal (+-1)
+  float signs[MAX_SD];  // TQ sign diagonal (+-1), one per stored coordinate
   float k_bnd[16];      // TQ K boundaries in t-space (2^k_bits - 1 used)
   float k_cen[16];      // TQ K centroids
   float v_bnd[16];      // TQ V boundaries

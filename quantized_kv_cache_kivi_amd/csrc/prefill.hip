@@ -103,10 +103,14 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
   int qpos[PT];  // position of the lane's column query (-1: no query)
   int qidx[PT], head[PT];
   const float cd = (float)(1.0 / __builtin_sqrt((double)D));
-  float sg0 = 0.f, sg1 = 0.f;  // TurboQuant signs of channels 2*lane, 2*lane + 1
+  // rows held by one wave: lane l holds channels 128h + 2l + e in element 2h + e (row_chan)
+  constexpr int RMD = D > 128 ? 256 : 128, NK = RMD / 64;
+  float sg[NK];  // TurboQuant signs of the lane's channels
+#pragma unroll
+  for (int k = 0; k < NK; ++k) sg[k] = 0.f;
   if constexpr (TQ) {
-    sg0 = 2 * lane < D ? lv.tables->signs[2 * lane] : 0.f;
-    sg1 = 2 * lane < D ? lv.tables->signs[2 * lane + 1] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NK; ++k) sg[k] = row_chan(lane, k) < D ? lv.tables->signs[row_chan(lane, k)] : 0.f;
     if (tid < 16) S.kcen[tid] = lv.tables->k_cen[tid & ((1 << KB) - 1)];
     if (tid >= 16 && tid < 32) S.vcen[tid - 16] = lv.tables->v_cen[(tid - 16) & ((1 << VB) - 1)];
   }
@@ -133,50 +137,54 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
         bq[tt][st] = v;
       }
     } else {
-      // rotate the wave's 16 column queries one by one (lane l holds channels 2l, 2l + 1) into a
-      // wave-private LDS tile, then read each lane's B-operand slice back as fp16 hi + lo
+      // rotate the wave's 16 column queries one by one (lane l holds channels row_chan(l, k)) into
+      // a wave-private LDS tile, then read each lane's B-operand slice back as fp16 hi + lo
       float* qs = reinterpret_cast<float*>(&S.khi[0][0]) + wv * 16 * D;
       for (int col = 0; col < 16; ++col) {
         int cq, ch;
         const bool cok = col_query(tt, col, &cq, &ch);
-        float y0 = 0.f, y1 = 0.f;
+        float y[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) y[k] = 0.f;
         if (!cok) {  // a padding column (uniform over the wave): zeros, nothing to turn
-          if (2 * lane < D) {
-            qs[col * D + 2 * lane] = 0.f;
-            qs[col * D + 2 * lane + 1] = 0.f;
-          }
+#pragma unroll
+          for (int k = 0; k < NK; ++k)
+            if (row_chan(lane, k) < D) qs[col * D + row_chan(lane, k)] = 0.f;
           continue;
         }
-        if (2 * lane < sh.Din) {  // query rows of Din channels (TurboQuant pads the rest with zeros)
-          const int64_t qrow = (((int64_t)b * sh.Hq + ch) * a.n + cq) * sh.Din;
-          if (sh.in_f32) {
-            const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qrow + 2 * lane);
-            y0 = w.x;
-            y1 = w.y;
-          } else {
-            const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + 2 * lane);
-            y0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-            y1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+        const int64_t qrow = (((int64_t)b * sh.Hq + ch) * a.n + cq) * sh.Din;
+#pragma unroll
+        for (int k = 0; k < NK; k += 2) {
+          const int c = row_chan(lane, k);
+          if (c < sh.Din) {  // query rows of Din channels (TurboQuant pads the rest with zeros)
+            if (sh.in_f32) {
+              const float2 w = *reinterpret_cast<const float2*>(static_cast<const float*>(a.q) + qrow + c);
+              y[k] = w.x;
+              y[k + 1] = w.y;
+            } else {
+              const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const _Float16*>(a.q) + qrow + c);
+              y[k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+              y[k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+            }
           }
         }
         if constexpr (TQ) {
-          y0 *= sg0;
-          y1 *= sg1;
-          wave_fwht(y0, y1, D, lane);
-          y0 *= cd;
-          y1 *= cd;
+#pragma unroll
+          for (int k = 0; k < NK; ++k) y[k] *= sg[k];
+          row_fwht<RMD>(y, D, lane);
+#pragma unroll
+          for (int k = 0; k < NK; ++k) y[k] *= cd;
         } else if (sh.rope) {  // RoPE: channel 2l pairs with 2l + D/2, held by lane l ^ (D/4)
-          const float p0 = __shfl_xor(y0, D / 4), p1 = __shfl_xor(y1, D / 4);
+          const float p0 = __shfl_xor(y[0], D / 4), p1 = __shfl_xor(y[1], D / 4);
           const int qi = cache_index(S.spos, S.nsink, a.lo, pbase + cq);
-          const float r0 = rope_val(y0, p0, 2 * lane, D, qi, lv.tables->rope_inv);
-          const float r1 = rope_val(y1, p1, 2 * lane + 1, D, qi, lv.tables->rope_inv);
-          y0 = r0;
-          y1 = r1;
+          const float r0 = rope_val(y[0], p0, 2 * lane, D, qi, lv.tables->rope_inv);
+          const float r1 = rope_val(y[1], p1, 2 * lane + 1, D, qi, lv.tables->rope_inv);
+          y[0] = r0;
+          y[1] = r1;
         }
-        if (2 * lane < D) {
-          qs[col * D + 2 * lane] = y0;
-          qs[col * D + 2 * lane + 1] = y1;
-        }
+#pragma unroll
+        for (int k = 0; k < NK; ++k)
+          if (row_chan(lane, k) < D) qs[col * D + row_chan(lane, k)] = y[k];
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -376,37 +384,44 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
           *vp = lv.sink_v + so * D;
         }
       };
-      if constexpr (TQ) {  // one row per wave pass, rotated: lane l holds channels 2l, 2l + 1
+      if constexpr (TQ) {  // one row per wave pass, rotated: lane l holds channels row_chan(l, k)
         for (int rr = 0; rr < G / PNW; ++rr) {
           const int tr = wv + PNW * rr;
           int64_t p;
           const uint16_t *kr, *vr;
           row_src(tr, &p, &kr, &vr);
-          float k0 = 0.f, k1 = 0.f, v0 = 0.f, v1 = 0.f;
-          if (kr && 2 * lane < D) {
-            const uint32_t kw2 = reinterpret_cast<const uint32_t*>(kr)[lane];
-            const uint32_t vw2 = reinterpret_cast<const uint32_t*>(vr)[lane];
-            k0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(kw2 & 0xFFFFu)) * sg0;
-            k1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(kw2 >> 16)) * sg1;
-            v0 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw2 & 0xFFFFu)) * sg0;
-            v1 = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw2 >> 16)) * sg1;
+          float ky[NK], vy[NK];
+#pragma unroll
+          for (int k = 0; k < NK; ++k) ky[k] = vy[k] = 0.f;
+#pragma unroll
+          for (int k = 0; k < NK; k += 2) {
+            const int c = row_chan(lane, k);
+            if (kr && c < D) {
+              const uint32_t kw2 = *reinterpret_cast<const uint32_t*>(kr + c);
+              const uint32_t vw2 = *reinterpret_cast<const uint32_t*>(vr + c);
+              ky[k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(kw2 & 0xFFFFu)) * sg[k];
+              ky[k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(kw2 >> 16)) * sg[k + 1];
+              vy[k] = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw2 & 0xFFFFu)) * sg[k];
+              vy[k + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(vw2 >> 16)) * sg[k + 1];
+            }
           }
-          wave_fwht(k0, k1, D, lane);
-          wave_fwht(v0, v1, D, lane);
-          k0 *= cd;
-          k1 *= cd;
-          v0 *= cd;
-          v1 *= cd;
-          if (2 * lane < D) {
-            const _Float16 hk0 = (_Float16)k0, hk1 = (_Float16)k1, hv0 = (_Float16)v0, hv1 = (_Float16)v1;
-            *reinterpret_cast<uint32_t*>(&S.khi[tr][2 * lane]) = (uint32_t)h16(k0) | ((uint32_t)h16(k1) << 16);
-            *reinterpret_cast<uint32_t*>(&S.klo[tr][2 * lane]) =
-                (uint32_t)h16(k0 - (float)hk0) | ((uint32_t)h16(k1 - (float)hk1) << 16);
-            const int kq = (tr & 15) >> 2, e = ((tr >> 4) << 2) | (tr & 3);
-            S.vt[2 * lane][8 * kq + e] = hv0;
-            S.vt[2 * lane + 1][8 * kq + e] = hv1;
-            S.vtl[2 * lane][8 * kq + e] = (_Float16)(v0 - (float)hv0);
-            S.vtl[2 * lane + 1][8 * kq + e] = (_Float16)(v1 - (float)hv1);
+          row_fwht<RMD>(ky, D, lane);
+          row_fwht<RMD>(vy, D, lane);
+          const int kq = (tr & 15) >> 2, e = ((tr >> 4) << 2) | (tr & 3);
+#pragma unroll
+          for (int k = 0; k < NK; k += 2) {
+            const int c = row_chan(lane, k);
+            if (c < D) {
+              const float k0 = ky[k] * cd, k1 = ky[k + 1] * cd, v0 = vy[k] * cd, v1 = vy[k + 1] * cd;
+              const _Float16 hk0 = (_Float16)k0, hk1 = (_Float16)k1, hv0 = (_Float16)v0, hv1 = (_Float16)v1;
+              *reinterpret_cast<uint32_t*>(&S.khi[tr][c]) = (uint32_t)h16(k0) | ((uint32_t)h16(k1) << 16);
+              *reinterpret_cast<uint32_t*>(&S.klo[tr][c]) =
+                  (uint32_t)h16(k0 - (float)hk0) | ((uint32_t)h16(k1 - (float)hk1) << 16);
+              S.vt[c][8 * kq + e] = hv0;
+              S.vt[c + 1][8 * kq + e] = hv1;
+              S.vtl[c][8 * kq + e] = (_Float16)(v0 - (float)hv0);
+              S.vtl[c + 1][8 * kq + e] = (_Float16)(v1 - (float)hv1);
+            }
           }
           if (lane == 0) S.pos[tr] = (int)p;
         }
@@ -561,12 +576,15 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
       for (int col = 0; col < 16; ++col) {
         int cq, ch;
         const bool cok = col_query(tt, col, &cq, &ch);
-        float y0 = 2 * lane < D ? os[col * D + 2 * lane] : 0.f;
-        float y1 = 2 * lane < D ? os[col * D + 2 * lane + 1] : 0.f;
-        wave_fwht(y0, y1, D, lane);
-        if (cok && 2 * lane < sh.Din) {
-          float* o = a.out + (((int64_t)b * sh.Hq + ch) * a.n + cq) * sh.Din;
-          *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(sg0 * (y0 * cd), sg1 * (y1 * cd));
+        float y[NK];
+#pragma unroll
+        for (int k = 0; k < NK; ++k) y[k] = row_chan(lane, k) < D ? os[col * D + row_chan(lane, k)] : 0.f;
+        row_fwht<RMD>(y, D, lane);
+        float* o = a.out + (((int64_t)b * sh.Hq + ch) * a.n + cq) * sh.Din;
+#pragma unroll
+        for (int k = 0; k < NK; k += 2) {
+          const int c = row_chan(lane, k);
+          if (cok && c < sh.Din) *reinterpret_cast<float2*>(o + c) = make_float2(sg[k] * (y[k] * cd), sg[k + 1] * (y[k + 1] * cd));
         }
       }
       __builtin_amdgcn_wave_barrier();
@@ -618,6 +636,12 @@ hipError_t launch_drp(const PrefillArgs& a, hipStream_t st) {
     case 32: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 32, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a); break;
     case 64: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 64, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a); break;
     case 128: hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 128, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a); break;
+    case 256:  // TurboQuant rows of head_dim 160, stored at 256
+      if constexpr (FMT == KVQ_FMT_TQ) {
+        hipLaunchKernelGGL((k_prefill_attn<FMT, KB, VB, 256, LQ, PTT, PW>), grid, dim3(64 * PW), 0, st, a);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -154,10 +154,11 @@ void make_tables(const kvq_config& cfg, Tables* t) {
   }
   gaussian_lloyd_max4(t->q2k_thr, t->q2k_lvl);
   const double base = cfg.rope_base > 0.f ? (double)cfg.rope_base : 10000.0;
-  for (int c = 0; c < cfg.head_dim / 2; ++c) t->rope_inv[c] = (float)std::pow(base, -2.0 * c / cfg.head_dim);
+  const int nrope = cfg.head_dim <= MAX_D ? cfg.head_dim / 2 : 0;  // RoPE is for the block formats (<= 128)
+  for (int c = 0; c < nrope; ++c) t->rope_inv[c] = (float)std::pow(base, -2.0 * c / cfg.head_dim);
   if (cfg.rope)
     for (int i = 0; i < 16; ++i)
-      for (int c = 0; c < cfg.head_dim / 2; ++c) {
+      for (int c = 0; c < nrope; ++c) {
         const double ang = (double)i * (double)t->rope_inv[c];
         t->rope_row[i][c][0] = (float)std::cos(ang);
         t->rope_row[i][c][1] = (float)std::sin(ang);

@@ -153,6 +153,8 @@ def get_layout(cfg):
 def format_tables(cfg):
     """Host tables the library computes: dict of fp32 lists."""
     d = cfg.head_dim
+    if cfg.format == FMT["tq"] and d in (96, 160):
+        d = 128 if d == 96 else 256  # one sign per stored coordinate (the padded width)
     kl, vl = 1 << cfg.k_bits, 1 << cfg.v_bits
     bufs = {"signs": (ctypes.c_float * d)(), "k_bnd": (ctypes.c_float * (kl - 1))(), "k_cen": (ctypes.c_float * kl)(),
             "v_bnd": (ctypes.c_float * (vl - 1))(), "v_cen": (ctypes.c_float * vl)(),

@@ -76,6 +76,16 @@ CASES = {
                              seed=21),
     "tq32_dense_d96": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=6, head_dim=96, fmt="tq", k_bits=3,
                            v_bits=2, capacity=512, seed=22, tq_dense3=True),
+    # head_dim 160: rows zero-padded to 256 (lanes hold four channels; the last transform stage pairs
+    # channel c with c + 128 in the lane), Beta(80, 80) codebooks, generic decode
+    "tq42_d160_r4_firstn_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=160, fmt="tq",
+                                    k_bits=4, v_bits=2, sink_mode="first_n", n_sink=3, residual=24,
+                                    capacity=512, seed=25),
+    "tq33_dense_d160_f32_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=160, fmt="tq",
+                                    k_bits=3, v_bits=3, sink_mode="first_n", n_sink=2, window=128, residual=8,
+                                    in_dtype="f32", seed=26, tq_dense3=True),
+    "tq34_d160_r3": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=6, head_dim=160, fmt="tq", k_bits=3,
+                         v_bits=4, capacity=512, seed=27),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]

@@ -2,7 +2,8 @@
 
 Bar: for every (b, query head, query) row, ||o - o_ref||_inf / ||o_ref||_inf <= 1e-3 (the decode
 attention bar); rows whose query has no valid position are zeros on both sides, exactly.  Cases
-cover GQA ratios 1, 2, 3 (padding columns), 4 and 8, head_dim 32, 64 and 128, KIVI widths, q2k and
+cover GQA ratios 1, 2, 3 (padding columns), 4 and 8, head_dim 32, 64 and 128 (and TurboQuant's padded
+96 and 160), KIVI widths, q2k and
 TurboQuant (every K/V width pair: rotated queries, rotated fp16 rows, outputs rotated back), top-k
 and first-n sinks, the fp16 window, an evicting ring (early queries whose own rows are gone),
 several query tiles per stream and a chunk that starts inside an open block.
@@ -63,6 +64,12 @@ CASES = {
                          sink_mode="first_n", n_sink=2, residual=16, capacity=1024, seed=23), [70, 33]),
     "tq44_r2_d96_f32_ring": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=96, fmt="tq", k_bits=4,
                                   v_bits=4, window=64, residual=8, in_dtype="f32", seed=24), [60, 20, 33]),
+    # head_dim 160: queries and outputs of 160 channels, rows padded to 256 (sixteen 16-channel tiles)
+    "tq42_r4_d160": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=160, fmt="tq", k_bits=4,
+                          v_bits=2, sink_mode="first_n", n_sink=2, residual=16, capacity=1024, seed=28), [70, 33]),
+    "tq33_dense_r2_d160_f32_ring": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=160, fmt="tq",
+                                         k_bits=3, v_bits=3, window=64, residual=8, in_dtype="f32", seed=29,
+                                         tq_dense3=True), [60, 20, 33]),
 }
 
 

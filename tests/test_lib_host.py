@@ -39,6 +39,9 @@ def test_config_validation(kvq):
     bad = [
         kvq.make_config(1, 2, 2, 7, 128, capacity=64),                       # GQA ratio
         kvq.make_config(1, 2, 2, 8, 96, capacity=64),                        # head_dim
+        kvq.make_config(1, 2, 2, 8, 160, capacity=64),                       # head_dim 160 needs TQ
+        kvq.make_config(1, 2, 2, 8, 160, "tq", 4, 2, "topk", 3, capacity=64),   # top-k at a padded width
+        kvq.make_config(1, 2, 2, 8, 256, "tq", 4, 2, capacity=64),           # wider than 160
         kvq.make_config(1, 2, 2, 8, 128, "kivi", 3, 2, capacity=64),         # bits
         kvq.make_config(1, 2, 2, 8, 128, "q2k", 2, 2, capacity=64),          # q2k bits
         kvq.make_config(1, 2, 2, 8, 128, "kivi", 2, 2, "none", 4, capacity=64),  # sinks without mode
@@ -48,6 +51,9 @@ def test_config_validation(kvq):
         kvq.make_config(1, 2, 2, 8, 128, "kivi", 2, 2, "topk", 17, capacity=64),
         kvq.make_config(1, 2, 2, 8, 128, "tq", 4, 2, capacity=64, rope=True),   # RoPE on read with TQ
     ]
+    for good in (kvq.make_config(1, 2, 2, 8, 96, "tq", 4, 2, "first_n", 3, capacity=64),
+                 kvq.make_config(1, 2, 2, 8, 160, "tq", 3, 3, "first_n", 3, capacity=64, tq_dense3=True)):
+        assert kvq.config_check(good) == 0
     for cfg in bad:
         assert kvq.config_check(cfg) == -1
         assert kvq.last_error() != ""
@@ -55,10 +61,13 @@ def test_config_validation(kvq):
 
 
 @pytest.mark.parametrize("fmt,kb,vb,D", [("kivi", 2, 2, 128), ("kivi", 4, 8, 64), ("kivi", 8, 8, 32),
-                                         ("q2k", 2, 4, 128), ("tq", 4, 2, 128), ("tq", 2, 4, 32)])
+                                         ("q2k", 2, 4, 128), ("tq", 4, 2, 128), ("tq", 2, 4, 32),
+                                         ("tq", 4, 4, 96), ("tq", 4, 2, 160)])
 def test_layout_matches_documented_format(kvq, fmt, kb, vb, D):
-    cfg = kvq.make_config(3, 2, 4, 8, D, fmt, kb, vb, "topk", 5, 256, 16, 0, "f16", 9)
+    padded = fmt == "tq" and D in (96, 160)
+    cfg = kvq.make_config(3, 2, 4, 8, D, fmt, kb, vb, "first_n" if padded else "topk", 5, 256, 16, 0, "f16", 9)
     lay = kvq.get_layout(cfg)
+    D = {96: 128, 160: 256}[D] if padded else D  # rows are stored at the padded width
     off, size, rec = olayout.record_sections(fmt, D, kb, vb)
     assert lay.record_bytes == rec
     assert (lay.rec_k_codes, lay.rec_v_codes, lay.rec_k_meta, lay.rec_v_meta) == \
@@ -80,10 +89,12 @@ def test_layout_matches_documented_format(kvq, fmt, kb, vb, D):
 
 
 def test_tables_match_oracle(kvq):
-    for d, kb, vb, seed in [(128, 4, 2, 0x5EED0004), (64, 2, 4, 3), (32, 4, 4, 11)]:
+    # (head_dim, stored width): 96 and 160 are padded to 128 and 256, one sign per stored coordinate
+    for d, dp, kb, vb, seed in [(128, 128, 4, 2, 0x5EED0004), (64, 64, 2, 4, 3), (32, 32, 4, 4, 11),
+                                (96, 128, 4, 3, 5), (160, 256, 4, 2, 6), (160, 256, 3, 4, 7)]:
         cfg = kvq.make_config(1, 1, 1, 1, d, "tq", kb, vb, capacity=64, seed=seed)
         t = kvq.format_tables(cfg)
-        assert np.array_equal(np.float32(t["signs"]), otq.signs(seed, d))
+        assert np.array_equal(np.float32(t["signs"]), otq.signs(seed, dp))
         okb, okc = otq.codebook(d, kb)
         ovb, ovc = otq.codebook(d, vb)
         assert np.array_equal(np.float32(t["k_bnd"]).view(np.uint32), okb.view(np.uint32))
