@@ -222,7 +222,7 @@ struct alignas(16) FastWave {
   float kp[RP ? 1 : R][64 + 4];   // zero-point (q2k: c0) term per head and lane (not with RoPE)
   uint32_t km[RP ? 2 : 1][RP ? 64 : 1];  // RoPE: the block's K scales and zeros, channel pairs
   uint32_t ab[4][NC][4 * 4 + 4];  // weights x V scale: [group][column][4 * token group + pair]
-  float f[R], zt[R][4], m[R], l[R];
+  float zt[R][4], m[R], l[R];
 };
 template <int R, bool RP>
 struct FastSmem {
@@ -601,11 +601,11 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
   }
   // a new running maximum somewhere in the wave: reduce the row maxima and rescale
   const bool resc = __any(grow);
+  float fc = 1.f;  // rescale factor of the head of this lane's MFMA column (i16 % R)
   if (resc) {
+    float fp[NPL];
 #pragma unroll
     for (int p = 0; p < NPL; ++p) {
-      const int jr = kg + 4 * p;
-      const int j = jr < R ? jr : R - 1;
       const float mold = S.m_[p];
       const float mnew = fmaxf(mold, row_max16(fmaxf(y0[p], y1[p])));
       const float f = mold == mnew ? 1.f : (mold == -INFINITY ? 0.f : ex2(mold - mnew));
@@ -614,7 +614,15 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
       S.l_[p] *= f;
 #pragma unroll
       for (int q = 0; q < 4; ++q) S.zacc[p][q] *= f;
-      if (tp == 0) W.f[j] = f;
+      fp[p] = f;
+    }
+    // head h sits in row h % 4 of slot h / 4 (every lane of a row holds its factor): a lane
+    // exchange instead of an LDS round trip
+    const int hc = i16 % R, src = 16 * (hc & 3);
+    fc = __shfl(fp[0], src);
+    if constexpr (NPL > 1) {
+      const float f1 = __shfl(fp[1], src);
+      fc = hc < 4 ? fc : f1;
     }
   }
 #pragma unroll
@@ -660,7 +668,6 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
   }
   // ---- values (rare: rescale the running sums to a new maximum first) ----
   if (resc) {
-    const float fc = W.f[i16 % R];
 #pragma unroll
     for (int mu = 0; mu < 8; ++mu) S.acc[mu] *= fc;
   }
