@@ -42,6 +42,19 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
 }
 __device__ __forceinline__ uint16_t h16(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+typedef _Float16 hv2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ hv2 HV(uint32_t w) { return __builtin_bit_cast(hv2, w); }
+
+// fp16 hi and lo halves of two fp32 values, packed: hi = x rounded toward zero (one packed
+// conversion), lo = rn(x - hi) (x - hi is exact in fp32; one mixed-precision fma per value, written
+// into its half).  hi + lo holds x to ~2^-21.  nm1 is -1 held in a register (an fma by a literal -1
+// would be rewritten as a subtraction, which the mixed-precision fma does not cover).
+__device__ __forceinline__ void split_pair(float a, float b, float nm1, uint32_t& hi, uint32_t& lo) {
+  const hv2 h = __builtin_bit_cast(hv2, __builtin_amdgcn_cvt_pkrtz(a, b));
+  hi = __builtin_bit_cast(uint32_t, h);
+  const hv2 l = hv2{(_Float16)__builtin_fmaf((float)h.x, nm1, a), (_Float16)__builtin_fmaf((float)h.y, nm1, b)};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
 
 template <int D>
 struct PfSmem {
@@ -219,6 +232,8 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
     for (int mu = 0; mu < NMU; ++mu) acc[tt][mu] = f4{0.f, 0.f, 0.f, 0.f};
   }
   const float al = a.scale * PLOG2E;
+  float nm1 = -1.f;
+  asm("" : "+v"(nm1));  // -1 opaque to the optimizer (no instruction): see split_pair
   const float lv0 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[0] : 0.f;
   const float lv1 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[1] : 0.f;
   const float lv2 = FMT == KVQ_FMT_Q2K ? lv.tables->q2k_lvl[2] : 0.f;
@@ -268,29 +283,46 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
             zc[i] = FMT == KVQ_FMT_KIVI ? km[D / 2 + c0 / 2 + i] : 0u;
           }
         }
+        uint32_t hk[CPT / 2], lk[CPT / 2];  // the thread's channels as fp16 hi / lo pairs
 #pragma unroll
         for (int i = 0; i < CPT / 2; ++i) {
           float x[2];
+          if constexpr (KB == 3) {  // dense 3-bit stream (TurboQuant): one code at a time
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int c = c0 + 2 * i + h, k = c % per;
-            const uint32_t u = KB == 3 ? code3_at(rec + lv.k_codes, k_bit3(t, c, D))
-                                       : (kw[c / per] >> (16 * (k & 1) + KB * (k >> 1))) & ((1u << KB) - 1u);
+            for (int h = 0; h < 2; ++h) x[h] = nk * S.kcen[code3_at(rec + lv.k_codes, k_bit3(t, c0 + 2 * i + h, D))];
+          } else {
+            // channels c, c + 1 (k even): codes k and k + 1 of their word sit at the same bit offset
+            // of its two 16-bit halves, so one shift and one mask put both in the halves' low bytes
+            const int c = c0 + 2 * i, k = c % per;
+            const uint32_t uu = (kw[c / per] >> (KB * (k >> 1))) & (((1u << KB) - 1u) * 0x10001u);
+            const float u0 = (float)(uu & 0xFFu), u1 = (float)(uu >> 16);
             if constexpr (TQ) {
-              x[h] = nk * S.kcen[u];
-            } else if constexpr (FMT == KVQ_FMT_KIVI) {
-              const float sf = f16_val((uint16_t)(sc[i] >> (16 * h)));
-              x[h] = (float)u * sf + f16_val((uint16_t)(zc[i] >> (16 * h)));
+              x[0] = nk * S.kcen[uu & 0xFFFFu];
+              x[1] = nk * S.kcen[uu >> 16];
+            } else if constexpr (FMT == KVQ_FMT_KIVI) {  // u s + z, one rounding
+              const hv2 s2 = HV(sc[i]), z2 = HV(zc[i]);
+              x[0] = __builtin_fmaf(u0, (float)s2.x, (float)z2.x);
+              x[1] = __builtin_fmaf(u1, (float)s2.y, (float)z2.y);
             } else {
-              const float sf = f16_val((uint16_t)(sc[i] >> (16 * h)));
-              const float lvl = u == 0 ? lv0 : (u == 1 ? lv1 : (u == 2 ? lv2 : lv3));
-              x[h] = lvl * sf;
+              const hv2 s2 = HV(sc[i]);
+              const uint32_t ua = uu & 0xFFFFu, ub = uu >> 16;
+              const float la = ua == 0 ? lv0 : (ua == 1 ? lv1 : (ua == 2 ? lv2 : lv3));
+              const float lb = ub == 0 ? lv0 : (ub == 1 ? lv1 : (ub == 2 ? lv2 : lv3));
+              x[0] = la * (float)s2.x;
+              x[1] = lb * (float)s2.y;
             }
           }
-          const _Float16 h0 = (_Float16)x[0], h1 = (_Float16)x[1];
-          *reinterpret_cast<uint32_t*>(&S.khi[t][c0 + 2 * i]) = (uint32_t)h16(x[0]) | ((uint32_t)h16(x[1]) << 16);
-          *reinterpret_cast<uint32_t*>(&S.klo[t][c0 + 2 * i]) =
-              (uint32_t)h16(x[0] - (float)h0) | ((uint32_t)h16(x[1] - (float)h1) << 16);
+          split_pair(x[0], x[1], nm1, hk[i], lk[i]);
+        }
+        if constexpr (CPT >= 8) {  // 16-byte LDS stores of the thread's run of channels
+#pragma unroll
+          for (int m = 0; m < CPT / 8; ++m) {
+            *reinterpret_cast<u4*>(&S.khi[t][c0 + 8 * m]) = u4{hk[4 * m], hk[4 * m + 1], hk[4 * m + 2], hk[4 * m + 3]};
+            *reinterpret_cast<u4*>(&S.klo[t][c0 + 8 * m]) = u4{lk[4 * m], lk[4 * m + 1], lk[4 * m + 2], lk[4 * m + 3]};
+          }
+        } else {
+          *reinterpret_cast<uint2*>(&S.khi[t][c0]) = make_uint2(hk[0], hk[1]);
+          *reinterpret_cast<uint2*>(&S.klo[t][c0]) = make_uint2(lk[0], lk[1]);
         }
         if (tid < G) {
           const int64_t p = beta * G + tid;
@@ -317,38 +349,31 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
 #pragma unroll
           for (int k0 = 0; k0 < VPW; k0 += EPW) {
             const int sq0 = wi * VPW + k0, mu = sq0 >> 3, e0 = sq0 & 7, c = 16 * mu + i, gq = c >> 5;
-            // metadata of the word's rows: token pairs (t, t+1) share a dword in each section
-            float hv[EPW], lvv[EPW];
+            // metadata of the word's rows: token pairs (t, t+1) share a dword in each section, and
+            // codes k, k + 1 (k even) of the word sit at the same bit offset of its two halves
+            uint32_t ph[EPW / 2], pl[EPW / 2];
 #pragma unroll
             for (int ee = 0; ee < EPW; ee += 2) {
               const int e = e0 + ee, tk = v_tok(kq, e);  // tk even, tk + 1 = v_tok(kq, e + 1)
               const int mi = v_meta_idx(tk, gq, NG) >> 1;
               const uint32_t sw = TQ ? 0u : vm[mi];
               const uint32_t zw = FMT == KVQ_FMT_KIVI ? vm[G * NG / 2 + mi] : 0u;
-              float nv[2] = {0.f, 0.f};  // TurboQuant: V norms of rows tk, tk + 1
-              if constexpr (TQ) {
-                nv[0] = reinterpret_cast<const float*>(rec + lv.v_meta)[tk];
-                nv[1] = reinterpret_cast<const float*>(rec + lv.v_meta)[tk + 1];
+              const int k = k0 + ee;
+              const uint32_t uu = (w >> (VB * (k >> 1))) & (((1u << VB) - 1u) * 0x10001u);
+              const float u0 = (float)(uu & 0xFFu), u1 = (float)(uu >> 16);
+              const hv2 s2 = HV(sw), z2 = HV(zw);
+              float x0, x1;
+              if constexpr (TQ) {  // V norms of rows tk, tk + 1 times their centroids
+                x0 = reinterpret_cast<const float*>(rec + lv.v_meta)[tk] * S.vcen[uu & 0xFFFFu];
+                x1 = reinterpret_cast<const float*>(rec + lv.v_meta)[tk + 1] * S.vcen[uu >> 16];
+              } else if constexpr (FMT == KVQ_FMT_KIVI) {  // u s + z, one rounding
+                x0 = __builtin_fmaf(u0, (float)s2.x, (float)z2.x);
+                x1 = __builtin_fmaf(u1, (float)s2.y, (float)z2.y);
+              } else {
+                x0 = (u0 - 8.f) * (float)s2.x;
+                x1 = (u1 - 8.f) * (float)s2.y;
               }
-#pragma unroll
-              for (int h = 0; h < 2; ++h) {
-                const int k = k0 + ee + h;
-                const uint32_t u = (w >> (16 * (k & 1) + VB * (k >> 1))) & ((1u << VB) - 1u);
-                const float sf = f16_val((uint16_t)(sw >> (16 * h)));
-                float x;
-                if constexpr (TQ) x = nv[h] * S.vcen[u];
-                else if constexpr (FMT == KVQ_FMT_KIVI) x = (float)u * sf + f16_val((uint16_t)(zw >> (16 * h)));
-                else x = ((float)u - 8.f) * sf;
-                const _Float16 hx = (_Float16)x;
-                hv[ee + h] = (float)hx;
-                lvv[ee + h] = x - (float)hx;
-              }
-            }
-            uint32_t ph[EPW / 2], pl[EPW / 2];
-#pragma unroll
-            for (int m = 0; m < EPW / 2; ++m) {
-              ph[m] = (uint32_t)h16(hv[2 * m]) | ((uint32_t)h16(hv[2 * m + 1]) << 16);
-              pl[m] = (uint32_t)h16(lvv[2 * m]) | ((uint32_t)h16(lvv[2 * m + 1]) << 16);
+              split_pair(x0, x1, nm1, ph[ee / 2], pl[ee / 2]);
             }
             if constexpr (EPW == 8) {
               *reinterpret_cast<u4*>(&S.vt[c][8 * kq]) = u4{ph[0], ph[1], ph[2], ph[3]};
@@ -518,17 +543,18 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
         for (int mu = 0; mu < NMU; ++mu) acc[tt][mu] *= f;
         m_[tt] = mnew;
       }
-      // weights as fp16 hi + lo halves (the pair is exact to ~2^-22 of the weight)
-      float ph[8], pl[8];
+      // weights as fp16 hi + lo halves (the pair holds the weight to ~2^-21)
+      float pw[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const float pw = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(y[k] - mnew);
-        l_[tt] += pw;
-        ph[k] = (float)(_Float16)pw;
-        pl[k] = pw - ph[k];
+        pw[k] = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(y[k] - mnew);
+        l_[tt] += pw[k];
       }
-      bph[tt] = u4{pk2(ph[0], ph[1]), pk2(ph[2], ph[3]), pk2(ph[4], ph[5]), pk2(ph[6], ph[7])};
-      bpl[tt] = u4{pk2(pl[0], pl[1]), pk2(pl[2], pl[3]), pk2(pl[4], pl[5]), pk2(pl[6], pl[7])};
+      uint32_t wh[4], wl[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) split_pair(pw[2 * m], pw[2 * m + 1], nm1, wh[m], wl[m]);
+      bph[tt] = u4{wh[0], wh[1], wh[2], wh[3]};
+      bpl[tt] = u4{wl[0], wl[1], wl[2], wl[3]};
     }
 #pragma unroll
     for (int mu = 0; mu < NMU; ++mu) {  // V_hi p_hi + V_hi p_lo + V_lo p_hi
