@@ -5,8 +5,9 @@
 // Lloyd-Max K levels times the block RMS, symmetric 4-bit V); the attention itself is the plain
 // softmax attention of decode, with a causal limit per query.
 //
-// One workgroup per (stream, tile of queries); its four waves each own two tiles of 16 MFMA columns
-// (16 / r queries times the r query heads of the KV head).  Key/value rows are taken 32 at a time
+// One workgroup per (stream, tile of queries); its waves each own one or two tiles of 16 MFMA columns
+// (16 / r queries times the r query heads of the KV head): 4 waves of 2 tiles (KIVI), 8 waves of 1
+// (q2k), 4 waves of 1 (TurboQuant; RoPE and fp32 queries on short chunks).  Key/value rows are taken 32 at a time
 // ("row blocks": a bulk block, or up to 32 fp16 window rows, or the sinks): the workgroup
 // dequantizes a row block once into LDS (K and V as fp16 hi + lo halves whose sum is the fp32
 // value, V transposed into the matrix-core token order), then every wave runs
@@ -23,11 +24,15 @@ namespace kvq {
 constexpr int PT = 2;     // 16-column tiles per wave (block formats)
 namespace {
 
-// Waves per workgroup (a template parameter of the kernel): 4.  With 8 (one staged row block feeding
-// 8 waves, half the staging work per column) the config-2 prefill took 5.6 ms instead of 4.9: one
-// 8-wave workgroup per CU leaves no second workgroup to compute while one stages.  Queries staged
-// through LDS (TurboQuant, RoPE, fp32) need 4: their staging tile holds 16 columns per wave.
-constexpr int PNW_DIRECT = 4, PNW_LDS = 4;
+// Waves per workgroup (a template parameter of the kernel) and 16-column tiles per wave.  KIVI: 4
+// waves of 2 tiles.  With 8 waves of 2 tiles (one staged row block feeding 8 waves) the config-2
+// prefill took 5.6 ms instead of 4.9: one 8-wave workgroup per CU (222 VGPRs) leaves no second
+// workgroup to compute while one stages; 4 waves of 1 tile (117 VGPRs, 4 waves per SIMD) took 4.5
+// ms instead of 4.3.  q2k, whose staging costs more (the level lookups): 8 waves of 1 tile (121
+// VGPRs, two workgroups per CU) took its 4096 queries at P = 32768 in 101 ms instead of 117 (4 waves
+// of 2 tiles) or 150 (4 waves of 1).  Queries staged through LDS (TurboQuant, RoPE, fp32) need 4
+// waves: their staging tile holds 16 columns per wave.
+constexpr int PNW_DIRECT = 4, PNW_LDS = 4, PNW_Q2K = 8;
 constexpr float PLOG2E = 1.4426950408889634f;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -63,6 +68,7 @@ struct PfSmem {
   alignas(16) _Float16 vt[D][G + 8];   // V transposed: [channel][slot], slot 8*kq + e <-> row v_tok(kq, e)
   alignas(16) _Float16 vtl[D][G + 8];  // its fp16 lo halves
   int pos[G];                          // position of each row (-1: not attended)
+  uint32_t meta[2][256];               // K and V metadata of bulk row blocks (<= 1 KB), by parity
   int spos[MAX_SINK], sslot[MAX_SINK];
   int nsink;
   float kcen[16], vcen[16];  // TurboQuant centroids (rotated domain)
@@ -258,29 +264,69 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
 #pragma unroll
   for (int tt = 0; tt < PT; ++tt) anyq = anyq || qpos[tt] >= 0;
   const bool live = __any(anyq);
+
+  // Block formats load a bulk row block one row block ahead, so the loads of the next one are in
+  // flight during this one's matrix work (TurboQuant loads it when it stages it: the registers held
+  // across the matrix work would cost its kernel a wave per SIMD).  Loaded: the code words of this
+  // thread's K channels and V chunk words into registers, and one dword per thread of the record's
+  // metadata (the K and V sections are contiguous), which is staged through LDS.  The barriers of the
+  // loop order LDS only, so loads in flight stay in flight across them.
+  constexpr bool PF = !TQ;
+  constexpr int CPT = D / SL;  // channels per staging thread
+  constexpr int KPER = KB == 3 ? 1 : 32 / KB;  // K codes per word (3-bit codes: the dense stream)
+  constexpr int KWN = KB == 3 ? 1 : (CPT >= KPER ? CPT / KPER : 1);  // K code words per thread
+  constexpr int NWI = (WPC + PNW - 1) / PNW;                          // V code words per thread
+  constexpr int KMW = FMT == KVQ_FMT_KIVI ? D : (FMT == KVQ_FMT_Q2K ? D / 2 : G);  // K metadata dwords
+  const int t = tid / SL, c0 = (tid % SL) * CPT;
+  const int nmeta = (int)((lv.rec - lv.k_meta) / 4);  // <= 256 for every format
+  auto rec_of = [&](int rbx) {
+    int slot = slot0 + rbx;
+    if (slot >= lv.cap_b) slot -= lv.cap_b;
+    return sbase + (int64_t)slot * lv.rec;
+  };
+  uint32_t pkc[KWN], pvc[NWI], pmeta = 0u;
+  auto fetch = [&](int rbx) {
+    const uint8_t* r = rec_of(rbx);
+    if constexpr (KB != 3) {
+      const uint32_t* kw = reinterpret_cast<const uint32_t*>(r + lv.k_codes) + t * (D * KB / 32) + c0 / KPER;
+#pragma unroll
+      for (int j = 0; j < KWN; ++j) pkc[j] = kw[j];
+    }
+    if constexpr (VB != 3 && PF) {  // (without the look-ahead the V words are read where used)
+      const uint32_t* vw = reinterpret_cast<const uint32_t*>(r + lv.v_codes);
+#pragma unroll
+      for (int n = 0; n < NWI; ++n) {
+        const int wi = wv + n * PNW;
+        pvc[n] = wi < WPC ? vw[lane * WPC + wi] : 0u;
+      }
+    }
+    if (PF && tid < nmeta) pmeta = reinterpret_cast<const uint32_t*>(r + lv.k_meta)[tid];
+  };
+  if (PF && rb_lo < nbulk) fetch(rb_lo);
+
   for (int rb = rb_lo; rb < rb_hi; ++rb) {
-    __syncthreads();  // the previous row block is consumed
+    // the metadata loaded ahead goes to the buffer of this row block's parity (last read while row
+    // block rb - 2 was staged, before the barrier that ended its staging)
+    if (PF && rb < nbulk && tid < nmeta) S.meta[rb & 1][tid] = pmeta;
+    lds_barrier();  // the previous row block is consumed; this one's metadata is visible
     // ---- stage the row block: thread (row t, channel slice) for K; chunk-wise for V ----
-    constexpr int CPT = D / SL;  // channels per staging thread
-    const int t = tid / SL, c0 = (tid % SL) * CPT;
     if (rb < nbulk) {
       const int64_t beta = blk0 + rb;
-      int slot = slot0 + rb;
-      if (slot >= lv.cap_b) slot -= lv.cap_b;
-      const uint8_t* rec = sbase + (int64_t)slot * lv.rec;
+      const uint8_t* rec = rec_of(rb);
+      // metadata dword i of the record: from LDS (loaded ahead), or read in place
+      const uint32_t* md = PF ? S.meta[rb & 1] : reinterpret_cast<const uint32_t*>(rec + lv.k_meta);
+      if constexpr (!PF) fetch(rb);  // the code words (TurboQuant's metadata is read in place)
       {  // K: codes of row t, channels c0 .. c0 + CPT - 1, with their metadata
-        constexpr int per = KB == 3 ? 1 : 32 / KB;  // (3-bit codes: the dense stream, read per code)
-        const uint32_t* kw = reinterpret_cast<const uint32_t*>(rec + lv.k_codes) + t * (D * KB / 32);
-        const uint32_t* km = reinterpret_cast<const uint32_t*>(rec + lv.k_meta);
+        constexpr int per = KPER;
         uint32_t sc[CPT / 2], zc[CPT / 2];
         float nk = 0.f;  // TurboQuant: the row's K norm
         if constexpr (TQ) {
-          nk = reinterpret_cast<const float*>(rec + lv.k_meta)[t];
+          nk = __builtin_bit_cast(float, md[t]);
         } else {
 #pragma unroll
           for (int i = 0; i < CPT / 2; ++i) {
-            sc[i] = km[c0 / 2 + i];
-            zc[i] = FMT == KVQ_FMT_KIVI ? km[D / 2 + c0 / 2 + i] : 0u;
+            sc[i] = md[c0 / 2 + i];
+            zc[i] = FMT == KVQ_FMT_KIVI ? md[D / 2 + c0 / 2 + i] : 0u;
           }
         }
         uint32_t hk[CPT / 2], lk[CPT / 2];  // the thread's channels as fp16 hi / lo pairs
@@ -294,7 +340,7 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
             // channels c, c + 1 (k even): codes k and k + 1 of their word sit at the same bit offset
             // of its two 16-bit halves, so one shift and one mask put both in the halves' low bytes
             const int c = c0 + 2 * i, k = c % per;
-            const uint32_t uu = (kw[c / per] >> (KB * (k >> 1))) & (((1u << KB) - 1u) * 0x10001u);
+            const uint32_t uu = (pkc[c / per - c0 / per] >> (KB * (k >> 1))) & (((1u << KB) - 1u) * 0x10001u);
             const float u0 = (float)(uu & 0xFFu), u1 = (float)(uu >> 16);
             if constexpr (TQ) {
               x[0] = nk * S.kcen[uu & 0xFFFFu];
@@ -320,9 +366,12 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
             *reinterpret_cast<u4*>(&S.khi[t][c0 + 8 * m]) = u4{hk[4 * m], hk[4 * m + 1], hk[4 * m + 2], hk[4 * m + 3]};
             *reinterpret_cast<u4*>(&S.klo[t][c0 + 8 * m]) = u4{lk[4 * m], lk[4 * m + 1], lk[4 * m + 2], lk[4 * m + 3]};
           }
-        } else {
+        } else if constexpr (CPT == 4) {
           *reinterpret_cast<uint2*>(&S.khi[t][c0]) = make_uint2(hk[0], hk[1]);
           *reinterpret_cast<uint2*>(&S.klo[t][c0]) = make_uint2(lk[0], lk[1]);
+        } else {  // one channel pair per thread (head_dim 32 with 8 waves)
+          *reinterpret_cast<uint32_t*>(&S.khi[t][c0]) = hk[0];
+          *reinterpret_cast<uint32_t*>(&S.klo[t][c0]) = lk[0];
         }
         if (tid < G) {
           const int64_t p = beta * G + tid;
@@ -330,7 +379,7 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
         }
       }
       if constexpr (VB == 3) {  // V from the dense 3-bit stream, one element per thread and pass
-        const float* vn = reinterpret_cast<const float*>(rec + lv.v_meta);
+        const float* vn = reinterpret_cast<const float*>(md + KMW);  // the V norms
         for (int idx = tid; idx < G * D; idx += PNT) {
           const int tv = idx % G, c = idx / G;
           const float x = vn[tv] * S.vcen[code3_at(rec + lv.v_codes, v_bit3(tv, c, D))];
@@ -340,12 +389,14 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
           S.vtl[c][8 * kq + e] = (_Float16)(x - (float)hx);
         }
       } else {  // V: chunk q = 16*kq + i holds, for channel tile mu, rows v_tok(kq, e) of channel 16*mu + i
-        const uint32_t* vw = reinterpret_cast<const uint32_t*>(rec + lv.v_codes);
-        const uint32_t* vm = reinterpret_cast<const uint32_t*>(rec + lv.v_meta);
+        const uint32_t* vm = md + KMW;
         const int q = tid & 63, kq = q >> 4, i = q & 15;
         constexpr int EPW = VPW < 8 ? VPW : 8;  // row slots of one channel a word covers
-        for (int wi = tid >> 6; wi < WPC; wi += PNW) {
-          const uint32_t w = vw[q * WPC + wi];
+#pragma unroll
+        for (int n = 0; n < NWI; ++n) {
+          const int wi = wv + n * PNW;
+          if (wi >= WPC) break;  // uniform over the wave
+          const uint32_t w = PF ? pvc[n] : reinterpret_cast<const uint32_t*>(rec + lv.v_codes)[lane * WPC + wi];
 #pragma unroll
           for (int k0 = 0; k0 < VPW; k0 += EPW) {
             const int sq0 = wi * VPW + k0, mu = sq0 >> 3, e0 = sq0 & 7, c = 16 * mu + i, gq = c >> 5;
@@ -364,8 +415,8 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
               const hv2 s2 = HV(sw), z2 = HV(zw);
               float x0, x1;
               if constexpr (TQ) {  // V norms of rows tk, tk + 1 times their centroids
-                x0 = reinterpret_cast<const float*>(rec + lv.v_meta)[tk] * S.vcen[uu & 0xFFFFu];
-                x1 = reinterpret_cast<const float*>(rec + lv.v_meta)[tk + 1] * S.vcen[uu >> 16];
+                x0 = __builtin_bit_cast(float, vm[tk]) * S.vcen[uu & 0xFFFFu];
+                x1 = __builtin_bit_cast(float, vm[tk + 1]) * S.vcen[uu >> 16];
               } else if constexpr (FMT == KVQ_FMT_KIVI) {  // u s + z, one rounding
                 x0 = __builtin_fmaf(u0, (float)s2.x, (float)z2.x);
                 x1 = __builtin_fmaf(u1, (float)s2.y, (float)z2.y);
@@ -473,7 +524,9 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
         if (tid % SL == 0) S.pos[t] = (int)p;
       }
     }
-    __syncthreads();
+    // the next bulk row block's loads, in flight during this row block's matrix work
+    if (PF && rb + 1 < rb_hi && rb + 1 < nbulk) fetch(rb + 1);
+    lds_barrier();
     if (LQ && sh.rope) {  // the staged keys turn by their rows' indices in the compressed cache
       constexpr int H = D / 2;
       for (int idx = tid; idx < G * H; idx += PNT) {
@@ -492,7 +545,7 @@ __global__ __launch_bounds__(64 * PW) void k_prefill_attn(PrefillArgs a) {
         S.khi[t][c + H] = h1;
         S.klo[t][c + H] = (_Float16)(y1 - (float)h1);
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     // ---- the wave's tiles against the row block: every LDS operand read feeds all tiles ----
@@ -653,9 +706,14 @@ int tiles_per_wave(const PrefillArgs& a) {
   return PT;
 }
 
+template <int FMT, bool LQ>
+constexpr int waves_per_wg() {
+  return (FMT == KVQ_FMT_TQ || LQ) ? PNW_LDS : (FMT == KVQ_FMT_Q2K ? PNW_Q2K : PNW_DIRECT);
+}
+
 template <int FMT, int KB, int VB, bool LQ, int PTT>
 hipError_t launch_drp(const PrefillArgs& a, hipStream_t st) {
-  constexpr int PW = (FMT == KVQ_FMT_TQ || LQ) ? PNW_LDS : PNW_DIRECT;
+  constexpr int PW = waves_per_wg<FMT, LQ>();
   const int QT = PW * PTT * (16 / (a.sh.Hq / a.sh.Hkv));
   const dim3 grid((a.n + QT - 1) / QT, a.sh.B * a.sh.Hkv, a.splits > 1 ? a.splits : 1);
   switch (a.sh.D) {
@@ -678,6 +736,7 @@ hipError_t launch_dr(const PrefillArgs& a, hipStream_t st) {
   hipError_t e;
   if constexpr (FMT == KVQ_FMT_TQ) e = launch_drp<FMT, KB, VB, LQ, 1>(a, st);
   else if constexpr (LQ) e = tiles_per_wave(a) == 1 ? launch_drp<FMT, KB, VB, LQ, 1>(a, st) : launch_drp<FMT, KB, VB, LQ, PT>(a, st);
+  else if constexpr (FMT == KVQ_FMT_Q2K) e = launch_drp<FMT, KB, VB, LQ, 1>(a, st);
   else e = launch_drp<FMT, KB, VB, LQ, PT>(a, st);
   if (e != hipSuccess || a.splits <= 1) return e;
   const dim3 mg((unsigned)((int64_t)a.sh.B * a.sh.Hq * a.n));
@@ -708,7 +767,9 @@ hipError_t launch_kivi(const PrefillArgs& a, hipStream_t st) {
 }  // namespace
 
 int prefill_queries_per_tile(int r, int fmt, int rope) {  // (long chunks, fp16 queries)
-  return fmt == KVQ_FMT_TQ ? PNW_LDS * (16 / r) : (rope ? PNW_LDS : PNW_DIRECT) * PT * (16 / r);
+  if (fmt == KVQ_FMT_TQ) return PNW_LDS * (16 / r);
+  if (rope) return PNW_LDS * PT * (16 / r);
+  return fmt == KVQ_FMT_Q2K ? PNW_Q2K * (16 / r) : PNW_DIRECT * PT * (16 / r);
 }
 
 int prefill_row_blocks(const PrefillArgs& a) {

@@ -23,6 +23,11 @@ CASES = {
                                  v_bits=2, sink_mode="topk", n_sink=3, residual=16, capacity=1024), [70, 100, 1, 33]),
     "q2k_r8_firstn_res40": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="q2k", k_bits=2,
                                  v_bits=4, sink_mode="first_n", n_sink=4, residual=40, capacity=1024), [200, 64, 7]),
+    # q2k runs 8 waves of one column tile: at head_dim 32 a staging thread holds one channel pair
+    "q2k_r2_d32_ring": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=32, fmt="q2k", k_bits=2,
+                             v_bits=4, sink_mode="first_n", n_sink=2, window=64, residual=8), [60, 20, 33]),
+    "q2k_r3_d64_topk": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=6, head_dim=64, fmt="q2k", k_bits=2,
+                             v_bits=4, sink_mode="topk", n_sink=3, residual=16, capacity=1024), [90, 33]),
     "kivi4_r2_d64_ring": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="kivi", k_bits=4,
                                v_bits=4, sink_mode="first_n", n_sink=2, window=32, residual=8), [60, 20, 33]),
     "kivi2_r4_ring_nosink": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="kivi", k_bits=2,
