@@ -265,8 +265,13 @@ kvq_status kvqw_decode_attn(kvqw_cache* c, int32_t layer, const void* q, float* 
   a.part = (float*)ws;
   a.scale = scale > 0.f ? scale : 1.0f / std::sqrt((float)cf.head_dim);
   const int nst = a.rows.nsk + a.rows.nring;
-  const int splits = std::min(MAX_SPLITS, (nst + MIN_SPLIT_ROWS - 1) / MIN_SPLIT_ROWS);
+  // the matrix-core kernel (head_dim 128) takes 32-row blocks, four per wave at least (512 rows per
+  // split: 26 us for the call on the batch-8, T = 4096 layer, against 31 us at 256 and 32 us at 1024;
+  // loading each wave's next block ahead gained nothing); only the last split ends early
+  const int min_rows = cf.head_dim == 128 ? 2 * MIN_SPLIT_ROWS : MIN_SPLIT_ROWS;
+  const int splits = std::min(MAX_SPLITS, (nst + min_rows - 1) / min_rows);
   a.rows_per_split = (nst + splits - 1) / splits;
+  if (cf.head_dim == 128) a.rows_per_split = (a.rows_per_split + 31) / 32 * 32;
   a.splits = (nst + a.rows_per_split - 1) / a.rows_per_split;
   hipError_t e = launch_decode(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "decode launch");

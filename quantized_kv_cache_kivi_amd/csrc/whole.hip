@@ -448,6 +448,347 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
   }
 }
 
+// ---- Decode attention on the matrix cores (head_dim 128) ----
+//
+// Same split partials as k_decode, computed with v_mfma_f32_16x16x32_f16 per 32-row block of a wave:
+//  * scores S[t][j] = sum_c u[t][c] q'[j][c] (+ kappa_j), u = q - qMin the unsigned code: A = the
+//    block's K rows, two codes per register as fp16 subnormals (the byte of a 16-bit half is worth
+//    u * 2^-24; bytes 0, 2 of a word with one mask, bytes 1, 3 after a shift), B = the folded query
+//    q' = q s_K times a power of two qs (its largest magnitude near 2^14), split into fp16 hi
+//    (column j) and lo (column R + j, times 2^11) halves with the same channel order;
+//  * out[j][c] = sum_t (p_tj s_t) u[t][c] + sum_t p_tj z_t: A = the weights times the V scale times
+//    a power of two ps (hi rows j, lo rows R + j), B = the V codes, 8 tokens of one channel per
+//    lane, gathered from the rows' words with one byte permute per register; MFMA (g, b) covers the
+//    channels 8n + 4g + b (n the column).  The zero term is a dot product per lane.
+// ps starts at 2^12 and is lowered (the accumulators scaled exactly) when a block's largest V scale
+// would take a weight operand past 2^14.
+constexpr float MX_LO_UP = 2048.f, MX_LO_DOWN = 1.f / 2048.f;
+constexpr float MX_CAP = 16384.f;  // largest magnitude an fp16 operand is scaled to
+constexpr float MX_U = 16777216.f;  // 2^24: the value of a code's unit as an fp16 subnormal
+constexpr int G = 32;              // rows per block of a wave
+
+typedef _Float16 mxh8 __attribute__((ext_vector_type(8)));
+typedef float mxf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mxu4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mxh2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ mxf4 mx_mfma(const mxu4& a, const mxu4& b, mxf4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(mxh8, a), __builtin_bit_cast(mxh8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t mx_pk(float x, float y) {
+  return __builtin_bit_cast(uint32_t, mxh2{(_Float16)x, (_Float16)y});
+}
+// hi = rn(x) as fp16 and lo = rn((x - hi) * 2^11): x - hi is exact in fp32
+__device__ __forceinline__ float mx_lo(float x) { return (x - (float)(_Float16)x) * MX_LO_UP; }
+// 2^floor(log2(MX_CAP / m)) for m > 0 (1 for m = 0): the power of two that takes m to about
+// (2^13, 2^14] (the exponent bits of the quotient; m is far from the fp32 range limits here)
+__device__ __forceinline__ float mx_pow2_for(float m) {
+  return m > 0.f ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, MX_CAP / m) & 0x7F800000u) : 1.f;
+}
+
+template <int R, bool F32>
+__global__ __launch_bounds__(NT) void k_decode_mx(DecodeArgs a) {
+  constexpr int D = 128, NW = NT / 64;
+  const Shape sh = a.sh;
+  const int s = blockIdx.y, split = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int i16 = lane & 15, kg = lane >> 4;
+  const int b = s / sh.H, g = s % sh.H;
+  const bool b8 = sh.bits == 8;
+  const uint32_t XR = b8 ? 0x80808080u : 0x08080808u;  // q - qMin of a two's-complement byte
+  const uint32_t MH = b8 ? 0x00FF00FFu : 0x000F000Fu;  // bytes 0 and 2 of a word
+  const uint32_t MB = b8 ? 0xFFFFFFFFu : 0x0F0F0F0Fu;  // every byte
+  __shared__ float sq[R][D];           // q' = q s_K
+  __shared__ float skap[R];            // kappa_j = sum_c q_jc z_c
+  __shared__ float sqmax[NW];
+  __shared__ alignas(16) float sp[NW][R][G + 4];  // a wave's weights of its current block [head][row]
+  __shared__ float so[NW][2 * R][D];   // wave outputs (hi rows, lo rows)
+  __shared__ float sm[NW][R], sl[NW][R], sz[NW][R], sps[NW];
+
+  // ---- query fold, kappa, the query scale ----
+  float qmx = 0.f;
+  for (int i = tid; i < R * D; i += NT) {
+    const int h = i / D, c = i % D;
+    const int64_t qi = ((int64_t)b * sh.Hq + g * R + h) * D + c;
+    const float qv = F32 ? static_cast<const float*>(a.q)[qi] : f16_val(static_cast<const uint16_t*>(a.q)[qi]);
+    const float qf = qv * f16_val(a.v.ks[(int64_t)s * D + c]);
+    sq[h][c] = qf;
+    qmx = fmaxf(qmx, fabsf(qf));
+    so[0][h][c] = qv * f16_val(a.v.kz[(int64_t)s * D + c]);  // q z, for kappa (so is free until the end)
+  }
+  for (int o = 32; o >= 1; o >>= 1) qmx = fmaxf(qmx, __shfl_xor(qmx, o));
+  if (lane == 0) sqmax[wv] = qmx;
+  __syncthreads();
+  if (wv == 0) {  // kappa_h: two channels per lane, then a wave sum
+#pragma unroll
+    for (int h = 0; h < R; ++h) {
+      float k = so[0][h][lane] + so[0][h][lane + 64];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) k = k + __shfl_xor(k, o);
+      if (lane == 0) skap[h] = k;
+    }
+  }
+  float qm = sqmax[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) qm = fmaxf(qm, sqmax[w]);
+  const float qs = mx_pow2_for(qm);
+  // B operand of the scores: lane (column i16, group kg), chunk st holds channels 32 kg + 8 st + pi(e)
+  // with pi = 0, 2, 1, 3, 4, 6, 5, 7 (the A register order below)
+  mxu4 bq[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    uint32_t r4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int c0 = 32 * kg + 8 * st + 4 * (r >> 1) + (r & 1);  // elements (c0, c0 + 2)
+      float x0 = 0.f, x1 = 0.f;
+      if (i16 < 2 * R) {
+        const int h = i16 < R ? i16 : i16 - R;
+        x0 = sq[h][c0] * qs;
+        x1 = sq[h][c0 + 2] * qs;
+        if (i16 >= R) {
+          x0 = mx_lo(x0);
+          x1 = mx_lo(x1);
+        }
+      }
+      r4[r] = mx_pk(x0, x1);
+    }
+    bq[st] = mxu4{r4[0], r4[1], r4[2], r4[3]};
+  }
+  __syncthreads();  // kappa visible; so free again
+  const float al = a.scale * LOG2E;
+  const float kap = skap[i16 < R ? i16 : 0];
+  const float sc_raw = MX_U / qs;
+
+  const int nst = a.rows.nsk + a.rows.nring;
+  const int j0 = split * a.rows_per_split, j1 = min(nst, j0 + a.rows_per_split);
+  const int nblk = j1 > j0 ? (j1 - j0 + G - 1) / G : 0;
+  float m_run = -INFINITY, l_run = 0.f, zacc = 0.f, ps = 4096.f;
+  mxf4 acc[2][4];
+#pragma unroll
+  for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb) acc[gg][bb] = mxf4{0.f, 0.f, 0.f, 0.f};
+  const int hm = i16 < R ? i16 : (i16 < 2 * R ? i16 - R : 0);  // head of A row i16 (weights operand)
+
+  for (int kb = wv; kb < nblk; kb += NW) {
+    const int jb = j0 + G * kb;
+    // ---- loads: K rows 16 tau + i16 (channels 32 kg .. + 31); V rows 8 kg + e (channels 8 i16 .. + 7) ----
+    uint4 kx[2][2];
+    uint2 vx[8];
+    float vsf[8], vzf[8];
+    // a full block inside the sinks or inside the ring without its wrap has contiguous slots: one
+    // base address per lane, rows at immediate offsets, the V metadata of 8 rows in one load each
+    const int slot0 = row_slot(a.rows, jb);
+    const bool contig = jb + G <= j1 && (jb + G <= a.rows.nsk ||
+                                         (jb >= a.rows.nsk && slot0 + G <= a.rows.n_sink + a.rows.ring));
+    if (contig) {  // uniform over the workgroup
+      const int64_t ro0 = (int64_t)s * sh.cap + slot0;
+      const int8_t* pk = a.v.kc + (ro0 + i16) * D + 32 * kg;
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        kx[tau][0] = *reinterpret_cast<const uint4*>(pk + 16 * tau * D);
+        kx[tau][1] = *reinterpret_cast<const uint4*>(pk + 16 * tau * D + 16);
+      }
+      const int8_t* pv = a.v.vc + (ro0 + 8 * kg) * D + 8 * i16;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vx[e] = *reinterpret_cast<const uint2*>(pv + e * D);
+      // 8 consecutive fp16 values at an 8-element boundary (cap is a multiple of 8 rows, and so is
+      // slot0 + 8 kg when slot0 is: otherwise read them one by one)
+      const int64_t mo = ro0 + 8 * kg;
+      if ((mo & 7) == 0) {
+        const uint4 ws = *reinterpret_cast<const uint4*>(a.v.vs + mo);
+        const uint4 wz = *reinterpret_cast<const uint4*>(a.v.vz + mo);
+        const uint32_t sw[4] = {ws.x, ws.y, ws.z, ws.w}, zw[4] = {wz.x, wz.y, wz.z, wz.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          vsf[2 * m] = lo16(sw[m]);
+          vsf[2 * m + 1] = hi16(sw[m]);
+          vzf[2 * m] = lo16(zw[m]);
+          vzf[2 * m + 1] = hi16(zw[m]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          vsf[e] = f16_val(a.v.vs[mo + e]);
+          vzf[e] = f16_val(a.v.vz[mo + e]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const int j = jb + 16 * tau + i16;
+        const int64_t ro = (int64_t)s * sh.cap + row_slot(a.rows, j < j1 ? j : j1 - 1);
+        const uint4* p = reinterpret_cast<const uint4*>(a.v.kc + ro * D + 32 * kg);
+        kx[tau][0] = p[0];
+        kx[tau][1] = p[1];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = jb + 8 * kg + e;
+        const int64_t ro = (int64_t)s * sh.cap + row_slot(a.rows, j < j1 ? j : j1 - 1);
+        vx[e] = *reinterpret_cast<const uint2*>(a.v.vc + ro * D + 8 * i16);
+        vsf[e] = j < j1 ? f16_val(a.v.vs[ro]) : 0.f;  // rows past the split: zero scale and zero
+        vzf[e] = j < j1 ? f16_val(a.v.vz[ro]) : 0.f;
+      }
+    }
+    // ---- scores ----
+    mxf4 c[2] = {mxf4{0.f, 0.f, 0.f, 0.f}, mxf4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau) {
+        const uint4 w = kx[tau][st >> 1];
+        const uint32_t x0 = ((st & 1) ? w.z : w.x) ^ XR, x1 = ((st & 1) ? w.w : w.y) ^ XR;
+        const mxu4 A = mxu4{x0 & MH, (x0 >> 8) & MH, x1 & MH, (x1 >> 8) & MH};
+        c[tau] = mx_mfma(A, bq[st], c[tau]);
+      }
+    // lane (column i16, group kg) holds rows 16 tau + 4 kg + e; the lo column of head j is j + R
+    float y[2][4];
+    float bm = -INFINITY;
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float hi = c[tau][e];
+        const float lo = __shfl_xor(hi, R);
+        const int j = jb + 16 * tau + 4 * kg + e;
+        y[tau][e] = j < j1 ? __builtin_fmaf(__builtin_fmaf(lo, MX_LO_DOWN, hi), sc_raw, kap) * al : -INFINITY;
+        bm = fmaxf(bm, y[tau][e]);
+      }
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    const float mnew = fmaxf(m_run, bm);
+    const float f = mnew == m_run ? 1.f : (m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mnew));
+    m_run = mnew;
+    float psum = 0.f;
+    float pw[2][4];
+#pragma unroll
+    for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pw[tau][e] = mnew == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(y[tau][e] - mnew);
+        psum += pw[tau][e];
+      }
+    l_run = l_run * f + psum;
+    if (i16 < R) {
+#pragma unroll
+      for (int tau = 0; tau < 2; ++tau)
+        *reinterpret_cast<float4*>(&sp[wv][i16][16 * tau + 4 * kg]) =
+            make_float4(pw[tau][0], pw[tau][1], pw[tau][2], pw[tau][3]);
+    }
+    // rescale: acc row 4 kg + e' belongs to head (4 kg + e') mod R, whose factor lane (head) holds
+    const bool resc = __any(i16 < R && f != 1.f);
+    if (resc) {
+      zacc *= __shfl(f, hm);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float fe = __shfl(f, (4 * kg + e) % R);
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+          for (int bb = 0; bb < 4; ++bb) acc[gg][bb][e] *= fe;
+      }
+    }
+    // the weight scale: the block's largest V scale times ps stays within MX_CAP (weights <= 1)
+    float smax = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) smax = fmaxf(smax, vsf[e]);
+    smax = fmaxf(smax, __shfl_xor(smax, 16));
+    smax = fmaxf(smax, __shfl_xor(smax, 32));
+    if (smax * ps > MX_CAP) {  // uniform over the wave
+      const float psn = mx_pow2_for(smax), fs = psn / ps;
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) acc[gg][bb] *= fs;
+      ps = psn;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ---- A operand: row i16 = weights x V scale x ps of head hm (hi rows < R, lo rows R .. 2R - 1)
+    //      over tokens 8 kg + e, the same rows as this lane's V loads ----
+    const float4 pa = *reinterpret_cast<const float4*>(&sp[wv][hm][8 * kg]);
+    const float4 pb = *reinterpret_cast<const float4*>(&sp[wv][hm][8 * kg + 4]);
+    const float pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    uint32_t ar[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x0 = pv[2 * r] * vsf[2 * r] * ps, x1 = pv[2 * r + 1] * vsf[2 * r + 1] * ps;
+      if (i16 >= R) {
+        x0 = mx_lo(x0);
+        x1 = mx_lo(x1);
+      }
+      if (i16 >= 2 * R) x0 = x1 = 0.f;
+      ar[r] = mx_pk(x0, x1);
+    }
+    const mxu4 A = mxu4{ar[0], ar[1], ar[2], ar[3]};
+    if (i16 < R) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zacc = __builtin_fmaf(pv[e], vzf[e], zacc);
+    }
+    // ---- values: B (g, b) register r = byte b of word g of tokens 2r, 2r + 1 ----
+    uint32_t xw[8][2];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xw[e][0] = (vx[e].x ^ XR) & MB;
+      xw[e][1] = (vx[e].y ^ XR) & MB;
+    }
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const uint32_t sel = (uint32_t)bb | 0x0C00u | ((uint32_t)(4 + bb) << 16) | 0x0C000000u;
+        const mxu4 B = mxu4{__builtin_amdgcn_perm(xw[1][gg], xw[0][gg], sel), __builtin_amdgcn_perm(xw[3][gg], xw[2][gg], sel),
+                            __builtin_amdgcn_perm(xw[5][gg], xw[4][gg], sel), __builtin_amdgcn_perm(xw[7][gg], xw[6][gg], sel)};
+        acc[gg][bb] = mx_mfma(A, B, acc[gg][bb]);
+      }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- wave results: l and the zero term summed over the row groups; acc rows to LDS ----
+  l_run = l_run + __shfl_xor(l_run, 16);
+  l_run = l_run + __shfl_xor(l_run, 32);
+  zacc = zacc + __shfl_xor(zacc, 16);
+  zacc = zacc + __shfl_xor(zacc, 32);
+  if (lane < R) {
+    sm[wv][lane] = m_run;
+    sl[wv][lane] = l_run;
+    sz[wv][lane] = zacc;
+  }
+  if (lane == 0) sps[wv] = ps;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int m = 4 * kg + e;
+    if (m < 2 * R) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg)
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) so[wv][m][8 * i16 + 4 * gg + bb] = acc[gg][bb][e];
+    }
+  }
+  __syncthreads();
+  // ---- the workgroup's partial: waves merged in order ----
+  for (int i = tid; i < R * D; i += NT) {
+    const int h = i / D, c = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm[w][h]);
+    float av = 0.f, lv = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = sm[w][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[w][h] - M);
+      const float ov = __builtin_fmaf(__builtin_fmaf(so[w][R + h][c], MX_LO_DOWN, so[w][h][c]), MX_U / sps[w], sz[w][h]);
+      av = av + ov * wt;
+      lv = lv + sl[w][h] * wt;
+    }
+    float* pp = a.part + (((int64_t)s * a.splits + split) * R + h) * (D + 2);
+    pp[c] = av;
+    if (c == 0) {
+      pp[D] = M;
+      pp[D + 1] = lv;
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
   const Shape sh = a.sh;
@@ -511,7 +852,8 @@ hipError_t append_d(const AppendArgs& a, hipStream_t st) {
 
 template <int D, int R, bool F32>
 hipError_t decode_r(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((k_decode<D, R, F32>), dim3(a.splits, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
+  if constexpr (D == 128) hipLaunchKernelGGL((k_decode_mx<R, F32>), dim3(a.splits, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
+  else hipLaunchKernelGGL((k_decode<D, R, F32>), dim3(a.splits, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_merge<D>), dim3(a.sh.B * a.sh.Hq), dim3(D), 0, st, a);
