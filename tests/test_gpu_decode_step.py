@@ -6,7 +6,7 @@ equal to the oracle (stored bytes bit-exact, attention within 1e-3).  The schedu
 boundaries (steps that open a block, which the fused launch handles, and steps that complete one, which
 run as separate launches), start from an empty cache in top-k mode (rows committed as sinks run as
 separate launches), and cover KIVI-2/4, q2k, RoPE on read, and configurations that never fuse
-(TurboQuant, a window shorter than a block, fp32 input)."""
+(TurboQuant, also at head_dim 160; a window shorter than a block, fp32 input)."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,9 @@ CASES = {
                                 50, 35),
     "kivi2_f32_never_fused": (dict(n_layers=1, batch=1, n_kv_heads=1, n_q_heads=2, head_dim=64, fmt="kivi", k_bits=2,
                                    v_bits=2, residual=32, capacity=256, in_dtype="f32"), 20, 35),
+    "tq33_d160_never_fused": (dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=160, fmt="tq", k_bits=3,
+                                   v_bits=3, sink_mode="first_n", n_sink=2, window=96, residual=16, seed=5,
+                                   tq_dense3=True), 40, 35),
 }
 
 
