@@ -759,7 +759,7 @@ template <int FMT, int KB, int VB, int D>
 __global__ __launch_bounds__(64 * FW) void k_append_full(AppendArgs a, int64_t fb0, int nfull) {
   constexpr bool Q2K = FMT == KVQ_FMT_Q2K;
   constexpr int LR = D / 8, RPI = 64 / LR, NI = G / RPI, NG = D / 32;
-  constexpr int KPW = 32 / KB, VPW = 32 / VB, WPC = D * VB / 64;
+  constexpr int VPW = 32 / VB, WPC = D * VB / 64;
   const Shape sh = a.sh;
   const LayerView lv = a.lv;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;

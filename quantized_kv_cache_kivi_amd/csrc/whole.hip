@@ -11,10 +11,12 @@
 //   append   k_stats:   per tile of 256 stored + new rows, the channel min/max of the stored K
 //                       (dequantised with the current metadata) and of the new rows; the new V rows
 //                       are quantised and stored on the way;
-//            k_requant: every tile reduces the per-tile extremes to the new metadata and codes its
-//                       rows again (stored rows from their dequantised values, new rows from the
-//                       input); tile 0 writes the metadata.  The previous metadata is read from the
-//                       copy k_stats left in the workspace, so no tile sees a half-written table.
+//            k_requant: every tile reduces the per-tile extremes to the new metadata, codes its
+//                       new rows from the input and codes again, from their dequantised values, the
+//                       stored rows of the channel groups whose scale or zero changed (the others
+//                       code to the same bytes); tile 0 writes the metadata.  The previous metadata
+//                       is read from the copy k_stats left in the workspace, so no tile sees a
+//                       half-written table.
 //   decode   k_decode:  split-K over the stored rows: the query is folded with the K scales once
 //                       per workgroup (q'_c = q_c s_c, kappa = sum_c q_c z_c), score = q'.u + kappa,
 //                       online softmax per row group, V rows dequantised in fp32; one partial
@@ -92,6 +94,8 @@ __device__ __forceinline__ uint2 quant8(const float* x, const float* s, const fl
   return make_uint2(w[0], w[1]);
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ void ld_meta8(const uint16_t* p, float* x) {
   const uint4 a = *reinterpret_cast<const uint4*>(p);
   const uint32_t w[4] = {a.x, a.y, a.z, a.w};
@@ -124,16 +128,40 @@ __global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
   }
   const int64_t in0 = (int64_t)s * a.n;
   const int jo = min(j1, nold);
-#pragma unroll 4
-  for (int j = j0 + rl; j < jo; j += RP) {  // stored rows
-    float x[8];
-    const int sl = row_slot(a.old, j);
-    codes8(*reinterpret_cast<const uint2*>(a.v.kc + ((int64_t)s * sh.cap + sl) * D + 8 * cg), qmin, x);
+  if (j0 + rl < jo) {
+    // stored rows: the dequantised value fl(fl(u s) + z) is non-decreasing in the code u (s > 0), so
+    // its extremes over the rows are those of the extreme codes, reduced as integers.  Every load of
+    // the thread is issued first; a row past the tile's stored rows repeats the thread's first row.
+    constexpr int NR = RPT / RP;
+    uint2 w[NR];
+    const int8_t* kc = a.v.kc + (int64_t)s * sh.cap * D + 8 * cg;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const int j = j0 + rl + r * RP;
+      w[r] = *reinterpret_cast<const uint2*>(kc + (int64_t)row_slot(a.old, j < jo ? j : j0 + rl) * D);
+    }
+    // per word m: the even bytes (mask 0x00FF00FF) and the odd bytes (shifted down) as 16-bit lanes
+    u16x2 lo[4], hi[4];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      const uint32_t ww[2] = {w[r].x, w[r].y};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t u = qmin == -128 ? ww[m] ^ 0x80808080u : (ww[m] ^ 0x08080808u) & 0x0F0F0F0Fu;
+        const u16x2 ev = __builtin_bit_cast(u16x2, u & 0x00FF00FFu), od = __builtin_bit_cast(u16x2, (u >> 8) & 0x00FF00FFu);
+        lo[2 * m] = r == 0 ? ev : __builtin_elementwise_min(lo[2 * m], ev);
+        hi[2 * m] = r == 0 ? ev : __builtin_elementwise_max(hi[2 * m], ev);
+        lo[2 * m + 1] = r == 0 ? od : __builtin_elementwise_min(lo[2 * m + 1], od);
+        hi[2 * m + 1] = r == 0 ? od : __builtin_elementwise_max(hi[2 * m + 1], od);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x[e] = x[e] * so[e] + zo[e];  // two roundings (no contraction)
-      mn[e] = fminf(mn[e], x[e]);
-      mx[e] = fmaxf(mx[e], x[e]);
+      // byte e of word e / 4: lane (e & 3) >> 1 of the even (e even) or odd word
+      const int wi = 2 * (e >> 2) + (e & 1), li = (e & 3) >> 1;
+      const float ulo = (float)lo[wi][li], uhi = (float)hi[wi][li];
+      mn[e] = ulo * so[e] + zo[e];  // two roundings (no contraction)
+      mx[e] = uhi * so[e] + zo[e];
     }
   }
   for (int j = j0 + rl; j < j1; j += RP) {  // new rows
@@ -249,27 +277,52 @@ __global__ __launch_bounds__(NT) void k_requant(AppendArgs a) {
     }
   }
   __syncthreads();
-  float ns[8], nz[8], so[8], zo[8];
+  // A stored code u of a channel whose scale s and zero z did not change codes to u again:
+  // fl(u s + z) - z and its quotient by s stay within 2^-24 (|z| / s + 3u) of u (u s is exact), below
+  // 1/2 when |z| <= 2^22 s.  Such channels keep their stored bytes; a group of 8 channels is coded
+  // again when any of them changed or fails the bound (a few per append in steady state).  The
+  // tile's (stored row, group to code again) pairs are spread over all threads, so a few changed
+  // groups cost a few pairs per thread.
+  __shared__ int glist[CG];
+  __shared__ int ngch;
+  if (tid < 64) {
+    bool same = true;
+    if (tid < CG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * tid + e;
+        same = same && sns[c] == sos[c] && snz[c] == soz[c] && fabsf(soz[c]) <= 4194304.f * sos[c];
+      }
+    }
+    const uint64_t chg = __ballot(tid < CG && !same);
+    if (tid < CG && !same) glist[__popcll(chg & ((1ull << tid) - 1ull))] = tid;
+    if (tid == 0) ngch = __popcll(chg);
+  }
+  __syncthreads();
+  const int64_t in0 = (int64_t)s * a.n;
+  const int jo = min(j1, nold), ng = ngch;
+  const int items = (jo > j0 ? jo - j0 : 0) * ng;
+#pragma unroll 2
+  for (int it = tid; it < items; it += NT) {  // stored rows of the changed groups, coded again in place
+    const int j = j0 + it / ng, gsel = glist[it % ng];
+    float x[8], gs[8], gz[8];
+    int8_t* row = a.v.kc + ((int64_t)s * sh.cap + row_slot(a.old, j)) * D + 8 * gsel;
+    codes8(*reinterpret_cast<const uint2*>(row), qmin, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[e] = x[e] * sos[8 * gsel + e] + soz[8 * gsel + e];
+      gs[e] = sns[8 * gsel + e];
+      gz[e] = snz[8 * gsel + e];
+    }
+    *reinterpret_cast<uint2*>(row) = quant8(x, gs, gz, L, qmin);
+  }
+  float ns[8], nz[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     ns[e] = sns[8 * cg + e];
     nz[e] = snz[8 * cg + e];
-    so[e] = sos[8 * cg + e];
-    zo[e] = soz[8 * cg + e];
   }
-  const int64_t in0 = (int64_t)s * a.n;
-  const int jo = min(j1, nold);
-#pragma unroll 4
-  for (int j = j0 + rl; j < jo; j += RP) {  // stored rows, coded again in place
-    float x[8];
-    int8_t* row = a.v.kc + ((int64_t)s * sh.cap + row_slot(a.old, j)) * D + 8 * cg;
-    codes8(*reinterpret_cast<const uint2*>(row), qmin, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = x[e] * so[e] + zo[e];
-    *reinterpret_cast<uint2*>(row) = quant8(x, ns, nz, L, qmin);
-  }
-  for (int j = j0 + rl; j < j1; j += RP) {  // new rows
-    if (j < nold) continue;
+  for (int j = max(j0, nold) + rl; j < j1; j += RP) {  // new rows
     float x[8];
     const int i = j - nold;
     ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);

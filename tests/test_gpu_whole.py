@@ -39,7 +39,7 @@ def _log(*a):
 
 
 class WPair:
-    def __init__(self, seed, **kw):
+    def __init__(self, seed, shift=None, spread=None, **kw):
         from quantized_kv_cache_kivi_amd import kvq
         self.ocfg = okw.WholeConfig(**kw)
         self.model = okw.WholeCache(self.ocfg)
@@ -52,11 +52,16 @@ class WPair:
         self.tag = 0
         self.dt = torch.float32 if c.in_dtype == "f32" else torch.float16
         self.mult = 6.0 ** synth.uniform(c.n_kv_heads * c.head_dim, seed, 999).reshape(c.n_kv_heads, 1, c.head_dim)
+        if spread is not None:  # per-channel K spread and offset [n_kv_heads, 1, head_dim]
+            self.mult = spread
+        self.shift = shift
 
     def rows(self, n):
         c = self.ocfg
         self.tag += 1
         k = synth.normal((c.batch, c.n_kv_heads, n, c.head_dim), self.seed, 1000 + self.tag) * self.mult
+        if self.shift is not None:
+            k = k + self.shift
         v = synth.normal((c.batch, c.n_kv_heads, n, c.head_dim), self.seed, 5000 + self.tag)
         return k.to(self.dt).contiguous(), v.to(self.dt).contiguous()
 
@@ -184,3 +189,30 @@ def test_whole_bench_bandwidth_size():
     pair.compare_bytes(0)
     err = max(err, pair.compare_attention(0, 2))
     _log(f"[whole bench size] P={pair.model.P[0]}: bytes exact, attention rel err {err:.2e}")
+
+
+@pytest.mark.parametrize("D,dt", [(128, "f32"), (32, "f16")])
+def test_whole_single_row_appends_keep_or_recode(D, dt):
+    """Single-row appends after a long prefill, as in decoding: most channels keep their scale and zero
+    (their stored codes are kept, not rewritten), a few widen (their stored rows are coded again); some
+    channels sit far from zero with a tiny spread (fp32 input: |zero| / scale far above 2^22, where
+    coding a stored value again may move its code, so those groups are always coded again).  Stored
+    bytes stay equal to the oracle's after every append."""
+    H = 2
+    spread = torch.full((H, 1, D), 1.0)
+    shift = torch.zeros((H, 1, D))
+    spread[0, 0, 3] = 1e-4 if dt == "f32" else 0.05
+    shift[0, 0, 3] = 1000.0
+    spread[1, 0, 17] = 1e-3
+    shift[1, 0, 17] = -300.0
+    pair = WPair(seed=31, shift=shift, spread=spread, n_layers=1, batch=2, n_kv_heads=H, n_q_heads=2 * H,
+                 head_dim=D, bits=8, capacity=640, in_dtype=dt)
+    pair.push(0, 300, False)
+    pair.compare_bytes(0)
+    for i in range(40):
+        pair.push(0, 1, False)
+        if i % 8 == 7:
+            pair.compare_bytes(0)
+    pair.compare_bytes(0)
+    err = pair.compare_attention(0, 3)
+    _log(f"[single-row appends D={D} {dt}] bytes exact after 40 appends, attention rel err {err:.2e}")

@@ -11,7 +11,7 @@ import os
 
 import numpy as np
 
-from oracle import kivi_whole as kw
+from oracle import kivi, kivi_whole as kw
 from oracle.numerics import from_f16_bits
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kivi_whole_bytes.json")))
@@ -120,6 +120,32 @@ def test_on_grid_values_stay_exact_through_recomputes():
             codes = c.kq[0, 0, 0][[c.slot(p) for p in pos]].astype(np.int32)
             want = np.rint((np.stack([vals[p][0] for p in pos]) - np.float32(z)) / np.float32(s)).astype(np.int32)
             assert np.array_equal(codes, want + kw.Q_MIN[bits])
+
+
+def test_unchanged_metadata_codes_back_to_the_same_code():
+    """A re-quantisation whose scale s and zero z equal the stored ones gives every stored code u back
+    when |z| <= 2^22 s: fl(fl(u s) + z) - z, divided by s, is within 2^-24 (|z| / s + 3u) of u, below
+    1/2.  Every positive fp16 scale at or above fp16(1e-5), zeros of both signs up to the bound (and
+    at it), every 8-bit and 4-bit code, through the oracle's own dequantisation and codes."""
+    rng = np.random.default_rng(11)
+    s_bits = np.arange(0x0001, 0x7C00, dtype=np.uint16)
+    s_bits = s_bits[from_f16_bits(s_bits) >= np.float32(np.float16(1e-5))]
+    for bits in (8, 4):
+        L = (1 << bits) - 1
+        u = np.arange(L + 1, dtype=np.int16)
+        for chunk in np.array_split(s_bits, 64):
+            sv = from_f16_bits(chunk).astype(np.float64)
+            bound = np.minimum(4194304.0 * sv, 65504.0)
+            # zeros: the bound itself (rounded down into fp16), half of it, random fractions, 0, both signs
+            zs = np.stack([bound, 0.5 * bound, rng.random(chunk.size) * bound, np.zeros(chunk.size)], 1)
+            zs = np.concatenate([zs, -zs], 1)
+            z16 = np.float16(zs).view(np.uint16)
+            over = np.abs(from_f16_bits(z16).astype(np.float64)) > 4194304.0 * sv[:, None]
+            z16 = np.where(over, np.float16(np.nextafter(np.float16(zs), np.float16(0))).view(np.uint16), z16)
+            for j in range(z16.shape[1]):
+                x = kivi.affine_dequant32(u[None, :], chunk[:, None], z16[:, j, None])
+                back = kivi.affine_codes(x, chunk[:, None], z16[:, j, None], bits)
+                assert np.array_equal(back.astype(np.int16), np.broadcast_to(u, back.shape)), (bits, j)
 
 
 def test_signed_code_range():
