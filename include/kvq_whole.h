@@ -36,6 +36,9 @@
  *   k_codes, v_codes   int8 [S][capacity][head_dim]   (slot-indexed rows)
  *   k_scale, k_zero    fp16 [S][head_dim]
  *   v_scale, v_zero    fp16 [S][capacity]
+ *   sync               uint32 [S]: arrival counters of the workgroups of one append or decode launch
+ *                      (the last to arrive finishes the stream); zero between calls, so calls on one
+ *                      cache must not overlap (calls on one stream never do)
  */
 #ifndef KVQ_WHOLE_H
 #define KVQ_WHOLE_H
@@ -71,6 +74,7 @@ typedef struct { /* byte offsets inside the caller's device buffer */
   uint64_t k_codes, v_codes;      /* int8 [S][capacity][head_dim] */
   uint64_t k_scale, k_zero;       /* fp16 [S][head_dim] */
   uint64_t v_scale, v_zero;       /* fp16 [S][capacity] */
+  uint64_t sync;                  /* uint32 [S] */
   uint64_t total;                 /* = kvqw_required_bytes */
   int32_t capacity;
   int32_t pad_;

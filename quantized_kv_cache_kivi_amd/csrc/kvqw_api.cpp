@@ -75,6 +75,8 @@ kvqw_layout make_layout(const kvqw_config& c) {
   off = a256(off + S * cap * 2);
   L.v_zero = off;
   off = a256(off + S * cap * 2);
+  L.sync = off;
+  off = a256(off + S * 4);
   L.layer_stride = off;
   L.total = (uint64_t)c.n_layers * off;
   return L;
@@ -124,6 +126,7 @@ View view_of(const kvqw_cache* c, int layer) {
   v.kz = (uint16_t*)(b + c->lay.k_zero);
   v.vs = (uint16_t*)(b + c->lay.v_scale);
   v.vz = (uint16_t*)(b + c->lay.v_zero);
+  v.sync = (uint32_t*)(b + c->lay.sync);
   return v;
 }
 

@@ -17,11 +17,14 @@
 //                       code to the same bytes); tile 0 writes the metadata.  The previous metadata
 //                       is read from the copy k_stats left in the workspace, so no tile sees a
 //                       half-written table.
+//            A short append to a short cache (FUSE_ROWS, FUSE_TILES) is one launch of k_stats: the
+//            last tile of a stream to finish (an arrival counter per stream) does the rest of
+//            k_requant's work for it.
 //   decode   k_decode:  split-K over the stored rows: the query is folded with the K scales once
 //                       per workgroup (q'_c = q_c s_c, kappa = sum_c q_c z_c), score = q'.u + kappa,
 //                       online softmax per row group, V rows dequantised in fp32; one partial
-//                       (acc, m, l) per split and head;
-//            k_merge:   the partials of a (b, query head) in fixed split order.
+//                       (acc, m, l) per split and head; the last split of a stream to finish merges
+//                       the stream's partials in fixed split order and writes the output.
 #include "whole_internal.h"
 
 namespace kvqw {
@@ -35,6 +38,28 @@ __device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cas
 __device__ __forceinline__ float f16_val(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 __device__ __forceinline__ float lo16(uint32_t w) { return f16_val((uint16_t)(w & 0xFFFFu)); }
 __device__ __forceinline__ float hi16(uint32_t w) { return f16_val((uint16_t)(w >> 16)); }
+
+// Values that another workgroup of the same launch reads are stored and read with device-scope
+// relaxed atomics (coherent across the XCDs' L2 caches); a workgroup waits for its stores
+// (vmcnt(0)) before it counts itself in the stream's arrival counter.
+__device__ __forceinline__ void st_dev(float* p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Counts the workgroup in counter `ctr` once its stores have completed; true in the last of `n`
+// workgroups, which also resets the counter to zero for the next launch.
+__device__ __forceinline__ bool arrive_last(uint32_t* ctr, int n) {
+  __shared__ int last;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's stores have completed
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t k = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = k == (uint32_t)(n - 1);
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return last != 0;
+}
 
 // Slot of stored row j (sinks first, then the ring rows).
 __device__ __forceinline__ int row_slot(const Rows& r, int j) {
@@ -107,6 +132,9 @@ __device__ __forceinline__ void ld_meta8(const uint16_t* p, float* x) {
 }
 
 template <int D, bool F32>
+__device__ void requant_last(const AppendArgs& a, int s);
+
+template <int D, bool F32, bool FUSED>
 __global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
   constexpr int CG = D / 8, RP = NT / CG;
   const Shape sh = a.sh;
@@ -220,12 +248,17 @@ __global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
       m1 = fmaxf(m1, smx[r * D + tid]);
     }
     float* pp = a.part + ((int64_t)s * a.tiles + tile) * 2 * D;
-    pp[tid] = m0;
-    pp[D + tid] = m1;
-    if (tile == 0) {
+    st_dev(pp + tid, m0);
+    st_dev(pp + D + tid, m1);
+    if (!FUSED && tile == 0) {
       a.oldm[(int64_t)s * 2 * D + tid] = a.v.ks[(int64_t)s * D + tid];
       a.oldm[(int64_t)s * 2 * D + D + tid] = a.v.kz[(int64_t)s * D + tid];
     }
+  }
+  if constexpr (FUSED) {
+    // every tile has read the stored codes and the previous metadata before it arrives: the last
+    // tile of the stream may rewrite both
+    if (arrive_last(a.v.sync + s, a.tiles)) requant_last<D, F32>(a, s);
   }
 }
 
@@ -328,6 +361,164 @@ __global__ __launch_bounds__(NT) void k_requant(AppendArgs a) {
     ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
     *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + new_slot(a, i)) * D + 8 * cg) =
         quant8(x, ns, nz, L, qmin);
+  }
+}
+
+// The rest of a short append, by the last tile of stream s (one workgroup): the new metadata from
+// every tile's extremes, the new rows coded against it, and the stored rows of the channel groups
+// whose scale or zero changed coded again (as in k_requant, over all the stream's stored rows).
+template <int D, bool F32>
+__device__ void requant_last(const AppendArgs& a, int s) {
+  constexpr int CG = D / 8, TG = NT / D;
+  const Shape sh = a.sh;
+  const int tid = threadIdx.x;
+  const int qmin = sh.bits == 8 ? -128 : -8;
+  const float L = (float)((1 << sh.bits) - 1);
+  const int nold = a.old.nsk + a.old.nring;
+  __shared__ float sns[D], snz[D], sos[D], soz[D];
+  __shared__ float rmn[TG][D], rmx[TG][D];
+  __shared__ int glist[CG];
+  __shared__ int ngch;
+  {
+    // MCH tiles per thread and memory round trip (a tile past the last one re-reads the last:
+    // min and max are unchanged by a repeat)
+    constexpr int MCH = 8;
+    const int c = tid % D, tg = tid / D;
+    float m0 = INFINITY, m1 = -INFINITY;
+    const float* pp = a.part + (int64_t)s * a.tiles * 2 * D;
+    for (int t0 = tg; t0 < a.tiles; t0 += TG * MCH) {
+      float lo[MCH], hi[MCH];
+#pragma unroll
+      for (int k = 0; k < MCH; ++k) {
+        const int t = min(t0 + k * TG, a.tiles - 1);
+        lo[k] = ld_dev(pp + t * 2 * D + c);
+        hi[k] = ld_dev(pp + t * 2 * D + D + c);
+      }
+#pragma unroll
+      for (int k = 0; k < MCH; ++k) {
+        m0 = fminf(m0, lo[k]);
+        m1 = fmaxf(m1, hi[k]);
+      }
+    }
+    rmn[tg][c] = m0;
+    rmx[tg][c] = m1;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float m0 = rmn[0][tid], m1 = rmx[0][tid];
+#pragma unroll
+    for (int t = 1; t < TG; ++t) {
+      m0 = fminf(m0, rmn[t][tid]);
+      m1 = fmaxf(m1, rmx[t][tid]);
+    }
+    m0 = m0 + 0.f;
+    m1 = m1 + 0.f;
+    const uint16_t s16 = f16_bits(fmaxf(EPS, (m1 - m0) / L)), z16 = f16_bits(m0);
+    sns[tid] = f16_val(s16);
+    snz[tid] = f16_val(z16);
+    sos[tid] = f16_val(a.v.ks[(int64_t)s * D + tid]);
+    soz[tid] = f16_val(a.v.kz[(int64_t)s * D + tid]);
+    a.v.ks[(int64_t)s * D + tid] = s16;
+    a.v.kz[(int64_t)s * D + tid] = z16;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    bool same = true;
+    if (tid < CG) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 8 * tid + e;
+        same = same && sns[c] == sos[c] && snz[c] == soz[c] && fabsf(soz[c]) <= 4194304.f * sos[c];
+      }
+    }
+    const uint64_t chg = __ballot(tid < CG && !same);
+    if (tid < CG && !same) glist[__popcll(chg & ((1ull << tid) - 1ull))] = tid;
+    if (tid == 0) ngch = __popcll(chg);
+  }
+  __syncthreads();
+  // stored rows of the changed groups, coded again in place: U (row, group) items per thread and
+  // memory round trip (an item past the last repeats the thread's first and is not stored)
+  constexpr int U = 16;
+  const int ng = ngch, items = nold * ng;
+  for (int it0 = tid; it0 < items; it0 += NT * U) {
+    uint2 w[U];
+    int8_t* rp[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int it = it0 + k * NT < items ? it0 + k * NT : it0;
+      rp[k] = a.v.kc + ((int64_t)s * sh.cap + row_slot(a.old, it / ng)) * D + 8 * glist[it % ng];
+      w[k] = *reinterpret_cast<const uint2*>(rp[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const int it = it0 + k * NT;
+      if (it < items) {
+        const int gsel = glist[it % ng];
+        float x[8], gs[8], gz[8];
+        codes8(w[k], qmin, x);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[e] = x[e] * sos[8 * gsel + e] + soz[8 * gsel + e];
+          gs[e] = sns[8 * gsel + e];
+          gz[e] = snz[8 * gsel + e];
+        }
+        *reinterpret_cast<uint2*>(rp[k]) = quant8(x, gs, gz, L, qmin);
+      }
+    }
+  }
+  const int64_t in0 = (int64_t)s * a.n;
+  for (int it = tid; it < a.n * CG; it += NT) {  // new rows
+    const int i = it / CG, cg = it % CG;
+    float x[8], gs[8], gz[8];
+    ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      gs[e] = sns[8 * cg + e];
+      gz[e] = snz[8 * cg + e];
+    }
+    *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + new_slot(a, i)) * D + 8 * cg) = quant8(x, gs, gz, L, qmin);
+  }
+}
+
+// The output of every query head of stream s, by the last split workgroup: the split partials
+// (acc, m, l) merged in split order, MC partials per memory round trip (the running maximum and sums
+// rescaled between chunks).
+template <int D, int R>
+__device__ void merge_last(const DecodeArgs& a, int s) {
+  constexpr int MC = 16;
+  const Shape sh = a.sh;
+  const int b = s / sh.H, g = s % sh.H;
+  const int64_t stride = (int64_t)R * (D + 2);
+  for (int i = threadIdx.x; i < R * D; i += NT) {
+    const int h = i / D, c = i % D;
+    const float* base = a.part + ((int64_t)s * a.splits * R + h) * (D + 2);
+    float M = -INFINITY, lv = 0.f, av = 0.f;
+    for (int q0 = 0; q0 < a.splits; q0 += MC) {
+      float mq[MC], lq[MC], xq[MC];
+#pragma unroll
+      for (int k = 0; k < MC; ++k) {  // past the last split: re-read it (no branch between the loads), unused
+        const bool in = q0 + k < a.splits;
+        const float* pq = base + (in ? q0 + k : a.splits - 1) * stride;
+        const float m = ld_dev(pq + D), l = ld_dev(pq + D + 1), x = ld_dev(pq + c);
+        mq[k] = in ? m : -INFINITY;
+        lq[k] = in ? l : 0.f;
+        xq[k] = in ? x : 0.f;
+      }
+      float Mn = M;
+#pragma unroll
+      for (int k = 0; k < MC; ++k) Mn = fmaxf(Mn, mq[k]);
+      const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);  // sums are 0 while M = -inf
+      av = av * fo;
+      lv = lv * fo;
+#pragma unroll
+      for (int k = 0; k < MC; ++k) {
+        const float w = mq[k] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mq[k] - Mn);
+        av = av + xq[k] * w;
+        lv = lv + lq[k] * w;
+      }
+      M = Mn;
+    }
+    a.out[((int64_t)b * sh.Hq + (int64_t)g * R + h) * D + c] = lv > 0.f ? av / lv : 0.f;
   }
 }
 
@@ -493,12 +684,13 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
       lv = lv + slw[w][h] * wt;
     }
     float* pp = a.part + (((int64_t)s * a.splits + split) * R + h) * (D + 2);
-    pp[c] = av;
+    st_dev(pp + c, av);
     if (c == 0) {
-      pp[D] = M;
-      pp[D + 1] = lv;
+      st_dev(pp + D, M);
+      st_dev(pp + D + 1, lv);
     }
   }
+  if (arrive_last(a.v.sync + s, a.splits)) merge_last<D, R>(a, s);
 }
 
 // ---- Decode attention on the matrix cores (head_dim 128) ----
@@ -834,40 +1026,13 @@ __global__ __launch_bounds__(NT) void k_decode_mx(DecodeArgs a) {
       lv = lv + sl[w][h] * wt;
     }
     float* pp = a.part + (((int64_t)s * a.splits + split) * R + h) * (D + 2);
-    pp[c] = av;
+    st_dev(pp + c, av);
     if (c == 0) {
-      pp[D] = M;
-      pp[D + 1] = lv;
+      st_dev(pp + D, M);
+      st_dev(pp + D + 1, lv);
     }
   }
-}
-
-template <int D>
-__global__ __launch_bounds__(D) void k_merge(DecodeArgs a) {
-  const Shape sh = a.sh;
-  const int bj = blockIdx.x, R = sh.Hq / sh.H;
-  const int b = bj / sh.Hq, jq = bj % sh.Hq, g = jq / R, h = jq % R, s = b * sh.H + g;
-  const int c = threadIdx.x;
-  const int64_t stride = (int64_t)R * (D + 2);
-  const float* base = a.part + ((int64_t)s * a.splits * R + h) * (D + 2);
-  __shared__ float sm[MAX_SPLITS], sw[MAX_SPLITS], sl[MAX_SPLITS];
-  for (int sp = c; sp < a.splits; sp += D) {  // every split's (m, l) at once, then the weights
-    sm[sp] = base[sp * stride + D];
-    sl[sp] = base[sp * stride + D + 1];
-  }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, sm[sp]);
-  __syncthreads();
-  for (int sp = c; sp < a.splits; sp += D) sw[sp] = sm[sp] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm[sp] - M);
-  __syncthreads();
-  float av = 0.f, lv = 0.f;
-#pragma unroll 8
-  for (int sp = 0; sp < a.splits; ++sp) {
-    av = av + base[sp * stride + c] * sw[sp];
-    lv = lv + sl[sp] * sw[sp];
-  }
-  a.out[(int64_t)bj * D + c] = lv > 0.f ? av / lv : 0.f;
+  if (arrive_last(a.v.sync + s, a.splits)) merge_last<D, R>(a, s);
 }
 
 __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
@@ -896,7 +1061,11 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
 template <int D, bool F32>
 hipError_t append_d(const AppendArgs& a, hipStream_t st) {
   const dim3 grid(a.tiles, a.sh.B * a.sh.H);
-  hipLaunchKernelGGL((k_stats<D, F32>), grid, dim3(NT), 0, st, a);
+  if (a.n <= FUSE_ROWS && a.tiles <= FUSE_TILES) {  // one launch: the last tile of each stream finishes it
+    hipLaunchKernelGGL((k_stats<D, F32, true>), grid, dim3(NT), 0, st, a);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((k_stats<D, F32, false>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_requant<D, F32>), grid, dim3(NT), 0, st, a);
@@ -907,9 +1076,6 @@ template <int D, int R, bool F32>
 hipError_t decode_r(const DecodeArgs& a, hipStream_t st) {
   if constexpr (D == 128) hipLaunchKernelGGL((k_decode_mx<R, F32>), dim3(a.splits, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
   else hipLaunchKernelGGL((k_decode<D, R, F32>), dim3(a.splits, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_merge<D>), dim3(a.sh.B * a.sh.Hq), dim3(D), 0, st, a);
   return hipGetLastError();
 }
 

@@ -12,6 +12,11 @@ namespace kvqw {
 constexpr int RPT = 256;           // rows per re-quantisation tile
 constexpr int MAX_SPLITS = 64;     // attention splits per stream
 constexpr int MIN_SPLIT_ROWS = 256;
+// Appends of at most FUSE_ROWS rows to at most FUSE_TILES * RPT stored rows run in one launch: the
+// last tile of each stream finishes it alone (larger caches keep the second launch, whose re-coding
+// of changed channel groups is spread over every tile).
+constexpr int FUSE_ROWS = 32;
+constexpr int FUSE_TILES = 4;
 
 struct View {
   int8_t* kc;    // [S][cap][D]
@@ -20,6 +25,7 @@ struct View {
   uint16_t* kz;
   uint16_t* vs;  // [S][cap]
   uint16_t* vz;
+  uint32_t* sync;  // [S] arrival counters of the workgroups of one launch (zero between calls)
 };
 
 // The stored rows of a stream in order j: the nsk sink rows (slot j), then nring ring rows

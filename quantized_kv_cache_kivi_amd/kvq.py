@@ -56,7 +56,7 @@ class kvqw_config(ctypes.Structure):
 
 class kvqw_layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
-        "layer_stride", "k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "total")] + [
+        "layer_stride", "k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero", "sync", "total")] + [
         ("capacity", ctypes.c_int32), ("pad_", ctypes.c_int32)]
 
 

@@ -191,13 +191,14 @@ def test_whole_bench_bandwidth_size():
     _log(f"[whole bench size] P={pair.model.P[0]}: bytes exact, attention rel err {err:.2e}")
 
 
-@pytest.mark.parametrize("D,dt", [(128, "f32"), (32, "f16")])
-def test_whole_single_row_appends_keep_or_recode(D, dt):
+@pytest.mark.parametrize("D,dt,T0,cap", [(128, "f32", 300, 640), (32, "f16", 300, 640), (64, "f16", 1200, 1280)])
+def test_whole_single_row_appends_keep_or_recode(D, dt, T0, cap):
     """Single-row appends after a long prefill, as in decoding: most channels keep their scale and zero
     (their stored codes are kept, not rewritten), a few widen (their stored rows are coded again); some
     channels sit far from zero with a tiny spread (fp32 input: |zero| / scale far above 2^22, where
     coding a stored value again may move its code, so those groups are always coded again).  Stored
-    bytes stay equal to the oracle's after every append."""
+    bytes stay equal to the oracle's after every append.  Up to 1024 stored rows a single-row append is
+    one launch (the last tile of a stream finishes it); the 1200-row case takes the two-launch path."""
     H = 2
     spread = torch.full((H, 1, D), 1.0)
     shift = torch.zeros((H, 1, D))
@@ -206,8 +207,8 @@ def test_whole_single_row_appends_keep_or_recode(D, dt):
     spread[1, 0, 17] = 1e-3
     shift[1, 0, 17] = -300.0
     pair = WPair(seed=31, shift=shift, spread=spread, n_layers=1, batch=2, n_kv_heads=H, n_q_heads=2 * H,
-                 head_dim=D, bits=8, capacity=640, in_dtype=dt)
-    pair.push(0, 300, False)
+                 head_dim=D, bits=8, capacity=cap, in_dtype=dt)
+    pair.push(0, T0, False)
     pair.compare_bytes(0)
     for i in range(40):
         pair.push(0, 1, False)
@@ -215,4 +216,4 @@ def test_whole_single_row_appends_keep_or_recode(D, dt):
             pair.compare_bytes(0)
     pair.compare_bytes(0)
     err = pair.compare_attention(0, 3)
-    _log(f"[single-row appends D={D} {dt}] bytes exact after 40 appends, attention rel err {err:.2e}")
+    _log(f"[single-row appends D={D} {dt} T0={T0}] bytes exact after 40 appends, attention rel err {err:.2e}")

@@ -123,7 +123,8 @@ def test_whole_config_validation_and_layout(kvq):
     assert lay.capacity == okw.default_capacity(4, 256)
     S, D, cap = 8, 32, lay.capacity
     assert lay.v_codes - lay.k_codes >= S * cap * D and lay.k_zero - lay.k_scale >= S * D * 2
-    assert lay.v_zero - lay.v_scale >= S * cap * 2 and lay.layer_stride >= lay.v_zero + S * cap * 2
+    assert lay.v_zero - lay.v_scale >= S * cap * 2 and lay.sync - lay.v_zero >= S * cap * 2
+    assert lay.layer_stride >= lay.sync + S * 4
     assert kvq.whole_required_bytes(ok) == 12 * lay.layer_stride
     assert kvq.whole_workspace_bytes(ok) > 0
     bad = [
