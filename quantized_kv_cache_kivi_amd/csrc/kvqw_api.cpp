@@ -272,7 +272,7 @@ kvq_status kvqw_decode_attn(kvqw_cache* c, int32_t layer, const void* q, float* 
   // split: 26 us for the call on the batch-8, T = 4096 layer, against 31 us at 256 and 32 us at 1024;
   // loading each wave's next block ahead gained nothing); only the last split ends early
   const int min_rows = cf.head_dim == 128 ? 2 * MIN_SPLIT_ROWS : MIN_SPLIT_ROWS;
-  const int splits = std::min(MAX_SPLITS, (nst + min_rows - 1) / min_rows);
+  const int splits = std::max(1, std::min(MAX_SPLITS, nst / min_rows));  // one split below 2 * min_rows
   a.rows_per_split = (nst + splits - 1) / splits;
   if (cf.head_dim == 128) a.rows_per_split = (a.rows_per_split + 31) / 32 * 32;
   a.splits = (nst + a.rows_per_split - 1) / a.rows_per_split;

@@ -17,9 +17,8 @@
 //                       code to the same bytes); tile 0 writes the metadata.  The previous metadata
 //                       is read from the copy k_stats left in the workspace, so no tile sees a
 //                       half-written table.
-//            A short append to a short cache (FUSE_ROWS, FUSE_TILES) is one launch of k_stats: the
-//            last tile of a stream to finish (an arrival counter per stream) does the rest of
-//            k_requant's work for it.
+//            A short append to a short cache (FUSE_ROWS, FUSE_TILES) is one launch of
+//            k_append_one: one workgroup per stream does both steps over all its tiles.
 //   decode   k_decode:  split-K over the stored rows: the query is folded with the K scales once
 //                       per workgroup (q'_c = q_c s_c, kappa = sum_c q_c z_c), score = q'.u + kappa,
 //                       online softmax per row group, V rows dequantised in fp32; one partial
@@ -131,29 +130,19 @@ __device__ __forceinline__ void ld_meta8(const uint16_t* p, float* x) {
   }
 }
 
+// Channel extremes of the rows of tile `tile` this thread covers (rows rl, rl + RP, ... of the tile,
+// channels 8 cg .. 8 cg + 7), folded into mn, mx: stored rows dequantised with the current metadata
+// (so, zo), new rows from the input; the new V rows are quantised and stored on the way.
 template <int D, bool F32>
-__device__ void requant_last(const AppendArgs& a, int s);
-
-template <int D, bool F32, bool FUSED>
-__global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
+__device__ __forceinline__ void tile_extremes(const AppendArgs& a, int s, int tile, const float* so, const float* zo,
+                                              float* mn, float* mx) {
   constexpr int CG = D / 8, RP = NT / CG;
   const Shape sh = a.sh;
-  const int s = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x;
-  const int cg = tid % CG, rl = tid / CG;
+  const int tid = threadIdx.x, cg = tid % CG, rl = tid / CG;
   const int qmin = sh.bits == 8 ? -128 : -8;
   const float L = (float)((1 << sh.bits) - 1);
   const int nold = a.old.nsk + a.old.nring, ntot = nold + a.n;
   const int j0 = tile * RPT, j1 = min(ntot, j0 + RPT);
-  __shared__ float smn[RP * D], smx[RP * D];
-  float so[8], zo[8];
-  ld_meta8(a.v.ks + (int64_t)s * D + 8 * cg, so);
-  ld_meta8(a.v.kz + (int64_t)s * D + 8 * cg, zo);
-  float mn[8], mx[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    mn[e] = INFINITY;
-    mx[e] = -INFINITY;
-  }
   const int64_t in0 = (int64_t)s * a.n;
   const int jo = min(j1, nold);
   if (j0 + rl < jo) {
@@ -188,46 +177,42 @@ __global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
       // byte e of word e / 4: lane (e & 3) >> 1 of the even (e even) or odd word
       const int wi = 2 * (e >> 2) + (e & 1), li = (e & 3) >> 1;
       const float ulo = (float)lo[wi][li], uhi = (float)hi[wi][li];
-      mn[e] = ulo * so[e] + zo[e];  // two roundings (no contraction)
-      mx[e] = uhi * so[e] + zo[e];
+      mn[e] = fminf(mn[e], ulo * so[e] + zo[e]);  // two roundings (no contraction)
+      mx[e] = fmaxf(mx[e], uhi * so[e] + zo[e]);
     }
   }
-  for (int j = j0 + rl; j < j1; j += RP) {  // new rows
-    if (j < nold) continue;
+  for (int j = max(j0, nold) + rl; j < j1; j += RP) {  // new rows
     float x[8];
-    {
-      const int i = j - nold;
-      ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
-      // the new V row: per-token min/max over all channels, final at append
-      float v[8];
-      ld8<F32>(a.vin, (in0 + i) * D + 8 * cg, v);
-      float vmn = v[0], vmx = v[0];
+    const int i = j - nold;
+    ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
+    // the new V row: per-token min/max over all channels, final at append
+    float v[8];
+    ld8<F32>(a.vin, (in0 + i) * D + 8 * cg, v);
+    float vmn = v[0], vmx = v[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) {
-        vmn = fminf(vmn, v[e]);
-        vmx = fmaxf(vmx, v[e]);
-      }
+    for (int e = 1; e < 8; ++e) {
+      vmn = fminf(vmn, v[e]);
+      vmx = fmaxf(vmx, v[e]);
+    }
 #pragma unroll
-      for (int o = CG / 2; o >= 1; o >>= 1) {
-        vmn = fminf(vmn, __shfl_xor(vmn, o));
-        vmx = fmaxf(vmx, __shfl_xor(vmx, o));
-      }
-      vmn = vmn + 0.f;
-      vmx = vmx + 0.f;
-      const uint16_t s16 = f16_bits(fmaxf(EPS, (vmx - vmn) / L)), z16 = f16_bits(vmn);
-      float sv[8], zv[8];
+    for (int o = CG / 2; o >= 1; o >>= 1) {
+      vmn = fminf(vmn, __shfl_xor(vmn, o));
+      vmx = fmaxf(vmx, __shfl_xor(vmx, o));
+    }
+    vmn = vmn + 0.f;
+    vmx = vmx + 0.f;
+    const uint16_t s16 = f16_bits(fmaxf(EPS, (vmx - vmn) / L)), z16 = f16_bits(vmn);
+    float sv[8], zv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = f16_val(s16);
-        zv[e] = f16_val(z16);
-      }
-      const int sl = new_slot(a, i);
-      const int64_t ro = (int64_t)s * sh.cap + sl;
-      *reinterpret_cast<uint2*>(a.v.vc + ro * D + 8 * cg) = quant8(v, sv, zv, L, qmin);
-      if (cg == 0) {
-        a.v.vs[ro] = s16;
-        a.v.vz[ro] = z16;
-      }
+    for (int e = 0; e < 8; ++e) {
+      sv[e] = f16_val(s16);
+      zv[e] = f16_val(z16);
+    }
+    const int64_t ro = (int64_t)s * sh.cap + new_slot(a, i);
+    *reinterpret_cast<uint2*>(a.v.vc + ro * D + 8 * cg) = quant8(v, sv, zv, L, qmin);
+    if (cg == 0) {
+      a.v.vs[ro] = s16;
+      a.v.vz[ro] = z16;
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -235,30 +220,54 @@ __global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
       mx[e] = fmaxf(mx[e], x[e]);
     }
   }
+}
+
+// Per-channel extremes of the workgroup's threads (mn, mx of each row lane) into m0[c], m1[c]
+// (c < D, threads tid < D).
+template <int D>
+__device__ __forceinline__ void block_extremes(const float* mn, const float* mx, float& m0, float& m1) {
+  constexpr int CG = D / 8, RP = NT / CG;
+  __shared__ float smn[RP * D], smx[RP * D];
+  const int tid = threadIdx.x, cg = tid % CG, rl = tid / CG;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     smn[rl * D + 8 * cg + e] = mn[e];
     smx[rl * D + 8 * cg + e] = mx[e];
   }
   __syncthreads();
+  m0 = INFINITY;
+  m1 = -INFINITY;
   if (tid < D) {
-    float m0 = INFINITY, m1 = -INFINITY;
     for (int r = 0; r < RP; ++r) {
       m0 = fminf(m0, smn[r * D + tid]);
       m1 = fmaxf(m1, smx[r * D + tid]);
     }
+  }
+}
+
+template <int D, bool F32>
+__global__ __launch_bounds__(NT) void k_stats(AppendArgs a) {
+  constexpr int CG = D / 8;
+  const int s = blockIdx.y, tile = blockIdx.x, tid = threadIdx.x, cg = tid % CG;
+  float so[8], zo[8], mn[8], mx[8];
+  ld_meta8(a.v.ks + (int64_t)s * D + 8 * cg, so);
+  ld_meta8(a.v.kz + (int64_t)s * D + 8 * cg, zo);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = INFINITY;
+    mx[e] = -INFINITY;
+  }
+  tile_extremes<D, F32>(a, s, tile, so, zo, mn, mx);
+  float m0, m1;
+  block_extremes<D>(mn, mx, m0, m1);
+  if (tid < D) {
     float* pp = a.part + ((int64_t)s * a.tiles + tile) * 2 * D;
-    st_dev(pp + tid, m0);
-    st_dev(pp + D + tid, m1);
-    if (!FUSED && tile == 0) {
+    pp[tid] = m0;
+    pp[D + tid] = m1;
+    if (tile == 0) {
       a.oldm[(int64_t)s * 2 * D + tid] = a.v.ks[(int64_t)s * D + tid];
       a.oldm[(int64_t)s * 2 * D + D + tid] = a.v.kz[(int64_t)s * D + tid];
     }
-  }
-  if constexpr (FUSED) {
-    // every tile has read the stored codes and the previous metadata before it arrives: the last
-    // tile of the stream may rewrite both
-    if (arrive_last(a.v.sync + s, a.tiles)) requant_last<D, F32>(a, s);
   }
 }
 
@@ -364,62 +373,43 @@ __global__ __launch_bounds__(NT) void k_requant(AppendArgs a) {
   }
 }
 
-// The rest of a short append, by the last tile of stream s (one workgroup): the new metadata from
-// every tile's extremes, the new rows coded against it, and the stored rows of the channel groups
-// whose scale or zero changed coded again (as in k_requant, over all the stream's stored rows).
+// A short append to a short cache (at most FUSE_TILES tiles) by one workgroup per stream: the tiles'
+// extremes in turn, then the new metadata, the new rows coded against it, and the stored rows of the
+// channel groups whose scale or zero changed coded again (as k_stats + k_requant do over all tiles).
 template <int D, bool F32>
-__device__ void requant_last(const AppendArgs& a, int s) {
-  constexpr int CG = D / 8, TG = NT / D;
+__global__ __launch_bounds__(NT) void k_append_one(AppendArgs a) {
+  constexpr int CG = D / 8;
   const Shape sh = a.sh;
-  const int tid = threadIdx.x;
+  const int s = blockIdx.y, tid = threadIdx.x, cg = tid % CG;
   const int qmin = sh.bits == 8 ? -128 : -8;
   const float L = (float)((1 << sh.bits) - 1);
   const int nold = a.old.nsk + a.old.nring;
   __shared__ float sns[D], snz[D], sos[D], soz[D];
-  __shared__ float rmn[TG][D], rmx[TG][D];
   __shared__ int glist[CG];
   __shared__ int ngch;
   {
-    // MCH tiles per thread and memory round trip (a tile past the last one re-reads the last:
-    // min and max are unchanged by a repeat)
-    constexpr int MCH = 8;
-    const int c = tid % D, tg = tid / D;
-    float m0 = INFINITY, m1 = -INFINITY;
-    const float* pp = a.part + (int64_t)s * a.tiles * 2 * D;
-    for (int t0 = tg; t0 < a.tiles; t0 += TG * MCH) {
-      float lo[MCH], hi[MCH];
+    float so[8], zo[8], mn[8], mx[8];
+    ld_meta8(a.v.ks + (int64_t)s * D + 8 * cg, so);
+    ld_meta8(a.v.kz + (int64_t)s * D + 8 * cg, zo);
 #pragma unroll
-      for (int k = 0; k < MCH; ++k) {
-        const int t = min(t0 + k * TG, a.tiles - 1);
-        lo[k] = ld_dev(pp + t * 2 * D + c);
-        hi[k] = ld_dev(pp + t * 2 * D + D + c);
-      }
-#pragma unroll
-      for (int k = 0; k < MCH; ++k) {
-        m0 = fminf(m0, lo[k]);
-        m1 = fmaxf(m1, hi[k]);
-      }
+    for (int e = 0; e < 8; ++e) {
+      mn[e] = INFINITY;
+      mx[e] = -INFINITY;
     }
-    rmn[tg][c] = m0;
-    rmx[tg][c] = m1;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float m0 = rmn[0][tid], m1 = rmx[0][tid];
-#pragma unroll
-    for (int t = 1; t < TG; ++t) {
-      m0 = fminf(m0, rmn[t][tid]);
-      m1 = fmaxf(m1, rmx[t][tid]);
+    for (int tile = 0; tile < a.tiles; ++tile) tile_extremes<D, F32>(a, s, tile, so, zo, mn, mx);
+    float m0, m1;
+    block_extremes<D>(mn, mx, m0, m1);
+    if (tid < D) {
+      m0 = m0 + 0.f;
+      m1 = m1 + 0.f;
+      const uint16_t s16 = f16_bits(fmaxf(EPS, (m1 - m0) / L)), z16 = f16_bits(m0);
+      sns[tid] = f16_val(s16);
+      snz[tid] = f16_val(z16);
+      sos[tid] = f16_val(a.v.ks[(int64_t)s * D + tid]);
+      soz[tid] = f16_val(a.v.kz[(int64_t)s * D + tid]);
+      a.v.ks[(int64_t)s * D + tid] = s16;
+      a.v.kz[(int64_t)s * D + tid] = z16;
     }
-    m0 = m0 + 0.f;
-    m1 = m1 + 0.f;
-    const uint16_t s16 = f16_bits(fmaxf(EPS, (m1 - m0) / L)), z16 = f16_bits(m0);
-    sns[tid] = f16_val(s16);
-    snz[tid] = f16_val(z16);
-    sos[tid] = f16_val(a.v.ks[(int64_t)s * D + tid]);
-    soz[tid] = f16_val(a.v.kz[(int64_t)s * D + tid]);
-    a.v.ks[(int64_t)s * D + tid] = s16;
-    a.v.kz[(int64_t)s * D + tid] = z16;
   }
   __syncthreads();
   if (tid < 64) {
@@ -468,15 +458,15 @@ __device__ void requant_last(const AppendArgs& a, int s) {
   }
   const int64_t in0 = (int64_t)s * a.n;
   for (int it = tid; it < a.n * CG; it += NT) {  // new rows
-    const int i = it / CG, cg = it % CG;
+    const int i = it / CG, g = it % CG;
     float x[8], gs[8], gz[8];
-    ld8<F32>(a.k, (in0 + i) * D + 8 * cg, x);
+    ld8<F32>(a.k, (in0 + i) * D + 8 * g, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      gs[e] = sns[8 * cg + e];
-      gz[e] = snz[8 * cg + e];
+      gs[e] = sns[8 * g + e];
+      gz[e] = snz[8 * g + e];
     }
-    *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + new_slot(a, i)) * D + 8 * cg) = quant8(x, gs, gz, L, qmin);
+    *reinterpret_cast<uint2*>(a.v.kc + ((int64_t)s * sh.cap + new_slot(a, i)) * D + 8 * g) = quant8(x, gs, gz, L, qmin);
   }
 }
 
@@ -683,6 +673,10 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
       av = av + sacc[w][h][c] * wt;
       lv = lv + slw[w][h] * wt;
     }
+    if (a.splits == 1) {  // the only split: its partial is the output
+      a.out[((int64_t)(s / a.sh.H) * a.sh.Hq + (int64_t)(s % a.sh.H) * R + h) * D + c] = lv > 0.f ? av / lv : 0.f;
+      continue;
+    }
     float* pp = a.part + (((int64_t)s * a.splits + split) * R + h) * (D + 2);
     st_dev(pp + c, av);
     if (c == 0) {
@@ -690,7 +684,7 @@ __global__ __launch_bounds__(NT) void k_decode(DecodeArgs a) {
       st_dev(pp + D + 1, lv);
     }
   }
-  if (arrive_last(a.v.sync + s, a.splits)) merge_last<D, R>(a, s);
+  if (a.splits > 1 && arrive_last(a.v.sync + s, a.splits)) merge_last<D, R>(a, s);
 }
 
 // ---- Decode attention on the matrix cores (head_dim 128) ----
@@ -1025,6 +1019,10 @@ __global__ __launch_bounds__(NT) void k_decode_mx(DecodeArgs a) {
       av = av + ov * wt;
       lv = lv + sl[w][h] * wt;
     }
+    if (a.splits == 1) {  // the only split: its partial is the output
+      a.out[((int64_t)(s / a.sh.H) * a.sh.Hq + (int64_t)(s % a.sh.H) * R + h) * D + c] = lv > 0.f ? av / lv : 0.f;
+      continue;
+    }
     float* pp = a.part + (((int64_t)s * a.splits + split) * R + h) * (D + 2);
     st_dev(pp + c, av);
     if (c == 0) {
@@ -1032,7 +1030,7 @@ __global__ __launch_bounds__(NT) void k_decode_mx(DecodeArgs a) {
       st_dev(pp + D + 1, lv);
     }
   }
-  if (arrive_last(a.v.sync + s, a.splits)) merge_last<D, R>(a, s);
+  if (a.splits > 1 && arrive_last(a.v.sync + s, a.splits)) merge_last<D, R>(a, s);
 }
 
 __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
@@ -1061,11 +1059,11 @@ __global__ __launch_bounds__(NT) void k_dequant(DequantArgs a) {
 template <int D, bool F32>
 hipError_t append_d(const AppendArgs& a, hipStream_t st) {
   const dim3 grid(a.tiles, a.sh.B * a.sh.H);
-  if (a.n <= FUSE_ROWS && a.tiles <= FUSE_TILES) {  // one launch: the last tile of each stream finishes it
-    hipLaunchKernelGGL((k_stats<D, F32, true>), grid, dim3(NT), 0, st, a);
+  if (a.n <= FUSE_ROWS && a.tiles <= FUSE_TILES) {  // one launch, one workgroup per stream
+    hipLaunchKernelGGL((k_append_one<D, F32>), dim3(1, a.sh.B * a.sh.H), dim3(NT), 0, st, a);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((k_stats<D, F32, false>), grid, dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((k_stats<D, F32>), grid, dim3(NT), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((k_requant<D, F32>), grid, dim3(NT), 0, st, a);

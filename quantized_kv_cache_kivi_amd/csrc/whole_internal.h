@@ -12,9 +12,8 @@ namespace kvqw {
 constexpr int RPT = 256;           // rows per re-quantisation tile
 constexpr int MAX_SPLITS = 64;     // attention splits per stream
 constexpr int MIN_SPLIT_ROWS = 256;
-// Appends of at most FUSE_ROWS rows to at most FUSE_TILES * RPT stored rows run in one launch: the
-// last tile of each stream finishes it alone (larger caches keep the second launch, whose re-coding
-// of changed channel groups is spread over every tile).
+// Appends of at most FUSE_ROWS rows to at most FUSE_TILES * RPT rows run in one launch, one workgroup
+// per stream (larger caches take two launches over every tile: the extremes, then the coding).
 constexpr int FUSE_ROWS = 32;
 constexpr int FUSE_TILES = 4;
 
