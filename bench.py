@@ -282,7 +282,7 @@ def whole_figure(dev, stream, with_oracle=False):
         "tokens_per_s": steps / el, "us_per_step": el / steps * 1e6, "stored_rows": stored,
         "append_us": ta, "decode_attn_us": td,
         "cache_bytes_12_layers": 12 * c.kvqw_account(0)["code_bytes"] + 12 * c.kvqw_account(0)["meta_bytes"],
-        "note": "launch-bound: 4 kernel launches per layer and step over 8 x 260 rows of 68 bytes"}
+        "note": "launch-bound: 2 kernel launches per layer and step (append, decode attention; evict is host-side) over 8 x 260 rows of 68 bytes"}
     if with_oracle:  # the oracle on one layer of the same model, steady state (260 stored rows), 1 thread
         from threadpoolctl import threadpool_limits
 
