@@ -31,6 +31,12 @@ CASES = {
                                      n_sink=3, capacity=1024, in_dtype="f32"), [2, 700, 1], False),
     "int4_d32_r2_f16_sink8_w20": (dict(n_layers=1, batch=3, n_kv_heads=1, n_q_heads=2, head_dim=32, bits=4, n_sink=8,
                                        window=20), [5, 10, 30] + [1] * 40, True),
+    # the one-launch append up to 32 rows and 4 tiles (992 + 32 = 1024 rows), two launches past either
+    # bound; one decode split below 2 x 512 stored rows at head_dim 128 (2 x 256 at 32), two at it
+    "int8_d128_r4_f16_launch_bounds": (dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, bits=8,
+                                            capacity=1216), [992, 32, 1, 31, 1], False),
+    "int4_d32_r1_f32_launch_bounds": (dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, bits=4,
+                                           capacity=1088, in_dtype="f32"), [500, 11, 1, 33, 1], False),
 }
 
 
