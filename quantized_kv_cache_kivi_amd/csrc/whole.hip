@@ -720,9 +720,11 @@ __device__ __forceinline__ uint32_t mx_pk(float x, float y) {
 // hi = rn(x) as fp16 and lo = rn((x - hi) * 2^11): x - hi is exact in fp32
 __device__ __forceinline__ float mx_lo(float x) { return (x - (float)(_Float16)x) * MX_LO_UP; }
 // 2^floor(log2(MX_CAP / m)) for m > 0 (1 for m = 0): the power of two that takes m to about
-// (2^13, 2^14] (the exponent bits of the quotient; m is far from the fp32 range limits here)
+// (2^13, 2^14] (the exponent bits of the quotient), at most 2^100 (a tiny fp32 query: the quotient
+// would overflow, and its scores are ~0 anyway)
 __device__ __forceinline__ float mx_pow2_for(float m) {
-  return m > 0.f ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, MX_CAP / m) & 0x7F800000u) : 1.f;
+  return m > 0.f ? __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, fminf(MX_CAP / m, 0x1p100f)) & 0x7F800000u)
+                 : 1.f;
 }
 
 template <int R, bool F32>

@@ -104,9 +104,9 @@ class WPair:
         for name in ("vs", "vz"):
             assert np.array_equal(g[name][:, :, sl], getattr(m, name)[layer][:, :, sl]), name
 
-    def compare_attention(self, layer, tag):
+    def compare_attention(self, layer, tag, qscale=1.0):
         c = self.ocfg
-        q = synth.normal((c.batch, c.n_q_heads, c.head_dim), self.seed, 9000 + tag).to(self.dt).contiguous()
+        q = (synth.normal((c.batch, c.n_q_heads, c.head_dim), self.seed, 9000 + tag) * qscale).to(self.dt).contiguous()
         out = torch.full((c.batch, c.n_q_heads, c.head_dim), float("nan"), dtype=torch.float32, device="cuda")
         self.gpu.kvqw_decode_attn(layer, q.cuda(), out)
         torch.cuda.synchronize()
@@ -223,3 +223,14 @@ def test_whole_single_row_appends_keep_or_recode(D, dt, T0, cap):
     pair.compare_bytes(0)
     err = pair.compare_attention(0, 3)
     _log(f"[single-row appends D={D} {dt} T0={T0}] bytes exact after 40 appends, attention rel err {err:.2e}")
+
+
+def test_whole_tiny_fp32_query():
+    """An fp32 query of magnitude 1e-36 at head_dim 128: the matrix-core kernel scales the folded query
+    up by a power of two before its fp16 split (capped, so the factor stays finite); every score is ~0
+    and the output is the plain mean of the V rows, as the oracle's."""
+    pair = WPair(seed=41, n_layers=1, batch=1, n_kv_heads=2, n_q_heads=4, head_dim=128, bits=8, capacity=1216,
+                 in_dtype="f32")
+    pair.push(0, 1100, False)
+    err = max(pair.compare_attention(0, 1, qscale=1e-36), pair.compare_attention(0, 2, qscale=1e-20))
+    _log(f"[tiny fp32 query] attention rel err {err:.2e}")
