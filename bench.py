@@ -394,7 +394,7 @@ def rope_figure(cfgno, kw, pre_k, pre_v, sinks_per_b, seed, dev, stream):
     return res
 
 
-def decode_figure(cfgno, dev, stream, ncalls=40):
+def decode_figure(cfgno, dev, stream, ncalls=40, kw_extra=None, label=None):
     """Decode attention of one workload on its full-size cache, cold: the cache is replicated until the
     replicas exceed 1 GB and consecutive calls read different replicas.  Reports the call's duration (HIP
     events on its stream, median), algorithmic GB/s and the fraction of the 8 TB/s peak, and next to it a
@@ -404,7 +404,7 @@ def decode_figure(cfgno, dev, stream, ncalls=40):
     import torch
     from quantized_kv_cache_kivi_amd import kvq, synth
     C = CONFIGS[cfgno]
-    kw = dict(C["kw"])
+    kw = dict(C["kw"], **(kw_extra or {}))
     seed, T0 = SEEDS[cfgno], C["prefill"]
     if kw.get("window", 0) == 0:
         kw["capacity"] = 32 * math.ceil((T0 + 32 + 64) / 32)
@@ -459,12 +459,13 @@ def decode_figure(cfgno, dev, stream, ncalls=40):
     gbps = nbytes / dec_med / 1e3
     read_gbps = rd_bytes / rd_med / 1e3
     tr = load_traffic(cfgno)
-    fig = {"workload": f"{C['name']}: {C['desc']}", "P": P, "lo": lo, "cache_replicas": nrep,
+    fig = {"workload": f"{C['name']}: {C['desc']}" + (f" ({label})" if label else ""), "P": P, "lo": lo,
+           "cache_replicas": nrep,
            "bytes_per_call": nbytes, "us_per_call": dec_med, "us_per_call_mean": dec_mean, "GBps": gbps,
            "frac_of_peak": gbps / HBM_PEAK_GBPS, "context_tokens_per_s": nctx / (dec_med * 1e-6),
            "stream_read": {"bytes": rd_bytes, "us": rd_med, "GBps": read_gbps, "frac_of_peak": read_gbps / HBM_PEAK_GBPS},
            "frac_of_stream_read": gbps / read_gbps,
-           "traffic_bytes_per_call": tr["bytes_per_call"] if tr else None}
+           "traffic_bytes_per_call": tr["bytes_per_call"] if tr and not kw_extra else None}
     if kw.get("window", 0) > 0:  # per-step append of one row + evict, on the one replica it advances
         steps = [make_rows(cfgno, kw, 1, seed, 10_000 + 3 * i, dev, kmult) for i in range(ncalls + 5)]
         c = reps[0]
@@ -487,6 +488,8 @@ def algorithmic_bytes(kw, P, lo, sinks_per_b):
     D, H, Hq, B = kw["head_dim"], kw["n_kv_heads"], kw["n_q_heads"], kw["batch"]
     R = kw.get("residual", 0)
     fmt, kb, vb = kw.get("fmt", "kivi"), kw.get("k_bits", 2), kw.get("v_bits", 2)
+    if fmt == "tq" and not kw.get("tq_dense3"):  # 3-bit TurboQuant codes sit in 4-bit slots
+        kb, vb = (4 if kb == 3 else kb), (4 if vb == 3 else vb)
     if fmt == "kivi":
         kmeta_blk, vmeta_tok = 4 * D, 4 * (D // 32)
     elif fmt == "q2k":
@@ -971,6 +974,14 @@ def main():
         for cn in by_cfg:
             log(f"[bench] decode attention of config {cn} at full size")
             res["decode_attn_by_config"][str(cn)] = decode_figure(cn, dev, stream)
+        if extras and 4 in by_cfg:
+            # the other TurboQuant widths and packings at config 4's shape (same inputs and cache size)
+            res["turboquant_widths"] = {}
+            for name, ex in (("k3v2", dict(k_bits=3, v_bits=2)), ("k3v2_dense3", dict(k_bits=3, v_bits=2, tq_dense3=True)),
+                             ("k4v3", dict(k_bits=4, v_bits=3)), ("k4v4", dict(k_bits=4, v_bits=4))):
+                log(f"[bench] decode attention of TurboQuant {name} at config 4's shape")
+                res["turboquant_widths"][name] = decode_figure(4, dev, stream, ncalls=20, kw_extra=ex,
+                                                               label=f"TurboQuant {name}")
     if not args.no_cpu_baseline:
         try:
             n_cpu = min(args.steps, 16)

@@ -55,6 +55,7 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u3 __attribute__((ext_vector_type(3)));
 
 constexpr int FD = 128;       // head_dim of this path
 constexpr int NW = DNT / 64;  // waves per workgroup
@@ -189,6 +190,26 @@ __device__ __forceinline__ void tq_cen_a(uint32_t w, const uint32_t* tab, u4& ah
   al = u4{ll[0], ll[1], ll[2], ll[3]};
 }
 
+// The same for 8 dense 3-bit codes: channel 2r + e of the step at bits 6r + 3e of x (the step's
+// 24-bit field of the dense stream), table entries 0..7.
+__device__ __forceinline__ void tq_cen_a3(uint32_t x, const uint32_t* tab, u4& ah, u4& al) {
+  uint32_t hh[4], ll[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t e0 = tab[(x >> (6 * r)) & 7u], e1 = tab[(x >> (6 * r + 3)) & 7u];
+    hh[r] = __builtin_amdgcn_perm(e1, e0, 0x05040100u);
+    ll[r] = __builtin_amdgcn_perm(e1, e0, 0x07060302u);
+  }
+  ah = u4{hh[0], hh[1], hh[2], hh[3]};
+  al = u4{ll[0], ll[1], ll[2], ll[3]};
+}
+// The 24-bit field of step st (channels 8 st .. 8 st + 7 of the lane's 32) in the lane's three
+// words of dense 3-bit K codes.
+__device__ __forceinline__ uint32_t dense3_step(const uint32_t* k, int st) {
+  return st == 0 ? k[0] : st == 1 ? __builtin_amdgcn_alignbit(k[1], k[0], 24)
+                        : st == 2 ? __builtin_amdgcn_alignbit(k[2], k[1], 16) : k[2] >> 8;
+}
+
 // Signed plane of code bit BIT of 2-bit codes, from the complemented code words nd: every element
 // is s = 2 * bit - 1 as fp16 +-1.0 (`one16` = 0x3C003C00; the sign bit is set where the code bit is
 // 0).  Planes of +-1 keep a symmetric 4-level grid free of a constant term, so sums over many
@@ -232,7 +253,7 @@ struct FastSmem {
   float rk[RP ? 16 : 1][RP ? 2 * 64 + 4 : 1];
   int sinks[MAX_SINK];  // committed sink positions (< P) of this batch element
   int nsinks;
-  uint32_t tq_tab[16];  // TurboQuant K centroids: fp16 hi | fp16 lo << 16
+  uint32_t tq_tab[32];  // TurboQuant K centroids, then V centroids times 8 (4-bit V slots): fp16 hi | lo << 16
 };
 // LDS of an fp16-row workgroup (shares the allocation of the bulk workgroups).
 template <int R>
@@ -317,6 +338,9 @@ __device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t 
     } else if constexpr (KB == 2) {
       const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, o.k[tau], rec_off, 0);
       d.kd[tau][0] = x.x, d.kd[tau][1] = x.y;
+    } else if constexpr (KB == 3) {  // TurboQuant's dense 3-bit stream: 32 codes in 3 words
+      const u3 x = __builtin_amdgcn_raw_buffer_load_b96(rs, o.k[tau], rec_off, 0);
+      d.kd[tau][0] = x.x, d.kd[tau][1] = x.y, d.kd[tau][2] = x.z;
     } else {
 #pragma unroll
       for (int k = 0; k < KB / 4; ++k) {
@@ -547,7 +571,8 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
           c1[tau] = mfma(plane_a<1>(d.kd[tau], st), b, c1[tau]);
         } else if constexpr (TQ) {  // centroid hi halves, then lo halves, into one accumulator
           u4 ah, al;
-          tq_cen_a(d.kd[tau][st], tab, ah, al);
+          if constexpr (KB == 3) tq_cen_a3(dense3_step(d.kd[tau], st), tab, ah, al);
+          else tq_cen_a(d.kd[tau][st], tab, ah, al);
           c0[tau] = mfma(ah, b, c0[tau]);
           c0[tau] = mfma(al, b, c0[tau]);
         } else {
@@ -632,7 +657,17 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
     // weights times the V position factor of this token pair; masked tokens give 2^-inf = 0
     const float e0 = ex2(y0[p] + S.lfm[p]), e1 = ex2(y1[p] + S.lfm[p]);
     S.l_[p] = __builtin_fmaf(e0 + e1, S.ifv, S.l_[p]);
-    if constexpr (TQ) {
+    if constexpr (TQ && VB == 4) {
+      // 3- and 4-bit V codes: the centroids (times 8) from the LDS table are the A operand, the
+      // weights times the V norm (times 1/8, so that they stay in the fp16 range) the B operand
+      const float w0 = e0 * F32(d.vs.x) * 0.125f, w1 = e1 * F32(d.vs.y) * 0.125f;
+      const h2 wh = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz(w0, w1));
+      const h2 wl = __builtin_bit_cast(h2, __builtin_amdgcn_cvt_pkrtz((w0 - (float)wh.x) * LO_UP,
+                                                                       (w1 - (float)wh.y) * LO_UP));
+      W.ab[0][j][4 * kgt + (et >> 1)] = U32(wh);
+      W.ab[0][R + j][4 * kgt + (et >> 1)] = U32(wl);
+      continue;
+    } else if constexpr (TQ) {
       // V level = cm + vb * s0 + vg * s1 (s = 2 * bit - 1) in the rotated domain, times the V
       // norm: the two signed bit planes take the weights w * vb and w * vg (split hi/lo), the cm
       // term is sum_t w (cm = 0 for the symmetric grids the library builds)
@@ -671,7 +706,16 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
 #pragma unroll
     for (int mu = 0; mu < 8; ++mu) S.acc[mu] *= fc;
   }
-  if constexpr (TQ) {
+  if constexpr (TQ && VB == 4) {  // centroid hi halves, then lo halves, into one accumulator
+    const u4 b0 = *reinterpret_cast<const u4*>(&W.ab[0][col][4 * kg]);
+#pragma unroll
+    for (int mu = 0; mu < 8; ++mu) {
+      u4 ah, al;
+      tq_cen_a(d.vd[mu], tab + 16, ah, al);
+      S.acc[mu] = mfma(ah, b0, S.acc[mu]);
+      S.acc[mu] = mfma(al, b0, S.acc[mu]);
+    }
+  } else if constexpr (TQ) {
     const u4 b0 = *reinterpret_cast<const u4*>(&W.ab[0][col][4 * kg]);
     const u4 b1 = *reinterpret_cast<const u4*>(&W.ab[1][col][4 * kg]);
     const uint32_t nd[4] = {~d.vd[0], ~d.vd[1], ~d.vd[2], ~d.vd[3]};
@@ -732,7 +776,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R, RP>& F, int sigma)
   St S;
   const float al = a.scale * LOG2E;
   float q2k_w = 0.f, tq_c0 = 0.f;
-  float sg0 = 0.f, sg1 = 0.f, kcen = 0.f;
+  float sg0 = 0.f, sg1 = 0.f, kcen = 0.f, vcen = 0.f;
   if constexpr (TQ) {
     // rotated-domain centroids enter the MFMA as real values: no code-position factor
     S.cs = al;
@@ -742,7 +786,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R, RP>& F, int sigma)
     const float c0 = lv.tables->v_cen[0], c3 = lv.tables->v_cen[3];
     S.vb = 0.5f * (lv.tables->v_cen[1] - c0);
     S.vg = 0.5f * (lv.tables->v_cen[2] - c0);
-    tq_c0 = 0.5f * (c0 + c3);
+    tq_c0 = VB == 2 ? 0.5f * (c0 + c3) : 0.f;  // 4-bit V slots: centroids from the table, no cm term
     sg0 = lv.tables->signs[2 * lane];
     sg1 = lv.tables->signs[2 * lane + 1];
     // 1 in every lane, as a per-lane run-time value (bit 29 of the fp32 +-1 sign entries), so the
@@ -751,6 +795,7 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R, RP>& F, int sigma)
     const uint32_t one = (F32bits(sg0) >> 29) & 1u;
     S.one16 = one * 0x3C003C00u;
     kcen = tid < 16 ? lv.tables->k_cen[tid] : 0.f;
+    vcen = tid < 16 ? 8.f * lv.tables->v_cen[tid] : 0.f;
   } else if constexpr (Q2K) {
     const float c0 = lv.tables->q2k_lvl[0], c1 = lv.tables->q2k_lvl[1] - c0, c2 = lv.tables->q2k_lvl[2] - c0;
     S.cs = ldexpf(c1 * al, 24);
@@ -838,8 +883,9 @@ __device__ void bulk_partial(const DecodeArgs& a, FastSmem<R, RP>& F, int sigma)
   for (int mu = 0; mu < 8; ++mu) S.acc[mu] = f4{0.f, 0.f, 0.f, 0.f};
   if constexpr (TQ) {
     if (tid < 16) {  // K centroid table: fp16 hi and lo halves
-      const _Float16 h = (_Float16)kcen;
+      const _Float16 h = (_Float16)kcen, hv = (_Float16)vcen;
       F.tq_tab[tid] = U32(h2{h, (_Float16)(kcen - (float)h)});
+      F.tq_tab[16 + tid] = U32(h2{hv, (_Float16)(vcen - (float)hv)});
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the query, the sink list and the first block
@@ -1357,6 +1403,9 @@ int fast_resident_slots(const Shape& sh) {
   }
   if (sh.fmt == KVQ_FMT_Q2K) return slots_r<KVQ_FMT_Q2K, 2, 4, false>(r, cus);
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return slots_r<KVQ_FMT_TQ, 4, 2, false>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 4) return slots_r<KVQ_FMT_TQ, 4, 4, false>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 2) return slots_r<KVQ_FMT_TQ, 3, 2, false>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 4) return slots_r<KVQ_FMT_TQ, 3, 4, false>(r, cus);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return slots_r<KVQ_FMT_KIVI, 2, 2, false>(r, cus);
     if (sh.kb == 4) return slots_r<KVQ_FMT_KIVI, 4, 4, false>(r, cus);
@@ -1382,6 +1431,9 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st) {
   }
   if (sh.fmt == KVQ_FMT_Q2K) return launch_r<KVQ_FMT_Q2K, 2, 4, false>(a, st);
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 2) return launch_r<KVQ_FMT_TQ, 4, 2, false>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 4) return launch_r<KVQ_FMT_TQ, 4, 4, false>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 2) return launch_r<KVQ_FMT_TQ, 3, 2, false>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 4) return launch_r<KVQ_FMT_TQ, 3, 4, false>(a, st);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2, false>(a, st);
     if (sh.kb == 4) return launch_r<KVQ_FMT_KIVI, 4, 4, false>(a, st);

@@ -49,15 +49,16 @@ CASES = {
                                   v_bits=4, sink_mode="first_n", n_sink=4, window=128, residual=4),
     "fast_tq42_r2_ring_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128, fmt="tq", k_bits=4,
                                   v_bits=2, window=160, residual=16, seed=13),
-    # 3-bit TurboQuant codes (two per byte, two bits unused): K3/V2 on the matrix-core path, K4/V3 and
-    # K3/V3 on the generic one
+    # 3-bit TurboQuant codes (two per byte, one bit unused): K3/V2 on the matrix-core path, the head_dim
+    # 64 and 32 cases on the generic one
     "fast_tq32_r4_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=3,
                                   v_bits=2, sink_mode="topk", n_sink=3, residual=24, capacity=512, seed=14),
     "tq43_d64_firstn_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=64, fmt="tq", k_bits=4,
                                 v_bits=3, sink_mode="first_n", n_sink=2, window=128, residual=8, seed=15),
     "tq33_d32_f32": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=32, fmt="tq", k_bits=3, v_bits=3,
                          capacity=512, in_dtype="f32", seed=16),
-    # the dense 8-in-3 stream (codes straddle words; V chunks are not word-aligned at head_dim 32)
+    # the dense 8-in-3 stream (codes straddle words; V chunks are not word-aligned at head_dim 32); dense
+    # 3-bit K at a stored width of 128 runs on the matrix-core path
     "tq32_dense_r4_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=3,
                                    v_bits=2, sink_mode="topk", n_sink=3, residual=24, capacity=512, seed=17,
                                    tq_dense3=True),
@@ -86,6 +87,19 @@ CASES = {
                                     in_dtype="f32", seed=26, tq_dense3=True),
     "tq34_d160_r3": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=6, head_dim=160, fmt="tq", k_bits=3,
                          v_bits=4, capacity=512, seed=27),
+    # 3- and 4-bit V codes in 4-bit slots on the matrix-core path (V centroids from an LDS table)
+    "fast_tq43_r4_topk_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=4,
+                                  v_bits=3, sink_mode="topk", n_sink=3, residual=24, capacity=512, seed=28),
+    "fast_tq44_r2_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128, fmt="tq", k_bits=4,
+                             v_bits=4, sink_mode="first_n", n_sink=4, window=160, residual=16, seed=29),
+    "fast_tq34_r8_res": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="tq", k_bits=3,
+                             v_bits=4, residual=40, capacity=512, seed=30),
+    "fast_tq43_d96_r1": dict(n_layers=1, batch=1, n_kv_heads=3, n_q_heads=3, head_dim=96, fmt="tq", k_bits=4,
+                             v_bits=3, sink_mode="first_n", n_sink=2, capacity=512, seed=31),
+    # dense 3-bit K (three words per lane and row chunk) with 4-bit V slots, on the matrix-core path
+    "fast_tq34_dense_r4_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=3,
+                                   v_bits=4, sink_mode="first_n", n_sink=3, window=128, residual=16, seed=32,
+                                   tq_dense3=True),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]
