@@ -978,7 +978,8 @@ def main():
             # the other TurboQuant widths and packings at config 4's shape (same inputs and cache size)
             res["turboquant_widths"] = {}
             for name, ex in (("k3v2", dict(k_bits=3, v_bits=2)), ("k3v2_dense3", dict(k_bits=3, v_bits=2, tq_dense3=True)),
-                             ("k4v3", dict(k_bits=4, v_bits=3)), ("k4v4", dict(k_bits=4, v_bits=4))):
+                             ("k4v3", dict(k_bits=4, v_bits=3)), ("k4v4", dict(k_bits=4, v_bits=4)),
+                             ("k3v3_dense3", dict(k_bits=3, v_bits=3, tq_dense3=True))):
                 log(f"[bench] decode attention of TurboQuant {name} at config 4's shape")
                 res["turboquant_widths"][name] = decode_figure(4, dev, stream, ncalls=20, kw_extra=ex,
                                                                label=f"TurboQuant {name}")

@@ -203,11 +203,13 @@ __device__ __forceinline__ void tq_cen_a3(uint32_t x, const uint32_t* tab, u4& a
   ah = u4{hh[0], hh[1], hh[2], hh[3]};
   al = u4{ll[0], ll[1], ll[2], ll[3]};
 }
-// The 24-bit field of step st (channels 8 st .. 8 st + 7 of the lane's 32) in the lane's three
-// words of dense 3-bit K codes.
-__device__ __forceinline__ uint32_t dense3_step(const uint32_t* k, int st) {
-  return st == 0 ? k[0] : st == 1 ? __builtin_amdgcn_alignbit(k[1], k[0], 24)
-                        : st == 2 ? __builtin_amdgcn_alignbit(k[2], k[1], 16) : k[2] >> 8;
+// The 24-bit field of group g of 8 dense 3-bit codes (bits 24 g .. 24 g + 23) in a lane's words:
+// K steps (three words per row chunk) and V channel tiles (six words per chunk).
+__device__ __forceinline__ uint32_t dense3_step(const uint32_t* k, int g) {
+  const uint32_t* w = k + 3 * (g >> 2);
+  const int st = g & 3;
+  return st == 0 ? w[0] : st == 1 ? __builtin_amdgcn_alignbit(w[1], w[0], 24)
+                        : st == 2 ? __builtin_amdgcn_alignbit(w[2], w[1], 16) : w[2] >> 8;
 }
 
 // Signed plane of code bit BIT of 2-bit codes, from the complemented code words nd: every element
@@ -356,10 +358,18 @@ __device__ __forceinline__ void load_blk(Blk<KB, VB>& d, __amdgpu_buffer_rsrc_t 
     d.ks = __builtin_amdgcn_raw_buffer_load_b32(rs, o.ks, rec_off, 0);
     d.kz = Q2K ? 0u : __builtin_amdgcn_raw_buffer_load_b32(rs, o.kz, rec_off, 0);
   }
+  if constexpr (VB == 3) {  // TurboQuant's dense 3-bit stream: 64 codes of the chunk in 6 words
 #pragma unroll
-  for (int k = 0; k < VB / 2; ++k) {
-    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * k, rec_off, 0);
-    d.vd[4 * k] = x.x, d.vd[4 * k + 1] = x.y, d.vd[4 * k + 2] = x.z, d.vd[4 * k + 3] = x.w;
+    for (int k = 0; k < 2; ++k) {
+      const u3 x = __builtin_amdgcn_raw_buffer_load_b96(rs, o.v + 12 * k, rec_off, 0);
+      d.vd[3 * k] = x.x, d.vd[3 * k + 1] = x.y, d.vd[3 * k + 2] = x.z;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < VB / 2; ++k) {
+      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, o.v + 16 * k, rec_off, 0);
+      d.vd[4 * k] = x.x, d.vd[4 * k + 1] = x.y, d.vd[4 * k + 2] = x.z, d.vd[4 * k + 3] = x.w;
+    }
   }
   if constexpr (TQ) {
     const u2 x = __builtin_amdgcn_raw_buffer_load_b64(rs, o.vs, rec_off, 0);
@@ -657,7 +667,7 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
     // weights times the V position factor of this token pair; masked tokens give 2^-inf = 0
     const float e0 = ex2(y0[p] + S.lfm[p]), e1 = ex2(y1[p] + S.lfm[p]);
     S.l_[p] = __builtin_fmaf(e0 + e1, S.ifv, S.l_[p]);
-    if constexpr (TQ && VB == 4) {
+    if constexpr (TQ && VB != 2) {
       // 3- and 4-bit V codes: the centroids (times 8) from the LDS table are the A operand, the
       // weights times the V norm (times 1/8, so that they stay in the fp16 range) the B operand
       const float w0 = e0 * F32(d.vs.x) * 0.125f, w1 = e1 * F32(d.vs.y) * 0.125f;
@@ -706,12 +716,13 @@ __device__ __forceinline__ void block_step(State<FMT, KB, VB, R>& S, FastWave<R,
 #pragma unroll
     for (int mu = 0; mu < 8; ++mu) S.acc[mu] *= fc;
   }
-  if constexpr (TQ && VB == 4) {  // centroid hi halves, then lo halves, into one accumulator
+  if constexpr (TQ && VB != 2) {  // centroid hi halves, then lo halves, into one accumulator
     const u4 b0 = *reinterpret_cast<const u4*>(&W.ab[0][col][4 * kg]);
 #pragma unroll
     for (int mu = 0; mu < 8; ++mu) {
       u4 ah, al;
-      tq_cen_a(d.vd[mu], tab + 16, ah, al);
+      if constexpr (VB == 3) tq_cen_a3(dense3_step(d.vd, mu), tab + 16, ah, al);
+      else tq_cen_a(d.vd[mu], tab + 16, ah, al);
       S.acc[mu] = mfma(ah, b0, S.acc[mu]);
       S.acc[mu] = mfma(al, b0, S.acc[mu]);
     }
@@ -1406,6 +1417,8 @@ int fast_resident_slots(const Shape& sh) {
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 4) return slots_r<KVQ_FMT_TQ, 4, 4, false>(r, cus);
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 2) return slots_r<KVQ_FMT_TQ, 3, 2, false>(r, cus);
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 4) return slots_r<KVQ_FMT_TQ, 3, 4, false>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 3) return slots_r<KVQ_FMT_TQ, 4, 3, false>(r, cus);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 3) return slots_r<KVQ_FMT_TQ, 3, 3, false>(r, cus);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return slots_r<KVQ_FMT_KIVI, 2, 2, false>(r, cus);
     if (sh.kb == 4) return slots_r<KVQ_FMT_KIVI, 4, 4, false>(r, cus);
@@ -1434,6 +1447,8 @@ hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t st) {
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 4) return launch_r<KVQ_FMT_TQ, 4, 4, false>(a, st);
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 2) return launch_r<KVQ_FMT_TQ, 3, 2, false>(a, st);
   if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 4) return launch_r<KVQ_FMT_TQ, 3, 4, false>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 4 && sh.vb == 3) return launch_r<KVQ_FMT_TQ, 4, 3, false>(a, st);
+  if (sh.fmt == KVQ_FMT_TQ && sh.kb == 3 && sh.vb == 3) return launch_r<KVQ_FMT_TQ, 3, 3, false>(a, st);
   if (sh.fmt == KVQ_FMT_KIVI && sh.kb == sh.vb) {
     if (sh.kb == 2) return launch_r<KVQ_FMT_KIVI, 2, 2, false>(a, st);
     if (sh.kb == 4) return launch_r<KVQ_FMT_KIVI, 4, 4, false>(a, st);

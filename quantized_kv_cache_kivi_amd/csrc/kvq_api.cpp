@@ -191,8 +191,7 @@ bool fast_path(const kvq_config& c) {
          (r == 1 || r == 2 || r == 4 || r == 8) &&
          (c.rope ? kivi_eq
                  : (c.format == KVQ_FMT_Q2K || kivi_eq ||
-                    (c.format == KVQ_FMT_TQ && (c.k_bits == 4 || c.k_bits == 3) &&
-                     (c.v_bits == 2 || slot_bits(c.v_bits, c.tq_dense3) == 4))));
+                    (c.format == KVQ_FMT_TQ && c.k_bits >= 3 && c.v_bits >= 2)));
 }
 
 // Split-K policy over nblk bulk blocks.  MFMA path: 4 waves per workgroup, whole rounds of the

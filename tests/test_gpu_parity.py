@@ -100,6 +100,13 @@ CASES = {
     "fast_tq34_dense_r4_win": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=8, head_dim=128, fmt="tq", k_bits=3,
                                    v_bits=4, sink_mode="first_n", n_sink=3, window=128, residual=16, seed=32,
                                    tq_dense3=True),
+    # dense 3-bit V (six words per lane's chunk) on the matrix-core path
+    "fast_tq33_dense_r2_topk": dict(n_layers=1, batch=2, n_kv_heads=2, n_q_heads=4, head_dim=128, fmt="tq", k_bits=3,
+                                    v_bits=3, sink_mode="topk", n_sink=2, residual=8, capacity=512, seed=33,
+                                    tq_dense3=True),
+    "fast_tq43_dense_r8_win": dict(n_layers=1, batch=1, n_kv_heads=2, n_q_heads=16, head_dim=128, fmt="tq", k_bits=4,
+                                   v_bits=3, sink_mode="first_n", n_sink=4, window=160, residual=24, seed=34,
+                                   tq_dense3=True),
 }
 
 SCHEDULE = [70, 1, 1, 33, 1, 100, 2, 31, 1]
