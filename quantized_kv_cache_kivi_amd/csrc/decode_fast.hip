@@ -33,6 +33,11 @@
 //    stored in this operand order); the weights times the V scale are split
 //    hi/lo the same way (packed fp16 product of fp16 halves of p and the fp16
 //    scale); the zero-point term sum_t p z is a packed dot product per lane.
+//  * TurboQuant ("TurboQuant KV Cache Compression — Spec", "Optimization: Fused
+//    dequant-dot"): scores against the rotated query (computed once), K
+//    centroids as fp16 hi and lo halves from a 16-entry LDS table; V2 as two
+//    +-1 bit planes (the symmetric 4-level grid), V3/V4 as centroids from a
+//    second table; 3-bit codes in 4-bit slots or in the dense 8-in-3 stream.
 // Four waves per workgroup take interleaved blocks of the split, each with the
 // next block in flight while it computes one, and merge in LDS; the workgroup
 // writes one partial.
