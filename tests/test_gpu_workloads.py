@@ -261,6 +261,18 @@ def test_workload_turboquant_16k():
     w.check_dequant(0, [(0, 33), (16384 - 31, 65)])
 
 
+@pytest.mark.parametrize("kb,vb,dense", [(4, 4, False), (3, 3, True)])
+def test_workload_turboquant_widths_16k(kb, vb, dense):
+    """Config 4's shape with other TurboQuant widths on the matrix-core decode: K4/V4 (V centroids from
+    the LDS table) and K3/V3 in the dense 8-in-3 stream; bytes after the prefill and after 3 steps."""
+    w = Workload(4, oracle="c", k_bits=kb, v_bits=vb, tq_dense3=dense)
+    w.prefill()
+    w.check_bytes(0)
+    w.check_attention(0, w.query(1))
+    _decode_steps(w, 3, {0, 2}, 0)
+    w.check_bytes(0)
+
+
 def test_workload_long_streaming_int4():
     """Batch 64, full 65540-token cache (sink 4, W = 65536), then 256 steps of append + evict + attention.
     The ring (2050 blocks, 65600 slots) wraps at step 60; attention at steps 0, 1, 2, 31, 32, 33, 127,
